@@ -1,0 +1,187 @@
+"""Benchmark of the routed-MoE block on one MI355X.
+
+Workload: the b=16 decode/verify step (H=4096, P=2048, I=1024, E=64,
+top_k=4, sigmoid scoring, MXFP4 experts), synthetic seeded inputs.  One step
+is one mb_moe_block call (router, routing, pooler, experts, tail, unpooler,
+boundary) on inputs already resident in HBM.  The steps rotate over several
+independently drawn weight sets (about 1 GB in total, four times the 256 MB
+Infinity Cache), so every step streams its weights from HBM, as the 60
+distinct layers of a decode step do.
+
+Prints one JSON line: rows/s (value), microseconds per block, the achieved
+algorithmic HBM bandwidth against the 8 TB/s peak (roofline), and the CPU
+oracle's rate on a bounded sample of the same workload (cpu_baseline).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-block rows/s + achieved HBM GB/s (% of peak) at b=16 decode, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+WEIGHT_SEEDS = (1, 1001, 2001, 3001)
+
+
+def algorithmic_bytes(d, n_active: int, norm_weights=(False, False, False)) -> int:
+    """Bytes the block must move: the used experts' MXFP4 w13/w2 and E8M0
+    scales, router weight and bias, pooler and unpooler, norm and gate
+    vectors, and the block's inputs and outputs (x, stream read and write,
+    x_next, ids and weights).  Intermediates that can stay on chip are not
+    counted."""
+    b, H, P, I, E, k = d.rows, d.hidden, d.pooled, d.inter, d.experts, d.top_k
+    expert = 2 * I * P // 2 + 2 * I * P // 32 + P * I // 2 + P * I // 32
+    pre, pff, win = norm_weights
+    return (n_active * expert + E * H * 4 + E * 4 + 2 * P * H * 2 + P * 2 * (1 + pre)
+            + H * 2 * (1 + pff + win) + b * H * 2 + 2 * b * H * 4 + b * H * 2 + b * k * 8)
+
+
+def cpu_baseline(blk, seconds: float) -> dict:
+    import numpy as np  # noqa: F401
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity
+        threads = len(os.sched_getaffinity(0))
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.block(blk)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(blk.dims.rows * n / el, 3), "unit": "rows/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} full b={blk.dims.rows} decode blocks (weight set 0) through the numpy "
+                      f"fp64 oracle, {el:.1f} s; cores = its BLAS thread pool"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--sets", type=int, default=len(WEIGHT_SEEDS))
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(the block has no multi-GPU path in this build)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import routed_expert_layer_amd as rel
+    import synth
+    from synth.device import dims_kwargs, upload, upload_weights
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    seeds = [WEIGHT_SEEDS[i % len(WEIGHT_SEEDS)] + 10000 * (i // len(WEIGHT_SEEDS))
+             for i in range(args.sets)]
+    print(f"[bench] generating {len(seeds)} c1 weight sets", file=sys.stderr, flush=True)
+    blocks = [synth.make_block("c1", seed=s) for s in seeds]
+    d = blocks[0].dims
+    wt0, x, stream = upload(blocks[0], dev)
+    tensors = [wt0] + [upload_weights(b, dev) for b in blocks[1:]]
+    weights = [rel.make_weights(**t) for t in tensors]
+    dims = rel.make_dims(**dims_kwargs(d))
+    ws = rel.workspace(dims, dev)
+    x_next = torch.zeros((d.rows, d.hidden), dtype=torch.bfloat16, device=dev)
+
+    # Experts each weight set's routing activates (|U| of the byte count).
+    n_act = torch.zeros(1, dtype=torch.int32, device=dev)
+    actives = []
+    for w in weights:
+        s = stream.clone()
+        rel.mb_moe_block(dims, x, w, s, x_next, ws, taps=rel.make_taps(n_active=n_act))
+        torch.cuda.synchronize()
+        actives.append(int(n_act.item()))
+    nw = (blocks[0].pre_norm_w is not None, blocks[0].ffn_norm_w is not None,
+          blocks[0].next_norm_w is not None)
+    b_alg = float(np.mean([algorithmic_bytes(d, a, nw) for a in actives]))
+
+    S = len(weights)
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        rel.mb_moe_block(dims, x, weights[i % S], stream, x_next, ws)
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    cur = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(cur)
+    for i in range(args.steps):
+        rel.mb_moe_block(dims, x, weights[i % S], stream, x_next, ws)
+    ev1.record(cur)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1)
+    ms_step = ms / args.steps
+    us_block = ms_step * 1e3
+    rows_s = d.rows * args.steps / (ms / 1e3)
+    achieved = b_alg / (us_block * 1e-6) / 1e9
+    print(f"[bench] {us_block:.2f} us/block, {rows_s:.0f} rows/s, {achieved:.0f} GB/s "
+          f"({100 * achieved / HBM_PEAK_GBS:.1f}% of 8 TB/s), wall {wall * 1e3 / args.steps:.2f} "
+          f"ms/step, active experts {actives}", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(blocks[0], args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(rows_s, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode verify step b=16: H=4096 P=2048 I=1024 E=64 top_k=4 sigmoid, "
+                        "MXFP4 experts, bf16 pooler/unpooler, fp32 router and stream",
+            "rows": d.rows, "weight_sets": S, "active_experts": actives,
+            "us_per_block": round(us_block, 3),
+            "algorithmic_bytes_per_block": int(b_alg),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "mb_moe_block",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,222 @@
+/*
+ * mb.h - C ABI of the MI355X (gfx950) routed-MoE block library libmb.so.
+ *
+ * The library computes one decode/verify step of a MuseSpark1x-style routed
+ * mixture-of-experts block on one GPU:
+ *
+ *   router (fp32) -> sigmoid/softmax scores -> top-k with a selection-only
+ *   expert bias -> normalised, scaled route weights -> route grouping
+ *   -> bf16 pooler H->P -> per-route MXFP4 experts (w13, gated activation, w2)
+ *   -> per-route RMSNorm over P -> weighted sum over routes -> bf16 unpooler
+ *   P->H -> boundary (RMSNorm, gated add into the fp32 residual stream, next
+ *   pre-norm).
+ *
+ * Sources, by page title and section:
+ *   [muse_moe_runner] vllm.models.muse_spark.amd.muse_moe_runner
+ *   [mono.decoder]    vllm.models.muse_spark.amd.mono.decoder
+ *   [providers]       vllm.models.muse_spark.nvidia.specialized_decode.runtime.providers
+ *
+ * Conventions (all entry points):
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *   - Every tensor pointer is DEVICE memory, row-major and contiguous, and
+ *     must be 16-byte aligned (MB_ERR_ALIGN otherwise).  Sizes are in
+ *     elements unless stated.
+ *   - The caller owns every buffer, including the workspace.  The library
+ *     never allocates, frees or synchronises; weights are read in place, never
+ *     copied ([mono.decoder] collect_layer_weights: views, no copy;
+ *     [providers] Provider: run allocates nothing).
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     null stream) ([providers]: every provider launches on the current
+ *     stream).  Argument checks happen on the host before any launch; a
+ *     nonzero status means nothing was enqueued, except MB_ERR_HIP, which
+ *     reports a failed launch.  Faults inside kernels surface at the caller's
+ *     next synchronisation.
+ *   - The workspace must be zero-filled once before its first use.  Every
+ *     call leaves the counters it uses back at zero, so one workspace serves
+ *     any number of calls.  Calls that share a workspace must not overlap.
+ *   - Limits (MB_ERR_UNSUPPORTED beyond them): rows <= 1024, experts <= 1024,
+ *     top_k <= 16, experts * ceil(rows / 64) <= 4096, hidden % 32 == 0,
+ *     pooled % 128 == 0, inter % 128 == 0.
+ */
+#ifndef MB_H
+#define MB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  MB_OK = 0,
+  MB_ERR_NULL = 1,        /* a required pointer is NULL */
+  MB_ERR_DIMS = 2,        /* non-positive size, top_k > experts, bad scoring */
+  MB_ERR_UNSUPPORTED = 3, /* outside the limits above */
+  MB_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
+  MB_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than mb_workspace_bytes */
+  MB_ERR_HIP = 6          /* a kernel launch failed */
+};
+
+/* Scoring functions ([muse_moe_runner] MuseSpark1xRouter: the score
+ * normalisation is "sigmoid" or "softmax"; anything else is a ValueError). */
+enum { MB_SCORING_SIGMOID = 0, MB_SCORING_SOFTMAX = 1 };
+
+/* mb_route flags. */
+enum {
+  MB_LOGITS_OUT = 1, /* also write the fp32 router logits [rows, experts] */
+  MB_LOGITS_IN = 2   /* skip the projection; route from the caller's logits */
+};
+
+/* Block sizes and routing scalars.
+ *   rows     b, the tokens (decode/verify rows) of the step
+ *   hidden   H, model width            pooled  P, expert input width
+ *   inter    I, expert intermediate    experts E, top_k k
+ * route_scale, router_multiplier and division_eps follow [muse_moe_runner]
+ * MuseSpark1xRouter: an absent multiplier is 1.0f and an absent eps is 0.0f
+ * (both leave the fp32 result unchanged).  norm_eps is the epsilon of every
+ * RMSNorm in the block. */
+typedef struct {
+  int32_t rows, hidden, pooled, inter, experts, top_k;
+  int32_t scoring;
+  float route_scale;
+  float router_multiplier;
+  float division_eps;
+  float norm_eps;
+} mb_dims;
+
+/* The block's weights, all device pointers, in the layouts the pages fix:
+ *   router_w    fp32 [E, H]   ([mono.decoder] layer_refusals: router fp32 (E, H))
+ *   expert_bias fp32 [E]      selection-only bias
+ *   pool_w      bf16 [P, H]   pooler   ([mono.decoder] layer_refusals)
+ *   pre_norm_w  bf16 [P] or NULL: optional RMSNorm of the pooler output
+ *               ([providers] MoEProvider: pre_expert_norm)
+ *   w13         u8 [E, 2I, P/2]  MXFP4 codes, rows [0, I) gate, [I, 2I) up
+ *   w13_scale   u8 [E, 2I, P/32] E8M0 scales
+ *   w2          u8 [E, P, I/2]   w2_scale u8 [E, P, I/32]
+ *               ([mono.decoder] MonoDims.expert_shapes; two E2M1 codes per
+ *               byte, the even element in the low nibble; one E8M0 scale per
+ *               32 elements along the contraction dimension)
+ *   post_norm_w bf16 [P]      per-route norm weight
+ *   unpool_w    bf16 [H, P]   unpooler ([mono.decoder] layer_refusals)
+ *   ffn_norm_w  bf16 [H] or NULL (= 1): boundary post-FFN norm weight
+ *   gate        bf16 [H]      boundary gate g
+ *   next_norm_w bf16 [H] or NULL (= 1): next layer's pre-norm weight
+ * Norm weights are the effective bf16 multipliers ([mono.decoder]
+ * effective_norm_weight), applied after normalising. */
+typedef struct {
+  const float *router_w;
+  const float *expert_bias;
+  const uint16_t *pool_w;
+  const uint16_t *pre_norm_w;
+  const uint8_t *w13;
+  const uint8_t *w13_scale;
+  const uint8_t *w2;
+  const uint8_t *w2_scale;
+  const uint16_t *post_norm_w;
+  const uint16_t *unpool_w;
+  const uint16_t *ffn_norm_w;
+  const uint16_t *gate;
+  const uint16_t *next_norm_w;
+} mb_weights;
+
+/* Optional intermediate outputs of mb_moe_block.  A NULL member is kept in
+ * the workspace instead.  Shapes as in mb_route / mb_pool / mb_experts /
+ * mb_unpool_boundary. */
+typedef struct {
+  float *logits;       /* fp32 [b, E] */
+  int32_t *topk_ids;   /* int32 [b, k] */
+  float *topk_w;       /* fp32 [b, k] */
+  int32_t *count;      /* int32 [E] */
+  int32_t *offset;     /* int32 [E + 1] */
+  int32_t *route_list; /* int32 [b * k] */
+  int32_t *active;     /* int32 [E] */
+  int32_t *n_active;   /* int32 [1] */
+  uint16_t *h;         /* bf16 [b, P] */
+  uint16_t *moe_out;   /* bf16 [b, P] */
+  uint16_t *u;         /* bf16 [b, H] */
+} mb_block_taps;
+
+/* Bytes of workspace every entry point needs for these dims (the same size
+ * serves all of them).  Returns MB_OK, MB_ERR_NULL, MB_ERR_DIMS or
+ * MB_ERR_UNSUPPORTED. */
+int mb_workspace_bytes(const mb_dims *dims, size_t *bytes);
+
+/* Router and routing ([muse_moe_runner] MuseSpark1xRouter and its
+ * _compute_routing_native recipe; [providers] RoutedTopk).
+ *   logits = x @ router_w^T (fp32 [b, E]; x bf16 [b, H]); optional output
+ *   multiplier; sigmoid or softmax; selection key = score + expert_bias
+ *   (selection only); top-k by key descending, lowest expert id first among
+ *   equal keys, slot j = rank j; weights = gathered UNBIASED scores divided by
+ *   (their sum + division_eps), times route_scale, in fp32.
+ * Outputs: topk_ids int32 [b, k], topk_w fp32 [b, k], and the route grouping
+ * the experts consume: count int32 [E] routes per expert; offset int32 [E+1]
+ * exclusive prefix sum (offset[E] = b*k); route_list int32 [b*k], the routes
+ * r = t*k + j sorted by (expert, r); active int32 [E], the experts with
+ * count > 0 ascending, n_active int32 [1] of them (the rest of `active` is
+ * left unwritten).
+ * flags: MB_LOGITS_OUT writes the logits to `logits` (may then not be NULL);
+ * MB_LOGITS_IN reads them from `logits` and ignores x and router_w. */
+int mb_route(const mb_dims *dims, const uint16_t *x, const mb_weights *w,
+             float *logits, int flags, int32_t *topk_ids, float *topk_w,
+             int32_t *count, int32_t *offset, int32_t *route_list,
+             int32_t *active, int32_t *n_active, void *workspace,
+             size_t workspace_bytes, void *stream);
+
+/* Pooler: h = bf16(x @ pool_w^T), bf16 [b, P]; then, if w->pre_norm_w is not
+ * NULL, h = bf16(RMSNorm_P(h) * pre_norm_w) ([providers] MoEProvider:
+ * pooler GEMM + pre_expert_norm; [mono.decoder] _K5Bucket: h bf16 [rows, P]).
+ * Independent of routing ([providers] RoutedMoE.run runs it beside the
+ * routing). */
+int mb_pool(const mb_dims *dims, const uint16_t *x, const mb_weights *w,
+            uint16_t *h, void *workspace, size_t workspace_bytes,
+            void *stream);
+
+/* Routed experts and tail ([muse_moe_runner] MuseSparkAiterExperts.apply:
+ * one unweighted output per route; MuseSparkTopKWeightAndReduce.apply:
+ * per-route norm, then route weight, then sum over routes, then cast).
+ * For each route (t, j) with e = topk_ids[t, j]:
+ *   gu  = dec(w13[e]) @ h[t]                 (fp32, 2I values)
+ *   act = bf16(silu(gu[0:I]) * gu[I:2I])
+ *   y   = dec(w2[e]) @ act                   (fp32, P values)
+ *   yn  = y / sqrt(mean(y^2) + norm_eps) * post_norm_w
+ * moe_out[t] = bf16(sum_j topk_w[t, j] * yn(t, j)), bf16 [b, P].
+ * The grouping arrays are mb_route's outputs for the same topk_ids. */
+int mb_experts(const mb_dims *dims, const uint16_t *h, const int32_t *topk_ids,
+               const float *topk_w, const int32_t *count,
+               const int32_t *offset, const int32_t *route_list,
+               const int32_t *active, const int32_t *n_active,
+               const mb_weights *w, uint16_t *moe_out, void *workspace,
+               size_t workspace_bytes, void *stream);
+
+/* Unpooler and boundary ([providers] BoundaryProvider: post_ffn_norm, the
+ * gated add into the fp32 stream in place, the next pre-norm into bf16 out;
+ * [providers] MoEProvider: the unpooler GEMM):
+ *   u      = bf16(moe_out @ unpool_w^T)                     bf16 [b, H]
+ *   v      = RMSNorm_H(u) * ffn_norm_w
+ *   stream = fp32(stream + gate * v)                        in place, fp32 [b, H]
+ *   x_next = bf16(RMSNorm_H(stream) * next_norm_w)          bf16 [b, H]
+ * u_out may be NULL (u then stays in the workspace). */
+int mb_unpool_boundary(const mb_dims *dims, const uint16_t *moe_out,
+                       const mb_weights *w, float *stream, uint16_t *x_next,
+                       uint16_t *u_out, void *workspace,
+                       size_t workspace_bytes, void *stream_handle);
+
+/* The whole block: mb_route + mb_pool, mb_experts, mb_unpool_boundary in one
+ * call ([providers] MoEProvider followed by BoundaryProvider; [mono.decoder]
+ * _K3Bucket runs the layer as a single launch at small row counts).  x bf16
+ * [b, H] in; stream fp32 [b, H] updated in place; x_next bf16 [b, H] out.
+ * taps may be NULL. */
+int mb_moe_block(const mb_dims *dims, const uint16_t *x, const mb_weights *w,
+                 float *stream, uint16_t *x_next, const mb_block_taps *taps,
+                 void *workspace, size_t workspace_bytes, void *stream_handle);
+
+/* A static, human-readable reason for a status code. */
+const char *mb_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MB_H */

@@ -1,0 +1,75 @@
+// The FFN boundary after the unpooler ([providers] BoundaryProvider:
+// post_ffn_norm, the gated add into the fp32 stream in place, and the next
+// pre-norm into a bf16 output):
+//   v      = u / sqrt(mean_H(u^2) + eps) * ffn_norm_w
+//   stream = fp32(stream + gate * v)          (one rounding: fma)
+//   x_next = bf16(stream / sqrt(mean_H(stream^2) + eps) * next_norm_w)
+// One workgroup per row; both sums of squares are fixed-order block sums.
+
+#include "mb_device.h"
+#include "mb_internal.h"
+
+namespace mb {
+namespace {
+
+__device__ __forceinline__ void unpack4(u32x2_t v, float o[4]) {
+  o[0] = bf16_bits_to_f32(v[0] & 0xFFFFu);
+  o[1] = bf16_bits_to_f32(v[0] >> 16);
+  o[2] = bf16_bits_to_f32(v[1] & 0xFFFFu);
+  o[3] = bf16_bits_to_f32(v[1] >> 16);
+}
+
+__global__ __launch_bounds__(256) void boundary_kernel(
+    const uint16_t *__restrict__ u, float *__restrict__ stream, const uint16_t *__restrict__ gate,
+    const uint16_t *__restrict__ wpff, const uint16_t *__restrict__ win,
+    uint16_t *__restrict__ x_next, int H, float eps) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const uint16_t *urow = u + (size_t)t * H;
+  float *srow = stream + (size_t)t * H;
+  float ss = 0.f;
+  for (int h = threadIdx.x * 4; h < H; h += blockDim.x * 4) {
+    float v[4];
+    unpack4(*reinterpret_cast<const u32x2_t *>(urow + h), v);
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  ss = block_sum(ss, red);
+  const float ru = 1.0f / sqrtf(ss / (float)H + eps);
+  float s2 = 0.f;
+  for (int h = threadIdx.x * 4; h < H; h += blockDim.x * 4) {
+    float v[4], gg[4], wf[4] = {1.f, 1.f, 1.f, 1.f};
+    unpack4(*reinterpret_cast<const u32x2_t *>(urow + h), v);
+    unpack4(*reinterpret_cast<const u32x2_t *>(gate + h), gg);
+    if (wpff) unpack4(*reinterpret_cast<const u32x2_t *>(wpff + h), wf);
+    f32x4_t s = *reinterpret_cast<const f32x4_t *>(srow + h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float vn = v[i] * ru * wf[i];
+      s[i] = fmaf(gg[i], vn, s[i]);
+      s2 += s[i] * s[i];
+    }
+    *reinterpret_cast<f32x4_t *>(srow + h) = s;
+  }
+  s2 = block_sum(s2, red);
+  const float rsn = 1.0f / sqrtf(s2 / (float)H + eps);
+  for (int h = threadIdx.x * 4; h < H; h += blockDim.x * 4) {
+    float wi[4] = {1.f, 1.f, 1.f, 1.f};
+    if (win) unpack4(*reinterpret_cast<const u32x2_t *>(win + h), wi);
+    const f32x4_t s = *reinterpret_cast<const f32x4_t *>(srow + h);
+    u32x2_t pk = {pack_bf16x2(s[0] * rsn * wi[0], s[1] * rsn * wi[1]),
+                  pack_bf16x2(s[2] * rsn * wi[2], s[3] * rsn * wi[3])};
+    *reinterpret_cast<u32x2_t *>(x_next + (size_t)t * H + h) = pk;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_boundary(const mb_dims &d, const uint16_t *u, float *stream,
+                           const uint16_t *gate, const uint16_t *ffn_norm_w,
+                           const uint16_t *next_norm_w, uint16_t *x_next, hipStream_t s) {
+  hipLaunchKernelGGL(boundary_kernel, dim3(d.rows), dim3(256), 0, s, u, stream, gate, ffn_norm_w,
+                     next_norm_w, x_next, d.hidden, d.norm_eps);
+  return hipGetLastError();
+}
+
+}  // namespace mb

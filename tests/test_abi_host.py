@@ -1,0 +1,147 @@
+"""Host-side checks of libmb.so that need no GPU: it loads, exports every entry
+point include/mb.h declares, and rejects bad arguments before any launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import routed_expert_layer_amd as rel
+from routed_expert_layer_amd import MB_ERR_ALIGN, MB_ERR_DIMS, MB_ERR_NULL, MB_ERR_UNSUPPORTED, MB_ERR_WORKSPACE, MB_OK
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(rel.LIB_PATH),
+                                reason="libmb.so not built (python -m routed_expert_layer_amd.build)")
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "mb.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mb_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = header_functions()
+    for n in ("mb_route", "mb_pool", "mb_experts", "mb_unpool_boundary", "mb_moe_block",
+              "mb_workspace_bytes", "mb_status_string"):
+        assert n in names
+    assert set(names) == set(rel.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(rel.LIB_PATH)
+    for n in header_functions():
+        assert hasattr(lib, n), n
+
+
+def c1_dims(**over):
+    kw = dict(rows=16, hidden=4096, pooled=2048, inter=1024, experts=64, top_k=4,
+              scoring="sigmoid", route_scale=2.5)
+    kw.update(over)
+    return rel.make_dims(**kw)
+
+
+def status_of_ws(d):
+    n = ctypes.c_size_t(0)
+    return rel.lib().mb_workspace_bytes(ctypes.byref(d), ctypes.byref(n)), n.value
+
+
+def test_workspace_bytes_ok_and_monotone():
+    st, n16 = status_of_ws(c1_dims())
+    assert st == MB_OK and n16 > 0 and n16 % 256 == 0
+    st, n64 = status_of_ws(c1_dims(rows=64))
+    assert st == MB_OK and n64 > n16
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(rows=0), MB_ERR_DIMS),
+    (dict(hidden=-32), MB_ERR_DIMS),
+    (dict(top_k=65), MB_ERR_DIMS),
+    (dict(scoring="relu"), MB_ERR_DIMS),
+    (dict(norm_eps=-1.0), MB_ERR_DIMS),
+    (dict(route_scale=float("inf")), MB_ERR_DIMS),
+    (dict(rows=1025), MB_ERR_UNSUPPORTED),
+    (dict(experts=2048, top_k=4), MB_ERR_UNSUPPORTED),
+    (dict(top_k=17), MB_ERR_UNSUPPORTED),
+    (dict(pooled=2000), MB_ERR_UNSUPPORTED),
+    (dict(inter=1000), MB_ERR_UNSUPPORTED),
+    (dict(hidden=4100), MB_ERR_UNSUPPORTED),
+    (dict(rows=1024, experts=512), MB_ERR_UNSUPPORTED),
+])
+def test_bad_dims_rejected(over, code):
+    assert status_of_ws(c1_dims(**over))[0] == code
+
+
+def test_status_strings():
+    assert rel.status_string(0) == "ok"
+    for st in range(1, 7):
+        assert len(rel.status_string(st)) > 10
+    assert rel.status_string(99) == "unknown status"
+
+
+FAKE = 0x100000  # a 16-byte-aligned address that is never dereferenced
+
+
+def call_route(d, x=FAKE, wts=None, flags=0, logits=None, ws=FAKE, ws_bytes=1 << 40, out=FAKE):
+    w = rel.Weights() if wts is None else wts
+    return rel.lib().mb_route(ctypes.byref(d), x, ctypes.byref(w), logits, flags, out, out, out,
+                              out, out, out, out, ws, ws_bytes, None)
+
+
+def full_weights(**over):
+    names = dict(router_w=FAKE, expert_bias=FAKE, pool_w=FAKE, w13=FAKE, w13_scale=FAKE, w2=FAKE,
+                 w2_scale=FAKE, post_norm_w=FAKE, unpool_w=FAKE, gate=FAKE)
+    names.update(over)
+    return rel.Weights(*[names.get(n) for n in rel._WEIGHT_FIELDS])
+
+
+def test_route_argument_checks_before_launch():
+    d = c1_dims()
+    assert call_route(d, wts=full_weights(router_w=None)) == MB_ERR_NULL
+    assert call_route(d, wts=full_weights(expert_bias=None)) == MB_ERR_NULL
+    assert call_route(d, wts=full_weights(), x=None) == MB_ERR_NULL
+    assert call_route(d, wts=full_weights(), out=None) == MB_ERR_NULL
+    assert call_route(d, wts=full_weights(), x=FAKE + 4) == MB_ERR_ALIGN
+    assert call_route(d, wts=full_weights(), flags=1) == MB_ERR_NULL  # logits out needs a buffer
+    assert call_route(d, wts=full_weights(), flags=3, logits=FAKE) == MB_ERR_DIMS
+    assert call_route(d, wts=full_weights(), flags=8, logits=FAKE) == MB_ERR_DIMS
+    assert call_route(d, wts=full_weights(), ws=None) == MB_ERR_WORKSPACE
+    assert call_route(d, wts=full_weights(), ws_bytes=16) == MB_ERR_WORKSPACE
+    assert call_route(d, wts=full_weights(), ws=FAKE + 8) == MB_ERR_ALIGN
+    # Routing from given logits needs neither x nor the router weight.
+    assert call_route(d, wts=full_weights(router_w=None), x=None, flags=2, logits=None) == MB_ERR_NULL
+
+
+def test_other_entry_points_check_arguments():
+    d = c1_dims()
+    L = rel.lib()
+    w = full_weights(w2=None)
+    assert L.mb_experts(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                        ctypes.byref(w), FAKE, FAKE, 1 << 40, None) == MB_ERR_NULL
+    w = full_weights(pool_w=FAKE + 2)
+    assert L.mb_pool(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE, 1 << 40, None) == MB_ERR_ALIGN
+    w = full_weights(gate=None)
+    assert L.mb_unpool_boundary(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE, None, FAKE,
+                                1 << 40, None) == MB_ERR_NULL
+    w = full_weights()
+    assert L.mb_unpool_boundary(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE, FAKE + 4, FAKE,
+                                1 << 40, None) == MB_ERR_ALIGN
+    taps = rel.Taps(*([None] * 8 + [FAKE + 2, None, None]))
+    assert L.mb_moe_block(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE, ctypes.byref(taps),
+                          FAKE, 1 << 40, None) == MB_ERR_ALIGN
+    assert L.mb_moe_block(ctypes.byref(d), FAKE, ctypes.byref(w), None, FAKE, None, FAKE, 1 << 40,
+                          None) == MB_ERR_NULL
+    bad = c1_dims(top_k=0)
+    assert L.mb_moe_block(ctypes.byref(bad), FAKE, ctypes.byref(w), FAKE, FAKE, None, FAKE,
+                          1 << 40, None) == MB_ERR_DIMS
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    d = c1_dims()
+    with pytest.raises(ValueError):
+        rel.mb_pool(d, torch.zeros(16, 4096, dtype=torch.bfloat16), rel.Weights(),
+                    torch.zeros(1), torch.zeros(8, dtype=torch.uint8))
