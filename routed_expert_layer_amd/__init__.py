@@ -48,7 +48,7 @@ class Dims(ctypes.Structure):
 _WEIGHT_FIELDS = ("router_w", "expert_bias", "pool_w", "pre_norm_w", "w13", "w13_scale", "w2",
                   "w2_scale", "post_norm_w", "unpool_w", "ffn_norm_w", "gate", "next_norm_w")
 _TAP_FIELDS = ("logits", "topk_ids", "topk_w", "count", "offset", "route_list", "active",
-               "n_active", "h", "moe_out", "u")
+               "n_active", "h", "moe_out", "u", "timeline")
 
 
 class Weights(ctypes.Structure):

@@ -3,7 +3,9 @@
 
 #include <math.h>
 
+#include "mb_block.h"
 #include "mb_internal.h"
+#include "mb_sync.h"
 
 namespace mb {
 
@@ -20,6 +22,12 @@ Layout layout_of(const mb_dims &d) {
     o = align256(o + bytes);
     return at;
   };
+  // Words the kernels leave at zero after every call come first, at offsets
+  // that depend only on H and P, so one workspace serves calls of any row
+  // count.
+  L.sync = take(sync_words(d.experts) * 4);
+  L.pool_cnt = take((P / 16) * 4);
+  L.unpool_cnt = take((H / 16) * 4);
   L.logits = take(b * E * 4);
   L.ids = take(R * 4);
   L.wts = take(R * 4);
@@ -35,7 +43,9 @@ Layout layout_of(const mb_dims &d) {
   L.moe_out = take(b * P * 2);
   L.u = take(b * H * 2);
   L.partial = take((size_t)kMaxSplitK * b * wide * 4);
-  L.counters = take(8 * (wide / 16) * 4);
+  L.logit_part = take((size_t)router_slices(d.rows, d.hidden) * b * E * 8);
+  L.pool_part = take((size_t)kMaxSplitK * b * P * 4);
+  L.unpool_part = take((size_t)kMaxSplitK * b * H * 4);
   L.total = o;
   return L;
 }
@@ -135,7 +145,7 @@ int run_pool(const mb_dims &d, const uint16_t *x, const mb_weights *w, uint16_t 
              hipStream_t s) {
   const Layout L = layout_of(d);
   MB_HIP(launch_gemm_bf16(x, w->pool_w, h, d.rows, d.pooled, d.hidden, at<float>(ws, L.partial),
-                          at<uint32_t>(ws, L.counters), s));
+                          nullptr, s));
   if (w->pre_norm_w) MB_HIP(launch_rownorm_bf16(h, w->pre_norm_w, d.rows, d.pooled, d.norm_eps, s));
   return MB_OK;
 }
@@ -157,8 +167,124 @@ int run_unpool_boundary(const mb_dims &d, const uint16_t *moe_out, const mb_weig
                         float *stream, uint16_t *x_next, uint16_t *u, void *ws, hipStream_t s) {
   const Layout L = layout_of(d);
   MB_HIP(launch_gemm_bf16(moe_out, w->unpool_w, u, d.rows, d.hidden, d.pooled,
-                          at<float>(ws, L.partial), at<uint32_t>(ws, L.counters), s));
+                          at<float>(ws, L.partial), nullptr, s));
   MB_HIP(launch_boundary(d, u, stream, w->gate, w->ffn_norm_w, w->next_norm_w, x_next, s));
+  return MB_OK;
+}
+
+// ---- the persistent block kernel (block.hip) --------------------------------
+
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
+// Fill the sizes, scalars and workspace pointers every phase set shares.
+BlockParams base_params(const mb_dims &d, const mb_weights *w, void *ws) {
+  const Layout L = layout_of(d);
+  BlockParams p{};
+  p.b = d.rows;
+  p.H = d.hidden;
+  p.P = d.pooled;
+  p.I = d.inter;
+  p.E = d.experts;
+  p.k = d.top_k;
+  p.scoring = d.scoring;
+  p.mult = d.router_multiplier;
+  p.div_eps = d.division_eps;
+  p.route_scale = d.route_scale;
+  p.norm_eps = d.norm_eps;
+  if (w) {
+    p.router_w = w->router_w;
+    p.bias = w->expert_bias;
+    p.pool_w = w->pool_w;
+    p.pre_norm_w = w->pre_norm_w;
+    p.w13 = w->w13;
+    p.w13s = w->w13_scale;
+    p.w2 = w->w2;
+    p.w2s = w->w2_scale;
+    p.post_norm_w = w->post_norm_w;
+    p.unpool_w = w->unpool_w;
+    p.ffn_norm_w = w->ffn_norm_w;
+    p.gate = w->gate;
+    p.next_norm_w = w->next_norm_w;
+  }
+  p.logit_part = at<double>(ws, L.logit_part);
+  p.pool_part = at<float>(ws, L.pool_part);
+  p.unpool_part = at<float>(ws, L.unpool_part);
+  p.y = at<float>(ws, L.y);
+  p.ssq = at<float>(ws, L.ssq);
+  p.act = at<uint16_t>(ws, L.act);
+  p.pool_cnt = at<unsigned>(ws, L.pool_cnt);
+  p.unpool_cnt = at<unsigned>(ws, L.unpool_cnt);
+  p.sync = at<unsigned>(ws, L.sync);
+  p.h = at<uint16_t>(ws, L.h);
+  p.moe_out = at<uint16_t>(ws, L.moe_out);
+  p.u = at<uint16_t>(ws, L.u);
+  p.ids = at<int32_t>(ws, L.ids);
+  p.wts = at<float>(ws, L.wts);
+  p.count = at<int32_t>(ws, L.count);
+  p.offset = at<int32_t>(ws, L.offset);
+  p.route_list = at<int32_t>(ws, L.route_list);
+  p.active = at<int32_t>(ws, L.active);
+  p.n_active = at<int32_t>(ws, L.n_active);
+  return p;
+}
+
+int split_for(int ntiles, int nchunks, int grid) {
+  int ks = ntiles > 0 ? grid / ntiles : 1;
+  if (ks > kMaxSplitK) ks = kMaxSplitK;
+  while (ks > 1 && nchunks / ks < 16) --ks;
+  return ks < 1 ? 1 : ks;
+}
+
+// Which steps one launch of the persistent kernel runs.
+struct Steps {
+  bool router = false;       // router logits (else given, or not needed)
+  bool pool = false;         // pooler (and the pre-expert norm when weighted)
+  bool experts = false;      // up, down, finalize
+  bool unpool = false;       // unpooler and boundary
+  bool routing_out = false;  // workgroup 0 writes the routing outputs
+  bool route_given = false;  // routing arrays come from the caller
+};
+
+// Launch the persistent kernel for `st`.  *used = false (and nothing
+// launched) when the sizes do not fit it; the caller then runs the per-step
+// kernels instead.
+int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
+  *used = false;
+  if (p.E > kBlockMaxExperts) return MB_OK;
+  const size_t route_bytes = route_lds_bytes(p.b, p.k, p.E);
+  const size_t lds = route_bytes + kBlockScratchBytes;
+  if (lds > 64 * 1024) return MB_OK;
+  const int occ = block_max_groups_per_cu(lds);
+  const int cus = device_cus();
+  if (occ < 1 || cus < 1) return MB_OK;
+  const int grid = cus * (occ < 2 ? occ : 2);
+  p.rslice = router_slice(p.b, p.H);
+  p.rslices = router_slices(p.b, p.H);
+  p.lds_route_bytes = (int)route_bytes;
+  p.pool_ks = split_for(p.P / 16, p.H / 32, grid);
+  p.unpool_ks = split_for(p.H / 16, p.P / 32, grid);
+  p.n_pool_tiles = p.P / 16;
+  p.needs_routing = (st.experts || st.routing_out) ? 1 : 0;
+  p.routing_out = st.routing_out ? 1 : 0;
+  p.route_given = st.route_given ? 1 : 0;
+  p.n_router = st.router ? p.E * p.rslices : 0;
+  const bool few_rows = (long)p.b * p.E <= 4096;
+  p.n_route = (p.needs_routing && !st.route_given && !few_rows) ? (p.b + 3) / 4 : 0;
+  p.n_pool = st.pool ? (p.P / 16) * p.pool_ks : 0;
+  p.n_prenorm = (st.pool && p.pre_norm_w) ? p.b : 0;
+  p.h_producers = st.pool ? (p.pre_norm_w ? p.b : p.P / 16) : 0;
+  p.has_up = st.experts ? 1 : 0;
+  p.n_fin = st.experts ? p.b * ((p.P + kFinChunk - 1) / kFinChunk) : 0;
+  p.n_unpool = st.unpool ? (p.H / 16) * p.unpool_ks : 0;
+  p.n_unpool_tiles = st.unpool ? p.H / 16 : 0;
+  p.n_boundary = st.unpool ? p.b : 0;
+  MB_HIP(launch_block(p, grid, lds, s));
+  *used = true;
   return MB_OK;
 }
 
@@ -185,6 +311,23 @@ int mb_route(const mb_dims *dims, const uint16_t *x, const mb_weights *w, float 
   MB_TRY(need({topk_ids, topk_w, count, offset, route_list, active, n_active}));
   if (flags) MB_TRY(need({logits}));
   MB_TRY(check_ws(dims, workspace, workspace_bytes));
+  BlockParams p = base_params(*dims, w, workspace);
+  Steps st;
+  st.router = !(flags & MB_LOGITS_IN);
+  st.routing_out = true;
+  p.x = x;
+  p.logits_in = (flags & MB_LOGITS_IN) ? 1 : 0;
+  p.logits = flags ? logits : nullptr;
+  p.ids = topk_ids;
+  p.wts = topk_w;
+  p.count = count;
+  p.offset = offset;
+  p.route_list = route_list;
+  p.active = active;
+  p.n_active = n_active;
+  bool used = false;
+  MB_TRY(run_fused(p, st, (hipStream_t)stream, &used));
+  if (used) return MB_OK;
   float *lg = flags ? logits : at<float>(workspace, layout_of(*dims).logits);
   return run_route(*dims, x, w, lg, flags, topk_ids, topk_w, count, offset, route_list, active,
                    n_active, (hipStream_t)stream);
@@ -196,6 +339,14 @@ int mb_pool(const mb_dims *dims, const uint16_t *x, const mb_weights *w, uint16_
   MB_TRY(check_weights_pool(w));
   MB_TRY(need({x, h}));
   MB_TRY(check_ws(dims, workspace, workspace_bytes));
+  BlockParams p = base_params(*dims, w, workspace);
+  Steps st;
+  st.pool = true;
+  p.x = x;
+  p.h = h;
+  bool used = false;
+  MB_TRY(run_fused(p, st, (hipStream_t)stream, &used));
+  if (used) return MB_OK;
   return run_pool(*dims, x, w, h, workspace, (hipStream_t)stream);
 }
 
@@ -208,6 +359,22 @@ int mb_experts(const mb_dims *dims, const uint16_t *h, const int32_t *topk_ids,
   MB_TRY(check_weights_experts(w));
   MB_TRY(need({h, topk_ids, topk_w, count, offset, route_list, active, n_active, moe_out}));
   MB_TRY(check_ws(dims, workspace, workspace_bytes));
+  BlockParams p = base_params(*dims, w, workspace);
+  Steps st;
+  st.experts = true;
+  st.route_given = true;
+  p.h = const_cast<uint16_t *>(h);
+  p.ids = const_cast<int32_t *>(topk_ids);
+  p.wts = const_cast<float *>(topk_w);
+  p.count = const_cast<int32_t *>(count);
+  p.offset = const_cast<int32_t *>(offset);
+  p.route_list = const_cast<int32_t *>(route_list);
+  p.active = const_cast<int32_t *>(active);
+  p.n_active = const_cast<int32_t *>(n_active);
+  p.moe_out = moe_out;
+  bool used = false;
+  MB_TRY(run_fused(p, st, (hipStream_t)stream, &used));
+  if (used) return MB_OK;
   return run_experts(*dims, h, topk_w, offset, route_list, active, n_active, w, moe_out, workspace,
                      (hipStream_t)stream);
 }
@@ -221,6 +388,16 @@ int mb_unpool_boundary(const mb_dims *dims, const uint16_t *moe_out, const mb_we
   MB_TRY(maybe({u_out}));
   MB_TRY(check_ws(dims, workspace, workspace_bytes));
   uint16_t *u = u_out ? u_out : at<uint16_t>(workspace, layout_of(*dims).u);
+  BlockParams p = base_params(*dims, w, workspace);
+  Steps st;
+  st.unpool = true;
+  p.moe_out = const_cast<uint16_t *>(moe_out);
+  p.u = u;
+  p.stream = stream;
+  p.x_next = x_next;
+  bool used = false;
+  MB_TRY(run_fused(p, st, (hipStream_t)stream_handle, &used));
+  if (used) return MB_OK;
   return run_unpool_boundary(*dims, moe_out, w, stream, x_next, u, workspace,
                              (hipStream_t)stream_handle);
 }
@@ -238,7 +415,7 @@ int mb_moe_block(const mb_dims *dims, const uint16_t *x, const mb_weights *w, fl
   if (taps) {
     tp = *taps;
     MB_TRY(maybe({tp.logits, tp.topk_ids, tp.topk_w, tp.count, tp.offset, tp.route_list,
-                  tp.active, tp.n_active, tp.h, tp.moe_out, tp.u}));
+                  tp.active, tp.n_active, tp.h, tp.moe_out, tp.u, tp.timeline}));
   }
   MB_TRY(check_ws(dims, workspace, workspace_bytes));
   const mb_dims &d = *dims;
@@ -256,6 +433,29 @@ int mb_moe_block(const mb_dims *dims, const uint16_t *x, const mb_weights *w, fl
   uint16_t *h = tp.h ? tp.h : at<uint16_t>(ws, L.h);
   uint16_t *moe_out = tp.moe_out ? tp.moe_out : at<uint16_t>(ws, L.moe_out);
   uint16_t *u = tp.u ? tp.u : at<uint16_t>(ws, L.u);
+  BlockParams p = base_params(d, w, ws);
+  Steps st;
+  st.router = st.pool = st.experts = st.unpool = true;
+  st.routing_out = tp.topk_ids || tp.topk_w || tp.count || tp.offset || tp.route_list || tp.active ||
+                   tp.n_active || tp.logits;
+  p.x = x;
+  p.logits = tp.logits;
+  p.ids = ids;
+  p.wts = wts;
+  p.count = count;
+  p.offset = offset;
+  p.route_list = route_list;
+  p.active = active;
+  p.n_active = n_active;
+  p.h = h;
+  p.moe_out = moe_out;
+  p.u = u;
+  p.stream = stream;
+  p.x_next = x_next;
+  p.timeline = tp.timeline;
+  bool used = false;
+  MB_TRY(run_fused(p, st, s, &used));
+  if (used) return MB_OK;
   MB_TRY(run_route(d, x, w, logits, 0, ids, wts, count, offset, route_list, active, n_active, s));
   MB_TRY(run_pool(d, x, w, h, ws, s));
   MB_TRY(run_experts(d, h, wts, offset, route_list, active, n_active, w, moe_out, ws, s));

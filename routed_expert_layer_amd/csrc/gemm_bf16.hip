@@ -11,9 +11,9 @@
 // in the A operand, activations in the B operand).  Lane l loads 16 bytes of
 // weight row (l % 16) at element 8*(l/16) of the chunk, so a wave load covers
 // 16 rows x 64 contiguous bytes.  When the contraction is split over several
-// workgroups, each writes fp32 partial sums and the last one to finish a tile
-// (a device-scope counter) adds them in split order and writes bf16: no
-// second launch, and a result independent of completion order.
+// workgroups, each writes fp32 partial sums and a second small kernel adds
+// them in split order and writes bf16, so the result does not depend on
+// completion order (and no workgroup pays for a device-wide cache flush).
 
 #include "mb_device.h"
 #include "mb_internal.h"
@@ -27,8 +27,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t *__restri
                                                         uint16_t *__restrict__ out, int rows,
                                                         int n_out, int kdim, int ks_count,
                                                         int chunks_per_wg,
-                                                        float *__restrict__ partial,
-                                                        uint32_t *__restrict__ counters) {
+                                                        float *__restrict__ partial) {
   const int lane = threadIdx.x % MB_WAVE, wave = threadIdx.x / MB_WAVE;
   const int g = lane >> 4, r16 = lane & 15;
   const int ntile = blockIdx.x, ks = blockIdx.y, rb = blockIdx.z;
@@ -76,7 +75,6 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t *__restri
   }
 
   __shared__ f32x4_t red[4][MG][MB_WAVE];
-  __shared__ int s_last;
 #pragma unroll
   for (int mg = 0; mg < MG; ++mg) red[wave][mg][lane] = acc[mg];
   __syncthreads();
@@ -93,35 +91,34 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t *__restri
       }
     }
   }
-  if (ks_count == 1) return;
+}
 
-  // Last finisher of this (feature tile, row block) adds the partials.
-  __threadfence();
-  __syncthreads();
-  const int tile_id = rb * gridDim.x + ntile;
-  if (threadIdx.x == 0) s_last = (atomicAdd(&counters[tile_id], 1u) == (uint32_t)(ks_count - 1));
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const int nrows = min(16 * MG, rows - row_base);
-  for (int idx = threadIdx.x; idx < nrows * 4; idx += blockDim.x) {
-    const int t = row_base + idx / 4;
-    const int n0 = ntile * 16 + 4 * (idx % 4);
-    f32x4_t s = *reinterpret_cast<const f32x4_t *>(partial + (size_t)t * n_out + n0);
+// out[t, n] = bf16(sum over splits q of partial[q, t, n]), in split order.
+__global__ __launch_bounds__(256) void splitk_sum_bf16_kernel(const float *__restrict__ partial,
+                                                              uint16_t *__restrict__ out, int rows,
+                                                              int n_out, int ks_count) {
+  const size_t n4 = (size_t)rows * n_out / 4;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (size_t)gridDim.x * blockDim.x) {
+    f32x4_t s = reinterpret_cast<const f32x4_t *>(partial)[i];
     for (int q = 1; q < ks_count; ++q)
-      s += *reinterpret_cast<const f32x4_t *>(partial + ((size_t)q * rows + t) * n_out + n0);
+      s += reinterpret_cast<const f32x4_t *>(partial + (size_t)q * rows * n_out)[i];
     u32x2_t pk = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
-    *reinterpret_cast<u32x2_t *>(out + (size_t)t * n_out + n0) = pk;
+    reinterpret_cast<u32x2_t *>(out)[i] = pk;
   }
-  if (threadIdx.x == 0) counters[tile_id] = 0u;
 }
 
 template <int MG, int UNR>
 hipError_t launch_mg(dim3 grid, hipStream_t s, const uint16_t *a, const uint16_t *w,
-                     uint16_t *out, int rows, int n_out, int kdim, int ks, int cpw, float *partial,
-                     uint32_t *counters) {
+                     uint16_t *out, int rows, int n_out, int kdim, int ks, int cpw, float *partial) {
   hipLaunchKernelGGL((gemm_bf16_kernel<MG, UNR>), grid, dim3(256), 0, s, a, w, out, rows, n_out,
-                     kdim, ks, cpw, partial, counters);
+                     kdim, ks, cpw, partial);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  if (ks > 1) {
+    const int n4 = rows * n_out / 4;
+    hipLaunchKernelGGL(splitk_sum_bf16_kernel, dim3((n4 + 255) / 256 < 1024 ? (n4 + 255) / 256 : 1024),
+                       dim3(256), 0, s, partial, out, rows, n_out, ks);
+  }
   return hipGetLastError();
 }
 
@@ -163,10 +160,10 @@ hipError_t launch_gemm_bf16(const uint16_t *a, const uint16_t *w, uint16_t *out,
   ks = (nchunks + cpw - 1) / cpw;
   dim3 grid(ntiles, ks, rblocks);
   switch (mg) {
-    case 1: return launch_mg<1, 8>(grid, s, a, w, out, rows, n_out, kdim, ks, cpw, partial, counters);
-    case 2: return launch_mg<2, 8>(grid, s, a, w, out, rows, n_out, kdim, ks, cpw, partial, counters);
-    case 4: return launch_mg<4, 4>(grid, s, a, w, out, rows, n_out, kdim, ks, cpw, partial, counters);
-    default: return launch_mg<8, 2>(grid, s, a, w, out, rows, n_out, kdim, ks, cpw, partial, counters);
+    case 1: return launch_mg<1, 8>(grid, s, a, w, out, rows, n_out, kdim, ks, cpw, partial);
+    case 2: return launch_mg<2, 8>(grid, s, a, w, out, rows, n_out, kdim, ks, cpw, partial);
+    case 4: return launch_mg<4, 4>(grid, s, a, w, out, rows, n_out, kdim, ks, cpw, partial);
+    default: return launch_mg<8, 2>(grid, s, a, w, out, rows, n_out, kdim, ks, cpw, partial);
   }
 }
 

@@ -17,8 +17,9 @@ constexpr int kMaxSplitK = 8;          // split-K factor of the bf16 projections
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct Layout {
-  size_t logits, ids, wts, count, offset, route_list, active, n_active;
-  size_t h, act, y, ssq, moe_out, u, partial, counters, total;
+  size_t sync, logits, ids, wts, count, offset, route_list, active, n_active;
+  size_t h, act, y, ssq, moe_out, u, partial;
+  size_t logit_part, pool_part, unpool_part, pool_cnt, unpool_cnt, total;
 };
 
 Layout layout_of(const mb_dims &d);

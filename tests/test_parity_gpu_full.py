@@ -22,7 +22,7 @@ def test_c1_decode_step():
     say("[gpu] c1 b=16 block")
     got = GpuBlock(blk).run_block()
     ref = oracle.block(blk)
-    assert_block(got, ref, "c1")
+    assert_block(got, ref, "c1", blk)
 
 
 @pytest.mark.parametrize("skew", ["calibrated", "literal", "uniform"])
@@ -31,7 +31,7 @@ def test_c2_softmax_block(skew):
     say(f"[gpu] c2 b=64 skew={skew}")
     got = GpuBlock(blk).run_block()
     ref = oracle.block(blk)
-    assert_block(got, ref, f"c2 {skew}")
+    assert_block(got, ref, f"c2 {skew}", blk)
     hot = synth.hot_experts(2, 128)
     share = np.isin(ref.routing.ids, hot).mean()
     say(f"[gpu] c2 {skew}: hot-expert share of routes {share:.3f}, active experts {ref.routing.n_active}")
@@ -56,7 +56,7 @@ def test_c3_bucket_sweep(c3_gpu, skew):
         g.x, g.stream0, g.blk = base_x, base_s, full
         g.set_rows(b)
         got = g.run_block()
-        assert_block(got, slice_result(ref, b, 128), f"c3 {skew} b={b}")
+        assert_block(got, slice_result(ref, b, 128), f"c3 {skew} b={b}", g.blk)
     g.x, g.stream0, g.blk = base_x, base_s, full
 
 
@@ -71,7 +71,7 @@ def test_c4_stack_teacher_forced():
         g = GpuBlock(blk)
         got = g.run_block()
         ref = oracle.block(blk)
-        assert_block(got, ref, f"c4 layer {layer}")
+        assert_block(got, ref, f"c4 layer {layer}", blk)
         x, s = got["x_next"], got["stream"]
         del g
         torch.cuda.empty_cache()

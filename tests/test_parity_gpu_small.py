@@ -32,7 +32,7 @@ def run_and_check(blk, name):
     g = GpuBlock(blk)
     got = g.run_block()
     ref = oracle.block(blk)
-    return assert_block(got, ref, name)
+    return assert_block(got, ref, name, blk)
 
 
 def test_c0_block():
