@@ -43,7 +43,6 @@ Layout layout_of(const mb_dims &d) {
   L.moe_out = take(b * P * 2);
   L.u = take(b * H * 2);
   L.partial = take((size_t)kMaxSplitK * b * wide * 4);
-  L.logit_part = take((size_t)router_slices(d.rows, d.hidden) * b * E * 8);
   L.pool_part = take((size_t)kMaxSplitK * b * P * 4);
   L.unpool_part = take((size_t)kMaxSplitK * b * H * 4);
   L.total = o;
@@ -211,7 +210,7 @@ BlockParams base_params(const mb_dims &d, const mb_weights *w, void *ws) {
     p.gate = w->gate;
     p.next_norm_w = w->next_norm_w;
   }
-  p.logit_part = at<double>(ws, L.logit_part);
+  p.logits_f = at<float>(ws, L.logits);
   p.pool_part = at<float>(ws, L.pool_part);
   p.unpool_part = at<float>(ws, L.unpool_part);
   p.y = at<float>(ws, L.y);
@@ -262,9 +261,8 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   const int occ = block_max_groups_per_cu(lds);
   const int cus = device_cus();
   if (occ < 1 || cus < 1) return MB_OK;
-  const int grid = cus * (occ < 2 ? occ : 2);
-  p.rslice = router_slice(p.b, p.H);
-  p.rslices = router_slices(p.b, p.H);
+  int grid = cus * (occ < kBlockGroupsPerCu ? occ : kBlockGroupsPerCu);
+  if (grid > kMaxGrid) grid = kMaxGrid;
   p.lds_route_bytes = (int)route_bytes;
   p.pool_ks = split_for(p.P / 16, p.H / 32, grid);
   p.unpool_ks = split_for(p.H / 16, p.P / 32, grid);
@@ -272,7 +270,8 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   p.needs_routing = (st.experts || st.routing_out) ? 1 : 0;
   p.routing_out = st.routing_out ? 1 : 0;
   p.route_given = st.route_given ? 1 : 0;
-  p.n_router = st.router ? p.E * p.rslices : 0;
+  p.n_router = st.router ? p.E * ((p.b + kRouterRowBlock - 1) / kRouterRowBlock) : 0;
+  p.n_logit_producers = p.n_router;
   const bool few_rows = (long)p.b * p.E <= 4096;
   p.n_route = (p.needs_routing && !st.route_given && !few_rows) ? (p.b + 3) / 4 : 0;
   p.n_pool = st.pool ? (p.P / 16) * p.pool_ks : 0;

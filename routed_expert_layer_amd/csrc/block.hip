@@ -1,53 +1,66 @@
-// The routed-MoE block as one persistent launch driven by a task list.
+// The routed-MoE block as one persistent launch.
 //
 // The block's steps ([providers] MoEProvider: router, routing, pooler, routed
 // experts, tail, unpooler; BoundaryProvider: the boundary; [mono.decoder]
-// _K3Bucket runs the whole layer as one launch at small row counts) become
-// one ordered list of tasks:
+// _K3Bucket runs the whole layer as one launch at small row counts) run as
+// four lists of work, in this order, in every workgroup:
 //
-//   router     (expert, hidden slice)   fp64 partial logits         [Wr]
-//   route      (4 rows)                 top-k and weights (many rows)
-//   pool       (16 features, K split)   h = bf16(x Wp^T)            [Wp]
-//   prenorm    (row)                    optional RMSNorm of h
-//   up         (expert, 16 columns)     act = bf16(silu(g) * u)     [w13]
-//   down       (expert, 32 features)    y, per-tile sums of squares [w2]
-//   finalize   (row, 512 features)      moe_out = bf16(sum_j w_j yn_j)
-//   unpool     (16 features, K split)   u = bf16(moe_out Wu^T)      [Wu]
-//   boundary   (row)                    stream, x_next
+//   1. workgroup tasks before routing
+//        router   (expert, hidden slice)  fp64 partial logits; the last
+//                                          slice of an expert to finish
+//                                          writes its fp32 logits          [Wr]
+//        route    (4 rows)                 top-k and weights (many rows)
+//        pool     (16 features, K split)   h = bf16(x Wp^T)                [Wp]
+//        prenorm  (row)                    optional RMSNorm of h
+//   2. the routing state, rebuilt in the workgroup's LDS
+//   3. wave units (each wave on its own: no workgroup barrier)
+//        up       (expert, 16 act columns) act = bf16(silu(g) * u)        [w13]
+//        down     (expert, 32 features)    y, per-tile sums of squares    [w2]
+//   4. workgroup tasks after the experts
+//        finalize (row, 512 features)      moe_out = bf16(sum_j w_j yn_j)
+//        unpool   (16 features, K split)   u = bf16(moe_out Wu^T)          [Wu]
+//        boundary (row)                    stream, x_next
 //
-// Workgroup w runs tasks w, w + G, w + 2G, ... in order (G workgroups, two
-// per CU, all resident: a cooperative launch).  A task waits only for the
-// tasks whose output it reads, through per-launch counters: up waits for the
-// pooler, down for the up tasks of its own expert, finalize for the down
-// tasks of its row's experts, unpool for all finalize tasks, boundary for all
-// unpool tiles.  Every dependency points to a lower task index, so the lowest
-// unfinished task can always run and the launch always completes; every wait
-// is also bounded (mb_sync.h).  Imbalance in one step is absorbed by the next
-// step's tasks instead of stalling every workgroup at a barrier.
-//
-// Routing state (ids, weights, route grouping) is rebuilt in each
-// workgroup's LDS from the logits (few rows) or from the route tasks' ids.
+// Workgroup w takes workgroup tasks w, w + G, ... of lists 1 and 4; wave v
+// (global index) takes units v, v + 4G, ... of list 3.  A task or unit waits
+// only for the work whose output it reads: routing for the logits (or the
+// route tasks), up for the pooler (or pre-norm), down for the up units of its
+// expert, finalize for the down units of its row's experts, unpool for the
+// finalize tasks, boundary for the unpool tiles.  Waits that every workgroup
+// makes are events (a flag per workgroup, set by the last arrival); the
+// others poll counters.  Every dependency points to earlier work in this
+// order and the grid is what the device holds at once, so the earliest
+// unfinished work can always run and the launch completes; every wait is also
+// bounded.
 //
 // Data one workgroup hands to another goes through coherent (sc1) buffer
-// accesses; weights are streamed with non-temporal loads.  Arithmetic:
-// fp64-accumulated router logits rounded once to fp32, the fp32 routing
-// recipe, bf16 MFMA with exact MXFP4 -> bf16 weight conversion and fp32
-// accumulation, fixed-order reductions (results do not depend on timing).
+// accesses; weights are streamed with non-temporal loads, each wave keeping
+// several chunks of its weight rows in flight.  Arithmetic: fp64-accumulated
+// router logits rounded once to fp32, the fp32 routing recipe, bf16 MFMA with
+// exact MXFP4 -> bf16 weight conversion and fp32 accumulation, fixed-order
+// reductions (results do not depend on timing).
 
 #include "mb_block.h"
 #include "mb_device.h"
 #include "mb_sync.h"
-
-// Each task is its own (non-inlined) function so that the register
-// allocation of one step's inner loop is not constrained by the others'.
 
 namespace mb {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / MB_WAVE;
+static_assert(kWaves == kBlockWaves, "routing LDS is laid out per wave");
 constexpr int kPoolMG = 4;      // 16-row groups per projection pass
-constexpr int kRouterRows = 8;  // rows per pass of a router task
+constexpr int kRing = 4;        // 128-element weight chunks a wave keeps in flight
+static_assert(kRing == 4, "one 16-byte scale load covers four chunks");
+constexpr int kProjBatch = 8;   // 32-element projection chunks a wave requests at once
+constexpr int kRouterBatch = 8;  // router loads a thread requests at once
+constexpr int kRankBatch = 8;    // order keys a lane reads at once
+constexpr int kBoundBatch = 4;   // boundary elements groups a thread requests at once
+
+// A value the wave holds in every lane (LDS reads, the wave index), moved to
+// a scalar register so that addresses and resources built from it are too.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 struct Lane {
   int lane, wave, g, r16;
@@ -59,40 +72,60 @@ struct Lane {
 // ---------------------------------------------------------------- dependencies
 
 struct Deps {
-  unsigned *words;  // [0] epoch, [1] abort
-  unsigned *set;    // this launch's counters
+  unsigned *s;  // the launch state (layout in mb_block.h)
   int E;
 
-  __device__ unsigned *ctr(int slot) const { return set + slot * kCtrStride; }
-  __device__ unsigned *up(int e) const { return ctr(kCtrUp + e); }
-  __device__ unsigned *down(int e) const { return ctr(kCtrUp + E + e); }
+  __device__ unsigned *line(size_t i) const { return s + i * kLine; }
+  __device__ unsigned *abort_word() const { return s + 1; }
+  __device__ unsigned *ctr(int i) const { return line(sync_line_ctr(i)); }
+  __device__ unsigned *up(int e) const { return line(sync_line_up(E, e)); }
+  __device__ unsigned *down(int e) const { return line(sync_line_down(E, e)); }
+  __device__ unsigned *fin(int g) const { return line(sync_line_fin(E, g)); }
+  __device__ unsigned *flag(int ev, int wg) const { return line(sync_line_flag(E, ev, wg)); }
 };
 
-// This launch uses counter set (epoch & 1); workgroup 0 clears the other set
-// for the next launch (the last workgroup to finish bumps the epoch).
-__device__ __forceinline__ Deps deps_init(const BlockParams &p) {
-  Deps d;
-  d.words = p.sync;
-  d.E = p.E;
-  const unsigned epoch = __hip_atomic_load(&p.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int n = kCtrUp + 2 * p.E;
-  d.set = p.sync + kSyncHeader + (epoch & 1u) * n * kCtrStride;
-  unsigned *other = p.sync + kSyncHeader + ((epoch & 1u) ^ 1u) * n * kCtrStride;
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < n; i += kThreads)
-      __hip_atomic_store(&other[i * kCtrStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return d;
+__device__ __forceinline__ unsigned atomic_inc(unsigned *c) {
+  return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// All coherent stores of this workgroup complete, then one increment.
+__device__ __forceinline__ void store_co(unsigned *w, unsigned v) {
+  __hip_atomic_store(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroup: every wave's coherent stores complete, then one increment.
 __device__ __forceinline__ void signal(unsigned *c) {
   wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) atomic_inc(c);
 }
 
-// Wave 0: each lane polls its own counter until every lane's has reached
-// `target`.  Bounded: on timeout the abort word is raised, and any wait that
+// One wave: its coherent stores complete, then one increment.
+__device__ __forceinline__ void wave_signal(unsigned *c) {
+  wait_stores();
+  if (threadIdx.x % MB_WAVE == 0) atomic_inc(c);
+}
+
+// Workgroup: after its coherent stores, add one to counter c; true in the
+// workgroup whose increment made it `of` (the last of `of` arrivals).
+__device__ __forceinline__ bool last_arrival(unsigned *c, unsigned of, int *flag) {
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) *flag = atomic_inc(c) == of - 1u;
+  __syncthreads();
+  const bool last = *flag != 0;
+  __syncthreads();
+  return last;
+}
+
+// Workgroup: one arrival at event ev, which expects `of`; the last arrival
+// sets every workgroup's flag.
+__device__ __forceinline__ void arrive(const Deps &d, int ev, unsigned of, int *flag) {
+  if (!last_arrival(d.ctr(ev), of, flag)) return;
+  for (int g = threadIdx.x; g < (int)gridDim.x; g += kThreads) store_co(d.flag(ev, g), 1u);
+}
+
+// One wave polls, each lane its own word, until every lane's has reached
+// `target`.  Bounded: on timeout the abort word is raised, and a wait that
 // sees it returns at once, so the launch drains.
 __device__ __forceinline__ void poll_ge(const Deps &d, const unsigned *mine, unsigned target) {
   const int lane = threadIdx.x % MB_WAVE;
@@ -101,9 +134,9 @@ __device__ __forceinline__ void poll_ge(const Deps &d, const unsigned *mine, uns
     const unsigned have = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (__all((int)(have >= target))) return;
     if ((++spins & 255u) == 0) {
-      if (__hip_atomic_load(&d.words[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
+      if (__hip_atomic_load(d.abort_word(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
       if (spins > kSpinLimit) {
-        if (lane == 0) __hip_atomic_store(&d.words[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) store_co(d.abort_word(), 1u);
         return;
       }
     }
@@ -111,88 +144,145 @@ __device__ __forceinline__ void poll_ge(const Deps &d, const unsigned *mine, uns
   }
 }
 
+// Workgroup wait on one counter.
 __device__ __forceinline__ void wait_ge(const Deps &d, const unsigned *c, unsigned target) {
   if (target == 0) return;
   if (threadIdx.x < MB_WAVE) poll_ge(d, c, target);
   __syncthreads();
 }
 
+// One wave / the workgroup waits for event ev (skipped when it has no
+// arrivals to wait for).
+__device__ __forceinline__ void wave_wait_event(const Deps &d, int ev, int arrivals) {
+  if (arrivals > 0) poll_ge(d, d.flag(ev, blockIdx.x), 1u);
+}
+__device__ __forceinline__ void wait_event(const Deps &d, int ev, int arrivals) {
+  if (arrivals == 0) return;
+  if (threadIdx.x < MB_WAVE) poll_ge(d, d.flag(ev, blockIdx.x), 1u);
+  __syncthreads();
+}
+
+// The end of a workgroup: count it finished (per group of kFinGroup, then
+// groups); the last workgroup sets the launch state back to zero for the
+// next launch (every other workgroup has finished all its waits).
+__device__ __forceinline__ void finish(const Deps &d, int *flag) {
+  const int G = gridDim.x, ngroups = (G + kFinGroup - 1) / kFinGroup;
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int grp = blockIdx.x / kFinGroup;
+    const unsigned gsize = (unsigned)min(kFinGroup, G - grp * kFinGroup);
+    bool last = false;
+    if (atomic_inc(d.fin(grp)) == gsize - 1u) last = atomic_inc(d.fin(kMaxGrid / kFinGroup)) == (unsigned)ngroups - 1u;
+    *flag = last;
+  }
+  __syncthreads();
+  if (!*flag) return;
+  for (int i = threadIdx.x; i < kNumCtr; i += kThreads) store_co(d.ctr(i), 0u);
+  for (int e = threadIdx.x; e < d.E; e += kThreads) {
+    store_co(d.up(e), 0u);
+    store_co(d.down(e), 0u);
+  }
+  for (int g = threadIdx.x; g < ngroups; g += kThreads) store_co(d.fin(g), 0u);
+  if (threadIdx.x == 0) store_co(d.fin(kMaxGrid / kFinGroup), 0u);
+  for (int i = threadIdx.x; i < kNumEvents * G; i += kThreads) store_co(d.flag(i / G, i % G), 0u);
+}
+
+// Tracing: workgroup thread 0 stamps the 100 MHz real-time counter at the
+// start (slot 0), when it enters its first task of each step (router 1,
+// route 2, pool 3, prenorm 4, finalize 8, unpool 9, boundary 10), when its
+// routing state is ready (5), when its waves start (6) and finish (11) their
+// expert units, and at the end (15); inside the steps: router task done (7),
+// logits event seen (12), logits staged (13), rows routed (14).
+__device__ __forceinline__ void stamp(const BlockParams &p, int slot) {
+  if (p.timeline && threadIdx.x == 0) {
+    asm volatile("" ::: "memory");
+    p.timeline[(size_t)blockIdx.x * kTimelineSlots + slot] = (int64_t)wall_clock64();
+    asm volatile("" ::: "memory");
+  }
+}
+
 // ---------------------------------------------------------------- router
 
-// Partial logits of expert e over hidden slice s for every row, in fp64
-// (bf16 x fp32 products are exact in fp64).  Each thread takes 4 consecutive
-// elements per 1024-element pass of the slice for up to 16 rows at a time;
-// the row sums are then reduced over the workgroup in a fixed order.
-__device__ __noinline__ void router_task(const BlockParams &p, const Deps &d, int task,
+// Logits of expert e for a block of kRouterRowBlock rows, in fp64 (bf16 x
+// fp32 products are exact in fp64), rounded once to fp32.  Thread (row r,
+// part q) adds the products of hidden elements 4q + 64i .. +3 in order; the
+// 16 parts of a row are then added in part order through LDS (no cross-lane
+// shuffles, whose dependent chains are slow).
+__device__ __forceinline__ void router_task(const BlockParams &p, const Deps &d, int task,
                                             unsigned char *lds) {
-  const Lane L;
-  const int e = task / p.rslices, s = task % p.rslices;
-  const int h_begin = s * p.rslice, h_end = min(p.H, h_begin + p.rslice);
-  const rsrc_t part = make_rsrc(p.logit_part);
-  double *red = reinterpret_cast<double *>(lds);  // [kWaves][kRouterRows]
-  for (int t0 = 0; t0 < p.b; t0 += kRouterRows) {
-    double acc[kRouterRows];
+  const int nrb = (p.b + kRouterRowBlock - 1) / kRouterRowBlock;
+  const int e = task / nrb, t0 = (task % nrb) * kRouterRowBlock;
+  const int r = threadIdx.x / 16, q = threadIdx.x % 16;
+  const int t = t0 + r;
+  double *red = reinterpret_cast<double *>(lds);  // [kRouterRowBlock][16]
+  int *flag = reinterpret_cast<int *>(lds + kRouterRowBlock * 16 * sizeof(double));
+  // Padding elements (past H, or rows past b) load zeros and add nothing.
+  double acc = 0.0;
+  const rsrc_t rw = make_rsrc(p.router_w + (size_t)e * p.H), rx = make_rsrc(p.x);
+  const uint32_t xrow = t < p.b ? (uint32_t)t * (uint32_t)p.H * 2u : kOob;
+  for (int h0 = 4 * q; h0 < p.H; h0 += 64 * kRouterBatch) {
+    f32x4_t w[kRouterBatch];
+    u32x2_t xv[kRouterBatch];
 #pragma unroll
-    for (int r = 0; r < kRouterRows; ++r) acc[r] = 0.0;
-    for (int h = h_begin + threadIdx.x * 4; h < h_end; h += kThreads * 4) {
-      const f32x4_t w = *reinterpret_cast<const f32x4_t *>(p.router_w + (size_t)e * p.H + h);
-      u32x2_t xv[kRouterRows];
-#pragma unroll
-      for (int r = 0; r < kRouterRows; ++r)
-        xv[r] = t0 + r < p.b ? *reinterpret_cast<const u32x2_t *>(p.x + (size_t)(t0 + r) * p.H + h)
-                             : u32x2_t{0, 0};
-#pragma unroll
-      for (int r = 0; r < kRouterRows; ++r) {
-        acc[r] = fma((double)bf16_bits_to_f32(xv[r][0] & 0xFFFFu), (double)w[0], acc[r]);
-        acc[r] = fma((double)bf16_bits_to_f32(xv[r][0] >> 16), (double)w[1], acc[r]);
-        acc[r] = fma((double)bf16_bits_to_f32(xv[r][1] & 0xFFFFu), (double)w[2], acc[r]);
-        acc[r] = fma((double)bf16_bits_to_f32(xv[r][1] >> 16), (double)w[3], acc[r]);
-      }
+    for (int u = 0; u < kRouterBatch; ++u) {
+      const uint32_t h = (uint32_t)(h0 + 64 * u);
+      const bool in = h < (uint32_t)p.H;
+      w[u] = __builtin_bit_cast(f32x4_t, ld_b128(rw, in ? h * 4 : kOob));
+      xv[u] = ld_b64(rx, in ? xrow + h * 2 : kOob);
     }
 #pragma unroll
-    for (int r = 0; r < kRouterRows; ++r) {
-      const double v = wave_sum(acc[r]);
-      if (L.lane == 0) red[L.wave * kRouterRows + r] = v;
+    for (int u = 0; u < kRouterBatch; ++u) {
+      acc = fma((double)bf16_bits_to_f32(xv[u][0] & 0xFFFFu), (double)w[u][0], acc);
+      acc = fma((double)bf16_bits_to_f32(xv[u][0] >> 16), (double)w[u][1], acc);
+      acc = fma((double)bf16_bits_to_f32(xv[u][1] & 0xFFFFu), (double)w[u][2], acc);
+      acc = fma((double)bf16_bits_to_f32(xv[u][1] >> 16), (double)w[u][3], acc);
     }
-    __syncthreads();
-    const int r = threadIdx.x;
-    if (r < kRouterRows && t0 + r < p.b) {
-      double v = red[r];
-      for (int q = 1; q < kWaves; ++q) v += red[q * kRouterRows + r];
-      st_co8(part, (uint32_t)((((size_t)s * p.b + t0 + r) * p.E + e) * 8), __builtin_bit_cast(u32x2_t, v));
-    }
-    __syncthreads();
   }
-  signal(d.ctr(kCtrLogits));
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x < kRouterRowBlock && t0 + (int)threadIdx.x < p.b) {
+    double v = red[threadIdx.x * 16];
+    for (int i = 1; i < 16; ++i) v += red[threadIdx.x * 16 + i];
+    const size_t te = (size_t)(t0 + threadIdx.x) * p.E + e;
+    st_co4(make_rsrc(p.logits_f), (uint32_t)(te * 4), __float_as_uint((float)v));
+  }
+  arrive(d, kCtrLogits, (unsigned)p.n_logit_producers, flag);
 }
 
 // ---------------------------------------------------------------- routing
 
-// Candidate order of the top-k: a valid number beats a NaN, which beats an
-// unavailable slot; larger keys first; equal keys (or two NaNs) to the lower id.
-__device__ __forceinline__ bool beats(int c1, float k1, int id1, int c2, float k2, int id2) {
-  if (c1 != c2) return c1 > c2;
-  if (c1 == 2 && k1 != k2) return k1 > k2;
-  return id1 < id2;
+// fp32 logit (t, e): given by the caller, or the router's.
+__device__ __forceinline__ float logit_of(const BlockParams &p, rsrc_t rl, int t, int e) {
+  if (p.logits_in) return p.logits[(size_t)t * p.E + e];
+  return __uint_as_float(ld_co4(rl, (uint32_t)(((size_t)t * p.E + e) * 4)));
 }
 
-// fp32 logit (t, e): the fp64 slice partials added in slice order, or given.
-__device__ __forceinline__ float logit_of(const BlockParams &p, rsrc_t part, int t, int e) {
-  if (p.logits_in) return p.logits[(size_t)t * p.E + e];
-  double acc = __builtin_bit_cast(double, ld_co8(part, (uint32_t)(((size_t)t * p.E + e) * 8)));
-  for (int s = 1; s < p.rslices; ++s)
-    acc += __builtin_bit_cast(double, ld_co8(part, (uint32_t)((((size_t)s * p.b + t) * p.E + e) * 8)));
-  return (float)acc;
+// Order key of a candidate: larger is better.  Valid numbers above NaN, then
+// the larger selection key, then the lower expert id; -0 counts as +0.
+__device__ __forceinline__ unsigned long long order_key(float key, int e) {
+  const float k = key + 0.0f;
+  uint32_t u = 0;
+  if (!isnan(k)) {
+    const uint32_t bits = __float_as_uint(k);
+    u = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+  }
+  return ((unsigned long long)u << 32) | (uint32_t)~(uint32_t)e;
 }
 
 // One row's routing by one wave from its fp32 logits l[i] (expert lane + 64 i):
-// multiplier, scores, keys = score + bias, k rounds of a wave-wide arg-max,
-// then the fp32 weights in slot order.  Lane j < k gets slot j.
+// multiplier, scores, keys = score + bias; each candidate's rank is the number
+// of candidates with a larger order key (read back from LDS; the keys are
+// distinct, so ranks are a permutation), and the candidates of rank < k fill
+// slots 0..k-1.  Then the fp32 weights in slot order.  Lane j < k gets slot j.
 template <int PER>
-__device__ __forceinline__ void route_one(const BlockParams &p, const float (&l)[PER], int &out_id,
-                                          float &out_w) {
-  const int lane = threadIdx.x % MB_WAVE;
-  float g[PER], sc[PER], key[PER];
+__device__ __forceinline__ void route_one(const BlockParams &p, const RouteLds &R, const float (&l)[PER],
+                                          int &out_id, float &out_w) {
+  const int lane = threadIdx.x % MB_WAVE, wave = threadIdx.x / MB_WAVE;
+  unsigned long long *rank = R.rank + (size_t)wave * rank_span(p.E);
+  int *slot_id = R.slot_id + wave * kMaxTopK;
+  float *slot_sc = R.slot_sc + wave * kMaxTopK;
+  float g[PER], sc[PER];
   bool live[PER];
   float gmax = -INFINITY;
 #pragma unroll
@@ -217,81 +307,66 @@ __device__ __forceinline__ void route_one(const BlockParams &p, const float (&l)
 #pragma unroll
     for (int i = 0; i < PER; ++i) sc[i] = live[i] ? (float)(z[i] / zs) : 0.0f;
   }
+  // Order keys to LDS, padded with zeros (below every candidate's key) to a
+  // multiple of kRankBatch.
+  const int Ep = rank_span(p.E);
+  unsigned long long mine[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + MB_WAVE * i;
+    mine[i] = live[i] ? order_key(sc[i] + p.bias[e], e) : 0ull;
+    if (e < Ep) rank[e] = mine[i];
+  }
+  // One wave's LDS accesses complete in order: the reads below see all writes.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  int above[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) above[i] = 0;
+  for (int j0 = 0; j0 < Ep; j0 += kRankBatch) {
+    unsigned long long o[kRankBatch];
+#pragma unroll
+    for (int u = 0; u < kRankBatch; ++u) o[u] = rank[j0 + u];
+#pragma unroll
+    for (int u = 0; u < kRankBatch; ++u)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) above[i] += o[u] > mine[i] ? 1 : 0;
+  }
 #pragma unroll
   for (int i = 0; i < PER; ++i)
-    key[i] = live[i] ? sc[i] + p.bias[min(lane + MB_WAVE * i, p.E - 1)] : 0.0f;
-
-  out_id = 0;
-  float my_sc = 0.0f;
-  float chosen[kMaxTopK];
-  for (int j = 0; j < p.k; ++j) {
-    int bc = 0, bid = 0x7FFFFFFF;
-    float bk = 0.0f, bs = 0.0f;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (live[i]) {
-        const int e = lane + MB_WAVE * i;
-        const int c = isnan(key[i]) ? 1 : 2;
-        if (beats(c, key[i], e, bc, bk, bid)) {
-          bc = c;
-          bk = key[i];
-          bid = e;
-          bs = sc[i];
-        }
-      }
+    if (live[i] && above[i] < p.k) {
+      slot_id[above[i]] = lane + MB_WAVE * i;
+      slot_sc[above[i]] = sc[i];
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const int oc = __shfl_xor(bc, m, MB_WAVE);
-      const float ok = __shfl_xor(bk, m, MB_WAVE);
-      const int oid = __shfl_xor(bid, m, MB_WAVE);
-      const float os = __shfl_xor(bs, m, MB_WAVE);
-      if (beats(oc, ok, oid, bc, bk, bid)) {
-        bc = oc;
-        bk = ok;
-        bid = oid;
-        bs = os;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (live[i] && lane + MB_WAVE * i == bid) live[i] = false;
-#pragma unroll
-    for (int jj = 0; jj < kMaxTopK; ++jj)
-      if (jj == j) chosen[jj] = bs;
-    if (lane == j) {
-      out_id = bid;
-      my_sc = bs;
-    }
-  }
-  float sum = chosen[0];
-#pragma unroll
-  for (int jj = 1; jj < kMaxTopK; ++jj)
-    if (jj < p.k) sum = sum + chosen[jj];
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  float sum = slot_sc[0];
+  for (int j = 1; j < p.k; ++j) sum = sum + slot_sc[j];
+  const int js = lane < p.k ? lane : 0;
+  out_id = slot_id[js];
   const float den = sum + p.div_eps;
-  const float q = my_sc / den;
+  const float q = slot_sc[js] / den;
   out_w = q * p.route_scale;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
 // Rows t_begin..t_end-1, one per wave in turn: logits from `lg` (LDS
-// [rows][E], row t_begin first) when given, else from the partials; results
-// to LDS and, when `out`, to the outputs.
+// [rows][E], row t_begin first) when given, else from global; results to LDS
+// and, when `out`, to the outputs.
 template <int PER>
 __device__ __forceinline__ void route_rows(const BlockParams &p, const RouteLds &R, const float *lg,
                                            int t_begin, int t_end, bool out) {
   const int lane = threadIdx.x % MB_WAVE;
-  const rsrc_t part = make_rsrc(p.logit_part);
+  const rsrc_t rl = make_rsrc(p.logits_f);
   for (int t = t_begin + threadIdx.x / MB_WAVE; t < t_end; t += kWaves) {
     float l[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = lane + MB_WAVE * i;
       l[i] = 0.f;
-      if (e < p.E) l[i] = lg ? lg[(size_t)(t - t_begin) * p.E + e] : logit_of(p, part, t, e);
+      if (e < p.E) l[i] = lg ? lg[(size_t)(t - t_begin) * p.E + e] : logit_of(p, rl, t, e);
     }
     int id;
     float w;
-    route_one<PER>(p, l, id, w);
+    route_one<PER>(p, R, l, id, w);
     if (lane < p.k) {
       R.ids[t * p.k + lane] = id;
       R.w[t * p.k + lane] = w;
@@ -401,9 +476,10 @@ __device__ __forceinline__ void group_routes(const BlockParams &p, const RouteLd
 
 // Route task (many rows): rows 4 task .. +3, one per wave; their ids and
 // weights go out coherently for every workgroup's grouping.
-__device__ __noinline__ void route_task(const BlockParams &p, const Deps &d, const RouteLds &R,
-                                           int task) {
-  wait_ge(d, d.ctr(kCtrLogits), (unsigned)p.n_router);
+__device__ __forceinline__ void route_task(const BlockParams &p, const Deps &d, const RouteLds &R,
+                                           int task, unsigned char *lds) {
+  int *flag = reinterpret_cast<int *>(lds);
+  wait_event(d, kCtrLogits, p.n_logit_producers);
   const int t0 = task * kWaves, t1 = min(p.b, t0 + kWaves);
   route_dispatch(p, R, nullptr, t0, t1, false);
   __syncthreads();
@@ -414,17 +490,17 @@ __device__ __noinline__ void route_task(const BlockParams &p, const Deps &d, con
     st_co4(rw, (uint32_t)(r * 4), __float_as_uint(R.w[r]));
   }
   if (p.logits && !p.logits_in) {
-    const rsrc_t part = make_rsrc(p.logit_part);
+    const rsrc_t rl = make_rsrc(p.logits_f);
     for (int i = threadIdx.x; i < (t1 - t0) * p.E; i += kThreads) {
       const int t = t0 + i / p.E, e = i % p.E;
-      p.logits[(size_t)t * p.E + e] = logit_of(p, part, t, e);
+      p.logits[(size_t)t * p.E + e] = logit_of(p, rl, t, e);
     }
   }
-  signal(d.ctr(kCtrRoute));
+  arrive(d, kCtrRoute, (unsigned)p.n_route, flag);
 }
 
-// The routing state a workgroup needs before its first expert task.
-__device__ __noinline__ void prepare_routing(const BlockParams &p, const Deps &d, const RouteLds &R,
+// The routing state a workgroup needs before its first expert unit.
+__device__ __forceinline__ void prepare_routing(const BlockParams &p, const Deps &d, const RouteLds &R,
                                                 unsigned char *scratch) {
   const bool out = p.routing_out && blockIdx.x == 0;
   if (p.route_given) {
@@ -442,16 +518,30 @@ __device__ __noinline__ void prepare_routing(const BlockParams &p, const Deps &d
   }
   if (p.n_route == 0) {
     // Few rows: every workgroup routes every row from logits staged in LDS.
-    wait_ge(d, d.ctr(kCtrLogits), (unsigned)p.n_router);
+    wait_event(d, kCtrLogits, p.n_logit_producers);
+    stamp(p, 12);
     float *lg = reinterpret_cast<float *>(scratch);
-    const rsrc_t part = make_rsrc(p.logit_part);
-    for (int i = threadIdx.x; i < p.b * p.E; i += kThreads) lg[i] = logit_of(p, part, i / p.E, i % p.E);
+    const rsrc_t rl = make_rsrc(p.logits_f);
+    const int n = p.b * p.E;
+    for (int i0 = threadIdx.x; i0 < n; i0 += kThreads * 4) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = min(i0 + kThreads * u, n - 1);
+        v[u] = logit_of(p, rl, i / p.E, i % p.E);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i0 + kThreads * u < n) lg[i0 + kThreads * u] = v[u];
+    }
     __syncthreads();
+    stamp(p, 13);
     route_dispatch(p, R, lg, 0, p.b, out);
+    stamp(p, 14);
     if (out && p.logits && !p.logits_in)
       for (int i = threadIdx.x; i < p.b * p.E; i += kThreads) p.logits[i] = lg[i];
   } else {
-    wait_ge(d, d.ctr(kCtrRoute), (unsigned)p.n_route);
+    wait_event(d, kCtrRoute, p.n_route);
     const rsrc_t ri = make_rsrc(p.ids), rw = make_rsrc(p.wts);
     for (int i = threadIdx.x; i < p.b * p.k; i += kThreads) {
       R.ids[i] = (int)ld_co4(ri, (uint32_t)(i * 4));
@@ -464,69 +554,67 @@ __device__ __noinline__ void prepare_routing(const BlockParams &p, const Deps &d
 
 // ---------------------------------------------------------------- projections
 
+constexpr size_t kProjRedBytes = kWaves * kPoolMG * MB_WAVE * sizeof(f32x4_t);
+__device__ __forceinline__ int *proj_flag(unsigned char *lds) {
+  return reinterpret_cast<int *>(lds + kProjRedBytes);
+}
+
 // One task of out[t, n] = bf16(sum_k a[t, k] w[n, k]): a 16-feature tile and
 // contraction split ks of ks_count, the split's 32-element chunks dealt to the
-// four waves; 16-row groups of activations share each weight fragment (weights
-// in the MFMA A operand, activations in B).  The first weight fragments are
-// requested before waiting for `a` (wait_ctr).  With ks_count > 1 the fp32
-// partials go to `part` and the last split to finish (tile counter) adds them
-// in split order and writes bf16.  Returns true in the workgroup that
-// completed the tile.
-__device__ __noinline__ bool proj_task(const Deps &d, const uint16_t *a, bool a_coherent,
-                                          const uint16_t *w, uint16_t *out, int rows, int n_out,
-                                          int kdim, int ks_count, float *part, unsigned *tile_ctr,
-                                          const unsigned *wait_ctr, unsigned wait_target, int task,
+// four waves, each requesting up to kProjBatch chunks at once; 16-row groups
+// of activations share each weight fragment (weights in the MFMA A operand,
+// activations in B, read coherently when another workgroup of the launch
+// wrote them: kCoherentA).  The first weight chunks are requested
+// before waiting for `a` (event wait_ev); padding chunks and rows load zeros.
+// With ks_count > 1 the fp32 partials go to `part` and the last split to
+// finish (tile counter) adds them in split order and writes bf16.  Returns
+// true in the workgroup that completed the tile.
+template <bool kCoherentA>
+__device__ __forceinline__ bool proj_task(const Deps &d, const uint16_t *a, const uint16_t *w, uint16_t *out,
+                                          int rows, int n_out, int kdim, int ks_count, float *part,
+                                          unsigned *tile_ctr, int wait_ev, int wait_arrivals, int task,
                                           unsigned char *lds) {
   const Lane L;
   const int nchunks = kdim / 32;
   const int cpw = (nchunks + ks_count - 1) / ks_count;
   f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);  // [kWaves][kPoolMG][64]
-  int *s_last = reinterpret_cast<int *>(lds + kWaves * kPoolMG * MB_WAVE * sizeof(f32x4_t));
-  const rsrc_t ra = make_rsrc(a), ro = make_rsrc(out), rp = make_rsrc(part);
+  int *flag = proj_flag(lds);
   const int tile = task / ks_count, ks = task % ks_count;
   const int c_begin = ks * cpw, c_end = min(nchunks, c_begin + cpw);
-  const uint16_t *wrow = w + (size_t)(tile * 16 + L.r16) * kdim + 8 * L.g;
+  const rsrc_t rw = make_rsrc(w + (size_t)tile * 16 * kdim), ra = make_rsrc(a), ro = make_rsrc(out),
+               rp = make_rsrc(part);
+  const uint32_t wrow = (uint32_t)((L.r16 * kdim + 8 * L.g) * 2);
   bool waited = false;
   for (int rb = 0; rb < rows; rb += 16 * kPoolMG) {
     f32x4_t acc[kPoolMG];
 #pragma unroll
     for (int mg = 0; mg < kPoolMG; ++mg) acc[mg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    u32x4_t wv[4];
-    const int c_first = c_begin + L.wave;
+    for (int c = c_begin + L.wave; c < c_end || !waited; c += kWaves * kProjBatch) {
+      u32x4_t wv[kProjBatch];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int cc = c_first + kWaves * u;
-      wv[u] = cc < c_end ? ld16_nt(wrow + cc * 32) : u32x4_t{0, 0, 0, 0};
-    }
-    if (!waited) {
-      wait_ge(d, wait_ctr, wait_target);
-      waited = true;
-    }
-    for (int c = c_first; c < c_end; c += kWaves * 4) {
-      if (c != c_first) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int cc = c + kWaves * u;
-          wv[u] = cc < c_end ? ld16_nt(wrow + cc * 32) : u32x4_t{0, 0, 0, 0};
-        }
+      for (int u = 0; u < kProjBatch; ++u) {
+        const int cc = c + kWaves * u;
+        wv[u] = ld_nt16(rw, cc < c_end ? wrow + (uint32_t)cc * 64u : kOob);
+      }
+      if (!waited) {
+        wait_event(d, wait_ev, wait_arrivals);
+        waited = true;
+        if (c >= c_end) break;
       }
 #pragma unroll
       for (int mg = 0; mg < kPoolMG; ++mg) {
-        const int t = rb + mg * 16 + L.r16;
         if (rb + mg * 16 >= rows) break;
-        u32x4_t av[4];
+        const int t = rb + mg * 16 + L.r16;
+        const uint32_t arow = t < rows ? (uint32_t)(((size_t)t * kdim + 8 * L.g) * 2) : kOob;
+        u32x4_t av[kProjBatch];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kProjBatch; ++u) {
           const int cc = c + kWaves * u;
-          const size_t off = (size_t)t * kdim + cc * 32 + 8 * L.g;
-          if (cc < c_end && t < rows)
-            av[u] = a_coherent ? ld_co16(ra, (uint32_t)(off * 2)) : ld16(a + off);
-          else
-            av[u] = u32x4_t{0, 0, 0, 0};
+          const uint32_t off = cc < c_end ? arow + (uint32_t)cc * 64u : kOob;
+          av[u] = kCoherentA ? ld_co16(ra, off) : ld_b128(ra, off);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (c + kWaves * u < c_end) acc[mg] = mfma_bf16(as_bf16x8(wv[u]), as_bf16x8(av[u]), acc[mg]);
+        for (int u = 0; u < kProjBatch; ++u) acc[mg] = mfma_bf16(as_bf16x8(wv[u]), as_bf16x8(av[u]), acc[mg]);
       }
     }
 #pragma unroll
@@ -547,264 +635,265 @@ __device__ __noinline__ bool proj_task(const Deps &d, const uint16_t *a, bool a_
     __syncthreads();
   }
   if (ks_count == 1) return true;
-  wait_stores();
-  __syncthreads();
-  if (threadIdx.x == 0)
-    *s_last = __hip_atomic_fetch_add(&tile_ctr[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              (unsigned)(ks_count - 1);
-  __syncthreads();
-  const bool last = *s_last != 0;
-  if (last) {
-    for (int idx = threadIdx.x; idx < rows * 4; idx += kThreads) {
-      const int t = idx / 4, n0 = tile * 16 + 4 * (idx % 4);
-      f32x4_t v = __builtin_bit_cast(f32x4_t, ld_co16(rp, (uint32_t)(((size_t)t * n_out + n0) * 4)));
-      for (int q = 1; q < ks_count; ++q)
-        v += __builtin_bit_cast(f32x4_t, ld_co16(rp, (uint32_t)((((size_t)q * rows + t) * n_out + n0) * 4)));
-      st_co8(ro, (uint32_t)(((size_t)t * n_out + n0) * 2),
-             u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
-    }
-    if (threadIdx.x == 0) __hip_atomic_store(&tile_ctr[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!last_arrival(&tile_ctr[tile], (unsigned)ks_count, flag)) return false;
+  for (int idx = threadIdx.x; idx < rows * 4; idx += kThreads) {
+    const int t = idx / 4, n0 = tile * 16 + 4 * (idx % 4);
+    f32x4_t part_v[kMaxSplitK];
+#pragma unroll
+    for (int q = 0; q < kMaxSplitK; ++q)
+      part_v[q] = __builtin_bit_cast(
+          f32x4_t, ld_co16(rp, q < ks_count ? (uint32_t)((((size_t)q * rows + t) * n_out + n0) * 4) : kOob));
+    f32x4_t v = part_v[0];
+#pragma unroll
+    for (int q = 1; q < kMaxSplitK; ++q)
+      if (q < ks_count) v += part_v[q];
+    st_co8(ro, (uint32_t)(((size_t)t * n_out + n0) * 2),
+           u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
   }
-  __syncthreads();
-  return last;
+  if (threadIdx.x == 0) __hip_atomic_store(&tile_ctr[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
 }
 
-// Optional pre-expert norm of h row t.
-__device__ __noinline__ void prenorm_task(const BlockParams &p, const Deps &d, int t,
+// Optional pre-expert norm of h row t: thread i takes elements 2i + 512 m,
+// +1, kBoundBatch of them per request.
+__device__ __forceinline__ void prenorm_task(const BlockParams &p, const Deps &d, int t,
                                              unsigned char *lds) {
-  wait_ge(d, d.ctr(kCtrPool), (unsigned)p.n_pool_tiles);
+  wait_event(d, kCtrPool, p.n_pool_tiles);
   float *red = reinterpret_cast<float *>(lds);
-  const rsrc_t rh = make_rsrc(p.h);
+  int *flag = reinterpret_cast<int *>(lds + 64);
+  const rsrc_t rh = make_rsrc(p.h + (size_t)t * p.P), rw = make_rsrc(p.pre_norm_w);
+  const uint32_t P2 = (uint32_t)p.P * 2;
   float ss = 0.f;
-  for (int i = threadIdx.x * 2; i < p.P; i += kThreads * 2) {
-    const uint32_t v = ld_co4(rh, (uint32_t)(((size_t)t * p.P + i) * 2));
-    const float a = bf16_bits_to_f32(v & 0xFFFFu), b = bf16_bits_to_f32(v >> 16);
-    ss += a * a + b * b;
+  for (int i0 = 2 * threadIdx.x; i0 < p.P; i0 += 512 * kBoundBatch) {
+    uint32_t v[kBoundBatch];
+#pragma unroll
+    for (int m = 0; m < kBoundBatch; ++m) {
+      const uint32_t off = (uint32_t)(i0 + 512 * m) * 2;
+      v[m] = ld_co4(rh, off < P2 ? off : kOob);
+    }
+#pragma unroll
+    for (int m = 0; m < kBoundBatch; ++m) {
+      const float a = bf16_bits_to_f32(v[m] & 0xFFFFu), b = bf16_bits_to_f32(v[m] >> 16);
+      ss += a * a + b * b;
+    }
   }
   ss = block_sum(ss, red);
   const float rs = 1.0f / sqrtf(ss / (float)p.P + p.norm_eps);
-  for (int i = threadIdx.x * 2; i < p.P; i += kThreads * 2) {
-    const uint32_t v = ld_co4(rh, (uint32_t)(((size_t)t * p.P + i) * 2));
-    const float a = bf16_bits_to_f32(v & 0xFFFFu) * rs, b = bf16_bits_to_f32(v >> 16) * rs;
-    const float wa = bf16_bits_to_f32(p.pre_norm_w[i]), wb = bf16_bits_to_f32(p.pre_norm_w[i + 1]);
-    st_co4(rh, (uint32_t)(((size_t)t * p.P + i) * 2), pack_bf16x2(a * wa, b * wb));
+  for (int i0 = 2 * threadIdx.x; i0 < p.P; i0 += 512 * kBoundBatch) {
+    uint32_t v[kBoundBatch], w[kBoundBatch];
+#pragma unroll
+    for (int m = 0; m < kBoundBatch; ++m) {
+      const uint32_t off = (uint32_t)(i0 + 512 * m) * 2;
+      v[m] = ld_co4(rh, off < P2 ? off : kOob);
+      w[m] = __builtin_amdgcn_raw_buffer_load_b32(rw, off < P2 ? off : kOob, 0, 0);
+    }
+#pragma unroll
+    for (int m = 0; m < kBoundBatch; ++m) {
+      const int i = i0 + 512 * m;
+      if (i >= p.P) break;
+      const float a = bf16_bits_to_f32(v[m] & 0xFFFFu) * rs, b = bf16_bits_to_f32(v[m] >> 16) * rs;
+      const float wa = bf16_bits_to_f32(w[m] & 0xFFFFu), wb = bf16_bits_to_f32(w[m] >> 16);
+      st_co4(rh, (uint32_t)i * 2, pack_bf16x2(a * wa, b * wb));
+    }
   }
-  signal(d.ctr(kCtrPrenorm));
+  arrive(d, kCtrPrenorm, (unsigned)p.n_prenorm, flag);
 }
 
 // ---------------------------------------------------------------- experts
 
-// w13 + gated activation for (active expert, 16 act columns): gate rows
-// i0..i0+15 and up rows I+i0..I+i0+15, contraction over P in 128-element
-// chunks dealt to the waves; per chunk a lane converts one 32-element MXFP4
-// block (16 bytes + a scale byte) of its weight row to bf16 for four MFMAs.
-__device__ __noinline__ void up_task(const BlockParams &p, const Deps &d, const RouteLds &R,
-                                        int task, bool &h_ready, unsigned char *lds) {
-  const Lane L;
+// One wave: D0 = W0 B and D1 = W1 B for two 16-row MXFP4 weight tiles over
+// nch 128-element chunks and up to kStageRows activation rows (bf16).
+//
+// Weights: in resource rw (scales rs) this lane's row of tile 0 / 1 starts at
+// byte o0 / o1 (so0 / so1), o0 / o1 already at the lane's 16-byte column (32
+// codes, one MX block per chunk).  Lane l gets output rows 4*(l/16)..+3 of
+// column l % 16; columns past the pass's rows hold garbage and are not used.
+// Per chunk a lane converts its MX block of each tile row to bf16 in
+// registers for four 16x16x32 MFMAs; kRing chunks are in flight.  The scales
+// of four chunks come in one 16-byte load per tile row (vec_scales: nch a
+// multiple of 4), else one 4-byte load per chunk; the lane keeps byte l / 16.
+//
+// Activations: lane l loads 16 bytes (elements 8 (l % 16) ..) of the chunk of
+// pass row l / 16 (a_ld0) and of row 4 + l / 16 (a_ld1, when `two`); kOob
+// gives zeros.  They go to the wave's staging LDS (la) and come back in MFMA
+// layout: lane l reads row l % 8.  Only the pass's rows are requested, in
+// full 16-byte pieces, instead of 16 padded rows per lane.
+//
+// Chunks past nch load zeros and add nothing, so the loop has no branches on
+// the data.  `wait` runs after the first weight requests, before the first
+// activation request.
+template <typename Wait>
+__device__ __forceinline__ void mx_pair(rsrc_t rw, uint32_t o0, uint32_t o1, rsrc_t rs, uint32_t so0,
+                                        uint32_t so1, bool vec_scales, int nch, rsrc_t ra, uint32_t a_ld0,
+                                        uint32_t a_ld1, bool two, unsigned char *la, f32x4_t &d0, f32x4_t &d1,
+                                        Wait wait) {
+  const int lane = threadIdx.x % MB_WAVE, g = lane >> 4;
+  u32x4_t W0[kRing], W1[kRing], A0[kRing], A1[kRing];
+  auto scales = [&](uint32_t so, int c0) {
+    if (vec_scales) return ld_b128(rs, c0 < nch ? so + 4u * c0 : kOob);
+    u32x4_t v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = ld_b32(rs, c0 + r < nch ? so + 4u * (c0 + r) : kOob);
+    return v;
+  };
+#pragma unroll
+  for (int r = 0; r < kRing; ++r) {
+    const bool ok = r < nch;
+    W0[r] = ld_b128(rw, ok ? o0 + 64u * r : kOob);
+    W1[r] = ld_b128(rw, ok ? o1 + 64u * r : kOob);
+  }
+  u32x4_t S0 = scales(so0, 0), S1 = scales(so1, 0);
+  wait();
+#pragma unroll
+  for (int r = 0; r < kRing; ++r) {
+    const bool ok = r < nch;
+    A0[r] = ld_b128(ra, ok ? a_ld0 + 256u * r : kOob);
+    A1[r] = two ? ld_b128(ra, ok ? a_ld1 + 256u * r : kOob) : u32x4_t{0, 0, 0, 0};
+  }
+  d0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  d1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint32_t st_off = (uint32_t)((lane >> 4) * kStageRowBytes + (lane & 15) * 16);
+  const uint32_t rd_off = (uint32_t)((lane & 7) * kStageRowBytes + 64 * g);
+  for (int c0 = 0; c0 < nch; c0 += kRing) {
+    // This round's activations to the staging LDS (one wave's LDS accesses
+    // complete in order, so the reads below see them and the next round's
+    // stores follow this round's reads).
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) {
+      *reinterpret_cast<u32x4_t *>(la + r * kStageRows * kStageRowBytes + st_off) = A0[r];
+      if (two) *reinterpret_cast<u32x4_t *>(la + r * kStageRows * kStageRowBytes + 4 * kStageRowBytes + st_off) = A1[r];
+    }
+    asm volatile("" ::: "memory");
+    const u32x4_t N0 = scales(so0, c0 + kRing), N1 = scales(so1, c0 + kRing);
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) {
+      u32x4_t B[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        B[i] = *reinterpret_cast<const u32x4_t *>(la + r * kStageRows * kStageRowBytes + rd_off + 16 * i);
+      bf16x8_t X0[4], X1[4];
+      dequant_fp4x32(W0[r], e8m0_to_f32((S0[r] >> (8 * g)) & 0xFFu), X0);
+      dequant_fp4x32(W1[r], e8m0_to_f32((S1[r] >> (8 * g)) & 0xFFu), X1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        d0 = mfma_bf16(X0[i], as_bf16x8(B[i]), d0);
+        d1 = mfma_bf16(X1[i], as_bf16x8(B[i]), d1);
+      }
+      const int cn = c0 + kRing + r;
+      const bool ok = cn < nch;
+      W0[r] = ld_b128(rw, ok ? o0 + 64u * cn : kOob);
+      W1[r] = ld_b128(rw, ok ? o1 + 64u * cn : kOob);
+      A0[r] = ld_b128(ra, ok ? a_ld0 + 256u * cn : kOob);
+      A1[r] = two ? ld_b128(ra, ok ? a_ld1 + 256u * cn : kOob) : u32x4_t{0, 0, 0, 0};
+    }
+    asm volatile("" ::: "memory");
+    S0 = N0;
+    S1 = N1;
+  }
+}
+
+// Up unit: w13 and the gated activation for (active expert, 16 act columns):
+// gate rows i0..i0+15 and up rows I+i0..I+i0+15 of the expert, over P, for
+// the expert's routes in passes of kStageRows.
+__device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, const RouteLds &R, int unit,
+                                        bool &h_ready, unsigned char *la) {
+  const int lane = threadIdx.x % MB_WAVE, g = lane >> 4, r16 = lane & 15;
   const int P = p.P, I = p.I;
   const int tiles = I / 16;
-  const int nch = P / 128;
-  const rsrc_t rh = make_rsrc(p.h), ract = make_rsrc(p.act);
-  f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);  // [kWaves][2][64]
-  const int a = task / tiles, tile = task % tiles;
-  const int e = R.act[a];
-  const int row0 = R.off[e], nrows = R.off[e + 1] - row0;
+  const int a = unit / tiles, tile = unit % tiles;
+  const int e = uniform(R.act[a]);
+  const int row0 = uniform(R.off[e]), nrows = uniform(R.off[e + 1]) - row0;
   const int i0 = tile * 16;
-  const size_t rg = (size_t)e * 2 * I + i0 + L.r16, ru = rg + I;
-  const uint8_t *wg = p.w13 + rg * (P / 2) + 16 * L.g;
-  const uint8_t *wu = p.w13 + ru * (P / 2) + 16 * L.g;
-  const uint8_t *sg = p.w13s + rg * (P / 32) + L.g;
-  const uint8_t *su = p.w13s + ru * (P / 32) + L.g;
-  for (int m0 = 0; m0 < nrows; m0 += 16) {
-    const int m = m0 + L.r16;
-    const bool valid = m < nrows;
-    const int t = valid ? R.rl[row0 + m] / p.k : 0;
-    const uint32_t hoff = (uint32_t)(((size_t)t * P + 32 * L.g) * 2);
-    f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
-    u32x4_t vg[4], vu[4];
-    uint32_t bg[4], bu[4];
-    const int c_first = L.wave;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int cc = c_first + kWaves * u;
-      const bool ok = cc < nch;
-      vg[u] = ok ? ld16_nt(wg + 64 * cc) : u32x4_t{0, 0, 0, 0};
-      vu[u] = ok ? ld16_nt(wu + 64 * cc) : u32x4_t{0, 0, 0, 0};
-      bg[u] = ok ? sg[4 * cc] : 0u;
-      bu[u] = ok ? su[4 * cc] : 0u;
-    }
-    if (!h_ready) {
-      wait_ge(d, d.ctr(p.pre_norm_w ? kCtrPrenorm : kCtrPool), (unsigned)p.h_producers);
-      h_ready = true;
-    }
-    for (int c = c_first; c < nch; c += kWaves * 4) {
-      if (c != c_first) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int cc = c + kWaves * u;
-          const bool ok = cc < nch;
-          vg[u] = ok ? ld16_nt(wg + 64 * cc) : u32x4_t{0, 0, 0, 0};
-          vu[u] = ok ? ld16_nt(wu + 64 * cc) : u32x4_t{0, 0, 0, 0};
-          bg[u] = ok ? sg[4 * cc] : 0u;
-          bu[u] = ok ? su[4 * cc] : 0u;
-        }
-      }
-      u32x4_t hv[4][4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int cc = c + kWaves * u;
-        const bool ok = cc < nch && valid;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          hv[u][i] = ok ? ld_co16(rh, hoff + (uint32_t)((128 * cc + 8 * i) * 2)) : u32x4_t{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (c + kWaves * u < nch) {
-          bf16x8_t G[4], U[4];
-          dequant_fp4x32(vg[u], e8m0_to_f32(bg[u]), G);
-          dequant_fp4x32(vu[u], e8m0_to_f32(bu[u]), U);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            ag = mfma_bf16(G[i], as_bf16x8(hv[u][i]), ag);
-            au = mfma_bf16(U[i], as_bf16x8(hv[u][i]), au);
-          }
-        }
-      }
-    }
-    red[(L.wave * 2 + 0) * MB_WAVE + L.lane] = ag;
-    red[(L.wave * 2 + 1) * MB_WAVE + L.lane] = au;
-    __syncthreads();
-    if (L.wave == 0 && valid) {
-      f32x4_t gs = red[0 * MB_WAVE + L.lane], us = red[1 * MB_WAVE + L.lane];
-      for (int q = 1; q < kWaves; ++q) {
-        gs += red[(q * 2 + 0) * MB_WAVE + L.lane];
-        us += red[(q * 2 + 1) * MB_WAVE + L.lane];
-      }
+  const rsrc_t rw = make_rsrc(p.w13 + (size_t)e * 2 * I * (P / 2));
+  const rsrc_t rs = make_rsrc(p.w13s + (size_t)e * 2 * I * (P / 32));
+  const uint32_t rg = (uint32_t)(i0 + r16), ru = rg + (uint32_t)I;
+  const rsrc_t rh = make_rsrc(p.h), ract = make_rsrc(p.act);
+  const int nch = P / 128;
+  for (int m0 = 0; m0 < nrows; m0 += kStageRows) {
+    const int mrows = min(kStageRows, nrows - m0);
+    const int ml0 = m0 + (lane >> 4), ml1 = ml0 + 4;
+    const uint32_t piece = (uint32_t)(lane & 15) * 16;
+    const uint32_t a0 = ml0 < nrows ? (uint32_t)((R.rl[row0 + ml0] / p.k) * P) * 2u + piece : kOob;
+    const uint32_t a1 = ml1 < nrows ? (uint32_t)((R.rl[row0 + ml1] / p.k) * P) * 2u + piece : kOob;
+    f32x4_t gs, us;
+    mx_pair(rw, rg * (P / 2) + 16 * g, ru * (P / 2) + 16 * g, rs, rg * (P / 32), ru * (P / 32), nch % 4 == 0, nch,
+            rh, a0, a1, mrows > 4, la, gs, us, [&]() {
+              if (!h_ready) {
+                wave_wait_event(d, p.pre_norm_w ? kCtrPrenorm : kCtrPool, p.h_producers);
+                h_ready = true;
+              }
+            });
+    const int m = m0 + r16;
+    if (r16 < kStageRows && m < nrows) {
       float o[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float z = gs[i];
         o[i] = (z / (1.0f + expf(-z))) * us[i];
       }
-      st_co8(ract, (uint32_t)((((size_t)(row0 + m)) * I + i0 + 4 * L.g) * 2),
+      st_co8(ract, (uint32_t)((((size_t)(row0 + m)) * I + i0 + 4 * g) * 2),
              u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
     }
-    __syncthreads();
   }
-  signal(d.up(e));
+  wave_signal(d.up(e));
 }
 
-// w2 for (active expert, 32 output features): y in route order and the
-// route's sum of squares over these 32 features.
-__device__ __noinline__ void down_task(const BlockParams &p, const Deps &d, const RouteLds &R,
-                                          int task, unsigned char *lds) {
-  const Lane L;
+// Down unit: w2 for (active expert, 32 output features): y in route order and
+// the route's sum of squares over these 32 features.
+__device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, const RouteLds &R, int unit,
+                                          unsigned char *la) {
+  const int lane = threadIdx.x % MB_WAVE, g = lane >> 4, r16 = lane & 15;
   const int P = p.P, I = p.I;
   const int tiles = P / 32;
-  const int nch = I / 128;
-  const rsrc_t ract = make_rsrc(p.act), ry = make_rsrc(p.y), rss = make_rsrc(p.ssq);
-  f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);  // [kWaves][2][64]
-  const int a = task / tiles, tile = task % tiles;
-  const int e = R.act[a];
-  const int row0 = R.off[e], nrows = R.off[e + 1] - row0;
+  const int a = unit / tiles, tile = unit % tiles;
+  const int e = uniform(R.act[a]);
+  const int row0 = uniform(R.off[e]), nrows = uniform(R.off[e + 1]) - row0;
   const int p0 = tile * 32;
-  const size_t r0 = (size_t)e * P + p0 + L.r16, r1 = r0 + 16;
-  const uint8_t *w0 = p.w2 + r0 * (I / 2) + 16 * L.g;
-  const uint8_t *w1 = p.w2 + r1 * (I / 2) + 16 * L.g;
-  const uint8_t *s0 = p.w2s + r0 * (I / 32) + L.g;
-  const uint8_t *s1 = p.w2s + r1 * (I / 32) + L.g;
+  const rsrc_t rw = make_rsrc(p.w2 + (size_t)e * P * (I / 2));
+  const rsrc_t rs = make_rsrc(p.w2s + (size_t)e * P * (I / 32));
+  const uint32_t r0 = (uint32_t)(p0 + r16), r1 = r0 + 16;
+  const rsrc_t ract = make_rsrc(p.act), ry = make_rsrc(p.y), rss = make_rsrc(p.ssq);
+  const int nch = I / 128;
   bool ready = false;
-  for (int m0 = 0; m0 < nrows; m0 += 16) {
-    const int m = m0 + L.r16;
-    const bool valid = m < nrows;
-    const uint32_t aoff = (uint32_t)((((size_t)(row0 + (valid ? m : 0))) * I + 32 * L.g) * 2);
-    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-    u32x4_t v0[4], v1[4];
-    uint32_t b0[4], b1[4];
-    const int c_first = L.wave;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int cc = c_first + kWaves * u;
-      const bool ok = cc < nch;
-      v0[u] = ok ? ld16_nt(w0 + 64 * cc) : u32x4_t{0, 0, 0, 0};
-      v1[u] = ok ? ld16_nt(w1 + 64 * cc) : u32x4_t{0, 0, 0, 0};
-      b0[u] = ok ? s0[4 * cc] : 0u;
-      b1[u] = ok ? s1[4 * cc] : 0u;
+  for (int m0 = 0; m0 < nrows; m0 += kStageRows) {
+    const int mrows = min(kStageRows, nrows - m0);
+    const int ml0 = m0 + (lane >> 4), ml1 = ml0 + 4;
+    const uint32_t piece = (uint32_t)(lane & 15) * 16;
+    const uint32_t a0 = ml0 < nrows ? (uint32_t)((row0 + ml0) * I) * 2u + piece : kOob;
+    const uint32_t a1 = ml1 < nrows ? (uint32_t)((row0 + ml1) * I) * 2u + piece : kOob;
+    f32x4_t y0, y1;
+    mx_pair(rw, r0 * (I / 2) + 16 * g, r1 * (I / 2) + 16 * g, rs, r0 * (I / 32), r1 * (I / 32), nch % 4 == 0, nch,
+            ract, a0, a1, mrows > 4, la, y0, y1, [&]() {
+              if (!ready) {
+                poll_ge(d, d.up(e), (unsigned)(I / 16));
+                ready = true;
+              }
+            });
+    const int m = m0 + r16;
+    const bool valid = r16 < kStageRows && m < nrows;
+    float ss = 0.f;
+    if (valid) {
+      ss = y0[0] * y0[0] + y0[1] * y0[1] + y0[2] * y0[2] + y0[3] * y0[3];
+      ss += y1[0] * y1[0] + y1[1] * y1[1] + y1[2] * y1[2] + y1[3] * y1[3];
     }
-    if (!ready) {
-      wait_ge(d, d.up(e), p.has_up ? (unsigned)(I / 16) : 0u);
-      ready = true;
+    ss += __shfl_xor(ss, 16, MB_WAVE);
+    ss += __shfl_xor(ss, 32, MB_WAVE);
+    if (valid) {
+      const int r = R.rl[row0 + m];
+      st_co16(ry, (uint32_t)(((size_t)r * P + p0 + 4 * g) * 4), __builtin_bit_cast(u32x4_t, y0));
+      st_co16(ry, (uint32_t)(((size_t)r * P + p0 + 16 + 4 * g) * 4), __builtin_bit_cast(u32x4_t, y1));
+      if (g == 0) st_co4(rss, (uint32_t)(((size_t)r * tiles + tile) * 4), __float_as_uint(ss));
     }
-    for (int c = c_first; c < nch; c += kWaves * 4) {
-      if (c != c_first) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int cc = c + kWaves * u;
-          const bool ok = cc < nch;
-          v0[u] = ok ? ld16_nt(w0 + 64 * cc) : u32x4_t{0, 0, 0, 0};
-          v1[u] = ok ? ld16_nt(w1 + 64 * cc) : u32x4_t{0, 0, 0, 0};
-          b0[u] = ok ? s0[4 * cc] : 0u;
-          b1[u] = ok ? s1[4 * cc] : 0u;
-        }
-      }
-      u32x4_t av[4][4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int cc = c + kWaves * u;
-        const bool ok = cc < nch && valid;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          av[u][i] = ok ? ld_co16(ract, aoff + (uint32_t)((128 * cc + 8 * i) * 2)) : u32x4_t{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (c + kWaves * u < nch) {
-          bf16x8_t A0[4], A1[4];
-          dequant_fp4x32(v0[u], e8m0_to_f32(b0[u]), A0);
-          dequant_fp4x32(v1[u], e8m0_to_f32(b1[u]), A1);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            a0 = mfma_bf16(A0[i], as_bf16x8(av[u][i]), a0);
-            a1 = mfma_bf16(A1[i], as_bf16x8(av[u][i]), a1);
-          }
-        }
-      }
-    }
-    red[(L.wave * 2 + 0) * MB_WAVE + L.lane] = a0;
-    red[(L.wave * 2 + 1) * MB_WAVE + L.lane] = a1;
-    __syncthreads();
-    if (L.wave == 0) {
-      f32x4_t y0 = red[0 * MB_WAVE + L.lane], y1 = red[1 * MB_WAVE + L.lane];
-      for (int q = 1; q < kWaves; ++q) {
-        y0 += red[(q * 2 + 0) * MB_WAVE + L.lane];
-        y1 += red[(q * 2 + 1) * MB_WAVE + L.lane];
-      }
-      float ss = 0.f;
-      if (valid) {
-        ss = y0[0] * y0[0] + y0[1] * y0[1] + y0[2] * y0[2] + y0[3] * y0[3];
-        ss += y1[0] * y1[0] + y1[1] * y1[1] + y1[2] * y1[2] + y1[3] * y1[3];
-      }
-      ss += __shfl_xor(ss, 16, MB_WAVE);
-      ss += __shfl_xor(ss, 32, MB_WAVE);
-      if (valid) {
-        const int r = R.rl[row0 + m];
-        st_co16(ry, (uint32_t)(((size_t)r * P + p0 + 4 * L.g) * 4), __builtin_bit_cast(u32x4_t, y0));
-        st_co16(ry, (uint32_t)(((size_t)r * P + p0 + 16 + 4 * L.g) * 4), __builtin_bit_cast(u32x4_t, y1));
-        if (L.g == 0) st_co4(rss, (uint32_t)(((size_t)r * tiles + tile) * 4), __float_as_uint(ss));
-      }
-    }
-    __syncthreads();
   }
-  signal(d.down(e));
+  wave_signal(d.down(e));
 }
 
 // ---------------------------------------------------------------- tail
 
 // moe_out[t, p] = bf16(sum_j (w_j / sqrt(ss_j / P + eps)) y_j[p] * w_post[p]),
 // ss_j = the route's per-tile sums of squares added in tile order, for the
-// task's features of row t; waits for the down tasks of the row's experts.
-__device__ __noinline__ void fin_task(const BlockParams &p, const Deps &d, const RouteLds &R,
+// task's features of row t; waits for the down units of the row's experts.
+__device__ __forceinline__ void fin_task(const BlockParams &p, const Deps &d, const RouteLds &R,
                                          int task, unsigned char *lds) {
   const int P = p.P, k = p.k;
   const int tiles = P / 32;
@@ -812,11 +901,10 @@ __device__ __noinline__ void fin_task(const BlockParams &p, const Deps &d, const
   const int t = task / chunks, p_begin = (task % chunks) * kFinChunk;
   const int p_end = min(P, p_begin + kFinChunk);
   const int lane = threadIdx.x % MB_WAVE, wave = threadIdx.x / MB_WAVE;
-  if (p.has_up) {
-    if (threadIdx.x < MB_WAVE) poll_ge(d, d.down(R.ids[t * k + (lane < k ? lane : 0)]), (unsigned)tiles);
-    __syncthreads();
-  }
+  if (threadIdx.x < MB_WAVE) poll_ge(d, d.down(R.ids[t * k + (lane < k ? lane : 0)]), (unsigned)tiles);
+  __syncthreads();
   float *coef = reinterpret_cast<float *>(lds);  // [k]
+  int *flag = reinterpret_cast<int *>(lds + 64 * sizeof(float));
   const rsrc_t rss = make_rsrc(p.ssq), ry = make_rsrc(p.y), ro = make_rsrc(p.moe_out);
   for (int j = wave; j < k; j += kWaves) {
     const int r = t * k + j;
@@ -829,10 +917,16 @@ __device__ __noinline__ void fin_task(const BlockParams &p, const Deps &d, const
   __syncthreads();
   for (int p4 = p_begin + threadIdx.x * 4; p4 < p_end; p4 += kThreads * 4) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const f32x4_t yv =
-          __builtin_bit_cast(f32x4_t, ld_co16(ry, (uint32_t)(((size_t)(t * k + j) * P + p4) * 4)));
-      acc += coef[j] * yv;
+    for (int j0 = 0; j0 < k; j0 += 4) {
+      f32x4_t yv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = min(j0 + u, k - 1);
+        yv[u] = __builtin_bit_cast(f32x4_t, ld_co16(ry, (uint32_t)(((size_t)(t * k + j) * P + p4) * 4)));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (j0 + u < k) acc += coef[j0 + u] * yv[u];
     }
     const u32x2_t pw = *reinterpret_cast<const u32x2_t *>(p.post_norm_w + p4);
     const float o0 = acc[0] * bf16_bits_to_f32(pw[0] & 0xFFFFu);
@@ -841,7 +935,7 @@ __device__ __noinline__ void fin_task(const BlockParams &p, const Deps &d, const
     const float o3 = acc[3] * bf16_bits_to_f32(pw[1] >> 16);
     st_co8(ro, (uint32_t)(((size_t)t * P + p4) * 2), u32x2_t{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)});
   }
-  signal(d.ctr(kCtrFin));
+  arrive(d, kCtrFin, (unsigned)p.n_fin, flag);
 }
 
 // ---------------------------------------------------------------- boundary
@@ -854,144 +948,200 @@ __device__ __forceinline__ void unpack4(u32x2_t v, float o[4]) {
 }
 
 // v = RMSNorm_H(u) * w_pff; stream = fp32(stream + g * v) (one fma);
-// x_next = bf16(RMSNorm_H(stream) * w_in), for row t.
-__device__ __noinline__ void boundary_task(const BlockParams &p, const Deps &d, int t,
+// x_next = bf16(RMSNorm_H(stream) * w_in), for row t.  Thread i takes
+// elements 4i + 1024 m .. +3; each pass requests kBoundBatch of them at once.
+__device__ __forceinline__ void boundary_task(const BlockParams &p, const Deps &d, int t,
                                               unsigned char *lds) {
   wait_ge(d, d.ctr(kCtrUnpool), (unsigned)p.n_unpool_tiles);
   float *red = reinterpret_cast<float *>(lds);
   const int H = p.H;
-  const rsrc_t ru = make_rsrc(p.u);
-  float *srow = p.stream + (size_t)t * H;
+  const rsrc_t ru = make_rsrc(p.u + (size_t)t * H), rg = make_rsrc(p.gate);
+  const rsrc_t rs = make_rsrc(p.stream + (size_t)t * H);
+  const uint32_t H2 = (uint32_t)H * 2;
   float ss = 0.f;
-  for (int h = threadIdx.x * 4; h < H; h += kThreads * 4) {
-    float v[4];
-    unpack4(ld_co8(ru, (uint32_t)(((size_t)t * H + h) * 2)), v);
-    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  for (int h0 = 4 * threadIdx.x; h0 < H; h0 += 1024 * kBoundBatch) {
+    u32x2_t uv[kBoundBatch];
+#pragma unroll
+    for (int m = 0; m < kBoundBatch; ++m) {
+      const uint32_t off = (uint32_t)(h0 + 1024 * m) * 2;
+      uv[m] = ld_co8(ru, off < H2 ? off : kOob);
+    }
+#pragma unroll
+    for (int m = 0; m < kBoundBatch; ++m) {
+      float v[4];
+      unpack4(uv[m], v);
+      ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    }
   }
   ss = block_sum(ss, red);
   const float rsu = 1.0f / sqrtf(ss / (float)H + p.norm_eps);
   float s2 = 0.f;
-  for (int h = threadIdx.x * 4; h < H; h += kThreads * 4) {
-    float v[4], gg[4], wf[4] = {1.f, 1.f, 1.f, 1.f};
-    unpack4(ld_co8(ru, (uint32_t)(((size_t)t * H + h) * 2)), v);
-    unpack4(*reinterpret_cast<const u32x2_t *>(p.gate + h), gg);
-    if (p.ffn_norm_w) unpack4(*reinterpret_cast<const u32x2_t *>(p.ffn_norm_w + h), wf);
-    f32x4_t s = *reinterpret_cast<const f32x4_t *>(srow + h);
+  for (int h0 = 4 * threadIdx.x; h0 < H; h0 += 1024 * kBoundBatch) {
+    u32x2_t uv[kBoundBatch], gv[kBoundBatch], fv[kBoundBatch];
+    f32x4_t sv[kBoundBatch];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float vn = v[i] * rsu * wf[i];
-      s[i] = fmaf(gg[i], vn, s[i]);
-      s2 += s[i] * s[i];
+    for (int m = 0; m < kBoundBatch; ++m) {
+      const uint32_t h = (uint32_t)(h0 + 1024 * m);
+      const bool in = h * 2 < H2;
+      uv[m] = ld_co8(ru, in ? h * 2 : kOob);
+      gv[m] = ld_b64(rg, in ? h * 2 : kOob);
+      sv[m] = __builtin_bit_cast(f32x4_t, ld_b128(rs, in ? h * 4 : kOob));
+      fv[m] = p.ffn_norm_w ? ld_b64(make_rsrc(p.ffn_norm_w), in ? h * 2 : kOob) : u32x2_t{0x3F803F80u, 0x3F803F80u};
     }
-    *reinterpret_cast<f32x4_t *>(srow + h) = s;
+#pragma unroll
+    for (int m = 0; m < kBoundBatch; ++m) {
+      const int h = h0 + 1024 * m;
+      if (h >= H) break;
+      float v[4], gg[4], wf[4];
+      unpack4(uv[m], v);
+      unpack4(gv[m], gg);
+      unpack4(fv[m], wf);
+      f32x4_t sn = sv[m];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float vn = v[i] * rsu * wf[i];
+        sn[i] = fmaf(gg[i], vn, sn[i]);
+        s2 += sn[i] * sn[i];
+      }
+      *reinterpret_cast<f32x4_t *>(p.stream + (size_t)t * H + h) = sn;
+      sv[m] = sn;
+    }
   }
   s2 = block_sum(s2, red);
   const float rss = 1.0f / sqrtf(s2 / (float)H + p.norm_eps);
-  for (int h = threadIdx.x * 4; h < H; h += kThreads * 4) {
-    float wi[4] = {1.f, 1.f, 1.f, 1.f};
-    if (p.next_norm_w) unpack4(*reinterpret_cast<const u32x2_t *>(p.next_norm_w + h), wi);
-    const f32x4_t s = *reinterpret_cast<const f32x4_t *>(srow + h);
-    *reinterpret_cast<u32x2_t *>(p.x_next + (size_t)t * H + h) =
-        u32x2_t{pack_bf16x2(s[0] * rss * wi[0], s[1] * rss * wi[1]),
-                pack_bf16x2(s[2] * rss * wi[2], s[3] * rss * wi[3])};
+  for (int h0 = 4 * threadIdx.x; h0 < H; h0 += 1024 * kBoundBatch) {
+    f32x4_t sv[kBoundBatch];
+    u32x2_t wv[kBoundBatch];
+#pragma unroll
+    for (int m = 0; m < kBoundBatch; ++m) {
+      const uint32_t h = (uint32_t)(h0 + 1024 * m);
+      const bool in = h * 2 < H2;
+      sv[m] = __builtin_bit_cast(f32x4_t, ld_b128(rs, in ? h * 4 : kOob));
+      wv[m] = p.next_norm_w ? ld_b64(make_rsrc(p.next_norm_w), in ? h * 2 : kOob) : u32x2_t{0x3F803F80u, 0x3F803F80u};
+    }
+#pragma unroll
+    for (int m = 0; m < kBoundBatch; ++m) {
+      const int h = h0 + 1024 * m;
+      if (h >= H) break;
+      float wi[4];
+      unpack4(wv[m], wi);
+      const f32x4_t sn = sv[m];
+      *reinterpret_cast<u32x2_t *>(p.x_next + (size_t)t * H + h) =
+          u32x2_t{pack_bf16x2(sn[0] * rss * wi[0], sn[1] * rss * wi[1]),
+                  pack_bf16x2(sn[2] * rss * wi[2], sn[3] * rss * wi[3])};
+    }
   }
   __syncthreads();
 }
 
 // ---------------------------------------------------------------- the kernel
 
-// Tracing: workgroup thread 0 stamps the 100 MHz real-time counter at the
-// start (slot 0), when routing is ready (5), when it enters its first task of
-// each step (1..10 by step) and at the end (15).
-__device__ __forceinline__ void stamp(const BlockParams &p, int slot) {
-  if (p.timeline && threadIdx.x == 0)
-    p.timeline[(size_t)blockIdx.x * kTimelineSlots + slot] = (int64_t)wall_clock64();
-}
-
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void block_kernel(BlockParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void block_kernel(BlockParams p) {
   extern __shared__ __align__(16) unsigned char lds[];
   stamp(p, 0);
-  const Deps d = deps_init(p);
+  const Deps d{p.sync, p.E};
   const RouteLds R = route_lds(p, lds);
   unsigned char *scratch = lds + p.lds_route_bytes;
   const int G = gridDim.x;
-  const int nR = p.n_router, nRT = p.n_route, nP = p.n_pool, nPN = p.n_prenorm;
-  const int nF = p.n_fin, nN = p.n_unpool, nB = p.n_boundary;
-  bool routed = false, h_ready = p.h_producers == 0;
-  int nU = 0, nD = 0;
-  int last_step = -1;
-  for (int idx = blockIdx.x;; idx += G) {
-    int step, j = idx;
-    if (j < nR) {
-      step = 1;
-    } else if ((j -= nR) < nRT) {
-      step = 2;
-    } else if ((j -= nRT) < nP) {
-      step = 3;
-    } else if ((j -= nP) < nPN) {
-      step = 4;
-    } else {
-      j -= nPN;
-      if (!routed && p.needs_routing) {
-        prepare_routing(p, d, R, scratch);
-        routed = true;
-        stamp(p, 5);
-        if (p.has_up) {
-          nU = *R.nact * (p.I / 16);
-          nD = *R.nact * (p.P / 32);
-        }
+
+  // 1. Workgroup tasks before routing.
+  {
+    const int nR = p.n_router, nRT = p.n_route, nP = p.n_pool, nPN = p.n_prenorm;
+    int last = -1;
+    for (int j = blockIdx.x; j < nR + nRT + nP + nPN; j += G) {
+      int step, i = j;
+      if (i < nR) {
+        step = 1;
+      } else if ((i -= nR) < nRT) {
+        step = 2;
+      } else if ((i -= nRT) < nP) {
+        step = 3;
+      } else {
+        i -= nP;
+        step = 4;
       }
-      if (j < nU) step = 6;
-      else if ((j -= nU) < nD) step = 7;
-      else if ((j -= nD) < nF) step = 8;
-      else if ((j -= nF) < nN) step = 9;
-      else if ((j -= nN) < nB) step = 10;
-      else break;
+      if (step != last) {
+        stamp(p, step);
+        last = step;
+      }
+      if (step == 1) {
+        router_task(p, d, i, scratch);
+      } else if (step == 2) {
+        route_task(p, d, R, i, scratch);
+      } else if (step == 3) {
+        if (proj_task<false>(d, p.x, p.pool_w, p.h, p.b, p.P, p.H, p.pool_ks, p.pool_part, p.pool_cnt, 0, 0, i,
+                      scratch))
+          arrive(d, kCtrPool, (unsigned)p.n_pool_tiles, proj_flag(scratch));
+      } else {
+        prenorm_task(p, d, i, scratch);
+      }
     }
-    if (step != last_step) {
-      stamp(p, step);
-      last_step = step;
+  }
+
+  // 2. Routing state (workgroup 0 also writes the routing outputs).
+  if (p.needs_routing && (p.has_up || (p.routing_out && blockIdx.x == 0))) {
+    prepare_routing(p, d, R, scratch);
+    stamp(p, 5);
+  }
+
+  // 3. Expert units, one wave each.
+  if (p.has_up) {
+    stamp(p, 6);
+    const int GW = G * kWaves;
+    unsigned char *stage = scratch + (threadIdx.x / MB_WAVE) * kStageWaveBytes;
+    const int nact = uniform(*R.nact);
+    const int nU = nact * (p.I / 16), nD = nact * (p.P / 32);
+    bool h_ready = p.h_producers == 0;
+    for (int u = blockIdx.x * kWaves + uniform(threadIdx.x / MB_WAVE); u < nU + nD; u += GW) {
+      if (u < nU) up_unit(p, d, R, u, h_ready, stage);
+      else down_unit(p, d, R, u - nU, stage);
     }
-    switch (step) {
-      case 1: router_task(p, d, j, scratch); break;
-      case 2: route_task(p, d, R, j); break;
-      case 3:
-        if (proj_task(d, p.x, false, p.pool_w, p.h, p.b, p.P, p.H, p.pool_ks, p.pool_part, p.pool_cnt,
-                      nullptr, 0u, j, scratch))
-          signal(d.ctr(kCtrPool));
-        break;
-      case 4: prenorm_task(p, d, j, scratch); break;
-      case 6: up_task(p, d, R, j, h_ready, scratch); break;
-      case 7: down_task(p, d, R, j, scratch); break;
-      case 8: fin_task(p, d, R, j, scratch); break;
-      case 9:
-        if (proj_task(d, p.moe_out, p.n_fin > 0, p.unpool_w, p.u, p.b, p.H, p.P, p.unpool_ks,
-                      p.unpool_part, p.unpool_cnt, d.ctr(kCtrFin), (unsigned)p.n_fin, j, scratch))
+    __syncthreads();
+    stamp(p, 11);
+  }
+
+  // 4. Workgroup tasks after the experts.
+  {
+    const int nF = p.n_fin, nN = p.n_unpool, nB = p.n_boundary;
+    int last = -1;
+    for (int j = blockIdx.x; j < nF + nN + nB; j += G) {
+      int step, i = j;
+      if (i < nF) {
+        step = 8;
+      } else if ((i -= nF) < nN) {
+        step = 9;
+      } else {
+        i -= nN;
+        step = 10;
+      }
+      if (step != last) {
+        stamp(p, step);
+        last = step;
+      }
+      if (step == 8) {
+        fin_task(p, d, R, i, scratch);
+      } else if (step == 9) {
+        if (proj_task<true>(d, p.moe_out, p.unpool_w, p.u, p.b, p.H, p.P, p.unpool_ks, p.unpool_part,
+                      p.unpool_cnt, kCtrFin, p.n_fin, i, scratch))
           signal(d.ctr(kCtrUnpool));
-        break;
-      case 10: boundary_task(p, d, j, scratch); break;
-      default: break;
+      } else {
+        boundary_task(p, d, i, scratch);
+      }
     }
   }
-  // Workgroup 0 writes the routing outputs even when it ran no routed step.
-  if (!routed && p.needs_routing && p.routing_out && blockIdx.x == 0) prepare_routing(p, d, R, scratch);
   stamp(p, 15);
-  // The last workgroup to finish ends the launch's epoch.
-  wait_stores();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned done =
-        __hip_atomic_fetch_add(d.ctr(kCtrFinished), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (done == (unsigned)G - 1) __hip_atomic_fetch_add(&p.sync[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+
+  finish(d, reinterpret_cast<int *>(scratch));
 }
 
 }  // namespace
 
+// An ordinary launch: the host sizes the grid to what the device holds at
+// once.  Should some workgroups only start after others finished work on
+// another kernel, the waits merely take longer (every one is bounded).
 hipError_t launch_block(const BlockParams &p, int grid, size_t lds, hipStream_t s) {
-  void *args[] = {const_cast<BlockParams *>(&p)};
-  return hipLaunchCooperativeKernel((const void *)block_kernel, dim3(grid), dim3(kThreads), args,
-                                    (unsigned)lds, s);
+  hipLaunchKernelGGL(block_kernel, dim3(grid), dim3(kThreads), lds, s, p);
+  return hipGetLastError();
 }
 
 int block_max_groups_per_cu(size_t lds) {

@@ -9,42 +9,59 @@
 
 namespace mb {
 
-// Per-launch dependency counters (mb_sync.h region at the workspace start):
-// words [0] epoch, [1] abort; then two counter sets of kCtrUp + 2E counters,
-// kCtrStride words apart.
-constexpr int kCtrStride = 16;
-constexpr int kSyncHeader = 64;
+// Cross-workgroup state of one launch, at the workspace start, in 128-byte
+// lines of kLine words so that no two polled words share a line:
+//   line 0            word 1: the abort word (set when a wait timed out)
+//   kNumCtr lines     step counters (kCtr*)
+//   2E lines          up units done per expert, then down units done
+//   kMaxGrid/kFinGroup + 1 lines   workgroups finished per group of
+//                     kFinGroup, then groups finished
+//   kNumEvents x kMaxGrid lines    event flags, one per event and workgroup
+// Everything but the abort word is zero when a launch starts, and the last
+// workgroup to finish sets it back to zero.
+//
+// An event is a counter whose last expected arrival sets every workgroup's
+// flag: waiting workgroups each poll their own line.  (Coherent accesses of
+// one address from hundreds of workgroups queue up behind each other, at
+// tens of nanoseconds each.)
+constexpr int kLine = 32;
+constexpr int kMaxGrid = 1024;  // workgroups of the persistent launch, at most
+constexpr int kFinGroup = 16;
 enum : int {
-  kCtrLogits = 0,    // router tasks done
-  kCtrRoute = 1,     // route tasks done
-  kCtrPool = 2,      // pooler tiles complete
-  kCtrPrenorm = 3,   // pre-norm rows done
-  kCtrFin = 4,       // finalize tasks done
-  kCtrUnpool = 5,    // unpooler tiles complete
-  kCtrFinished = 6,  // workgroups finished
-  kCtrUp = 8,        // [E] up tasks done per expert, then [E] down tasks done
+  kCtrLogits = 0,   // event: experts whose logits are written
+  kCtrRoute = 1,    // event: route tasks done
+  kCtrPool = 2,     // event: pooler tiles complete
+  kCtrPrenorm = 3,  // event: pre-norm rows done
+  kCtrFin = 4,      // event: finalize tasks done
+  kCtrUnpool = 5,   // unpooler tiles complete
+  kNumEvents = 5,   // counters 0 .. kNumEvents-1 are events
+  kNumCtr = 8,
 };
+__host__ __device__ inline size_t sync_line_ctr(int i) { return 1 + (size_t)i; }
+__host__ __device__ inline size_t sync_line_up(int E, int e) { return sync_line_ctr(kNumCtr) + e; }
+__host__ __device__ inline size_t sync_line_down(int E, int e) { return sync_line_up(E, E) + e; }
+__host__ __device__ inline size_t sync_line_fin(int E, int g) { return sync_line_down(E, E) + g; }
+__host__ __device__ inline size_t sync_line_flag(int E, int ev, int wg) {
+  return sync_line_fin(E, kMaxGrid / kFinGroup + 1) + (size_t)ev * kMaxGrid + wg;
+}
+inline size_t sync_words(int E) { return sync_line_flag(E, kNumEvents, 0) * kLine; }
+
 constexpr int kFinChunk = 512;  // features per finalize task
 constexpr int kBlockMaxExperts = 256;  // larger expert counts use the per-step kernels
 constexpr int kTimelineSlots = 16;
+constexpr int kBlockGroupsPerCu = 3;  // resident workgroups per CU (one wave per SIMD each)
 
-// Router hidden slice width (a multiple of 256, at most H) so that a router
-// task does about 16K fp64 multiply-adds, and the slice count.
-inline int router_slice(int b, int H) {
-  int sw = 16384 / b;
-  sw = (sw / 256) * 256;
-  if (sw < 256) sw = 256;
-  return sw > H ? H : sw;
-}
-inline int router_slices(int b, int H) { return (H + router_slice(b, H) - 1) / router_slice(b, H); }
+constexpr int kBlockWaves = 4;      // waves per workgroup
+constexpr int kRouterRowBlock = 16;  // rows per router task
 
-inline size_t sync_words(int E) { return kSyncHeader + 2 * (size_t)(kCtrUp + 2 * E) * kCtrStride; }
+// Order keys a wave ranks: the expert count rounded up to a multiple of 8.
+__host__ __device__ inline int rank_span(int E) { return (E + 7) & ~7; }
 
 struct BlockParams {
   int b, H, P, I, E, k, scoring;
   float mult, div_eps, route_scale, norm_eps;
   // task counts (0 = step absent) and step switches
-  int rslices, rslice;             // router hidden slices
+  int n_logit_producers;           // router tasks to wait for (0: logits given)
   int n_router, n_route, n_pool, n_prenorm, n_fin, n_unpool, n_boundary;
   int pool_ks, unpool_ks, n_pool_tiles, n_unpool_tiles, h_producers;
   int has_up, needs_routing, routing_out, route_given, logits_in;
@@ -63,7 +80,7 @@ struct BlockParams {
   float *wts;
   uint16_t *h, *moe_out, *u;
   // workspace
-  double *logit_part;
+  float *logits_f;  // the router's fp32 logits
   float *pool_part, *unpool_part, *y, *ssq;
   uint16_t *act;
   unsigned *pool_cnt, *unpool_cnt, *sync;
@@ -79,6 +96,9 @@ struct RouteLds {
   int *act;    // [E]
   int *nact;   // [1]
   int *red;    // [8] scan scratch
+  unsigned long long *rank;  // [kBlockWaves][E] candidate order keys of a wave's row
+  int *slot_id;              // [kBlockWaves][kMaxTopK] a wave's chosen experts
+  float *slot_sc;            // [kBlockWaves][kMaxTopK] and their scores
   unsigned long long *bits;  // [E * ceil(b/64)]
 };
 
@@ -86,7 +106,8 @@ __host__ __device__ inline size_t align16(size_t v) { return (v + 15) & ~(size_t
 
 __host__ __device__ inline size_t route_lds_bytes(int b, int k, int E) {
   const size_t R = (size_t)b * k, W = (size_t)(b + 63) / 64;
-  return align16(R * 4) * 3 + align16((E + 1) * 4) + align16(E * 4) + 16 + 32 + align16(E * W * 8);
+  return align16(R * 4) * 3 + align16((E + 1) * 4) + align16(E * 4) + 16 + 32 +
+         (size_t)kBlockWaves * (rank_span(E) * 8 + kMaxTopK * 8) + align16(E * W * 8);
 }
 
 __device__ inline RouteLds route_lds(const BlockParams &p, unsigned char *base) {
@@ -107,13 +128,31 @@ __device__ inline RouteLds route_lds(const BlockParams &p, unsigned char *base) 
   o += 16;
   r.red = reinterpret_cast<int *>(base + o);
   o += 32;
+  r.rank = reinterpret_cast<unsigned long long *>(base + o);
+  o += (size_t)kBlockWaves * rank_span(p.E) * 8;
+  r.slot_id = reinterpret_cast<int *>(base + o);
+  o += kBlockWaves * kMaxTopK * 4;
+  r.slot_sc = reinterpret_cast<float *>(base + o);
+  o += kBlockWaves * kMaxTopK * 4;
   r.bits = reinterpret_cast<unsigned long long *>(base + o);
   (void)W;
   return r;
 }
 
-// Scratch LDS the phases need beyond the routing state.
-constexpr size_t kBlockScratchBytes = 4 * 4 * 64 * 16 + 64;
+// Activation staging of the expert units: per wave, kStageSlots chunks of
+// kStageRows rows x 128 bf16, rows kStageRowBytes apart (16 bytes of padding
+// spread the rows over the LDS banks).
+constexpr int kStageRows = 8;
+constexpr int kStageSlots = 4;
+constexpr int kStageRowBytes = 272;
+constexpr int kStageWaveBytes = kStageSlots * kStageRows * kStageRowBytes;
+
+// Scratch LDS the phases need beyond the routing state: the projection
+// partials and flag (16 KB + 64 bytes), or the staging of the expert units
+// (never live at the same time).
+constexpr size_t kProjScratchBytes = 4 * 4 * 64 * 16 + 64;
+constexpr size_t kBlockScratchBytes =
+    kProjScratchBytes > (size_t)kBlockWaves * kStageWaveBytes ? kProjScratchBytes : (size_t)kBlockWaves * kStageWaveBytes;
 
 hipError_t launch_block(const BlockParams &p, int grid, size_t lds, hipStream_t s);
 int block_max_groups_per_cu(size_t lds);

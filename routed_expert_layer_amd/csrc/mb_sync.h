@@ -45,6 +45,30 @@ __device__ __forceinline__ void st_co4(rsrc_t r, uint32_t off, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kCoherent);
 }
 
+// Streaming (non-temporal) buffer loads of weights.  An offset at or above
+// kOob lies outside every resource made by make_rsrc: the load reads no
+// memory and returns zeros (buffer range checking), which lets loops issue
+// padding loads without branches.
+constexpr int kNonTemporal = 2;  // nt
+constexpr uint32_t kOob = 0x80000000u;
+
+__device__ __forceinline__ u32x4_t ld_nt16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal));
+}
+// Plain (cached) buffer loads of data no other workgroup writes in the launch.
+__device__ __forceinline__ u32x4_t ld_b128(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2_t ld_b64(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t ld_b32(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t ld_b8(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 constexpr unsigned kSpinLimit = 1u << 21;  // polls before a wait gives up
