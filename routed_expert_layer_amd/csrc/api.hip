@@ -25,7 +25,7 @@ Layout layout_of(const mb_dims &d) {
   // Words the kernels leave at zero after every call come first, at offsets
   // that depend only on H and P, so one workspace serves calls of any row
   // count.
-  L.sync = take(sync_words(d.experts) * 4);
+  L.sync = take(sync_words(d.experts, kMaxRows) * 4);
   L.pool_cnt = take((P / 16) * 4);
   L.unpool_cnt = take((H / 16) * 4);
   L.logits = take(b * E * 4);
@@ -232,8 +232,12 @@ BlockParams base_params(const mb_dims &d, const mb_weights *w, void *ws) {
   return p;
 }
 
-int split_for(int ntiles, int nchunks, int grid) {
-  int ks = ntiles > 0 ? grid / ntiles : 1;
+// Split-K factor of a projection with `ntiles` 16-feature tiles over
+// `nchunks` 32-element chunks: as many splits as the `slots` workgroups not
+// taken by the phase's other tasks allow (each workgroup then runs at most
+// one task of the phase), at most kMaxSplitK, and at least 16 chunks each.
+int split_for(int ntiles, int nchunks, int slots) {
+  int ks = ntiles > 0 ? slots / ntiles : 1;
   if (ks > kMaxSplitK) ks = kMaxSplitK;
   while (ks > 1 && nchunks / ks < 16) --ks;
   return ks < 1 ? 1 : ks;
@@ -254,7 +258,7 @@ struct Steps {
 // kernels instead.
 int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   *used = false;
-  if (p.E > kBlockMaxExperts) return MB_OK;
+  if (p.E > kBlockMaxExperts || p.H > 1024 * kBoundGroups) return MB_OK;
   const size_t route_bytes = route_lds_bytes(p.b, p.k, p.E);
   const size_t lds = route_bytes + kBlockScratchBytes;
   if (lds > 64 * 1024) return MB_OK;
@@ -264,24 +268,31 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   int grid = cus * (occ < kBlockGroupsPerCu ? occ : kBlockGroupsPerCu);
   if (grid > kMaxGrid) grid = kMaxGrid;
   p.lds_route_bytes = (int)route_bytes;
-  p.pool_ks = split_for(p.P / 16, p.H / 32, grid);
-  p.unpool_ks = split_for(p.H / 16, p.P / 32, grid);
+  const int n_router = st.router ? p.E * ((p.b + kRouterRowBlock - 1) / kRouterRowBlock) : 0;
+  const int n_fin = st.experts ? p.b * ((p.P + kFinChunk - 1) / kFinChunk) : 0;
+  const int n_boundary = st.unpool ? p.b : 0;
+  const int n_prenorm = (st.pool && p.pre_norm_w) ? p.b : 0;
+  const bool needs_routing = st.experts || st.routing_out;
+  // Route tasks (4 rows each) publish ids and weights for every workgroup's
+  // grouping.  (Every workgroup routing every row itself costs each of them
+  // b/4 rows one after another.)
+  const int n_route = (needs_routing && !st.route_given) ? (p.b + 3) / 4 : 0;
+  p.pool_ks = split_for(p.P / 16, p.H / 32, grid - n_router - n_route - n_prenorm);
+  p.unpool_ks = split_for(p.H / 16, p.P / 32, grid - n_fin - n_boundary);
   p.n_pool_tiles = p.P / 16;
-  p.needs_routing = (st.experts || st.routing_out) ? 1 : 0;
+  p.needs_routing = needs_routing ? 1 : 0;
   p.routing_out = st.routing_out ? 1 : 0;
   p.route_given = st.route_given ? 1 : 0;
-  p.n_router = st.router ? p.E * ((p.b + kRouterRowBlock - 1) / kRouterRowBlock) : 0;
+  p.n_router = n_router;
   p.n_logit_producers = p.n_router;
-  const bool few_rows = (long)p.b * p.E <= 4096;
-  p.n_route = (p.needs_routing && !st.route_given && !few_rows) ? (p.b + 3) / 4 : 0;
+  p.n_route = n_route;
   p.n_pool = st.pool ? (p.P / 16) * p.pool_ks : 0;
-  p.n_prenorm = (st.pool && p.pre_norm_w) ? p.b : 0;
+  p.n_prenorm = n_prenorm;
   p.h_producers = st.pool ? (p.pre_norm_w ? p.b : p.P / 16) : 0;
   p.has_up = st.experts ? 1 : 0;
-  p.n_fin = st.experts ? p.b * ((p.P + kFinChunk - 1) / kFinChunk) : 0;
+  p.n_fin = n_fin;
   p.n_unpool = st.unpool ? (p.H / 16) * p.unpool_ks : 0;
-  p.n_unpool_tiles = st.unpool ? p.H / 16 : 0;
-  p.n_boundary = st.unpool ? p.b : 0;
+  p.n_boundary = n_boundary;
   MB_HIP(launch_block(p, grid, lds, s));
   *used = true;
   return MB_OK;

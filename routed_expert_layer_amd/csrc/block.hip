@@ -50,13 +50,14 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / MB_WAVE;
 static_assert(kWaves == kBlockWaves, "routing LDS is laid out per wave");
+static_assert(kRouterRowBlock == kWaves, "a router task gives each wave one row");
 constexpr int kPoolMG = 4;      // 16-row groups per projection pass
 constexpr int kRing = 4;        // 128-element weight chunks a wave keeps in flight
 static_assert(kRing == 4, "one 16-byte scale load covers four chunks");
 constexpr int kProjBatch = 8;   // 32-element projection chunks a wave requests at once
-constexpr int kRouterBatch = 8;  // router loads a thread requests at once
+constexpr int kRouterBatch = 16;  // router loads a thread requests at once
 constexpr int kRankBatch = 8;    // order keys a lane reads at once
-constexpr int kBoundBatch = 4;   // boundary elements groups a thread requests at once
+constexpr int kBoundBatch = 4;   // pre-norm element groups a thread requests at once
 
 // A value the wave holds in every lane (LDS reads, the wave index), moved to
 // a scalar register so that addresses and resources built from it are too.
@@ -77,11 +78,12 @@ struct Deps {
 
   __device__ unsigned *line(size_t i) const { return s + i * kLine; }
   __device__ unsigned *abort_word() const { return s + 1; }
-  __device__ unsigned *ctr(int i) const { return line(sync_line_ctr(i)); }
+  __device__ unsigned *ctr(int i, int rep = 0) const { return line(sync_line_ctr(i, rep)); }
+  // The copy of counter i that this workgroup (or wave: index w) polls.
+  __device__ unsigned *mine(int i, int w) const { return ctr(i, w % replicas(i)); }
   __device__ unsigned *up(int e) const { return line(sync_line_up(E, e)); }
   __device__ unsigned *down(int e) const { return line(sync_line_down(E, e)); }
-  __device__ unsigned *fin(int g) const { return line(sync_line_fin(E, g)); }
-  __device__ unsigned *flag(int ev, int wg) const { return line(sync_line_flag(E, ev, wg)); }
+  __device__ unsigned *logits(int rb) const { return line(sync_line_logits(E, rb)); }
 };
 
 __device__ __forceinline__ unsigned atomic_inc(unsigned *c) {
@@ -97,6 +99,14 @@ __device__ __forceinline__ void signal(unsigned *c) {
   wait_stores();
   __syncthreads();
   if (threadIdx.x == 0) atomic_inc(c);
+}
+
+// Workgroup: every wave's coherent stores complete, then one increment of
+// every copy of step counter i.
+__device__ __forceinline__ void signal_step(const Deps &d, int i) {
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x < replicas(i)) atomic_inc(d.ctr(i, threadIdx.x));
 }
 
 // One wave: its coherent stores complete, then one increment.
@@ -115,13 +125,6 @@ __device__ __forceinline__ bool last_arrival(unsigned *c, unsigned of, int *flag
   const bool last = *flag != 0;
   __syncthreads();
   return last;
-}
-
-// Workgroup: one arrival at event ev, which expects `of`; the last arrival
-// sets every workgroup's flag.
-__device__ __forceinline__ void arrive(const Deps &d, int ev, unsigned of, int *flag) {
-  if (!last_arrival(d.ctr(ev), of, flag)) return;
-  for (int g = threadIdx.x; g < (int)gridDim.x; g += kThreads) store_co(d.flag(ev, g), 1u);
 }
 
 // One wave polls, each lane its own word, until every lane's has reached
@@ -151,49 +154,38 @@ __device__ __forceinline__ void wait_ge(const Deps &d, const unsigned *c, unsign
   __syncthreads();
 }
 
-// One wave / the workgroup waits for event ev (skipped when it has no
-// arrivals to wait for).
-__device__ __forceinline__ void wave_wait_event(const Deps &d, int ev, int arrivals) {
-  if (arrivals > 0) poll_ge(d, d.flag(ev, blockIdx.x), 1u);
+// Workgroup / one wave waits until step counter i reached `target`.
+__device__ __forceinline__ void wait_step(const Deps &d, int i, int target) {
+  wait_ge(d, d.mine(i, blockIdx.x), (unsigned)target);
 }
-__device__ __forceinline__ void wait_event(const Deps &d, int ev, int arrivals) {
-  if (arrivals == 0) return;
-  if (threadIdx.x < MB_WAVE) poll_ge(d, d.flag(ev, blockIdx.x), 1u);
-  __syncthreads();
+__device__ __forceinline__ void wave_wait_step(const Deps &d, int i, int target) {
+  if (target > 0) poll_ge(d, d.mine(i, blockIdx.x * kWaves + threadIdx.x / MB_WAVE), (unsigned)target);
 }
 
-// The end of a workgroup: count it finished (per group of kFinGroup, then
-// groups); the last workgroup sets the launch state back to zero for the
-// next launch (every other workgroup has finished all its waits).
-__device__ __forceinline__ void finish(const Deps &d, int *flag) {
-  const int G = gridDim.x, ngroups = (G + kFinGroup - 1) / kFinGroup;
+// The end of a workgroup: count it finished; the last workgroup sets the
+// launch state back to zero for the next launch (every other workgroup has
+// finished all its waits).
+__device__ __forceinline__ void finish(const Deps &d, int nrb, int *flag) {
   wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const int grp = blockIdx.x / kFinGroup;
-    const unsigned gsize = (unsigned)min(kFinGroup, G - grp * kFinGroup);
-    bool last = false;
-    if (atomic_inc(d.fin(grp)) == gsize - 1u) last = atomic_inc(d.fin(kMaxGrid / kFinGroup)) == (unsigned)ngroups - 1u;
-    *flag = last;
-  }
+  if (threadIdx.x == 0) *flag = atomic_inc(d.ctr(kCtrFinished)) == gridDim.x - 1u;
   __syncthreads();
   if (!*flag) return;
-  for (int i = threadIdx.x; i < kNumCtr; i += kThreads) store_co(d.ctr(i), 0u);
+  for (int i = threadIdx.x; i < kNumCtr * kReplicas; i += kThreads)
+    if (i % kReplicas < replicas(i / kReplicas)) store_co(d.ctr(i / kReplicas, i % kReplicas), 0u);
   for (int e = threadIdx.x; e < d.E; e += kThreads) {
     store_co(d.up(e), 0u);
     store_co(d.down(e), 0u);
   }
-  for (int g = threadIdx.x; g < ngroups; g += kThreads) store_co(d.fin(g), 0u);
-  if (threadIdx.x == 0) store_co(d.fin(kMaxGrid / kFinGroup), 0u);
-  for (int i = threadIdx.x; i < kNumEvents * G; i += kThreads) store_co(d.flag(i / G, i % G), 0u);
+  for (int rb = threadIdx.x; rb < nrb; rb += kThreads) store_co(d.logits(rb), 0u);
 }
 
 // Tracing: workgroup thread 0 stamps the 100 MHz real-time counter at the
 // start (slot 0), when it enters its first task of each step (router 1,
 // route 2, pool 3, prenorm 4, finalize 8, unpool 9, boundary 10), when its
 // routing state is ready (5), when its waves start (6) and finish (11) their
-// expert units, and at the end (15); inside the steps: router task done (7),
-// logits event seen (12), logits staged (13), rows routed (14).
+// expert units, and at the end (15); inside the steps: logits seen by a
+// route task (12), its rows routed (14), routes seen by the workgroup (13).
 __device__ __forceinline__ void stamp(const BlockParams &p, int slot) {
   if (p.timeline && threadIdx.x == 0) {
     asm volatile("" ::: "memory");
@@ -204,29 +196,29 @@ __device__ __forceinline__ void stamp(const BlockParams &p, int slot) {
 
 // ---------------------------------------------------------------- router
 
-// Logits of expert e for a block of kRouterRowBlock rows, in fp64 (bf16 x
-// fp32 products are exact in fp64), rounded once to fp32.  Thread (row r,
-// part q) adds the products of hidden elements 4q + 64i .. +3 in order; the
-// 16 parts of a row are then added in part order through LDS (no cross-lane
-// shuffles, whose dependent chains are slow).
+// Logits of expert e for a block of kRouterRowBlock (4) rows, in fp64 (bf16 x
+// fp32 products are exact in fp64), rounded once to fp32.  Wave r takes row
+// r; its lane q adds the products of hidden elements 4q + 256i .. +3 in
+// order, requesting kRouterBatch of them at once; the 64 lane sums of a row
+// are then added through LDS in a fixed order (16 groups of 4, then the 16
+// group sums), with no cross-lane shuffles.
 __device__ __forceinline__ void router_task(const BlockParams &p, const Deps &d, int task,
                                             unsigned char *lds) {
   const int nrb = (p.b + kRouterRowBlock - 1) / kRouterRowBlock;
   const int e = task / nrb, t0 = (task % nrb) * kRouterRowBlock;
-  const int r = threadIdx.x / 16, q = threadIdx.x % 16;
+  const int r = threadIdx.x / MB_WAVE, q = threadIdx.x % MB_WAVE;
   const int t = t0 + r;
-  double *red = reinterpret_cast<double *>(lds);  // [kRouterRowBlock][16]
-  int *flag = reinterpret_cast<int *>(lds + kRouterRowBlock * 16 * sizeof(double));
+  double *red = reinterpret_cast<double *>(lds);  // [kRouterRowBlock][64], then [kRouterRowBlock][16]
   // Padding elements (past H, or rows past b) load zeros and add nothing.
   double acc = 0.0;
   const rsrc_t rw = make_rsrc(p.router_w + (size_t)e * p.H), rx = make_rsrc(p.x);
   const uint32_t xrow = t < p.b ? (uint32_t)t * (uint32_t)p.H * 2u : kOob;
-  for (int h0 = 4 * q; h0 < p.H; h0 += 64 * kRouterBatch) {
+  for (int h0 = 4 * q; h0 < p.H; h0 += 256 * kRouterBatch) {
     f32x4_t w[kRouterBatch];
     u32x2_t xv[kRouterBatch];
 #pragma unroll
     for (int u = 0; u < kRouterBatch; ++u) {
-      const uint32_t h = (uint32_t)(h0 + 64 * u);
+      const uint32_t h = (uint32_t)(h0 + 256 * u);
       const bool in = h < (uint32_t)p.H;
       w[u] = __builtin_bit_cast(f32x4_t, ld_b128(rw, in ? h * 4 : kOob));
       xv[u] = ld_b64(rx, in ? xrow + h * 2 : kOob);
@@ -241,13 +233,19 @@ __device__ __forceinline__ void router_task(const BlockParams &p, const Deps &d,
   }
   red[threadIdx.x] = acc;
   __syncthreads();
+  if (threadIdx.x < kRouterRowBlock * 16) {
+    const double *g = red + (threadIdx.x / 16) * MB_WAVE + (threadIdx.x % 16) * 4;
+    red[kRouterRowBlock * MB_WAVE + threadIdx.x] = ((g[0] + g[1]) + g[2]) + g[3];
+  }
+  __syncthreads();
   if (threadIdx.x < kRouterRowBlock && t0 + (int)threadIdx.x < p.b) {
-    double v = red[threadIdx.x * 16];
-    for (int i = 1; i < 16; ++i) v += red[threadIdx.x * 16 + i];
+    const double *g = red + kRouterRowBlock * MB_WAVE + threadIdx.x * 16;
+    double v = g[0];
+    for (int i = 1; i < 16; ++i) v += g[i];
     const size_t te = (size_t)(t0 + threadIdx.x) * p.E + e;
     st_co4(make_rsrc(p.logits_f), (uint32_t)(te * 4), __float_as_uint((float)v));
   }
-  arrive(d, kCtrLogits, (unsigned)p.n_logit_producers, flag);
+  signal(d.logits(t0 / kRouterRowBlock));
 }
 
 // ---------------------------------------------------------------- routing
@@ -348,12 +346,10 @@ __device__ __forceinline__ void route_one(const BlockParams &p, const RouteLds &
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-// Rows t_begin..t_end-1, one per wave in turn: logits from `lg` (LDS
-// [rows][E], row t_begin first) when given, else from global; results to LDS
-// and, when `out`, to the outputs.
+// Rows t_begin..t_end-1, one per wave in turn, from their fp32 logits; the
+// ids and weights go to LDS.
 template <int PER>
-__device__ __forceinline__ void route_rows(const BlockParams &p, const RouteLds &R, const float *lg,
-                                           int t_begin, int t_end, bool out) {
+__device__ __forceinline__ void route_rows(const BlockParams &p, const RouteLds &R, int t_begin, int t_end) {
   const int lane = threadIdx.x % MB_WAVE;
   const rsrc_t rl = make_rsrc(p.logits_f);
   for (int t = t_begin + threadIdx.x / MB_WAVE; t < t_end; t += kWaves) {
@@ -361,8 +357,7 @@ __device__ __forceinline__ void route_rows(const BlockParams &p, const RouteLds 
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = lane + MB_WAVE * i;
-      l[i] = 0.f;
-      if (e < p.E) l[i] = lg ? lg[(size_t)(t - t_begin) * p.E + e] : logit_of(p, rl, t, e);
+      l[i] = e < p.E ? logit_of(p, rl, t, e) : 0.f;
     }
     int id;
     float w;
@@ -370,20 +365,15 @@ __device__ __forceinline__ void route_rows(const BlockParams &p, const RouteLds 
     if (lane < p.k) {
       R.ids[t * p.k + lane] = id;
       R.w[t * p.k + lane] = w;
-      if (out) {
-        p.ids[(size_t)t * p.k + lane] = id;
-        p.wts[(size_t)t * p.k + lane] = w;
-      }
     }
   }
 }
 
-__device__ __forceinline__ void route_dispatch(const BlockParams &p, const RouteLds &R, const float *lg,
-                                               int t0, int t1, bool out) {
+__device__ __forceinline__ void route_dispatch(const BlockParams &p, const RouteLds &R, int t0, int t1) {
   // The host sends larger expert counts to the per-step kernels.
-  if (p.E <= 64) route_rows<1>(p, R, lg, t0, t1, out);
-  else if (p.E <= 128) route_rows<2>(p, R, lg, t0, t1, out);
-  else route_rows<4>(p, R, lg, t0, t1, out);
+  if (p.E <= 64) route_rows<1>(p, R, t0, t1);
+  else if (p.E <= 128) route_rows<2>(p, R, t0, t1);
+  else route_rows<4>(p, R, t0, t1);
 }
 
 // Exclusive prefix sum over the workgroup of one value per thread, in a fixed
@@ -477,11 +467,12 @@ __device__ __forceinline__ void group_routes(const BlockParams &p, const RouteLd
 // Route task (many rows): rows 4 task .. +3, one per wave; their ids and
 // weights go out coherently for every workgroup's grouping.
 __device__ __forceinline__ void route_task(const BlockParams &p, const Deps &d, const RouteLds &R,
-                                           int task, unsigned char *lds) {
-  int *flag = reinterpret_cast<int *>(lds);
-  wait_event(d, kCtrLogits, p.n_logit_producers);
+                                           int task) {
+  if (p.n_logit_producers > 0) wait_ge(d, d.logits(task), (unsigned)p.E);
+  stamp(p, 12);
   const int t0 = task * kWaves, t1 = min(p.b, t0 + kWaves);
-  route_dispatch(p, R, nullptr, t0, t1, false);
+  route_dispatch(p, R, t0, t1);
+  stamp(p, 14);
   __syncthreads();
   const rsrc_t ri = make_rsrc(p.ids), rw = make_rsrc(p.wts);
   for (int i = threadIdx.x; i < (t1 - t0) * p.k; i += kThreads) {
@@ -496,12 +487,11 @@ __device__ __forceinline__ void route_task(const BlockParams &p, const Deps &d, 
       p.logits[(size_t)t * p.E + e] = logit_of(p, rl, t, e);
     }
   }
-  arrive(d, kCtrRoute, (unsigned)p.n_route, flag);
+  signal_step(d, kCtrRoute);
 }
 
 // The routing state a workgroup needs before its first expert unit.
-__device__ __forceinline__ void prepare_routing(const BlockParams &p, const Deps &d, const RouteLds &R,
-                                                unsigned char *scratch) {
+__device__ __forceinline__ void prepare_routing(const BlockParams &p, const Deps &d, const RouteLds &R) {
   const bool out = p.routing_out && blockIdx.x == 0;
   if (p.route_given) {
     // From the caller (mb_experts).
@@ -516,37 +506,12 @@ __device__ __forceinline__ void prepare_routing(const BlockParams &p, const Deps
     __syncthreads();
     return;
   }
-  if (p.n_route == 0) {
-    // Few rows: every workgroup routes every row from logits staged in LDS.
-    wait_event(d, kCtrLogits, p.n_logit_producers);
-    stamp(p, 12);
-    float *lg = reinterpret_cast<float *>(scratch);
-    const rsrc_t rl = make_rsrc(p.logits_f);
-    const int n = p.b * p.E;
-    for (int i0 = threadIdx.x; i0 < n; i0 += kThreads * 4) {
-      float v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = min(i0 + kThreads * u, n - 1);
-        v[u] = logit_of(p, rl, i / p.E, i % p.E);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (i0 + kThreads * u < n) lg[i0 + kThreads * u] = v[u];
-    }
-    __syncthreads();
-    stamp(p, 13);
-    route_dispatch(p, R, lg, 0, p.b, out);
-    stamp(p, 14);
-    if (out && p.logits && !p.logits_in)
-      for (int i = threadIdx.x; i < p.b * p.E; i += kThreads) p.logits[i] = lg[i];
-  } else {
-    wait_event(d, kCtrRoute, p.n_route);
-    const rsrc_t ri = make_rsrc(p.ids), rw = make_rsrc(p.wts);
-    for (int i = threadIdx.x; i < p.b * p.k; i += kThreads) {
-      R.ids[i] = (int)ld_co4(ri, (uint32_t)(i * 4));
-      R.w[i] = __uint_as_float(ld_co4(rw, (uint32_t)(i * 4)));
-    }
+  wait_step(d, kCtrRoute, p.n_route);
+  stamp(p, 13);
+  const rsrc_t ri = make_rsrc(p.ids), rw = make_rsrc(p.wts);
+  for (int i = threadIdx.x; i < p.b * p.k; i += kThreads) {
+    R.ids[i] = (int)ld_co4(ri, (uint32_t)(i * 4));
+    R.w[i] = __uint_as_float(ld_co4(rw, (uint32_t)(i * 4)));
   }
   __syncthreads();
   group_routes(p, R, out);
@@ -565,15 +530,18 @@ __device__ __forceinline__ int *proj_flag(unsigned char *lds) {
 // of activations share each weight fragment (weights in the MFMA A operand,
 // activations in B, read coherently when another workgroup of the launch
 // wrote them: kCoherentA).  The first weight chunks are requested
-// before waiting for `a` (event wait_ev); padding chunks and rows load zeros.
-// With ks_count > 1 the fp32 partials go to `part` and the last split to
-// finish (tile counter) adds them in split order and writes bf16.  Returns
-// true in the workgroup that completed the tile.
+// before waiting for `a` (step counter wait_ev), unless wait_first puts the
+// wait before everything; padding chunks and rows load zeros.
+// With ks_count > 1 the fp32 partials go to `part`; then either the consumer
+// adds them (defer_sum) or the last split to finish (tile counter) adds them
+// in split order and writes bf16.  Returns true when the task's part of the
+// output is complete: always with defer_sum, else in the workgroup that
+// completed the tile.
 template <bool kCoherentA>
 __device__ __forceinline__ bool proj_task(const Deps &d, const uint16_t *a, const uint16_t *w, uint16_t *out,
                                           int rows, int n_out, int kdim, int ks_count, float *part,
-                                          unsigned *tile_ctr, int wait_ev, int wait_arrivals, int task,
-                                          unsigned char *lds) {
+                                          unsigned *tile_ctr, int wait_ev, int wait_arrivals, bool wait_first,
+                                          int task, bool defer_sum, unsigned char *lds) {
   const Lane L;
   const int nchunks = kdim / 32;
   const int cpw = (nchunks + ks_count - 1) / ks_count;
@@ -585,6 +553,10 @@ __device__ __forceinline__ bool proj_task(const Deps &d, const uint16_t *a, cons
                rp = make_rsrc(part);
   const uint32_t wrow = (uint32_t)((L.r16 * kdim + 8 * L.g) * 2);
   bool waited = false;
+  if (wait_first) {
+    wait_step(d, wait_ev, wait_arrivals);
+    waited = true;
+  }
   for (int rb = 0; rb < rows; rb += 16 * kPoolMG) {
     f32x4_t acc[kPoolMG];
 #pragma unroll
@@ -597,7 +569,7 @@ __device__ __forceinline__ bool proj_task(const Deps &d, const uint16_t *a, cons
         wv[u] = ld_nt16(rw, cc < c_end ? wrow + (uint32_t)cc * 64u : kOob);
       }
       if (!waited) {
-        wait_event(d, wait_ev, wait_arrivals);
+        wait_step(d, wait_ev, wait_arrivals);
         waited = true;
         if (c >= c_end) break;
       }
@@ -634,7 +606,7 @@ __device__ __forceinline__ bool proj_task(const Deps &d, const uint16_t *a, cons
     }
     __syncthreads();
   }
-  if (ks_count == 1) return true;
+  if (ks_count == 1 || defer_sum) return true;
   if (!last_arrival(&tile_ctr[tile], (unsigned)ks_count, flag)) return false;
   for (int idx = threadIdx.x; idx < rows * 4; idx += kThreads) {
     const int t = idx / 4, n0 = tile * 16 + 4 * (idx % 4);
@@ -658,9 +630,8 @@ __device__ __forceinline__ bool proj_task(const Deps &d, const uint16_t *a, cons
 // +1, kBoundBatch of them per request.
 __device__ __forceinline__ void prenorm_task(const BlockParams &p, const Deps &d, int t,
                                              unsigned char *lds) {
-  wait_event(d, kCtrPool, p.n_pool_tiles);
+  wait_step(d, kCtrPool, p.n_pool_tiles);
   float *red = reinterpret_cast<float *>(lds);
-  int *flag = reinterpret_cast<int *>(lds + 64);
   const rsrc_t rh = make_rsrc(p.h + (size_t)t * p.P), rw = make_rsrc(p.pre_norm_w);
   const uint32_t P2 = (uint32_t)p.P * 2;
   float ss = 0.f;
@@ -696,7 +667,7 @@ __device__ __forceinline__ void prenorm_task(const BlockParams &p, const Deps &d
       st_co4(rh, (uint32_t)i * 2, pack_bf16x2(a * wa, b * wb));
     }
   }
-  arrive(d, kCtrPrenorm, (unsigned)p.n_prenorm, flag);
+  signal_step(d, kCtrPrenorm);
 }
 
 // ---------------------------------------------------------------- experts
@@ -713,7 +684,8 @@ __device__ __forceinline__ void prenorm_task(const BlockParams &p, const Deps &d
 // of four chunks come in one 16-byte load per tile row (vec_scales: nch a
 // multiple of 4), else one 4-byte load per chunk; the lane keeps byte l / 16.
 //
-// Activations: lane l loads 16 bytes (elements 8 (l % 16) ..) of the chunk of
+// Activations (written by other workgroups of the launch, so read
+// coherently): lane l loads 16 bytes (elements 8 (l % 16) ..) of the chunk of
 // pass row l / 16 (a_ld0) and of row 4 + l / 16 (a_ld1, when `two`); kOob
 // gives zeros.  They go to the wave's staging LDS (la) and come back in MFMA
 // layout: lane l reads row l % 8.  Only the pass's rows are requested, in
@@ -747,8 +719,8 @@ __device__ __forceinline__ void mx_pair(rsrc_t rw, uint32_t o0, uint32_t o1, rsr
 #pragma unroll
   for (int r = 0; r < kRing; ++r) {
     const bool ok = r < nch;
-    A0[r] = ld_b128(ra, ok ? a_ld0 + 256u * r : kOob);
-    A1[r] = two ? ld_b128(ra, ok ? a_ld1 + 256u * r : kOob) : u32x4_t{0, 0, 0, 0};
+    A0[r] = ld_co16(ra, ok ? a_ld0 + 256u * r : kOob);
+    A1[r] = two ? ld_co16(ra, ok ? a_ld1 + 256u * r : kOob) : u32x4_t{0, 0, 0, 0};
   }
   d0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
   d1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -783,8 +755,8 @@ __device__ __forceinline__ void mx_pair(rsrc_t rw, uint32_t o0, uint32_t o1, rsr
       const bool ok = cn < nch;
       W0[r] = ld_b128(rw, ok ? o0 + 64u * cn : kOob);
       W1[r] = ld_b128(rw, ok ? o1 + 64u * cn : kOob);
-      A0[r] = ld_b128(ra, ok ? a_ld0 + 256u * cn : kOob);
-      A1[r] = two ? ld_b128(ra, ok ? a_ld1 + 256u * cn : kOob) : u32x4_t{0, 0, 0, 0};
+      A0[r] = ld_co16(ra, ok ? a_ld0 + 256u * cn : kOob);
+      A1[r] = two ? ld_co16(ra, ok ? a_ld1 + 256u * cn : kOob) : u32x4_t{0, 0, 0, 0};
     }
     asm volatile("" ::: "memory");
     S0 = N0;
@@ -819,7 +791,7 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
     mx_pair(rw, rg * (P / 2) + 16 * g, ru * (P / 2) + 16 * g, rs, rg * (P / 32), ru * (P / 32), nch % 4 == 0, nch,
             rh, a0, a1, mrows > 4, la, gs, us, [&]() {
               if (!h_ready) {
-                wave_wait_event(d, p.pre_norm_w ? kCtrPrenorm : kCtrPool, p.h_producers);
+                wave_wait_step(d, p.pre_norm_w ? kCtrPrenorm : kCtrPool, p.h_producers);
                 h_ready = true;
               }
             });
@@ -892,7 +864,9 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
 
 // moe_out[t, p] = bf16(sum_j (w_j / sqrt(ss_j / P + eps)) y_j[p] * w_post[p]),
 // ss_j = the route's per-tile sums of squares added in tile order, for the
-// task's features of row t; waits for the down units of the row's experts.
+// task's features of row t (4 per thread); waits for the down units of the
+// row's experts.  The post-norm weights are requested before the wait, the
+// route rows of y and the sums of squares together after it.
 __device__ __forceinline__ void fin_task(const BlockParams &p, const Deps &d, const RouteLds &R,
                                          int task, unsigned char *lds) {
   const int P = p.P, k = p.k;
@@ -901,41 +875,45 @@ __device__ __forceinline__ void fin_task(const BlockParams &p, const Deps &d, co
   const int t = task / chunks, p_begin = (task % chunks) * kFinChunk;
   const int p_end = min(P, p_begin + kFinChunk);
   const int lane = threadIdx.x % MB_WAVE, wave = threadIdx.x / MB_WAVE;
+  const int p4 = p_begin + threadIdx.x * 4;
+  const bool mine = p4 < p_end;
+  const u32x2_t pw = ld_b64(make_rsrc(p.post_norm_w), mine ? (uint32_t)p4 * 2 : kOob);
   if (threadIdx.x < MB_WAVE) poll_ge(d, d.down(R.ids[t * k + (lane < k ? lane : 0)]), (unsigned)tiles);
   __syncthreads();
   float *coef = reinterpret_cast<float *>(lds);  // [k]
-  int *flag = reinterpret_cast<int *>(lds + 64 * sizeof(float));
   const rsrc_t rss = make_rsrc(p.ssq), ry = make_rsrc(p.y), ro = make_rsrc(p.moe_out);
+  f32x4_t yv[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    yv[j] = __builtin_bit_cast(
+        f32x4_t, ld_co16(ry, (mine && j < k) ? (uint32_t)(((size_t)(t * k + j) * P + p4) * 4) : kOob));
   for (int j = wave; j < k; j += kWaves) {
     const int r = t * k + j;
-    float s = 0.f;
-    for (int c = lane; c < tiles; c += MB_WAVE)
-      s += __uint_as_float(ld_co4(rss, (uint32_t)(((size_t)r * tiles + c) * 4)));
+    float sv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = lane + MB_WAVE * q;
+      sv[q] = __uint_as_float(ld_co4(rss, c < tiles ? (uint32_t)(((size_t)r * tiles + c) * 4) : kOob));
+    }
+    float s = sv[0] + sv[1] + sv[2] + sv[3];
+    for (int c0 = MB_WAVE * 4; c0 < tiles; c0 += MB_WAVE)
+      s += __uint_as_float(ld_co4(rss, lane + c0 < tiles ? (uint32_t)(((size_t)r * tiles + lane + c0) * 4) : kOob));
     s = wave_sum(s);
     if (lane == 0) coef[j] = R.w[r] * (1.0f / sqrtf(s / (float)P + p.norm_eps));
   }
   __syncthreads();
-  for (int p4 = p_begin + threadIdx.x * 4; p4 < p_end; p4 += kThreads * 4) {
+  if (mine) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < k; j0 += 4) {
-      f32x4_t yv[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = min(j0 + u, k - 1);
-        yv[u] = __builtin_bit_cast(f32x4_t, ld_co16(ry, (uint32_t)(((size_t)(t * k + j) * P + p4) * 4)));
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (j0 + u < k) acc += coef[j0 + u] * yv[u];
-    }
-    const u32x2_t pw = *reinterpret_cast<const u32x2_t *>(p.post_norm_w + p4);
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (j < k) acc += coef[j] * yv[j];
     const float o0 = acc[0] * bf16_bits_to_f32(pw[0] & 0xFFFFu);
     const float o1 = acc[1] * bf16_bits_to_f32(pw[0] >> 16);
     const float o2 = acc[2] * bf16_bits_to_f32(pw[1] & 0xFFFFu);
     const float o3 = acc[3] * bf16_bits_to_f32(pw[1] >> 16);
     st_co8(ro, (uint32_t)(((size_t)t * P + p4) * 2), u32x2_t{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)});
   }
-  arrive(d, kCtrFin, (unsigned)p.n_fin, flag);
+  signal_step(d, kCtrFin);
 }
 
 // ---------------------------------------------------------------- boundary
@@ -948,88 +926,117 @@ __device__ __forceinline__ void unpack4(u32x2_t v, float o[4]) {
 }
 
 // v = RMSNorm_H(u) * w_pff; stream = fp32(stream + g * v) (one fma);
-// x_next = bf16(RMSNorm_H(stream) * w_in), for row t.  Thread i takes
-// elements 4i + 1024 m .. +3; each pass requests kBoundBatch of them at once.
+// x_next = bf16(RMSNorm_H(stream) * w_in), for row t.  Thread i holds
+// elements 4i + 1024 m .. +3 (m < NG, so H <= 1024 NG)
+// in registers across the passes; the gate and the stream are requested
+// before the wait.  With a split unpooler, u = bf16 of its fp32 partials added here in
+// split order (and written out).
+template <int NG>
 __device__ __forceinline__ void boundary_task(const BlockParams &p, const Deps &d, int t,
                                               unsigned char *lds) {
-  wait_ge(d, d.ctr(kCtrUnpool), (unsigned)p.n_unpool_tiles);
   float *red = reinterpret_cast<float *>(lds);
   const int H = p.H;
-  const rsrc_t ru = make_rsrc(p.u + (size_t)t * H), rg = make_rsrc(p.gate);
-  const rsrc_t rs = make_rsrc(p.stream + (size_t)t * H);
   const uint32_t H2 = (uint32_t)H * 2;
+  const rsrc_t rg = make_rsrc(p.gate), rs = make_rsrc(p.stream + (size_t)t * H);
+  u32x2_t gv[NG], fv[NG], wv[NG];
+  f32x4_t sv[NG];
+#pragma unroll
+  for (int m = 0; m < NG; ++m) {
+    const uint32_t h = (uint32_t)(4 * threadIdx.x + 1024 * m);
+    const bool in = h * 2 < H2;
+    gv[m] = ld_b64(rg, in ? h * 2 : kOob);
+    sv[m] = __builtin_bit_cast(f32x4_t, ld_b128(rs, in ? h * 4 : kOob));
+  }
+  wait_step(d, kCtrUnpool, p.n_unpool);
+  // The norm weights are needed only after the first reduction.
+#pragma unroll
+  for (int m = 0; m < NG; ++m) {
+    const uint32_t h = (uint32_t)(4 * threadIdx.x + 1024 * m);
+    const bool in = h * 2 < H2;
+    fv[m] = p.ffn_norm_w ? ld_b64(make_rsrc(p.ffn_norm_w), in ? h * 2 : kOob) : u32x2_t{0x3F803F80u, 0x3F803F80u};
+  }
+  u32x2_t uv[NG];
+  if (p.unpool_ks > 1) {
+    // u = bf16(sum of the split partials in split order).
+    const rsrc_t rp = make_rsrc(p.unpool_part), ru = make_rsrc(p.u + (size_t)t * H);
+    // Partials requested QB splits at a time (fewer when the row is wide).
+    constexpr int QB = NG <= 4 ? 2 : 1;
+    f32x4_t av[NG];
+    for (int q0 = 0; q0 < p.unpool_ks; q0 += QB) {
+      f32x4_t pv[QB][NG];
+#pragma unroll
+      for (int q = 0; q < QB; ++q)
+#pragma unroll
+        for (int m = 0; m < NG; ++m) {
+          const uint32_t h = (uint32_t)(4 * threadIdx.x + 1024 * m);
+          const bool in = h * 2 < H2 && q0 + q < p.unpool_ks;
+          pv[q][m] = __builtin_bit_cast(
+              f32x4_t, ld_co16(rp, in ? (uint32_t)((((size_t)(q0 + q) * p.b + t) * H + h) * 4) : kOob));
+        }
+#pragma unroll
+      for (int m = 0; m < NG; ++m) {
+        av[m] = q0 == 0 ? pv[0][m] : av[m] + pv[0][m];
+#pragma unroll
+        for (int q = 1; q < QB; ++q)
+          if (q0 + q < p.unpool_ks) av[m] += pv[q][m];
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NG; ++m) {
+      const uint32_t h = (uint32_t)(4 * threadIdx.x + 1024 * m);
+      uv[m] = u32x2_t{pack_bf16x2(av[m][0], av[m][1]), pack_bf16x2(av[m][2], av[m][3])};
+      if (h * 2 < H2) st_co8(ru, h * 2, uv[m]);
+    }
+  } else {
+    const rsrc_t ru = make_rsrc(p.u + (size_t)t * H);
+#pragma unroll
+    for (int m = 0; m < NG; ++m) {
+      const uint32_t h = (uint32_t)(4 * threadIdx.x + 1024 * m);
+      uv[m] = ld_co8(ru, h * 2 < H2 ? h * 2 : kOob);
+    }
+  }
   float ss = 0.f;
-  for (int h0 = 4 * threadIdx.x; h0 < H; h0 += 1024 * kBoundBatch) {
-    u32x2_t uv[kBoundBatch];
 #pragma unroll
-    for (int m = 0; m < kBoundBatch; ++m) {
-      const uint32_t off = (uint32_t)(h0 + 1024 * m) * 2;
-      uv[m] = ld_co8(ru, off < H2 ? off : kOob);
-    }
+  for (int m = 0; m < NG; ++m) {
+    float v[4];
+    unpack4(uv[m], v);
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
 #pragma unroll
-    for (int m = 0; m < kBoundBatch; ++m) {
-      float v[4];
-      unpack4(uv[m], v);
-      ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
-    }
+  for (int m = 0; m < NG; ++m) {
+    const uint32_t h = (uint32_t)(4 * threadIdx.x + 1024 * m);
+    const bool in = h * 2 < H2;
+    wv[m] = p.next_norm_w ? ld_b64(make_rsrc(p.next_norm_w), in ? h * 2 : kOob) : u32x2_t{0x3F803F80u, 0x3F803F80u};
   }
   ss = block_sum(ss, red);
   const float rsu = 1.0f / sqrtf(ss / (float)H + p.norm_eps);
   float s2 = 0.f;
-  for (int h0 = 4 * threadIdx.x; h0 < H; h0 += 1024 * kBoundBatch) {
-    u32x2_t uv[kBoundBatch], gv[kBoundBatch], fv[kBoundBatch];
-    f32x4_t sv[kBoundBatch];
 #pragma unroll
-    for (int m = 0; m < kBoundBatch; ++m) {
-      const uint32_t h = (uint32_t)(h0 + 1024 * m);
-      const bool in = h * 2 < H2;
-      uv[m] = ld_co8(ru, in ? h * 2 : kOob);
-      gv[m] = ld_b64(rg, in ? h * 2 : kOob);
-      sv[m] = __builtin_bit_cast(f32x4_t, ld_b128(rs, in ? h * 4 : kOob));
-      fv[m] = p.ffn_norm_w ? ld_b64(make_rsrc(p.ffn_norm_w), in ? h * 2 : kOob) : u32x2_t{0x3F803F80u, 0x3F803F80u};
-    }
+  for (int m = 0; m < NG; ++m) {
+    float v[4], gg[4], wf[4];
+    unpack4(uv[m], v);
+    unpack4(gv[m], gg);
+    unpack4(fv[m], wf);
 #pragma unroll
-    for (int m = 0; m < kBoundBatch; ++m) {
-      const int h = h0 + 1024 * m;
-      if (h >= H) break;
-      float v[4], gg[4], wf[4];
-      unpack4(uv[m], v);
-      unpack4(gv[m], gg);
-      unpack4(fv[m], wf);
-      f32x4_t sn = sv[m];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float vn = v[i] * rsu * wf[i];
-        sn[i] = fmaf(gg[i], vn, sn[i]);
-        s2 += sn[i] * sn[i];
-      }
-      *reinterpret_cast<f32x4_t *>(p.stream + (size_t)t * H + h) = sn;
-      sv[m] = sn;
+    for (int i = 0; i < 4; ++i) {
+      const float vn = v[i] * rsu * wf[i];
+      sv[m][i] = fmaf(gg[i], vn, sv[m][i]);
+      s2 += sv[m][i] * sv[m][i];
     }
   }
   s2 = block_sum(s2, red);
   const float rss = 1.0f / sqrtf(s2 / (float)H + p.norm_eps);
-  for (int h0 = 4 * threadIdx.x; h0 < H; h0 += 1024 * kBoundBatch) {
-    f32x4_t sv[kBoundBatch];
-    u32x2_t wv[kBoundBatch];
 #pragma unroll
-    for (int m = 0; m < kBoundBatch; ++m) {
-      const uint32_t h = (uint32_t)(h0 + 1024 * m);
-      const bool in = h * 2 < H2;
-      sv[m] = __builtin_bit_cast(f32x4_t, ld_b128(rs, in ? h * 4 : kOob));
-      wv[m] = p.next_norm_w ? ld_b64(make_rsrc(p.next_norm_w), in ? h * 2 : kOob) : u32x2_t{0x3F803F80u, 0x3F803F80u};
-    }
-#pragma unroll
-    for (int m = 0; m < kBoundBatch; ++m) {
-      const int h = h0 + 1024 * m;
-      if (h >= H) break;
-      float wi[4];
-      unpack4(wv[m], wi);
-      const f32x4_t sn = sv[m];
-      *reinterpret_cast<u32x2_t *>(p.x_next + (size_t)t * H + h) =
-          u32x2_t{pack_bf16x2(sn[0] * rss * wi[0], sn[1] * rss * wi[1]),
-                  pack_bf16x2(sn[2] * rss * wi[2], sn[3] * rss * wi[3])};
-    }
+  for (int m = 0; m < NG; ++m) {
+    const int h = 4 * threadIdx.x + 1024 * m;
+    if (h >= H) break;
+    float wi[4];
+    unpack4(wv[m], wi);
+    const f32x4_t sn = sv[m];
+    *reinterpret_cast<f32x4_t *>(p.stream + (size_t)t * H + h) = sn;
+    *reinterpret_cast<u32x2_t *>(p.x_next + (size_t)t * H + h) =
+        u32x2_t{pack_bf16x2(sn[0] * rss * wi[0], sn[1] * rss * wi[1]),
+                pack_bf16x2(sn[2] * rss * wi[2], sn[3] * rss * wi[3])};
   }
   __syncthreads();
 }
@@ -1067,11 +1074,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       if (step == 1) {
         router_task(p, d, i, scratch);
       } else if (step == 2) {
-        route_task(p, d, R, i, scratch);
+        route_task(p, d, R, i);
       } else if (step == 3) {
-        if (proj_task<false>(d, p.x, p.pool_w, p.h, p.b, p.P, p.H, p.pool_ks, p.pool_part, p.pool_cnt, 0, 0, i,
-                      scratch))
-          arrive(d, kCtrPool, (unsigned)p.n_pool_tiles, proj_flag(scratch));
+        if (proj_task<false>(d, p.x, p.pool_w, p.h, p.b, p.P, p.H, p.pool_ks, p.pool_part, p.pool_cnt, 0, 0, false,
+                             i, false, scratch))
+          signal_step(d, kCtrPool);
       } else {
         prenorm_task(p, d, i, scratch);
       }
@@ -1080,7 +1087,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
   // 2. Routing state (workgroup 0 also writes the routing outputs).
   if (p.needs_routing && (p.has_up || (p.routing_out && blockIdx.x == 0))) {
-    prepare_routing(p, d, R, scratch);
+    prepare_routing(p, d, R);
     stamp(p, 5);
   }
 
@@ -1121,17 +1128,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       if (step == 8) {
         fin_task(p, d, R, i, scratch);
       } else if (step == 9) {
-        if (proj_task<true>(d, p.moe_out, p.unpool_w, p.u, p.b, p.H, p.P, p.unpool_ks, p.unpool_part,
-                      p.unpool_cnt, kCtrFin, p.n_fin, i, scratch))
-          signal(d.ctr(kCtrUnpool));
+        proj_task<true>(d, p.moe_out, p.unpool_w, p.u, p.b, p.H, p.P, p.unpool_ks, p.unpool_part, p.unpool_cnt,
+                         kCtrFin, p.n_fin, false, i, true, scratch);
+        signal_step(d, kCtrUnpool);
       } else {
-        boundary_task(p, d, i, scratch);
+        if (p.H <= 4096) boundary_task<4>(p, d, i, scratch);
+        else boundary_task<kBoundGroups>(p, d, i, scratch);
       }
     }
   }
   stamp(p, 15);
 
-  finish(d, reinterpret_cast<int *>(scratch));
+  finish(d, (p.b + kRouterRowBlock - 1) / kRouterRowBlock, reinterpret_cast<int *>(scratch));
 }
 
 }  // namespace

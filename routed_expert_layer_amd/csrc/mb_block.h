@@ -9,50 +9,55 @@
 
 namespace mb {
 
+constexpr int kBlockWaves = 4;      // waves per workgroup
+constexpr int kRouterRowBlock = 4;   // rows per router task (one wave each)
+
 // Cross-workgroup state of one launch, at the workspace start, in 128-byte
-// lines of kLine words so that no two polled words share a line:
-//   line 0            word 1: the abort word (set when a wait timed out)
-//   kNumCtr lines     step counters (kCtr*)
-//   2E lines          up units done per expert, then down units done
-//   kMaxGrid/kFinGroup + 1 lines   workgroups finished per group of
-//                     kFinGroup, then groups finished
-//   kNumEvents x kMaxGrid lines    event flags, one per event and workgroup
+// lines of kLine words so that no two counters share a line:
+//   line 0      word 1: the abort word (set when a wait timed out)
+//   kNumCtr x kReplicas lines   step counters (kCtr*), each in replicas(i)
+//               copies
+//   2E lines    up units done per expert, then down units done
+//   ceil(b/4) lines   router tasks done per block of kRouterRowBlock rows
 // Everything but the abort word is zero when a launch starts, and the last
-// workgroup to finish sets it back to zero.
-//
-// An event is a counter whose last expected arrival sets every workgroup's
-// flag: waiting workgroups each poll their own line.  (Coherent accesses of
-// one address from hundreds of workgroups queue up behind each other, at
-// tens of nanoseconds each.)
+// workgroup to finish sets it back to zero.  A producer adds one to every
+// copy of a step counter after its coherent stores completed (one atomic per
+// lane of one instruction); a consumer polls the copy its workgroup index
+// selects.  Increments of one address are serialized, and polls of an
+// address delay the increments to it, so a counter many workgroups wait for
+// has more copies, one with many producers fewer.
 constexpr int kLine = 32;
+constexpr int kReplicas = 16;
 constexpr int kMaxGrid = 1024;  // workgroups of the persistent launch, at most
-constexpr int kFinGroup = 16;
 enum : int {
-  kCtrLogits = 0,   // event: experts whose logits are written
-  kCtrRoute = 1,    // event: route tasks done
-  kCtrPool = 2,     // event: pooler tiles complete
-  kCtrPrenorm = 3,  // event: pre-norm rows done
-  kCtrFin = 4,      // event: finalize tasks done
-  kCtrUnpool = 5,   // unpooler tiles complete
-  kNumEvents = 5,   // counters 0 .. kNumEvents-1 are events
+  kCtrLogits = 0,    // (unused: router tasks count per row block)
+  kCtrRoute = 1,     // route tasks done
+  kCtrPool = 2,      // pooler tiles complete
+  kCtrPrenorm = 3,   // pre-norm rows done
+  kCtrFin = 4,       // finalize tasks done
+  kCtrUnpool = 5,    // unpooler tasks done
+  kCtrFinished = 6,  // workgroups finished
   kNumCtr = 8,
 };
-__host__ __device__ inline size_t sync_line_ctr(int i) { return 1 + (size_t)i; }
-__host__ __device__ inline size_t sync_line_up(int E, int e) { return sync_line_ctr(kNumCtr) + e; }
-__host__ __device__ inline size_t sync_line_down(int E, int e) { return sync_line_up(E, E) + e; }
-__host__ __device__ inline size_t sync_line_fin(int E, int g) { return sync_line_down(E, E) + g; }
-__host__ __device__ inline size_t sync_line_flag(int E, int ev, int wg) {
-  return sync_line_fin(E, kMaxGrid / kFinGroup + 1) + (size_t)ev * kMaxGrid + wg;
+// Copies of step counter i: the pooler, route and finalize counters are
+// awaited by every workgroup or wave; the unpooler's by the boundary tasks.
+__host__ __device__ constexpr int replicas(int i) {
+  return (i == kCtrRoute || i == kCtrPool || i == kCtrPrenorm || i == kCtrFin) ? kReplicas : 1;
 }
-inline size_t sync_words(int E) { return sync_line_flag(E, kNumEvents, 0) * kLine; }
+__host__ __device__ inline size_t sync_line_ctr(int i, int rep) { return 1 + (size_t)i * kReplicas + rep; }
+__host__ __device__ inline size_t sync_line_up(int E, int e) { return sync_line_ctr(kNumCtr, 0) + e; }
+__host__ __device__ inline size_t sync_line_down(int E, int e) { return sync_line_up(E, E) + e; }
+__host__ __device__ inline size_t sync_line_logits(int E, int rb) { return sync_line_down(E, E) + rb; }
+inline size_t sync_words(int E, int rows) {
+  return sync_line_logits(E, (rows + kRouterRowBlock - 1) / kRouterRowBlock) * kLine;
+}
 
 constexpr int kFinChunk = 512;  // features per finalize task
 constexpr int kBlockMaxExperts = 256;  // larger expert counts use the per-step kernels
 constexpr int kTimelineSlots = 16;
 constexpr int kBlockGroupsPerCu = 3;  // resident workgroups per CU (one wave per SIMD each)
 
-constexpr int kBlockWaves = 4;      // waves per workgroup
-constexpr int kRouterRowBlock = 16;  // rows per router task
+constexpr int kBoundGroups = 8;      // 4-element groups per thread of a boundary row (H <= 8192)
 
 // Order keys a wave ranks: the expert count rounded up to a multiple of 8.
 __host__ __device__ inline int rank_span(int E) { return (E + 7) & ~7; }
@@ -63,7 +68,7 @@ struct BlockParams {
   // task counts (0 = step absent) and step switches
   int n_logit_producers;           // router tasks to wait for (0: logits given)
   int n_router, n_route, n_pool, n_prenorm, n_fin, n_unpool, n_boundary;
-  int pool_ks, unpool_ks, n_pool_tiles, n_unpool_tiles, h_producers;
+  int pool_ks, unpool_ks, n_pool_tiles, h_producers;
   int has_up, needs_routing, routing_out, route_given, logits_in;
   int lds_route_bytes;
   // inputs
