@@ -277,7 +277,11 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   // grouping.  (Every workgroup routing every row itself costs each of them
   // b/4 rows one after another.)
   const int n_route = (needs_routing && !st.route_given) ? (p.b + 3) / 4 : 0;
-  p.pool_ks = split_for(p.P / 16, p.H / 32, grid - n_router - n_route - n_prenorm);
+  // The pooler is not split: its output is needed only once routing is
+  // done, and a split adds a partial store, a last-arrival round trip and a
+  // partial load before h is complete.
+  p.pool_ks = 1;
+  (void)n_prenorm;
   p.unpool_ks = split_for(p.H / 16, p.P / 32, grid - n_fin - n_boundary);
   p.n_pool_tiles = p.P / 16;
   p.needs_routing = needs_routing ? 1 : 0;

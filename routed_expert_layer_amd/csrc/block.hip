@@ -22,13 +22,14 @@
 //        boundary (row)                    stream, x_next
 //
 // Workgroup w takes workgroup tasks w, w + G, ... of lists 1 and 4; wave v
-// (global index) takes units v, v + 4G, ... of list 3.  A task or unit waits
+// (global index) takes up units v, v + 4G, ..., then down units v, v + 4G, ...  A task or unit waits
 // only for the work whose output it reads: routing for the logits (or the
 // route tasks), up for the pooler (or pre-norm), down for the up units of its
 // expert, finalize for the down units of its row's experts, unpool for the
-// finalize tasks, boundary for the unpool tiles.  Waits that every workgroup
-// makes are events (a flag per workgroup, set by the last arrival); the
-// others poll counters.  Every dependency points to earlier work in this
+// finalize tasks, boundary for the unpool tasks.  Producers add to counters
+// after their coherent stores completed and consumers poll them (mb_block.h:
+// the layout, and copies of widely awaited counters).  Every dependency points
+// to earlier work in this
 // order and the grid is what the device holds at once, so the earliest
 // unfinished work can always run and the launch completes; every wait is also
 // bounded.
@@ -184,7 +185,8 @@ __device__ __forceinline__ void finish(const Deps &d, int nrb, int *flag) {
 // start (slot 0), when it enters its first task of each step (router 1,
 // route 2, pool 3, prenorm 4, finalize 8, unpool 9, boundary 10), when its
 // routing state is ready (5), when its waves start (6) and finish (11) their
-// expert units, and at the end (15); inside the steps: logits seen by a
+// expert units, and at the end (15); inside the steps: pool task done (7),
+// logits seen by a
 // route task (12), its rows routed (14), routes seen by the workgroup (13).
 __device__ __forceinline__ void stamp(const BlockParams &p, int slot) {
   if (p.timeline && threadIdx.x == 0) {
@@ -1079,6 +1081,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         if (proj_task<false>(d, p.x, p.pool_w, p.h, p.b, p.P, p.H, p.pool_ks, p.pool_part, p.pool_cnt, 0, 0, false,
                              i, false, scratch))
           signal_step(d, kCtrPool);
+        stamp(p, 7);
       } else {
         prenorm_task(p, d, i, scratch);
       }
@@ -1099,10 +1102,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const int nact = uniform(*R.nact);
     const int nU = nact * (p.I / 16), nD = nact * (p.P / 32);
     bool h_ready = p.h_producers == 0;
-    for (int u = blockIdx.x * kWaves + uniform(threadIdx.x / MB_WAVE); u < nU + nD; u += GW) {
-      if (u < nU) up_unit(p, d, R, u, h_ready, stage);
-      else down_unit(p, d, R, u - nU, stage);
-    }
+    // Up units and down units are dealt separately, so a wave's down units
+    // belong to the experts of its own up units (with as many tiles per
+    // expert): they wait on waves that started with them.  (Waves that
+    // reach the memory system later -- the later workgroups on a CU -- finish
+    // their up units later.)
+    const int gw = blockIdx.x * kWaves + uniform(threadIdx.x / MB_WAVE);
+    for (int u = gw; u < nU; u += GW) up_unit(p, d, R, u, h_ready, stage);
+    for (int u = gw; u < nD; u += GW) down_unit(p, d, R, u, stage);
     __syncthreads();
     stamp(p, 11);
   }
