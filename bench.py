@@ -16,6 +16,7 @@ oracle's rate on a bounded sample of the same workload (cpu_baseline).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -41,6 +42,33 @@ def algorithmic_bytes(d, n_active: int, norm_weights=(False, False, False)) -> i
     pre, pff, win = norm_weights
     return (n_active * expert + E * H * 4 + E * 4 + 2 * P * H * 2 + P * 2 * (1 + pre)
             + H * 2 * (1 + pff + win) + b * H * 2 + 2 * b * H * 4 + b * H * 2 + b * k * 8)
+
+
+# Sources whose change invalidates a stored traffic measurement of the block
+# kernel (its code and its launch configuration).
+KERNEL_SOURCES = ("block.hip", "api.hip", "mb_block.h", "mb_device.h", "mb_sync.h", "mb_internal.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_kernel_c1_traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "routed_expert_layer_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per launch of the block kernel from the committed counter
+    summary, if it was taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            kv = dict(line.split(":", 1) for line in fh if ":" in line)
+        if kv.get("kernel_source_sha256", "").strip() != kernel_source_hash():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(blk, seconds: float) -> dict:
@@ -76,7 +104,14 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=len(WEIGHT_SEEDS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
+                    help="first run one plain elementwise copy of MB MiB (reads and writes MB MiB), "
+                         "the reference kernel for scaling the HBM byte counters")
+    ap.add_argument("--print-source-hash", action="store_true")
     args = ap.parse_args()
+    if args.print_source_hash:
+        print(kernel_source_hash())
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
               "(the block has no multi-GPU path in this build)", file=sys.stderr)
@@ -115,6 +150,17 @@ def main() -> int:
     nw = (blocks[0].pre_norm_w is not None, blocks[0].ffn_norm_w is not None,
           blocks[0].next_norm_w is not None)
     b_alg = float(np.mean([algorithmic_bytes(d, a, nw) for a in actives]))
+
+    if args.copy_probe > 0:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(f"[bench] copy probe: one elementwise kernel reading and writing {args.copy_probe} MiB",
+              file=sys.stderr, flush=True)
+        del src, dst
 
     S = len(weights)
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
@@ -170,12 +216,12 @@ def main() -> int:
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "mb_moe_block",
+            "kernel": "block_kernel (the single launch of mb_moe_block)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": stored_traffic(),
         },
         "cpu_baseline": cpu,
     }

@@ -1045,19 +1045,35 @@ __device__ __forceinline__ void boundary_task(const BlockParams &p, const Deps &
 
 // ---------------------------------------------------------------- the kernel
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void block_kernel(BlockParams p) {
+// The parameters, read through a pointer to the kernel-argument segment that
+// each phase (and each task of a loop) obtains afresh: the compiler cannot
+// merge the loads of a field across phases, so no field stays live in a
+// register from the first phase to the last.  (Kept live, the fields overflow
+// the scalar registers into vector registers and scratch memory, and the
+// scratch lines are written back to HBM at the end of every launch.)
+__device__ __forceinline__ const BlockParams &kparams() {
+  const __attribute__((address_space(4))) BlockParams *pp =
+      (const __attribute__((address_space(4))) BlockParams *)(__builtin_amdgcn_kernarg_segment_ptr());
+  asm volatile("" : "+s"(pp));
+  return *(const BlockParams *)pp;
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void block_kernel(BlockParams p_arg) {
   extern __shared__ __align__(16) unsigned char lds[];
-  stamp(p, 0);
-  const Deps d{p.sync, p.E};
-  const RouteLds R = route_lds(p, lds);
-  unsigned char *scratch = lds + p.lds_route_bytes;
+  (void)p_arg;  // read through kparams()
+  stamp(kparams(), 0);
   const int G = gridDim.x;
 
   // 1. Workgroup tasks before routing.
   {
-    const int nR = p.n_router, nRT = p.n_route, nP = p.n_pool, nPN = p.n_prenorm;
     int last = -1;
-    for (int j = blockIdx.x; j < nR + nRT + nP + nPN; j += G) {
+    for (int j = blockIdx.x;; j += G) {
+      const BlockParams &p = kparams();
+      const Deps d{p.sync, p.E};
+      const RouteLds R = route_lds(p, lds);
+      unsigned char *scratch = lds + p.lds_route_bytes;
+      const int nR = p.n_router, nRT = p.n_route, nP = p.n_pool, nPN = p.n_prenorm;
+      if (j >= nR + nRT + nP + nPN) break;
       int step, i = j;
       if (i < nR) {
         step = 1;
@@ -1089,13 +1105,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
 
   // 2. Routing state (workgroup 0 also writes the routing outputs).
+  {
+  const BlockParams &p = kparams();
+  const Deps d{p.sync, p.E};
+  const RouteLds R = route_lds(p, lds);
   if (p.needs_routing && (p.has_up || (p.routing_out && blockIdx.x == 0))) {
     prepare_routing(p, d, R);
     stamp(p, 5);
   }
+  }
 
   // 3. Expert units, one wave each.
-  if (p.has_up) {
+  if (kparams().has_up) {
+    const BlockParams &p = kparams();
+    const Deps d{p.sync, p.E};
+    const RouteLds R = route_lds(p, lds);
+    unsigned char *scratch = lds + p.lds_route_bytes;
     stamp(p, 6);
     const int GW = G * kWaves;
     unsigned char *stage = scratch + (threadIdx.x / MB_WAVE) * kStageWaveBytes;
@@ -1116,9 +1141,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
   // 4. Workgroup tasks after the experts.
   {
-    const int nF = p.n_fin, nN = p.n_unpool, nB = p.n_boundary;
     int last = -1;
-    for (int j = blockIdx.x; j < nF + nN + nB; j += G) {
+    for (int j = blockIdx.x;; j += G) {
+      const BlockParams &p = kparams();
+      const Deps d{p.sync, p.E};
+      const RouteLds R = route_lds(p, lds);
+      unsigned char *scratch = lds + p.lds_route_bytes;
+      const int nF = p.n_fin, nN = p.n_unpool, nB = p.n_boundary;
+      if (j >= nF + nN + nB) break;
       int step, i = j;
       if (i < nF) {
         step = 8;
@@ -1144,9 +1174,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       }
     }
   }
+  {
+  const BlockParams &p = kparams();
+  const Deps d{p.sync, p.E};
+  unsigned char *scratch = lds + p.lds_route_bytes;
   stamp(p, 15);
-
   finish(d, (p.b + kRouterRowBlock - 1) / kRouterRowBlock, reinterpret_cast<int *>(scratch));
+  }
 }
 
 }  // namespace
