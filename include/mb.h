@@ -136,9 +136,9 @@ typedef struct {
   uint16_t *h;         /* bf16 [b, P] */
   uint16_t *moe_out;   /* bf16 [b, P] */
   uint16_t *u;         /* bf16 [b, H] */
-  int64_t *timeline;   /* tracing: int64 [2048][16]; workgroup w writes the
+  int64_t *timeline;   /* tracing: int64 [1024][32]; workgroup w writes the
                           100 MHz real-time counter at its phase boundaries
-                          into row w (slots 0..13; the per-step path leaves it
+                          into row w (slots 0..21; the per-step path leaves it
                           untouched) */
 } mb_block_taps;
 

@@ -73,6 +73,14 @@ struct Lane {
 
 // ---------------------------------------------------------------- dependencies
 
+// threadIdx.x, read afresh at each use: values derived from it are then not
+// kept in registers from one phase of the kernel to the next.
+__device__ __forceinline__ unsigned tid() {
+  unsigned t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 struct Deps {
   unsigned *s;  // the launch state (layout in mb_block.h)
   int E;
@@ -80,8 +88,9 @@ struct Deps {
   __device__ unsigned *line(size_t i) const { return s + i * kLine; }
   __device__ unsigned *abort_word() const { return s + 1; }
   __device__ unsigned *ctr(int i, int rep = 0) const { return line(sync_line_ctr(i, rep)); }
-  // The copy of counter i that this workgroup (or wave: index w) polls.
-  __device__ unsigned *mine(int i, int w) const { return ctr(i, w % replicas(i)); }
+  // The first stripe of the copy of counter i that this workgroup (or wave:
+  // index w) polls.
+  __device__ unsigned *mine(int i, int w) const { return ctr(i, (w % replicas(i)) * stripes(i)); }
   __device__ unsigned *up(int e) const { return line(sync_line_up(E, e)); }
   __device__ unsigned *down(int e) const { return line(sync_line_down(E, e)); }
   __device__ unsigned *logits(int rb) const { return line(sync_line_logits(E, rb)); }
@@ -99,21 +108,21 @@ __device__ __forceinline__ void store_co(unsigned *w, unsigned v) {
 __device__ __forceinline__ void signal(unsigned *c) {
   wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0) atomic_inc(c);
+  if (tid() == 0) atomic_inc(c);
 }
 
 // Workgroup: every wave's coherent stores complete, then one increment of
-// every copy of step counter i.
+// this workgroup's stripe in every copy of step counter i.
 __device__ __forceinline__ void signal_step(const Deps &d, int i) {
   wait_stores();
   __syncthreads();
-  if (threadIdx.x < replicas(i)) atomic_inc(d.ctr(i, threadIdx.x));
+  if (tid() < replicas(i)) atomic_inc(d.ctr(i, tid() * stripes(i) + (int)(blockIdx.x % stripes(i))));
 }
 
 // One wave: its coherent stores complete, then one increment.
 __device__ __forceinline__ void wave_signal(unsigned *c) {
   wait_stores();
-  if (threadIdx.x % MB_WAVE == 0) atomic_inc(c);
+  if (tid() % MB_WAVE == 0) atomic_inc(c);
 }
 
 // Workgroup: after its coherent stores, add one to counter c; true in the
@@ -121,7 +130,7 @@ __device__ __forceinline__ void wave_signal(unsigned *c) {
 __device__ __forceinline__ bool last_arrival(unsigned *c, unsigned of, int *flag) {
   wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0) *flag = atomic_inc(c) == of - 1u;
+  if (tid() == 0) *flag = atomic_inc(c) == of - 1u;
   __syncthreads();
   const bool last = *flag != 0;
   __syncthreads();
@@ -132,7 +141,7 @@ __device__ __forceinline__ bool last_arrival(unsigned *c, unsigned of, int *flag
 // `target`.  Bounded: on timeout the abort word is raised, and a wait that
 // sees it returns at once, so the launch drains.
 __device__ __forceinline__ void poll_ge(const Deps &d, const unsigned *mine, unsigned target) {
-  const int lane = threadIdx.x % MB_WAVE;
+  const int lane = tid() % MB_WAVE;
   unsigned spins = 0;
   while (true) {
     const unsigned have = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -148,19 +157,44 @@ __device__ __forceinline__ void poll_ge(const Deps &d, const unsigned *mine, uns
   }
 }
 
+// One wave polls the n stripes (consecutive lines from `first`, one per
+// lane) until their sum reached `target`.  Bounded like poll_ge.
+__device__ __forceinline__ void poll_sum_ge(const Deps &d, const unsigned *first, int n, unsigned target) {
+  const int lane = tid() % MB_WAVE;
+  const unsigned *mine = first + (lane < n ? lane : 0) * kLine;
+  unsigned spins = 0;
+  while (true) {
+    const unsigned have = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned sum = 0;
+    for (int l = 0; l < n; ++l) sum += __builtin_amdgcn_readlane(have, l);
+    if (sum >= target) return;
+    if ((++spins & 255u) == 0) {
+      if (__hip_atomic_load(d.abort_word(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
+      if (spins > kSpinLimit) {
+        if (lane == 0) store_co(d.abort_word(), 1u);
+        return;
+      }
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
 // Workgroup wait on one counter.
 __device__ __forceinline__ void wait_ge(const Deps &d, const unsigned *c, unsigned target) {
   if (target == 0) return;
-  if (threadIdx.x < MB_WAVE) poll_ge(d, c, target);
+  if (tid() < MB_WAVE) poll_ge(d, c, target);
   __syncthreads();
 }
 
 // Workgroup / one wave waits until step counter i reached `target`.
 __device__ __forceinline__ void wait_step(const Deps &d, int i, int target) {
-  wait_ge(d, d.mine(i, blockIdx.x), (unsigned)target);
+  if (target == 0) return;
+  if (tid() < MB_WAVE) poll_sum_ge(d, d.mine(i, blockIdx.x), stripes(i), (unsigned)target);
+  __syncthreads();
 }
 __device__ __forceinline__ void wave_wait_step(const Deps &d, int i, int target) {
-  if (target > 0) poll_ge(d, d.mine(i, blockIdx.x * kWaves + threadIdx.x / MB_WAVE), (unsigned)target);
+  if (target > 0)
+    poll_sum_ge(d, d.mine(i, blockIdx.x * kWaves + tid() / MB_WAVE), stripes(i), (unsigned)target);
 }
 
 // The end of a workgroup: count it finished; the last workgroup sets the
@@ -169,16 +203,17 @@ __device__ __forceinline__ void wave_wait_step(const Deps &d, int i, int target)
 __device__ __forceinline__ void finish(const Deps &d, int nrb, int *flag) {
   wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0) *flag = atomic_inc(d.ctr(kCtrFinished)) == gridDim.x - 1u;
+  if (tid() == 0) *flag = atomic_inc(d.ctr(kCtrFinished)) == gridDim.x - 1u;
   __syncthreads();
   if (!*flag) return;
-  for (int i = threadIdx.x; i < kNumCtr * kReplicas; i += kThreads)
-    if (i % kReplicas < replicas(i / kReplicas)) store_co(d.ctr(i / kReplicas, i % kReplicas), 0u);
-  for (int e = threadIdx.x; e < d.E; e += kThreads) {
+  for (int i = tid(); i < kNumCtr * kReplicas; i += kThreads)
+    if (i % kReplicas < replicas(i / kReplicas) * stripes(i / kReplicas))
+      store_co(d.ctr(i / kReplicas, i % kReplicas), 0u);
+  for (int e = tid(); e < d.E; e += kThreads) {
     store_co(d.up(e), 0u);
     store_co(d.down(e), 0u);
   }
-  for (int rb = threadIdx.x; rb < nrb; rb += kThreads) store_co(d.logits(rb), 0u);
+  for (int rb = tid(); rb < nrb; rb += kThreads) store_co(d.logits(rb), 0u);
 }
 
 // Tracing: workgroup thread 0 stamps the 100 MHz real-time counter at the
@@ -186,10 +221,12 @@ __device__ __forceinline__ void finish(const Deps &d, int nrb, int *flag) {
 // route 2, pool 3, prenorm 4, finalize 8, unpool 9, boundary 10), when its
 // routing state is ready (5), when its waves start (6) and finish (11) their
 // expert units, and at the end (15); inside the steps: pool task done (7),
-// logits seen by a
-// route task (12), its rows routed (14), routes seen by the workgroup (13).
+// logits seen by a route task (12), its rows routed (14), routes seen by the
+// workgroup (13), unpool task done (16), boundary's unpooler wait over (17),
+// boundary done (18), finalize's expert wait over (19), wave 0's up units
+// done (20), finalize done (21).
 __device__ __forceinline__ void stamp(const BlockParams &p, int slot) {
-  if (p.timeline && threadIdx.x == 0) {
+  if (p.timeline && tid() == 0) {
     asm volatile("" ::: "memory");
     p.timeline[(size_t)blockIdx.x * kTimelineSlots + slot] = (int64_t)wall_clock64();
     asm volatile("" ::: "memory");
@@ -208,7 +245,7 @@ __device__ __forceinline__ void router_task(const BlockParams &p, const Deps &d,
                                             unsigned char *lds) {
   const int nrb = (p.b + kRouterRowBlock - 1) / kRouterRowBlock;
   const int e = task / nrb, t0 = (task % nrb) * kRouterRowBlock;
-  const int r = threadIdx.x / MB_WAVE, q = threadIdx.x % MB_WAVE;
+  const int r = tid() / MB_WAVE, q = tid() % MB_WAVE;
   const int t = t0 + r;
   double *red = reinterpret_cast<double *>(lds);  // [kRouterRowBlock][64], then [kRouterRowBlock][16]
   // Padding elements (past H, or rows past b) load zeros and add nothing.
@@ -233,18 +270,18 @@ __device__ __forceinline__ void router_task(const BlockParams &p, const Deps &d,
       acc = fma((double)bf16_bits_to_f32(xv[u][1] >> 16), (double)w[u][3], acc);
     }
   }
-  red[threadIdx.x] = acc;
+  red[tid()] = acc;
   __syncthreads();
-  if (threadIdx.x < kRouterRowBlock * 16) {
-    const double *g = red + (threadIdx.x / 16) * MB_WAVE + (threadIdx.x % 16) * 4;
-    red[kRouterRowBlock * MB_WAVE + threadIdx.x] = ((g[0] + g[1]) + g[2]) + g[3];
+  if (tid() < kRouterRowBlock * 16) {
+    const double *g = red + (tid() / 16) * MB_WAVE + (tid() % 16) * 4;
+    red[kRouterRowBlock * MB_WAVE + tid()] = ((g[0] + g[1]) + g[2]) + g[3];
   }
   __syncthreads();
-  if (threadIdx.x < kRouterRowBlock && t0 + (int)threadIdx.x < p.b) {
-    const double *g = red + kRouterRowBlock * MB_WAVE + threadIdx.x * 16;
+  if (tid() < kRouterRowBlock && t0 + (int)tid() < p.b) {
+    const double *g = red + kRouterRowBlock * MB_WAVE + tid() * 16;
     double v = g[0];
     for (int i = 1; i < 16; ++i) v += g[i];
-    const size_t te = (size_t)(t0 + threadIdx.x) * p.E + e;
+    const size_t te = (size_t)(t0 + tid()) * p.E + e;
     st_co4(make_rsrc(p.logits_f), (uint32_t)(te * 4), __float_as_uint((float)v));
   }
   signal(d.logits(t0 / kRouterRowBlock));
@@ -278,7 +315,7 @@ __device__ __forceinline__ unsigned long long order_key(float key, int e) {
 template <int PER>
 __device__ __forceinline__ void route_one(const BlockParams &p, const RouteLds &R, const float (&l)[PER],
                                           int &out_id, float &out_w) {
-  const int lane = threadIdx.x % MB_WAVE, wave = threadIdx.x / MB_WAVE;
+  const int lane = tid() % MB_WAVE, wave = tid() / MB_WAVE;
   unsigned long long *rank = R.rank + (size_t)wave * rank_span(p.E);
   int *slot_id = R.slot_id + wave * kMaxTopK;
   float *slot_sc = R.slot_sc + wave * kMaxTopK;
@@ -352,9 +389,9 @@ __device__ __forceinline__ void route_one(const BlockParams &p, const RouteLds &
 // ids and weights go to LDS.
 template <int PER>
 __device__ __forceinline__ void route_rows(const BlockParams &p, const RouteLds &R, int t_begin, int t_end) {
-  const int lane = threadIdx.x % MB_WAVE;
+  const int lane = tid() % MB_WAVE;
   const rsrc_t rl = make_rsrc(p.logits_f);
-  for (int t = t_begin + threadIdx.x / MB_WAVE; t < t_end; t += kWaves) {
+  for (int t = t_begin + tid() / MB_WAVE; t < t_end; t += kWaves) {
     float l[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -381,7 +418,7 @@ __device__ __forceinline__ void route_dispatch(const BlockParams &p, const Route
 // Exclusive prefix sum over the workgroup of one value per thread, in a fixed
 // order; `total` receives the sum.  `red` holds kWaves ints.
 __device__ __forceinline__ int wg_excl_scan(int v, int *red, int &total) {
-  const int lane = threadIdx.x % MB_WAVE, wave = threadIdx.x / MB_WAVE;
+  const int lane = tid() % MB_WAVE, wave = tid() / MB_WAVE;
   int x = v;
 #pragma unroll
   for (int o = 1; o < MB_WAVE; o <<= 1) {
@@ -407,14 +444,14 @@ __device__ __forceinline__ int wg_excl_scan(int v, int *red, int &total) {
 __device__ __forceinline__ void group_routes(const BlockParams &p, const RouteLds &R, bool out) {
   const int W = (p.b + 63) / 64;
   const int Rn = p.b * p.k;
-  for (int i = threadIdx.x; i < p.E * W; i += kThreads) R.bits[i] = 0ull;
+  for (int i = tid(); i < p.E * W; i += kThreads) R.bits[i] = 0ull;
   __syncthreads();
-  for (int r = threadIdx.x; r < Rn; r += kThreads) {
+  for (int r = tid(); r < Rn; r += kThreads) {
     const int t = r / p.k, e = R.ids[r];
     atomicOr(&R.bits[e * W + t / 64], 1ull << (t & 63));
   }
   __syncthreads();
-  const int e0 = threadIdx.x * 4;
+  const int e0 = tid() * 4;
   int c[4], csum = 0, asum = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -445,7 +482,7 @@ __device__ __forceinline__ void group_routes(const BlockParams &p, const RouteLd
       oc += c[q];
     }
   }
-  if (threadIdx.x == 0) {
+  if (tid() == 0) {
     R.off[p.E] = tot_c;
     *R.nact = tot_a;
     if (out) {
@@ -454,7 +491,7 @@ __device__ __forceinline__ void group_routes(const BlockParams &p, const RouteLd
     }
   }
   __syncthreads();
-  for (int r = threadIdx.x; r < Rn; r += kThreads) {
+  for (int r = tid(); r < Rn; r += kThreads) {
     const int t = r / p.k, e = R.ids[r];
     const unsigned long long *b = R.bits + e * W;
     int rank = 0;
@@ -477,14 +514,14 @@ __device__ __forceinline__ void route_task(const BlockParams &p, const Deps &d, 
   stamp(p, 14);
   __syncthreads();
   const rsrc_t ri = make_rsrc(p.ids), rw = make_rsrc(p.wts);
-  for (int i = threadIdx.x; i < (t1 - t0) * p.k; i += kThreads) {
+  for (int i = tid(); i < (t1 - t0) * p.k; i += kThreads) {
     const int r = t0 * p.k + i;
     st_co4(ri, (uint32_t)(r * 4), (uint32_t)R.ids[r]);
     st_co4(rw, (uint32_t)(r * 4), __float_as_uint(R.w[r]));
   }
   if (p.logits && !p.logits_in) {
     const rsrc_t rl = make_rsrc(p.logits_f);
-    for (int i = threadIdx.x; i < (t1 - t0) * p.E; i += kThreads) {
+    for (int i = tid(); i < (t1 - t0) * p.E; i += kThreads) {
       const int t = t0 + i / p.E, e = i % p.E;
       p.logits[(size_t)t * p.E + e] = logit_of(p, rl, t, e);
     }
@@ -497,21 +534,21 @@ __device__ __forceinline__ void prepare_routing(const BlockParams &p, const Deps
   const bool out = p.routing_out && blockIdx.x == 0;
   if (p.route_given) {
     // From the caller (mb_experts).
-    for (int i = threadIdx.x; i < p.b * p.k; i += kThreads) {
+    for (int i = tid(); i < p.b * p.k; i += kThreads) {
       R.ids[i] = p.ids[i];
       R.w[i] = p.wts[i];
       R.rl[i] = p.route_list[i];
     }
-    for (int i = threadIdx.x; i <= p.E; i += kThreads) R.off[i] = p.offset[i];
-    for (int i = threadIdx.x; i < p.E; i += kThreads) R.act[i] = p.active[i];
-    if (threadIdx.x == 0) *R.nact = *p.n_active;
+    for (int i = tid(); i <= p.E; i += kThreads) R.off[i] = p.offset[i];
+    for (int i = tid(); i < p.E; i += kThreads) R.act[i] = p.active[i];
+    if (tid() == 0) *R.nact = *p.n_active;
     __syncthreads();
     return;
   }
   wait_step(d, kCtrRoute, p.n_route);
   stamp(p, 13);
   const rsrc_t ri = make_rsrc(p.ids), rw = make_rsrc(p.wts);
-  for (int i = threadIdx.x; i < p.b * p.k; i += kThreads) {
+  for (int i = tid(); i < p.b * p.k; i += kThreads) {
     R.ids[i] = (int)ld_co4(ri, (uint32_t)(i * 4));
     R.w[i] = __uint_as_float(ld_co4(rw, (uint32_t)(i * 4)));
   }
@@ -610,7 +647,7 @@ __device__ __forceinline__ bool proj_task(const Deps &d, const uint16_t *a, cons
   }
   if (ks_count == 1 || defer_sum) return true;
   if (!last_arrival(&tile_ctr[tile], (unsigned)ks_count, flag)) return false;
-  for (int idx = threadIdx.x; idx < rows * 4; idx += kThreads) {
+  for (int idx = tid(); idx < rows * 4; idx += kThreads) {
     const int t = idx / 4, n0 = tile * 16 + 4 * (idx % 4);
     f32x4_t part_v[kMaxSplitK];
 #pragma unroll
@@ -624,7 +661,7 @@ __device__ __forceinline__ bool proj_task(const Deps &d, const uint16_t *a, cons
     st_co8(ro, (uint32_t)(((size_t)t * n_out + n0) * 2),
            u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
   }
-  if (threadIdx.x == 0) __hip_atomic_store(&tile_ctr[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid() == 0) __hip_atomic_store(&tile_ctr[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
 }
 
@@ -637,7 +674,7 @@ __device__ __forceinline__ void prenorm_task(const BlockParams &p, const Deps &d
   const rsrc_t rh = make_rsrc(p.h + (size_t)t * p.P), rw = make_rsrc(p.pre_norm_w);
   const uint32_t P2 = (uint32_t)p.P * 2;
   float ss = 0.f;
-  for (int i0 = 2 * threadIdx.x; i0 < p.P; i0 += 512 * kBoundBatch) {
+  for (int i0 = 2 * tid(); i0 < p.P; i0 += 512 * kBoundBatch) {
     uint32_t v[kBoundBatch];
 #pragma unroll
     for (int m = 0; m < kBoundBatch; ++m) {
@@ -652,7 +689,7 @@ __device__ __forceinline__ void prenorm_task(const BlockParams &p, const Deps &d
   }
   ss = block_sum(ss, red);
   const float rs = 1.0f / sqrtf(ss / (float)p.P + p.norm_eps);
-  for (int i0 = 2 * threadIdx.x; i0 < p.P; i0 += 512 * kBoundBatch) {
+  for (int i0 = 2 * tid(); i0 < p.P; i0 += 512 * kBoundBatch) {
     uint32_t v[kBoundBatch], w[kBoundBatch];
 #pragma unroll
     for (int m = 0; m < kBoundBatch; ++m) {
@@ -673,6 +710,19 @@ __device__ __forceinline__ void prenorm_task(const BlockParams &p, const Deps &d
 }
 
 // ---------------------------------------------------------------- experts
+
+// Issue priority of a wave streaming a unit, from its progress: 3 in the
+// first quarter of the chunks down to 0 in the last.  Among waves of equal
+// priority the oldest issues first, which leaves the waves of the youngest
+// workgroups on a CU far behind; ranking by progress lets the waves that are
+// behind catch up, so the units of an expert finish together.
+__device__ __forceinline__ void set_progress_priority(int c, int n) {
+  const int q = (4 * c) / n;
+  if (q <= 0) __builtin_amdgcn_s_setprio(3);
+  else if (q == 1) __builtin_amdgcn_s_setprio(2);
+  else if (q == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
 
 // One wave: D0 = W0 B and D1 = W1 B for two 16-row MXFP4 weight tiles over
 // nch 128-element chunks and up to kStageRows activation rows (bf16).
@@ -701,7 +751,7 @@ __device__ __forceinline__ void mx_pair(rsrc_t rw, uint32_t o0, uint32_t o1, rsr
                                         uint32_t so1, bool vec_scales, int nch, rsrc_t ra, uint32_t a_ld0,
                                         uint32_t a_ld1, bool two, unsigned char *la, f32x4_t &d0, f32x4_t &d1,
                                         Wait wait) {
-  const int lane = threadIdx.x % MB_WAVE, g = lane >> 4;
+  const int lane = tid() % MB_WAVE, g = lane >> 4;
   u32x4_t W0[kRing], W1[kRing], A0[kRing], A1[kRing];
   auto scales = [&](uint32_t so, int c0) {
     if (vec_scales) return ld_b128(rs, c0 < nch ? so + 4u * c0 : kOob);
@@ -729,6 +779,7 @@ __device__ __forceinline__ void mx_pair(rsrc_t rw, uint32_t o0, uint32_t o1, rsr
   const uint32_t st_off = (uint32_t)((lane >> 4) * kStageRowBytes + (lane & 15) * 16);
   const uint32_t rd_off = (uint32_t)((lane & 7) * kStageRowBytes + 64 * g);
   for (int c0 = 0; c0 < nch; c0 += kRing) {
+    set_progress_priority(c0, nch);
     // This round's activations to the staging LDS (one wave's LDS accesses
     // complete in order, so the reads below see them and the next round's
     // stores follow this round's reads).
@@ -771,7 +822,7 @@ __device__ __forceinline__ void mx_pair(rsrc_t rw, uint32_t o0, uint32_t o1, rsr
 // the expert's routes in passes of kStageRows.
 __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, const RouteLds &R, int unit,
                                         bool &h_ready, unsigned char *la) {
-  const int lane = threadIdx.x % MB_WAVE, g = lane >> 4, r16 = lane & 15;
+  const int lane = tid() % MB_WAVE, g = lane >> 4, r16 = lane & 15;
   const int P = p.P, I = p.I;
   const int tiles = I / 16;
   const int a = unit / tiles, tile = unit % tiles;
@@ -816,7 +867,7 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
 // the route's sum of squares over these 32 features.
 __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, const RouteLds &R, int unit,
                                           unsigned char *la) {
-  const int lane = threadIdx.x % MB_WAVE, g = lane >> 4, r16 = lane & 15;
+  const int lane = tid() % MB_WAVE, g = lane >> 4, r16 = lane & 15;
   const int P = p.P, I = p.I;
   const int tiles = P / 32;
   const int a = unit / tiles, tile = unit % tiles;
@@ -876,12 +927,13 @@ __device__ __forceinline__ void fin_task(const BlockParams &p, const Deps &d, co
   const int chunks = (P + kFinChunk - 1) / kFinChunk;
   const int t = task / chunks, p_begin = (task % chunks) * kFinChunk;
   const int p_end = min(P, p_begin + kFinChunk);
-  const int lane = threadIdx.x % MB_WAVE, wave = threadIdx.x / MB_WAVE;
-  const int p4 = p_begin + threadIdx.x * 4;
+  const int lane = tid() % MB_WAVE, wave = tid() / MB_WAVE;
+  const int p4 = p_begin + tid() * 4;
   const bool mine = p4 < p_end;
   const u32x2_t pw = ld_b64(make_rsrc(p.post_norm_w), mine ? (uint32_t)p4 * 2 : kOob);
-  if (threadIdx.x < MB_WAVE) poll_ge(d, d.down(R.ids[t * k + (lane < k ? lane : 0)]), (unsigned)tiles);
+  if (tid() < MB_WAVE) poll_ge(d, d.down(R.ids[t * k + (lane < k ? lane : 0)]), (unsigned)tiles);
   __syncthreads();
+  stamp(p, 19);
   float *coef = reinterpret_cast<float *>(lds);  // [k]
   const rsrc_t rss = make_rsrc(p.ssq), ry = make_rsrc(p.y), ro = make_rsrc(p.moe_out);
   f32x4_t yv[kMaxTopK];
@@ -916,6 +968,7 @@ __device__ __forceinline__ void fin_task(const BlockParams &p, const Deps &d, co
     st_co8(ro, (uint32_t)(((size_t)t * P + p4) * 2), u32x2_t{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)});
   }
   signal_step(d, kCtrFin);
+  stamp(p, 21);
 }
 
 // ---------------------------------------------------------------- boundary
@@ -944,16 +997,17 @@ __device__ __forceinline__ void boundary_task(const BlockParams &p, const Deps &
   f32x4_t sv[NG];
 #pragma unroll
   for (int m = 0; m < NG; ++m) {
-    const uint32_t h = (uint32_t)(4 * threadIdx.x + 1024 * m);
+    const uint32_t h = (uint32_t)(4 * tid() + 1024 * m);
     const bool in = h * 2 < H2;
     gv[m] = ld_b64(rg, in ? h * 2 : kOob);
     sv[m] = __builtin_bit_cast(f32x4_t, ld_b128(rs, in ? h * 4 : kOob));
   }
   wait_step(d, kCtrUnpool, p.n_unpool);
+  stamp(p, 17);
   // The norm weights are needed only after the first reduction.
 #pragma unroll
   for (int m = 0; m < NG; ++m) {
-    const uint32_t h = (uint32_t)(4 * threadIdx.x + 1024 * m);
+    const uint32_t h = (uint32_t)(4 * tid() + 1024 * m);
     const bool in = h * 2 < H2;
     fv[m] = p.ffn_norm_w ? ld_b64(make_rsrc(p.ffn_norm_w), in ? h * 2 : kOob) : u32x2_t{0x3F803F80u, 0x3F803F80u};
   }
@@ -970,7 +1024,7 @@ __device__ __forceinline__ void boundary_task(const BlockParams &p, const Deps &
       for (int q = 0; q < QB; ++q)
 #pragma unroll
         for (int m = 0; m < NG; ++m) {
-          const uint32_t h = (uint32_t)(4 * threadIdx.x + 1024 * m);
+          const uint32_t h = (uint32_t)(4 * tid() + 1024 * m);
           const bool in = h * 2 < H2 && q0 + q < p.unpool_ks;
           pv[q][m] = __builtin_bit_cast(
               f32x4_t, ld_co16(rp, in ? (uint32_t)((((size_t)(q0 + q) * p.b + t) * H + h) * 4) : kOob));
@@ -985,7 +1039,7 @@ __device__ __forceinline__ void boundary_task(const BlockParams &p, const Deps &
     }
 #pragma unroll
     for (int m = 0; m < NG; ++m) {
-      const uint32_t h = (uint32_t)(4 * threadIdx.x + 1024 * m);
+      const uint32_t h = (uint32_t)(4 * tid() + 1024 * m);
       uv[m] = u32x2_t{pack_bf16x2(av[m][0], av[m][1]), pack_bf16x2(av[m][2], av[m][3])};
       if (h * 2 < H2) st_co8(ru, h * 2, uv[m]);
     }
@@ -993,7 +1047,7 @@ __device__ __forceinline__ void boundary_task(const BlockParams &p, const Deps &
     const rsrc_t ru = make_rsrc(p.u + (size_t)t * H);
 #pragma unroll
     for (int m = 0; m < NG; ++m) {
-      const uint32_t h = (uint32_t)(4 * threadIdx.x + 1024 * m);
+      const uint32_t h = (uint32_t)(4 * tid() + 1024 * m);
       uv[m] = ld_co8(ru, h * 2 < H2 ? h * 2 : kOob);
     }
   }
@@ -1006,7 +1060,7 @@ __device__ __forceinline__ void boundary_task(const BlockParams &p, const Deps &
   }
 #pragma unroll
   for (int m = 0; m < NG; ++m) {
-    const uint32_t h = (uint32_t)(4 * threadIdx.x + 1024 * m);
+    const uint32_t h = (uint32_t)(4 * tid() + 1024 * m);
     const bool in = h * 2 < H2;
     wv[m] = p.next_norm_w ? ld_b64(make_rsrc(p.next_norm_w), in ? h * 2 : kOob) : u32x2_t{0x3F803F80u, 0x3F803F80u};
   }
@@ -1030,7 +1084,7 @@ __device__ __forceinline__ void boundary_task(const BlockParams &p, const Deps &
   const float rss = 1.0f / sqrtf(s2 / (float)H + p.norm_eps);
 #pragma unroll
   for (int m = 0; m < NG; ++m) {
-    const int h = 4 * threadIdx.x + 1024 * m;
+    const int h = 4 * tid() + 1024 * m;
     if (h >= H) break;
     float wi[4];
     unpack4(wv[m], wi);
@@ -1123,7 +1177,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     unsigned char *scratch = lds + p.lds_route_bytes;
     stamp(p, 6);
     const int GW = G * kWaves;
-    unsigned char *stage = scratch + (threadIdx.x / MB_WAVE) * kStageWaveBytes;
+    unsigned char *stage = scratch + (tid() / MB_WAVE) * kStageWaveBytes;
     const int nact = uniform(*R.nact);
     const int nU = nact * (p.I / 16), nD = nact * (p.P / 32);
     bool h_ready = p.h_producers == 0;
@@ -1132,9 +1186,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // expert): they wait on waves that started with them.  (Waves that
     // reach the memory system later -- the later workgroups on a CU -- finish
     // their up units later.)
-    const int gw = blockIdx.x * kWaves + uniform(threadIdx.x / MB_WAVE);
+    const int gw = blockIdx.x * kWaves + uniform(tid() / MB_WAVE);
     for (int u = gw; u < nU; u += GW) up_unit(p, d, R, u, h_ready, stage);
+    stamp(p, 20);
     for (int u = gw; u < nD; u += GW) down_unit(p, d, R, u, stage);
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();
     stamp(p, 11);
   }
@@ -1168,9 +1224,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         proj_task<true>(d, p.moe_out, p.unpool_w, p.u, p.b, p.H, p.P, p.unpool_ks, p.unpool_part, p.unpool_cnt,
                          kCtrFin, p.n_fin, false, i, true, scratch);
         signal_step(d, kCtrUnpool);
+        stamp(p, 16);
       } else {
         if (p.H <= 4096) boundary_task<4>(p, d, i, scratch);
         else boundary_task<kBoundGroups>(p, d, i, scratch);
+        stamp(p, 18);
       }
     }
   }

@@ -15,17 +15,19 @@ constexpr int kRouterRowBlock = 4;   // rows per router task (one wave each)
 // Cross-workgroup state of one launch, at the workspace start, in 128-byte
 // lines of kLine words so that no two counters share a line:
 //   line 0      word 1: the abort word (set when a wait timed out)
-//   kNumCtr x kReplicas lines   step counters (kCtr*), each in replicas(i)
-//               copies
+//   kNumCtr x kReplicas lines   step counters (kCtr*), each spread over
+//               stripes(i) x replicas(i) lines
 //   2E lines    up units done per expert, then down units done
 //   ceil(b/4) lines   router tasks done per block of kRouterRowBlock rows
 // Everything but the abort word is zero when a launch starts, and the last
-// workgroup to finish sets it back to zero.  A producer adds one to every
-// copy of a step counter after its coherent stores completed (one atomic per
-// lane of one instruction); a consumer polls the copy its workgroup index
-// selects.  Increments of one address are serialized, and polls of an
-// address delay the increments to it, so a counter many workgroups wait for
-// has more copies, one with many producers fewer.
+// workgroup to finish sets it back to zero.  Increments of one address are
+// serialized, and polls of an address delay the increments to it.  So a step
+// counter is held in replicas(i) copies, each split into stripes(i) lines: a
+// producer adds one to its stripe (chosen by its workgroup index) of every
+// copy, after its coherent stores completed (one atomic per lane of one
+// instruction); a consumer sums the stripes of the copy its workgroup or
+// wave index selects.  Many consumers call for copies, many producers for
+// stripes.
 constexpr int kLine = 32;
 constexpr int kReplicas = 16;
 constexpr int kMaxGrid = 1024;  // workgroups of the persistent launch, at most
@@ -39,11 +41,26 @@ enum : int {
   kCtrFinished = 6,  // workgroups finished
   kNumCtr = 8,
 };
-// Copies of step counter i: the pooler, route and finalize counters are
-// awaited by every workgroup or wave; the unpooler's by the boundary tasks.
+// Copies and stripes of step counter i (replicas x stripes <= kReplicas).
+// The route and pre-norm counters have few producers and are awaited by
+// every workgroup or wave; the pooler's has 128 producers (H / 16 tiles) and
+// every wave as consumer; the finalize counter has b * P / 512 producers and
+// the unpooler tasks as consumers; the unpooler's has H / 16 (times its
+// split) producers and only the b boundary tasks as consumers.
 __host__ __device__ constexpr int replicas(int i) {
-  return (i == kCtrRoute || i == kCtrPool || i == kCtrPrenorm || i == kCtrFin) ? kReplicas : 1;
+  return (i == kCtrRoute || i == kCtrPrenorm) ? kReplicas
+         : (i == kCtrPool || i == kCtrFin)    ? 4
+                                              : 1;
 }
+__host__ __device__ constexpr int stripes(int i) {
+  return (i == kCtrPool || i == kCtrFin) ? 4 : i == kCtrUnpool ? kReplicas : 1;
+}
+constexpr bool counters_fit() {
+  for (int i = 0; i < kNumCtr; ++i)
+    if (replicas(i) * stripes(i) > kReplicas) return false;
+  return true;
+}
+static_assert(counters_fit(), "a step counter needs more lines than it has");
 __host__ __device__ inline size_t sync_line_ctr(int i, int rep) { return 1 + (size_t)i * kReplicas + rep; }
 __host__ __device__ inline size_t sync_line_up(int E, int e) { return sync_line_ctr(kNumCtr, 0) + e; }
 __host__ __device__ inline size_t sync_line_down(int E, int e) { return sync_line_up(E, E) + e; }
@@ -54,7 +71,7 @@ inline size_t sync_words(int E, int rows) {
 
 constexpr int kFinChunk = 512;  // features per finalize task
 constexpr int kBlockMaxExperts = 256;  // larger expert counts use the per-step kernels
-constexpr int kTimelineSlots = 16;
+constexpr int kTimelineSlots = 32;
 constexpr int kBlockGroupsPerCu = 3;  // resident workgroups per CU (one wave per SIMD each)
 
 constexpr int kBoundGroups = 8;      // 4-element groups per thread of a boundary row (H <= 8192)
