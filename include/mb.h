@@ -103,6 +103,11 @@ typedef struct {
  *   ffn_norm_w  bf16 [H] or NULL (= 1): boundary post-FFN norm weight
  *   gate        bf16 [H]      boundary gate g
  *   next_norm_w bf16 [H] or NULL (= 1): next layer's pre-norm weight
+ *   experts_packed  NULL, or the output of mb_pack_experts for these
+ *               w13 / w2: the experts in the layout the block kernel
+ *               streams.  When set, w13, w13_scale, w2 and w2_scale may be
+ *               NULL; the per-step kernels (sizes the block kernel does not
+ *               take) need them and return MB_ERR_UNSUPPORTED without them.
  * Norm weights are the effective bf16 multipliers ([mono.decoder]
  * effective_norm_weight), applied after normalising. */
 typedef struct {
@@ -119,6 +124,7 @@ typedef struct {
   const uint16_t *ffn_norm_w;
   const uint16_t *gate;
   const uint16_t *next_norm_w;
+  const uint8_t *experts_packed;
 } mb_weights;
 
 /* Optional intermediate outputs of mb_moe_block.  A NULL member is kept in
@@ -217,6 +223,24 @@ int mb_moe_block(const mb_dims *dims, const uint16_t *x, const mb_weights *w,
                  void *workspace, size_t workspace_bytes, void *stream_handle);
 
 /* A static, human-readable reason for a status code. */
+/* Bytes of the streaming layout of all E experts (for mb_pack_experts). */
+int mb_packed_experts_bytes(const mb_dims *dims, size_t *bytes);
+
+/* Copy the MXFP4 experts (w13, w13_scale, w2, w2_scale of `w`, all required)
+ * into `packed` (device memory, at least mb_packed_experts_bytes, 16-byte
+ * aligned) in the layout the block kernel streams: per expert and unit (16
+ * gate + 16 up rows of w13, then 32 rows of w2), per 128-element chunk, the
+ * 1 KB that one wave loads for each of the unit's two 16-row tiles, lane l
+ * getting bytes 64 c + 16 (l / 16) of row l % 16; then the unit's E8M0
+ * scales, 16 bytes per row and 4 chunks, padded with 127 (= 2^0).  The values
+ * are unchanged, so results are bit-identical to the caller's layout.  Meant
+ * for load time, like the weight preparation of [muse_moe_runner]
+ * MuseSparkAiterExperts; the caller owns `packed` and keeps it with the
+ * weights.  Asynchronous on `stream`.  MB_ERR_WORKSPACE if packed_bytes is
+ * too small. */
+int mb_pack_experts(const mb_dims *dims, const mb_weights *w, uint8_t *packed, size_t packed_bytes,
+                    void *stream);
+
 const char *mb_status_string(int status);
 
 #ifdef __cplusplus

@@ -28,6 +28,8 @@ EXPORTS = (
     "mb_experts",
     "mb_unpool_boundary",
     "mb_moe_block",
+    "mb_packed_experts_bytes",
+    "mb_pack_experts",
     "mb_status_string",
 )
 
@@ -46,7 +48,8 @@ class Dims(ctypes.Structure):
 
 
 _WEIGHT_FIELDS = ("router_w", "expert_bias", "pool_w", "pre_norm_w", "w13", "w13_scale", "w2",
-                  "w2_scale", "post_norm_w", "unpool_w", "ffn_norm_w", "gate", "next_norm_w")
+                  "w2_scale", "post_norm_w", "unpool_w", "ffn_norm_w", "gate", "next_norm_w",
+                  "experts_packed")
 _TAP_FIELDS = ("logits", "topk_ids", "topk_w", "count", "offset", "route_list", "active",
                "n_active", "h", "moe_out", "u", "timeline")
 
@@ -86,6 +89,8 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_size_t, _vp]
         L.mb_moe_block.argtypes = [P(Dims), _vp, P(Weights), _vp, _vp, P(Taps), _vp,
                                    ctypes.c_size_t, _vp]
+        L.mb_packed_experts_bytes.argtypes = [P(Dims), P(ctypes.c_size_t)]
+        L.mb_pack_experts.argtypes = [P(Dims), P(Weights), _vp, ctypes.c_size_t, _vp]
         L.mb_status_string.argtypes = [ctypes.c_int]
         L.mb_status_string.restype = ctypes.c_char_p
         for name in EXPORTS:
@@ -151,6 +156,27 @@ def mb_workspace_bytes(dims: Dims) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().mb_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)), "mb_workspace_bytes")
     return int(n.value)
+
+
+def mb_packed_experts_bytes(dims: Dims) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().mb_packed_experts_bytes(ctypes.byref(dims), ctypes.byref(n)),
+           "mb_packed_experts_bytes")
+    return int(n.value)
+
+
+def mb_pack_experts(dims: Dims, weights: Weights, packed: torch.Tensor) -> None:
+    _check(lib().mb_pack_experts(ctypes.byref(dims), ctypes.byref(weights), _p(packed),
+                                 packed.numel() * packed.element_size(), _stream()),
+           "mb_pack_experts")
+
+
+def pack_experts(dims: Dims, weights: Weights, device="cuda") -> torch.Tensor:
+    """A new device buffer holding the experts of `weights` in the streaming
+    layout (set it as the experts_packed weight; keep it alive with them)."""
+    packed = torch.empty(mb_packed_experts_bytes(dims), dtype=torch.uint8, device=device)
+    mb_pack_experts(dims, weights, packed)
+    return packed
 
 
 def workspace(dims: Dims, device="cuda") -> torch.Tensor:

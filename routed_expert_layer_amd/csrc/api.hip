@@ -114,10 +114,16 @@ int check_weights_route(const mb_weights *w, int flags, const uint16_t *x) {
   return MB_OK;
 }
 
+// The experts come in the caller's layout, in the streaming layout, or both.
 int check_weights_experts(const mb_weights *w) {
   if (!w) return MB_ERR_NULL;
-  return need({w->w13, w->w13_scale, w->w2, w->w2_scale, w->post_norm_w});
+  MB_TRY(need({w->post_norm_w}));
+  MB_TRY(maybe({w->w13, w->w13_scale, w->w2, w->w2_scale, w->experts_packed}));
+  if (w->experts_packed) return MB_OK;
+  return need({w->w13, w->w13_scale, w->w2, w->w2_scale});
 }
+
+bool has_plain_experts(const mb_weights *w) { return w->w13 && w->w13_scale && w->w2 && w->w2_scale; }
 
 int check_weights_boundary(const mb_weights *w) {
   if (!w) return MB_ERR_NULL;
@@ -204,6 +210,12 @@ BlockParams base_params(const mb_dims &d, const mb_weights *w, void *ws) {
     p.w13s = w->w13_scale;
     p.w2 = w->w2;
     p.w2s = w->w2_scale;
+    p.xp = w->experts_packed;
+    const PackedExperts X = packed_experts(d.pooled, d.inter);
+    p.xp_stride = X.stride;
+    p.xp_up_s = X.up_s;
+    p.xp_down = X.down;
+    p.xp_down_s = X.down_s;
     p.post_norm_w = w->post_norm_w;
     p.unpool_w = w->unpool_w;
     p.ffn_norm_w = w->ffn_norm_w;
@@ -389,6 +401,7 @@ int mb_experts(const mb_dims *dims, const uint16_t *h, const int32_t *topk_ids,
   bool used = false;
   MB_TRY(run_fused(p, st, (hipStream_t)stream, &used));
   if (used) return MB_OK;
+  if (!has_plain_experts(w)) return MB_ERR_UNSUPPORTED;  // the per-step kernels read the caller's layout
   return run_experts(*dims, h, topk_w, offset, route_list, active, n_active, w, moe_out, workspace,
                      (hipStream_t)stream);
 }
@@ -470,10 +483,30 @@ int mb_moe_block(const mb_dims *dims, const uint16_t *x, const mb_weights *w, fl
   bool used = false;
   MB_TRY(run_fused(p, st, s, &used));
   if (used) return MB_OK;
+  if (!has_plain_experts(w)) return MB_ERR_UNSUPPORTED;  // the per-step kernels read the caller's layout
   MB_TRY(run_route(d, x, w, logits, 0, ids, wts, count, offset, route_list, active, n_active, s));
   MB_TRY(run_pool(d, x, w, h, ws, s));
   MB_TRY(run_experts(d, h, wts, offset, route_list, active, n_active, w, moe_out, ws, s));
   return run_unpool_boundary(d, moe_out, w, stream, x_next, u, ws, s);
+}
+
+int mb_packed_experts_bytes(const mb_dims *dims, size_t *bytes) {
+  MB_TRY(check_dims(dims));
+  if (!bytes) return MB_ERR_NULL;
+  *bytes = (size_t)dims->experts * packed_experts(dims->pooled, dims->inter).stride;
+  return MB_OK;
+}
+
+int mb_pack_experts(const mb_dims *dims, const mb_weights *w, uint8_t *packed, size_t packed_bytes,
+                    void *stream) {
+  MB_TRY(check_dims(dims));
+  if (!w) return MB_ERR_NULL;
+  MB_TRY(need({w->w13, w->w13_scale, w->w2, w->w2_scale, packed}));
+  size_t bytes = 0;
+  MB_TRY(mb_packed_experts_bytes(dims, &bytes));
+  if (packed_bytes < bytes) return MB_ERR_WORKSPACE;
+  MB_HIP(launch_pack_experts(*dims, w->w13, w->w13_scale, w->w2, w->w2_scale, packed, (hipStream_t)stream));
+  return MB_OK;
 }
 
 const char *mb_status_string(int status) {
@@ -487,7 +520,8 @@ const char *mb_status_string(int status) {
                                     "1024, top_k <= 16, experts*ceil(rows/64) <= 4096, hidden % 32, "
                                     "pooled % 128, inter % 128)";
     case MB_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
-    case MB_ERR_WORKSPACE: return "workspace missing or smaller than mb_workspace_bytes";
+    case MB_ERR_WORKSPACE: return "workspace (or packed-experts buffer) missing or smaller than "
+                                  "mb_workspace_bytes (mb_packed_experts_bytes)";
     case MB_ERR_HIP: return "a kernel launch failed";
     default: return "unknown status";
   }

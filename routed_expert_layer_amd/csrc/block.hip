@@ -224,7 +224,8 @@ __device__ __forceinline__ void finish(const Deps &d, int nrb, int *flag) {
 // logits seen by a route task (12), its rows routed (14), routes seen by the
 // workgroup (13), unpool task done (16), boundary's unpooler wait over (17),
 // boundary done (18), finalize's expert wait over (19), wave 0's up units
-// done (20), finalize done (21).
+// done (20), finalize done (21), router task done (22), router products
+// summed in wave 0 (23).
 __device__ __forceinline__ void stamp(const BlockParams &p, int slot) {
   if (p.timeline && tid() == 0) {
     asm volatile("" ::: "memory");
@@ -270,6 +271,7 @@ __device__ __forceinline__ void router_task(const BlockParams &p, const Deps &d,
       acc = fma((double)bf16_bits_to_f32(xv[u][1] >> 16), (double)w[u][3], acc);
     }
   }
+  stamp(p, 23);
   red[tid()] = acc;
   __syncthreads();
   if (tid() < kRouterRowBlock * 16) {
@@ -285,6 +287,7 @@ __device__ __forceinline__ void router_task(const BlockParams &p, const Deps &d,
     st_co4(make_rsrc(p.logits_f), (uint32_t)(te * 4), __float_as_uint((float)v));
   }
   signal(d.logits(t0 / kRouterRowBlock));
+  stamp(p, 22);
 }
 
 // ---------------------------------------------------------------- routing
@@ -711,17 +714,52 @@ __device__ __forceinline__ void prenorm_task(const BlockParams &p, const Deps &d
 
 // ---------------------------------------------------------------- experts
 
-// Issue priority of a wave streaming a unit, from its progress: 3 in the
-// first quarter of the chunks down to 0 in the last.  Among waves of equal
-// priority the oldest issues first, which leaves the waves of the youngest
-// workgroups on a CU far behind; ranking by progress lets the waves that are
-// behind catch up, so the units of an expert finish together.
+// Issue priority of a wave streaming its units, from its progress through
+// all of them (c of n chunks, up units first): 3 in the first quarter down to
+// 0 in the last.  Among waves of equal priority the oldest issues first, which
+// leaves the waves of the youngest workgroups on a CU far behind; ranking by
+// progress lets the waves that are behind catch up, so the units of an expert
+// finish together, and up units (which down units wait for) go before down
+// units.
 __device__ __forceinline__ void set_progress_priority(int c, int n) {
   const int q = (4 * c) / n;
   if (q <= 0) __builtin_amdgcn_s_setprio(3);
   else if (q == 1) __builtin_amdgcn_s_setprio(2);
   else if (q == 2) __builtin_amdgcn_s_setprio(1);
   else __builtin_amdgcn_s_setprio(0);
+}
+
+// Where a wave finds the two 16-row MXFP4 tiles of a unit: codes of chunk c
+// of tile 0 / 1 at o0 / o1 + wstride * c in rw (o0 / o1 already at this
+// lane's 16 bytes), the scales of chunks c .. c + 3 at so0 / so1 + sstride * c
+// in rs (vec: one 16-byte load per 4 chunks, else one 4-byte load per chunk).
+struct MxTiles {
+  rsrc_t rw, rs;
+  uint32_t o0, o1, so0, so1, wstride, sstride;
+  bool vec;
+};
+
+// The tiles of rows r0 .. r0 + 15 and r1 .. r1 + 15 of one expert's matrix of
+// `kdim`-element rows, in the caller's row-major layout: lane l reads row
+// l % 16, bytes 64 c + 16 (l / 16) of each 64-byte chunk c.
+__device__ __forceinline__ MxTiles mx_plain(const uint8_t *codes, const uint8_t *scales, int r0, int r1, int kdim,
+                                            int lane) {
+  const uint32_t r16 = (uint32_t)(lane & 15), g = (uint32_t)(lane >> 4);
+  const uint32_t rb = (uint32_t)kdim / 2, sb = (uint32_t)kdim / 32;
+  return MxTiles{make_rsrc(codes), make_rsrc(scales), (r0 + r16) * rb + 16 * g, (r1 + r16) * rb + 16 * g,
+                 (r0 + r16) * sb, (r1 + r16) * sb, 64u, 4u, (kdim / 128) % 4 == 0};
+}
+
+// Unit `unit` of one section of the streaming layout (mb_pack_experts): per
+// chunk the two tiles' 1 KB wave loads follow each other, lane l at 16 l;
+// per group of four chunks the two tiles' 16 rows x 16 scale bytes, row l % 16
+// at 16 (l % 16).
+__device__ __forceinline__ MxTiles mx_packed(const uint8_t *codes, const uint8_t *scales, int unit, int kdim,
+                                             int lane) {
+  const uint32_t nch = (uint32_t)kdim / 128, ngr = (nch + 3) / 4;
+  const uint32_t o = (uint32_t)unit * nch * 2048u + 16u * (uint32_t)lane;
+  const uint32_t so = (uint32_t)unit * ngr * 512u + 16u * (uint32_t)(lane & 15);
+  return MxTiles{make_rsrc(codes), make_rsrc(scales), o, o + 1024u, so, so + 256u, 2048u, 128u, true};
 }
 
 // One wave: D0 = W0 B and D1 = W1 B for two 16-row MXFP4 weight tiles over
@@ -747,14 +785,16 @@ __device__ __forceinline__ void set_progress_priority(int c, int n) {
 // the data.  `wait` runs after the first weight requests, before the first
 // activation request.
 template <typename Wait>
-__device__ __forceinline__ void mx_pair(rsrc_t rw, uint32_t o0, uint32_t o1, rsrc_t rs, uint32_t so0,
-                                        uint32_t so1, bool vec_scales, int nch, rsrc_t ra, uint32_t a_ld0,
-                                        uint32_t a_ld1, bool two, unsigned char *la, f32x4_t &d0, f32x4_t &d1,
-                                        Wait wait) {
+__device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, rsrc_t ra, uint32_t a_ld0, uint32_t a_ld1,
+                                        bool two, unsigned char *la, f32x4_t &d0, f32x4_t &d1, int prog,
+                                        int prog_total, Wait wait) {
   const int lane = tid() % MB_WAVE, g = lane >> 4;
+  const rsrc_t rw = T.rw, rs = T.rs;
+  const uint32_t o0 = T.o0, o1 = T.o1, so0 = T.so0, so1 = T.so1, ws = T.wstride, ss = T.sstride;
+  const bool vec_scales = T.vec;
   u32x4_t W0[kRing], W1[kRing], A0[kRing], A1[kRing];
   auto scales = [&](uint32_t so, int c0) {
-    if (vec_scales) return ld_b128(rs, c0 < nch ? so + 4u * c0 : kOob);
+    if (vec_scales) return ld_b128(rs, c0 < nch ? so + ss * c0 : kOob);
     u32x4_t v;
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] = ld_b32(rs, c0 + r < nch ? so + 4u * (c0 + r) : kOob);
@@ -763,8 +803,8 @@ __device__ __forceinline__ void mx_pair(rsrc_t rw, uint32_t o0, uint32_t o1, rsr
 #pragma unroll
   for (int r = 0; r < kRing; ++r) {
     const bool ok = r < nch;
-    W0[r] = ld_b128(rw, ok ? o0 + 64u * r : kOob);
-    W1[r] = ld_b128(rw, ok ? o1 + 64u * r : kOob);
+    W0[r] = ld_b128(rw, ok ? o0 + ws * r : kOob);
+    W1[r] = ld_b128(rw, ok ? o1 + ws * r : kOob);
   }
   u32x4_t S0 = scales(so0, 0), S1 = scales(so1, 0);
   wait();
@@ -779,7 +819,7 @@ __device__ __forceinline__ void mx_pair(rsrc_t rw, uint32_t o0, uint32_t o1, rsr
   const uint32_t st_off = (uint32_t)((lane >> 4) * kStageRowBytes + (lane & 15) * 16);
   const uint32_t rd_off = (uint32_t)((lane & 7) * kStageRowBytes + 64 * g);
   for (int c0 = 0; c0 < nch; c0 += kRing) {
-    set_progress_priority(c0, nch);
+    set_progress_priority(prog + c0, prog_total);
     // This round's activations to the staging LDS (one wave's LDS accesses
     // complete in order, so the reads below see them and the next round's
     // stores follow this round's reads).
@@ -806,8 +846,8 @@ __device__ __forceinline__ void mx_pair(rsrc_t rw, uint32_t o0, uint32_t o1, rsr
       }
       const int cn = c0 + kRing + r;
       const bool ok = cn < nch;
-      W0[r] = ld_b128(rw, ok ? o0 + 64u * cn : kOob);
-      W1[r] = ld_b128(rw, ok ? o1 + 64u * cn : kOob);
+      W0[r] = ld_b128(rw, ok ? o0 + ws * cn : kOob);
+      W1[r] = ld_b128(rw, ok ? o1 + ws * cn : kOob);
       A0[r] = ld_co16(ra, ok ? a_ld0 + 256u * cn : kOob);
       A1[r] = two ? ld_co16(ra, ok ? a_ld1 + 256u * cn : kOob) : u32x4_t{0, 0, 0, 0};
     }
@@ -821,7 +861,7 @@ __device__ __forceinline__ void mx_pair(rsrc_t rw, uint32_t o0, uint32_t o1, rsr
 // gate rows i0..i0+15 and up rows I+i0..I+i0+15 of the expert, over P, for
 // the expert's routes in passes of kStageRows.
 __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, const RouteLds &R, int unit,
-                                        bool &h_ready, unsigned char *la) {
+                                        bool &h_ready, unsigned char *la, int &prog, int prog_total) {
   const int lane = tid() % MB_WAVE, g = lane >> 4, r16 = lane & 15;
   const int P = p.P, I = p.I;
   const int tiles = I / 16;
@@ -829,9 +869,10 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
   const int e = uniform(R.act[a]);
   const int row0 = uniform(R.off[e]), nrows = uniform(R.off[e + 1]) - row0;
   const int i0 = tile * 16;
-  const rsrc_t rw = make_rsrc(p.w13 + (size_t)e * 2 * I * (P / 2));
-  const rsrc_t rs = make_rsrc(p.w13s + (size_t)e * 2 * I * (P / 32));
-  const uint32_t rg = (uint32_t)(i0 + r16), ru = rg + (uint32_t)I;
+  const MxTiles T =
+      p.xp ? mx_packed(p.xp + (size_t)e * p.xp_stride, p.xp + (size_t)e * p.xp_stride + p.xp_up_s, tile, P, lane)
+           : mx_plain(p.w13 + (size_t)e * 2 * I * (P / 2), p.w13s + (size_t)e * 2 * I * (P / 32), i0, I + i0, P,
+                      lane);
   const rsrc_t rh = make_rsrc(p.h), ract = make_rsrc(p.act);
   const int nch = P / 128;
   for (int m0 = 0; m0 < nrows; m0 += kStageRows) {
@@ -841,13 +882,13 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
     const uint32_t a0 = ml0 < nrows ? (uint32_t)((R.rl[row0 + ml0] / p.k) * P) * 2u + piece : kOob;
     const uint32_t a1 = ml1 < nrows ? (uint32_t)((R.rl[row0 + ml1] / p.k) * P) * 2u + piece : kOob;
     f32x4_t gs, us;
-    mx_pair(rw, rg * (P / 2) + 16 * g, ru * (P / 2) + 16 * g, rs, rg * (P / 32), ru * (P / 32), nch % 4 == 0, nch,
-            rh, a0, a1, mrows > 4, la, gs, us, [&]() {
+    mx_pair(T, nch, rh, a0, a1, mrows > 4, la, gs, us, prog, prog_total, [&]() {
               if (!h_ready) {
                 wave_wait_step(d, p.pre_norm_w ? kCtrPrenorm : kCtrPool, p.h_producers);
                 h_ready = true;
               }
             });
+    prog += nch;
     const int m = m0 + r16;
     if (r16 < kStageRows && m < nrows) {
       float o[4];
@@ -866,7 +907,7 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
 // Down unit: w2 for (active expert, 32 output features): y in route order and
 // the route's sum of squares over these 32 features.
 __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, const RouteLds &R, int unit,
-                                          unsigned char *la) {
+                                          unsigned char *la, int &prog, int prog_total) {
   const int lane = tid() % MB_WAVE, g = lane >> 4, r16 = lane & 15;
   const int P = p.P, I = p.I;
   const int tiles = P / 32;
@@ -874,9 +915,10 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
   const int e = uniform(R.act[a]);
   const int row0 = uniform(R.off[e]), nrows = uniform(R.off[e + 1]) - row0;
   const int p0 = tile * 32;
-  const rsrc_t rw = make_rsrc(p.w2 + (size_t)e * P * (I / 2));
-  const rsrc_t rs = make_rsrc(p.w2s + (size_t)e * P * (I / 32));
-  const uint32_t r0 = (uint32_t)(p0 + r16), r1 = r0 + 16;
+  const MxTiles T =
+      p.xp ? mx_packed(p.xp + (size_t)e * p.xp_stride + p.xp_down, p.xp + (size_t)e * p.xp_stride + p.xp_down_s,
+                       tile, I, lane)
+           : mx_plain(p.w2 + (size_t)e * P * (I / 2), p.w2s + (size_t)e * P * (I / 32), p0, p0 + 16, I, lane);
   const rsrc_t ract = make_rsrc(p.act), ry = make_rsrc(p.y), rss = make_rsrc(p.ssq);
   const int nch = I / 128;
   bool ready = false;
@@ -887,13 +929,13 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
     const uint32_t a0 = ml0 < nrows ? (uint32_t)((row0 + ml0) * I) * 2u + piece : kOob;
     const uint32_t a1 = ml1 < nrows ? (uint32_t)((row0 + ml1) * I) * 2u + piece : kOob;
     f32x4_t y0, y1;
-    mx_pair(rw, r0 * (I / 2) + 16 * g, r1 * (I / 2) + 16 * g, rs, r0 * (I / 32), r1 * (I / 32), nch % 4 == 0, nch,
-            ract, a0, a1, mrows > 4, la, y0, y1, [&]() {
+    mx_pair(T, nch, ract, a0, a1, mrows > 4, la, y0, y1, prog, prog_total, [&]() {
               if (!ready) {
                 poll_ge(d, d.up(e), (unsigned)(I / 16));
                 ready = true;
               }
             });
+    prog += nch;
     const int m = m0 + r16;
     const bool valid = r16 < kStageRows && m < nrows;
     float ss = 0.f;
@@ -1187,9 +1229,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // reach the memory system later -- the later workgroups on a CU -- finish
     // their up units later.)
     const int gw = blockIdx.x * kWaves + uniform(tid() / MB_WAVE);
-    for (int u = gw; u < nU; u += GW) up_unit(p, d, R, u, h_ready, stage);
+    // Chunks this wave streams (one pass per unit), for its issue priority.
+    const int my_up = gw < nU ? (nU - gw + GW - 1) / GW : 0, my_down = gw < nD ? (nD - gw + GW - 1) / GW : 0;
+    const int prog_total = my_up * (p.P / 128) + my_down * (p.I / 128);
+    int prog = 0;
+    for (int u = gw; u < nU; u += GW) up_unit(p, d, R, u, h_ready, stage, prog, prog_total);
     stamp(p, 20);
-    for (int u = gw; u < nD; u += GW) down_unit(p, d, R, u, stage);
+    for (int u = gw; u < nD; u += GW) down_unit(p, d, R, u, stage, prog, prog_total);
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();
     stamp(p, 11);

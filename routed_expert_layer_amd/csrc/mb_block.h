@@ -79,6 +79,28 @@ constexpr int kBoundGroups = 8;      // 4-element groups per thread of a boundar
 // Order keys a wave ranks: the expert count rounded up to a multiple of 8.
 __host__ __device__ inline int rank_span(int E) { return (E + 7) & ~7; }
 
+// Streaming layout of the MXFP4 experts (mb_pack_experts).  Per expert, in
+// this order:
+//   up codes     [I/16 units][P/128 chunks][2 tiles][64 lanes][16 B]
+//   up scales    [I/16 units][ceil(P/512) groups][2 tiles][16 rows][16 B]
+//   down codes   [P/32 units][I/128 chunks][2 tiles][64 lanes][16 B]
+//   down scales  [P/32 units][ceil(I/512) groups][2 tiles][16 rows][16 B]
+// Up unit u has tiles w13 rows 16u.. (gate) and I + 16u.. (up); down unit u
+// has w2 rows 32u.. and 32u + 16..  Lane l's 16 code bytes of chunk c are
+// bytes 64 c + 16 (l / 16) of tile row l % 16 (its 32-element MX block of the
+// chunk); a row's 16 scale bytes of group q are its scale bytes 16 q .. + 15,
+// padded with 127 (2^0) past the row's end.
+struct PackedExperts {
+  size_t up_s, down, down_s, stride;  // byte offsets within an expert; expert stride
+};
+__host__ __device__ inline PackedExperts packed_experts(int P, int I) {
+  const size_t up = (size_t)I * P;  // (I/16) * (P/128) * 2048
+  const size_t up_s = (size_t)(I / 16) * ((P / 128 + 3) / 4) * 512;
+  const size_t down = (size_t)P * I / 2;
+  const size_t down_s = (size_t)(P / 32) * ((I / 128 + 3) / 4) * 512;
+  return PackedExperts{up, up + up_s, up + up_s + down, up + up_s + down + down_s};
+}
+
 struct BlockParams {
   int b, H, P, I, E, k, scoring;
   float mult, div_eps, route_scale, norm_eps;
@@ -93,6 +115,9 @@ struct BlockParams {
   const float *router_w, *bias;
   const uint16_t *pool_w, *pre_norm_w;
   const uint8_t *w13, *w13s, *w2, *w2s;
+  // the experts in the streaming layout (or NULL), and its byte offsets
+  const uint8_t *xp;
+  size_t xp_stride, xp_up_s, xp_down, xp_down_s;
   const uint16_t *post_norm_w, *unpool_w, *ffn_norm_w, *gate, *next_norm_w;
   // in/out
   float *stream;

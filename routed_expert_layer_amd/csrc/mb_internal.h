@@ -64,6 +64,10 @@ hipError_t launch_experts_finalize(const mb_dims &d, const float *y, const float
                                    const float *wts, const uint16_t *post_norm_w,
                                    uint16_t *moe_out, hipStream_t s);
 
+// The experts' codes and scales in the streaming layout (PackedExperts).
+hipError_t launch_pack_experts(const mb_dims &d, const uint8_t *w13, const uint8_t *w13s, const uint8_t *w2,
+                               const uint8_t *w2s, uint8_t *packed, hipStream_t s);
+
 // Boundary: RMSNorm of u, gated add into the fp32 stream, next pre-norm.
 hipError_t launch_boundary(const mb_dims &d, const uint16_t *u, float *stream,
                            const uint16_t *gate, const uint16_t *ffn_norm_w,

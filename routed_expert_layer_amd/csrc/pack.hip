@@ -1,0 +1,92 @@
+// Repacking of the MXFP4 expert weights into the streaming layout the block
+// kernel reads (layout in mb_block.h, PackedExperts).
+//
+// The values are the caller's: the codes and E8M0 scales of w13 and w2 in the
+// layout of [mono.decoder] MonoDims.expert_shapes, moved so that each wave
+// load of an expert unit is one contiguous kilobyte instead of sixteen
+// 64-byte pieces of sixteen rows.  This is done once per set of weights, when
+// they are loaded ([muse_moe_runner] MuseSparkAiterExperts: the ROCm experts
+// likewise take their weights in a layout prepared at load time).
+
+#include "mb_block.h"
+
+namespace mb {
+namespace {
+
+// One 16-byte piece of one code section per thread: piece q of expert
+// blockIdx.y is lane q % 64 of tile (q / 64) % 2 of chunk (q / 128) % nch of
+// unit q / (128 nch).  Tile t of unit u is rows unit_rows * u + t * t1_row ..
+// + 15 of the expert's [rows, kdim / 2]-byte matrix.
+__global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t *__restrict__ src, size_t src_stride,
+                                                         uint8_t *__restrict__ dst, size_t dst_stride,
+                                                         size_t dst_off, int units, int nch, int kdim,
+                                                         int unit_rows, int t1_row) {
+  const size_t pieces = (size_t)units * nch * 128;
+  const uint8_t *s = src + (size_t)blockIdx.y * src_stride;
+  uint8_t *o = dst + (size_t)blockIdx.y * dst_stride + dst_off;
+  for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < pieces; q += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(q % 64), t = (int)((q / 64) % 2), c = (int)((q / 128) % nch);
+    const int u = (int)(q / (128 * (size_t)nch));
+    const size_t row = (size_t)unit_rows * u + (size_t)t * t1_row + (lane & 15);
+    const size_t from = row * (size_t)(kdim / 2) + 64 * (size_t)c + 16 * (size_t)(lane >> 4);
+    *reinterpret_cast<uint4 *>(o + 16 * q) = *reinterpret_cast<const uint4 *>(s + from);
+  }
+}
+
+// One 16-byte piece of one scale section per thread: piece q is row q % 16 of
+// tile (q / 16) % 2 of group (q / 32) % ngr of unit q / (32 ngr); it holds the
+// row's scale bytes 16 g .. 16 g + 15, with 127 (2^0) past the row's kdim / 32.
+__global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t *__restrict__ src, size_t src_stride,
+                                                          uint8_t *__restrict__ dst, size_t dst_stride,
+                                                          size_t dst_off, int units, int ngr, int kdim,
+                                                          int unit_rows, int t1_row) {
+  const size_t pieces = (size_t)units * ngr * 32;
+  const int row_bytes = kdim / 32;
+  const uint8_t *s = src + (size_t)blockIdx.y * src_stride;
+  uint8_t *o = dst + (size_t)blockIdx.y * dst_stride + dst_off;
+  for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < pieces; q += (size_t)gridDim.x * blockDim.x) {
+    const int r = (int)(q % 16), t = (int)((q / 16) % 2), g = (int)((q / 32) % ngr);
+    const int u = (int)(q / (32 * (size_t)ngr));
+    const size_t row = (size_t)unit_rows * u + (size_t)t * t1_row + r;
+    uint8_t v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int b = 16 * g + i;
+      v[i] = b < row_bytes ? s[row * row_bytes + b] : (uint8_t)127;
+    }
+    uint4 w;
+    w.x = v[0] | v[1] << 8 | v[2] << 16 | (uint32_t)v[3] << 24;
+    w.y = v[4] | v[5] << 8 | v[6] << 16 | (uint32_t)v[7] << 24;
+    w.z = v[8] | v[9] << 8 | v[10] << 16 | (uint32_t)v[11] << 24;
+    w.w = v[12] | v[13] << 8 | v[14] << 16 | (uint32_t)v[15] << 24;
+    *reinterpret_cast<uint4 *>(o + 16 * q) = w;
+  }
+}
+
+dim3 grid_for(size_t pieces, int experts) {
+  size_t x = (pieces + 255) / 256;
+  if (x > 1024) x = 1024;
+  return dim3((unsigned)x, (unsigned)experts);
+}
+
+}  // namespace
+
+hipError_t launch_pack_experts(const mb_dims &d, const uint8_t *w13, const uint8_t *w13s, const uint8_t *w2,
+                               const uint8_t *w2s, uint8_t *packed, hipStream_t s) {
+  const int P = d.pooled, I = d.inter, E = d.experts;
+  const PackedExperts L = packed_experts(P, I);
+  const int up_units = I / 16, down_units = P / 32;
+  const int up_nch = P / 128, down_nch = I / 128;
+  const int up_ngr = (up_nch + 3) / 4, down_ngr = (down_nch + 3) / 4;
+  hipLaunchKernelGGL(pack_codes_kernel, grid_for((size_t)up_units * up_nch * 128, E), dim3(256), 0, s, w13,
+                     (size_t)2 * I * (P / 2), packed, L.stride, (size_t)0, up_units, up_nch, P, 16, I);
+  hipLaunchKernelGGL(pack_scales_kernel, grid_for((size_t)up_units * up_ngr * 32, E), dim3(256), 0, s, w13s,
+                     (size_t)2 * I * (P / 32), packed, L.stride, L.up_s, up_units, up_ngr, P, 16, I);
+  hipLaunchKernelGGL(pack_codes_kernel, grid_for((size_t)down_units * down_nch * 128, E), dim3(256), 0, s, w2,
+                     (size_t)P * (I / 2), packed, L.stride, L.down, down_units, down_nch, I, 32, 16);
+  hipLaunchKernelGGL(pack_scales_kernel, grid_for((size_t)down_units * down_ngr * 32, E), dim3(256), 0, s, w2s,
+                     (size_t)P * (I / 32), packed, L.stride, L.down_s, down_units, down_ngr, I, 32, 16);
+  return hipGetLastError();
+}
+
+}  // namespace mb

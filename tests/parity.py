@@ -40,6 +40,18 @@ class GpuBlock:
         self.stream0 = self.stream0[:b].contiguous()
         self.dims = rel.make_dims(**dims_kwargs(self.blk.dims))
 
+    def use_packed(self, keep_plain: bool = False) -> torch.Tensor:
+        """Stream the experts from mb_pack_experts' layout (and, unless
+        keep_plain, pass no caller-layout expert pointers at all)."""
+        packed = rel.pack_experts(self.dims, self.weights)
+        torch.cuda.synchronize()
+        self.wt["experts_packed"] = packed
+        if not keep_plain:
+            for n in ("w13", "w13_scale", "w2", "w2_scale"):
+                self.wt.pop(n, None)
+        self.weights = rel.make_weights(**self.wt)
+        return packed
+
     def set_bias(self, bias: np.ndarray) -> None:
         self.blk.expert_bias = bias
         self.wt["expert_bias"] = to_tensor(bias)

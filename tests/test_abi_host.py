@@ -26,7 +26,7 @@ def header_functions():
 def test_header_declares_the_five_calls():
     names = header_functions()
     for n in ("mb_route", "mb_pool", "mb_experts", "mb_unpool_boundary", "mb_moe_block",
-              "mb_workspace_bytes", "mb_status_string"):
+              "mb_workspace_bytes", "mb_packed_experts_bytes", "mb_pack_experts", "mb_status_string"):
         assert n in names
     assert set(names) == set(rel.EXPORTS)
 
@@ -145,3 +145,48 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         rel.mb_pool(d, torch.zeros(16, 4096, dtype=torch.bfloat16), rel.Weights(),
                     torch.zeros(1), torch.zeros(8, dtype=torch.uint8))
+
+
+def test_packed_experts_bytes():
+    # c1: per expert, up codes I*P, up scales (I/16) * ceil(P/512) * 512,
+    # down codes P*I/2, down scales (P/32) * ceil(I/512) * 512: the caller
+    # layout's bytes when P and I are multiples of 512.
+    n = ctypes.c_size_t(0)
+    assert rel.lib().mb_packed_experts_bytes(ctypes.byref(c1_dims()), ctypes.byref(n)) == 0
+    P, I, E = 2048, 1024, 64
+    assert n.value == E * (2 * I * P // 2 + 2 * I * P // 32 + P * I // 2 + P * I // 32)
+    # Scales padded to groups of four chunks: P = 128 (one chunk), I = 384 (three).
+    d = c1_dims(pooled=128, inter=384, experts=3, top_k=2)
+    assert rel.lib().mb_packed_experts_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
+    assert n.value == 3 * (384 * 128 + (384 // 16) * 512 + 128 * 384 // 2 + (128 // 32) * 512)
+    assert rel.lib().mb_packed_experts_bytes(ctypes.byref(c1_dims(pooled=96)), ctypes.byref(n)) == 3
+
+
+def test_pack_experts_argument_checks_before_launch():
+    d = c1_dims()
+    L = rel.lib()
+    n = ctypes.c_size_t(0)
+    L.mb_packed_experts_bytes(ctypes.byref(d), ctypes.byref(n))
+    w = full_weights()
+    assert L.mb_pack_experts(ctypes.byref(d), ctypes.byref(w), None, n.value, None) == MB_ERR_NULL
+    assert L.mb_pack_experts(ctypes.byref(d), ctypes.byref(w), FAKE, n.value - 1, None) == MB_ERR_WORKSPACE
+    assert L.mb_pack_experts(ctypes.byref(d), ctypes.byref(w), FAKE + 8, n.value, None) == MB_ERR_ALIGN
+    w = full_weights(w2_scale=None)
+    assert L.mb_pack_experts(ctypes.byref(d), ctypes.byref(w), FAKE, n.value, None) == MB_ERR_NULL
+
+
+def test_packed_experts_stand_in_for_the_caller_layout():
+    d = c1_dims()
+    L = rel.lib()
+    # Packed experts alone satisfy the experts' checks (the call then fails
+    # on the missing workspace, before any launch) ...
+    w = full_weights(w13=None, w13_scale=None, w2=None, w2_scale=None, experts_packed=FAKE)
+    assert L.mb_moe_block(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE, None, None, 0,
+                          None) == MB_ERR_WORKSPACE
+    # ... a misaligned buffer is refused, and without either layout the experts are missing.
+    w = full_weights(experts_packed=FAKE + 4)
+    assert L.mb_moe_block(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE, None, FAKE, 1 << 40,
+                          None) == MB_ERR_ALIGN
+    w = full_weights(w13=None)
+    assert L.mb_moe_block(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE, None, FAKE, 1 << 40,
+                          None) == MB_ERR_NULL

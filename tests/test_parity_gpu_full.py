@@ -17,19 +17,27 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 torch = pytest.importorskip("torch")
 
 
-def test_c1_decode_step():
+@pytest.mark.parametrize("layout", ["caller", "packed"])
+def test_c1_decode_step(layout):
     blk = synth.make_block("c1")
-    say("[gpu] c1 b=16 block")
-    got = GpuBlock(blk).run_block()
+    say(f"[gpu] c1 b=16 block, {layout} expert layout")
+    g = GpuBlock(blk)
+    if layout == "packed":
+        g.use_packed()
+    got = g.run_block()
     ref = oracle.block(blk)
     assert_block(got, ref, "c1", blk)
 
 
-@pytest.mark.parametrize("skew", ["calibrated", "literal", "uniform"])
-def test_c2_softmax_block(skew):
+@pytest.mark.parametrize("skew,layout", [("calibrated", "caller"), ("literal", "caller"), ("uniform", "caller"),
+                                         ("calibrated", "packed")])
+def test_c2_softmax_block(skew, layout):
     blk = synth.make_block("c2", skew=skew)
-    say(f"[gpu] c2 b=64 skew={skew}")
-    got = GpuBlock(blk).run_block()
+    say(f"[gpu] c2 b=64 skew={skew}, {layout} expert layout")
+    g = GpuBlock(blk)
+    if layout == "packed":
+        g.use_packed()
+    got = g.run_block()
     ref = oracle.block(blk)
     assert_block(got, ref, f"c2 {skew}", blk)
     hot = synth.hot_experts(2, 128)

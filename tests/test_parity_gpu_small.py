@@ -138,3 +138,72 @@ def test_binding_raises_on_unsupported_dims():
     with pytest.raises(rel.MbError) as ei:
         rel.mb_pool(d, g.x, g.weights, h, g.ws)
     assert ei.value.status == rel.MB_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- streaming layout
+
+def packed_reference(blk) -> np.ndarray:
+    """The streaming layout that mb_pack_experts documents, built on the host
+    from the caller-layout weights (test code: index arithmetic only)."""
+    d = blk.dims
+    P, I, E = d.pooled, d.inter, d.experts
+
+    def codes(w, units, nch, unit_rows, t1_row):
+        u, c, t, l = np.meshgrid(np.arange(units), np.arange(nch), np.arange(2), np.arange(64), indexing="ij")
+        row = unit_rows * u + t * t1_row + (l & 15)
+        col = 64 * c + 16 * (l >> 4)
+        idx = col[..., None] + np.arange(16)
+        return w[:, row[..., None], idx].reshape(E, -1)
+
+    def scales(s, units, ngr, unit_rows, t1_row):
+        rb = s.shape[2]
+        pad = np.full((E, s.shape[1], ngr * 16), 127, np.uint8)
+        pad[:, :, :rb] = s
+        u, g, t, r = np.meshgrid(np.arange(units), np.arange(ngr), np.arange(2), np.arange(16), indexing="ij")
+        row = unit_rows * u + t * t1_row + r
+        idx = (16 * g)[..., None] + np.arange(16)
+        return pad[:, row[..., None], idx].reshape(E, -1)
+
+    nch_p, nch_i = P // 128, I // 128
+    parts = [codes(blk.w13, I // 16, nch_p, 16, I), scales(blk.w13_scale, I // 16, (nch_p + 3) // 4, 16, I),
+             codes(blk.w2, P // 32, nch_i, 32, 16), scales(blk.w2_scale, P // 32, (nch_i + 3) // 4, 32, 16)]
+    return np.concatenate(parts, axis=1).reshape(-1)
+
+
+@pytest.mark.parametrize("dims", [dict(), dict(hidden=96, pooled=640, inter=384, experts=5),
+                                  dict(pooled=2048, inter=1024, experts=3)])
+def test_packed_layout_is_the_documented_one(dims):
+    blk = synth.make_block("c0", seed=21, dims=small(**dims))
+    g = GpuBlock(blk)
+    say(f"[gpu] pack experts {blk.dims}")
+    packed = g.use_packed().cpu().numpy()
+    want = packed_reference(blk)
+    assert packed.shape == want.shape
+    assert np.array_equal(packed, want)
+
+
+@pytest.mark.parametrize("case", [dict(), dict(rows=17), dict(rows=100, experts=16, top_k=4),
+                                  dict(hidden=96, pooled=640, inter=384, rows=21),
+                                  dict(hidden=4096, pooled=2048, inter=1024, experts=64, top_k=4, rows=16)])
+def test_packed_experts_match_caller_layout(case):
+    """Same values, same arithmetic order: every output bit-identical to the
+    caller-layout run, and both match the oracle."""
+    blk = synth.make_block("c0", seed=31, dims=small(**case))
+    g = GpuBlock(blk)
+    say(f"[gpu] packed vs caller layout {case}")
+    plain = g.run_block()
+    g.use_packed()
+    packed = g.run_block()
+    for n in plain:
+        assert np.array_equal(plain[n], packed[n], equal_nan=True), n
+    assert_block(packed, oracle.block(blk), f"packed {case}", blk)
+
+
+def test_packed_only_refused_where_the_block_kernel_declines():
+    import routed_expert_layer_amd as rel
+    blk = synth.make_block("c0", seed=41, dims=small(rows=3, experts=300, top_k=2, inter=128))
+    g = GpuBlock(blk)
+    g.use_packed()
+    with pytest.raises(rel.MbError) as e:
+        g.run_block()
+    assert e.value.status == rel.MB_ERR_UNSUPPORTED
