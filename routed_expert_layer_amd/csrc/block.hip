@@ -203,7 +203,17 @@ __device__ __forceinline__ void wave_wait_step(const Deps &d, int i, int target)
 __device__ __forceinline__ void finish(const Deps &d, int nrb, int *flag) {
   wait_stores();
   __syncthreads();
-  if (tid() == 0) *flag = atomic_inc(d.ctr(kCtrFinished)) == gridDim.x - 1u;
+  // Two levels: workgroup w counts into stripe w % 16, and the workgroup that
+  // completes a stripe counts into the top word.  (Hundreds of workgroups
+  // ending together on one address queue their increments ahead of every
+  // other atomic of the launch.)
+  if (tid() == 0) {
+    const unsigned G = gridDim.x, ns = G < (unsigned)kReplicas ? G : (unsigned)kReplicas, s = blockIdx.x % ns;
+    const unsigned quota = (G - s + ns - 1) / ns;
+    bool last = false;
+    if (atomic_inc(d.ctr(kCtrFinished, (int)s)) == quota - 1u) last = atomic_inc(d.ctr(kCtrFinishedTop)) == ns - 1u;
+    *flag = last;
+  }
   __syncthreads();
   if (!*flag) return;
   for (int i = tid(); i < kNumCtr * kReplicas; i += kThreads)

@@ -32,7 +32,7 @@ constexpr int kLine = 32;
 constexpr int kReplicas = 16;
 constexpr int kMaxGrid = 1024;  // workgroups of the persistent launch, at most
 enum : int {
-  kCtrLogits = 0,    // (unused: router tasks count per row block)
+  kCtrFinishedTop = 0,  // stripes of kCtrFinished completed
   kCtrRoute = 1,     // route tasks done
   kCtrPool = 2,      // pooler tiles complete
   kCtrPrenorm = 3,   // pre-norm rows done
@@ -46,14 +46,15 @@ enum : int {
 // every workgroup or wave; the pooler's has 128 producers (H / 16 tiles) and
 // every wave as consumer; the finalize counter has b * P / 512 producers and
 // the unpooler tasks as consumers; the unpooler's has H / 16 (times its
-// split) producers and only the b boundary tasks as consumers.
+// split) producers and only the b boundary tasks as consumers; the finished
+// counter has every workgroup as producer (and a second level, the top word).
 __host__ __device__ constexpr int replicas(int i) {
   return (i == kCtrRoute || i == kCtrPrenorm) ? kReplicas
          : (i == kCtrPool || i == kCtrFin)    ? 4
                                               : 1;
 }
 __host__ __device__ constexpr int stripes(int i) {
-  return (i == kCtrPool || i == kCtrFin) ? 4 : i == kCtrUnpool ? kReplicas : 1;
+  return (i == kCtrPool || i == kCtrFin) ? 4 : (i == kCtrUnpool || i == kCtrFinished) ? kReplicas : 1;
 }
 constexpr bool counters_fit() {
   for (int i = 0; i < kNumCtr; ++i)
