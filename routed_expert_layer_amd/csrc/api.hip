@@ -287,7 +287,7 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   const bool needs_routing = st.experts || st.routing_out;
   // Route tasks (4 rows each) publish ids and weights for every workgroup's
   // grouping.  (Every workgroup routing every row itself costs each of them
-  // b/4 rows one after another.)
+  // b/4 rows one after another, and has all of them read every logit.)
   const int n_route = (needs_routing && !st.route_given) ? (p.b + 3) / 4 : 0;
   // The pooler is not split: its output is needed only once routing is
   // done, and a split adds a partial store, a last-arrival round trip and a

@@ -57,7 +57,6 @@ constexpr int kRing = 4;        // 128-element weight chunks a wave keeps in fli
 static_assert(kRing == 4, "one 16-byte scale load covers four chunks");
 constexpr int kProjBatch = 8;   // 32-element projection chunks a wave requests at once
 constexpr int kRouterBatch = 16;  // router loads a thread requests at once
-constexpr int kRankBatch = 8;    // order keys a lane reads at once
 constexpr int kBoundBatch = 4;   // pre-norm element groups a thread requests at once
 
 // A value the wave holds in every lane (LDS reads, the wave index), moved to
@@ -320,18 +319,38 @@ __device__ __forceinline__ unsigned long long order_key(float key, int e) {
   return ((unsigned long long)u << 32) | (uint32_t)~(uint32_t)e;
 }
 
-// One row's routing by one wave from its fp32 logits l[i] (expert lane + 64 i):
-// multiplier, scores, keys = score + bias; each candidate's rank is the number
-// of candidates with a larger order key (read back from LDS; the keys are
-// distinct, so ranks are a permutation), and the candidates of rank < k fill
-// slots 0..k-1.  Then the fp32 weights in slot order.  Lane j < k gets slot j.
+// Wave-wide maximum of a 64-bit key, on every lane: DPP row shifts by 1, 2,
+// 4, 8 leave each 16-lane row's maximum in its last lane, and two row
+// broadcasts (15, 31) carry it to lane 63.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void key_max_step(uint32_t &hi, uint32_t &lo) {
+  const uint32_t h = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROWS, 0xF, false);
+  const uint32_t l = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROWS, 0xF, false);
+  const bool gt = h > hi || (h == hi && l > lo);
+  hi = gt ? h : hi;
+  lo = gt ? l : lo;
+}
+__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long key) {
+  uint32_t hi = (uint32_t)(key >> 32), lo = (uint32_t)key;
+  key_max_step<0x111, 0xF>(hi, lo);  // row_shr:1
+  key_max_step<0x112, 0xF>(hi, lo);  // row_shr:2
+  key_max_step<0x114, 0xF>(hi, lo);  // row_shr:4
+  key_max_step<0x118, 0xF>(hi, lo);  // row_shr:8
+  key_max_step<0x142, 0xA>(hi, lo);  // row_bcast:15
+  key_max_step<0x143, 0xC>(hi, lo);  // row_bcast:31
+  return ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)hi, 63) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
+}
+
+// One row's routing by one wave from its fp32 logits l[i] and expert biases
+// bias[i] (expert lane + 64 i): multiplier, scores, keys = score + bias; then
+// k rounds, each taking the largest remaining order key (the keys are
+// distinct) into the next slot.  Then the fp32 weights in slot order.  Lane
+// j < k gets slot j.
 template <int PER>
-__device__ __forceinline__ void route_one(const BlockParams &p, const RouteLds &R, const float (&l)[PER],
+__device__ __forceinline__ void route_one(const BlockParams &p, const float (&l)[PER], const float (&bias)[PER],
                                           int &out_id, float &out_w) {
-  const int lane = tid() % MB_WAVE, wave = tid() / MB_WAVE;
-  unsigned long long *rank = R.rank + (size_t)wave * rank_span(p.E);
-  int *slot_id = R.slot_id + wave * kMaxTopK;
-  float *slot_sc = R.slot_sc + wave * kMaxTopK;
+  const int lane = tid() % MB_WAVE;
   float g[PER], sc[PER];
   bool live[PER];
   float gmax = -INFINITY;
@@ -357,54 +376,53 @@ __device__ __forceinline__ void route_one(const BlockParams &p, const RouteLds &
 #pragma unroll
     for (int i = 0; i < PER; ++i) sc[i] = live[i] ? (float)(z[i] / zs) : 0.0f;
   }
-  // Order keys to LDS, padded with zeros (below every candidate's key) to a
-  // multiple of kRankBatch.
-  const int Ep = rank_span(p.E);
-  unsigned long long mine[PER];
+  // Order keys; lanes past E hold 0, below every candidate's key.
+  unsigned long long key[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = lane + MB_WAVE * i;
-    mine[i] = live[i] ? order_key(sc[i] + p.bias[e], e) : 0ull;
-    if (e < Ep) rank[e] = mine[i];
-  }
-  // One wave's LDS accesses complete in order: the reads below see all writes.
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  int above[PER];
+  for (int i = 0; i < PER; ++i) key[i] = live[i] ? order_key(sc[i] + bias[i], lane + MB_WAVE * i) : 0ull;
+  int my_id = 0;
+  float my_sc = 0.f, sum = 0.f;
+  for (int j = 0; j < p.k; ++j) {
+    unsigned long long best = key[0];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) above[i] = 0;
-  for (int j0 = 0; j0 < Ep; j0 += kRankBatch) {
-    unsigned long long o[kRankBatch];
+    for (int i = 1; i < PER; ++i) best = key[i] > best ? key[i] : best;
+    const unsigned long long m = wave_max_key(best);
+    const int id = uniform((int)~(uint32_t)m);
+    const int src = id % MB_WAVE, part = id / MB_WAVE;
+    float s = 0.f;
 #pragma unroll
-    for (int u = 0; u < kRankBatch; ++u) o[u] = rank[j0 + u];
-#pragma unroll
-    for (int u = 0; u < kRankBatch; ++u)
-#pragma unroll
-      for (int i = 0; i < PER; ++i) above[i] += o[u] > mine[i] ? 1 : 0;
-  }
-#pragma unroll
-  for (int i = 0; i < PER; ++i)
-    if (live[i] && above[i] < p.k) {
-      slot_id[above[i]] = lane + MB_WAVE * i;
-      slot_sc[above[i]] = sc[i];
+    for (int i = 0; i < PER; ++i) {
+      if (i == part) {
+        s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc[i]), src));
+        if (lane == src) key[i] = 0ull;  // taken
+      }
     }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  float sum = slot_sc[0];
-  for (int j = 1; j < p.k; ++j) sum = sum + slot_sc[j];
-  const int js = lane < p.k ? lane : 0;
-  out_id = slot_id[js];
+    sum = j == 0 ? s : sum + s;
+    if (lane == j) {
+      my_id = id;
+      my_sc = s;
+    }
+  }
+  out_id = my_id;
   const float den = sum + p.div_eps;
-  const float q = slot_sc[js] / den;
+  const float q = my_sc / den;
   out_w = q * p.route_scale;
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
 // Rows t_begin..t_end-1, one per wave in turn, from their fp32 logits; the
-// ids and weights go to LDS.
+// ids and weights go to LDS.  Each wave requests its row's logits and the
+// expert biases together.
 template <int PER>
 __device__ __forceinline__ void route_rows(const BlockParams &p, const RouteLds &R, int t_begin, int t_end) {
   const int lane = tid() % MB_WAVE;
   const rsrc_t rl = make_rsrc(p.logits_f);
-  for (int t = t_begin + tid() / MB_WAVE; t < t_end; t += kWaves) {
+  float bias[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + MB_WAVE * i;
+    bias[i] = e < p.E ? p.bias[e] : 0.f;
+  }
+  for (int t = t_begin + (int)(tid() / MB_WAVE); t < t_end; t += kWaves) {
     float l[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -413,7 +431,7 @@ __device__ __forceinline__ void route_rows(const BlockParams &p, const RouteLds 
     }
     int id;
     float w;
-    route_one<PER>(p, R, l, id, w);
+    route_one<PER>(p, l, bias, id, w);
     if (lane < p.k) {
       R.ids[t * p.k + lane] = id;
       R.w[t * p.k + lane] = w;

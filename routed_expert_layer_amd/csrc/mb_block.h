@@ -49,9 +49,7 @@ enum : int {
 // split) producers and only the b boundary tasks as consumers; the finished
 // counter has every workgroup as producer (and a second level, the top word).
 __host__ __device__ constexpr int replicas(int i) {
-  return (i == kCtrRoute || i == kCtrPrenorm) ? kReplicas
-         : (i == kCtrPool || i == kCtrFin)    ? 4
-                                              : 1;
+  return (i == kCtrRoute || i == kCtrPrenorm) ? kReplicas : (i == kCtrPool || i == kCtrFin) ? 4 : 1;
 }
 __host__ __device__ constexpr int stripes(int i) {
   return (i == kCtrPool || i == kCtrFin) ? 4 : (i == kCtrUnpool || i == kCtrFinished) ? kReplicas : 1;
@@ -77,8 +75,6 @@ constexpr int kBlockGroupsPerCu = 3;  // resident workgroups per CU (one wave pe
 
 constexpr int kBoundGroups = 8;      // 4-element groups per thread of a boundary row (H <= 8192)
 
-// Order keys a wave ranks: the expert count rounded up to a multiple of 8.
-__host__ __device__ inline int rank_span(int E) { return (E + 7) & ~7; }
 
 // Streaming layout of the MXFP4 experts (mb_pack_experts).  Per expert, in
 // this order:
@@ -144,9 +140,6 @@ struct RouteLds {
   int *act;    // [E]
   int *nact;   // [1]
   int *red;    // [8] scan scratch
-  unsigned long long *rank;  // [kBlockWaves][E] candidate order keys of a wave's row
-  int *slot_id;              // [kBlockWaves][kMaxTopK] a wave's chosen experts
-  float *slot_sc;            // [kBlockWaves][kMaxTopK] and their scores
   unsigned long long *bits;  // [E * ceil(b/64)]
 };
 
@@ -154,8 +147,7 @@ __host__ __device__ inline size_t align16(size_t v) { return (v + 15) & ~(size_t
 
 __host__ __device__ inline size_t route_lds_bytes(int b, int k, int E) {
   const size_t R = (size_t)b * k, W = (size_t)(b + 63) / 64;
-  return align16(R * 4) * 3 + align16((E + 1) * 4) + align16(E * 4) + 16 + 32 +
-         (size_t)kBlockWaves * (rank_span(E) * 8 + kMaxTopK * 8) + align16(E * W * 8);
+  return align16(R * 4) * 3 + align16((E + 1) * 4) + align16(E * 4) + 16 + 32 + align16(E * W * 8);
 }
 
 __device__ inline RouteLds route_lds(const BlockParams &p, unsigned char *base) {
@@ -176,12 +168,6 @@ __device__ inline RouteLds route_lds(const BlockParams &p, unsigned char *base) 
   o += 16;
   r.red = reinterpret_cast<int *>(base + o);
   o += 32;
-  r.rank = reinterpret_cast<unsigned long long *>(base + o);
-  o += (size_t)kBlockWaves * rank_span(p.E) * 8;
-  r.slot_id = reinterpret_cast<int *>(base + o);
-  o += kBlockWaves * kMaxTopK * 4;
-  r.slot_sc = reinterpret_cast<float *>(base + o);
-  o += kBlockWaves * kMaxTopK * 4;
   r.bits = reinterpret_cast<unsigned long long *>(base + o);
   (void)W;
   return r;
