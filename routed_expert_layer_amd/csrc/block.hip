@@ -791,36 +791,33 @@ __device__ __forceinline__ MxTiles mx_packed(const uint8_t *codes, const uint8_t
 }
 
 // One wave: D0 = W0 B and D1 = W1 B for two 16-row MXFP4 weight tiles over
-// nch 128-element chunks and up to kStageRows activation rows (bf16).
+// nch 128-element chunks and up to kStageRows activation rows (bf16).  The
+// four waves of a workgroup call this together for units of the same expert
+// (so with the same rows): the activations are staged once per workgroup.
 //
-// Weights: in resource rw (scales rs) this lane's row of tile 0 / 1 starts at
-// byte o0 / o1 (so0 / so1), o0 / o1 already at the lane's 16-byte column (32
-// codes, one MX block per chunk).  Lane l gets output rows 4*(l/16)..+3 of
-// column l % 16; columns past the pass's rows hold garbage and are not used.
-// Per chunk a lane converts its MX block of each tile row to bf16 in
-// registers for four 16x16x32 MFMAs; kRing chunks are in flight.  The scales
-// of four chunks come in one 16-byte load per tile row (vec_scales: nch a
-// multiple of 4), else one 4-byte load per chunk; the lane keeps byte l / 16.
+// Weights: see MxTiles.  Lane l gets output rows 4*(l/16)..+3 of column
+// l % 16; columns past the pass's rows are zero.  Per chunk a lane converts
+// its MX block of each tile row to bf16 in registers for four 16x16x32
+// MFMAs; kRing chunks are in flight, requested before `wait` (which returns
+// once the activations' producers are done).
 //
 // Activations (written by other workgroups of the launch, so read
-// coherently): lane l loads 16 bytes (elements 8 (l % 16) ..) of the chunk of
-// pass row l / 16 (a_ld0) and of row 4 + l / 16 (a_ld1, when `two`); kOob
-// gives zeros.  They go to the wave's staging LDS (la) and come back in MFMA
-// layout: lane l reads row l % 8.  Only the pass's rows are requested, in
-// full 16-byte pieces, instead of 16 padded rows per lane.
+// coherently): the rows' elements of up to kSegChunks chunks at a time are
+// loaded by the whole workgroup in 16-byte pieces into `stage` (row m at
+// m * kSegRowBytes; rows past the pass and chunks past nch as zeros), then
+// each wave reads its MFMA operand from there: lane l reads row l % 8.
+// row_off(m) is the byte offset of pass row m's element 0, or kOob.
 //
-// Chunks past nch load zeros and add nothing, so the loop has no branches on
-// the data.  `wait` runs after the first weight requests, before the first
-// activation request.
-template <typename Wait>
-__device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, rsrc_t ra, uint32_t a_ld0, uint32_t a_ld1,
-                                        bool two, unsigned char *la, f32x4_t &d0, f32x4_t &d1, int prog,
-                                        int prog_total, Wait wait) {
+// Chunks past nch have zero weights and zero activations and add nothing,
+// so the loop has no branches on the data.
+template <typename Wait, typename RowOff>
+__device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, rsrc_t ra, RowOff row_off, unsigned char *stage,
+                                        f32x4_t &d0, f32x4_t &d1, int prog, int prog_total, Wait wait) {
   const int lane = tid() % MB_WAVE, g = lane >> 4;
   const rsrc_t rw = T.rw, rs = T.rs;
   const uint32_t o0 = T.o0, o1 = T.o1, so0 = T.so0, so1 = T.so1, ws = T.wstride, ss = T.sstride;
   const bool vec_scales = T.vec;
-  u32x4_t W0[kRing], W1[kRing], A0[kRing], A1[kRing];
+  u32x4_t W0[kRing], W1[kRing];
   auto scales = [&](uint32_t so, int c0) {
     if (vec_scales) return ld_b128(rs, c0 < nch ? so + ss * c0 : kOob);
     u32x4_t v;
@@ -836,52 +833,54 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, rsrc_t ra, ui
   }
   u32x4_t S0 = scales(so0, 0), S1 = scales(so1, 0);
   wait();
-#pragma unroll
-  for (int r = 0; r < kRing; ++r) {
-    const bool ok = r < nch;
-    A0[r] = ld_co16(ra, ok ? a_ld0 + 256u * r : kOob);
-    A1[r] = two ? ld_co16(ra, ok ? a_ld1 + 256u * r : kOob) : u32x4_t{0, 0, 0, 0};
-  }
   d0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
   d1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const uint32_t st_off = (uint32_t)((lane >> 4) * kStageRowBytes + (lane & 15) * 16);
-  const uint32_t rd_off = (uint32_t)((lane & 7) * kStageRowBytes + 64 * g);
-  for (int c0 = 0; c0 < nch; c0 += kRing) {
-    set_progress_priority(prog + c0, prog_total);
-    // This round's activations to the staging LDS (one wave's LDS accesses
-    // complete in order, so the reads below see them and the next round's
-    // stores follow this round's reads).
+  const uint32_t rd_off = (uint32_t)((lane & 7) * kSegRowBytes + 64 * g);
+  for (int seg0 = 0; seg0 < nch; seg0 += kSegChunks) {
+    // This segment's activations, chunks rounded up to whole rounds.
+    const int segn = min(kSegChunks, nch - seg0);
+    const int ppr = ((segn + kRing - 1) / kRing) * kRing * 16;  // 16-byte pieces per row
+    u32x4_t v[kSegLoads];
 #pragma unroll
-    for (int r = 0; r < kRing; ++r) {
-      *reinterpret_cast<u32x4_t *>(la + r * kStageRows * kStageRowBytes + st_off) = A0[r];
-      if (two) *reinterpret_cast<u32x4_t *>(la + r * kStageRows * kStageRowBytes + 4 * kStageRowBytes + st_off) = A1[r];
+    for (int n = 0; n < kSegLoads; ++n) {
+      const int q = (int)tid() + kThreads * n;
+      const int m = q / ppr, pc = q % ppr;
+      const uint32_t ro = m < kStageRows ? row_off(m) : kOob;
+      v[n] = ld_co16(ra, (ro != kOob && pc < segn * 16) ? ro + (uint32_t)(seg0 * 256 + pc * 16) : kOob);
     }
-    asm volatile("" ::: "memory");
-    const u32x4_t N0 = scales(so0, c0 + kRing), N1 = scales(so1, c0 + kRing);
 #pragma unroll
-    for (int r = 0; r < kRing; ++r) {
-      u32x4_t B[4];
+    for (int n = 0; n < kSegLoads; ++n) {
+      const int q = (int)tid() + kThreads * n;
+      const int m = q / ppr, pc = q % ppr;
+      if (m < kStageRows) *reinterpret_cast<u32x4_t *>(stage + m * kSegRowBytes + pc * 16) = v[n];
+    }
+    __syncthreads();
+    for (int c0 = seg0; c0 < seg0 + segn; c0 += kRing) {
+      set_progress_priority(prog + c0, prog_total);
+      const u32x4_t N0 = scales(so0, c0 + kRing), N1 = scales(so1, c0 + kRing);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        B[i] = *reinterpret_cast<const u32x4_t *>(la + r * kStageRows * kStageRowBytes + rd_off + 16 * i);
-      bf16x8_t X0[4], X1[4];
-      dequant_fp4x32(W0[r], e8m0_to_f32((S0[r] >> (8 * g)) & 0xFFu), X0);
-      dequant_fp4x32(W1[r], e8m0_to_f32((S1[r] >> (8 * g)) & 0xFFu), X1);
+      for (int r = 0; r < kRing; ++r) {
+        u32x4_t B[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        d0 = mfma_bf16(X0[i], as_bf16x8(B[i]), d0);
-        d1 = mfma_bf16(X1[i], as_bf16x8(B[i]), d1);
+        for (int i = 0; i < 4; ++i)
+          B[i] = *reinterpret_cast<const u32x4_t *>(stage + rd_off + (c0 + r - seg0) * 256 + 16 * i);
+        bf16x8_t X0[4], X1[4];
+        dequant_fp4x32(W0[r], e8m0_to_f32((S0[r] >> (8 * g)) & 0xFFu), X0);
+        dequant_fp4x32(W1[r], e8m0_to_f32((S1[r] >> (8 * g)) & 0xFFu), X1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          d0 = mfma_bf16(X0[i], as_bf16x8(B[i]), d0);
+          d1 = mfma_bf16(X1[i], as_bf16x8(B[i]), d1);
+        }
+        const int cn = c0 + kRing + r;
+        const bool ok = cn < nch;
+        W0[r] = ld_b128(rw, ok ? o0 + ws * cn : kOob);
+        W1[r] = ld_b128(rw, ok ? o1 + ws * cn : kOob);
       }
-      const int cn = c0 + kRing + r;
-      const bool ok = cn < nch;
-      W0[r] = ld_b128(rw, ok ? o0 + ws * cn : kOob);
-      W1[r] = ld_b128(rw, ok ? o1 + ws * cn : kOob);
-      A0[r] = ld_co16(ra, ok ? a_ld0 + 256u * cn : kOob);
-      A1[r] = two ? ld_co16(ra, ok ? a_ld1 + 256u * cn : kOob) : u32x4_t{0, 0, 0, 0};
+      S0 = N0;
+      S1 = N1;
     }
-    asm volatile("" ::: "memory");
-    S0 = N0;
-    S1 = N1;
+    __syncthreads();
   }
 }
 
@@ -889,7 +888,7 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, rsrc_t ra, ui
 // gate rows i0..i0+15 and up rows I+i0..I+i0+15 of the expert, over P, for
 // the expert's routes in passes of kStageRows.
 __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, const RouteLds &R, int unit,
-                                        bool &h_ready, unsigned char *la, int &prog, int prog_total) {
+                                        bool &h_ready, unsigned char *stage, int &prog, int prog_total) {
   const int lane = tid() % MB_WAVE, g = lane >> 4, r16 = lane & 15;
   const int P = p.P, I = p.I;
   const int tiles = I / 16;
@@ -904,18 +903,16 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
   const rsrc_t rh = make_rsrc(p.h), ract = make_rsrc(p.act);
   const int nch = P / 128;
   for (int m0 = 0; m0 < nrows; m0 += kStageRows) {
-    const int mrows = min(kStageRows, nrows - m0);
-    const int ml0 = m0 + (lane >> 4), ml1 = ml0 + 4;
-    const uint32_t piece = (uint32_t)(lane & 15) * 16;
-    const uint32_t a0 = ml0 < nrows ? (uint32_t)((R.rl[row0 + ml0] / p.k) * P) * 2u + piece : kOob;
-    const uint32_t a1 = ml1 < nrows ? (uint32_t)((R.rl[row0 + ml1] / p.k) * P) * 2u + piece : kOob;
     f32x4_t gs, us;
-    mx_pair(T, nch, rh, a0, a1, mrows > 4, la, gs, us, prog, prog_total, [&]() {
-              if (!h_ready) {
-                wave_wait_step(d, p.pre_norm_w ? kCtrPrenorm : kCtrPool, p.h_producers);
-                h_ready = true;
-              }
-            });
+    mx_pair(
+        T, nch, rh,
+        [&](int m) { return m0 + m < nrows ? (uint32_t)((R.rl[row0 + m0 + m] / p.k) * P) * 2u : kOob; }, stage,
+        gs, us, prog, prog_total, [&]() {
+          if (!h_ready) {
+            wave_wait_step(d, p.pre_norm_w ? kCtrPrenorm : kCtrPool, p.h_producers);
+            h_ready = true;
+          }
+        });
     prog += nch;
     const int m = m0 + r16;
     if (r16 < kStageRows && m < nrows) {
@@ -935,7 +932,7 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
 // Down unit: w2 for (active expert, 32 output features): y in route order and
 // the route's sum of squares over these 32 features.
 __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, const RouteLds &R, int unit,
-                                          unsigned char *la, int &prog, int prog_total) {
+                                          unsigned char *stage, int &prog, int prog_total) {
   const int lane = tid() % MB_WAVE, g = lane >> 4, r16 = lane & 15;
   const int P = p.P, I = p.I;
   const int tiles = P / 32;
@@ -951,18 +948,15 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
   const int nch = I / 128;
   bool ready = false;
   for (int m0 = 0; m0 < nrows; m0 += kStageRows) {
-    const int mrows = min(kStageRows, nrows - m0);
-    const int ml0 = m0 + (lane >> 4), ml1 = ml0 + 4;
-    const uint32_t piece = (uint32_t)(lane & 15) * 16;
-    const uint32_t a0 = ml0 < nrows ? (uint32_t)((row0 + ml0) * I) * 2u + piece : kOob;
-    const uint32_t a1 = ml1 < nrows ? (uint32_t)((row0 + ml1) * I) * 2u + piece : kOob;
     f32x4_t y0, y1;
-    mx_pair(T, nch, ract, a0, a1, mrows > 4, la, y0, y1, prog, prog_total, [&]() {
-              if (!ready) {
-                poll_ge(d, d.up(e), (unsigned)(I / 16));
-                ready = true;
-              }
-            });
+    mx_pair(
+        T, nch, ract, [&](int m) { return m0 + m < nrows ? (uint32_t)((row0 + m0 + m) * I) * 2u : kOob; }, stage,
+        y0, y1, prog, prog_total, [&]() {
+          if (!ready) {
+            poll_ge(d, d.up(e), (unsigned)(I / 16));
+            ready = true;
+          }
+        });
     prog += nch;
     const int m = m0 + r16;
     const bool valid = r16 < kStageRows && m < nrows;
@@ -1247,7 +1241,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     unsigned char *scratch = lds + p.lds_route_bytes;
     stamp(p, 6);
     const int GW = G * kWaves;
-    unsigned char *stage = scratch + (tid() / MB_WAVE) * kStageWaveBytes;
+    unsigned char *stage = scratch;
     const int nact = uniform(*R.nact);
     const int nU = nact * (p.I / 16), nD = nact * (p.P / 32);
     bool h_ready = p.h_producers == 0;

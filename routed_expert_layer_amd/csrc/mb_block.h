@@ -173,20 +173,17 @@ __device__ inline RouteLds route_lds(const BlockParams &p, unsigned char *base) 
   return r;
 }
 
-// Activation staging of the expert units: per wave, kStageSlots chunks of
-// kStageRows rows x 128 bf16, rows kStageRowBytes apart (16 bytes of padding
-// spread the rows over the LDS banks).
+// Activation staging of the expert units, per workgroup: kStageRows rows of
+// up to kSegChunks chunks of 128 bf16, rows kSegRowBytes apart (16 bytes of
+// padding spread the rows over the LDS banks); each thread loads kSegLoads
+// 16-byte pieces of a segment.
 constexpr int kStageRows = 8;
-constexpr int kStageSlots = 4;
-constexpr int kStageRowBytes = 272;
-constexpr int kStageWaveBytes = kStageSlots * kStageRows * kStageRowBytes;
-
-// Scratch LDS the phases need beyond the routing state: the projection
-// partials and flag (16 KB + 64 bytes), or the staging of the expert units
-// (never live at the same time).
+constexpr int kSegChunks = 16;
+constexpr int kSegRowBytes = kSegChunks * 256 + 16;
+constexpr int kSegLoads = kStageRows * kSegChunks * 16 / 256;
+constexpr size_t kStageBytes = (size_t)kStageRows * kSegRowBytes;
 constexpr size_t kProjScratchBytes = 4 * 4 * 64 * 16 + 64;
-constexpr size_t kBlockScratchBytes =
-    kProjScratchBytes > (size_t)kBlockWaves * kStageWaveBytes ? kProjScratchBytes : (size_t)kBlockWaves * kStageWaveBytes;
+constexpr size_t kBlockScratchBytes = kProjScratchBytes > kStageBytes ? kProjScratchBytes : kStageBytes;
 
 hipError_t launch_block(const BlockParams &p, int grid, size_t lds, hipStream_t s);
 int block_max_groups_per_cu(size_t lds);
