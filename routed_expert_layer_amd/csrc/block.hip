@@ -54,7 +54,8 @@ static_assert(kWaves == kBlockWaves, "routing LDS is laid out per wave");
 static_assert(kRouterRowBlock == kWaves, "a router task gives each wave one row");
 constexpr int kPoolMG = 4;      // 16-row groups per projection pass
 constexpr int kRing = 4;        // 128-element weight chunks a wave keeps in flight
-static_assert(kRing == 4, "one 16-byte scale load covers four chunks");
+static_assert(kRing % 4 == 0, "one 16-byte scale load covers four chunks");
+static_assert(kSegChunks % kRing == 0, "activation segments hold whole rounds of chunks");
 constexpr int kProjBatch = 8;   // 32-element projection chunks a wave requests at once
 constexpr int kRouterBatch = 16;  // router loads a thread requests at once
 constexpr int kBoundBatch = 4;   // pre-norm element groups a thread requests at once
@@ -831,7 +832,12 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, rsrc_t ra, Ro
     W0[r] = ld_b128(rw, ok ? o0 + ws * r : kOob);
     W1[r] = ld_b128(rw, ok ? o1 + ws * r : kOob);
   }
-  u32x4_t S0 = scales(so0, 0), S1 = scales(so1, 0);
+  u32x4_t S0[kRing / 4], S1[kRing / 4];
+#pragma unroll
+  for (int q = 0; q < kRing / 4; ++q) {
+    S0[q] = scales(so0, 4 * q);
+    S1[q] = scales(so1, 4 * q);
+  }
   wait();
   d0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
   d1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -857,28 +863,32 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, rsrc_t ra, Ro
     __syncthreads();
     for (int c0 = seg0; c0 < seg0 + segn; c0 += kRing) {
       set_progress_priority(prog + c0, prog_total);
-      const u32x4_t N0 = scales(so0, c0 + kRing), N1 = scales(so1, c0 + kRing);
+      u32x4_t N0[kRing / 4], N1[kRing / 4];
+#pragma unroll
+      for (int q = 0; q < kRing / 4; ++q) {
+        N0[q] = scales(so0, c0 + kRing + 4 * q);
+        N1[q] = scales(so1, c0 + kRing + 4 * q);
+      }
 #pragma unroll
       for (int r = 0; r < kRing; ++r) {
-        u32x4_t B[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          B[i] = *reinterpret_cast<const u32x4_t *>(stage + rd_off + (c0 + r - seg0) * 256 + 16 * i);
-        bf16x8_t X0[4], X1[4];
-        dequant_fp4x32(W0[r], e8m0_to_f32((S0[r] >> (8 * g)) & 0xFFu), X0);
-        dequant_fp4x32(W1[r], e8m0_to_f32((S1[r] >> (8 * g)) & 0xFFu), X1);
+        const float s0 = e8m0_to_f32((S0[r / 4][r % 4] >> (8 * g)) & 0xFFu);
+        const float s1 = e8m0_to_f32((S1[r / 4][r % 4] >> (8 * g)) & 0xFFu);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          d0 = mfma_bf16(X0[i], as_bf16x8(B[i]), d0);
-          d1 = mfma_bf16(X1[i], as_bf16x8(B[i]), d1);
+          const u32x4_t B = *reinterpret_cast<const u32x4_t *>(stage + rd_off + (c0 + r - seg0) * 256 + 16 * i);
+          d0 = mfma_bf16(dequant_fp4x8(W0[r][i], s0), as_bf16x8(B), d0);
+          d1 = mfma_bf16(dequant_fp4x8(W1[r][i], s1), as_bf16x8(B), d1);
         }
         const int cn = c0 + kRing + r;
         const bool ok = cn < nch;
         W0[r] = ld_b128(rw, ok ? o0 + ws * cn : kOob);
         W1[r] = ld_b128(rw, ok ? o1 + ws * cn : kOob);
       }
-      S0 = N0;
-      S1 = N1;
+#pragma unroll
+      for (int q = 0; q < kRing / 4; ++q) {
+        S0[q] = N0[q];
+        S1[q] = N1[q];
+      }
     }
     __syncthreads();
   }

@@ -47,6 +47,16 @@ __device__ __forceinline__ void dequant_fp4x32(u32x4_t v, float scale, bf16x8_t 
   }
 }
 
+// Group d of dequant_fp4x32: 4 packed E2M1 bytes (8 codes) times the block
+// scale -> 8 bf16.
+__device__ __forceinline__ bf16x8_t dequant_fp4x8(uint32_t v, float scale) {
+  bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 0);
+  bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 1);
+  bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 2);
+  bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 3);
+  return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 // D[16x16] += A[16 x 32] * B[32 x 16] in fp32.  Lane l holds row (l % 16) of
 // A and column (l % 16) of B, contraction elements 8*(l/16) .. +8; it gets
 // back D rows 4*(l/16) .. +4 of column (l % 16).
