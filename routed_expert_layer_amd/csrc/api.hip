@@ -41,6 +41,7 @@ Layout layout_of(const mb_dims &d) {
   L.y = take(R * P * 4);
   L.ssq = take(R * (P / 32) * 4);
   L.moe_out = take(b * P * 2);
+  L.moe_rep = take((size_t)kMoeReplicas * b * P * 2);
   L.u = take(b * H * 2);
   L.partial = take((size_t)kMaxSplitK * b * wide * 4);
   L.pool_part = take((size_t)kMaxSplitK * b * P * 4);
@@ -228,6 +229,7 @@ BlockParams base_params(const mb_dims &d, const mb_weights *w, void *ws) {
   p.y = at<float>(ws, L.y);
   p.ssq = at<float>(ws, L.ssq);
   p.act = at<uint16_t>(ws, L.act);
+  p.moe_rep = at<uint16_t>(ws, L.moe_rep);
   p.pool_cnt = at<unsigned>(ws, L.pool_cnt);
   p.unpool_cnt = at<unsigned>(ws, L.unpool_cnt);
   p.sync = at<unsigned>(ws, L.sync);

@@ -343,6 +343,35 @@ __device__ __forceinline__ unsigned long long wave_max_key(unsigned long long ke
          (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
 }
 
+// Wave-wide fp32 sum on every lane, by the same DPP tree as wave_max_key.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float sum_step(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF,
+                                                                   false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = sum_step<0x111, 0xF>(v);
+  v = sum_step<0x112, 0xF>(v);
+  v = sum_step<0x114, 0xF>(v);
+  v = sum_step<0x118, 0xF>(v);
+  v = sum_step<0x142, 0xA>(v);
+  v = sum_step<0x143, 0xC>(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Workgroup fp32 sum (fixed order: the wave trees, then the waves in order)
+// through red[slot * kWaves ..]; calls with different slots need no barrier
+// between them.
+__device__ __forceinline__ float wg_sum(float v, float *red, int slot) {
+  v = wave_sum_dpp(v);
+  if (tid() % MB_WAVE == 0) red[slot * kWaves + tid() / MB_WAVE] = v;
+  __syncthreads();
+  float t = red[slot * kWaves];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) t += red[slot * kWaves + w];
+  return t;
+}
+
 // One row's routing by one wave from its fp32 logits l[i] and expert biases
 // bias[i] (expert lane + 64 i): multiplier, scores, keys = score + bias; then
 // k rounds, each taking the largest remaining order key (the keys are
@@ -719,7 +748,7 @@ __device__ __forceinline__ void prenorm_task(const BlockParams &p, const Deps &d
       ss += a * a + b * b;
     }
   }
-  ss = block_sum(ss, red);
+  ss = wg_sum(ss, red, 0);
   const float rs = 1.0f / sqrtf(ss / (float)p.P + p.norm_eps);
   for (int i0 = 2 * tid(); i0 < p.P; i0 += 512 * kBoundBatch) {
     uint32_t v[kBoundBatch], w[kBoundBatch];
@@ -1009,7 +1038,7 @@ __device__ __forceinline__ void fin_task(const BlockParams &p, const Deps &d, co
   __syncthreads();
   stamp(p, 19);
   float *coef = reinterpret_cast<float *>(lds);  // [k]
-  const rsrc_t rss = make_rsrc(p.ssq), ry = make_rsrc(p.y), ro = make_rsrc(p.moe_out);
+  const rsrc_t rss = make_rsrc(p.ssq), ry = make_rsrc(p.y);
   f32x4_t yv[kMaxTopK];
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j)
@@ -1039,7 +1068,15 @@ __device__ __forceinline__ void fin_task(const BlockParams &p, const Deps &d, co
     const float o1 = acc[1] * bf16_bits_to_f32(pw[0] >> 16);
     const float o2 = acc[2] * bf16_bits_to_f32(pw[1] & 0xFFFFu);
     const float o3 = acc[3] * bf16_bits_to_f32(pw[1] >> 16);
-    st_co8(ro, (uint32_t)(((size_t)t * P + p4) * 2), u32x2_t{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)});
+    const u32x2_t v = u32x2_t{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+    const uint32_t off = (uint32_t)(((size_t)t * P + p4) * 2);
+    *reinterpret_cast<u32x2_t *>(reinterpret_cast<unsigned char *>(p.moe_out) + off) = v;
+    // Copies for the unpooler tasks, each reading the one its workgroup
+    // index selects: hundreds of workgroups reading one copy queue on it.
+    const rsrc_t rr = make_rsrc(p.moe_rep);
+    const uint32_t rep_bytes = (uint32_t)(p.b * P * 2);
+#pragma unroll
+    for (int c = 0; c < kMoeReplicas; ++c) st_co8(rr, off + rep_bytes * c, v);
   }
   signal_step(d, kCtrFin);
   stamp(p, 21);
@@ -1138,7 +1175,7 @@ __device__ __forceinline__ void boundary_task(const BlockParams &p, const Deps &
     const bool in = h * 2 < H2;
     wv[m] = p.next_norm_w ? ld_b64(make_rsrc(p.next_norm_w), in ? h * 2 : kOob) : u32x2_t{0x3F803F80u, 0x3F803F80u};
   }
-  ss = block_sum(ss, red);
+  ss = wg_sum(ss, red, 0);
   const float rsu = 1.0f / sqrtf(ss / (float)H + p.norm_eps);
   float s2 = 0.f;
 #pragma unroll
@@ -1154,7 +1191,7 @@ __device__ __forceinline__ void boundary_task(const BlockParams &p, const Deps &
       s2 += sv[m][i] * sv[m][i];
     }
   }
-  s2 = block_sum(s2, red);
+  s2 = wg_sum(s2, red, 1);
   const float rss = 1.0f / sqrtf(s2 / (float)H + p.norm_eps);
 #pragma unroll
   for (int m = 0; m < NG; ++m) {
@@ -1299,8 +1336,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       if (step == 8) {
         fin_task(p, d, R, i, scratch);
       } else if (step == 9) {
-        proj_task<true>(d, p.moe_out, p.unpool_w, p.u, p.b, p.H, p.P, p.unpool_ks, p.unpool_part, p.unpool_cnt,
-                         kCtrFin, p.n_fin, false, i, true, scratch);
+        proj_task<true>(d, p.n_fin > 0 ? p.moe_rep + (size_t)(blockIdx.x % kMoeReplicas) * p.b * p.P : p.moe_out,
+                        p.unpool_w, p.u, p.b, p.H, p.P, p.unpool_ks, p.unpool_part, p.unpool_cnt, kCtrFin, p.n_fin,
+                        false, i, true, scratch);
         signal_step(d, kCtrUnpool);
         stamp(p, 16);
       } else {

@@ -69,6 +69,7 @@ inline size_t sync_words(int E, int rows) {
 }
 
 constexpr int kFinChunk = 512;  // features per finalize task
+constexpr int kMoeReplicas = 8;  // copies of the MoE output for the unpooler tasks
 constexpr int kBlockMaxExperts = 256;  // larger expert counts use the per-step kernels
 constexpr int kTimelineSlots = 32;
 constexpr int kBlockGroupsPerCu = 3;  // resident workgroups per CU (one wave per SIMD each)
@@ -126,7 +127,7 @@ struct BlockParams {
   // workspace
   float *logits_f;  // the router's fp32 logits
   float *pool_part, *unpool_part, *y, *ssq;
-  uint16_t *act;
+  uint16_t *act, *moe_rep;  // moe_rep: kMoeReplicas copies of [b, P]
   unsigned *pool_cnt, *unpool_cnt, *sync;
   int64_t *timeline;  // optional [grid][kTimelineSlots]
 };

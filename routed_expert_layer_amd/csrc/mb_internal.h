@@ -18,7 +18,7 @@ constexpr int kMaxSplitK = 8;          // split-K factor of the bf16 projections
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct Layout {
   size_t sync, logits, ids, wts, count, offset, route_list, active, n_active;
-  size_t h, act, y, ssq, moe_out, u, partial;
+  size_t h, act, y, ssq, moe_out, moe_rep, u, partial;
   size_t pool_part, unpool_part, pool_cnt, unpool_cnt, total;
 };
 
