@@ -53,9 +53,13 @@ constexpr int kWaves = kThreads / MB_WAVE;
 static_assert(kWaves == kBlockWaves, "routing LDS is laid out per wave");
 static_assert(kRouterRowBlock == kWaves, "a router task gives each wave one row");
 constexpr int kPoolMG = 4;      // 16-row groups per projection pass
-constexpr int kRing = 4;        // 128-element weight chunks a wave keeps in flight
-static_assert(kRing % 4 == 0, "one 16-byte scale load covers four chunks");
-static_assert(kSegChunks % kRing == 0, "activation segments hold whole rounds of chunks");
+// 128-element weight chunks a wave keeps in flight in an up / a down unit (a
+// down unit, half the size, waits for its expert's up units: more of it is
+// requested before that wait).
+constexpr int kRingUp = 4, kRingDown = 4;
+static_assert(kRingUp % 4 == 0 && kRingDown % 4 == 0, "one 16-byte scale load covers four chunks");
+static_assert(kSegChunks % kRingUp == 0 && kSegChunks % kRingDown == 0,
+              "activation segments hold whole rounds of chunks");
 constexpr int kProjBatch = 8;   // 32-element projection chunks a wave requests at once
 constexpr int kRouterBatch = 16;  // router loads a thread requests at once
 constexpr int kBoundBatch = 4;   // pre-norm element groups a thread requests at once
@@ -476,16 +480,27 @@ __device__ __forceinline__ void route_dispatch(const BlockParams &p, const Route
   else route_rows<4>(p, R, t0, t1);
 }
 
+// Inclusive prefix sum over the wave's 64 lanes (DPP: row shifts 1, 2, 4, 8,
+// then the row broadcasts 15 and 31 add the earlier rows' totals).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int scan_step(int v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v = scan_step<0x111, 0xF>(v);
+  v = scan_step<0x112, 0xF>(v);
+  v = scan_step<0x114, 0xF>(v);
+  v = scan_step<0x118, 0xF>(v);
+  v = scan_step<0x142, 0xA>(v);
+  v = scan_step<0x143, 0xC>(v);
+  return v;
+}
+
 // Exclusive prefix sum over the workgroup of one value per thread, in a fixed
 // order; `total` receives the sum.  `red` holds kWaves ints.
 __device__ __forceinline__ int wg_excl_scan(int v, int *red, int &total) {
   const int lane = tid() % MB_WAVE, wave = tid() / MB_WAVE;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < MB_WAVE; o <<= 1) {
-    const int y = __shfl_up(x, o, MB_WAVE);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(v);
   __syncthreads();
   if (lane == MB_WAVE - 1) red[wave] = x;
   __syncthreads();
@@ -502,16 +517,17 @@ __device__ __forceinline__ int wg_excl_scan(int v, int *red, int &total) {
 // independent of order), popcount counts, exclusive scans for offsets and
 // the active list, and route (t, j) of expert e at offset[e] + the number of
 // earlier rows that chose e (routes sorted by (expert, t*k + j)).
+// Row t of route r = t k + j joins expert e's bitmap (R.bits zeroed at the
+// start of the launch).
+__device__ __forceinline__ void mark_route(const BlockParams &p, const RouteLds &R, int r, int e) {
+  const int W = (p.b + 63) / 64, t = r / p.k;
+  atomicOr(&R.bits[e * W + t / 64], 1ull << (t & 63));
+}
+
+// (Expects every route marked, and a barrier since.)
 __device__ __forceinline__ void group_routes(const BlockParams &p, const RouteLds &R, bool out) {
   const int W = (p.b + 63) / 64;
   const int Rn = p.b * p.k;
-  for (int i = tid(); i < p.E * W; i += kThreads) R.bits[i] = 0ull;
-  __syncthreads();
-  for (int r = tid(); r < Rn; r += kThreads) {
-    const int t = r / p.k, e = R.ids[r];
-    atomicOr(&R.bits[e * W + t / 64], 1ull << (t & 63));
-  }
-  __syncthreads();
   const int e0 = tid() * 4;
   int c[4], csum = 0, asum = 0;
 #pragma unroll
@@ -523,9 +539,11 @@ __device__ __forceinline__ void group_routes(const BlockParams &p, const RouteLd
     csum += c[q];
     asum += c[q] > 0 ? 1 : 0;
   }
-  int tot_c = 0, tot_a = 0;
-  int oc = wg_excl_scan(csum, R.red, tot_c);
-  int oa = wg_excl_scan(asum, R.red, tot_a);
+  // Counts (< 2^16) and active flags in one scan: count in the low half.
+  int tot = 0;
+  const int packed = wg_excl_scan(csum | (asum << 16), R.red, tot);
+  int oc = packed & 0xFFFF, oa = packed >> 16;
+  const int tot_c = tot & 0xFFFF, tot_a = tot >> 16;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = e0 + q;
@@ -610,8 +628,10 @@ __device__ __forceinline__ void prepare_routing(const BlockParams &p, const Deps
   stamp(p, 13);
   const rsrc_t ri = make_rsrc(p.ids), rw = make_rsrc(p.wts);
   for (int i = tid(); i < p.b * p.k; i += kThreads) {
-    R.ids[i] = (int)ld_co4(ri, (uint32_t)(i * 4));
+    const int e = (int)ld_co4(ri, (uint32_t)(i * 4));
+    R.ids[i] = e;
     R.w[i] = __uint_as_float(ld_co4(rw, (uint32_t)(i * 4)));
+    mark_route(p, R, i, e);
   }
   __syncthreads();
   group_routes(p, R, out);
@@ -840,7 +860,7 @@ __device__ __forceinline__ MxTiles mx_packed(const uint8_t *codes, const uint8_t
 //
 // Chunks past nch have zero weights and zero activations and add nothing,
 // so the loop has no branches on the data.
-template <typename Wait, typename RowOff>
+template <int kRing, typename Wait, typename RowOff>
 __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, rsrc_t ra, RowOff row_off, unsigned char *stage,
                                         f32x4_t &d0, f32x4_t &d1, int prog, int prog_total, Wait wait) {
   const int lane = tid() % MB_WAVE, g = lane >> 4;
@@ -875,19 +895,23 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, rsrc_t ra, Ro
     // This segment's activations, chunks rounded up to whole rounds.
     const int segn = min(kSegChunks, nch - seg0);
     const int ppr = ((segn + kRing - 1) / kRing) * kRing * 16;  // 16-byte pieces per row
-    u32x4_t v[kSegLoads];
+    // In two batches of half the pieces (registers).
 #pragma unroll
-    for (int n = 0; n < kSegLoads; ++n) {
-      const int q = (int)tid() + kThreads * n;
-      const int m = q / ppr, pc = q % ppr;
-      const uint32_t ro = m < kStageRows ? row_off(m) : kOob;
-      v[n] = ld_co16(ra, (ro != kOob && pc < segn * 16) ? ro + (uint32_t)(seg0 * 256 + pc * 16) : kOob);
-    }
+    for (int n0 = 0; n0 < kSegLoads; n0 += kSegLoads / 2) {
+      u32x4_t v[kSegLoads / 2];
 #pragma unroll
-    for (int n = 0; n < kSegLoads; ++n) {
-      const int q = (int)tid() + kThreads * n;
-      const int m = q / ppr, pc = q % ppr;
-      if (m < kStageRows) *reinterpret_cast<u32x4_t *>(stage + m * kSegRowBytes + pc * 16) = v[n];
+      for (int n = 0; n < kSegLoads / 2; ++n) {
+        const int q = (int)tid() + kThreads * (n0 + n);
+        const int m = q / ppr, pc = q % ppr;
+        const uint32_t ro = m < kStageRows ? row_off(m) : kOob;
+        v[n] = ld_co16(ra, (ro != kOob && pc < segn * 16) ? ro + (uint32_t)(seg0 * 256 + pc * 16) : kOob);
+      }
+#pragma unroll
+      for (int n = 0; n < kSegLoads / 2; ++n) {
+        const int q = (int)tid() + kThreads * (n0 + n);
+        const int m = q / ppr, pc = q % ppr;
+        if (m < kStageRows) *reinterpret_cast<u32x4_t *>(stage + m * kSegRowBytes + pc * 16) = v[n];
+      }
     }
     __syncthreads();
     for (int c0 = seg0; c0 < seg0 + segn; c0 += kRing) {
@@ -943,7 +967,7 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
   const int nch = P / 128;
   for (int m0 = 0; m0 < nrows; m0 += kStageRows) {
     f32x4_t gs, us;
-    mx_pair(
+    mx_pair<kRingUp>(
         T, nch, rh,
         [&](int m) { return m0 + m < nrows ? (uint32_t)((R.rl[row0 + m0 + m] / p.k) * P) * 2u : kOob; }, stage,
         gs, us, prog, prog_total, [&]() {
@@ -988,7 +1012,7 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
   bool ready = false;
   for (int m0 = 0; m0 < nrows; m0 += kStageRows) {
     f32x4_t y0, y1;
-    mx_pair(
+    mx_pair<kRingDown>(
         T, nch, ract, [&](int m) { return m0 + m < nrows ? (uint32_t)((row0 + m0 + m) * I) * 2u : kOob; }, stage,
         y0, y1, prog, prog_total, [&]() {
           if (!ready) {
@@ -1228,6 +1252,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   (void)p_arg;  // read through kparams()
   stamp(kparams(), 0);
   const int G = gridDim.x;
+  {
+    // The grouping's per-expert row bitmaps start empty.
+    const BlockParams &p = kparams();
+    if (p.needs_routing && !p.route_given) {
+      const RouteLds R = route_lds(p, lds);
+      for (int i = tid(); i < p.E * ((p.b + 63) / 64); i += kThreads) R.bits[i] = 0ull;
+    }
+    __syncthreads();
+  }
 
   // 1. Workgroup tasks before routing.
   {
