@@ -96,6 +96,113 @@ def cpu_baseline(blk, seconds: float) -> dict:
                       f"fp64 oracle, {el:.1f} s; cores = its BLAS thread pool"}
 
 
+def sweep(args) -> int:
+    """Every workload once, each on its own seeded weight sets: microseconds per
+    block, rows/s and algorithmic HBM bandwidth for c0, c2 (both skew
+    readings), each c3 row bucket (uniform and calibrated skew) and the
+    60-layer c4 stack.  One JSON line per case on stdout."""
+    import numpy as np
+    import torch
+
+    import routed_expert_layer_amd as rel
+    import synth
+    from synth.device import dims_kwargs, to_tensor, upload_weights
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    def prepare(blocks):
+        dims = rel.make_dims(**dims_kwargs(blocks[0].dims))
+        tensors = [upload_weights(b, dev) for b in blocks]
+        weights = [rel.make_weights(**t) for t in tensors]
+        if args.layout == "packed":
+            for t, w in zip(tensors, weights):
+                t["experts_packed"] = rel.pack_experts(dims, w, dev)
+            weights = [rel.make_weights(**t) for t in tensors]
+        torch.cuda.synchronize()
+        return dims, tensors, weights
+
+    def n_active(dims, x, w, stream, ws):
+        n = torch.zeros(1, dtype=torch.int32, device=dev)
+        xn = torch.empty((x.shape[0], x.shape[1]), dtype=torch.bfloat16, device=dev)
+        rel.mb_moe_block(dims, x, w, stream.clone(), xn, ws, taps=rel.make_taps(n_active=n))
+        torch.cuda.synchronize()
+        return int(n.item())
+
+    def timed(fn, steps, warmup):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    def report(case, d, us, actives, blocks_per_step=1):
+        b_alg = float(np.mean([algorithmic_bytes(d, a) for a in actives])) * blocks_per_step
+        gbs = b_alg / (us * 1e-6) / 1e9
+        line = {"case": case, "rows": d.rows, "us_per_step": round(us, 2),
+                "blocks_per_step": blocks_per_step,
+                "rows_per_s": round(d.rows * blocks_per_step / (us * 1e-6), 1),
+                "algorithmic_bytes_per_step": int(b_alg), "achieved_GBps": round(gbs, 1),
+                "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4), "active_experts": actives,
+                "expert_layout": args.layout}
+        print(json.dumps(line), flush=True)
+        print(f"[sweep] {case}: {us:.1f} us/step, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)",
+              file=sys.stderr, flush=True)
+
+    def run_block_case(case, blocks, steps, warmup=10):
+        d = blocks[0].dims
+        dims, tensors, weights = prepare(blocks)
+        x, stream = to_tensor(blocks[0].x, dev), to_tensor(blocks[0].stream, dev)
+        ws = rel.workspace(dims, dev)
+        xn = torch.empty((d.rows, d.hidden), dtype=torch.bfloat16, device=dev)
+        actives = [n_active(dims, x, w, stream, ws) for w in weights]
+        S = len(weights)
+        us = timed(lambda i: rel.mb_moe_block(dims, x, weights[i % S], stream, xn, ws), steps, warmup)
+        report(case, d, us, actives)
+
+    print("[sweep] c0", file=sys.stderr, flush=True)
+    run_block_case("c0 tiny block", [synth.make_block("c0")], 1000)
+    for skew in ("calibrated", "literal"):
+        print(f"[sweep] c2 {skew}: generating 2 weight sets", file=sys.stderr, flush=True)
+        blocks = [synth.make_block("c2", seed=s, skew=skew) for s in (2, 1002)]
+        run_block_case(f"c2 b=64 softmax, skew {skew}", blocks, 100)
+        del blocks
+        torch.cuda.empty_cache()
+    for skew in (None, "calibrated"):
+        print(f"[sweep] c3 skew={skew}: generating 2 weight sets", file=sys.stderr, flush=True)
+        full = [synth.make_c3_block(skew, seed=s) for s in (3, 1003)]
+        for b in synth.inputs.C3_BUCKETS:
+            run_block_case(f"c3 b={b} sigmoid, {skew or 'uniform'}", [f.rows(b) for f in full], 100)
+        del full
+        torch.cuda.empty_cache()
+    # c4: 60 chained layers (x_next feeds the next layer); 8 distinct layer
+    # weight sets cycled, about 32 times the Infinity Cache.
+    n_distinct = 8
+    print(f"[sweep] c4: generating {n_distinct} layer weight sets", file=sys.stderr, flush=True)
+    layers = [synth.make_c4_layer(l) for l in range(n_distinct)]
+    x0, s0 = synth.make_c4_stream()
+    d = layers[0].dims
+    dims, tensors, weights = prepare(layers)
+    x = to_tensor(x0, dev)
+    stream = to_tensor(s0, dev)
+    ws = rel.workspace(dims, dev)
+    xs = [x.clone(), torch.empty_like(x)]
+    actives = [n_active(dims, x, w, stream, ws) for w in weights]
+
+    def stack(_):
+        for layer in range(60):
+            rel.mb_moe_block(dims, xs[layer % 2], weights[layer % n_distinct], stream, xs[(layer + 1) % 2], ws)
+
+    us = timed(stack, 10, 2)
+    report("c4 60-layer stack b=32 (per stack)", d, us, actives, blocks_per_step=60)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +218,9 @@ def main() -> int:
                     help="expert weights streamed from mb_pack_experts' layout (prepared once per "
                          "weight set, outside the timed region) or from the caller's layout")
     ap.add_argument("--print-source-hash", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the c1 metric, time every workload (c0, c2, c3 buckets, c4 "
+                         "stack) and print one JSON line per case")
     args = ap.parse_args()
     if args.print_source_hash:
         print(kernel_source_hash())
@@ -119,6 +229,9 @@ def main() -> int:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
               "(the block has no multi-GPU path in this build)", file=sys.stderr)
         return 2
+
+    if args.sweep:
+        return sweep(args)
 
     import numpy as np
     import torch
