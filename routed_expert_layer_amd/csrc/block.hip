@@ -58,7 +58,7 @@ constexpr int kPoolMG = 4;      // 16-row groups per projection pass
 // requested before that wait).
 constexpr int kRingUp = 4, kRingDown = 4;
 static_assert(kRingUp % 4 == 0 && kRingDown % 4 == 0, "one 16-byte scale load covers four chunks");
-static_assert(kSegChunks % kRingUp == 0 && kSegChunks % kRingDown == 0,
+static_assert((kStageChunkRows / 32) % kRingUp == 0 && (kStageChunkRows / 32) % kRingDown == 0,
               "activation segments hold whole rounds of chunks");
 constexpr int kProjBatch = 8;   // 32-element projection chunks a wave requests at once
 constexpr int kRouterBatch = 16;  // router loads a thread requests at once
@@ -840,8 +840,12 @@ __device__ __forceinline__ MxTiles mx_packed(const uint8_t *codes, const uint8_t
   return MxTiles{make_rsrc(codes), make_rsrc(scales), o, o + 1024u, so, so + 256u, 2048u, 128u, true};
 }
 
+// Activation rows per pass over a unit's weights: 8, 16 or 32 (as one or two
+// 16-column MFMA blocks); more rows take several passes.
+__device__ __forceinline__ int pass_rows(int nrows) { return nrows <= 8 ? 8 : nrows <= 16 ? 16 : 32; }
+
 // One wave: D0 = W0 B and D1 = W1 B for two 16-row MXFP4 weight tiles over
-// nch 128-element chunks and up to kStageRows activation rows (bf16).  The
+// nch 128-element chunks and a pass of pr activation rows (bf16).  The
 // four waves of a workgroup call this together for units of the same expert
 // (so with the same rows): the activations are staged once per workgroup.
 //
@@ -852,17 +856,19 @@ __device__ __forceinline__ MxTiles mx_packed(const uint8_t *codes, const uint8_t
 // once the activations' producers are done).
 //
 // Activations (written by other workgroups of the launch, so read
-// coherently): the rows' elements of up to kSegChunks chunks at a time are
+// coherently): the rows' elements of up to kStageChunkRows / pr chunks at a time are
 // loaded by the whole workgroup in 16-byte pieces into `stage` (row m at
-// m * kSegRowBytes; rows past the pass and chunks past nch as zeros), then
-// each wave reads its MFMA operand from there: lane l reads row l % 8.
+// m * (its chunks * 256 + 16); rows past the pass and chunks past nch as zeros), then
+// each wave reads its MFMA operand from there: lane l reads row l % 8 (pr 8)
+// or l % 16 (of each 16-row block).
 // row_off(m) is the byte offset of pass row m's element 0, or kOob.
 //
 // Chunks past nch have zero weights and zero activations and add nothing,
 // so the loop has no branches on the data.
 template <int kRing, typename Wait, typename RowOff>
-__device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, rsrc_t ra, RowOff row_off, unsigned char *stage,
-                                        f32x4_t &d0, f32x4_t &d1, int prog, int prog_total, Wait wait) {
+__device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, int pr, rsrc_t ra, RowOff row_off,
+                                        unsigned char *stage, f32x4_t (&d0)[2], f32x4_t (&d1)[2], int prog,
+                                        int prog_total, Wait wait) {
   const int lane = tid() % MB_WAVE, g = lane >> 4;
   const rsrc_t rw = T.rw, rs = T.rs;
   const uint32_t o0 = T.o0, o1 = T.o1, so0 = T.so0, so1 = T.so1, ws = T.wstride, ss = T.sstride;
@@ -888,12 +894,18 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, rsrc_t ra, Ro
     S1[q] = scales(so1, 4 * q);
   }
   wait();
-  d0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  d1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const uint32_t rd_off = (uint32_t)((lane & 7) * kSegRowBytes + 64 * g);
-  for (int seg0 = 0; seg0 < nch; seg0 += kSegChunks) {
+  // pr rows (8, 16 or 32) in segments of seg chunks: pr * seg = 128.
+  const int seg = kStageChunkRows / pr, srow = seg * 256 + 16;  // row stride in the stage
+  const int nb = pr > 16 ? 2 : 1;                             // 16-row column blocks
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    d0[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    d1[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const uint32_t rd_off = (uint32_t)((lane & (pr == 8 ? 7 : 15)) * srow + 64 * g);
+  for (int seg0 = 0; seg0 < nch; seg0 += seg) {
     // This segment's activations, chunks rounded up to whole rounds.
-    const int segn = min(kSegChunks, nch - seg0);
+    const int segn = min(seg, nch - seg0);
     const int ppr = ((segn + kRing - 1) / kRing) * kRing * 16;  // 16-byte pieces per row
     // In two batches of half the pieces (registers).
 #pragma unroll
@@ -903,14 +915,14 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, rsrc_t ra, Ro
       for (int n = 0; n < kSegLoads / 2; ++n) {
         const int q = (int)tid() + kThreads * (n0 + n);
         const int m = q / ppr, pc = q % ppr;
-        const uint32_t ro = m < kStageRows ? row_off(m) : kOob;
+        const uint32_t ro = m < pr ? row_off(m) : kOob;
         v[n] = ld_co16(ra, (ro != kOob && pc < segn * 16) ? ro + (uint32_t)(seg0 * 256 + pc * 16) : kOob);
       }
 #pragma unroll
       for (int n = 0; n < kSegLoads / 2; ++n) {
         const int q = (int)tid() + kThreads * (n0 + n);
         const int m = q / ppr, pc = q % ppr;
-        if (m < kStageRows) *reinterpret_cast<u32x4_t *>(stage + m * kSegRowBytes + pc * 16) = v[n];
+        if (m < pr) *reinterpret_cast<u32x4_t *>(stage + m * srow + pc * 16) = v[n];
       }
     }
     __syncthreads();
@@ -928,9 +940,16 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, rsrc_t ra, Ro
         const float s1 = e8m0_to_f32((S1[r / 4][r % 4] >> (8 * g)) & 0xFFu);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const u32x4_t B = *reinterpret_cast<const u32x4_t *>(stage + rd_off + (c0 + r - seg0) * 256 + 16 * i);
-          d0 = mfma_bf16(dequant_fp4x8(W0[r][i], s0), as_bf16x8(B), d0);
-          d1 = mfma_bf16(dequant_fp4x8(W1[r][i], s1), as_bf16x8(B), d1);
+          const unsigned char *bp = stage + rd_off + (c0 + r - seg0) * 256 + 16 * i;
+          const bf16x8_t x0 = dequant_fp4x8(W0[r][i], s0), x1 = dequant_fp4x8(W1[r][i], s1);
+          const u32x4_t B = *reinterpret_cast<const u32x4_t *>(bp);
+          d0[0] = mfma_bf16(x0, as_bf16x8(B), d0[0]);
+          d1[0] = mfma_bf16(x1, as_bf16x8(B), d1[0]);
+          if (nb > 1) {
+            const u32x4_t B1 = *reinterpret_cast<const u32x4_t *>(bp + 16 * srow);
+            d0[1] = mfma_bf16(x0, as_bf16x8(B1), d0[1]);
+            d1[1] = mfma_bf16(x1, as_bf16x8(B1), d1[1]);
+          }
         }
         const int cn = c0 + kRing + r;
         const bool ok = cn < nch;
@@ -949,7 +968,7 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, rsrc_t ra, Ro
 
 // Up unit: w13 and the gated activation for (active expert, 16 act columns):
 // gate rows i0..i0+15 and up rows I+i0..I+i0+15 of the expert, over P, for
-// the expert's routes in passes of kStageRows.
+// the expert's routes in passes of pass_rows.
 __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, const RouteLds &R, int unit,
                                         bool &h_ready, unsigned char *stage, int &prog, int prog_total) {
   const int lane = tid() % MB_WAVE, g = lane >> 4, r16 = lane & 15;
@@ -965,10 +984,11 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
                       lane);
   const rsrc_t rh = make_rsrc(p.h), ract = make_rsrc(p.act);
   const int nch = P / 128;
-  for (int m0 = 0; m0 < nrows; m0 += kStageRows) {
-    f32x4_t gs, us;
+  const int pr = pass_rows(nrows);
+  for (int m0 = 0; m0 < nrows; m0 += pr) {
+    f32x4_t gs[2], us[2];
     mx_pair<kRingUp>(
-        T, nch, rh,
+        T, nch, pr, rh,
         [&](int m) { return m0 + m < nrows ? (uint32_t)((R.rl[row0 + m0 + m] / p.k) * P) * 2u : kOob; }, stage,
         gs, us, prog, prog_total, [&]() {
           if (!h_ready) {
@@ -977,16 +997,19 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
           }
         });
     prog += nch;
-    const int m = m0 + r16;
-    if (r16 < kStageRows && m < nrows) {
-      float o[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float z = gs[i];
-        o[i] = (z / (1.0f + expf(-z))) * us[i];
+    for (int b = 0; b < 2; ++b) {
+      const int m = m0 + 16 * b + r16;
+      if ((b == 0 || pr > 16) && (pr > 8 || r16 < 8) && m < nrows) {
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float z = gs[b][i];
+          o[i] = (z / (1.0f + expf(-z))) * us[b][i];
+        }
+        st_co8(ract, (uint32_t)((((size_t)(row0 + m)) * I + i0 + 4 * g) * 2),
+               u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
       }
-      st_co8(ract, (uint32_t)((((size_t)(row0 + m)) * I + i0 + 4 * g) * 2),
-             u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
     }
   }
   wave_signal(d.up(e));
@@ -1010,10 +1033,11 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
   const rsrc_t ract = make_rsrc(p.act), ry = make_rsrc(p.y), rss = make_rsrc(p.ssq);
   const int nch = I / 128;
   bool ready = false;
-  for (int m0 = 0; m0 < nrows; m0 += kStageRows) {
-    f32x4_t y0, y1;
+  const int pr = pass_rows(nrows);
+  for (int m0 = 0; m0 < nrows; m0 += pr) {
+    f32x4_t y0[2], y1[2];
     mx_pair<kRingDown>(
-        T, nch, ract, [&](int m) { return m0 + m < nrows ? (uint32_t)((row0 + m0 + m) * I) * 2u : kOob; }, stage,
+        T, nch, pr, ract, [&](int m) { return m0 + m < nrows ? (uint32_t)((row0 + m0 + m) * I) * 2u : kOob; }, stage,
         y0, y1, prog, prog_total, [&]() {
           if (!ready) {
             poll_ge(d, d.up(e), (unsigned)(I / 16));
@@ -1021,20 +1045,24 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
           }
         });
     prog += nch;
-    const int m = m0 + r16;
-    const bool valid = r16 < kStageRows && m < nrows;
-    float ss = 0.f;
-    if (valid) {
-      ss = y0[0] * y0[0] + y0[1] * y0[1] + y0[2] * y0[2] + y0[3] * y0[3];
-      ss += y1[0] * y1[0] + y1[1] * y1[1] + y1[2] * y1[2] + y1[3] * y1[3];
-    }
-    ss += __shfl_xor(ss, 16, MB_WAVE);
-    ss += __shfl_xor(ss, 32, MB_WAVE);
-    if (valid) {
-      const int r = R.rl[row0 + m];
-      st_co16(ry, (uint32_t)(((size_t)r * P + p0 + 4 * g) * 4), __builtin_bit_cast(u32x4_t, y0));
-      st_co16(ry, (uint32_t)(((size_t)r * P + p0 + 16 + 4 * g) * 4), __builtin_bit_cast(u32x4_t, y1));
-      if (g == 0) st_co4(rss, (uint32_t)(((size_t)r * tiles + tile) * 4), __float_as_uint(ss));
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      if (b == 1 && pr <= 16) break;
+      const int m = m0 + 16 * b + r16;
+      const bool valid = (pr > 8 || r16 < 8) && m < nrows;
+      float ss = 0.f;
+      if (valid) {
+        ss = y0[b][0] * y0[b][0] + y0[b][1] * y0[b][1] + y0[b][2] * y0[b][2] + y0[b][3] * y0[b][3];
+        ss += y1[b][0] * y1[b][0] + y1[b][1] * y1[b][1] + y1[b][2] * y1[b][2] + y1[b][3] * y1[b][3];
+      }
+      ss += __shfl_xor(ss, 16, MB_WAVE);
+      ss += __shfl_xor(ss, 32, MB_WAVE);
+      if (valid) {
+        const int r = R.rl[row0 + m];
+        st_co16(ry, (uint32_t)(((size_t)r * P + p0 + 4 * g) * 4), __builtin_bit_cast(u32x4_t, y0[b]));
+        st_co16(ry, (uint32_t)(((size_t)r * P + p0 + 16 + 4 * g) * 4), __builtin_bit_cast(u32x4_t, y1[b]));
+        if (g == 0) st_co4(rss, (uint32_t)(((size_t)r * tiles + tile) * 4), __float_as_uint(ss));
+      }
     }
   }
   wave_signal(d.down(e));

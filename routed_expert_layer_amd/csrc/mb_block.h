@@ -174,15 +174,13 @@ __device__ inline RouteLds route_lds(const BlockParams &p, unsigned char *base) 
   return r;
 }
 
-// Activation staging of the expert units, per workgroup: kStageRows rows of
-// up to kSegChunks chunks of 128 bf16, rows kSegRowBytes apart (16 bytes of
-// padding spread the rows over the LDS banks); each thread loads kSegLoads
-// 16-byte pieces of a segment.
-constexpr int kStageRows = 8;
-constexpr int kSegChunks = 16;
-constexpr int kSegRowBytes = kSegChunks * 256 + 16;
-constexpr int kSegLoads = kStageRows * kSegChunks * 16 / 256;
-constexpr size_t kStageBytes = (size_t)kStageRows * kSegRowBytes;
+// Activation staging of the expert units, per workgroup: pr rows (8, 16 or
+// 32) of up to kStageChunkRows / pr chunks of 128 bf16, with 16 bytes of
+// padding after each row (spreading the rows over the LDS banks); each thread
+// loads kSegLoads 16-byte pieces of a segment.
+constexpr int kStageChunkRows = 128;  // rows x chunks of one segment
+constexpr int kSegLoads = kStageChunkRows * 16 / 256;
+constexpr size_t kStageBytes = 32 * ((kStageChunkRows / 32) * 256 + 16);  // the largest of the three shapes
 constexpr size_t kProjScratchBytes = 4 * 4 * 64 * 16 + 64;
 constexpr size_t kBlockScratchBytes = kProjScratchBytes > kStageBytes ? kProjScratchBytes : kStageBytes;
 
