@@ -3,6 +3,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "mb_block.h"
 #include "mb_internal.h"
 #include "mb_sync.h"
@@ -44,7 +46,7 @@ Layout layout_of(const mb_dims &d) {
   L.moe_rep = take((size_t)kMoeReplicas * b * P * 2);
   L.u = take(b * H * 2);
   L.partial = take((size_t)kMaxSplitK * b * wide * 4);
-  L.pool_part = take((size_t)kMaxSplitK * b * P * 4);
+  L.pool_part = take((size_t)kMaxPoolSplit * b * P * 4);
   L.unpool_part = take((size_t)kMaxSplitK * b * H * 4);
   L.total = o;
   return L;
@@ -291,22 +293,27 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   // grouping.  (Every workgroup routing every row itself costs each of them
   // b/4 rows one after another, and has all of them read every logit.)
   const int n_route = (needs_routing && !st.route_given) ? (p.b + 3) / 4 : 0;
-  // The pooler is not split: its output is needed only once routing is
-  // done, and a split adds a partial store, a last-arrival round trip and a
-  // partial load before h is complete.
-  p.pool_ks = 1;
-  (void)n_prenorm;
+  // The pooler: wide tiles of 64 features, split along H so that the router,
+  // route and pooler tasks fill the workgroups about once (at least half of
+  // them for the pooler), each split a multiple of 32 elements.
+  {
+    const int groups = (p.P + 63) / 64;
+    const int slots = std::max(grid - n_router - n_route - n_prenorm, grid / 2);
+    int ks = std::min(kMaxPoolSplit, std::max(1, slots / groups));
+    while (ks > 1 && (p.H % ks != 0 || (p.H / ks) % 32 != 0)) --ks;
+    p.pool_ks = ks;
+  }
   p.unpool_ks = split_for(p.H / 16, p.P / 32, grid - n_fin - n_boundary);
-  p.n_pool_tiles = p.P / 16;
+  p.n_pool_tiles = (p.P + 63) / 64;
   p.needs_routing = needs_routing ? 1 : 0;
   p.routing_out = st.routing_out ? 1 : 0;
   p.route_given = st.route_given ? 1 : 0;
   p.n_router = n_router;
   p.n_logit_producers = p.n_router;
   p.n_route = n_route;
-  p.n_pool = st.pool ? (p.P / 16) * p.pool_ks : 0;
+  p.n_pool = st.pool ? p.n_pool_tiles * p.pool_ks : 0;
   p.n_prenorm = n_prenorm;
-  p.h_producers = st.pool ? (p.pre_norm_w ? p.b : p.P / 16) : 0;
+  p.h_producers = st.pool ? (p.pre_norm_w ? p.b : p.n_pool_tiles) : 0;
   p.has_up = st.experts ? 1 : 0;
   p.n_fin = n_fin;
   p.n_unpool = st.unpool ? (p.H / 16) * p.unpool_ks : 0;

@@ -644,6 +644,112 @@ __device__ __forceinline__ int *proj_flag(unsigned char *lds) {
   return reinterpret_cast<int *>(lds + kProjRedBytes);
 }
 
+// Wide projection tile: out[t, n] over features n0 = 64 gi .. +63 (wave w:
+// n0 + 16 w .. +15, its weights in the MFMA A operand), every row t, and the
+// contraction split q of ks (elements q kr .. + kr, kr = kdim / ks).  The
+// workgroup stages the activations a[t, k] of the split once, in segments,
+// in `stage` (read coherently when another workgroup of the launch wrote
+// them: kCoherentA); each wave streams its own weights kWideRing chunks of
+// 32 elements ahead.  Rows go in passes of up to 64 (four 16-row MFMA
+// blocks); features and rows past the ends load zeros and are not stored.
+// With ks == 1 the result goes to `out` in bf16, else the fp32 partial to
+// part[q].
+constexpr int kWideRing = 8;
+constexpr int kWideCols = 16 * kWaves;
+template <bool kCoherentA>
+__device__ __forceinline__ void proj_wide(rsrc_t ra, const uint16_t *w, int rows, int n_out, int kdim, int gi, int q,
+                                          int ks, float *part, uint16_t *out, unsigned char *stage) {
+  const int lane = (int)(tid() % MB_WAVE), wave = (int)(tid() / MB_WAVE), g = lane >> 4, r16 = lane & 15;
+  const int kr = kdim / ks, k0 = q * kr, nch = kr / 32;
+  const int f = gi * kWideCols + 16 * wave + r16;  // this lane's weight row
+  const rsrc_t rw = make_rsrc(w);
+  const uint32_t wrow = f < n_out ? (uint32_t)(((size_t)f * kdim + k0 + 8 * g) * 2) : kOob;
+  auto wload = [&](int c) { return ld_nt16(rw, (wrow != kOob && c < nch) ? wrow + (uint32_t)c * 64u : kOob); };
+  const rsrc_t ro = make_rsrc(out), rp = make_rsrc(part);
+  for (int t0 = 0; t0 < rows; t0 += 64) {
+    const int rp_ = min(64, rows - t0), nb = (rp_ + 15) / 16;
+    // Segment length (elements, a multiple of 32 kWideRing): rows x segment fits the stage.
+    const int seg = min((rp_ <= 16 ? 1024 : rp_ <= 32 ? 512 : 256), ((kr + 255) / 256) * 256);
+    const int srow = seg * 2 + 16;
+    u32x4_t W[kWideRing];
+#pragma unroll
+    for (int r = 0; r < kWideRing; ++r) W[r] = wload(r);
+    f32x4_t acc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nch; s0 += seg / 32) {
+      // Rows t0 .. t0 + 16 nb, elements k0 + 32 s0 .. + seg, in 16-byte pieces.
+      const int ppr = seg / 8, pieces = 16 * nb * ppr;
+      for (int i0 = 0; i0 < pieces; i0 += kThreads * 4) {
+        u32x4_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + (int)tid() + kThreads * u;
+          const int m = i / ppr, pc = i % ppr;
+          const int t = t0 + m, k = 32 * s0 + 8 * pc;
+          const bool in = i < pieces && t < rows && k < kr;
+          const uint32_t off = in ? (uint32_t)(((size_t)t * kdim + k0 + k) * 2) : kOob;
+          v[u] = kCoherentA ? ld_co16(ra, off) : ld_b128(ra, off);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + (int)tid() + kThreads * u;
+          if (i < pieces) *reinterpret_cast<u32x4_t *>(stage + (i / ppr) * srow + (i % ppr) * 16) = v[u];
+        }
+      }
+      __syncthreads();
+      for (int c0 = s0; c0 < s0 + seg / 32 && c0 < nch; c0 += kWideRing) {
+#pragma unroll
+        for (int r = 0; r < kWideRing; ++r) {
+          const unsigned char *bp = stage + r16 * srow + ((c0 + r - s0) * 32 + 8 * g) * 2;
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            if (b < nb)
+              acc[b] = mfma_bf16(as_bf16x8(W[r]), as_bf16x8(*reinterpret_cast<const u32x4_t *>(bp + 16 * b * srow)),
+                                 acc[b]);
+          W[r] = wload(c0 + kWideRing + r);
+        }
+      }
+      __syncthreads();
+    }
+    // Lane: features 4 g .. + 3 of the wave's 16 (rows of D), row r16 of each block.
+    const int n = gi * kWideCols + 16 * wave + 4 * g;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int t = t0 + 16 * b + r16;
+      if (b >= nb || t >= rows || n >= n_out) continue;
+      if (ks == 1)
+        st_co8(ro, (uint32_t)(((size_t)t * n_out + n) * 2),
+               u32x2_t{pack_bf16x2(acc[b][0], acc[b][1]), pack_bf16x2(acc[b][2], acc[b][3])});
+      else
+        st_co16(rp, (uint32_t)((((size_t)q * rows + t) * n_out + n) * 4), __builtin_bit_cast(u32x4_t, acc[b]));
+    }
+  }
+}
+
+// The last split of a wide tile: out[t, n] = bf16(sum over q of part[q][t][n]),
+// in split order, for the tile's 64 features and every row.
+__device__ __forceinline__ void proj_wide_sum(const float *part, uint16_t *out, int rows, int n_out, int gi,
+                                              int ks) {
+  const rsrc_t rp = make_rsrc(part), ro = make_rsrc(out);
+  for (int idx = (int)tid(); idx < rows * (kWideCols / 4); idx += kThreads) {
+    const int t = idx / (kWideCols / 4), n = gi * kWideCols + 4 * (idx % (kWideCols / 4));
+    if (n >= n_out) continue;
+    f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int q0 = 0; q0 < ks; q0 += 8) {
+      f32x4_t pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        pv[u] = __builtin_bit_cast(
+            f32x4_t, ld_co16(rp, q0 + u < ks ? (uint32_t)((((size_t)(q0 + u) * rows + t) * n_out + n) * 4) : kOob));
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (q0 + u < ks) v = (q0 + u == 0) ? pv[u] : v + pv[u];
+    }
+    st_co8(ro, (uint32_t)(((size_t)t * n_out + n) * 2), u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
+  }
+}
+
 // One task of out[t, n] = bf16(sum_k a[t, k] w[n, k]): a 16-feature tile and
 // contraction split ks of ks_count, the split's 32-element chunks dealt to the
 // four waves, each requesting up to kProjBatch chunks at once; 16-row groups
@@ -1320,9 +1426,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       } else if (step == 2) {
         route_task(p, d, R, i);
       } else if (step == 3) {
-        if (proj_task<false>(d, p.x, p.pool_w, p.h, p.b, p.P, p.H, p.pool_ks, p.pool_part, p.pool_cnt, 0, 0, false,
-                             i, false, scratch))
-          signal_step(d, kCtrPool);
+        // Pooler: wide tiles, the splits added by the last to finish.
+        const int gi = i / p.pool_ks, q = i % p.pool_ks;
+        proj_wide<false>(make_rsrc(p.x), p.pool_w, p.b, p.P, p.H, gi, q, p.pool_ks, p.pool_part, p.h, scratch);
+        bool done = true;
+        if (p.pool_ks > 1) {
+          done = last_arrival(&p.pool_cnt[gi], (unsigned)p.pool_ks, proj_flag(scratch));
+          if (done) {
+            proj_wide_sum(p.pool_part, p.h, p.b, p.P, gi, p.pool_ks);
+            if (tid() == 0) __hip_atomic_store(&p.pool_cnt[gi], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+        if (done) signal_step(d, kCtrPool);
         stamp(p, 7);
       } else {
         prenorm_task(p, d, i, scratch);

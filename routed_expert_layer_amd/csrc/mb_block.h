@@ -69,6 +69,7 @@ inline size_t sync_words(int E, int rows) {
 }
 
 constexpr int kFinChunk = 512;  // features per finalize task
+constexpr int kMaxPoolSplit = 32;  // contraction splits of the pooler
 constexpr int kMoeReplicas = 8;  // copies of the MoE output for the unpooler tasks
 constexpr int kBlockMaxExperts = 256;  // larger expert counts use the per-step kernels
 constexpr int kTimelineSlots = 32;
@@ -180,7 +181,7 @@ __device__ inline RouteLds route_lds(const BlockParams &p, unsigned char *base) 
 // loads kSegLoads 16-byte pieces of a segment.
 constexpr int kStageChunkRows = 128;  // rows x chunks of one segment
 constexpr int kSegLoads = kStageChunkRows * 16 / 256;
-constexpr size_t kStageBytes = 32 * ((kStageChunkRows / 32) * 256 + 16);  // the largest of the three shapes
+constexpr size_t kStageBytes = 64 * (256 * 2 + 16);  // also the projections' 64 rows x 256 elements
 constexpr size_t kProjScratchBytes = 4 * 4 * 64 * 16 + 64;
 constexpr size_t kBlockScratchBytes = kProjScratchBytes > kStageBytes ? kProjScratchBytes : kStageBytes;
 
