@@ -303,7 +303,18 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
     while (ks > 1 && (p.H % ks != 0 || (p.H / ks) % 32 != 0)) --ks;
     p.pool_ks = ks;
   }
-  p.unpool_ks = split_for(p.H / 16, p.P / 32, grid - n_fin - n_boundary);
+  // The unpooler: 16-feature tiles with every weight requested before the
+  // wait at few rows; at many rows 64-feature tiles, so that the MoE output
+  // is read once per 64 features.
+  p.unpool_wide = p.b > 16 ? 1 : 0;
+  if (p.unpool_wide) {
+    const int groups = (p.H + 63) / 64;
+    int ks = std::min(kMaxSplitK, std::max(1, (grid - n_fin - n_boundary) / groups));
+    while (ks > 1 && (p.P % ks != 0 || (p.P / ks) % 32 != 0)) --ks;
+    p.unpool_ks = ks;
+  } else {
+    p.unpool_ks = split_for(p.H / 16, p.P / 32, grid - n_fin - n_boundary);
+  }
   p.n_pool_tiles = (p.P + 63) / 64;
   p.needs_routing = needs_routing ? 1 : 0;
   p.routing_out = st.routing_out ? 1 : 0;
@@ -316,7 +327,7 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   p.h_producers = st.pool ? (p.pre_norm_w ? p.b : p.n_pool_tiles) : 0;
   p.has_up = st.experts ? 1 : 0;
   p.n_fin = n_fin;
-  p.n_unpool = st.unpool ? (p.H / 16) * p.unpool_ks : 0;
+  p.n_unpool = st.unpool ? (p.unpool_wide ? (p.H + 63) / 64 : p.H / 16) * p.unpool_ks : 0;
   p.n_boundary = n_boundary;
   MB_HIP(launch_block(p, grid, lds, s));
   *used = true;

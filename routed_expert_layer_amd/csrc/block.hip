@@ -653,12 +653,13 @@ __device__ __forceinline__ int *proj_flag(unsigned char *lds) {
 // 32 elements ahead.  Rows go in passes of up to 64 (four 16-row MFMA
 // blocks); features and rows past the ends load zeros and are not stored.
 // With ks == 1 the result goes to `out` in bf16, else the fp32 partial to
-// part[q].
+// part[q].  `wait` runs after the first weight requests, before the first
+// activation request.
 constexpr int kWideRing = 8;
 constexpr int kWideCols = 16 * kWaves;
-template <bool kCoherentA>
+template <bool kCoherentA, typename Wait>
 __device__ __forceinline__ void proj_wide(rsrc_t ra, const uint16_t *w, int rows, int n_out, int kdim, int gi, int q,
-                                          int ks, float *part, uint16_t *out, unsigned char *stage) {
+                                          int ks, float *part, uint16_t *out, unsigned char *stage, Wait wait) {
   const int lane = (int)(tid() % MB_WAVE), wave = (int)(tid() / MB_WAVE), g = lane >> 4, r16 = lane & 15;
   const int kr = kdim / ks, k0 = q * kr, nch = kr / 32;
   const int f = gi * kWideCols + 16 * wave + r16;  // this lane's weight row
@@ -674,6 +675,7 @@ __device__ __forceinline__ void proj_wide(rsrc_t ra, const uint16_t *w, int rows
     u32x4_t W[kWideRing];
 #pragma unroll
     for (int r = 0; r < kWideRing; ++r) W[r] = wload(r);
+    if (t0 == 0) wait();
     f32x4_t acc[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1428,7 +1430,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       } else if (step == 3) {
         // Pooler: wide tiles, the splits added by the last to finish.
         const int gi = i / p.pool_ks, q = i % p.pool_ks;
-        proj_wide<false>(make_rsrc(p.x), p.pool_w, p.b, p.P, p.H, gi, q, p.pool_ks, p.pool_part, p.h, scratch);
+        proj_wide<false>(make_rsrc(p.x), p.pool_w, p.b, p.P, p.H, gi, q, p.pool_ks, p.pool_part, p.h, scratch,
+                         []() {});
         bool done = true;
         if (p.pool_ks > 1) {
           done = last_arrival(&p.pool_cnt[gi], (unsigned)p.pool_ks, proj_flag(scratch));
@@ -1512,9 +1515,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       if (step == 8) {
         fin_task(p, d, R, i, scratch);
       } else if (step == 9) {
-        proj_task<true>(d, p.n_fin > 0 ? p.moe_rep + (size_t)(blockIdx.x % kMoeReplicas) * p.b * p.P : p.moe_out,
-                        p.unpool_w, p.u, p.b, p.H, p.P, p.unpool_ks, p.unpool_part, p.unpool_cnt, kCtrFin, p.n_fin,
-                        false, i, true, scratch);
+        const uint16_t *mo =
+            p.n_fin > 0 ? p.moe_rep + (size_t)(blockIdx.x % kMoeReplicas) * p.b * p.P : p.moe_out;
+        if (p.unpool_wide) {
+          // Many rows: wide tiles, so each workgroup reads the MoE output once per 64 features.
+          proj_wide<true>(make_rsrc(mo), p.unpool_w, p.b, p.H, p.P, i / p.unpool_ks, i % p.unpool_ks, p.unpool_ks,
+                          p.unpool_part, p.u, scratch, [&]() { wait_step(d, kCtrFin, p.n_fin); });
+        } else {
+          proj_task<true>(d, mo, p.unpool_w, p.u, p.b, p.H, p.P, p.unpool_ks, p.unpool_part, p.unpool_cnt, kCtrFin,
+                          p.n_fin, false, i, true, scratch);
+        }
         signal_step(d, kCtrUnpool);
         stamp(p, 16);
       } else {

@@ -108,6 +108,7 @@ struct BlockParams {
   int n_router, n_route, n_pool, n_prenorm, n_fin, n_unpool, n_boundary;
   int pool_ks, unpool_ks, n_pool_tiles, h_producers;
   int has_up, needs_routing, routing_out, route_given, logits_in;
+  int unpool_wide;  // unpooler in 64-feature tiles (many rows)
   int lds_route_bytes;
   // inputs
   const uint16_t *x;
