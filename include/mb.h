@@ -232,7 +232,8 @@ int mb_packed_experts_bytes(const mb_dims *dims, size_t *bytes);
  * gate + 16 up rows of w13, then 32 rows of w2), per 128-element chunk, the
  * 1 KB that one wave loads for each of the unit's two 16-row tiles, lane l
  * getting bytes 64 c + 16 (l / 16) of row l % 16; then the unit's E8M0
- * scales, 16 bytes per row and 4 chunks, padded with 127 (= 2^0).  The values
+ * scales, per 4 chunks and tile 256 bytes, lane l's 4 bytes (at 4 l) being the
+ * scales of its blocks of the 4 chunks, padded with 127 (= 2^0).  The values
  * are unchanged, so results are bit-identical to the caller's layout.  Meant
  * for load time, like the weight preparation of [muse_moe_runner]
  * MuseSparkAiterExperts; the caller owns `packed` and keeps it with the

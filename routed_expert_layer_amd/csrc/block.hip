@@ -922,8 +922,12 @@ __device__ __forceinline__ void set_progress_priority(int c, int n) {
 struct MxTiles {
   rsrc_t rw, rs;
   uint32_t o0, o1, so0, so1, wstride, sstride;
-  bool vec;
+  int smode;  // kScalesRow4, kScalesRow16 or kScalesLane (what one scale load holds)
 };
+// A lane's scale load per four chunks: the row's four 4-byte words (one per
+// chunk, byte g = block g), as one 16-byte load or four 4-byte loads; or the
+// lane's own 4-byte word (byte j = its block of chunk j).
+constexpr int kScalesRow4 = 0, kScalesRow16 = 1, kScalesLane = 2;
 
 // The tiles of rows r0 .. r0 + 15 and r1 .. r1 + 15 of one expert's matrix of
 // `kdim`-element rows, in the caller's row-major layout: lane l reads row
@@ -933,19 +937,19 @@ __device__ __forceinline__ MxTiles mx_plain(const uint8_t *codes, const uint8_t 
   const uint32_t r16 = (uint32_t)(lane & 15), g = (uint32_t)(lane >> 4);
   const uint32_t rb = (uint32_t)kdim / 2, sb = (uint32_t)kdim / 32;
   return MxTiles{make_rsrc(codes), make_rsrc(scales), (r0 + r16) * rb + 16 * g, (r1 + r16) * rb + 16 * g,
-                 (r0 + r16) * sb, (r1 + r16) * sb, 64u, 4u, (kdim / 128) % 4 == 0};
+                 (r0 + r16) * sb, (r1 + r16) * sb, 64u, 4u, (kdim / 128) % 4 == 0 ? kScalesRow16 : kScalesRow4};
 }
 
 // Unit `unit` of one section of the streaming layout (mb_pack_experts): per
 // chunk the two tiles' 1 KB wave loads follow each other, lane l at 16 l;
-// per group of four chunks the two tiles' 16 rows x 16 scale bytes, row l % 16
-// at 16 (l % 16).
+// per group of four chunks the two tiles' 256-byte wave loads of scales, lane
+// l at 4 l (the scales its codes need: row l % 16, block l / 16, four chunks).
 __device__ __forceinline__ MxTiles mx_packed(const uint8_t *codes, const uint8_t *scales, int unit, int kdim,
                                              int lane) {
   const uint32_t nch = (uint32_t)kdim / 128, ngr = (nch + 3) / 4;
   const uint32_t o = (uint32_t)unit * nch * 2048u + 16u * (uint32_t)lane;
-  const uint32_t so = (uint32_t)unit * ngr * 512u + 16u * (uint32_t)(lane & 15);
-  return MxTiles{make_rsrc(codes), make_rsrc(scales), o, o + 1024u, so, so + 256u, 2048u, 128u, true};
+  const uint32_t so = (uint32_t)unit * ngr * 512u + 4u * (uint32_t)lane;
+  return MxTiles{make_rsrc(codes), make_rsrc(scales), o, o + 1024u, so, so + 256u, 2048u, 128u, kScalesLane};
 }
 
 // Activation rows per pass over a unit's weights: 8, 16 or 32 (as one or two
@@ -973,21 +977,34 @@ __device__ __forceinline__ int pass_rows(int nrows) { return nrows <= 8 ? 8 : nr
 //
 // Chunks past nch have zero weights and zero activations and add nothing,
 // so the loop has no branches on the data.
-template <int kRing, typename Wait, typename RowOff>
+template <bool kLane> struct ScaleWord { using type = u32x4_t; };
+template <> struct ScaleWord<true> { using type = uint32_t; };
+
+template <int kRing, bool kLane, typename Wait, typename RowOff>
 __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, int pr, rsrc_t ra, RowOff row_off,
                                         unsigned char *stage, f32x4_t (&d0)[2], f32x4_t (&d1)[2], int prog,
                                         int prog_total, Wait wait) {
   const int lane = tid() % MB_WAVE, g = lane >> 4;
   const rsrc_t rw = T.rw, rs = T.rs;
   const uint32_t o0 = T.o0, o1 = T.o1, so0 = T.so0, so1 = T.so1, ws = T.wstride, ss = T.sstride;
-  const bool vec_scales = T.vec;
+  const bool row16 = T.smode == kScalesRow16;
   u32x4_t W0[kRing], W1[kRing];
+  using SW = typename ScaleWord<kLane>::type;
   auto scales = [&](uint32_t so, int c0) {
-    if (vec_scales) return ld_b128(rs, c0 < nch ? so + ss * c0 : kOob);
-    u32x4_t v;
+    if constexpr (kLane) {
+      return ld_b32(rs, c0 < nch ? so + ss * c0 : kOob);
+    } else {
+      if (row16) return ld_b128(rs, c0 < nch ? so + ss * c0 : kOob);
+      u32x4_t v;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = ld_b32(rs, c0 + r < nch ? so + 4u * (c0 + r) : kOob);
-    return v;
+      for (int r = 0; r < 4; ++r) v[r] = ld_b32(rs, c0 + r < nch ? so + 4u * (c0 + r) : kOob);
+      return v;
+    }
+  };
+  // The lane's scale of chunk r of a group.
+  auto scale_of = [&](const SW &v, int r) {
+    if constexpr (kLane) return e8m0_to_f32((v >> (8 * r)) & 0xFFu);
+    else return e8m0_to_f32((v[r] >> (8 * g)) & 0xFFu);
   };
 #pragma unroll
   for (int r = 0; r < kRing; ++r) {
@@ -995,7 +1012,7 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, int pr, rsrc_
     W0[r] = ld_b128(rw, ok ? o0 + ws * r : kOob);
     W1[r] = ld_b128(rw, ok ? o1 + ws * r : kOob);
   }
-  u32x4_t S0[kRing / 4], S1[kRing / 4];
+  SW S0[kRing / 4], S1[kRing / 4];
 #pragma unroll
   for (int q = 0; q < kRing / 4; ++q) {
     S0[q] = scales(so0, 4 * q);
@@ -1036,7 +1053,7 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, int pr, rsrc_
     __syncthreads();
     for (int c0 = seg0; c0 < seg0 + segn; c0 += kRing) {
       set_progress_priority(prog + c0, prog_total);
-      u32x4_t N0[kRing / 4], N1[kRing / 4];
+      SW N0[kRing / 4], N1[kRing / 4];
 #pragma unroll
       for (int q = 0; q < kRing / 4; ++q) {
         N0[q] = scales(so0, c0 + kRing + 4 * q);
@@ -1044,8 +1061,7 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, int pr, rsrc_
       }
 #pragma unroll
       for (int r = 0; r < kRing; ++r) {
-        const float s0 = e8m0_to_f32((S0[r / 4][r % 4] >> (8 * g)) & 0xFFu);
-        const float s1 = e8m0_to_f32((S1[r / 4][r % 4] >> (8 * g)) & 0xFFu);
+        const float s0 = scale_of(S0[r / 4], r % 4), s1 = scale_of(S1[r / 4], r % 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const unsigned char *bp = stage + rd_off + (c0 + r - seg0) * 256 + 16 * i;
@@ -1077,6 +1093,7 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, int pr, rsrc_
 // Up unit: w13 and the gated activation for (active expert, 16 act columns):
 // gate rows i0..i0+15 and up rows I+i0..I+i0+15 of the expert, over P, for
 // the expert's routes in passes of pass_rows.
+template <bool kPacked>
 __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, const RouteLds &R, int unit,
                                         bool &h_ready, unsigned char *stage, int &prog, int prog_total) {
   const int lane = tid() % MB_WAVE, g = lane >> 4, r16 = lane & 15;
@@ -1087,7 +1104,7 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
   const int row0 = uniform(R.off[e]), nrows = uniform(R.off[e + 1]) - row0;
   const int i0 = tile * 16;
   const MxTiles T =
-      p.xp ? mx_packed(p.xp + (size_t)e * p.xp_stride, p.xp + (size_t)e * p.xp_stride + p.xp_up_s, tile, P, lane)
+      kPacked ? mx_packed(p.xp + (size_t)e * p.xp_stride, p.xp + (size_t)e * p.xp_stride + p.xp_up_s, tile, P, lane)
            : mx_plain(p.w13 + (size_t)e * 2 * I * (P / 2), p.w13s + (size_t)e * 2 * I * (P / 32), i0, I + i0, P,
                       lane);
   const rsrc_t rh = make_rsrc(p.h), ract = make_rsrc(p.act);
@@ -1095,7 +1112,7 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
   const int pr = pass_rows(nrows);
   for (int m0 = 0; m0 < nrows; m0 += pr) {
     f32x4_t gs[2], us[2];
-    mx_pair<kRingUp>(
+    mx_pair<kRingUp, kPacked>(
         T, nch, pr, rh,
         [&](int m) { return m0 + m < nrows ? (uint32_t)((R.rl[row0 + m0 + m] / p.k) * P) * 2u : kOob; }, stage,
         gs, us, prog, prog_total, [&]() {
@@ -1125,6 +1142,7 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
 
 // Down unit: w2 for (active expert, 32 output features): y in route order and
 // the route's sum of squares over these 32 features.
+template <bool kPacked>
 __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, const RouteLds &R, int unit,
                                           unsigned char *stage, int &prog, int prog_total) {
   const int lane = tid() % MB_WAVE, g = lane >> 4, r16 = lane & 15;
@@ -1135,7 +1153,7 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
   const int row0 = uniform(R.off[e]), nrows = uniform(R.off[e + 1]) - row0;
   const int p0 = tile * 32;
   const MxTiles T =
-      p.xp ? mx_packed(p.xp + (size_t)e * p.xp_stride + p.xp_down, p.xp + (size_t)e * p.xp_stride + p.xp_down_s,
+      kPacked ? mx_packed(p.xp + (size_t)e * p.xp_stride + p.xp_down, p.xp + (size_t)e * p.xp_stride + p.xp_down_s,
                        tile, I, lane)
            : mx_plain(p.w2 + (size_t)e * P * (I / 2), p.w2s + (size_t)e * P * (I / 32), p0, p0 + 16, I, lane);
   const rsrc_t ract = make_rsrc(p.act), ry = make_rsrc(p.y), rss = make_rsrc(p.ssq);
@@ -1144,7 +1162,7 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
   const int pr = pass_rows(nrows);
   for (int m0 = 0; m0 < nrows; m0 += pr) {
     f32x4_t y0[2], y1[2];
-    mx_pair<kRingDown>(
+    mx_pair<kRingDown, kPacked>(
         T, nch, pr, ract, [&](int m) { return m0 + m < nrows ? (uint32_t)((row0 + m0 + m) * I) * 2u : kOob; }, stage,
         y0, y1, prog, prog_total, [&]() {
           if (!ready) {
@@ -1481,9 +1499,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const int my_up = gw < nU ? (nU - gw + GW - 1) / GW : 0, my_down = gw < nD ? (nD - gw + GW - 1) / GW : 0;
     const int prog_total = my_up * (p.P / 128) + my_down * (p.I / 128);
     int prog = 0;
-    for (int u = gw; u < nU; u += GW) up_unit(p, d, R, u, h_ready, stage, prog, prog_total);
-    stamp(p, 20);
-    for (int u = gw; u < nD; u += GW) down_unit(p, d, R, u, stage, prog, prog_total);
+    // (The expert layout is a template argument: each has its own registers.)
+    if (p.xp) {
+      for (int u = gw; u < nU; u += GW) up_unit<true>(p, d, R, u, h_ready, stage, prog, prog_total);
+      stamp(p, 20);
+      for (int u = gw; u < nD; u += GW) down_unit<true>(p, d, R, u, stage, prog, prog_total);
+    } else {
+      for (int u = gw; u < nU; u += GW) up_unit<false>(p, d, R, u, h_ready, stage, prog, prog_total);
+      stamp(p, 20);
+      for (int u = gw; u < nD; u += GW) down_unit<false>(p, d, R, u, stage, prog, prog_total);
+    }
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();
     stamp(p, 11);

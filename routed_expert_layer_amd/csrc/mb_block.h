@@ -81,14 +81,15 @@ constexpr int kBoundGroups = 8;      // 4-element groups per thread of a boundar
 // Streaming layout of the MXFP4 experts (mb_pack_experts).  Per expert, in
 // this order:
 //   up codes     [I/16 units][P/128 chunks][2 tiles][64 lanes][16 B]
-//   up scales    [I/16 units][ceil(P/512) groups][2 tiles][16 rows][16 B]
+//   up scales    [I/16 units][ceil(P/512) groups][2 tiles][64 lanes][4 B]
 //   down codes   [P/32 units][I/128 chunks][2 tiles][64 lanes][16 B]
-//   down scales  [P/32 units][ceil(I/512) groups][2 tiles][16 rows][16 B]
+//   down scales  [P/32 units][ceil(I/512) groups][2 tiles][64 lanes][4 B]
 // Up unit u has tiles w13 rows 16u.. (gate) and I + 16u.. (up); down unit u
 // has w2 rows 32u.. and 32u + 16..  Lane l's 16 code bytes of chunk c are
 // bytes 64 c + 16 (l / 16) of tile row l % 16 (its 32-element MX block of the
-// chunk); a row's 16 scale bytes of group q are its scale bytes 16 q .. + 15,
-// padded with 127 (2^0) past the row's end.
+// chunk); its 4 scale bytes of group q are the scales of that block in chunks
+// 4q .. 4q + 3 (scale bytes 4 (4q + j) + l / 16 of the row), padded with 127
+// (2^0) past the row's end.
 struct PackedExperts {
   size_t up_s, down, down_s, stride;  // byte offsets within an expert; expert stride
 };

@@ -33,33 +33,29 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t *__restri
   }
 }
 
-// One 16-byte piece of one scale section per thread: piece q is row q % 16 of
-// tile (q / 16) % 2 of group (q / 32) % ngr of unit q / (32 ngr); it holds the
-// row's scale bytes 16 g .. 16 g + 15, with 127 (2^0) past the row's kdim / 32.
+// One 4-byte word of one scale section per thread: word q is lane q % 64 of
+// tile (q / 64) % 2 of group (q / 128) % ngr of unit q / (128 ngr); byte j
+// holds the scale of row q % 16 of the tile, block (q % 64) / 16 of chunk
+// 4 ((q / 128) % ngr) + j, with 127 (2^0) past the row's kdim / 32.
 __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t *__restrict__ src, size_t src_stride,
                                                           uint8_t *__restrict__ dst, size_t dst_stride,
                                                           size_t dst_off, int units, int ngr, int kdim,
                                                           int unit_rows, int t1_row) {
-  const size_t pieces = (size_t)units * ngr * 32;
+  const size_t words = (size_t)units * ngr * 128;
   const int row_bytes = kdim / 32;
   const uint8_t *s = src + (size_t)blockIdx.y * src_stride;
   uint8_t *o = dst + (size_t)blockIdx.y * dst_stride + dst_off;
-  for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < pieces; q += (size_t)gridDim.x * blockDim.x) {
-    const int r = (int)(q % 16), t = (int)((q / 16) % 2), g = (int)((q / 32) % ngr);
-    const int u = (int)(q / (32 * (size_t)ngr));
-    const size_t row = (size_t)unit_rows * u + (size_t)t * t1_row + r;
-    uint8_t v[16];
+  for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < words; q += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(q % 64), t = (int)((q / 64) % 2), g = (int)((q / 128) % ngr);
+    const int u = (int)(q / (128 * (size_t)ngr));
+    const size_t row = (size_t)unit_rows * u + (size_t)t * t1_row + (lane & 15);
+    uint32_t w = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int b = 16 * g + i;
-      v[i] = b < row_bytes ? s[row * row_bytes + b] : (uint8_t)127;
+    for (int j = 0; j < 4; ++j) {
+      const int b = 4 * (4 * g + j) + (lane >> 4);
+      w |= (uint32_t)(b < row_bytes ? s[row * row_bytes + b] : (uint8_t)127) << (8 * j);
     }
-    uint4 w;
-    w.x = v[0] | v[1] << 8 | v[2] << 16 | (uint32_t)v[3] << 24;
-    w.y = v[4] | v[5] << 8 | v[6] << 16 | (uint32_t)v[7] << 24;
-    w.z = v[8] | v[9] << 8 | v[10] << 16 | (uint32_t)v[11] << 24;
-    w.w = v[12] | v[13] << 8 | v[14] << 16 | (uint32_t)v[15] << 24;
-    *reinterpret_cast<uint4 *>(o + 16 * q) = w;
+    *reinterpret_cast<uint32_t *>(o + 4 * q) = w;
   }
 }
 
@@ -80,11 +76,11 @@ hipError_t launch_pack_experts(const mb_dims &d, const uint8_t *w13, const uint8
   const int up_ngr = (up_nch + 3) / 4, down_ngr = (down_nch + 3) / 4;
   hipLaunchKernelGGL(pack_codes_kernel, grid_for((size_t)up_units * up_nch * 128, E), dim3(256), 0, s, w13,
                      (size_t)2 * I * (P / 2), packed, L.stride, (size_t)0, up_units, up_nch, P, 16, I);
-  hipLaunchKernelGGL(pack_scales_kernel, grid_for((size_t)up_units * up_ngr * 32, E), dim3(256), 0, s, w13s,
+  hipLaunchKernelGGL(pack_scales_kernel, grid_for((size_t)up_units * up_ngr * 128, E), dim3(256), 0, s, w13s,
                      (size_t)2 * I * (P / 32), packed, L.stride, L.up_s, up_units, up_ngr, P, 16, I);
   hipLaunchKernelGGL(pack_codes_kernel, grid_for((size_t)down_units * down_nch * 128, E), dim3(256), 0, s, w2,
                      (size_t)P * (I / 2), packed, L.stride, L.down, down_units, down_nch, I, 32, 16);
-  hipLaunchKernelGGL(pack_scales_kernel, grid_for((size_t)down_units * down_ngr * 32, E), dim3(256), 0, s, w2s,
+  hipLaunchKernelGGL(pack_scales_kernel, grid_for((size_t)down_units * down_ngr * 128, E), dim3(256), 0, s, w2s,
                      (size_t)P * (I / 32), packed, L.stride, L.down_s, down_units, down_ngr, I, 32, 16);
   return hipGetLastError();
 }

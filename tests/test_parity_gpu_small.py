@@ -159,9 +159,9 @@ def packed_reference(blk) -> np.ndarray:
         rb = s.shape[2]
         pad = np.full((E, s.shape[1], ngr * 16), 127, np.uint8)
         pad[:, :, :rb] = s
-        u, g, t, r = np.meshgrid(np.arange(units), np.arange(ngr), np.arange(2), np.arange(16), indexing="ij")
-        row = unit_rows * u + t * t1_row + r
-        idx = (16 * g)[..., None] + np.arange(16)
+        u, g, t, l = np.meshgrid(np.arange(units), np.arange(ngr), np.arange(2), np.arange(64), indexing="ij")
+        row = unit_rows * u + t * t1_row + (l & 15)
+        idx = 4 * (4 * g[..., None] + np.arange(4)) + (l >> 4)[..., None]
         return pad[:, row[..., None], idx].reshape(E, -1)
 
     nch_p, nch_i = P // 128, I // 128
