@@ -57,6 +57,9 @@ constexpr int kPoolMG = 4;      // 16-row groups per projection pass
 // down unit, half the size, waits for its expert's up units: more of it is
 // requested before that wait).
 constexpr int kRingUp = 4, kRingDown = 4;
+// Down units of at most this many chunks (in the streaming layout, passes of
+// up to 16 rows) request all their weights before waiting for the up units.
+constexpr int kDownAll = 8;
 static_assert(kRingUp % 4 == 0 && kRingDown % 4 == 0, "one 16-byte scale load covers four chunks");
 static_assert((kStageChunkRows / 32) % kRingUp == 0 && (kStageChunkRows / 32) % kRingDown == 0,
               "activation segments hold whole rounds of chunks");
@@ -1090,6 +1093,70 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, int pr, rsrc_
   }
 }
 
+// mx_pair for units of at most kAll chunks and passes of at most 16 rows, in
+// the streaming layout: all of the unit's weights and scales are requested
+// before `wait` (a down unit waits for its expert's up units, so its whole
+// weight stream is in flight meanwhile), then the activations are staged in
+// one segment and every chunk is computed with no further weight requests.
+// Same operands, staging and results as mx_pair (block 0 of d0 / d1 only).
+template <int kAll, typename Wait, typename RowOff>
+__device__ __forceinline__ void mx_pair_all(const MxTiles &T, int nch, int pr, rsrc_t ra, RowOff row_off,
+                                            unsigned char *stage, f32x4_t (&d0)[2], f32x4_t (&d1)[2], Wait wait) {
+  static_assert(kAll % 4 == 0 && 16 * kAll <= kStageChunkRows, "whole scale words; 16 rows x kAll chunks staged");
+  const int lane = tid() % MB_WAVE, g = lane >> 4;
+  const rsrc_t rw = T.rw, rs = T.rs;
+  const uint32_t o0 = T.o0, o1 = T.o1, so0 = T.so0, so1 = T.so1, ws = T.wstride, ss = T.sstride;
+  u32x4_t W0[kAll], W1[kAll];
+  uint32_t S0[kAll / 4], S1[kAll / 4];
+#pragma unroll
+  for (int r = 0; r < kAll; ++r) {
+    const bool ok = r < nch;
+    W0[r] = ld_b128(rw, ok ? o0 + ws * r : kOob);
+    W1[r] = ld_b128(rw, ok ? o1 + ws * r : kOob);
+  }
+#pragma unroll
+  for (int q = 0; q < kAll / 4; ++q) {
+    S0[q] = ld_b32(rs, 4 * q < nch ? so0 + ss * (4 * q) : kOob);
+    S1[q] = ld_b32(rs, 4 * q < nch ? so1 + ss * (4 * q) : kOob);
+  }
+  wait();
+  const int srow = kAll * 256 + 16;  // row stride in the stage
+  d0[0] = d1[0] = d0[1] = d1[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // Rows past the pass and chunks past nch are staged as zeros.
+  constexpr int ppr = kAll * 16;  // 16-byte pieces per row
+#pragma unroll
+  for (int n0 = 0; n0 < kSegLoads; n0 += kSegLoads / 2) {
+    u32x4_t v[kSegLoads / 2];
+#pragma unroll
+    for (int n = 0; n < kSegLoads / 2; ++n) {
+      const int q = (int)tid() + kThreads * (n0 + n);
+      const int m = q / ppr, pc = q % ppr;
+      const uint32_t ro = m < pr ? row_off(m) : kOob;
+      v[n] = ld_co16(ra, (ro != kOob && pc < nch * 16) ? ro + (uint32_t)(pc * 16) : kOob);
+    }
+#pragma unroll
+    for (int n = 0; n < kSegLoads / 2; ++n) {
+      const int q = (int)tid() + kThreads * (n0 + n);
+      const int m = q / ppr, pc = q % ppr;
+      if (m < pr) *reinterpret_cast<u32x4_t *>(stage + m * srow + pc * 16) = v[n];
+    }
+  }
+  __syncthreads();
+  const uint32_t rd_off = (uint32_t)((lane & (pr == 8 ? 7 : 15)) * srow + 64 * g);
+#pragma unroll
+  for (int r = 0; r < kAll; ++r) {
+    const float s0 = e8m0_to_f32((S0[r / 4] >> (8 * (r % 4))) & 0xFFu);
+    const float s1 = e8m0_to_f32((S1[r / 4] >> (8 * (r % 4))) & 0xFFu);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4_t B = *reinterpret_cast<const u32x4_t *>(stage + rd_off + r * 256 + 16 * i);
+      d0[0] = mfma_bf16(dequant_fp4x8(W0[r][i], s0), as_bf16x8(B), d0[0]);
+      d1[0] = mfma_bf16(dequant_fp4x8(W1[r][i], s1), as_bf16x8(B), d1[0]);
+    }
+  }
+  __syncthreads();
+}
+
 // Up unit: w13 and the gated activation for (active expert, 16 act columns):
 // gate rows i0..i0+15 and up rows I+i0..I+i0+15 of the expert, over P, for
 // the expert's routes in passes of pass_rows.
@@ -1162,14 +1229,17 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
   const int pr = pass_rows(nrows);
   for (int m0 = 0; m0 < nrows; m0 += pr) {
     f32x4_t y0[2], y1[2];
-    mx_pair<kRingDown, kPacked>(
-        T, nch, pr, ract, [&](int m) { return m0 + m < nrows ? (uint32_t)((row0 + m0 + m) * I) * 2u : kOob; }, stage,
-        y0, y1, prog, prog_total, [&]() {
-          if (!ready) {
-            poll_ge(d, d.up(e), (unsigned)(I / 16));
-            ready = true;
-          }
-        });
+    auto row_off = [&](int m) { return m0 + m < nrows ? (uint32_t)((row0 + m0 + m) * I) * 2u : kOob; };
+    auto wait = [&]() {
+      if (!ready) {
+        poll_ge(d, d.up(e), (unsigned)(I / 16));
+        ready = true;
+      }
+    };
+    if (kPacked && nch <= kDownAll && pr <= 16)
+      mx_pair_all<kDownAll>(T, nch, pr, ract, row_off, stage, y0, y1, wait);
+    else
+      mx_pair<kRingDown, kPacked>(T, nch, pr, ract, row_off, stage, y0, y1, prog, prog_total, wait);
     prog += nch;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
