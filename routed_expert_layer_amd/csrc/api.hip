@@ -284,6 +284,7 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   int grid = cus * (occ < kBlockGroupsPerCu ? occ : kBlockGroupsPerCu);
   if (grid > kMaxGrid) grid = kMaxGrid;
   p.lds_route_bytes = (int)route_bytes;
+  p.cus = cus;
   const int n_router = st.router ? p.E * ((p.b + kRouterRowBlock - 1) / kRouterRowBlock) : 0;
   const int n_fin = st.experts ? p.b * ((p.P + kFinChunk - 1) / kFinChunk) : 0;
   const int n_boundary = st.unpool ? p.b : 0;

@@ -53,14 +53,12 @@ constexpr int kWaves = kThreads / MB_WAVE;
 static_assert(kWaves == kBlockWaves, "routing LDS is laid out per wave");
 static_assert(kRouterRowBlock == kWaves, "a router task gives each wave one row");
 constexpr int kPoolMG = 4;      // 16-row groups per projection pass
-// 128-element weight chunks a wave keeps in flight in an up / a down unit (a
-// down unit, half the size, waits for its expert's up units: more of it is
-// requested before that wait).
+// 128-element weight chunks a wave keeps in flight in an up / a down unit.
 constexpr int kRingUp = 4, kRingDown = 4;
 // Down units of at most this many chunks (in the streaming layout, passes of
 // up to 16 rows) request all their weights before waiting for the up units.
 constexpr int kDownAll = 8;
-static_assert(kRingUp % 4 == 0 && kRingDown % 4 == 0, "one 16-byte scale load covers four chunks");
+static_assert(kRingUp % 4 == 0 && kRingDown % 4 == 0, "one scale load covers four chunks");
 static_assert((kStageChunkRows / 32) % kRingUp == 0 && (kStageChunkRows / 32) % kRingDown == 0,
               "activation segments hold whole rounds of chunks");
 constexpr int kProjBatch = 8;   // 32-element projection chunks a wave requests at once
@@ -447,18 +445,20 @@ __device__ __forceinline__ void route_one(const BlockParams &p, const float (&l)
 }
 
 // Rows t_begin..t_end-1, one per wave in turn, from their fp32 logits; the
-// ids and weights go to LDS.  Each wave requests its row's logits and the
-// expert biases together.
-template <int PER>
-__device__ __forceinline__ void route_rows(const BlockParams &p, const RouteLds &R, int t_begin, int t_end) {
+// ids and weights go to LDS.  The expert biases are requested before `wait`
+// (which returns once the logits are written).
+template <int PER, typename Wait>
+__device__ __forceinline__ void route_rows(const BlockParams &p, const RouteLds &R, int t_begin, int t_end,
+                                           Wait wait) {
   const int lane = tid() % MB_WAVE;
-  const rsrc_t rl = make_rsrc(p.logits_f);
+  const rsrc_t rl = make_rsrc(p.logits_f), rb = make_rsrc(p.bias);
   float bias[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + MB_WAVE * i;
-    bias[i] = e < p.E ? p.bias[e] : 0.f;
+    bias[i] = __uint_as_float(ld_b32(rb, e < p.E ? (uint32_t)e * 4u : kOob));
   }
+  wait();
   for (int t = t_begin + (int)(tid() / MB_WAVE); t < t_end; t += kWaves) {
     float l[PER];
 #pragma unroll
@@ -476,11 +476,12 @@ __device__ __forceinline__ void route_rows(const BlockParams &p, const RouteLds 
   }
 }
 
-__device__ __forceinline__ void route_dispatch(const BlockParams &p, const RouteLds &R, int t0, int t1) {
+template <typename Wait>
+__device__ __forceinline__ void route_dispatch(const BlockParams &p, const RouteLds &R, int t0, int t1, Wait wait) {
   // The host sends larger expert counts to the per-step kernels.
-  if (p.E <= 64) route_rows<1>(p, R, t0, t1);
-  else if (p.E <= 128) route_rows<2>(p, R, t0, t1);
-  else route_rows<4>(p, R, t0, t1);
+  if (p.E <= 64) route_rows<1>(p, R, t0, t1, wait);
+  else if (p.E <= 128) route_rows<2>(p, R, t0, t1, wait);
+  else route_rows<4>(p, R, t0, t1, wait);
 }
 
 // Inclusive prefix sum over the wave's 64 lanes (DPP: row shifts 1, 2, 4, 8,
@@ -589,10 +590,11 @@ __device__ __forceinline__ void group_routes(const BlockParams &p, const RouteLd
 // weights go out coherently for every workgroup's grouping.
 __device__ __forceinline__ void route_task(const BlockParams &p, const Deps &d, const RouteLds &R,
                                            int task) {
-  if (p.n_logit_producers > 0) wait_ge(d, d.logits(task), (unsigned)p.E);
-  stamp(p, 12);
   const int t0 = task * kWaves, t1 = min(p.b, t0 + kWaves);
-  route_dispatch(p, R, t0, t1);
+  route_dispatch(p, R, t0, t1, [&]() {
+    if (p.n_logit_producers > 0) wait_ge(d, d.logits(task), (unsigned)p.E);
+    stamp(p, 12);
+  });
   stamp(p, 14);
   __syncthreads();
   const rsrc_t ri = make_rsrc(p.ids), rw = make_rsrc(p.wts);
@@ -903,19 +905,17 @@ __device__ __forceinline__ void prenorm_task(const BlockParams &p, const Deps &d
 
 // ---------------------------------------------------------------- experts
 
-// Issue priority of a wave streaming its units, from its progress through
-// all of them (c of n chunks, up units first): 3 in the first quarter down to
-// 0 in the last.  Among waves of equal priority the oldest issues first, which
-// leaves the waves of the youngest workgroups on a CU far behind; ranking by
-// progress lets the waves that are behind catch up, so the units of an expert
-// finish together, and up units (which down units wait for) go before down
-// units.
-__device__ __forceinline__ void set_progress_priority(int c, int n) {
-  const int q = (4 * c) / n;
-  if (q <= 0) __builtin_amdgcn_s_setprio(3);
-  else if (q == 1) __builtin_amdgcn_s_setprio(2);
-  else if (q == 2) __builtin_amdgcn_s_setprio(1);
-  else __builtin_amdgcn_s_setprio(0);
+// Issue priority of the waves streaming expert units: the workgroups
+// sharing a CU are launched one after another (slot = blockIdx / CUs), and
+// among waves of equal priority the oldest issues first, which leaves the
+// waves of the later workgroups on a CU behind -- and a down unit waits for
+// the slowest up unit of its expert.  So from its first round of chunks on,
+// the later a workgroup's slot, the higher its waves' priority (1, 2, 3); the
+// first requests of the units phase go out oldest first, at priority 0.
+__device__ __forceinline__ void set_slot_priority(int slot) {
+  if (slot <= 0) __builtin_amdgcn_s_setprio(1);
+  else if (slot == 1) __builtin_amdgcn_s_setprio(2);
+  else __builtin_amdgcn_s_setprio(3);
 }
 
 // Where a wave finds the two 16-row MXFP4 tiles of a unit: codes of chunk c
@@ -979,14 +979,16 @@ __device__ __forceinline__ int pass_rows(int nrows) { return nrows <= 8 ? 8 : nr
 // row_off(m) is the byte offset of pass row m's element 0, or kOob.
 //
 // Chunks past nch have zero weights and zero activations and add nothing,
-// so the loop has no branches on the data.
+// so the loop has no branches on the data.  Each round of chunks runs at the
+// issue priority of the workgroup's slot (set_slot_priority).  kLane: the
+// scales in the streaming layout's per-lane words.
 template <bool kLane> struct ScaleWord { using type = u32x4_t; };
 template <> struct ScaleWord<true> { using type = uint32_t; };
 
 template <int kRing, bool kLane, typename Wait, typename RowOff>
 __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, int pr, rsrc_t ra, RowOff row_off,
-                                        unsigned char *stage, f32x4_t (&d0)[2], f32x4_t (&d1)[2], int prog,
-                                        int prog_total, Wait wait) {
+                                        unsigned char *stage, f32x4_t (&d0)[2], f32x4_t (&d1)[2], int slot,
+                                        Wait wait) {
   const int lane = tid() % MB_WAVE, g = lane >> 4;
   const rsrc_t rw = T.rw, rs = T.rs;
   const uint32_t o0 = T.o0, o1 = T.o1, so0 = T.so0, so1 = T.so1, ws = T.wstride, ss = T.sstride;
@@ -1055,7 +1057,7 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, int pr, rsrc_
     }
     __syncthreads();
     for (int c0 = seg0; c0 < seg0 + segn; c0 += kRing) {
-      set_progress_priority(prog + c0, prog_total);
+      set_slot_priority(slot);
       SW N0[kRing / 4], N1[kRing / 4];
 #pragma unroll
       for (int q = 0; q < kRing / 4; ++q) {
@@ -1162,7 +1164,7 @@ __device__ __forceinline__ void mx_pair_all(const MxTiles &T, int nch, int pr, r
 // the expert's routes in passes of pass_rows.
 template <bool kPacked>
 __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, const RouteLds &R, int unit,
-                                        bool &h_ready, unsigned char *stage, int &prog, int prog_total) {
+                                        bool &h_ready, unsigned char *stage) {
   const int lane = tid() % MB_WAVE, g = lane >> 4, r16 = lane & 15;
   const int P = p.P, I = p.I;
   const int tiles = I / 16;
@@ -1182,13 +1184,12 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
     mx_pair<kRingUp, kPacked>(
         T, nch, pr, rh,
         [&](int m) { return m0 + m < nrows ? (uint32_t)((R.rl[row0 + m0 + m] / p.k) * P) * 2u : kOob; }, stage,
-        gs, us, prog, prog_total, [&]() {
+        gs, us, (int)blockIdx.x / p.cus, [&]() {
           if (!h_ready) {
             wave_wait_step(d, p.pre_norm_w ? kCtrPrenorm : kCtrPool, p.h_producers);
             h_ready = true;
           }
         });
-    prog += nch;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int m = m0 + 16 * b + r16;
@@ -1211,7 +1212,7 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
 // the route's sum of squares over these 32 features.
 template <bool kPacked>
 __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, const RouteLds &R, int unit,
-                                          unsigned char *stage, int &prog, int prog_total) {
+                                          unsigned char *stage) {
   const int lane = tid() % MB_WAVE, g = lane >> 4, r16 = lane & 15;
   const int P = p.P, I = p.I;
   const int tiles = P / 32;
@@ -1239,8 +1240,7 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
     if (kPacked && nch <= kDownAll && pr <= 16)
       mx_pair_all<kDownAll>(T, nch, pr, ract, row_off, stage, y0, y1, wait);
     else
-      mx_pair<kRingDown, kPacked>(T, nch, pr, ract, row_off, stage, y0, y1, prog, prog_total, wait);
-    prog += nch;
+      mx_pair<kRingDown, kPacked>(T, nch, pr, ract, row_off, stage, y0, y1, (int)blockIdx.x / p.cus, wait);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       if (b == 1 && pr <= 16) break;
@@ -1565,19 +1565,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // reach the memory system later -- the later workgroups on a CU -- finish
     // their up units later.)
     const int gw = blockIdx.x * kWaves + uniform(tid() / MB_WAVE);
-    // Chunks this wave streams (one pass per unit), for its issue priority.
-    const int my_up = gw < nU ? (nU - gw + GW - 1) / GW : 0, my_down = gw < nD ? (nD - gw + GW - 1) / GW : 0;
-    const int prog_total = my_up * (p.P / 128) + my_down * (p.I / 128);
-    int prog = 0;
     // (The expert layout is a template argument: each has its own registers.)
     if (p.xp) {
-      for (int u = gw; u < nU; u += GW) up_unit<true>(p, d, R, u, h_ready, stage, prog, prog_total);
+      for (int u = gw; u < nU; u += GW) up_unit<true>(p, d, R, u, h_ready, stage);
       stamp(p, 20);
-      for (int u = gw; u < nD; u += GW) down_unit<true>(p, d, R, u, stage, prog, prog_total);
+      for (int u = gw; u < nD; u += GW) down_unit<true>(p, d, R, u, stage);
     } else {
-      for (int u = gw; u < nU; u += GW) up_unit<false>(p, d, R, u, h_ready, stage, prog, prog_total);
+      for (int u = gw; u < nU; u += GW) up_unit<false>(p, d, R, u, h_ready, stage);
       stamp(p, 20);
-      for (int u = gw; u < nD; u += GW) down_unit<false>(p, d, R, u, stage, prog, prog_total);
+      for (int u = gw; u < nD; u += GW) down_unit<false>(p, d, R, u, stage);
     }
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();

@@ -110,6 +110,7 @@ struct BlockParams {
   int pool_ks, unpool_ks, n_pool_tiles, h_producers;
   int has_up, needs_routing, routing_out, route_given, logits_in;
   int unpool_wide;  // unpooler in 64-feature tiles (many rows)
+  int cus;          // compute units (the grid holds grid / cus workgroups per CU)
   int lds_route_bytes;
   // inputs
   const uint16_t *x;
