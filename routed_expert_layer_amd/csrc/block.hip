@@ -51,7 +51,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / MB_WAVE;
 static_assert(kWaves == kBlockWaves, "routing LDS is laid out per wave");
-static_assert(kRouterRowBlock == kWaves, "a router task gives each wave one row");
+static_assert(kRouterRowBlock == kWaves, "a router task covers as many rows as it has waves");
 constexpr int kPoolMG = 4;      // 16-row groups per projection pass
 // 128-element weight chunks a wave keeps in flight in an up / a down unit.
 constexpr int kRingUp = 4, kRingDown = 4;
@@ -62,7 +62,7 @@ static_assert(kRingUp % 4 == 0 && kRingDown % 4 == 0, "one scale load covers fou
 static_assert((kStageChunkRows / 32) % kRingUp == 0 && (kStageChunkRows / 32) % kRingDown == 0,
               "activation segments hold whole rounds of chunks");
 constexpr int kProjBatch = 8;   // 32-element projection chunks a wave requests at once
-constexpr int kRouterBatch = 16;  // router loads a thread requests at once
+constexpr int kRouterBatch = 4;   // router element blocks a thread requests at once (x 4 rows)
 constexpr int kBoundBatch = 4;   // pre-norm element groups a thread requests at once
 
 // A value the wave holds in every lane (LDS reads, the wave index), moved to
@@ -252,56 +252,69 @@ __device__ __forceinline__ void stamp(const BlockParams &p, int slot) {
 // ---------------------------------------------------------------- router
 
 // Logits of expert e for a block of kRouterRowBlock (4) rows, in fp64 (bf16 x
-// fp32 products are exact in fp64), rounded once to fp32.  Wave r takes row
-// r; its lane q adds the products of hidden elements 4q + 256i .. +3 in
-// order, requesting kRouterBatch of them at once; the 64 lane sums of a row
-// are then added through LDS in a fixed order (16 groups of 4, then the 16
+// fp32 products are exact in fp64), rounded once to fp32.  The expert's
+// router row is read once per workgroup: wave w takes hidden elements in
+// 256-element blocks w, w + 4, w + 8, ..; its lane q adds, for each of the
+// four rows, the products of elements 4q .. 4q + 3 of those blocks in order,
+// requesting kRouterBatch blocks at once.  The 256 lane sums of a row are
+// then added through LDS in a fixed order (16 groups of 16, then the 16
 // group sums), with no cross-lane shuffles.
 __device__ __forceinline__ void router_task(const BlockParams &p, const Deps &d, int task,
                                             unsigned char *lds) {
-  const int nrb = (p.b + kRouterRowBlock - 1) / kRouterRowBlock;
-  const int e = task / nrb, t0 = (task % nrb) * kRouterRowBlock;
-  const int r = tid() / MB_WAVE, q = tid() % MB_WAVE;
-  const int t = t0 + r;
-  double *red = reinterpret_cast<double *>(lds);  // [kRouterRowBlock][64], then [kRouterRowBlock][16]
+  constexpr int RB = kRouterRowBlock;
+  const int nrb = (p.b + RB - 1) / RB;
+  const int e = task / nrb, t0 = (task % nrb) * RB;
+  const int w = tid() / MB_WAVE, q = tid() % MB_WAVE;
+  double *red = reinterpret_cast<double *>(lds);  // [RB][kThreads], then [RB][16]
   // Padding elements (past H, or rows past b) load zeros and add nothing.
-  double acc = 0.0;
+  double acc[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) acc[r] = 0.0;
   const rsrc_t rw = make_rsrc(p.router_w + (size_t)e * p.H), rx = make_rsrc(p.x);
-  const uint32_t xrow = t < p.b ? (uint32_t)t * (uint32_t)p.H * 2u : kOob;
-  for (int h0 = 4 * q; h0 < p.H; h0 += 256 * kRouterBatch) {
-    f32x4_t w[kRouterBatch];
-    u32x2_t xv[kRouterBatch];
+  uint32_t xrow[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) xrow[r] = t0 + r < p.b ? (uint32_t)(t0 + r) * (uint32_t)p.H * 2u : kOob;
+  for (int h0 = 4 * q + 256 * w; h0 < p.H; h0 += 256 * kWaves * kRouterBatch) {
+    f32x4_t wv[kRouterBatch];
+    u32x2_t xv[kRouterBatch][RB];
 #pragma unroll
     for (int u = 0; u < kRouterBatch; ++u) {
-      const uint32_t h = (uint32_t)(h0 + 256 * u);
+      const uint32_t h = (uint32_t)(h0 + 256 * kWaves * u);
       const bool in = h < (uint32_t)p.H;
-      w[u] = __builtin_bit_cast(f32x4_t, ld_b128(rw, in ? h * 4 : kOob));
-      xv[u] = ld_b64(rx, in ? xrow + h * 2 : kOob);
+      wv[u] = __builtin_bit_cast(f32x4_t, ld_b128(rw, in ? h * 4 : kOob));
+#pragma unroll
+      for (int r = 0; r < RB; ++r) xv[u][r] = ld_b64(rx, (in && xrow[r] != kOob) ? xrow[r] + h * 2 : kOob);
     }
 #pragma unroll
     for (int u = 0; u < kRouterBatch; ++u) {
-      acc = fma((double)bf16_bits_to_f32(xv[u][0] & 0xFFFFu), (double)w[u][0], acc);
-      acc = fma((double)bf16_bits_to_f32(xv[u][0] >> 16), (double)w[u][1], acc);
-      acc = fma((double)bf16_bits_to_f32(xv[u][1] & 0xFFFFu), (double)w[u][2], acc);
-      acc = fma((double)bf16_bits_to_f32(xv[u][1] >> 16), (double)w[u][3], acc);
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        acc[r] = fma((double)bf16_bits_to_f32(xv[u][r][0] & 0xFFFFu), (double)wv[u][0], acc[r]);
+        acc[r] = fma((double)bf16_bits_to_f32(xv[u][r][0] >> 16), (double)wv[u][1], acc[r]);
+        acc[r] = fma((double)bf16_bits_to_f32(xv[u][r][1] & 0xFFFFu), (double)wv[u][2], acc[r]);
+        acc[r] = fma((double)bf16_bits_to_f32(xv[u][r][1] >> 16), (double)wv[u][3], acc[r]);
+      }
     }
   }
   stamp(p, 23);
-  red[tid()] = acc;
+#pragma unroll
+  for (int r = 0; r < RB; ++r) red[r * kThreads + tid()] = acc[r];
   __syncthreads();
-  if (tid() < kRouterRowBlock * 16) {
-    const double *g = red + (tid() / 16) * MB_WAVE + (tid() % 16) * 4;
-    red[kRouterRowBlock * MB_WAVE + tid()] = ((g[0] + g[1]) + g[2]) + g[3];
+  if (tid() < RB * 16) {
+    const double *g = red + (tid() / 16) * kThreads + (tid() % 16) * 16;
+    double v = g[0];
+    for (int i = 1; i < 16; ++i) v += g[i];
+    red[RB * kThreads + tid()] = v;
   }
   __syncthreads();
-  if (tid() < kRouterRowBlock && t0 + (int)tid() < p.b) {
-    const double *g = red + kRouterRowBlock * MB_WAVE + tid() * 16;
+  if (tid() < RB && t0 + (int)tid() < p.b) {
+    const double *g = red + RB * kThreads + tid() * 16;
     double v = g[0];
     for (int i = 1; i < 16; ++i) v += g[i];
     const size_t te = (size_t)(t0 + tid()) * p.E + e;
     st_co4(make_rsrc(p.logits_f), (uint32_t)(te * 4), __float_as_uint((float)v));
   }
-  signal(d.logits(t0 / kRouterRowBlock));
+  signal(d.logits(t0 / RB));
   stamp(p, 22);
 }
 
