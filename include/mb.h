@@ -32,8 +32,11 @@
  *     reports a failed launch.  Faults inside kernels surface at the caller's
  *     next synchronisation.
  *   - The workspace must be zero-filled once before its first use.  Every
- *     call leaves the counters it uses back at zero, so one workspace serves
- *     any number of calls.  Calls that share a workspace must not overlap.
+ *     call leaves it ready for the next (the persistent launch keeps two
+ *     counter sets there and a generation count that picks one; each launch
+ *     clears the set the next one uses), so one workspace serves any number
+ *     of calls, also replays of a captured graph.  Calls that share a
+ *     workspace must not overlap.
  *   - Limits (MB_ERR_UNSUPPORTED beyond them): rows <= 1024, experts <= 1024,
  *     top_k <= 16, experts * ceil(rows / 64) <= 4096, hidden % 32 == 0,
  *     pooled % 128 == 0, inter % 128 == 0.

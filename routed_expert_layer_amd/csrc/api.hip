@@ -24,10 +24,11 @@ Layout layout_of(const mb_dims &d) {
     o = align256(o + bytes);
     return at;
   };
-  // Words the kernels leave at zero after every call come first, at offsets
-  // that depend only on H and P, so one workspace serves calls of any row
-  // count.
-  L.sync = take(sync_words(d.experts, kMaxRows) * 4);
+  // The persistent launch's state (a fixed size), then the tile counters the
+  // kernels leave at zero after every call, at offsets that depend only on H
+  // and P, so one workspace serves calls of any row count.
+  static_assert(kMaxRows <= kSyncMaxRows, "the counter sets cover every row count");
+  L.sync = take(kSyncWords * 4);
   L.pool_cnt = take((P / 16) * 4);
   L.unpool_cnt = take((H / 16) * 4);
   L.logits = take(b * E * 4);

@@ -6,11 +6,10 @@
 // four lists of work, in this order, in every workgroup:
 //
 //   1. workgroup tasks before routing
-//        router   (expert, hidden slice)  fp64 partial logits; the last
-//                                          slice of an expert to finish
-//                                          writes its fp32 logits          [Wr]
-//        route    (4 rows)                 top-k and weights (many rows)
-//        pool     (16 features, K split)   h = bf16(x Wp^T)                [Wp]
+//        router   (expert, 4 rows)         fp32 logits (fp64 sums)         [Wr]
+//        route    (4 rows)                 top-k and weights
+//        pool     (64 features, K split)   h = bf16(x Wp^T); the last
+//                                          split of a tile adds them       [Wp]
 //        prenorm  (row)                    optional RMSNorm of h
 //   2. the routing state, rebuilt in the workgroup's LDS
 //   3. wave units (each wave on its own: no workgroup barrier)
@@ -18,7 +17,8 @@
 //        down     (expert, 32 features)    y, per-tile sums of squares    [w2]
 //   4. workgroup tasks after the experts
 //        finalize (row, 512 features)      moe_out = bf16(sum_j w_j yn_j)
-//        unpool   (16 features, K split)   u = bf16(moe_out Wu^T)          [Wu]
+//        unpool   (16 or 64 features,      u = moe_out Wu^T, K-split
+//                  K split)                  partials                      [Wu]
 //        boundary (row)                    stream, x_next
 //
 // Workgroup w takes workgroup tasks w, w + G, ... of lists 1 and 4; wave v
@@ -28,7 +28,8 @@
 // expert, finalize for the down units of its row's experts, unpool for the
 // finalize tasks, boundary for the unpool tasks.  Producers add to counters
 // after their coherent stores completed and consumers poll them (mb_block.h:
-// the layout, and copies of widely awaited counters).  Every dependency points
+// the layout, the two counter sets that alternate from launch to launch, and
+// copies of widely awaited counters).  Every dependency points
 // to earlier work in this
 // order and the grid is what the device holds at once, so the earliest
 // unfinished work can always run and the launch completes; every wait is also
@@ -87,18 +88,21 @@ __device__ __forceinline__ unsigned tid() {
 }
 
 struct Deps {
-  unsigned *s;  // the launch state (layout in mb_block.h)
-  int E;
+  unsigned *s;   // the launch state (layout in mb_block.h)
+  unsigned gen;  // this launch's generation (every lane): its counter set is gen % 2
 
-  __device__ unsigned *line(size_t i) const { return s + i * kLine; }
+  __device__ unsigned *line(size_t i) const {
+    const unsigned set = (unsigned)__builtin_amdgcn_readfirstlane((int)gen) & 1u;
+    return s + (sync_line_set((int)set) + i) * kLine;
+  }
   __device__ unsigned *abort_word() const { return s + 1; }
   __device__ unsigned *ctr(int i, int rep = 0) const { return line(sync_line_ctr(i, rep)); }
   // The first stripe of the copy of counter i that this workgroup (or wave:
   // index w) polls.
   __device__ unsigned *mine(int i, int w) const { return ctr(i, (w % replicas(i)) * stripes(i)); }
-  __device__ unsigned *up(int e) const { return line(sync_line_up(E, e)); }
-  __device__ unsigned *down(int e) const { return line(sync_line_down(E, e)); }
-  __device__ unsigned *logits(int rb) const { return line(sync_line_logits(E, rb)); }
+  __device__ unsigned *up(int e) const { return line(sync_line_up(e)); }
+  __device__ unsigned *down(int e) const { return line(sync_line_down(e)); }
+  __device__ unsigned *logits(int rb) const { return line(sync_line_logits(rb)); }
 };
 
 __device__ __forceinline__ unsigned atomic_inc(unsigned *c) {
@@ -107,6 +111,34 @@ __device__ __forceinline__ unsigned atomic_inc(unsigned *c) {
 
 __device__ __forceinline__ void store_co(unsigned *w, unsigned v) {
   __hip_atomic_store(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Generation not yet requested: a workgroup that starts with a router task
+// requests it inside that task (should the generation itself equal this
+// value, a later router task of the workgroup merely requests it again).
+constexpr unsigned kGenPending = 0xFFFFFFFFu;
+
+// This workgroup's generation word (coherent: the previous launch wrote it).
+// The offset is opaque to the compiler, so the value stays in a vector
+// register and is first waited for where a counter is used, not here.
+__device__ __forceinline__ unsigned load_generation(const unsigned *state) {
+  uint32_t off = (uint32_t)(kLine + blockIdx.x) * 4u;
+  asm volatile("" : "+v"(off));
+  return ld_co4(make_rsrc(state), off);
+}
+
+// For the next launch, at the end of a workgroup: clear its share of the
+// other counter set (16-byte stores) and advance the generation words it
+// owns (b, b + G, ..).  Nothing reads either during this launch.
+__device__ __forceinline__ void prepare_next_launch(unsigned *state, unsigned gen) {
+  const unsigned G = gridDim.x;
+  const rsrc_t rs = make_rsrc(state);
+  const uint32_t other = (uint32_t)(sync_line_set((int)((gen + 1u) & 1u)) * kLine * 4);
+  constexpr uint32_t kPieces = (uint32_t)(kSetLines * kLine / 4);
+  for (uint32_t i = blockIdx.x * kThreads + tid(); i < kPieces; i += G * kThreads)
+    st_co16(rs, other + 16u * i, u32x4_t{0u, 0u, 0u, 0u});
+  for (unsigned w = blockIdx.x + G * tid(); w < (unsigned)kMaxGrid; w += G * kThreads)
+    st_co4(rs, (uint32_t)(kLine + w) * 4u, gen + 1u);
 }
 
 // Workgroup: every wave's coherent stores complete, then one increment.
@@ -202,35 +234,6 @@ __device__ __forceinline__ void wave_wait_step(const Deps &d, int i, int target)
     poll_sum_ge(d, d.mine(i, blockIdx.x * kWaves + tid() / MB_WAVE), stripes(i), (unsigned)target);
 }
 
-// The end of a workgroup: count it finished; the last workgroup sets the
-// launch state back to zero for the next launch (every other workgroup has
-// finished all its waits).
-__device__ __forceinline__ void finish(const Deps &d, int nrb, int *flag) {
-  wait_stores();
-  __syncthreads();
-  // Two levels: workgroup w counts into stripe w % 16, and the workgroup that
-  // completes a stripe counts into the top word.  (Hundreds of workgroups
-  // ending together on one address queue their increments ahead of every
-  // other atomic of the launch.)
-  if (tid() == 0) {
-    const unsigned G = gridDim.x, ns = G < (unsigned)kReplicas ? G : (unsigned)kReplicas, s = blockIdx.x % ns;
-    const unsigned quota = (G - s + ns - 1) / ns;
-    bool last = false;
-    if (atomic_inc(d.ctr(kCtrFinished, (int)s)) == quota - 1u) last = atomic_inc(d.ctr(kCtrFinishedTop)) == ns - 1u;
-    *flag = last;
-  }
-  __syncthreads();
-  if (!*flag) return;
-  for (int i = tid(); i < kNumCtr * kReplicas; i += kThreads)
-    if (i % kReplicas < replicas(i / kReplicas) * stripes(i / kReplicas))
-      store_co(d.ctr(i / kReplicas, i % kReplicas), 0u);
-  for (int e = tid(); e < d.E; e += kThreads) {
-    store_co(d.up(e), 0u);
-    store_co(d.down(e), 0u);
-  }
-  for (int rb = tid(); rb < nrb; rb += kThreads) store_co(d.logits(rb), 0u);
-}
-
 // Tracing: workgroup thread 0 stamps the 100 MHz real-time counter at the
 // start (slot 0), when it enters its first task of each step (router 1,
 // route 2, pool 3, prenorm 4, finalize 8, unpool 9, boundary 10), when its
@@ -259,8 +262,7 @@ __device__ __forceinline__ void stamp(const BlockParams &p, int slot) {
 // requesting kRouterBatch blocks at once.  The 256 lane sums of a row are
 // then added through LDS in a fixed order (16 groups of 16, then the 16
 // group sums), with no cross-lane shuffles.
-__device__ __forceinline__ void router_task(const BlockParams &p, const Deps &d, int task,
-                                            unsigned char *lds) {
+__device__ __forceinline__ void router_task(const BlockParams &p, unsigned &gen, int task, unsigned char *lds) {
   constexpr int RB = kRouterRowBlock;
   const int nrb = (p.b + RB - 1) / RB;
   const int e = task / nrb, t0 = (task % nrb) * RB;
@@ -274,6 +276,7 @@ __device__ __forceinline__ void router_task(const BlockParams &p, const Deps &d,
   uint32_t xrow[RB];
 #pragma unroll
   for (int r = 0; r < RB; ++r) xrow[r] = t0 + r < p.b ? (uint32_t)(t0 + r) * (uint32_t)p.H * 2u : kOob;
+  bool need_gen = gen == kGenPending;
   for (int h0 = 4 * q + 256 * w; h0 < p.H; h0 += 256 * kWaves * kRouterBatch) {
     f32x4_t wv[kRouterBatch];
     u32x2_t xv[kRouterBatch][RB];
@@ -284,6 +287,12 @@ __device__ __forceinline__ void router_task(const BlockParams &p, const Deps &d,
       wv[u] = __builtin_bit_cast(f32x4_t, ld_b128(rw, in ? h * 4 : kOob));
 #pragma unroll
       for (int r = 0; r < RB; ++r) xv[u][r] = ld_b64(rx, (in && xrow[r] != kOob) ? xrow[r] + h * 2 : kOob);
+    }
+    // The workgroup's generation, behind the wave's first router requests
+    // (its waits for them do not include it).
+    if (need_gen) {
+      gen = load_generation(p.sync);
+      need_gen = false;
     }
 #pragma unroll
     for (int u = 0; u < kRouterBatch; ++u) {
@@ -296,6 +305,8 @@ __device__ __forceinline__ void router_task(const BlockParams &p, const Deps &d,
       }
     }
   }
+  // (A wave with no hidden elements here requests it now.)
+  if (need_gen) gen = load_generation(p.sync);
   stamp(p, 23);
 #pragma unroll
   for (int r = 0; r < RB; ++r) red[r * kThreads + tid()] = acc[r];
@@ -314,6 +325,7 @@ __device__ __forceinline__ void router_task(const BlockParams &p, const Deps &d,
     const size_t te = (size_t)(t0 + tid()) * p.E + e;
     st_co4(make_rsrc(p.logits_f), (uint32_t)(te * 4), __float_as_uint((float)v));
   }
+  const Deps d{p.sync, gen};
   signal(d.logits(t0 / RB));
   stamp(p, 22);
 }
@@ -1488,6 +1500,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   extern __shared__ __align__(16) unsigned char lds[];
   (void)p_arg;  // read through kparams()
   stamp(kparams(), 0);
+  // Requested now, first needed at a counter.
+  // (A workgroup that starts with a router task requests it there.)
+  unsigned gen = blockIdx.x < (unsigned)kparams().n_router ? kGenPending : load_generation(kparams().sync);
   const int G = gridDim.x;
   {
     // The grouping's per-expert row bitmaps start empty.
@@ -1504,7 +1519,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     int last = -1;
     for (int j = blockIdx.x;; j += G) {
       const BlockParams &p = kparams();
-      const Deps d{p.sync, p.E};
+      const Deps d{p.sync, gen};
       const RouteLds R = route_lds(p, lds);
       unsigned char *scratch = lds + p.lds_route_bytes;
       const int nR = p.n_router, nRT = p.n_route, nP = p.n_pool, nPN = p.n_prenorm;
@@ -1525,7 +1540,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         last = step;
       }
       if (step == 1) {
-        router_task(p, d, i, scratch);
+        router_task(p, gen, i, scratch);
       } else if (step == 2) {
         route_task(p, d, R, i);
       } else if (step == 3) {
@@ -1552,7 +1567,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // 2. Routing state (workgroup 0 also writes the routing outputs).
   {
   const BlockParams &p = kparams();
-  const Deps d{p.sync, p.E};
+  const Deps d{p.sync, gen};
   const RouteLds R = route_lds(p, lds);
   if (p.needs_routing && (p.has_up || (p.routing_out && blockIdx.x == 0))) {
     prepare_routing(p, d, R);
@@ -1563,7 +1578,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // 3. Expert units, one wave each.
   if (kparams().has_up) {
     const BlockParams &p = kparams();
-    const Deps d{p.sync, p.E};
+    const Deps d{p.sync, gen};
     const RouteLds R = route_lds(p, lds);
     unsigned char *scratch = lds + p.lds_route_bytes;
     stamp(p, 6);
@@ -1598,7 +1613,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     int last = -1;
     for (int j = blockIdx.x;; j += G) {
       const BlockParams &p = kparams();
-      const Deps d{p.sync, p.E};
+      const Deps d{p.sync, gen};
       const RouteLds R = route_lds(p, lds);
       unsigned char *scratch = lds + p.lds_route_bytes;
       const int nF = p.n_fin, nN = p.n_unpool, nB = p.n_boundary;
@@ -1638,13 +1653,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       }
     }
   }
-  {
-  const BlockParams &p = kparams();
-  const Deps d{p.sync, p.E};
-  unsigned char *scratch = lds + p.lds_route_bytes;
-  stamp(p, 15);
-  finish(d, (p.b + kRouterRowBlock - 1) / kRouterRowBlock, reinterpret_cast<int *>(scratch));
-  }
+  prepare_next_launch(kparams().sync, gen);
+  stamp(kparams(), 15);
 }
 
 }  // namespace

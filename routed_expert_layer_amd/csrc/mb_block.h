@@ -12,47 +12,52 @@ namespace mb {
 constexpr int kBlockWaves = 4;      // waves per workgroup
 constexpr int kRouterRowBlock = 4;   // rows per router task (one wave each)
 
-// Cross-workgroup state of one launch, at the workspace start, in 128-byte
-// lines of kLine words so that no two counters share a line:
+// Cross-workgroup state, at the workspace start, in 128-byte lines of kLine
+// words so that no two counters share a line:
 //   line 0      word 1: the abort word (set when a wait timed out)
-//   kNumCtr x kReplicas lines   step counters (kCtr*), each spread over
-//               stripes(i) x replicas(i) lines
-//   2E lines    up units done per expert, then down units done
-//   ceil(b/4) lines   router tasks done per block of kRouterRowBlock rows
-// Everything but the abort word is zero when a launch starts, and the last
-// workgroup to finish sets it back to zero.  Increments of one address are
-// serialized, and polls of an address delay the increments to it.  So a step
-// counter is held in replicas(i) copies, each split into stripes(i) lines: a
-// producer adds one to its stripe (chosen by its workgroup index) of every
-// copy, after its coherent stores completed (one atomic per lane of one
-// instruction); a consumer sums the stripes of the copy its workgroup or
-// wave index selects.  Many consumers call for copies, many producers for
-// stripes.
+//   kGenLines lines   the generation words, one per workgroup index
+//   two counter sets of kSetLines lines each, a set being
+//     kNumCtr x kReplicas lines   step counters (kCtr*), each spread over
+//                 stripes(i) x replicas(i) lines
+//     2 kBlockMaxExperts lines   up units done per expert, then down units
+//     kSyncMaxRows / 4 lines     router tasks done per block of 4 rows
+// Between launches every generation word holds the same value g (0 in a
+// zero-filled workspace).  A launch uses counter set g % 2, which is zero
+// when it starts; its workgroups clear set (g + 1) % 2, which the previous
+// launch used, and each workgroup b writes g + 1 into the generation words
+// b, b + G, b + 2G, .. (G = the grid), so that every word advances by one
+// whatever the grid.  No workgroup has to find out that it is the last.
+// Increments of one address are serialized, and polls of an address delay
+// the increments to it.  So a step counter is held in replicas(i) copies,
+// each split into stripes(i) lines: a producer adds one to its stripe (chosen
+// by its workgroup index) of every copy, after its coherent stores completed
+// (one atomic per lane of one instruction); a consumer sums the stripes of
+// the copy its workgroup or wave index selects.  Many consumers call for
+// copies, many producers for stripes.
 constexpr int kLine = 32;
 constexpr int kReplicas = 16;
 constexpr int kMaxGrid = 1024;  // workgroups of the persistent launch, at most
+constexpr int kBlockMaxExperts = 256;  // larger expert counts use the per-step kernels
+constexpr int kSyncMaxRows = 1024;     // rows the counter sets provide for
 enum : int {
-  kCtrFinishedTop = 0,  // stripes of kCtrFinished completed
-  kCtrRoute = 1,     // route tasks done
-  kCtrPool = 2,      // pooler tiles complete
-  kCtrPrenorm = 3,   // pre-norm rows done
-  kCtrFin = 4,       // finalize tasks done
-  kCtrUnpool = 5,    // unpooler tasks done
-  kCtrFinished = 6,  // workgroups finished
-  kNumCtr = 8,
+  kCtrRoute = 0,     // route tasks done
+  kCtrPool = 1,      // pooler tiles complete
+  kCtrPrenorm = 2,   // pre-norm rows done
+  kCtrFin = 3,       // finalize tasks done
+  kCtrUnpool = 4,    // unpooler tasks done
+  kNumCtr = 5,
 };
 // Copies and stripes of step counter i (replicas x stripes <= kReplicas).
 // The route and pre-norm counters have few producers and are awaited by
 // every workgroup or wave; the pooler's has 128 producers (H / 16 tiles) and
 // every wave as consumer; the finalize counter has b * P / 512 producers and
 // the unpooler tasks as consumers; the unpooler's has H / 16 (times its
-// split) producers and only the b boundary tasks as consumers; the finished
-// counter has every workgroup as producer (and a second level, the top word).
+// split) producers and only the b boundary tasks as consumers.
 __host__ __device__ constexpr int replicas(int i) {
   return (i == kCtrRoute || i == kCtrPrenorm) ? kReplicas : (i == kCtrPool || i == kCtrFin) ? 4 : 1;
 }
 __host__ __device__ constexpr int stripes(int i) {
-  return (i == kCtrPool || i == kCtrFin) ? 4 : (i == kCtrUnpool || i == kCtrFinished) ? kReplicas : 1;
+  return (i == kCtrPool || i == kCtrFin) ? 4 : i == kCtrUnpool ? kReplicas : 1;
 }
 constexpr bool counters_fit() {
   for (int i = 0; i < kNumCtr; ++i)
@@ -60,18 +65,20 @@ constexpr bool counters_fit() {
   return true;
 }
 static_assert(counters_fit(), "a step counter needs more lines than it has");
-__host__ __device__ inline size_t sync_line_ctr(int i, int rep) { return 1 + (size_t)i * kReplicas + rep; }
-__host__ __device__ inline size_t sync_line_up(int E, int e) { return sync_line_ctr(kNumCtr, 0) + e; }
-__host__ __device__ inline size_t sync_line_down(int E, int e) { return sync_line_up(E, E) + e; }
-__host__ __device__ inline size_t sync_line_logits(int E, int rb) { return sync_line_down(E, E) + rb; }
-inline size_t sync_words(int E, int rows) {
-  return sync_line_logits(E, (rows + kRouterRowBlock - 1) / kRouterRowBlock) * kLine;
-}
+constexpr int kGenLines = kMaxGrid / kLine;
+// Lines within a counter set.
+__host__ __device__ constexpr size_t sync_line_ctr(int i, int rep) { return (size_t)i * kReplicas + rep; }
+__host__ __device__ constexpr size_t sync_line_up(int e) { return sync_line_ctr(kNumCtr, 0) + e; }
+__host__ __device__ constexpr size_t sync_line_down(int e) { return sync_line_up(kBlockMaxExperts) + e; }
+__host__ __device__ constexpr size_t sync_line_logits(int rb) { return sync_line_down(kBlockMaxExperts) + rb; }
+constexpr size_t kSetLines = sync_line_logits((kSyncMaxRows + kRouterRowBlock - 1) / kRouterRowBlock);
+// Line of counter set `set`'s first line, from the start of the state.
+__host__ __device__ constexpr size_t sync_line_set(int set) { return 1 + kGenLines + (size_t)set * kSetLines; }
+constexpr size_t kSyncWords = sync_line_set(2) * kLine;
 
 constexpr int kFinChunk = 512;  // features per finalize task
 constexpr int kMaxPoolSplit = 32;  // contraction splits of the pooler
 constexpr int kMoeReplicas = 8;  // copies of the MoE output for the unpooler tasks
-constexpr int kBlockMaxExperts = 256;  // larger expert counts use the per-step kernels
 constexpr int kTimelineSlots = 32;
 constexpr int kBlockGroupsPerCu = 3;  // resident workgroups per CU (one wave per SIMD each)
 
