@@ -1379,22 +1379,23 @@ __device__ __forceinline__ void boundary_task(const BlockParams &p, const Deps &
   const rsrc_t rg = make_rsrc(p.gate), rs = make_rsrc(p.stream + (size_t)t * H);
   u32x2_t gv[NG], fv[NG], wv[NG];
   f32x4_t sv[NG];
+  // Everything but the unpooler's output is requested before the wait (the
+  // next norm's weights later for wide rows: registers).
+  constexpr bool kEarlyNext = NG <= 4;
+  auto next_norm = [&](bool in, uint32_t h) {
+    return p.next_norm_w ? ld_b64(make_rsrc(p.next_norm_w), in ? h * 2 : kOob) : u32x2_t{0x3F803F80u, 0x3F803F80u};
+  };
 #pragma unroll
   for (int m = 0; m < NG; ++m) {
     const uint32_t h = (uint32_t)(4 * tid() + 1024 * m);
     const bool in = h * 2 < H2;
     gv[m] = ld_b64(rg, in ? h * 2 : kOob);
     sv[m] = __builtin_bit_cast(f32x4_t, ld_b128(rs, in ? h * 4 : kOob));
+    fv[m] = p.ffn_norm_w ? ld_b64(make_rsrc(p.ffn_norm_w), in ? h * 2 : kOob) : u32x2_t{0x3F803F80u, 0x3F803F80u};
+    if (kEarlyNext) wv[m] = next_norm(in, h);
   }
   wait_step(d, kCtrUnpool, p.n_unpool);
   stamp(p, 17);
-  // The norm weights are needed only after the first reduction.
-#pragma unroll
-  for (int m = 0; m < NG; ++m) {
-    const uint32_t h = (uint32_t)(4 * tid() + 1024 * m);
-    const bool in = h * 2 < H2;
-    fv[m] = p.ffn_norm_w ? ld_b64(make_rsrc(p.ffn_norm_w), in ? h * 2 : kOob) : u32x2_t{0x3F803F80u, 0x3F803F80u};
-  }
   u32x2_t uv[NG];
   if (p.unpool_ks > 1) {
     // u = bf16(sum of the split partials in split order).
@@ -1442,11 +1443,12 @@ __device__ __forceinline__ void boundary_task(const BlockParams &p, const Deps &
     unpack4(uv[m], v);
     ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
   }
+  if (!kEarlyNext) {
 #pragma unroll
-  for (int m = 0; m < NG; ++m) {
-    const uint32_t h = (uint32_t)(4 * tid() + 1024 * m);
-    const bool in = h * 2 < H2;
-    wv[m] = p.next_norm_w ? ld_b64(make_rsrc(p.next_norm_w), in ? h * 2 : kOob) : u32x2_t{0x3F803F80u, 0x3F803F80u};
+    for (int m = 0; m < NG; ++m) {
+      const uint32_t h = (uint32_t)(4 * tid() + 1024 * m);
+      wv[m] = next_norm(h * 2 < H2, h);
+    }
   }
   ss = wg_sum(ss, red, 0);
   const float rsu = 1.0f / sqrtf(ss / (float)H + p.norm_eps);
