@@ -156,10 +156,15 @@ __device__ __forceinline__ void signal_step(const Deps &d, int i) {
   if (tid() < replicas(i)) atomic_inc(d.ctr(i, tid() * stripes(i) + (int)(blockIdx.x % stripes(i))));
 }
 
-// One wave: its coherent stores complete, then one increment.
-__device__ __forceinline__ void wave_signal(unsigned *c) {
+// Workgroup after expert units: every wave's coherent stores complete, then
+// one increment by the workgroup's kWaves units.  (Units go to workgroups
+// four at a time, consecutive tiles of one expert, so a workgroup's waves
+// take their units together and the expert's counter sees a quarter of the
+// increments -- and of the polls -- it would see from every wave.)
+__device__ __forceinline__ void signal_units(unsigned *c) {
   wait_stores();
-  if (tid() % MB_WAVE == 0) atomic_inc(c);
+  __syncthreads();
+  if (tid() == 0) __hip_atomic_fetch_add(c, (unsigned)kWaves, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Workgroup: after its coherent stores, add one to counter c; true in the
@@ -1230,7 +1235,7 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
       }
     }
   }
-  wave_signal(d.up(e));
+  signal_units(d.up(e));
 }
 
 // Down unit: w2 for (active expert, 32 output features): y in route order and
@@ -1258,7 +1263,9 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
     auto row_off = [&](int m) { return m0 + m < nrows ? (uint32_t)((row0 + m0 + m) * I) * 2u : kOob; };
     auto wait = [&]() {
       if (!ready) {
-        poll_ge(d, d.up(e), (unsigned)(I / 16));
+        // (One wave polls for the workgroup.)
+        if (tid() < MB_WAVE) poll_ge(d, d.up(e), (unsigned)(I / 16));
+        __syncthreads();
         ready = true;
       }
     };
@@ -1286,7 +1293,7 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
       }
     }
   }
-  wave_signal(d.down(e));
+  signal_units(d.down(e));
 }
 
 // ---------------------------------------------------------------- tail
@@ -1593,7 +1600,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // belong to the experts of its own up units (with as many tiles per
     // expert): they wait on waves that started with them.  (Waves that
     // reach the memory system later -- the later workgroups on a CU -- finish
-    // their up units later.)
+    // their up units later.)  Unit counts are multiples of four (I / 16 and
+    // P / 32 tiles per expert) and so is the wave count, so the four waves of
+    // a workgroup always have units, of one expert, in the same rounds: the
+    // units' workgroup barriers and signals rely on it.
     const int gw = blockIdx.x * kWaves + uniform(tid() / MB_WAVE);
     // (The expert layout is a template argument: each has its own registers.)
     if (p.xp) {
