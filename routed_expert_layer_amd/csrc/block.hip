@@ -1003,7 +1003,9 @@ __device__ __forceinline__ int pass_rows(int nrows) { return nrows <= 8 ? 8 : nr
 // Activations (written by other workgroups of the launch, so read
 // coherently): the rows' elements of up to kStageChunkRows / pr chunks at a time are
 // loaded by the whole workgroup in 16-byte pieces into `stage` (row m at
-// m * (its chunks * 256 + 16); rows past the pass and chunks past nch as zeros), then
+// m * (its chunks * 256 + 16); chunks past nch as zeros; rows past the pass's
+// vrows valid rows hold whatever the stage held -- their columns are never
+// stored), then
 // each wave reads its MFMA operand from there: lane l reads row l % 8 (pr 8)
 // or l % 16 (of each 16-row block).
 // row_off(m) is the byte offset of pass row m's element 0, or kOob.
@@ -1016,7 +1018,7 @@ template <bool kLane> struct ScaleWord { using type = u32x4_t; };
 template <> struct ScaleWord<true> { using type = uint32_t; };
 
 template <int kRing, bool kLane, typename Wait, typename RowOff>
-__device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, int pr, rsrc_t ra, RowOff row_off,
+__device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, int pr, int vrows, rsrc_t ra, RowOff row_off,
                                         unsigned char *stage, f32x4_t (&d0)[2], f32x4_t (&d1)[2], int slot,
                                         Wait wait) {
   const int lane = tid() % MB_WAVE, g = lane >> 4;
@@ -1067,9 +1069,12 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, int pr, rsrc_
     // This segment's activations, chunks rounded up to whole rounds.
     const int segn = min(seg, nch - seg0);
     const int ppr = ((segn + kRing - 1) / kRing) * kRing * 16;  // 16-byte pieces per row
-    // In two batches of half the pieces (registers).
+    // In two batches of half the pieces (registers); the second only if it
+    // holds one of the pass's vrows rows (the rest are padding: their
+    // columns are not stored).
 #pragma unroll
     for (int n0 = 0; n0 < kSegLoads; n0 += kSegLoads / 2) {
+      if (n0 > 0 && (kThreads * n0) / ppr >= vrows) continue;
       u32x4_t v[kSegLoads / 2];
 #pragma unroll
       for (int n = 0; n < kSegLoads / 2; ++n) {
@@ -1132,7 +1137,7 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, int pr, rsrc_
 // one segment and every chunk is computed with no further weight requests.
 // Same operands, staging and results as mx_pair (block 0 of d0 / d1 only).
 template <int kAll, typename Wait, typename RowOff>
-__device__ __forceinline__ void mx_pair_all(const MxTiles &T, int nch, int pr, rsrc_t ra, RowOff row_off,
+__device__ __forceinline__ void mx_pair_all(const MxTiles &T, int nch, int pr, int vrows, rsrc_t ra, RowOff row_off,
                                             unsigned char *stage, f32x4_t (&d0)[2], f32x4_t (&d1)[2], Wait wait) {
   static_assert(kAll % 4 == 0 && 16 * kAll <= kStageChunkRows, "whole scale words; 16 rows x kAll chunks staged");
   const int lane = tid() % MB_WAVE, g = lane >> 4;
@@ -1154,10 +1159,12 @@ __device__ __forceinline__ void mx_pair_all(const MxTiles &T, int nch, int pr, r
   wait();
   const int srow = kAll * 256 + 16;  // row stride in the stage
   d0[0] = d1[0] = d0[1] = d1[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // Rows past the pass and chunks past nch are staged as zeros.
+  // Chunks past nch are staged as zeros; the second batch only if it holds
+  // one of the pass's vrows rows.
   constexpr int ppr = kAll * 16;  // 16-byte pieces per row
 #pragma unroll
   for (int n0 = 0; n0 < kSegLoads; n0 += kSegLoads / 2) {
+    if (n0 > 0 && (kThreads * n0) / ppr >= vrows) continue;
     u32x4_t v[kSegLoads / 2];
 #pragma unroll
     for (int n = 0; n < kSegLoads / 2; ++n) {
@@ -1212,7 +1219,7 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
   for (int m0 = 0; m0 < nrows; m0 += pr) {
     f32x4_t gs[2], us[2];
     mx_pair<kRingUp, kPacked>(
-        T, nch, pr, rh,
+        T, nch, pr, min(pr, nrows - m0), rh,
         [&](int m) { return m0 + m < nrows ? (uint32_t)((R.rl[row0 + m0 + m] / p.k) * P) * 2u : kOob; }, stage,
         gs, us, (int)blockIdx.x / p.cus, [&]() {
           if (!h_ready) {
@@ -1270,9 +1277,10 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
       }
     };
     if (kPacked && nch <= kDownAll && pr <= 16)
-      mx_pair_all<kDownAll>(T, nch, pr, ract, row_off, stage, y0, y1, wait);
+      mx_pair_all<kDownAll>(T, nch, pr, min(pr, nrows - m0), ract, row_off, stage, y0, y1, wait);
     else
-      mx_pair<kRingDown, kPacked>(T, nch, pr, ract, row_off, stage, y0, y1, (int)blockIdx.x / p.cus, wait);
+      mx_pair<kRingDown, kPacked>(T, nch, pr, min(pr, nrows - m0), ract, row_off, stage, y0, y1, (int)blockIdx.x / p.cus,
+                                  wait);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       if (b == 1 && pr <= 16) break;
