@@ -307,11 +307,13 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   }
   // The unpooler: 16-feature tiles with every weight requested before the
   // wait at few rows; at many rows 64-feature tiles, so that the MoE output
-  // is read once per 64 features.
+  // is read once per 64 features, split along P to fill the grid (its tasks
+  // follow the finalize tasks, which all end before any unpooler work can
+  // start, so the whole grid is theirs).
   p.unpool_wide = p.b > 16 ? 1 : 0;
   if (p.unpool_wide) {
     const int groups = (p.H + 63) / 64;
-    int ks = std::min(kMaxSplitK, std::max(1, (grid - n_fin - n_boundary) / groups));
+    int ks = std::min(kMaxSplitK, std::max(1, grid / groups));
     while (ks > 1 && (p.P % ks != 0 || (p.P / ks) % 32 != 0)) --ks;
     p.unpool_ks = ks;
   } else {
