@@ -286,7 +286,12 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   if (grid > kMaxGrid) grid = kMaxGrid;
   p.lds_route_bytes = (int)route_bytes;
   p.cus = cus;
-  const int n_router = st.router ? p.E * ((p.b + kRouterRowBlock - 1) / kRouterRowBlock) : 0;
+  // Router tasks: one expert x 4 rows, or kRouterExperts experts x 4 rows
+  // when one-expert tasks would not fit the grid at once.
+  const int nrb = (p.b + kRouterRowBlock - 1) / kRouterRowBlock;
+  p.router_multi = p.E * nrb > grid ? 1 : 0;
+  const int n_router =
+      st.router ? (p.router_multi ? (p.E + kRouterExperts - 1) / kRouterExperts : p.E) * nrb : 0;
   const int n_fin = st.experts ? p.b * ((p.P + kFinChunk - 1) / kFinChunk) : 0;
   const int n_boundary = st.unpool ? p.b : 0;
   const int n_prenorm = (st.pool && p.pre_norm_w) ? p.b : 0;

@@ -335,6 +335,88 @@ __device__ __forceinline__ void router_task(const BlockParams &p, unsigned &gen,
   stamp(p, 22);
 }
 
+// Many rows (more router tasks than workgroups at one expert each): the
+// logits of kRouterExperts (4) experts for a block of 4 rows.  Same split of
+// the hidden elements over the waves and lanes as router_task, the lane
+// holding 16 fp64 sums; each (expert, row) sum is reduced across the wave
+// (butterfly, the same in every lane) and then over the four waves in wave
+// order, and rounded once to fp32.  The hidden states are read once per four
+// experts instead of once per expert.
+__device__ __forceinline__ void router_task_multi(const BlockParams &p, unsigned &gen, int task,
+                                                  unsigned char *lds) {
+  constexpr int RB = kRouterRowBlock, XE = kRouterExperts, kB = 2;  // blocks per request batch
+  const int nrb = (p.b + RB - 1) / RB;
+  const int e0 = (task / nrb) * XE, t0 = (task % nrb) * RB;
+  const int w = tid() / MB_WAVE, q = tid() % MB_WAVE;
+  double *red = reinterpret_cast<double *>(lds);  // [kWaves][XE * RB]
+  double acc[XE][RB];
+#pragma unroll
+  for (int j = 0; j < XE; ++j)
+#pragma unroll
+    for (int r = 0; r < RB; ++r) acc[j][r] = 0.0;
+  const rsrc_t rw = make_rsrc(p.router_w), rx = make_rsrc(p.x);
+  uint32_t xrow[RB], wrow[XE];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) xrow[r] = t0 + r < p.b ? (uint32_t)(t0 + r) * (uint32_t)p.H * 2u : kOob;
+#pragma unroll
+  for (int j = 0; j < XE; ++j) wrow[j] = e0 + j < p.E ? (uint32_t)(e0 + j) * (uint32_t)p.H * 4u : kOob;
+  bool need_gen = gen == kGenPending;
+  for (int h0 = 4 * q + 256 * w; h0 < p.H; h0 += 256 * kWaves * kB) {
+    f32x4_t wv[kB][XE];
+    u32x2_t xv[kB][RB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const uint32_t h = (uint32_t)(h0 + 256 * kWaves * u);
+      const bool in = h < (uint32_t)p.H;
+#pragma unroll
+      for (int j = 0; j < XE; ++j)
+        wv[u][j] = __builtin_bit_cast(f32x4_t, ld_b128(rw, (in && wrow[j] != kOob) ? wrow[j] + h * 4 : kOob));
+#pragma unroll
+      for (int r = 0; r < RB; ++r) xv[u][r] = ld_b64(rx, (in && xrow[r] != kOob) ? xrow[r] + h * 2 : kOob);
+    }
+    if (need_gen) {
+      gen = load_generation(p.sync);
+      need_gen = false;
+    }
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        const double x0 = bf16_bits_to_f32(xv[u][r][0] & 0xFFFFu), x1 = bf16_bits_to_f32(xv[u][r][0] >> 16);
+        const double x2 = bf16_bits_to_f32(xv[u][r][1] & 0xFFFFu), x3 = bf16_bits_to_f32(xv[u][r][1] >> 16);
+#pragma unroll
+        for (int j = 0; j < XE; ++j) {
+          acc[j][r] = fma(x0, (double)wv[u][j][0], acc[j][r]);
+          acc[j][r] = fma(x1, (double)wv[u][j][1], acc[j][r]);
+          acc[j][r] = fma(x2, (double)wv[u][j][2], acc[j][r]);
+          acc[j][r] = fma(x3, (double)wv[u][j][3], acc[j][r]);
+        }
+      }
+  }
+  if (need_gen) gen = load_generation(p.sync);
+  stamp(p, 23);
+#pragma unroll
+  for (int j = 0; j < XE; ++j)
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const double v = wave_sum(acc[j][r]);
+      if (q == 0) red[w * XE * RB + j * RB + r] = v;
+    }
+  __syncthreads();
+  if (tid() < XE * RB) {
+    const int j = tid() / RB, r = tid() % RB;
+    double v = red[tid()];
+    for (int ww = 1; ww < kWaves; ++ww) v += red[ww * XE * RB + tid()];
+    if (t0 + r < p.b && e0 + j < p.E) {
+      const size_t te = (size_t)(t0 + r) * p.E + e0 + j;
+      st_co4(make_rsrc(p.logits_f), (uint32_t)(te * 4), __float_as_uint((float)v));
+    }
+  }
+  const Deps d{p.sync, gen};
+  signal(d.logits(t0 / RB));
+  stamp(p, 22);
+}
+
 // ---------------------------------------------------------------- routing
 
 // fp32 logit (t, e): given by the caller, or the router's.
@@ -622,7 +704,8 @@ __device__ __forceinline__ void route_task(const BlockParams &p, const Deps &d, 
                                            int task) {
   const int t0 = task * kWaves, t1 = min(p.b, t0 + kWaves);
   route_dispatch(p, R, t0, t1, [&]() {
-    if (p.n_logit_producers > 0) wait_ge(d, d.logits(task), (unsigned)p.E);
+    if (p.n_logit_producers > 0)
+      wait_ge(d, d.logits(task), (unsigned)(p.router_multi ? (p.E + kRouterExperts - 1) / kRouterExperts : p.E));
     stamp(p, 12);
   });
   stamp(p, 14);
@@ -1557,7 +1640,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         last = step;
       }
       if (step == 1) {
-        router_task(p, gen, i, scratch);
+        if (p.router_multi) router_task_multi(p, gen, i, scratch);
+        else router_task(p, gen, i, scratch);
       } else if (step == 2) {
         route_task(p, d, R, i);
       } else if (step == 3) {

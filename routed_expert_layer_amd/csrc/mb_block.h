@@ -10,7 +10,8 @@
 namespace mb {
 
 constexpr int kBlockWaves = 4;      // waves per workgroup
-constexpr int kRouterRowBlock = 4;   // rows per router task (one wave each)
+constexpr int kRouterRowBlock = 4;   // rows per router task
+constexpr int kRouterExperts = 4;    // experts per router task when there are many rows
 
 // Cross-workgroup state, at the workspace start, in 128-byte lines of kLine
 // words so that no two counters share a line:
@@ -117,6 +118,7 @@ struct BlockParams {
   int pool_ks, unpool_ks, n_pool_tiles, h_producers;
   int has_up, needs_routing, routing_out, route_given, logits_in;
   int unpool_wide;  // unpooler in 64-feature tiles (many rows)
+  int router_multi; // router tasks of kRouterExperts experts (many rows)
   int cus;          // compute units (the grid holds grid / cus workgroups per CU)
   int lds_route_bytes;
   // inputs
