@@ -32,8 +32,10 @@ from .steps import (  # noqa: F401
     decode_e8m0,
     dequant_mxfp4,
     experts,
+    fake_quant_mxfp4,
     group_routes,
     pool,
+    quantize_mxfp4,
     rms_norm,
     round_bf16,
     route,

@@ -24,6 +24,14 @@ Readings where the pages leave a step open (each restated where it is used):
 * MXFP4: E2M1 codes, two per byte, the even element in the low nibble; one
   E8M0 scale per 32 elements along the contraction dimension (OCP Microscaling
   Formats v1.0, sections 5.3.3 and 5.4.1).
+* MXFP4 activations (the W4A4 variant; the pages leave the quantizer to their
+  AITER backend): OCP Microscaling Formats v1.0, section 6.3 -- per block of 32
+  along the contraction dimension, shared exponent floor(log2(amax)) - 2 (2 =
+  E2M1's largest exponent) kept within E8M0's [-127, 127], each element divided
+  by 2**shared_exp and rounded to the nearest E2M1 value, ties to the even
+  mantissa, magnitudes above 6 saturating to 6; an all-zero block gets the
+  smallest scale.  h and the gated activation are quantized from their bf16
+  values (the same intermediates as the bf16 path).
 """
 
 from __future__ import annotations
@@ -97,6 +105,39 @@ def dequant_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     vals[:, 0::2] = table[codes & 0x0F]
     vals[:, 1::2] = table[codes >> 4]
     return vals * np.repeat(decode_e8m0(scales), 32, axis=1)
+
+
+E2M1_MAGS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def quantize_mxfp4(v: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """fp64 [..., K] (K a multiple of 32) -> E2M1 codes [..., K] (one per
+    element, sign in bit 3) and E8M0 scale bytes [..., K/32], by the conversion
+    of OCP Microscaling Formats v1.0, section 6.3 (see the module notes)."""
+    v = np.asarray(v, dtype=F64)
+    blocks = v.reshape(v.shape[:-1] + (v.shape[-1] // 32, 32))
+    amax = np.max(np.abs(blocks), axis=-1)
+    _, e = np.frexp(amax)  # amax = m * 2**e, m in [0.5, 1): floor(log2(amax)) = e - 1
+    shared = np.where(amax > 0, e - 1 - 2, -127)
+    shared = np.clip(shared, -127, 127)
+    x = blocks / np.ldexp(1.0, shared)[..., None]
+    a = np.abs(x)
+    # Nearest E2M1 magnitude, ties to the even mantissa (even index), saturating.
+    idx = np.searchsorted(E2M1_MAGS, a, side="right") - 1  # largest magnitude <= a
+    idx = np.clip(idx, 0, 7)
+    lo = E2M1_MAGS[idx]
+    hi = E2M1_MAGS[np.minimum(idx + 1, 7)]
+    up = (a - lo > hi - a) | ((a - lo == hi - a) & (idx % 2 == 1))
+    q = np.where((idx < 7) & up, idx + 1, idx)
+    codes = (q | np.where(x < 0, 8, 0)).astype(np.uint8)
+    return codes.reshape(v.shape), (shared + 127).astype(np.uint8)
+
+
+def fake_quant_mxfp4(v: np.ndarray) -> np.ndarray:
+    """The values an MXFP4 quantization of v (along the last axis) stands for."""
+    codes, scales = quantize_mxfp4(v)
+    k = codes.shape[-1]
+    return decode_e2m1(codes) * np.repeat(decode_e8m0(scales), 32, axis=-1).reshape(codes.shape[:-1] + (k,))
 
 
 def rms_norm(v: np.ndarray, weight: Optional[np.ndarray], eps: float) -> np.ndarray:
@@ -265,7 +306,7 @@ def silu(z: np.ndarray) -> np.ndarray:
 
 
 def experts(h: np.ndarray, ids: np.ndarray, weights: np.ndarray, w13, w13_scale, w2, w2_scale,
-            post_norm_w: np.ndarray, norm_eps: float, want_routes: bool = False):
+            post_norm_w: np.ndarray, norm_eps: float, want_routes: bool = False, act_quant: bool = False):
     """Per-route MXFP4 experts, per-route RMSNorm over P, weighted sum over routes.
 
     For route (t, j) with e = ids[t, j]:
@@ -279,10 +320,14 @@ def experts(h: np.ndarray, ids: np.ndarray, weights: np.ndarray, w13, w13_scale,
     are applied after the per-route norm ([muse_moe_runner]
     MuseSparkAiterExperts.apply and MuseSparkTopKWeightAndReduce.apply:
     norm, then multiply by the route weight, then sum over k, then cast).
+    With act_quant (the W4A4 variant) the expert GEMMs take h and act as their
+    MXFP4 quantizations (quantize_mxfp4, blocks of 32 along P and I).
     Returns moe_out (bf16 bits [b, P]) and, with want_routes, the per-route
     act [b, k, I] (bf16 bits) and y [b, k, P] (fp64)."""
     b, k = ids.shape
     hf = bf16_to_f64(h)
+    if act_quant:
+        hf = fake_quant_mxfp4(hf)
     P = hf.shape[1]
     I = w2.shape[2] * 2
     act = np.zeros((b, k, I), dtype=np.uint16)
@@ -294,7 +339,8 @@ def experts(h: np.ndarray, ids: np.ndarray, weights: np.ndarray, w13, w13_scale,
         rows = hf[sel[:, 0]]  # [n, P]
         gu = rows @ W13.T  # [n, 2I]
         a = round_bf16(silu(gu[:, :I]) * gu[:, I:])
-        yy = bf16_to_f64(a) @ W2.T  # [n, P]
+        af = bf16_to_f64(a)
+        yy = (fake_quant_mxfp4(af) if act_quant else af) @ W2.T  # [n, P]
         act[sel[:, 0], sel[:, 1]] = a
         y[sel[:, 0], sel[:, 1]] = yy
     yn = rms_norm(y, post_norm_w, norm_eps)
@@ -337,14 +383,15 @@ class BlockResult:
     y: Optional[np.ndarray] = None
 
 
-def block(inp, want_routes: bool = False) -> BlockResult:
+def block(inp, want_routes: bool = False, act_quant: bool = False) -> BlockResult:
     """The whole block on a synth.BlockInputs: routing and pooler (independent,
-    [providers] RoutedMoE.run), experts and tail, unpooler, boundary."""
+    [providers] RoutedMoE.run), experts and tail, unpooler, boundary
+    (act_quant: the W4A4 experts)."""
     d = inp.dims
     r = route(inp)
     h = pool(inp.x, inp.pool_w, inp.pre_norm_w, d.norm_eps)
     ex = experts(h, r.ids, r.weights, inp.w13, inp.w13_scale, inp.w2, inp.w2_scale,
-                 inp.post_norm_w, d.norm_eps, want_routes=want_routes)
+                 inp.post_norm_w, d.norm_eps, want_routes=want_routes, act_quant=act_quant)
     moe_out, act, y = ex if want_routes else (ex, None, None)
     u = unpool(moe_out, inp.unpool_w)
     s_new, x_next = boundary(u, inp.stream, inp.gate, inp.ffn_norm_w, inp.next_norm_w, d.norm_eps)
