@@ -71,7 +71,7 @@ def stored_traffic():
         return None
 
 
-def cpu_baseline(blk, seconds: float) -> dict:
+def cpu_baseline(blk, seconds: float, act_quant: bool = False) -> dict:
     import numpy as np  # noqa: F401
 
     import oracle
@@ -85,7 +85,7 @@ def cpu_baseline(blk, seconds: float) -> dict:
     n = 0
     t0 = time.perf_counter()
     while True:
-        oracle.block(blk)
+        oracle.block(blk, act_quant=act_quant)
         n += 1
         if time.perf_counter() - t0 >= seconds:
             break
@@ -112,7 +112,7 @@ def sweep(args) -> int:
     torch.cuda.set_device(0)
 
     def prepare(blocks):
-        dims = rel.make_dims(**dims_kwargs(blocks[0].dims))
+        dims = rel.make_dims(**dims_kwargs(blocks[0].dims), act_quant=int(args.act_quant))
         tensors = [upload_weights(b, dev) for b in blocks]
         weights = [rel.make_weights(**t) for t in tensors]
         if args.layout == "packed":
@@ -149,7 +149,7 @@ def sweep(args) -> int:
                 "rows_per_s": round(d.rows * blocks_per_step / (us * 1e-6), 1),
                 "algorithmic_bytes_per_step": int(b_alg), "achieved_GBps": round(gbs, 1),
                 "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4), "active_experts": actives,
-                "expert_layout": args.layout}
+                "expert_layout": args.layout, "act_quant": int(args.act_quant)}
         print(json.dumps(line), flush=True)
         print(f"[sweep] {case}: {us:.1f} us/step, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)",
               file=sys.stderr, flush=True)
@@ -217,11 +217,16 @@ def main() -> int:
     ap.add_argument("--layout", choices=("packed", "caller"), default="packed",
                     help="expert weights streamed from mb_pack_experts' layout (prepared once per "
                          "weight set, outside the timed region) or from the caller's layout")
+    ap.add_argument("--act-quant", action="store_true",
+                    help="the W4A4 variant: the experts' activations quantized to MXFP4 (needs the "
+                         "packed layout); not the headline line")
     ap.add_argument("--print-source-hash", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the c1 metric, time every workload (c0, c2, c3 buckets, c4 "
                          "stack) and print one JSON line per case")
     args = ap.parse_args()
+    if args.act_quant and args.layout != "packed":
+        ap.error("--act-quant needs --layout packed")
     if args.print_source_hash:
         print(kernel_source_hash())
         return 0
@@ -251,7 +256,7 @@ def main() -> int:
     wt0, x, stream = upload(blocks[0], dev)
     tensors = [wt0] + [upload_weights(b, dev) for b in blocks[1:]]
     weights = [rel.make_weights(**t) for t in tensors]
-    dims = rel.make_dims(**dims_kwargs(d))
+    dims = rel.make_dims(**dims_kwargs(d), act_quant=int(args.act_quant))
     if args.layout == "packed":
         # Load-time preparation: the experts also in the streaming layout.
         for t, w in zip(tensors, weights):
@@ -314,7 +319,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(blocks[0], args.cpu_seconds)
+        cpu = cpu_baseline(blocks[0], args.cpu_seconds, args.act_quant)
 
     out = {
         "metric": METRIC,
@@ -333,6 +338,7 @@ def main() -> int:
             "workload": "decode verify step b=16: H=4096 P=2048 I=1024 E=64 top_k=4 sigmoid, "
                         "MXFP4 experts, bf16 pooler/unpooler, fp32 router and stream",
             "expert_layout": args.layout,
+            "activations": "mxfp4 (W4A4)" if args.act_quant else "bf16",
             "rows": d.rows, "weight_sets": S, "active_experts": actives,
             "us_per_block": round(us_block, 3),
             "algorithmic_bytes_per_block": int(b_alg),
@@ -344,7 +350,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": stored_traffic(),
+            "traffic": None if args.act_quant else stored_traffic(),
         },
         "cpu_baseline": cpu,
     }

@@ -79,7 +79,18 @@ enum {
  * route_scale, router_multiplier and division_eps follow [muse_moe_runner]
  * MuseSpark1xRouter: an absent multiplier is 1.0f and an absent eps is 0.0f
  * (both leave the fp32 result unchanged).  norm_eps is the epsilon of every
- * RMSNorm in the block. */
+ * RMSNorm in the block.
+ * act_quant 0: the experts multiply bf16 activations (h, act) by the
+ * dequantized MXFP4 weights.  act_quant 1 (the W4A4 variant, [providers]
+ * MoEProvider: the FP4 x FP4 expert recipe): h and act are each quantized to
+ * MXFP4 along the contraction, per block of 32 consecutive elements, by the
+ * OCP Microscaling v1.0 conversion (shared scale 2^(floor(log2 amax) - 2) as
+ * an E8M0 byte, clamped to [2^-127, 2^127], 1 for an all-zero block;
+ * elements scaled and rounded to the nearest E2M1 value, ties to the even
+ * code, magnitudes above 6 saturating to 6), and each contraction runs on
+ * fp4 x fp4 products.  act_quant 1 runs in the block kernel only: it needs
+ * w->experts_packed and sizes the block kernel takes (experts <= 64, hidden
+ * <= 8192, route tables within its LDS), else MB_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t rows, hidden, pooled, inter, experts, top_k;
   int32_t scoring;
@@ -87,6 +98,7 @@ typedef struct {
   float router_multiplier;
   float division_eps;
   float norm_eps;
+  int32_t act_quant;
 } mb_dims;
 
 /* The block's weights, all device pointers, in the layouts the pages fix:
@@ -149,6 +161,9 @@ typedef struct {
                           100 MHz real-time counter at its phase boundaries
                           into row w (slots 0..21; the per-step path leaves it
                           untouched) */
+  uint16_t *act;       /* bf16 [b * k, I]: the experts' gated activations
+                          act = bf16(silu(gu[0:I]) * gu[I:2I]) (mb_experts),
+                          row i for route route_list[i] (grouped by expert) */
 } mb_block_taps;
 
 /* Bytes of workspace every entry point needs for these dims (the same size

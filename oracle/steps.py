@@ -328,29 +328,40 @@ def experts(h: np.ndarray, ids: np.ndarray, weights: np.ndarray, w13, w13_scale,
     hf = bf16_to_f64(h)
     if act_quant:
         hf = fake_quant_mxfp4(hf)
-    P = hf.shape[1]
     I = w2.shape[2] * 2
     act = np.zeros((b, k, I), dtype=np.uint16)
-    y = np.zeros((b, k, P), dtype=F64)
     for e in sorted(set(int(v) for v in np.asarray(ids).reshape(-1))):
         sel = np.argwhere(np.asarray(ids) == e)  # (t, j) pairs
         W13 = dequant_mxfp4(w13[e], w13_scale[e])  # [2I, P]
+        gu = hf[sel[:, 0]] @ W13.T  # [n, 2I]
+        act[sel[:, 0], sel[:, 1]] = round_bf16(silu(gu[:, :I]) * gu[:, I:])
+    moe_out, y = experts_down(act, ids, weights, w2, w2_scale, post_norm_w, norm_eps, act_quant)
+    if want_routes:
+        return moe_out, act, y
+    return moe_out
+
+
+def experts_down(act: np.ndarray, ids: np.ndarray, weights: np.ndarray, w2, w2_scale,
+                 post_norm_w: np.ndarray, norm_eps: float, act_quant: bool = False):
+    """The second half of `experts`, from the per-route act (bf16 bits
+    [b, k, I]): y = dec(w2[e]) @ act (act as its MXFP4 quantization with
+    act_quant), the per-route RMSNorm over P, the route weight, the sum over
+    the k slots in slot order and the bf16 cast ([muse_moe_runner]
+    MuseSparkAiterExperts.apply, MuseSparkTopKWeightAndReduce.apply).
+    Returns (moe_out bf16 bits [b, P], y fp64 [b, k, P])."""
+    b, k = ids.shape
+    P = w2.shape[1]
+    y = np.zeros((b, k, P), dtype=F64)
+    for e in sorted(set(int(v) for v in np.asarray(ids).reshape(-1))):
+        sel = np.argwhere(np.asarray(ids) == e)
         W2 = dequant_mxfp4(w2[e], w2_scale[e])  # [P, I]
-        rows = hf[sel[:, 0]]  # [n, P]
-        gu = rows @ W13.T  # [n, 2I]
-        a = round_bf16(silu(gu[:, :I]) * gu[:, I:])
-        af = bf16_to_f64(a)
-        yy = (fake_quant_mxfp4(af) if act_quant else af) @ W2.T  # [n, P]
-        act[sel[:, 0], sel[:, 1]] = a
-        y[sel[:, 0], sel[:, 1]] = yy
+        af = bf16_to_f64(act[sel[:, 0], sel[:, 1]])
+        y[sel[:, 0], sel[:, 1]] = (fake_quant_mxfp4(af) if act_quant else af) @ W2.T
     yn = rms_norm(y, post_norm_w, norm_eps)
     acc = np.zeros((b, P), dtype=F64)
     for j in range(k):
         acc = acc + np.asarray(weights, dtype=F32).astype(F64)[:, j:j + 1] * yn[:, j]
-    moe_out = round_bf16(acc)
-    if want_routes:
-        return moe_out, act, y
-    return moe_out
+    return round_bf16(acc), y
 
 
 def unpool(moe_out: np.ndarray, unpool_w: np.ndarray) -> np.ndarray:

@@ -68,6 +68,7 @@ int check_dims(const mb_dims *d) {
     return MB_ERR_DIMS;
   if (d->top_k > d->experts) return MB_ERR_DIMS;
   if (d->scoring != MB_SCORING_SIGMOID && d->scoring != MB_SCORING_SOFTMAX) return MB_ERR_DIMS;
+  if (d->act_quant != 0 && d->act_quant != 1) return MB_ERR_DIMS;
   if (!(d->norm_eps >= 0.0f) || !isfinite(d->norm_eps) || !isfinite(d->route_scale) ||
       !isfinite(d->router_multiplier) || !isfinite(d->division_eps))
     return MB_ERR_DIMS;
@@ -161,9 +162,9 @@ int run_pool(const mb_dims &d, const uint16_t *x, const mb_weights *w, uint16_t 
 
 int run_experts(const mb_dims &d, const uint16_t *h, const float *wts, const int32_t *offset,
                 const int32_t *route_list, const int32_t *active, const int32_t *n_active,
-                const mb_weights *w, uint16_t *moe_out, void *ws, hipStream_t s) {
+                const mb_weights *w, uint16_t *moe_out, void *ws, hipStream_t s, uint16_t *act_out = nullptr) {
   const Layout L = layout_of(d);
-  uint16_t *act = at<uint16_t>(ws, L.act);
+  uint16_t *act = act_out ? act_out : at<uint16_t>(ws, L.act);
   float *y = at<float>(ws, L.y), *ssq = at<float>(ws, L.ssq);
   MB_HIP(launch_experts_up(d, h, offset, route_list, active, n_active, w->w13, w->w13_scale, act, s));
   MB_HIP(launch_experts_down(d, act, offset, route_list, active, n_active, w->w2, w->w2_scale, y,
@@ -205,6 +206,7 @@ BlockParams base_params(const mb_dims &d, const mb_weights *w, void *ws) {
   p.div_eps = d.division_eps;
   p.route_scale = d.route_scale;
   p.norm_eps = d.norm_eps;
+  p.w4a4 = d.act_quant;
   if (w) {
     p.router_w = w->router_w;
     p.bias = w->expert_bias;
@@ -275,13 +277,16 @@ struct Steps {
 // kernels instead.
 int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   *used = false;
-  if (p.E > kBlockMaxExperts || p.H > 1024 * kBoundGroups) return MB_OK;
+  // MXFP4 activations exist in the block kernel's streaming path only.
+  const int none = (st.experts && p.w4a4) ? MB_ERR_UNSUPPORTED : MB_OK;
+  if (st.experts && p.w4a4 && !p.xp) return MB_ERR_UNSUPPORTED;
+  if (p.E > kBlockMaxExperts || p.H > 1024 * kBoundGroups) return none;
   const size_t route_bytes = route_lds_bytes(p.b, p.k, p.E);
   const size_t lds = route_bytes + kBlockScratchBytes;
-  if (lds > 64 * 1024) return MB_OK;
+  if (lds > 64 * 1024) return none;
   const int occ = block_max_groups_per_cu(lds);
   const int cus = device_cus();
-  if (occ < 1 || cus < 1) return MB_OK;
+  if (occ < 1 || cus < 1) return none;
   int grid = cus * (occ < kBlockGroupsPerCu ? occ : kBlockGroupsPerCu);
   if (grid > kMaxGrid) grid = kMaxGrid;
   p.lds_route_bytes = (int)route_bytes;
@@ -471,7 +476,7 @@ int mb_moe_block(const mb_dims *dims, const uint16_t *x, const mb_weights *w, fl
   if (taps) {
     tp = *taps;
     MB_TRY(maybe({tp.logits, tp.topk_ids, tp.topk_w, tp.count, tp.offset, tp.route_list,
-                  tp.active, tp.n_active, tp.h, tp.moe_out, tp.u, tp.timeline}));
+                  tp.active, tp.n_active, tp.h, tp.moe_out, tp.u, tp.timeline, tp.act}));
   }
   MB_TRY(check_ws(dims, workspace, workspace_bytes));
   const mb_dims &d = *dims;
@@ -509,13 +514,14 @@ int mb_moe_block(const mb_dims *dims, const uint16_t *x, const mb_weights *w, fl
   p.stream = stream;
   p.x_next = x_next;
   p.timeline = tp.timeline;
+  if (tp.act) p.act = tp.act;
   bool used = false;
   MB_TRY(run_fused(p, st, s, &used));
   if (used) return MB_OK;
   if (!has_plain_experts(w)) return MB_ERR_UNSUPPORTED;  // the per-step kernels read the caller's layout
   MB_TRY(run_route(d, x, w, logits, 0, ids, wts, count, offset, route_list, active, n_active, s));
   MB_TRY(run_pool(d, x, w, h, ws, s));
-  MB_TRY(run_experts(d, h, wts, offset, route_list, active, n_active, w, moe_out, ws, s));
+  MB_TRY(run_experts(d, h, wts, offset, route_list, active, n_active, w, moe_out, ws, s, tp.act));
   return run_unpool_boundary(d, moe_out, w, stream, x_next, u, ws, s);
 }
 

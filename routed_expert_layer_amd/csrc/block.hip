@@ -1279,10 +1279,180 @@ __device__ __forceinline__ void mx_pair_all(const MxTiles &T, int nch, int pr, i
   __syncthreads();
 }
 
+// ---- MXFP4 activations (the W4A4 variant), streaming layout only
+
+// Quantized staging of one segment: pass rows 0 .. pr - 1 (row_off(m)), bf16
+// elements of chunks seg0 .. seg0 + segn (segc >= segn chunks, a multiple of
+// 4), read coherently in 16-byte pieces as the bf16 staging does, quantized
+// per 32-element block (four consecutive lanes hold a block: their amax by
+// two butterfly steps; then the block's E8M0 byte and each element's E2M1
+// code by mx_scale_byte / e2m1_code) and written to `stage` rows of srowq
+// bytes: chunk c's block g's 16 code bytes at (4c + g) * 16, its scale byte
+// at segc * 64 + g * segc + c (so a lane's scales of four chunks form one
+// word).  Rows past vrows are left as they are (their columns are not stored).
+template <typename RowOff>
+__device__ __forceinline__ void mxq_stage(rsrc_t ra, RowOff row_off, int pr, int vrows, int seg0, int segn,
+                                          int segc, int srowq, unsigned char *stage) {
+  const int ppr = segc * 16;  // bf16 pieces (8 elements) per row
+#pragma unroll
+  for (int n0 = 0; n0 < kSegLoads; n0 += kSegLoads / 2) {
+    if (n0 > 0 && (kThreads * n0) / ppr >= vrows) continue;
+    u32x4_t v[kSegLoads / 2];
+#pragma unroll
+    for (int n = 0; n < kSegLoads / 2; ++n) {
+      const int q = (int)tid() + kThreads * (n0 + n);
+      const int m = q / ppr, pc = q % ppr;
+      const uint32_t ro = m < pr ? row_off(m) : kOob;
+      v[n] = ld_co16(ra, (ro != kOob && pc < segn * 16) ? ro + (uint32_t)(seg0 * 256 + pc * 16) : kOob);
+    }
+#pragma unroll
+    for (int n = 0; n < kSegLoads / 2; ++n) {
+      const int q = (int)tid() + kThreads * (n0 + n);
+      const int m = q / ppr, pc = q % ppr;
+      float f[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_bits_to_f32(v[n][i] & 0xFFFFu);
+        f[2 * i + 1] = bf16_bits_to_f32(v[n][i] >> 16);
+      }
+      float am = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(f[i]));
+      am = fmaxf(am, __shfl_xor(am, 1, MB_WAVE));
+      am = fmaxf(am, __shfl_xor(am, 2, MB_WAVE));
+      const uint32_t sb = mx_scale_byte(am);
+      const int se = (int)sb - 127;
+      uint32_t w = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w |= e2m1_code(ldexpf(f[i], -se)) << (4 * i);
+      if (m < pr) {
+        const int c = pc / 16, gq = (pc % 16) / 4, pw = pc % 4;
+        *reinterpret_cast<uint32_t *>(stage + m * srowq + (4 * c + gq) * 16 + 4 * pw) = w;
+        if (pw == 0) stage[m * srowq + segc * 64 + gq * segc + c] = (unsigned char)sb;
+      }
+    }
+  }
+}
+
+// One scaled MFMA per 128-element chunk of each tile, the chunk's byte r of
+// the lanes' scale words selecting its scales.
+__device__ __forceinline__ f32x4_t mfma_fp4_r(int r, u32x4_t a, u32x4_t b, f32x4_t c, uint32_t sa, uint32_t sb) {
+  switch (r & 3) {
+    case 0: return mfma_fp4<0>(a, b, c, sa, sb);
+    case 1: return mfma_fp4<1>(a, b, c, sa, sb);
+    case 2: return mfma_fp4<2>(a, b, c, sa, sb);
+    default: return mfma_fp4<3>(a, b, c, sa, sb);
+  }
+}
+
+// mx_pair with MXFP4 activations: the same weight ring, scales, waits,
+// passes and results' layout, but the activations staged as MXFP4
+// (mxq_stage) and each chunk of a tile one scaled fp4 x fp4 MFMA with the
+// weights' codes as loaded (no conversion to bf16).
+template <int kRing, typename Wait, typename RowOff>
+__device__ __forceinline__ void mxq_pair(const MxTiles &T, int nch, int pr, int vrows, rsrc_t ra, RowOff row_off,
+                                         unsigned char *stage, f32x4_t (&d0)[2], f32x4_t (&d1)[2], int slot,
+                                         Wait wait) {
+  static_assert(kRing == 4, "one scale word covers the four chunks of a round");
+  const int lane = tid() % MB_WAVE, g = lane >> 4;
+  const rsrc_t rw = T.rw, rs = T.rs;
+  const uint32_t o0 = T.o0, o1 = T.o1, so0 = T.so0, so1 = T.so1, ws = T.wstride, ss = T.sstride;
+  u32x4_t W0[kRing], W1[kRing];
+#pragma unroll
+  for (int r = 0; r < kRing; ++r) {
+    const bool ok = r < nch;
+    W0[r] = ld_b128(rw, ok ? o0 + ws * r : kOob);
+    W1[r] = ld_b128(rw, ok ? o1 + ws * r : kOob);
+  }
+  uint32_t S0 = ld_b32(rs, so0), S1 = ld_b32(rs, so1);
+  wait();
+  const int seg = kStageChunkRows / pr, nb = pr > 16 ? 2 : 1;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    d0[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    d1[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const int rrow = lane & (pr == 8 ? 7 : 15);
+  for (int seg0 = 0; seg0 < nch; seg0 += seg) {
+    const int segn = min(seg, nch - seg0), segc = ((segn + 3) / 4) * 4, srowq = segc * 68 + 16;
+    mxq_stage(ra, row_off, pr, vrows, seg0, segn, segc, srowq, stage);
+    __syncthreads();
+    for (int c0 = seg0; c0 < seg0 + segn; c0 += kRing) {
+      set_slot_priority(slot);
+      const uint32_t N0 = ld_b32(rs, c0 + kRing < nch ? so0 + ss * (c0 + kRing) : kOob);
+      const uint32_t N1 = ld_b32(rs, c0 + kRing < nch ? so1 + ss * (c0 + kRing) : kOob);
+      uint32_t sbw[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        sbw[b] = b < nb ? *reinterpret_cast<const uint32_t *>(stage + (rrow + 16 * b) * srowq + segc * 64 +
+                                                               g * segc + (c0 - seg0))
+                        : 0u;
+#pragma unroll
+      for (int r = 0; r < kRing; ++r) {
+        const int cr = c0 + r - seg0;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          if (b >= nb) break;
+          const u32x4_t B = *reinterpret_cast<const u32x4_t *>(stage + (rrow + 16 * b) * srowq + (4 * cr + g) * 16);
+          d0[b] = mfma_fp4_r(r, W0[r], B, d0[b], S0, sbw[b]);
+          d1[b] = mfma_fp4_r(r, W1[r], B, d1[b], S1, sbw[b]);
+        }
+        const int cn = c0 + kRing + r;
+        const bool ok = cn < nch;
+        W0[r] = ld_b128(rw, ok ? o0 + ws * cn : kOob);
+        W1[r] = ld_b128(rw, ok ? o1 + ws * cn : kOob);
+      }
+      S0 = N0;
+      S1 = N1;
+    }
+    __syncthreads();
+  }
+}
+
+// mx_pair_all with MXFP4 activations (as mxq_pair is to mx_pair).
+template <int kAll, typename Wait, typename RowOff>
+__device__ __forceinline__ void mxq_pair_all(const MxTiles &T, int nch, int pr, int vrows, rsrc_t ra, RowOff row_off,
+                                             unsigned char *stage, f32x4_t (&d0)[2], f32x4_t (&d1)[2], Wait wait) {
+  static_assert(kAll % 4 == 0, "whole scale words");
+  const int lane = tid() % MB_WAVE, g = lane >> 4;
+  const rsrc_t rw = T.rw, rs = T.rs;
+  const uint32_t o0 = T.o0, o1 = T.o1, so0 = T.so0, so1 = T.so1, ws = T.wstride, ss = T.sstride;
+  u32x4_t W0[kAll], W1[kAll];
+  uint32_t S0[kAll / 4], S1[kAll / 4];
+#pragma unroll
+  for (int r = 0; r < kAll; ++r) {
+    const bool ok = r < nch;
+    W0[r] = ld_b128(rw, ok ? o0 + ws * r : kOob);
+    W1[r] = ld_b128(rw, ok ? o1 + ws * r : kOob);
+  }
+#pragma unroll
+  for (int q = 0; q < kAll / 4; ++q) {
+    S0[q] = ld_b32(rs, 4 * q < nch ? so0 + ss * (4 * q) : kOob);
+    S1[q] = ld_b32(rs, 4 * q < nch ? so1 + ss * (4 * q) : kOob);
+  }
+  wait();
+  constexpr int segc = kAll, srowq = segc * 68 + 16;
+  d0[0] = d1[0] = d0[1] = d1[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  mxq_stage(ra, row_off, pr, vrows, 0, nch, segc, srowq, stage);
+  __syncthreads();
+  const int rrow = lane & (pr == 8 ? 7 : 15);
+  uint32_t sbw[kAll / 4];
+#pragma unroll
+  for (int q = 0; q < kAll / 4; ++q)
+    sbw[q] = *reinterpret_cast<const uint32_t *>(stage + rrow * srowq + segc * 64 + g * segc + 4 * q);
+#pragma unroll
+  for (int r = 0; r < kAll; ++r) {
+    const u32x4_t B = *reinterpret_cast<const u32x4_t *>(stage + rrow * srowq + (4 * r + g) * 16);
+    d0[0] = mfma_fp4_r(r, W0[r], B, d0[0], S0[r / 4], sbw[r / 4]);
+    d1[0] = mfma_fp4_r(r, W1[r], B, d1[0], S1[r / 4], sbw[r / 4]);
+  }
+  __syncthreads();
+}
+
 // Up unit: w13 and the gated activation for (active expert, 16 act columns):
 // gate rows i0..i0+15 and up rows I+i0..I+i0+15 of the expert, over P, for
 // the expert's routes in passes of pass_rows.
-template <bool kPacked>
+template <bool kPacked, bool kQ>
 __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, const RouteLds &R, int unit,
                                         bool &h_ready, unsigned char *stage) {
   const int lane = tid() % MB_WAVE, g = lane >> 4, r16 = lane & 15;
@@ -1301,15 +1471,18 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
   const int pr = pass_rows(nrows);
   for (int m0 = 0; m0 < nrows; m0 += pr) {
     f32x4_t gs[2], us[2];
-    mx_pair<kRingUp, kPacked>(
-        T, nch, pr, min(pr, nrows - m0), rh,
-        [&](int m) { return m0 + m < nrows ? (uint32_t)((R.rl[row0 + m0 + m] / p.k) * P) * 2u : kOob; }, stage,
-        gs, us, (int)blockIdx.x / p.cus, [&]() {
-          if (!h_ready) {
-            wave_wait_step(d, p.pre_norm_w ? kCtrPrenorm : kCtrPool, p.h_producers);
-            h_ready = true;
-          }
-        });
+    auto row_off = [&](int m) { return m0 + m < nrows ? (uint32_t)((R.rl[row0 + m0 + m] / p.k) * P) * 2u : kOob; };
+    auto wait = [&]() {
+      if (!h_ready) {
+        wave_wait_step(d, p.pre_norm_w ? kCtrPrenorm : kCtrPool, p.h_producers);
+        h_ready = true;
+      }
+    };
+    if constexpr (kQ)
+      mxq_pair<kRingUp>(T, nch, pr, min(pr, nrows - m0), rh, row_off, stage, gs, us, (int)blockIdx.x / p.cus, wait);
+    else
+      mx_pair<kRingUp, kPacked>(T, nch, pr, min(pr, nrows - m0), rh, row_off, stage, gs, us, (int)blockIdx.x / p.cus,
+                                wait);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int m = m0 + 16 * b + r16;
@@ -1330,7 +1503,7 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
 
 // Down unit: w2 for (active expert, 32 output features): y in route order and
 // the route's sum of squares over these 32 features.
-template <bool kPacked>
+template <bool kPacked, bool kQ>
 __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, const RouteLds &R, int unit,
                                           unsigned char *stage) {
   const int lane = tid() % MB_WAVE, g = lane >> 4, r16 = lane & 15;
@@ -1359,7 +1532,13 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
         ready = true;
       }
     };
-    if (kPacked && nch <= kDownAll && pr <= 16)
+    if constexpr (kQ) {
+      if (nch <= kDownAll && pr <= 16)
+        mxq_pair_all<kDownAll>(T, nch, pr, min(pr, nrows - m0), ract, row_off, stage, y0, y1, wait);
+      else
+        mxq_pair<kRingDown>(T, nch, pr, min(pr, nrows - m0), ract, row_off, stage, y0, y1, (int)blockIdx.x / p.cus,
+                            wait);
+    } else if (kPacked && nch <= kDownAll && pr <= 16)
       mx_pair_all<kDownAll>(T, nch, pr, min(pr, nrows - m0), ract, row_off, stage, y0, y1, wait);
     else
       mx_pair<kRingDown, kPacked>(T, nch, pr, min(pr, nrows - m0), ract, row_off, stage, y0, y1, (int)blockIdx.x / p.cus,
@@ -1697,15 +1876,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // a workgroup always have units, of one expert, in the same rounds: the
     // units' workgroup barriers and signals rely on it.
     const int gw = blockIdx.x * kWaves + uniform(tid() / MB_WAVE);
-    // (The expert layout is a template argument: each has its own registers.)
-    if (p.xp) {
-      for (int u = gw; u < nU; u += GW) up_unit<true>(p, d, R, u, h_ready, stage);
+    // (The expert layout and the activation format are template arguments:
+    // each has its own registers.)
+    if (p.xp && p.w4a4) {
+      for (int u = gw; u < nU; u += GW) up_unit<true, true>(p, d, R, u, h_ready, stage);
       stamp(p, 20);
-      for (int u = gw; u < nD; u += GW) down_unit<true>(p, d, R, u, stage);
+      for (int u = gw; u < nD; u += GW) down_unit<true, true>(p, d, R, u, stage);
+    } else if (p.xp) {
+      for (int u = gw; u < nU; u += GW) up_unit<true, false>(p, d, R, u, h_ready, stage);
+      stamp(p, 20);
+      for (int u = gw; u < nD; u += GW) down_unit<true, false>(p, d, R, u, stage);
     } else {
-      for (int u = gw; u < nU; u += GW) up_unit<false>(p, d, R, u, h_ready, stage);
+      for (int u = gw; u < nU; u += GW) up_unit<false, false>(p, d, R, u, h_ready, stage);
       stamp(p, 20);
-      for (int u = gw; u < nD; u += GW) down_unit<false>(p, d, R, u, stage);
+      for (int u = gw; u < nD; u += GW) down_unit<false, false>(p, d, R, u, stage);
     }
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();

@@ -119,6 +119,7 @@ struct BlockParams {
   int has_up, needs_routing, routing_out, route_given, logits_in;
   int unpool_wide;  // unpooler in 64-feature tiles (many rows)
   int router_multi; // router tasks of kRouterExperts experts (many rows)
+  int w4a4;         // MXFP4 activations into the experts (streaming layout)
   int cus;          // compute units (the grid holds grid / cus workgroups per CU)
   int lds_route_bytes;
   // inputs

@@ -64,6 +64,37 @@ __device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// D += (A with its lanes' E8M0 scales) x (B with theirs), A and B MXFP4: the
+// 16x16x128 scaled MFMA with E2M1 operands.  A lane holds 32 codes (16 bytes,
+// element k at nibble k % 8 of word k / 8, low nibble first) of row / column
+// lane % 16, K block lane / 16; byte OP of sa / sb is its block's scale.  D is
+// laid out as for the 16x16x32 bf16 MFMA.
+template <int OP>
+__device__ __forceinline__ f32x4_t mfma_fp4(u32x4_t a, u32x4_t b, f32x4_t c, uint32_t sa, uint32_t sb) {
+  typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+  const i32x8_t A = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  const i32x8_t B = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 4, OP, (int)sa, OP, (int)sb);
+}
+
+// E2M1 code of x (already divided by its block scale): the nearest of 0, 0.5,
+// 1, 1.5, 2, 3, 4, 6, ties to the even mantissa, saturating at 6; sign in
+// bit 3 (OCP Microscaling Formats v1.0: E2M1, and section 6.3's rounding).
+__device__ __forceinline__ uint32_t e2m1_code(float x) {
+  const float a = fabsf(x);
+  const uint32_t m = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                   : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return m | (x < 0.f ? 8u : 0u);
+}
+
+// E8M0 byte of a block's shared exponent: floor(log2(amax)) - 2, within
+// [-127, 127] (amax 0: the smallest, 2^-127).  amax is a normal fp32 value or 0.
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
+  const int e = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127 : -127;
+  const int se = min(127, max(-127, e - 2));
+  return (uint32_t)(se + 127);
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }

@@ -70,6 +70,8 @@ def test_workspace_bytes_ok_and_monotone():
     (dict(inter=1000), MB_ERR_UNSUPPORTED),
     (dict(hidden=4100), MB_ERR_UNSUPPORTED),
     (dict(rows=1024, experts=512), MB_ERR_UNSUPPORTED),
+    (dict(act_quant=2), MB_ERR_DIMS),
+    (dict(act_quant=-1), MB_ERR_DIMS),
 ])
 def test_bad_dims_rejected(over, code):
     assert status_of_ws(c1_dims(**over))[0] == code
@@ -190,3 +192,15 @@ def test_packed_experts_stand_in_for_the_caller_layout():
     w = full_weights(w13=None)
     assert L.mb_moe_block(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE, None, FAKE, 1 << 40,
                           None) == MB_ERR_NULL
+
+
+def test_mxfp4_activations_need_the_streaming_layout():
+    # act_quant 1 runs only in the block kernel's streaming path: without
+    # experts_packed it is refused before any launch.
+    d = c1_dims(act_quant=1)
+    L = rel.lib()
+    w = full_weights()
+    assert L.mb_moe_block(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE, None, FAKE, 1 << 40,
+                          None) == MB_ERR_UNSUPPORTED
+    assert L.mb_experts(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                        ctypes.byref(w), FAKE, FAKE, 1 << 40, None) == MB_ERR_UNSUPPORTED
