@@ -1285,8 +1285,9 @@ __device__ __forceinline__ void mx_pair_all(const MxTiles &T, int nch, int pr, i
 // elements of chunks seg0 .. seg0 + segn (segc >= segn chunks, a multiple of
 // 4), read coherently in 16-byte pieces as the bf16 staging does, quantized
 // per 32-element block (four consecutive lanes hold a block: their amax by
-// two butterfly steps; then the block's E8M0 byte and each element's E2M1
-// code by mx_scale_byte / e2m1_code) and written to `stage` rows of srowq
+// two butterfly steps; then the block's E8M0 byte by mx_scale_byte and the
+// elements' E2M1 codes by the hardware's scaled conversion) and written to
+// `stage` rows of srowq
 // bytes: chunk c's block g's 16 code bytes at (4c + g) * 16, its scale byte
 // at segc * 64 + g * segc + c (so a lane's scales of four chunks form one
 // word).  Rows past vrows are left as they are (their columns are not stored).
@@ -1321,10 +1322,23 @@ __device__ __forceinline__ void mxq_stage(rsrc_t ra, RowOff row_off, int pr, int
       am = fmaxf(am, __shfl_xor(am, 1, MB_WAVE));
       am = fmaxf(am, __shfl_xor(am, 2, MB_WAVE));
       const uint32_t sb = mx_scale_byte(am);
-      const int se = (int)sb - 127;
       uint32_t w = 0;
+      if (sb == 0u && am > 0.f) {
+        // Scale 2^-127 (a block below 2^-124): no normal fp32 divisor.
 #pragma unroll
-      for (int i = 0; i < 8; ++i) w |= e2m1_code(ldexpf(f[i], -se)) << (4 * i);
+        for (int i = 0; i < 8; ++i) w |= e2m1_code(ldexpf(f[i], 127)) << (4 * i);
+      } else {
+        // The hardware conversion divides by the scale and rounds to
+        // nearest even, saturating at 6: the rule above, exactly.  (An
+        // all-zero block converts to zeros with any scale.)  Each writes
+        // two codes into byte i of w.  (The fp32-input form: the compiler
+        // at hand merges the bf16-input form's four calls into one.)
+        const float scl = __uint_as_float((sb > 0u ? sb : 1u) << 23);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[0], f[1], scl, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[2], f[3], scl, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[4], f[5], scl, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[6], f[7], scl, 3);
+      }
       if (m < pr) {
         const int c = pc / 16, gq = (pc % 16) / 4, pw = pc % 4;
         *reinterpret_cast<uint32_t *>(stage + m * srowq + (4 * c + gq) * 16 + 4 * pw) = w;
@@ -1775,6 +1789,9 @@ __device__ __forceinline__ const BlockParams &kparams() {
   return *(const BlockParams *)pp;
 }
 
+// kQ: the W4A4 variant (MXFP4 activations into the experts), a kernel of its
+// own so that each keeps its own code layout and registers.
+template <bool kQ>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void block_kernel(BlockParams p_arg) {
   extern __shared__ __align__(16) unsigned char lds[];
   (void)p_arg;  // read through kparams()
@@ -1878,7 +1895,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const int gw = blockIdx.x * kWaves + uniform(tid() / MB_WAVE);
     // (The expert layout and the activation format are template arguments:
     // each has its own registers.)
-    if (p.xp && p.w4a4) {
+    if constexpr (kQ) {
       for (int u = gw; u < nU; u += GW) up_unit<true, true>(p, d, R, u, h_ready, stage);
       stamp(p, 20);
       for (int u = gw; u < nD; u += GW) down_unit<true, true>(p, d, R, u, stage);
@@ -1950,16 +1967,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 // An ordinary launch: the host sizes the grid to what the device holds at
 // once.  Should some workgroups only start after others finished work on
 // another kernel, the waits merely take longer (every one is bounded).
+// The W4A4 kernel is built from this file in a translation unit of its own
+// (block_w4a4.hip): sharing one code object moved the bf16 kernel's code
+// and cost it ~0.6 us per launch.
+#ifndef MB_BLOCK_W4A4
 hipError_t launch_block(const BlockParams &p, int grid, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL(block_kernel, dim3(grid), dim3(kThreads), lds, s, p);
+  if (p.w4a4) return launch_block_w4a4(p, grid, lds, s);
+  hipLaunchKernelGGL(block_kernel<false>, dim3(grid), dim3(kThreads), lds, s, p);
   return hipGetLastError();
 }
 
-int block_max_groups_per_cu(size_t lds) {
+int block_max_groups_per_cu(size_t lds, bool w4a4) {
+  if (w4a4) return block_max_groups_per_cu_w4a4(lds);
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_kernel, kThreads, lds) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_kernel<false>, kThreads, lds) != hipSuccess)
     return 0;
   return n;
 }
+#else
+hipError_t launch_block_w4a4(const BlockParams &p, int grid, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL(block_kernel<true>, dim3(grid), dim3(kThreads), lds, s, p);
+  return hipGetLastError();
+}
+
+int block_max_groups_per_cu_w4a4(size_t lds) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_kernel<true>, kThreads, lds) != hipSuccess)
+    return 0;
+  return n;
+}
+#endif
 
 }  // namespace mb

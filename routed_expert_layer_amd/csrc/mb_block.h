@@ -119,7 +119,6 @@ struct BlockParams {
   int has_up, needs_routing, routing_out, route_given, logits_in;
   int unpool_wide;  // unpooler in 64-feature tiles (many rows)
   int router_multi; // router tasks of kRouterExperts experts (many rows)
-  int w4a4;         // MXFP4 activations into the experts (streaming layout)
   int cus;          // compute units (the grid holds grid / cus workgroups per CU)
   int lds_route_bytes;
   // inputs
@@ -144,6 +143,9 @@ struct BlockParams {
   uint16_t *act, *moe_rep;  // moe_rep: kMoeReplicas copies of [b, P]
   unsigned *pool_cnt, *unpool_cnt, *sync;
   int64_t *timeline;  // optional [grid][kTimelineSlots]
+  // MXFP4 activations into the experts (streaming layout).  Last, so that the
+  // other fields keep their kernel-argument offsets.
+  int w4a4;
 };
 
 // Routing state each workgroup keeps in LDS.
@@ -199,6 +201,8 @@ constexpr size_t kProjScratchBytes = 4 * 4 * 64 * 16 + 64;
 constexpr size_t kBlockScratchBytes = kProjScratchBytes > kStageBytes ? kProjScratchBytes : kStageBytes;
 
 hipError_t launch_block(const BlockParams &p, int grid, size_t lds, hipStream_t s);
-int block_max_groups_per_cu(size_t lds);
+int block_max_groups_per_cu(size_t lds, bool w4a4);
+hipError_t launch_block_w4a4(const BlockParams &p, int grid, size_t lds, hipStream_t s);
+int block_max_groups_per_cu_w4a4(size_t lds);
 
 }  // namespace mb
