@@ -240,7 +240,6 @@ int mb_moe_block(const mb_dims *dims, const uint16_t *x, const mb_weights *w,
                  float *stream, uint16_t *x_next, const mb_block_taps *taps,
                  void *workspace, size_t workspace_bytes, void *stream_handle);
 
-/* A static, human-readable reason for a status code. */
 /* Bytes of the streaming layout of all E experts (for mb_pack_experts). */
 int mb_packed_experts_bytes(const mb_dims *dims, size_t *bytes);
 
@@ -260,6 +259,37 @@ int mb_packed_experts_bytes(const mb_dims *dims, size_t *bytes);
 int mb_pack_experts(const mb_dims *dims, const mb_weights *w, uint8_t *packed, size_t packed_bytes,
                     void *stream);
 
+/* The attention boundary, the step before the block ([providers]
+ * AttentionBoundaryProvider: post_attn_norm, the gated add into the fp32
+ * stream in place, pre_ffn_norm into bf16 out).  The provider first
+ * all-reduces the attention's row-parallel o_proj partial across ranks; on
+ * one GPU `partial` is that sum already.
+ *   v      = RMSNorm_H(partial) * post_attn_norm_w
+ *   stream = fp32(stream + gate * v)                        in place, fp32 [b, H]
+ *   out    = bf16(RMSNorm_H(stream) * pre_ffn_norm_w)       bf16 [b, H] (the block's x)
+ * partial bf16 [b, H]; gate bf16 [H] (the attention add's gate); the norm
+ * weights bf16 [H] or NULL (= 1), effective multipliers as in mb_weights;
+ * epsilon dims->norm_eps.  Device pointers, 16-byte aligned; `out` must not
+ * overlap `partial`.  Asynchronous on `stream_handle`; no workspace. */
+int mb_attn_boundary(const mb_dims *dims, const uint16_t *partial, const uint16_t *post_attn_norm_w,
+                     const uint16_t *gate, const uint16_t *pre_ffn_norm_w, float *stream, uint16_t *out,
+                     void *stream_handle);
+
+/* The next layer's QKV projection, the step after the block ([mono.decoder]
+ * LayerWeights: w_qkvg, the next layer's qkv_proj weight, which the HB launch
+ * applies to x_next after the FFN boundary; its rows are
+ * MonoDims.qkvg_rows = 2 * q_rows + 2 * kv_rows: q, k, v and the o-gate):
+ *   qkvg = bf16(x_next @ w_qkvg^T)                          bf16 [b, n_out]
+ * x_next bf16 [b, H]; w_qkvg bf16 [n_out, H] row-major; n_out > 0 and a
+ * multiple of 16 (else MB_ERR_DIMS / MB_ERR_UNSUPPORTED).  fp32 accumulation
+ * split along H, the splits added in a fixed order.  The split partials go to
+ * the workspace (mb_workspace_bytes of the same dims); the split is capped so
+ * that they fit.  The QK norm, RoPE and KV insert of the attention's QKV front
+ * are not part of this call. */
+int mb_next_qkv(const mb_dims *dims, const uint16_t *x_next, const uint16_t *w_qkvg, int32_t n_out,
+                uint16_t *qkvg, void *workspace, size_t workspace_bytes, void *stream);
+
+/* A static, human-readable reason for a status code. */
 const char *mb_status_string(int status);
 
 #ifdef __cplusplus

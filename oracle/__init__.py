@@ -24,6 +24,7 @@ stream).  Everything else is computed in fp64.
 
 from .steps import (  # noqa: F401
     BlockResult,
+    attn_boundary,
     Routing,
     bf16_to_f64,
     block,
@@ -35,6 +36,7 @@ from .steps import (  # noqa: F401
     experts_down,
     fake_quant_mxfp4,
     group_routes,
+    next_qkv,
     pool,
     quantize_mxfp4,
     rms_norm,

@@ -382,6 +382,30 @@ def boundary(u: np.ndarray, stream: np.ndarray, gate: np.ndarray, ffn_norm_w, ne
     return s_new, x_next
 
 
+def attn_boundary(partial: np.ndarray, stream: np.ndarray, gate: np.ndarray, post_attn_norm_w,
+                  pre_ffn_norm_w, norm_eps: float):
+    """The attention boundary, the step before the block ([providers]
+    AttentionBoundaryProvider: post_attn_norm of the attention's (all-reduced)
+    o_proj partial, the gated add into the fp32 stream in place, pre_ffn_norm
+    into the bf16 out, the block's x).  The same three operations as the FFN
+    boundary, with the attention side's weights:
+      v = RMSNorm_H(partial) * w_post_attn;  stream' = fp32(stream + g * v);
+      out = bf16(RMSNorm_H(stream') * w_pre_ffn).
+    Returns (stream' fp32 [b, H], out bf16 bits [b, H])."""
+    v = rms_norm(bf16_to_f64(partial), post_attn_norm_w, norm_eps)
+    s_new = (np.asarray(stream, dtype=F32).astype(F64) + bf16_to_f64(gate) * v).astype(F32)
+    out = round_bf16(rms_norm(s_new.astype(F64), pre_ffn_norm_w, norm_eps))
+    return s_new, out
+
+
+def next_qkv(x_next: np.ndarray, w_qkvg: np.ndarray) -> np.ndarray:
+    """The next layer's QKV (+ o-gate) projection on the block's x_next
+    ([mono.decoder] LayerWeights: w_qkvg, the next layer's qkv_proj weight, bf16
+    [qkvg_rows, H] with qkvg_rows = 2 q_rows + 2 kv_rows, applied after the FFN
+    boundary): bf16(x_next @ w_qkvg^T), bf16 bits [b, qkvg_rows]."""
+    return round_bf16(bf16_to_f64(x_next) @ bf16_to_f64(w_qkvg).T)
+
+
 @dataclasses.dataclass
 class BlockResult:
     routing: Routing

@@ -30,6 +30,8 @@ EXPORTS = (
     "mb_moe_block",
     "mb_packed_experts_bytes",
     "mb_pack_experts",
+    "mb_attn_boundary",
+    "mb_next_qkv",
     "mb_status_string",
 )
 
@@ -91,6 +93,8 @@ def lib() -> ctypes.CDLL:
                                    ctypes.c_size_t, _vp]
         L.mb_packed_experts_bytes.argtypes = [P(Dims), P(ctypes.c_size_t)]
         L.mb_pack_experts.argtypes = [P(Dims), P(Weights), _vp, ctypes.c_size_t, _vp]
+        L.mb_attn_boundary.argtypes = [P(Dims), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.mb_next_qkv.argtypes = [P(Dims), _vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_size_t, _vp]
         L.mb_status_string.argtypes = [ctypes.c_int]
         L.mb_status_string.restype = ctypes.c_char_p
         for name in EXPORTS:
@@ -212,6 +216,21 @@ def mb_unpool_boundary(dims: Dims, moe_out, weights: Weights, stream, x_next,
     _check(lib().mb_unpool_boundary(ctypes.byref(dims), _p(moe_out), ctypes.byref(weights),
                                     _p(stream), _p(x_next), _p(u_out), _p(ws), ws.numel(),
                                     _stream()), "mb_unpool_boundary")
+
+
+def mb_attn_boundary(dims: Dims, partial, gate, stream, out, post_attn_norm_w=None,
+                     pre_ffn_norm_w=None) -> None:
+    """The attention boundary (post_attn_norm, gated add into the fp32 stream
+    in place, pre_ffn_norm into out): the block's input x."""
+    _check(lib().mb_attn_boundary(ctypes.byref(dims), _p(partial), _p(post_attn_norm_w), _p(gate),
+                                  _p(pre_ffn_norm_w), _p(stream), _p(out), _stream()),
+           "mb_attn_boundary")
+
+
+def mb_next_qkv(dims: Dims, x_next, w_qkvg, qkvg, ws: torch.Tensor) -> None:
+    """qkvg = bf16(x_next @ w_qkvg^T), the next layer's QKV + o-gate projection."""
+    _check(lib().mb_next_qkv(ctypes.byref(dims), _p(x_next), _p(w_qkvg), int(w_qkvg.shape[0]), _p(qkvg),
+                             _p(ws), ws.numel(), _stream()), "mb_next_qkv")
 
 
 def mb_moe_block(dims: Dims, x, weights: Weights, stream, x_next, ws: torch.Tensor,

@@ -544,6 +544,35 @@ int mb_pack_experts(const mb_dims *dims, const mb_weights *w, uint8_t *packed, s
   return MB_OK;
 }
 
+int mb_attn_boundary(const mb_dims *dims, const uint16_t *partial, const uint16_t *post_attn_norm_w,
+                     const uint16_t *gate, const uint16_t *pre_ffn_norm_w, float *stream, uint16_t *out,
+                     void *stream_handle) {
+  MB_TRY(check_dims(dims));
+  MB_TRY(need({partial, gate, stream, out}));
+  MB_TRY(maybe({post_attn_norm_w, pre_ffn_norm_w}));
+  if (dims->hidden > 1024 * kBoundGroups) return MB_ERR_UNSUPPORTED;
+  MB_HIP(launch_boundary(*dims, partial, stream, gate, post_attn_norm_w, pre_ffn_norm_w, out,
+                         (hipStream_t)stream_handle));
+  return MB_OK;
+}
+
+int mb_next_qkv(const mb_dims *dims, const uint16_t *x_next, const uint16_t *w_qkvg, int32_t n_out,
+                uint16_t *qkvg, void *workspace, size_t workspace_bytes, void *stream) {
+  MB_TRY(check_dims(dims));
+  if (n_out <= 0) return MB_ERR_DIMS;
+  if (n_out % 16) return MB_ERR_UNSUPPORTED;
+  MB_TRY(need({x_next, w_qkvg, qkvg}));
+  MB_TRY(check_ws(dims, workspace, workspace_bytes));
+  // Split partials [ks][b][n_out] fp32 in the workspace's partial area.
+  const Layout L = layout_of(*dims);
+  const size_t per_split = (size_t)dims->rows * n_out * 4;
+  const size_t room = (size_t)kMaxSplitK * dims->rows * std::max(dims->pooled, dims->hidden) * 4;  // its size
+  const int cap = (int)std::min<size_t>(kMaxSplitK, room / per_split);
+  MB_HIP(launch_gemm_bf16(x_next, w_qkvg, qkvg, dims->rows, n_out, dims->hidden, at<float>(workspace, L.partial),
+                          nullptr, (hipStream_t)stream, cap < 1 ? 1 : cap));
+  return MB_OK;
+}
+
 const char *mb_status_string(int status) {
   switch (status) {
     case MB_OK: return "ok";

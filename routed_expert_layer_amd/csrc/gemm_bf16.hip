@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void rownorm_bf16_kernel(uint16_t *__restrict_
 
 hipError_t launch_gemm_bf16(const uint16_t *a, const uint16_t *w, uint16_t *out, int rows,
                             int n_out, int kdim, float *partial, uint32_t *counters,
-                            hipStream_t s) {
+                            hipStream_t s, int ks_cap) {
   const int ntiles = n_out / 16;
   const int nchunks = kdim / 32;
   const int per_pass = rows < 128 ? rows : 128;
@@ -155,7 +155,7 @@ hipError_t launch_gemm_bf16(const uint16_t *a, const uint16_t *w, uint16_t *out,
   // Enough workgroups to keep every CU streaming, but at least 16 chunks
   // (4 per wave) per workgroup.
   int ks = 1;
-  while (ks < kMaxSplitK && ntiles * rblocks * ks < 1024 && nchunks / (2 * ks) >= 16) ks *= 2;
+  while (2 * ks <= ks_cap && ntiles * rblocks * ks < 1024 && nchunks / (2 * ks) >= 16) ks *= 2;
   const int cpw = (nchunks + ks - 1) / ks;
   ks = (nchunks + cpw - 1) / cpw;
   dim3 grid(ntiles, ks, rblocks);

@@ -41,9 +41,11 @@ hipError_t launch_route_group(const mb_dims &d, const int32_t *ids, int32_t *cou
 // out[t, n] = bf16(sum_k a[t, k] * w[n, k]) for t < rows, n < n_out; a bf16
 // [rows, kdim], w bf16 [n_out, kdim].  Split-K partials and per-tile counters
 // come from the workspace.
+// out = bf16(a @ w^T), split along kdim into at most ks_cap (<= kMaxSplitK)
+// parts whose fp32 partials [ks][rows][n_out] go to `partial`.
 hipError_t launch_gemm_bf16(const uint16_t *a, const uint16_t *w, uint16_t *out, int rows,
                             int n_out, int kdim, float *partial, uint32_t *counters,
-                            hipStream_t s);
+                            hipStream_t s, int ks_cap = kMaxSplitK);
 
 // In-place h[t] = bf16(RMSNorm(h[t]) * w) over `width` elements.
 hipError_t launch_rownorm_bf16(uint16_t *h, const uint16_t *w, int rows, int width, float eps,

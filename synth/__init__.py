@@ -14,6 +14,7 @@ from .inputs import (  # noqa: F401
     Dims,
     f32_to_bf16_bits,
     bf16_bits_to_f32,
+    make_attn_side,
     make_block,
     make_c3_block,
     make_c4_layer,

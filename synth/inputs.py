@@ -249,3 +249,19 @@ def routing_inputs(name: str, skew: Optional[str] = None):
     if name == "c4":
         x = make_c4_stream()[0]
     return x, w, bias
+
+
+def make_attn_side(rows: int, hidden: int, qkvg_rows: int, seed: int, norm_weights: bool = True) -> dict:
+    """Inputs of the steps either side of the block: the attention's o_proj
+    partial bf16 N(0, 1) [rows, H], the attention add's gate bf16 N(0.5, 0.1),
+    the post-attention and pre-FFN norm weights bf16 N(1, 0.1) (or None), the
+    stream fp32 N(0, 1), and the next layer's QKV + o-gate weight bf16
+    N(0, 0.02) [qkvg_rows, H]; drawn in that order."""
+    rng = np.random.default_rng(seed)
+    out = {"partial": _normal_bf16(rng, (rows, hidden), 0.0, 1.0),
+           "gate": _normal_bf16(rng, (hidden,), 0.5, 0.1)}
+    out["post_attn_norm_w"] = _normal_bf16(rng, (hidden,), 1.0, 0.1) if norm_weights else None
+    out["pre_ffn_norm_w"] = _normal_bf16(rng, (hidden,), 1.0, 0.1) if norm_weights else None
+    out["stream"] = rng.standard_normal((rows, hidden)).astype(np.float32)
+    out["w_qkvg"] = _normal_bf16(rng, (qkvg_rows, hidden), 0.0, 0.02)
+    return out

@@ -26,7 +26,8 @@ def header_functions():
 def test_header_declares_the_five_calls():
     names = header_functions()
     for n in ("mb_route", "mb_pool", "mb_experts", "mb_unpool_boundary", "mb_moe_block",
-              "mb_workspace_bytes", "mb_packed_experts_bytes", "mb_pack_experts", "mb_status_string"):
+              "mb_workspace_bytes", "mb_packed_experts_bytes", "mb_pack_experts", "mb_status_string",
+              "mb_attn_boundary", "mb_next_qkv"):
         assert n in names
     assert set(names) == set(rel.EXPORTS)
 
@@ -204,3 +205,19 @@ def test_mxfp4_activations_need_the_streaming_layout():
                           None) == MB_ERR_UNSUPPORTED
     assert L.mb_experts(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                         ctypes.byref(w), FAKE, FAKE, 1 << 40, None) == MB_ERR_UNSUPPORTED
+
+
+def test_steps_around_the_block_check_arguments():
+    d = c1_dims()
+    L = rel.lib()
+    # mb_attn_boundary(dims, partial, post_attn_norm_w, gate, pre_ffn_norm_w, stream, out, s)
+    assert L.mb_attn_boundary(ctypes.byref(d), FAKE, None, None, None, FAKE, FAKE, None) == MB_ERR_NULL
+    assert L.mb_attn_boundary(ctypes.byref(d), FAKE, FAKE + 2, FAKE, None, FAKE, FAKE, None) == MB_ERR_ALIGN
+    assert L.mb_attn_boundary(ctypes.byref(d), FAKE, None, FAKE, None, None, FAKE, None) == MB_ERR_NULL
+    assert L.mb_attn_boundary(ctypes.byref(c1_dims(hidden=16384)), FAKE, None, FAKE, None, FAKE, FAKE,
+                              None) == MB_ERR_UNSUPPORTED
+    # mb_next_qkv(dims, x_next, w_qkvg, n_out, qkvg, ws, ws_bytes, s)
+    assert L.mb_next_qkv(ctypes.byref(d), FAKE, FAKE, 0, FAKE, FAKE, 1 << 40, None) == MB_ERR_DIMS
+    assert L.mb_next_qkv(ctypes.byref(d), FAKE, FAKE, 24, FAKE, FAKE, 1 << 40, None) == MB_ERR_UNSUPPORTED
+    assert L.mb_next_qkv(ctypes.byref(d), FAKE, None, 32, FAKE, FAKE, 1 << 40, None) == MB_ERR_NULL
+    assert L.mb_next_qkv(ctypes.byref(d), FAKE, FAKE, 32, FAKE, FAKE, 16, None) == MB_ERR_WORKSPACE

@@ -454,6 +454,47 @@ def test_boundary_constant_rows_closed_form():
     assert np.array_equal(xn[0], want_x)
 
 
+# ------------------------------------------- steps either side of the block
+
+def test_attn_boundary_closed_forms():
+    """A zero gate leaves the stream unchanged; a constant partial row normalises
+    to 1 (times the post-attention norm weight) and adds g * w there; the out
+    row is the stream row over its root mean square, times the pre-FFN weight."""
+    H, eps = 8, 1e-6
+    rng = np.random.default_rng(21)
+    s = rng.standard_normal((2, H)).astype(F32)
+    part = bf16(rng.standard_normal((2, H)))
+    s0, _ = oracle.attn_boundary(part, s, np.zeros(H, np.uint16), None, None, eps)
+    assert np.array_equal(s0, s)
+    c = -1.5
+    part = bf16(np.full((1, H), c))
+    g = bf16(np.array([0.5, 0.25, 1.0, 0.5, 0.125, 2.0, 0.5, 0.75]))
+    wa = bf16(np.array([1.0, 2.0, 0.5, 1.0, 1.0, 0.25, 1.0, 4.0]))
+    wf = bf16(np.array([2.0, 1.0, 1.0, 0.5, 1.0, 1.0, 0.25, 1.0]))
+    s1 = s[:1]
+    s_new, out = oracle.attn_boundary(part, s1, g, wa, wf, eps)
+    v = c / math.sqrt(c * c + eps)
+    want_s = [F32(float(s1[0, i]) + float(f(g[i])) * v * float(f(wa[i]))) for i in range(H)]
+    assert list(s_new[0]) == want_s
+    ms = sum(float(x) ** 2 for x in want_s) / H
+    want_o = bf16(np.array([float(x) / math.sqrt(ms + eps) * float(f(wf[i])) for i, x in enumerate(want_s)]))
+    assert np.array_equal(out[0], want_o)
+
+
+def test_next_qkv_one_hot_and_linearity():
+    rng = np.random.default_rng(22)
+    H, N = 64, 48
+    w = bf16(rng.standard_normal((N, H)) * 0.02)
+    x = np.zeros((2, H), np.uint16)
+    x[0, 7] = 0x3F80  # 1.0: the projection is column 7 of w exactly
+    x[1, 7] = 0x3F80
+    x[1, 40] = 0xBF80  # -1.0
+    q = oracle.next_qkv(x, w)
+    assert q.shape == (2, N)
+    assert np.array_equal(q[0], w[:, 7])
+    assert np.array_equal(q[1], bf16(f(w[:, 7]) - f(w[:, 40])))
+
+
 # ---------------------------------------------------------------- whole block
 
 def test_rows_are_independent():

@@ -1,0 +1,91 @@
+"""GPU parity of the steps either side of the block: the attention boundary
+(mb_attn_boundary) that produces the block's input x, and the next layer's
+QKV + o-gate projection (mb_next_qkv) of the block's x_next; then the three
+chained as one layer's FFN half (teacher-forced stage by stage).
+
+The QKV shape is synthetic: 32 query heads and 8 KV heads of 128, so
+qkvg_rows = 2 * 4096 + 2 * 1024 = 10240 at H = 4096."""
+
+import pytest
+
+import oracle
+import routed_expert_layer_amd as rel
+import synth
+from parity import BF16, GpuBlock, assert_block, assert_close, say
+from synth.device import bits, to_tensor
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+QKVG_C1 = 10240
+
+
+def _dims(rows, hidden, pooled=2048):
+    return rel.make_dims(rows=rows, hidden=hidden, pooled=pooled, inter=1024, experts=64, top_k=4,
+                         scoring="sigmoid", route_scale=2.5)
+
+
+def _attn(rows, hidden, seed, norm_weights=True):
+    a = synth.make_attn_side(rows, hidden, 16, seed, norm_weights)
+    say(f"[gpu] attention boundary rows {rows} H {hidden} norms {norm_weights}")
+    d = _dims(rows, hidden)
+    stream = to_tensor(a["stream"])
+    out = torch.zeros((rows, hidden), dtype=BF16, device="cuda")
+    t = {k: (None if a[k] is None else to_tensor(a[k])) for k in ("partial", "gate", "post_attn_norm_w",
+                                                                  "pre_ffn_norm_w")}
+    rel.mb_attn_boundary(d, t["partial"], t["gate"], stream, out, t["post_attn_norm_w"], t["pre_ffn_norm_w"])
+    torch.cuda.synchronize()
+    s_ref, o_ref = oracle.attn_boundary(a["partial"], a["stream"], a["gate"], a["post_attn_norm_w"],
+                                        a["pre_ffn_norm_w"], 1e-6)
+    assert_close(stream.cpu().numpy(), s_ref, "stream", atol=1e-5, rtol=1e-5, is_bf16=False)
+    assert_close(bits(out), o_ref, "out")
+
+
+@pytest.mark.parametrize("rows,hidden,norms", [(16, 4096, True), (37, 4096, False), (1, 7168, True),
+                                               (64, 7168, True)])
+def test_attn_boundary(rows, hidden, norms):
+    _attn(rows, hidden, 50 + rows, norms)
+
+
+@pytest.mark.parametrize("rows,hidden,n_out", [(16, 4096, QKVG_C1), (37, 4096, 1040), (1, 4096, 16),
+                                               (64, 7168, 2048)])
+def test_next_qkv(rows, hidden, n_out):
+    a = synth.make_attn_side(rows, hidden, n_out, 60 + rows)
+    say(f"[gpu] next qkv rows {rows} H {hidden} n_out {n_out}")
+    d = _dims(rows, hidden)
+    ws = rel.workspace(d)
+    x = to_tensor(a["partial"])  # any bf16 [rows, H] stands for x_next
+    q = torch.zeros((rows, n_out), dtype=BF16, device="cuda")
+    rel.mb_next_qkv(d, x, to_tensor(a["w_qkvg"]), q, ws)
+    torch.cuda.synchronize()
+    assert_close(bits(q), oracle.next_qkv(a["partial"], a["w_qkvg"]), "qkvg")
+
+
+def test_ffn_half_of_a_layer_chained():
+    """attention boundary -> block -> next QKV at c1, each stage checked on the
+    GPU's own input to it (the block end to end as in the block tests)."""
+    blk = synth.make_block("c1")
+    d = blk.dims
+    a = synth.make_attn_side(d.rows, d.hidden, QKVG_C1, 70)
+    say("[gpu] chained: attention boundary, block, next qkv (c1)")
+    g = GpuBlock(blk)
+    stream = to_tensor(a["stream"])
+    x = torch.zeros((d.rows, d.hidden), dtype=BF16, device="cuda")
+    t = {k: to_tensor(a[k]) for k in ("partial", "gate", "post_attn_norm_w", "pre_ffn_norm_w")}
+    rel.mb_attn_boundary(g.dims, t["partial"], t["gate"], stream, x, t["post_attn_norm_w"], t["pre_ffn_norm_w"])
+    torch.cuda.synchronize()
+    s1_ref, x_ref = oracle.attn_boundary(a["partial"], a["stream"], a["gate"], a["post_attn_norm_w"],
+                                         a["pre_ffn_norm_w"], d.norm_eps)
+    s1 = stream.cpu().numpy()
+    assert_close(s1, s1_ref, "stream after attention", atol=1e-5, rtol=1e-5, is_bf16=False)
+    assert_close(bits(x), x_ref, "x")
+    # The block on the GPU's x and stream.
+    blk.x, blk.stream = bits(x), s1
+    g.x, g.stream0 = x, stream
+    got = g.run_block()
+    assert_block(got, oracle.block(blk), "c1 after attention boundary", blk)
+    q = torch.zeros((d.rows, QKVG_C1), dtype=BF16, device="cuda")
+    rel.mb_next_qkv(g.dims, to_tensor(got["x_next"]), to_tensor(a["w_qkvg"]), q, g.ws)
+    torch.cuda.synchronize()
+    assert_close(bits(q), oracle.next_qkv(got["x_next"], a["w_qkvg"]), "qkvg on GPU x_next")
