@@ -165,6 +165,39 @@ def sweep(args) -> int:
         us = timed(lambda i: rel.mb_moe_block(dims, x, weights[i % S], stream, xn, ws), steps, warmup)
         report(case, d, us, actives)
 
+    def report_bytes(case, rows, us, b_alg):
+        gbs = b_alg / (us * 1e-6) / 1e9
+        line = {"case": case, "rows": rows, "us_per_step": round(us, 2), "blocks_per_step": 1,
+                "rows_per_s": round(rows / (us * 1e-6), 1), "algorithmic_bytes_per_step": int(b_alg),
+                "achieved_GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4),
+                "active_experts": None, "expert_layout": None, "act_quant": None}
+        print(json.dumps(line), flush=True)
+        print(f"[sweep] {case}: {us:.1f} us/step, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)",
+              file=sys.stderr, flush=True)
+
+    # The steps either side of the block at the decode size (b = 16, H = 4096):
+    # the attention boundary, and the next QKV projection with 32 query and 8
+    # KV heads of 128 (10240 rows); four weight sets rotated for the latter.
+    print("[sweep] steps around the block", file=sys.stderr, flush=True)
+    b16, H16, NQ = 16, 4096, 10240
+    side = synth.make_attn_side(b16, H16, NQ, 80)
+    d16 = rel.make_dims(rows=b16, hidden=H16, pooled=2048, inter=1024, experts=64, top_k=4,
+                        scoring="sigmoid", route_scale=2.5)
+    ws16 = rel.workspace(d16, dev)
+    tp = {k: to_tensor(side[k], dev) for k in ("partial", "gate", "post_attn_norm_w", "pre_ffn_norm_w", "stream")}
+    xo = torch.empty((b16, H16), dtype=torch.bfloat16, device=dev)
+    us = timed(lambda i: rel.mb_attn_boundary(d16, tp["partial"], tp["gate"], tp["stream"], xo,
+                                              tp["post_attn_norm_w"], tp["pre_ffn_norm_w"]), 1000, 50)
+    report_bytes("attention boundary b=16 H=4096", b16, us, b16 * H16 * 2 + 2 * b16 * H16 * 4 + b16 * H16 * 2 + 3 * H16 * 2)
+    wq = [to_tensor(synth.make_attn_side(1, H16, NQ, 81 + i)["w_qkvg"], dev) for i in range(4)]
+    q = torch.empty((b16, NQ), dtype=torch.bfloat16, device=dev)
+    us = timed(lambda i: rel.mb_next_qkv(d16, xo, wq[i % 4], q, ws16), 500, 20)
+    report_bytes("next qkv projection b=16 H=4096 -> 10240", b16, us, NQ * H16 * 2 + b16 * H16 * 2 + b16 * NQ * 2)
+    del wq, tp, ws16
+    torch.cuda.empty_cache()
+    if args.steps_around_only:
+        return 0
+
     print("[sweep] c0", file=sys.stderr, flush=True)
     run_block_case("c0 tiny block", [synth.make_block("c0")], 1000)
     for skew in ("calibrated", "literal"):
@@ -221,6 +254,8 @@ def main() -> int:
                     help="the W4A4 variant: the experts' activations quantized to MXFP4 (needs the "
                          "packed layout); not the headline line")
     ap.add_argument("--print-source-hash", action="store_true")
+    ap.add_argument("--steps-around-only", action="store_true",
+                    help="with --sweep: only the attention boundary and the next QKV projection")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the c1 metric, time every workload (c0, c2, c3 buckets, c4 "
                          "stack) and print one JSON line per case")

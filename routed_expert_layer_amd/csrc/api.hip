@@ -550,7 +550,6 @@ int mb_attn_boundary(const mb_dims *dims, const uint16_t *partial, const uint16_
   MB_TRY(check_dims(dims));
   MB_TRY(need({partial, gate, stream, out}));
   MB_TRY(maybe({post_attn_norm_w, pre_ffn_norm_w}));
-  if (dims->hidden > 1024 * kBoundGroups) return MB_ERR_UNSUPPORTED;
   MB_HIP(launch_boundary(*dims, partial, stream, gate, post_attn_norm_w, pre_ffn_norm_w, out,
                          (hipStream_t)stream_handle));
   return MB_OK;

@@ -214,8 +214,6 @@ def test_steps_around_the_block_check_arguments():
     assert L.mb_attn_boundary(ctypes.byref(d), FAKE, None, None, None, FAKE, FAKE, None) == MB_ERR_NULL
     assert L.mb_attn_boundary(ctypes.byref(d), FAKE, FAKE + 2, FAKE, None, FAKE, FAKE, None) == MB_ERR_ALIGN
     assert L.mb_attn_boundary(ctypes.byref(d), FAKE, None, FAKE, None, None, FAKE, None) == MB_ERR_NULL
-    assert L.mb_attn_boundary(ctypes.byref(c1_dims(hidden=16384)), FAKE, None, FAKE, None, FAKE, FAKE,
-                              None) == MB_ERR_UNSUPPORTED
     # mb_next_qkv(dims, x_next, w_qkvg, n_out, qkvg, ws, ws_bytes, s)
     assert L.mb_next_qkv(ctypes.byref(d), FAKE, FAKE, 0, FAKE, FAKE, 1 << 40, None) == MB_ERR_DIMS
     assert L.mb_next_qkv(ctypes.byref(d), FAKE, FAKE, 24, FAKE, FAKE, 1 << 40, None) == MB_ERR_UNSUPPORTED

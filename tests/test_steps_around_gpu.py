@@ -43,7 +43,7 @@ def _attn(rows, hidden, seed, norm_weights=True):
 
 
 @pytest.mark.parametrize("rows,hidden,norms", [(16, 4096, True), (37, 4096, False), (1, 7168, True),
-                                               (64, 7168, True)])
+                                               (64, 7168, True), (3, 12288, True)])
 def test_attn_boundary(rows, hidden, norms):
     _attn(rows, hidden, 50 + rows, norms)
 
