@@ -289,6 +289,18 @@ int mb_attn_boundary(const mb_dims *dims, const uint16_t *partial, const uint16_
 int mb_next_qkv(const mb_dims *dims, const uint16_t *x_next, const uint16_t *w_qkvg, int32_t n_out,
                 uint16_t *qkvg, void *workspace, size_t workspace_bytes, void *stream);
 
+/* The bf16 norm multiplier of a norm with a zero-centred gamma ([mono.decoder]
+ * effective_norm_weight: the multiplier a norm applies is its weight, plus its
+ * gain centre when the gamma is zero-centred):
+ *   out[i] = bf16(fp32(weight[i] + gain_center))   (zero_centered != 0)
+ *   out[i] = bf16(weight[i])                          (zero_centered == 0)
+ * weight fp32 [n] (the norm's parameter, widened), out bf16 [n]; device
+ * pointers.  Load-time preparation of the norm weights every entry point
+ * takes (mb_weights' *_norm_w, the attention boundary's).  Asynchronous on
+ * `stream`.  MB_ERR_DIMS if n <= 0 or gain_center is not finite. */
+int mb_effective_norm_weight(const float *weight, int32_t n, float gain_center, int32_t zero_centered,
+                             uint16_t *out, void *stream);
+
 /* A static, human-readable reason for a status code. */
 const char *mb_status_string(int status);
 

@@ -32,6 +32,7 @@ from .steps import (  # noqa: F401
     decode_e2m1,
     decode_e8m0,
     dequant_mxfp4,
+    effective_norm_weight,
     experts,
     experts_down,
     fake_quant_mxfp4,

@@ -398,6 +398,16 @@ def attn_boundary(partial: np.ndarray, stream: np.ndarray, gate: np.ndarray, pos
     return s_new, out
 
 
+def effective_norm_weight(weight: np.ndarray, gain_center: float, zero_centered: bool) -> np.ndarray:
+    """The bf16 multiplier a norm applies ([mono.decoder] effective_norm_weight):
+    the weight widened to fp32, plus the gain centre when the gamma is
+    zero-centred (an fp32 addition), rounded to bf16.  Returns bf16 bits."""
+    w = np.asarray(weight, dtype=F32)
+    if zero_centered:
+        w = (w + F32(gain_center)).astype(F32)
+    return round_bf16(w.astype(F64))
+
+
 def next_qkv(x_next: np.ndarray, w_qkvg: np.ndarray) -> np.ndarray:
     """The next layer's QKV (+ o-gate) projection on the block's x_next
     ([mono.decoder] LayerWeights: w_qkvg, the next layer's qkv_proj weight, bf16

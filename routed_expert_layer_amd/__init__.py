@@ -32,6 +32,7 @@ EXPORTS = (
     "mb_pack_experts",
     "mb_attn_boundary",
     "mb_next_qkv",
+    "mb_effective_norm_weight",
     "mb_status_string",
 )
 
@@ -95,6 +96,7 @@ def lib() -> ctypes.CDLL:
         L.mb_pack_experts.argtypes = [P(Dims), P(Weights), _vp, ctypes.c_size_t, _vp]
         L.mb_attn_boundary.argtypes = [P(Dims), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.mb_next_qkv.argtypes = [P(Dims), _vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_size_t, _vp]
+        L.mb_effective_norm_weight.argtypes = [_vp, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, _vp, _vp]
         L.mb_status_string.argtypes = [ctypes.c_int]
         L.mb_status_string.restype = ctypes.c_char_p
         for name in EXPORTS:
@@ -231,6 +233,15 @@ def mb_next_qkv(dims: Dims, x_next, w_qkvg, qkvg, ws: torch.Tensor) -> None:
     """qkvg = bf16(x_next @ w_qkvg^T), the next layer's QKV + o-gate projection."""
     _check(lib().mb_next_qkv(ctypes.byref(dims), _p(x_next), _p(w_qkvg), int(w_qkvg.shape[0]), _p(qkvg),
                              _p(ws), ws.numel(), _stream()), "mb_next_qkv")
+
+
+def mb_effective_norm_weight(weight, gain_center: float = 0.0, zero_centered: bool = False):
+    """The bf16 multiplier of a norm: bf16(weight (+ gain_center)), weight fp32 on the device."""
+    out = torch.empty(weight.shape, dtype=torch.bfloat16, device=weight.device)
+    _check(lib().mb_effective_norm_weight(_p(weight), int(weight.numel()), float(gain_center),
+                                          int(bool(zero_centered)), _p(out), _stream()),
+           "mb_effective_norm_weight")
+    return out
 
 
 def mb_moe_block(dims: Dims, x, weights: Weights, stream, x_next, ws: torch.Tensor,

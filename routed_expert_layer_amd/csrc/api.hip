@@ -572,6 +572,14 @@ int mb_next_qkv(const mb_dims *dims, const uint16_t *x_next, const uint16_t *w_q
   return MB_OK;
 }
 
+int mb_effective_norm_weight(const float *weight, int32_t n, float gain_center, int32_t zero_centered,
+                             uint16_t *out, void *stream) {
+  if (n <= 0 || !isfinite(gain_center)) return MB_ERR_DIMS;
+  if (!weight || !out) return MB_ERR_NULL;
+  MB_HIP(launch_norm_weight(weight, n, zero_centered ? gain_center : 0.0f, out, (hipStream_t)stream));
+  return MB_OK;
+}
+
 const char *mb_status_string(int status) {
   switch (status) {
     case MB_OK: return "ok";

@@ -131,7 +131,20 @@ __global__ __launch_bounds__(256) void boundary_kernel(
   }
 }
 
+// out[i] = bf16(fp32(weight[i] + add)), round to nearest even.
+__global__ __launch_bounds__(256) void norm_weight_kernel(const float *__restrict__ weight, int n, float add,
+                                                          uint16_t *__restrict__ out) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256)
+    out[i] = f32_to_bf16_bits(weight[i] + add);
+}
+
 }  // namespace
+
+hipError_t launch_norm_weight(const float *weight, int n, float add, uint16_t *out, hipStream_t s) {
+  const int blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+  hipLaunchKernelGGL(norm_weight_kernel, dim3(blocks), dim3(256), 0, s, weight, n, add, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_boundary(const mb_dims &d, const uint16_t *u, float *stream,
                            const uint16_t *gate, const uint16_t *ffn_norm_w,

@@ -70,6 +70,9 @@ hipError_t launch_experts_finalize(const mb_dims &d, const float *y, const float
 hipError_t launch_pack_experts(const mb_dims &d, const uint8_t *w13, const uint8_t *w13s, const uint8_t *w2,
                                const uint8_t *w2s, uint8_t *packed, hipStream_t s);
 
+// Effective norm multiplier: out = bf16(weight + add).
+hipError_t launch_norm_weight(const float *weight, int n, float add, uint16_t *out, hipStream_t s);
+
 // Boundary: RMSNorm of u, gated add into the fp32 stream, next pre-norm.
 hipError_t launch_boundary(const mb_dims &d, const uint16_t *u, float *stream,
                            const uint16_t *gate, const uint16_t *ffn_norm_w,

@@ -27,7 +27,7 @@ def test_header_declares_the_five_calls():
     names = header_functions()
     for n in ("mb_route", "mb_pool", "mb_experts", "mb_unpool_boundary", "mb_moe_block",
               "mb_workspace_bytes", "mb_packed_experts_bytes", "mb_pack_experts", "mb_status_string",
-              "mb_attn_boundary", "mb_next_qkv"):
+              "mb_attn_boundary", "mb_next_qkv", "mb_effective_norm_weight"):
         assert n in names
     assert set(names) == set(rel.EXPORTS)
 
@@ -219,3 +219,10 @@ def test_steps_around_the_block_check_arguments():
     assert L.mb_next_qkv(ctypes.byref(d), FAKE, FAKE, 24, FAKE, FAKE, 1 << 40, None) == MB_ERR_UNSUPPORTED
     assert L.mb_next_qkv(ctypes.byref(d), FAKE, None, 32, FAKE, FAKE, 1 << 40, None) == MB_ERR_NULL
     assert L.mb_next_qkv(ctypes.byref(d), FAKE, FAKE, 32, FAKE, FAKE, 16, None) == MB_ERR_WORKSPACE
+
+
+def test_effective_norm_weight_checks_arguments():
+    L = rel.lib()
+    assert L.mb_effective_norm_weight(FAKE, 0, 1.0, 1, FAKE, None) == MB_ERR_DIMS
+    assert L.mb_effective_norm_weight(FAKE, 8, float("nan"), 1, FAKE, None) == MB_ERR_DIMS
+    assert L.mb_effective_norm_weight(None, 8, 1.0, 1, FAKE, None) == MB_ERR_NULL

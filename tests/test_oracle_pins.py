@@ -481,6 +481,17 @@ def test_attn_boundary_closed_forms():
     assert np.array_equal(out[0], want_o)
 
 
+def test_effective_norm_weight_hand_cases():
+    w = np.array([0.0, -1.0, 0.25, 2.0 ** -9, 2.0 ** -8, 3 * 2.0 ** -8, 0.5], np.float32)
+    got = oracle.effective_norm_weight(w, 1.0, True)
+    # 1, 0, 1.25, 1 + 2^-9 -> 1.0 (below half an ulp), 1 + 2^-8 -> 1.0 (tie, even),
+    # 1 + 3 * 2^-8 -> 1 + 2^-6 (tie, even), 1.5
+    assert got.tolist() == [0x3F80, 0x0000, 0x3FA0, 0x3F80, 0x3F80, 0x3F82, 0x3FC0]
+    assert oracle.effective_norm_weight(w[[2, 6]], 1.0, False).tolist() == [0x3E80, 0x3F00]
+    # The gain centre is added in fp32 before the bf16 rounding.
+    assert oracle.effective_norm_weight(np.array([1e-8], np.float32), 1.0, True).tolist() == [0x3F80]
+
+
 def test_next_qkv_one_hot_and_linearity():
     rng = np.random.default_rng(22)
     H, N = 64, 48

@@ -89,3 +89,15 @@ def test_ffn_half_of_a_layer_chained():
     rel.mb_next_qkv(g.dims, to_tensor(got["x_next"]), to_tensor(a["w_qkvg"]), q, g.ws)
     torch.cuda.synchronize()
     assert_close(bits(q), oracle.next_qkv(got["x_next"], a["w_qkvg"]), "qkvg on GPU x_next")
+
+
+@pytest.mark.parametrize("zero_centered", [False, True])
+def test_effective_norm_weight(zero_centered):
+    import numpy as np
+    rng = np.random.default_rng(90)
+    w = (rng.standard_normal(5000) * 0.1).astype(np.float32)
+    w[:4] = [0.0, -1.0, 2.0 ** -8, 3 * 2.0 ** -8]
+    say(f"[gpu] effective norm weight zero_centered={zero_centered}")
+    out = rel.mb_effective_norm_weight(to_tensor(w), 1.0, zero_centered)
+    torch.cuda.synchronize()
+    assert (bits(out) == oracle.effective_norm_weight(w, 1.0, zero_centered)).all()
