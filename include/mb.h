@@ -90,7 +90,11 @@ enum {
  * code, magnitudes above 6 saturating to 6), and each contraction runs on
  * fp4 x fp4 products.  act_quant 1 runs in the block kernel only: it needs
  * w->experts_packed and sizes the block kernel takes (experts <= 64, hidden
- * <= 8192, route tables within its LDS), else MB_ERR_UNSUPPORTED. */
+ * <= 8192, route tables within its LDS), else MB_ERR_UNSUPPORTED.
+ * qkv_rows 0: mb_moe_block ends at the boundary.  qkv_rows > 0 (a multiple
+ * of 16, at most 65536): mb_moe_block also runs the next layer's QKV
+ * projection of x_next (as mb_next_qkv, with w->next_qkv_w bf16
+ * [qkv_rows, H]) in the same launch, into taps->qkvg (both required). */
 typedef struct {
   int32_t rows, hidden, pooled, inter, experts, top_k;
   int32_t scoring;
@@ -99,6 +103,7 @@ typedef struct {
   float division_eps;
   float norm_eps;
   int32_t act_quant;
+  int32_t qkv_rows;
 } mb_dims;
 
 /* The block's weights, all device pointers, in the layouts the pages fix:
@@ -140,6 +145,7 @@ typedef struct {
   const uint16_t *gate;
   const uint16_t *next_norm_w;
   const uint8_t *experts_packed;
+  const uint16_t *next_qkv_w;  /* bf16 [dims->qkv_rows, H] or NULL (qkv_rows 0) */
 } mb_weights;
 
 /* Optional intermediate outputs of mb_moe_block.  A NULL member is kept in
@@ -164,6 +170,8 @@ typedef struct {
   uint16_t *act;       /* bf16 [b * k, I]: the experts' gated activations
                           act = bf16(silu(gu[0:I]) * gu[I:2I]) (mb_experts),
                           row i for route route_list[i] (grouped by expert) */
+  uint16_t *qkvg;      /* bf16 [b, qkv_rows]: the fused next-QKV projection
+                          of x_next (required when dims->qkv_rows > 0) */
 } mb_block_taps;
 
 /* Bytes of workspace every entry point needs for these dims (the same size

@@ -47,14 +47,15 @@ class Dims(ctypes.Structure):
     _fields_ = [("rows", _c_i32), ("hidden", _c_i32), ("pooled", _c_i32), ("inter", _c_i32),
                 ("experts", _c_i32), ("top_k", _c_i32), ("scoring", _c_i32),
                 ("route_scale", _c_f32), ("router_multiplier", _c_f32),
-                ("division_eps", _c_f32), ("norm_eps", _c_f32), ("act_quant", _c_i32)]
+                ("division_eps", _c_f32), ("norm_eps", _c_f32), ("act_quant", _c_i32),
+                ("qkv_rows", _c_i32)]
 
 
 _WEIGHT_FIELDS = ("router_w", "expert_bias", "pool_w", "pre_norm_w", "w13", "w13_scale", "w2",
                   "w2_scale", "post_norm_w", "unpool_w", "ffn_norm_w", "gate", "next_norm_w",
-                  "experts_packed")
+                  "experts_packed", "next_qkv_w")
 _TAP_FIELDS = ("logits", "topk_ids", "topk_w", "count", "offset", "route_list", "active",
-               "n_active", "h", "moe_out", "u", "timeline", "act")
+               "n_active", "h", "moe_out", "u", "timeline", "act", "qkvg")
 
 
 class Weights(ctypes.Structure):
@@ -132,17 +133,18 @@ def _stream():
 
 
 def make_dims(rows, hidden, pooled, inter, experts, top_k, scoring, route_scale,
-              router_multiplier=None, division_eps=None, norm_eps=1e-6, act_quant=0) -> Dims:
+              router_multiplier=None, division_eps=None, norm_eps=1e-6, act_quant=0, qkv_rows=0) -> Dims:
     """Dims from Python values; scoring is "sigmoid" / "softmax" or 0 / 1; an
     absent multiplier is 1.0 and an absent division eps is 0.0; act_quant 1
-    quantizes the experts' activations to MXFP4 (the W4A4 variant)."""
+    quantizes the experts' activations to MXFP4 (the W4A4 variant); qkv_rows > 0
+    fuses the next layer's QKV projection into mb_moe_block."""
     if isinstance(scoring, str):
         scoring = {"sigmoid": MB_SCORING_SIGMOID, "softmax": MB_SCORING_SOFTMAX}.get(scoring, -1)
     return Dims(int(rows), int(hidden), int(pooled), int(inter), int(experts), int(top_k),
                 int(scoring), float(route_scale),
                 1.0 if router_multiplier is None else float(router_multiplier),
                 0.0 if division_eps is None else float(division_eps), float(norm_eps),
-                int(act_quant))
+                int(act_quant), int(qkv_rows))
 
 
 def make_weights(**tensors) -> Weights:

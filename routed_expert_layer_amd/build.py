@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmb.so")
-SOURCES = ["api.hip", "block.hip", "block_w4a4.hip", "route.hip", "gemm_bf16.hip", "experts.hip", "boundary.hip", "pack.hip"]
+SOURCES = ["api.hip", "block.hip", "block_w4a4.hip", "block_qkv.hip", "route.hip", "gemm_bf16.hip", "experts.hip", "boundary.hip", "pack.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

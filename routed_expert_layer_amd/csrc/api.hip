@@ -31,6 +31,7 @@ Layout layout_of(const mb_dims &d) {
   L.sync = take(kSyncWords * 4);
   L.pool_cnt = take((P / 16) * 4);
   L.unpool_cnt = take((H / 16) * 4);
+  L.qkv_cnt = take(kMaxQkvGroups * 4);
   L.logits = take(b * E * 4);
   L.ids = take(R * 4);
   L.wts = take(R * 4);
@@ -49,6 +50,7 @@ Layout layout_of(const mb_dims &d) {
   L.partial = take((size_t)kMaxSplitK * b * wide * 4);
   L.pool_part = take((size_t)kMaxPoolSplit * b * P * 4);
   L.unpool_part = take((size_t)kMaxSplitK * b * H * 4);
+  L.qkv_part = take((size_t)kMaxSplitK * b * (size_t)d.qkv_rows * 4);
   L.total = o;
   return L;
 }
@@ -69,6 +71,8 @@ int check_dims(const mb_dims *d) {
   if (d->top_k > d->experts) return MB_ERR_DIMS;
   if (d->scoring != MB_SCORING_SIGMOID && d->scoring != MB_SCORING_SOFTMAX) return MB_ERR_DIMS;
   if (d->act_quant != 0 && d->act_quant != 1) return MB_ERR_DIMS;
+  if (d->qkv_rows < 0) return MB_ERR_DIMS;
+  if (d->qkv_rows % 16 || d->qkv_rows > 64 * kMaxQkvGroups) return MB_ERR_UNSUPPORTED;
   if (!(d->norm_eps >= 0.0f) || !isfinite(d->norm_eps) || !isfinite(d->route_scale) ||
       !isfinite(d->router_multiplier) || !isfinite(d->division_eps))
     return MB_ERR_DIMS;
@@ -284,7 +288,8 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   const size_t route_bytes = route_lds_bytes(p.b, p.k, p.E);
   const size_t lds = route_bytes + kBlockScratchBytes;
   if (lds > 64 * 1024) return none;
-  const int occ = block_max_groups_per_cu(lds, p.w4a4 != 0);
+  if (p.n_qkv > 0 && p.w4a4) return MB_ERR_UNSUPPORTED;  // no kernel instance for both
+  const int occ = block_max_groups_per_cu(lds, p.w4a4 != 0, p.n_qkv > 0);
   const int cus = device_cus();
   if (occ < 1 || cus < 1) return none;
   int grid = cus * (occ < kBlockGroupsPerCu ? occ : kBlockGroupsPerCu);
@@ -476,7 +481,7 @@ int mb_moe_block(const mb_dims *dims, const uint16_t *x, const mb_weights *w, fl
   if (taps) {
     tp = *taps;
     MB_TRY(maybe({tp.logits, tp.topk_ids, tp.topk_w, tp.count, tp.offset, tp.route_list,
-                  tp.active, tp.n_active, tp.h, tp.moe_out, tp.u, tp.timeline, tp.act}));
+                  tp.active, tp.n_active, tp.h, tp.moe_out, tp.u, tp.timeline, tp.act, tp.qkvg}));
   }
   MB_TRY(check_ws(dims, workspace, workspace_bytes));
   const mb_dims &d = *dims;
@@ -515,6 +520,22 @@ int mb_moe_block(const mb_dims *dims, const uint16_t *x, const mb_weights *w, fl
   p.x_next = x_next;
   p.timeline = tp.timeline;
   if (tp.act) p.act = tp.act;
+  if (d.qkv_rows > 0) {
+    // The next-QKV projection fused after the boundary: 64-feature tiles,
+    // split along H to about fill the grid (each split a multiple of 32).
+    MB_TRY(need({w->next_qkv_w, tp.qkvg}));
+    const int groups = (d.qkv_rows + 63) / 64;
+    const int grid = device_cus() * kBlockGroupsPerCu;
+    int ks = std::max(1, std::min(kMaxSplitK, grid / groups));
+    while (ks > 1 && (d.hidden % ks != 0 || (d.hidden / ks) % 32 != 0)) --ks;
+    p.qkv_w = w->next_qkv_w;
+    p.qkvg = tp.qkvg;
+    p.qkv_rows = d.qkv_rows;
+    p.qkv_ks = ks;
+    p.n_qkv = groups * ks;
+    p.qkv_part = at<float>(ws, L.qkv_part);
+    p.qkv_cnt = at<unsigned>(ws, L.qkv_cnt);
+  }
   bool used = false;
   MB_TRY(run_fused(p, st, s, &used));
   if (used) return MB_OK;
@@ -522,7 +543,11 @@ int mb_moe_block(const mb_dims *dims, const uint16_t *x, const mb_weights *w, fl
   MB_TRY(run_route(d, x, w, logits, 0, ids, wts, count, offset, route_list, active, n_active, s));
   MB_TRY(run_pool(d, x, w, h, ws, s));
   MB_TRY(run_experts(d, h, wts, offset, route_list, active, n_active, w, moe_out, ws, s, tp.act));
-  return run_unpool_boundary(d, moe_out, w, stream, x_next, u, ws, s);
+  MB_TRY(run_unpool_boundary(d, moe_out, w, stream, x_next, u, ws, s));
+  if (d.qkv_rows > 0)
+    MB_HIP(launch_gemm_bf16(x_next, w->next_qkv_w, tp.qkvg, d.rows, d.qkv_rows, d.hidden, at<float>(ws, L.qkv_part),
+                            nullptr, s));
+  return MB_OK;
 }
 
 int mb_packed_experts_bytes(const mb_dims *dims, size_t *bytes) {

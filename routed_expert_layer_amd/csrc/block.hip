@@ -1661,7 +1661,10 @@ __device__ __forceinline__ void unpack4(u32x2_t v, float o[4]) {
 // in registers across the passes; the gate and the stream are requested
 // before the wait.  With a split unpooler, u = bf16 of its fp32 partials added here in
 // split order (and written out).
-template <int NG>
+//
+// kSignal (the next-QKV projection follows in the launch): x_next is written
+// coherently and the row signals kCtrBound.
+template <int NG, bool kSignal = false>
 __device__ __forceinline__ void boundary_task(const BlockParams &p, const Deps &d, int t,
                                               unsigned char *lds) {
   float *red = reinterpret_cast<float *>(lds);
@@ -1767,10 +1770,14 @@ __device__ __forceinline__ void boundary_task(const BlockParams &p, const Deps &
     unpack4(wv[m], wi);
     const f32x4_t sn = sv[m];
     *reinterpret_cast<f32x4_t *>(p.stream + (size_t)t * H + h) = sn;
-    *reinterpret_cast<u32x2_t *>(p.x_next + (size_t)t * H + h) =
-        u32x2_t{pack_bf16x2(sn[0] * rss * wi[0], sn[1] * rss * wi[1]),
-                pack_bf16x2(sn[2] * rss * wi[2], sn[3] * rss * wi[3])};
+    const u32x2_t xv = u32x2_t{pack_bf16x2(sn[0] * rss * wi[0], sn[1] * rss * wi[1]),
+                               pack_bf16x2(sn[2] * rss * wi[2], sn[3] * rss * wi[3])};
+    if constexpr (kSignal)
+      st_co8(make_rsrc(p.x_next), (uint32_t)(((size_t)t * H + h) * 2), xv);
+    else
+      *reinterpret_cast<u32x2_t *>(p.x_next + (size_t)t * H + h) = xv;
   }
+  if constexpr (kSignal) signal_step(d, kCtrBound);
   __syncthreads();
 }
 
@@ -1791,7 +1798,8 @@ __device__ __forceinline__ const BlockParams &kparams() {
 
 // kQ: the W4A4 variant (MXFP4 activations into the experts), a kernel of its
 // own so that each keeps its own code layout and registers.
-template <bool kQ>
+// kQKV: the next layer's QKV projection follows the boundary in the launch.
+template <bool kQ, bool kQKV = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void block_kernel(BlockParams p_arg) {
   extern __shared__ __align__(16) unsigned char lds[];
   (void)p_arg;  // read through kparams()
@@ -1921,16 +1929,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       const Deps d{p.sync, gen};
       const RouteLds R = route_lds(p, lds);
       unsigned char *scratch = lds + p.lds_route_bytes;
-      const int nF = p.n_fin, nN = p.n_unpool, nB = p.n_boundary;
-      if (j >= nF + nN + nB) break;
+      const int nF = p.n_fin, nN = p.n_unpool, nB = p.n_boundary, nQ = kQKV ? p.n_qkv : 0;
+      if (j >= nF + nN + nB + nQ) break;
       int step, i = j;
       if (i < nF) {
         step = 8;
       } else if ((i -= nF) < nN) {
         step = 9;
-      } else {
-        i -= nN;
+      } else if ((i -= nN) < nB) {
         step = 10;
+      } else {
+        i -= nB;
+        step = 24;
       }
       if (step != last) {
         stamp(p, step);
@@ -1951,10 +1961,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         }
         signal_step(d, kCtrUnpool);
         stamp(p, 16);
-      } else {
-        if (p.H <= 4096) boundary_task<4>(p, d, i, scratch);
-        else boundary_task<kBoundGroups>(p, d, i, scratch);
+      } else if (step == 10) {
+        if (p.H <= 4096) boundary_task<4, kQKV>(p, d, i, scratch);
+        else boundary_task<kBoundGroups, kQKV>(p, d, i, scratch);
         stamp(p, 18);
+      } else if constexpr (kQKV) {
+        // The next layer's QKV projection of x_next: wide tiles, the splits
+        // added by the last to finish.
+        const int gi = i / p.qkv_ks, q = i % p.qkv_ks;
+        proj_wide<true>(make_rsrc(p.x_next), p.qkv_w, p.b, p.qkv_rows, p.H, gi, q, p.qkv_ks, p.qkv_part, p.qkvg,
+                        scratch, [&]() { wait_step(d, kCtrBound, p.n_boundary); });
+        if (p.qkv_ks > 1 && last_arrival(&p.qkv_cnt[gi], (unsigned)p.qkv_ks, proj_flag(scratch))) {
+          proj_wide_sum(p.qkv_part, p.qkvg, p.b, p.qkv_rows, gi, p.qkv_ks);
+          if (tid() == 0) __hip_atomic_store(&p.qkv_cnt[gi], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        stamp(p, 25);
       }
     }
   }
@@ -1967,24 +1988,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 // An ordinary launch: the host sizes the grid to what the device holds at
 // once.  Should some workgroups only start after others finished work on
 // another kernel, the waits merely take longer (every one is bounded).
-// The W4A4 kernel is built from this file in a translation unit of its own
-// (block_w4a4.hip): sharing one code object moved the bf16 kernel's code
-// and cost it ~0.6 us per launch.
-#ifndef MB_BLOCK_W4A4
+// The W4A4 kernel and the kernel with the fused next-QKV projection are
+// built from this file in translation units of their own (block_w4a4.hip,
+// block_qkv.hip): sharing one code object moved the bf16 kernel's code and
+// cost it ~0.6 us per launch.
+#if !defined(MB_BLOCK_W4A4) && !defined(MB_BLOCK_QKV)
 hipError_t launch_block(const BlockParams &p, int grid, size_t lds, hipStream_t s) {
   if (p.w4a4) return launch_block_w4a4(p, grid, lds, s);
+  if (p.n_qkv > 0) return launch_block_qkv(p, grid, lds, s);
   hipLaunchKernelGGL(block_kernel<false>, dim3(grid), dim3(kThreads), lds, s, p);
   return hipGetLastError();
 }
 
-int block_max_groups_per_cu(size_t lds, bool w4a4) {
+int block_max_groups_per_cu(size_t lds, bool w4a4, bool qkv) {
   if (w4a4) return block_max_groups_per_cu_w4a4(lds);
+  if (qkv) return block_max_groups_per_cu_qkv(lds);
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_kernel<false>, kThreads, lds) != hipSuccess)
     return 0;
   return n;
 }
-#else
+#elif defined(MB_BLOCK_W4A4)
 hipError_t launch_block_w4a4(const BlockParams &p, int grid, size_t lds, hipStream_t s) {
   hipLaunchKernelGGL(block_kernel<true>, dim3(grid), dim3(kThreads), lds, s, p);
   return hipGetLastError();
@@ -1993,6 +2017,18 @@ hipError_t launch_block_w4a4(const BlockParams &p, int grid, size_t lds, hipStre
 int block_max_groups_per_cu_w4a4(size_t lds) {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_kernel<true>, kThreads, lds) != hipSuccess)
+    return 0;
+  return n;
+}
+#else
+hipError_t launch_block_qkv(const BlockParams &p, int grid, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL((block_kernel<false, true>), dim3(grid), dim3(kThreads), lds, s, p);
+  return hipGetLastError();
+}
+
+int block_max_groups_per_cu_qkv(size_t lds) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_kernel<false, true>, kThreads, lds) != hipSuccess)
     return 0;
   return n;
 }

@@ -1,0 +1,5 @@
+// The block kernel with the next layer's QKV projection fused after the
+// boundary: block.hip built again, with only that kernel, in a code object of
+// its own.
+#define MB_BLOCK_QKV 1
+#include "block.hip"

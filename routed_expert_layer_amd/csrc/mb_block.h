@@ -46,7 +46,8 @@ enum : int {
   kCtrPrenorm = 2,   // pre-norm rows done
   kCtrFin = 3,       // finalize tasks done
   kCtrUnpool = 4,    // unpooler tasks done
-  kNumCtr = 5,
+  kCtrBound = 5,     // boundary rows done (awaited by the fused next-QKV tiles)
+  kNumCtr = 6,
 };
 // Copies and stripes of step counter i (replicas x stripes <= kReplicas).
 // The route and pre-norm counters have few producers and are awaited by
@@ -55,7 +56,7 @@ enum : int {
 // the unpooler tasks as consumers; the unpooler's has H / 16 (times its
 // split) producers and only the b boundary tasks as consumers.
 __host__ __device__ constexpr int replicas(int i) {
-  return (i == kCtrRoute || i == kCtrPrenorm) ? kReplicas : (i == kCtrPool || i == kCtrFin) ? 4 : 1;
+  return (i == kCtrRoute || i == kCtrPrenorm || i == kCtrBound) ? kReplicas : (i == kCtrPool || i == kCtrFin) ? 4 : 1;
 }
 __host__ __device__ constexpr int stripes(int i) {
   return (i == kCtrPool || i == kCtrFin) ? 4 : i == kCtrUnpool ? kReplicas : 1;
@@ -146,7 +147,15 @@ struct BlockParams {
   // MXFP4 activations into the experts (streaming layout).  Last, so that the
   // other fields keep their kernel-argument offsets.
   int w4a4;
+  // The next layer's QKV projection fused after the boundary (n_qkv tasks:
+  // 64-feature tiles x qkv_ks contraction splits), or n_qkv = 0.
+  const uint16_t *qkv_w;
+  uint16_t *qkvg;
+  float *qkv_part;
+  unsigned *qkv_cnt;
+  int qkv_rows, n_qkv, qkv_ks;
 };
+constexpr int kMaxQkvGroups = 1024;  // 64-feature tiles of the fused projection (qkv_rows <= 65536)
 
 // Routing state each workgroup keeps in LDS.
 struct RouteLds {
@@ -201,8 +210,10 @@ constexpr size_t kProjScratchBytes = 4 * 4 * 64 * 16 + 64;
 constexpr size_t kBlockScratchBytes = kProjScratchBytes > kStageBytes ? kProjScratchBytes : kStageBytes;
 
 hipError_t launch_block(const BlockParams &p, int grid, size_t lds, hipStream_t s);
-int block_max_groups_per_cu(size_t lds, bool w4a4);
+int block_max_groups_per_cu(size_t lds, bool w4a4, bool qkv);
 hipError_t launch_block_w4a4(const BlockParams &p, int grid, size_t lds, hipStream_t s);
 int block_max_groups_per_cu_w4a4(size_t lds);
+hipError_t launch_block_qkv(const BlockParams &p, int grid, size_t lds, hipStream_t s);
+int block_max_groups_per_cu_qkv(size_t lds);
 
 }  // namespace mb

@@ -12,7 +12,7 @@ import oracle
 import routed_expert_layer_amd as rel
 import synth
 from parity import BF16, GpuBlock, assert_block, assert_close, say
-from synth.device import bits, to_tensor
+from synth.device import bits, dims_kwargs, to_tensor
 
 pytestmark = pytest.mark.gpu
 
@@ -101,3 +101,42 @@ def test_effective_norm_weight(zero_centered):
     out = rel.mb_effective_norm_weight(to_tensor(w), 1.0, zero_centered)
     torch.cuda.synchronize()
     assert (bits(out) == oracle.effective_norm_weight(w, 1.0, zero_centered)).all()
+
+
+def _block_with_qkv(g, n_out, w_qkvg):
+    """mb_moe_block with the next-QKV projection fused (qkv_rows = n_out)."""
+    d = g.blk.dims
+    dims = rel.make_dims(**dims_kwargs(d), qkv_rows=n_out)
+    wt = dict(g.wt, next_qkv_w=to_tensor(w_qkvg))
+    ws = rel.workspace(dims)
+    stream = g.stream0.clone()
+    x_next = torch.zeros((d.rows, d.hidden), dtype=BF16, device="cuda")
+    qkvg = torch.zeros((d.rows, n_out), dtype=BF16, device="cuda")
+    rel.mb_moe_block(dims, g.x, rel.make_weights(**wt), stream, x_next, ws, taps=rel.make_taps(qkvg=qkvg))
+    torch.cuda.synchronize()
+    assert int(ws[4:8].cpu().view(torch.int32)[0]) == 0, "block kernel aborted a wait"
+    return {"stream": stream.cpu().numpy(), "x_next": bits(x_next), "qkvg": bits(qkvg)}, (dims, wt, ws)
+
+
+@pytest.mark.parametrize("case,n_out", [("c1", QKVG_C1), ("b37", 1040), ("c2", 2048)])
+def test_fused_next_qkv(case, n_out):
+    """The block with the projection fused: the block's own outputs bit-identical
+    to the block without it, qkvg within the bf16 tolerance of the oracle's
+    projection of the GPU's x_next, and a second call on the same workspace
+    bit-identical to the first (the tile counters are left at zero)."""
+    import numpy as np
+    if case == "b37":
+        blk = synth.make_block("c0", seed=47, dims=synth.Dims(37, 512, 384, 640, 16, 4, "sigmoid", 2.5, None, 1e-20))
+    else:
+        blk = synth.make_block(case)
+    d = blk.dims
+    w_qkvg = synth.make_attn_side(1, d.hidden, n_out, 91)["w_qkvg"]
+    say(f"[gpu] fused next qkv: {case} rows {d.rows} H {d.hidden} qkv_rows {n_out}")
+    g = GpuBlock(blk)
+    plain = g.run_block()
+    got, (dims, wt, ws) = _block_with_qkv(g, n_out, w_qkvg)
+    assert np.array_equal(got["stream"], plain["stream"])
+    assert np.array_equal(got["x_next"], plain["x_next"])
+    assert_close(got["qkvg"], oracle.next_qkv(got["x_next"], w_qkvg), f"{case}: fused qkvg")
+    again, _ = _block_with_qkv(g, n_out, w_qkvg)
+    assert np.array_equal(again["qkvg"], got["qkvg"])
