@@ -193,7 +193,34 @@ def sweep(args) -> int:
     q = torch.empty((b16, NQ), dtype=torch.bfloat16, device=dev)
     us = timed(lambda i: rel.mb_next_qkv(d16, xo, wq[i % 4], q, ws16), 500, 20)
     report_bytes("next qkv projection b=16 H=4096 -> 10240", b16, us, NQ * H16 * 2 + b16 * H16 * 2 + b16 * NQ * 2)
-    del wq, tp, ws16
+    # The c1 block followed by the next QKV projection: fused into its launch
+    # (mb_dims.qkv_rows) against a second launch (mb_next_qkv); two c1 weight
+    # sets and two projection weights rotated (about 0.5 GB, past the
+    # Infinity Cache).
+    blocks = [synth.make_block("c1", seed=s) for s in (1, 1001)]
+    dq = rel.make_dims(**dims_kwargs(blocks[0].dims), qkv_rows=NQ)
+    dims1, tensors1, weights1 = prepare(blocks)
+    for i, t in enumerate(tensors1):
+        t["next_qkv_w"] = wq[i]
+    weights_q = [rel.make_weights(**t) for t in tensors1]
+    x1, s1 = to_tensor(blocks[0].x, dev), to_tensor(blocks[0].stream, dev)
+    wsq = rel.workspace(dq, dev)
+    xn1 = torch.empty((b16, H16), dtype=torch.bfloat16, device=dev)
+    tq = rel.make_taps(qkvg=q)
+    bytes_block = float(np.mean([algorithmic_bytes(blocks[0].dims, n_active(dims1, x1, w, s1, wsq))
+                                 for w in weights1]))
+    us = timed(lambda i: rel.mb_moe_block(dims1, x1, weights1[i % 2], s1, xn1, wsq), 500, 20)
+    report_bytes("c1 block alone (two weight sets)", b16, us, bytes_block)
+    us = timed(lambda i: rel.mb_moe_block(dq, x1, weights_q[i % 2], s1, xn1, wsq, taps=tq), 500, 20)
+    report_bytes("c1 block + next qkv 10240 fused in its launch", b16, us, bytes_block + NQ * H16 * 2 + b16 * NQ * 2)
+
+    def two(i):
+        rel.mb_moe_block(dims1, x1, weights1[i % 2], s1, xn1, wsq)
+        rel.mb_next_qkv(dims1, xn1, wq[i % 2], q, wsq)
+
+    us = timed(two, 500, 20)
+    report_bytes("c1 block, then next qkv 10240 as a second launch", b16, us, bytes_block + NQ * H16 * 2 + b16 * NQ * 2)
+    del wq, tp, ws16, blocks, tensors1, weights1, weights_q, wsq
     torch.cuda.empty_cache()
     if args.steps_around_only:
         return 0
