@@ -226,3 +226,21 @@ def test_effective_norm_weight_checks_arguments():
     assert L.mb_effective_norm_weight(FAKE, 0, 1.0, 1, FAKE, None) == MB_ERR_DIMS
     assert L.mb_effective_norm_weight(FAKE, 8, float("nan"), 1, FAKE, None) == MB_ERR_DIMS
     assert L.mb_effective_norm_weight(None, 8, 1.0, 1, FAKE, None) == MB_ERR_NULL
+
+
+def test_fused_qkv_options_checked_before_launch():
+    assert status_of_ws(c1_dims(qkv_rows=-16))[0] == MB_ERR_DIMS
+    assert status_of_ws(c1_dims(qkv_rows=24))[0] == MB_ERR_UNSUPPORTED
+    assert status_of_ws(c1_dims(qkv_rows=65536 + 16))[0] == MB_ERR_UNSUPPORTED
+    st, n0 = status_of_ws(c1_dims())
+    st, n1 = status_of_ws(c1_dims(qkv_rows=1024))
+    assert st == MB_OK and n1 > n0  # room for the projection's split partials
+    L = rel.lib()
+    d = c1_dims(qkv_rows=1024)
+    w = full_weights()  # no next_qkv_w
+    taps = rel.Taps(*([None] * len(rel._TAP_FIELDS)))
+    assert L.mb_moe_block(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE, ctypes.byref(taps), FAKE,
+                          1 << 40, None) == MB_ERR_NULL
+    w = full_weights(next_qkv_w=FAKE)
+    assert L.mb_moe_block(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE, None, FAKE, 1 << 40,
+                          None) == MB_ERR_NULL  # qkvg tap missing
