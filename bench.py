@@ -183,7 +183,10 @@ def sweep(args) -> int:
     side = synth.make_attn_side(b16, H16, NQ, 80)
     d16 = rel.make_dims(rows=b16, hidden=H16, pooled=2048, inter=1024, experts=64, top_k=4,
                         scoring="sigmoid", route_scale=2.5)
-    ws16 = rel.workspace(d16, dev)
+    # (A workspace sized with qkv_rows = 10240: mb_next_qkv then runs as the
+    # block kernel's projection step.)
+    ws16 = rel.workspace(rel.make_dims(rows=b16, hidden=H16, pooled=2048, inter=1024, experts=64, top_k=4,
+                                       scoring="sigmoid", route_scale=2.5, qkv_rows=NQ), dev)
     tp = {k: to_tensor(side[k], dev) for k in ("partial", "gate", "post_attn_norm_w", "pre_ffn_norm_w", "stream")}
     xo = torch.empty((b16, H16), dtype=torch.bfloat16, device=dev)
     us = timed(lambda i: rel.mb_attn_boundary(d16, tp["partial"], tp["gate"], tp["stream"], xo,

@@ -291,10 +291,13 @@ int mb_attn_boundary(const mb_dims *dims, const uint16_t *partial, const uint16_
  *   qkvg = bf16(x_next @ w_qkvg^T)                          bf16 [b, n_out]
  * x_next bf16 [b, H]; w_qkvg bf16 [n_out, H] row-major; n_out > 0 and a
  * multiple of 16 (else MB_ERR_DIMS / MB_ERR_UNSUPPORTED).  fp32 accumulation
- * split along H, the splits added in a fixed order.  The split partials go to
- * the workspace (mb_workspace_bytes of the same dims); the split is capped so
- * that they fit.  The QK norm, RoPE and KV insert of the attention's QKV front
- * are not part of this call. */
+ * split along H, the splits added in a fixed order; the split partials go to
+ * the workspace.  With a workspace of mb_workspace_bytes for these dims with
+ * qkv_rows = n_out (and act_quant 0), the projection runs as the block
+ * kernel's projection step (the one mb_moe_block fuses after the boundary);
+ * with one of mb_workspace_bytes(dims) only, as a split-K GEMM whose split is
+ * capped so that its partials fit.  The QK norm, RoPE and KV insert of the
+ * attention's QKV front are not part of this call. */
 int mb_next_qkv(const mb_dims *dims, const uint16_t *x_next, const uint16_t *w_qkvg, int32_t n_out,
                 uint16_t *qkvg, void *workspace, size_t workspace_bytes, void *stream);
 

@@ -266,6 +266,23 @@ int split_for(int ntiles, int nchunks, int slots) {
   return ks < 1 ? 1 : ks;
 }
 
+// The next-QKV projection as a step of the persistent launch: 64-feature
+// tiles, split along H to about fill the grid (each split a multiple of 32).
+void set_qkv(BlockParams &p, const mb_dims &d, const uint16_t *w_qkvg, uint16_t *qkvg, void *ws) {
+  const Layout L = layout_of(d);
+  const int groups = (d.qkv_rows + 63) / 64;
+  const int grid = device_cus() * kBlockGroupsPerCu;
+  int ks = std::max(1, std::min(kMaxSplitK, grid / groups));
+  while (ks > 1 && (d.hidden % ks != 0 || (d.hidden / ks) % 32 != 0)) --ks;
+  p.qkv_w = w_qkvg;
+  p.qkvg = qkvg;
+  p.qkv_rows = d.qkv_rows;
+  p.qkv_ks = ks;
+  p.n_qkv = groups * ks;
+  p.qkv_part = at<float>(ws, L.qkv_part);
+  p.qkv_cnt = at<unsigned>(ws, L.qkv_cnt);
+}
+
 // Which steps one launch of the persistent kernel runs.
 struct Steps {
   bool router = false;       // router logits (else given, or not needed)
@@ -521,20 +538,9 @@ int mb_moe_block(const mb_dims *dims, const uint16_t *x, const mb_weights *w, fl
   p.timeline = tp.timeline;
   if (tp.act) p.act = tp.act;
   if (d.qkv_rows > 0) {
-    // The next-QKV projection fused after the boundary: 64-feature tiles,
-    // split along H to about fill the grid (each split a multiple of 32).
+    // The next-QKV projection fused after the boundary.
     MB_TRY(need({w->next_qkv_w, tp.qkvg}));
-    const int groups = (d.qkv_rows + 63) / 64;
-    const int grid = device_cus() * kBlockGroupsPerCu;
-    int ks = std::max(1, std::min(kMaxSplitK, grid / groups));
-    while (ks > 1 && (d.hidden % ks != 0 || (d.hidden / ks) % 32 != 0)) --ks;
-    p.qkv_w = w->next_qkv_w;
-    p.qkvg = tp.qkvg;
-    p.qkv_rows = d.qkv_rows;
-    p.qkv_ks = ks;
-    p.n_qkv = groups * ks;
-    p.qkv_part = at<float>(ws, L.qkv_part);
-    p.qkv_cnt = at<unsigned>(ws, L.qkv_cnt);
+    set_qkv(p, d, w->next_qkv_w, tp.qkvg, ws);
   }
   bool used = false;
   MB_TRY(run_fused(p, st, s, &used));
@@ -587,7 +593,21 @@ int mb_next_qkv(const mb_dims *dims, const uint16_t *x_next, const uint16_t *w_q
   if (n_out % 16) return MB_ERR_UNSUPPORTED;
   MB_TRY(need({x_next, w_qkvg, qkvg}));
   MB_TRY(check_ws(dims, workspace, workspace_bytes));
-  // Split partials [ks][b][n_out] fp32 in the workspace's partial area.
+  // The persistent kernel's projection step alone (no boundary to wait for),
+  // with its partials in the workspace sized for these dims and n_out.
+  {
+    mb_dims dq = *dims;
+    dq.qkv_rows = n_out;
+    if (dq.act_quant == 0 && layout_of(dq).total <= workspace_bytes && n_out <= 64 * kMaxQkvGroups) {
+      BlockParams p = base_params(dq, nullptr, workspace);
+      p.x_next = const_cast<uint16_t *>(x_next);
+      set_qkv(p, dq, w_qkvg, qkvg, workspace);
+      bool used = false;
+      MB_TRY(run_fused(p, Steps{}, (hipStream_t)stream, &used));
+      if (used) return MB_OK;
+    }
+  }
+  // Else the split-K GEMM, its partials [ks][b][n_out] fp32 in the partial area.
   const Layout L = layout_of(*dims);
   const size_t per_split = (size_t)dims->rows * n_out * 4;
   const size_t room = (size_t)kMaxSplitK * dims->rows * std::max(dims->pooled, dims->hidden) * 4;  // its size

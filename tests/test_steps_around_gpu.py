@@ -26,6 +26,11 @@ def _dims(rows, hidden, pooled=2048):
                          scoring="sigmoid", route_scale=2.5)
 
 
+def _dims_q(rows, hidden, n_out):
+    return rel.make_dims(rows=rows, hidden=hidden, pooled=2048, inter=1024, experts=64, top_k=4,
+                         scoring="sigmoid", route_scale=2.5, qkv_rows=n_out)
+
+
 def _attn(rows, hidden, seed, norm_weights=True):
     a = synth.make_attn_side(rows, hidden, 16, seed, norm_weights)
     say(f"[gpu] attention boundary rows {rows} H {hidden} norms {norm_weights}")
@@ -48,13 +53,15 @@ def test_attn_boundary(rows, hidden, norms):
     _attn(rows, hidden, 50 + rows, norms)
 
 
+@pytest.mark.parametrize("persistent", [False, True])
 @pytest.mark.parametrize("rows,hidden,n_out", [(16, 4096, QKVG_C1), (37, 4096, 1040), (1, 4096, 16),
                                                (64, 7168, 2048)])
-def test_next_qkv(rows, hidden, n_out):
+def test_next_qkv(rows, hidden, n_out, persistent):
     a = synth.make_attn_side(rows, hidden, n_out, 60 + rows)
-    say(f"[gpu] next qkv rows {rows} H {hidden} n_out {n_out}")
+    say(f"[gpu] next qkv rows {rows} H {hidden} n_out {n_out} persistent {persistent}")
     d = _dims(rows, hidden)
-    ws = rel.workspace(d)
+    # A workspace sized with qkv_rows = n_out selects the block kernel's projection step.
+    ws = rel.workspace(_dims_q(rows, hidden, n_out) if persistent else d)
     x = to_tensor(a["partial"])  # any bf16 [rows, H] stands for x_next
     q = torch.zeros((rows, n_out), dtype=BF16, device="cuda")
     rel.mb_next_qkv(d, x, to_tensor(a["w_qkvg"]), q, ws)
