@@ -297,7 +297,7 @@ def main() -> int:
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
-              "(the block has no multi-GPU path in this build)", file=sys.stderr)
+              "(the block runs on one GPU: it has no multi-GPU path)", file=sys.stderr)
         return 2
 
     if args.sweep:
