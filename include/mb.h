@@ -94,8 +94,7 @@ enum {
  * qkv_rows 0: mb_moe_block ends at the boundary.  qkv_rows > 0 (a multiple
  * of 16, at most 65536): mb_moe_block also runs the next layer's QKV
  * projection of x_next (as mb_next_qkv, with w->next_qkv_w bf16
- * [qkv_rows, H]) in the same launch, into taps->qkvg (both required).
- * act_quant 1 together with qkv_rows > 0 is MB_ERR_UNSUPPORTED. */
+ * [qkv_rows, H]) in the same launch, into taps->qkvg (both required). */
 typedef struct {
   int32_t rows, hidden, pooled, inter, experts, top_k;
   int32_t scoring;

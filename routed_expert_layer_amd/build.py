@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmb.so")
-SOURCES = ["api.hip", "block.hip", "block_w4a4.hip", "block_qkv.hip", "route.hip", "gemm_bf16.hip", "experts.hip", "boundary.hip", "pack.hip"]
+SOURCES = ["api.hip", "block.hip", "block_w4a4.hip", "block_qkv.hip", "block_w4a4_qkv.hip", "route.hip", "gemm_bf16.hip", "experts.hip", "boundary.hip", "pack.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -52,7 +52,8 @@ def build(verbose: bool = False) -> str:
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # -z defs: an unresolved symbol fails the link rather than the first call.
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

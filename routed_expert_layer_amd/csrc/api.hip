@@ -305,7 +305,6 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   const size_t route_bytes = route_lds_bytes(p.b, p.k, p.E);
   const size_t lds = route_bytes + kBlockScratchBytes;
   if (lds > 64 * 1024) return none;
-  if (p.n_qkv > 0 && p.w4a4) return MB_ERR_UNSUPPORTED;  // no kernel instance for both
   const int occ = block_max_groups_per_cu(lds, p.w4a4 != 0, p.n_qkv > 0);
   const int cus = device_cus();
   if (occ < 1 || cus < 1) return none;

@@ -1988,10 +1988,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 // An ordinary launch: the host sizes the grid to what the device holds at
 // once.  Should some workgroups only start after others finished work on
 // another kernel, the waits merely take longer (every one is bounded).
-// The W4A4 kernel and the kernel with the fused next-QKV projection are
-// built from this file in translation units of their own (block_w4a4.hip,
-// block_qkv.hip): sharing one code object moved the bf16 kernel's code and
-// cost it ~0.6 us per launch.
+// The W4A4 kernel, the kernel with the fused next-QKV projection and the
+// kernel with both are built from this file in translation units of their own
+// (block_w4a4.hip, block_qkv.hip, block_w4a4_qkv.hip): sharing one code object
+// moved the bf16 kernel's code and cost it ~0.6 us per launch.
 #if !defined(MB_BLOCK_W4A4) && !defined(MB_BLOCK_QKV)
 hipError_t launch_block(const BlockParams &p, int grid, size_t lds, hipStream_t s) {
   if (p.w4a4) return launch_block_w4a4(p, grid, lds, s);
@@ -2001,26 +2001,28 @@ hipError_t launch_block(const BlockParams &p, int grid, size_t lds, hipStream_t 
 }
 
 int block_max_groups_per_cu(size_t lds, bool w4a4, bool qkv) {
-  if (w4a4) return block_max_groups_per_cu_w4a4(lds);
+  if (w4a4) return block_max_groups_per_cu_w4a4(lds, qkv);
   if (qkv) return block_max_groups_per_cu_qkv(lds);
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_kernel<false>, kThreads, lds) != hipSuccess)
     return 0;
   return n;
 }
-#elif defined(MB_BLOCK_W4A4)
+#elif defined(MB_BLOCK_W4A4) && !defined(MB_BLOCK_QKV)
 hipError_t launch_block_w4a4(const BlockParams &p, int grid, size_t lds, hipStream_t s) {
+  if (p.n_qkv > 0) return launch_block_w4a4_qkv(p, grid, lds, s);
   hipLaunchKernelGGL(block_kernel<true>, dim3(grid), dim3(kThreads), lds, s, p);
   return hipGetLastError();
 }
 
-int block_max_groups_per_cu_w4a4(size_t lds) {
+int block_max_groups_per_cu_w4a4(size_t lds, bool qkv) {
+  if (qkv) return block_max_groups_per_cu_w4a4_qkv(lds);
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_kernel<true>, kThreads, lds) != hipSuccess)
     return 0;
   return n;
 }
-#else
+#elif defined(MB_BLOCK_QKV) && !defined(MB_BLOCK_W4A4)
 hipError_t launch_block_qkv(const BlockParams &p, int grid, size_t lds, hipStream_t s) {
   hipLaunchKernelGGL((block_kernel<false, true>), dim3(grid), dim3(kThreads), lds, s, p);
   return hipGetLastError();
@@ -2029,6 +2031,18 @@ hipError_t launch_block_qkv(const BlockParams &p, int grid, size_t lds, hipStrea
 int block_max_groups_per_cu_qkv(size_t lds) {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_kernel<false, true>, kThreads, lds) != hipSuccess)
+    return 0;
+  return n;
+}
+#else
+hipError_t launch_block_w4a4_qkv(const BlockParams &p, int grid, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL((block_kernel<true, true>), dim3(grid), dim3(kThreads), lds, s, p);
+  return hipGetLastError();
+}
+
+int block_max_groups_per_cu_w4a4_qkv(size_t lds) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_kernel<true, true>, kThreads, lds) != hipSuccess)
     return 0;
   return n;
 }

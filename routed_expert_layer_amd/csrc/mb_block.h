@@ -212,8 +212,10 @@ constexpr size_t kBlockScratchBytes = kProjScratchBytes > kStageBytes ? kProjScr
 hipError_t launch_block(const BlockParams &p, int grid, size_t lds, hipStream_t s);
 int block_max_groups_per_cu(size_t lds, bool w4a4, bool qkv);
 hipError_t launch_block_w4a4(const BlockParams &p, int grid, size_t lds, hipStream_t s);
-int block_max_groups_per_cu_w4a4(size_t lds);
+int block_max_groups_per_cu_w4a4(size_t lds, bool qkv);
 hipError_t launch_block_qkv(const BlockParams &p, int grid, size_t lds, hipStream_t s);
+hipError_t launch_block_w4a4_qkv(const BlockParams &p, int grid, size_t lds, hipStream_t s);
+int block_max_groups_per_cu_w4a4_qkv(size_t lds);
 int block_max_groups_per_cu_qkv(size_t lds);
 
 }  // namespace mb

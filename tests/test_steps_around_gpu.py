@@ -147,3 +147,31 @@ def test_fused_next_qkv(case, n_out):
     assert_close(got["qkvg"], oracle.next_qkv(got["x_next"], w_qkvg), f"{case}: fused qkvg")
     again, _ = _block_with_qkv(g, n_out, w_qkvg)
     assert np.array_equal(again["qkvg"], got["qkvg"])
+
+
+def test_fused_next_qkv_with_w4a4():
+    """Both options at once (c1): the W4A4 block's own outputs bit-identical
+    with and without the fused projection, qkvg against the oracle on the
+    GPU's x_next."""
+    import numpy as np
+    blk = synth.make_block("c1")
+    d = blk.dims
+    w_qkvg = synth.make_attn_side(1, d.hidden, 1024, 92)["w_qkvg"]
+    say("[gpu] fused next qkv with W4A4 experts (c1, qkv_rows 1024)")
+    g = GpuBlock(blk)
+    g.use_packed()
+    outs = []
+    for qkv_rows in (0, 1024):
+        dims = rel.make_dims(**dims_kwargs(d), act_quant=1, qkv_rows=qkv_rows)
+        wt = dict(g.wt, next_qkv_w=to_tensor(w_qkvg))
+        ws = rel.workspace(dims)
+        stream = g.stream0.clone()
+        x_next = torch.zeros((d.rows, d.hidden), dtype=BF16, device="cuda")
+        qkvg = torch.zeros((d.rows, 1024), dtype=BF16, device="cuda")
+        rel.mb_moe_block(dims, g.x, rel.make_weights(**wt), stream, x_next, ws,
+                         taps=rel.make_taps(qkvg=qkvg if qkv_rows else None))
+        torch.cuda.synchronize()
+        assert int(ws[4:8].cpu().view(torch.int32)[0]) == 0, "block kernel aborted a wait"
+        outs.append((stream.cpu().numpy(), bits(x_next), bits(qkvg)))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    assert_close(outs[1][2], oracle.next_qkv(outs[1][1], w_qkvg), "W4A4 fused qkvg")
