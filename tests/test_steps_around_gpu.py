@@ -125,7 +125,7 @@ def _block_with_qkv(g, n_out, w_qkvg):
     return {"stream": stream.cpu().numpy(), "x_next": bits(x_next), "qkvg": bits(qkvg)}, (dims, wt, ws)
 
 
-@pytest.mark.parametrize("case,n_out", [("c1", QKVG_C1), ("b37", 1040), ("c2", 2048)])
+@pytest.mark.parametrize("case,n_out", [("c1", QKVG_C1), ("b37", 1040), ("c2", 2048), ("b1", 16)])
 def test_fused_next_qkv(case, n_out):
     """The block with the projection fused: the block's own outputs bit-identical
     to the block without it, qkvg within the bf16 tolerance of the oracle's
@@ -134,6 +134,8 @@ def test_fused_next_qkv(case, n_out):
     import numpy as np
     if case == "b37":
         blk = synth.make_block("c0", seed=47, dims=synth.Dims(37, 512, 384, 640, 16, 4, "sigmoid", 2.5, None, 1e-20))
+    elif case == "b1":
+        blk = synth.make_block("c0", seed=48, dims=synth.Dims(1, 256, 128, 256, 8, 2, "sigmoid", 2.5, None, 1e-20))
     else:
         blk = synth.make_block(case)
     d = blk.dims
