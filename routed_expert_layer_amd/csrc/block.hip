@@ -16,7 +16,7 @@
 //        up       (expert, 16 act columns) act = bf16(silu(g) * u)        [w13]
 //        down     (expert, 32 features)    y, per-tile sums of squares    [w2]
 //   4. workgroup tasks after the experts
-//        finalize (row, 512 features)      moe_out = bf16(sum_j w_j yn_j)
+//        finalize (row, 1024 features)     moe_out = bf16(sum_j w_j yn_j)
 //        unpool   (16 or 64 features,      u = moe_out Wu^T, K-split
 //                  K split)                  partials                      [Wu]
 //        boundary (row)                    stream, x_next

@@ -78,7 +78,7 @@ constexpr size_t kSetLines = sync_line_logits((kSyncMaxRows + kRouterRowBlock - 
 __host__ __device__ constexpr size_t sync_line_set(int set) { return 1 + kGenLines + (size_t)set * kSetLines; }
 constexpr size_t kSyncWords = sync_line_set(2) * kLine;
 
-constexpr int kFinChunk = 512;  // features per finalize task
+constexpr int kFinChunk = 1024;  // features per finalize task (4 per thread: the most one task covers)
 constexpr int kMaxPoolSplit = 32;  // contraction splits of the pooler
 constexpr int kMoeReplicas = 8;  // copies of the MoE output for the unpooler tasks
 constexpr int kTimelineSlots = 32;
