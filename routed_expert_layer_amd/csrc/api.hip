@@ -51,7 +51,20 @@ Layout layout_of(const mb_dims &d) {
   L.pool_part = take((size_t)kMaxPoolSplit * b * P * 4);
   L.unpool_part = take((size_t)kMaxSplitK * b * H * 4);
   L.qkv_part = take((size_t)kMaxSplitK * b * (size_t)d.qkv_rows * 4);
-  L.total = o;
+  // Tagged hand-off words of the block kernel (8 bytes each).
+  size_t t = 0;
+  auto ttake = [&](size_t bytes) {
+    const size_t at = t;
+    t = align256(t + bytes);
+    return at;
+  };
+  L.t_logits = ttake(b * E * 8);
+  L.t_routes = ttake((size_t)kRouteReps * 2 * R * 8);
+  L.t_h = ttake(b * P * 4);
+  L.t_hn = ttake(b * P * 4);
+  L.t_act = ttake(R * I * 4);
+  L.tagged = t;
+  L.total = o + t;
   return L;
 }
 
@@ -196,8 +209,9 @@ int device_cus() {
 }
 
 // Fill the sizes, scalars and workspace pointers every phase set shares.
-BlockParams base_params(const mb_dims &d, const mb_weights *w, void *ws) {
+BlockParams base_params(const mb_dims &d, const mb_weights *w, void *ws, size_t ws_bytes) {
   const Layout L = layout_of(d);
+  const size_t tb = tagged_base(L, ws_bytes);
   BlockParams p{};
   p.b = d.rows;
   p.H = d.hidden;
@@ -252,6 +266,11 @@ BlockParams base_params(const mb_dims &d, const mb_weights *w, void *ws) {
   p.route_list = at<int32_t>(ws, L.route_list);
   p.active = at<int32_t>(ws, L.active);
   p.n_active = at<int32_t>(ws, L.n_active);
+  p.logits_t = at<uint32_t>(ws, tb + L.t_logits);
+  p.routes_t = at<uint32_t>(ws, tb + L.t_routes);
+  p.h_t = at<uint32_t>(ws, tb + L.t_h);
+  p.hn_t = at<uint32_t>(ws, tb + L.t_hn);
+  p.act_t = at<uint32_t>(ws, tb + L.t_act);
   return p;
 }
 
@@ -359,7 +378,7 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   p.n_route = n_route;
   p.n_pool = st.pool ? p.n_pool_tiles * p.pool_ks : 0;
   p.n_prenorm = n_prenorm;
-  p.h_producers = st.pool ? (p.pre_norm_w ? p.b : p.n_pool_tiles) : 0;
+  p.h_tagged = st.pool ? 1 : 0;
   p.has_up = st.experts ? 1 : 0;
   p.n_fin = n_fin;
   p.n_unpool = st.unpool ? (p.unpool_wide ? (p.H + 63) / 64 : p.H / 16) * p.unpool_ks : 0;
@@ -392,7 +411,7 @@ int mb_route(const mb_dims *dims, const uint16_t *x, const mb_weights *w, float 
   MB_TRY(need({topk_ids, topk_w, count, offset, route_list, active, n_active}));
   if (flags) MB_TRY(need({logits}));
   MB_TRY(check_ws(dims, workspace, workspace_bytes));
-  BlockParams p = base_params(*dims, w, workspace);
+  BlockParams p = base_params(*dims, w, workspace, workspace_bytes);
   Steps st;
   st.router = !(flags & MB_LOGITS_IN);
   st.routing_out = true;
@@ -420,11 +439,12 @@ int mb_pool(const mb_dims *dims, const uint16_t *x, const mb_weights *w, uint16_
   MB_TRY(check_weights_pool(w));
   MB_TRY(need({x, h}));
   MB_TRY(check_ws(dims, workspace, workspace_bytes));
-  BlockParams p = base_params(*dims, w, workspace);
+  BlockParams p = base_params(*dims, w, workspace, workspace_bytes);
   Steps st;
   st.pool = true;
   p.x = x;
   p.h = h;
+  p.h_plain = 1;
   bool used = false;
   MB_TRY(run_fused(p, st, (hipStream_t)stream, &used));
   if (used) return MB_OK;
@@ -440,7 +460,7 @@ int mb_experts(const mb_dims *dims, const uint16_t *h, const int32_t *topk_ids,
   MB_TRY(check_weights_experts(w));
   MB_TRY(need({h, topk_ids, topk_w, count, offset, route_list, active, n_active, moe_out}));
   MB_TRY(check_ws(dims, workspace, workspace_bytes));
-  BlockParams p = base_params(*dims, w, workspace);
+  BlockParams p = base_params(*dims, w, workspace, workspace_bytes);
   Steps st;
   st.experts = true;
   st.route_given = true;
@@ -470,7 +490,7 @@ int mb_unpool_boundary(const mb_dims *dims, const uint16_t *moe_out, const mb_we
   MB_TRY(maybe({u_out}));
   MB_TRY(check_ws(dims, workspace, workspace_bytes));
   uint16_t *u = u_out ? u_out : at<uint16_t>(workspace, layout_of(*dims).u);
-  BlockParams p = base_params(*dims, w, workspace);
+  BlockParams p = base_params(*dims, w, workspace, workspace_bytes);
   Steps st;
   st.unpool = true;
   p.moe_out = const_cast<uint16_t *>(moe_out);
@@ -515,7 +535,7 @@ int mb_moe_block(const mb_dims *dims, const uint16_t *x, const mb_weights *w, fl
   uint16_t *h = tp.h ? tp.h : at<uint16_t>(ws, L.h);
   uint16_t *moe_out = tp.moe_out ? tp.moe_out : at<uint16_t>(ws, L.moe_out);
   uint16_t *u = tp.u ? tp.u : at<uint16_t>(ws, L.u);
-  BlockParams p = base_params(d, w, ws);
+  BlockParams p = base_params(d, w, ws, workspace_bytes);
   Steps st;
   st.router = st.pool = st.experts = st.unpool = true;
   st.routing_out = tp.topk_ids || tp.topk_w || tp.count || tp.offset || tp.route_list || tp.active ||
@@ -535,7 +555,8 @@ int mb_moe_block(const mb_dims *dims, const uint16_t *x, const mb_weights *w, fl
   p.stream = stream;
   p.x_next = x_next;
   p.timeline = tp.timeline;
-  if (tp.act) p.act = tp.act;
+  p.act_tap = tp.act;
+  p.h_plain = tp.h ? 1 : 0;
   if (d.qkv_rows > 0) {
     // The next-QKV projection fused after the boundary.
     MB_TRY(need({w->next_qkv_w, tp.qkvg}));
@@ -598,7 +619,7 @@ int mb_next_qkv(const mb_dims *dims, const uint16_t *x_next, const uint16_t *w_q
     mb_dims dq = *dims;
     dq.qkv_rows = n_out;
     if (dq.act_quant == 0 && layout_of(dq).total <= workspace_bytes && n_out <= 64 * kMaxQkvGroups) {
-      BlockParams p = base_params(dq, nullptr, workspace);
+      BlockParams p = base_params(dq, nullptr, workspace, workspace_bytes);
       p.x_next = const_cast<uint16_t *>(x_next);
       set_qkv(p, dq, w_qkvg, qkvg, workspace);
       bool used = false;

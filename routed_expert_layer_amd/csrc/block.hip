@@ -26,14 +26,15 @@
 // only for the work whose output it reads: routing for the logits (or the
 // route tasks), up for the pooler (or pre-norm), down for the up units of its
 // expert, finalize for the down units of its row's experts, unpool for the
-// finalize tasks, boundary for the unpool tasks.  Producers add to counters
-// after their coherent stores completed and consumers poll them (mb_block.h:
-// the layout, the two counter sets that alternate from launch to launch, and
-// copies of widely awaited counters).  Every dependency points
-// to earlier work in this
-// order and the grid is what the device holds at once, so the earliest
-// unfinished work can always run and the launch completes; every wait is also
-// bounded.
+// finalize tasks, boundary for the unpool tasks.  The logits, the routes, h
+// and act go from producer to consumer as tagged words (payload and the
+// launch's tag in one 8-byte store), which the consumer polls directly; the
+// later steps use dependency counters that producers add to after their
+// coherent stores completed (mb_block.h: the layout, the two counter sets
+// that alternate from launch to launch, and copies of widely awaited
+// counters).  Every dependency points to earlier work in this order and the
+// grid is what the device holds at once, so the earliest unfinished work can
+// always run and the launch completes; every wait is also bounded.
 //
 // Data one workgroup hands to another goes through coherent (sc1) buffer
 // accesses; weights are streamed with non-temporal loads, each wave keeping
@@ -96,6 +97,9 @@ struct Deps {
     return s + (sync_line_set((int)set) + i) * kLine;
   }
   __device__ unsigned *abort_word() const { return s + 1; }
+  // The tag of this launch's hand-off words (the generation + 1, never the
+  // 0 of a zero-filled workspace within 2^32 launches).
+  __device__ unsigned tag() const { return gen + 1u; }
   __device__ unsigned *ctr(int i, int rep = 0) const { return line(sync_line_ctr(i, rep)); }
   // The first stripe of the copy of counter i that this workgroup (or wave:
   // index w) polls.
@@ -239,6 +243,47 @@ __device__ __forceinline__ void wave_wait_step(const Deps &d, int i, int target)
     poll_sum_ge(d, d.mine(i, blockIdx.x * kWaves + tid() / MB_WAVE), stripes(i), (unsigned)target);
 }
 
+// Tagged hand-off words: 8 bytes, the payload first and then the tag of the
+// launch that wrote it, stored and loaded whole with coherent accesses (an
+// aligned 8-byte access is single-copy atomic), so a consumer that reads this
+// launch's tag reads the payload stored with it.  A consumer polls the data
+// itself: no store-completion wait, counter or second load on the way.  Words
+// of earlier launches carry their own (older) tags.
+__device__ __forceinline__ void st_tagged(rsrc_t r, uint32_t off, uint32_t v, uint32_t tag) {
+  st_co8(r, off, u32x2_t{v, tag});
+}
+
+// A polling wave, every 256 polls: whether to stop waiting (the abort word
+// is up, or this wait has run out of polls and raises it).
+__device__ __forceinline__ bool give_up(const Deps &d, unsigned &spins) {
+  if ((++spins & 255u) != 0) return false;
+  if (__hip_atomic_load(d.abort_word(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return true;
+  if (spins > kSpinLimit) {
+    if (tid() % MB_WAVE == 0) store_co(d.abort_word(), 1u);
+    return true;
+  }
+  return false;
+}
+
+// One wave: until every word its lanes hold (v[i] from offset off[i]; kOob:
+// no word) carries this launch's tag, request again the words that do not.
+// Bounded like poll_ge.
+template <int N>
+__device__ __forceinline__ void await_tagged(const Deps &d, rsrc_t r, const uint32_t (&off)[N], u32x2_t (&v)[N]) {
+  const uint32_t tag = d.tag();
+  unsigned spins = 0;
+  while (true) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < N; ++i) ok = ok && (off[i] == kOob || v[i][1] == tag);
+    if (__all((int)ok) || give_up(d, spins)) return;
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (off[i] != kOob && v[i][1] != tag) v[i] = ld_co8(r, off[i]);
+  }
+}
+
 // Tracing: workgroup thread 0 stamps the 100 MHz real-time counter at the
 // start (slot 0), when it enters its first task of each step (router 1,
 // route 2, pool 3, prenorm 4, finalize 8, unpool 9, boundary 10), when its
@@ -328,10 +373,10 @@ __device__ __forceinline__ void router_task(const BlockParams &p, unsigned &gen,
     double v = g[0];
     for (int i = 1; i < 16; ++i) v += g[i];
     const size_t te = (size_t)(t0 + tid()) * p.E + e;
-    st_co4(make_rsrc(p.logits_f), (uint32_t)(te * 4), __float_as_uint((float)v));
+    const Deps d{p.sync, gen};
+    st_tagged(make_rsrc(p.logits_t), (uint32_t)(te * 8), __float_as_uint((float)v), d.tag());
   }
-  const Deps d{p.sync, gen};
-  signal(d.logits(t0 / RB));
+  __syncthreads();  // (the workgroup's next task reuses the LDS)
   stamp(p, 22);
 }
 
@@ -409,21 +454,15 @@ __device__ __forceinline__ void router_task_multi(const BlockParams &p, unsigned
     for (int ww = 1; ww < kWaves; ++ww) v += red[ww * XE * RB + tid()];
     if (t0 + r < p.b && e0 + j < p.E) {
       const size_t te = (size_t)(t0 + r) * p.E + e0 + j;
-      st_co4(make_rsrc(p.logits_f), (uint32_t)(te * 4), __float_as_uint((float)v));
+      const Deps d{p.sync, gen};
+      st_tagged(make_rsrc(p.logits_t), (uint32_t)(te * 8), __float_as_uint((float)v), d.tag());
     }
   }
-  const Deps d{p.sync, gen};
-  signal(d.logits(t0 / RB));
+  __syncthreads();  // (the workgroup's next task reuses the LDS)
   stamp(p, 22);
 }
 
 // ---------------------------------------------------------------- routing
-
-// fp32 logit (t, e): given by the caller, or the router's.
-__device__ __forceinline__ float logit_of(const BlockParams &p, rsrc_t rl, int t, int e) {
-  if (p.logits_in) return p.logits[(size_t)t * p.E + e];
-  return __uint_as_float(ld_co4(rl, (uint32_t)(((size_t)t * p.E + e) * 4)));
-}
 
 // Order key of a candidate: larger is better.  Valid numbers above NaN, then
 // the larger selection key, then the lower expert id; -0 counts as +0.
@@ -556,44 +595,72 @@ __device__ __forceinline__ void route_one(const BlockParams &p, const float (&l)
   out_w = q * p.route_scale;
 }
 
-// Rows t_begin..t_end-1, one per wave in turn, from their fp32 logits; the
-// ids and weights go to LDS.  The expert biases are requested before `wait`
-// (which returns once the logits are written).
-template <int PER, typename Wait>
-__device__ __forceinline__ void route_rows(const BlockParams &p, const RouteLds &R, int t_begin, int t_end,
-                                           Wait wait) {
+// Rows t_begin..t_end-1, one per wave in turn, from their fp32 logits: the
+// caller's, or the router's tagged words, polled until this launch's are all
+// there (the expert biases are requested first).  The ids and weights go out
+// as tagged words to every copy of the routes, and to the caller's routing
+// outputs (ids, weights, logits) when it asked for them.
+template <int PER>
+__device__ __forceinline__ void route_rows(const BlockParams &p, const Deps &d, int t_begin, int t_end) {
   const int lane = tid() % MB_WAVE;
-  const rsrc_t rl = make_rsrc(p.logits_f), rb = make_rsrc(p.bias);
+  const rsrc_t rl = make_rsrc(p.logits_t), rb = make_rsrc(p.bias), rr = make_rsrc(p.routes_t);
   float bias[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + MB_WAVE * i;
     bias[i] = __uint_as_float(ld_b32(rb, e < p.E ? (uint32_t)e * 4u : kOob));
   }
-  wait();
+  const int R2 = 2 * p.b * p.k;
   for (int t = t_begin + (int)(tid() / MB_WAVE); t < t_end; t += kWaves) {
     float l[PER];
+    if (p.logits_in) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = lane + MB_WAVE * i;
-      l[i] = e < p.E ? logit_of(p, rl, t, e) : 0.f;
+      for (int i = 0; i < PER; ++i) {
+        const int e = lane + MB_WAVE * i;
+        l[i] = e < p.E ? p.logits[(size_t)t * p.E + e] : 0.f;
+      }
+    } else {
+      uint32_t off[PER];
+      u32x2_t v[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int e = lane + MB_WAVE * i;
+        off[i] = e < p.E ? (uint32_t)(((size_t)t * p.E + e) * 8) : kOob;
+        v[i] = ld_co8(rl, off[i]);
+      }
+      await_tagged(d, rl, off, v);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        l[i] = __uint_as_float(v[i][0]);
+        const int e = lane + MB_WAVE * i;
+        if (p.logits && e < p.E) p.logits[(size_t)t * p.E + e] = l[i];
+      }
     }
+    stamp(p, 12);
     int id;
     float w;
     route_one<PER>(p, l, bias, id, w);
     if (lane < p.k) {
-      R.ids[t * p.k + lane] = id;
-      R.w[t * p.k + lane] = w;
+      const int r = t * p.k + lane;
+      const uint32_t tag = d.tag();
+#pragma unroll 1
+      for (int c = 0; c < kRouteReps; ++c) {
+        st_tagged(rr, (uint32_t)(((size_t)c * R2 + r) * 8), (uint32_t)id, tag);
+        st_tagged(rr, (uint32_t)(((size_t)c * R2 + R2 / 2 + r) * 8), __float_as_uint(w), tag);
+      }
+      if (p.routing_out) {
+        p.ids[r] = id;
+        p.wts[r] = w;
+      }
     }
   }
 }
 
-template <typename Wait>
-__device__ __forceinline__ void route_dispatch(const BlockParams &p, const RouteLds &R, int t0, int t1, Wait wait) {
+__device__ __forceinline__ void route_dispatch(const BlockParams &p, const Deps &d, int t0, int t1) {
   // The host sends larger expert counts to the per-step kernels.
-  if (p.E <= 64) route_rows<1>(p, R, t0, t1, wait);
-  else if (p.E <= 128) route_rows<2>(p, R, t0, t1, wait);
-  else route_rows<4>(p, R, t0, t1, wait);
+  if (p.E <= 64) route_rows<1>(p, d, t0, t1);
+  else if (p.E <= 128) route_rows<2>(p, d, t0, t1);
+  else route_rows<4>(p, d, t0, t1);
 }
 
 // Inclusive prefix sum over the wave's 64 lanes (DPP: row shifts 1, 2, 4, 8,
@@ -698,35 +765,19 @@ __device__ __forceinline__ void group_routes(const BlockParams &p, const RouteLd
   __syncthreads();
 }
 
-// Route task (many rows): rows 4 task .. +3, one per wave; their ids and
-// weights go out coherently for every workgroup's grouping.
-__device__ __forceinline__ void route_task(const BlockParams &p, const Deps &d, const RouteLds &R,
-                                           int task) {
+// Route task: rows 4 task .. +3, one per wave.
+__device__ __forceinline__ void route_task(const BlockParams &p, const Deps &d, int task) {
   const int t0 = task * kWaves, t1 = min(p.b, t0 + kWaves);
-  route_dispatch(p, R, t0, t1, [&]() {
-    if (p.n_logit_producers > 0)
-      wait_ge(d, d.logits(task), (unsigned)(p.router_multi ? (p.E + kRouterExperts - 1) / kRouterExperts : p.E));
-    stamp(p, 12);
-  });
+  route_dispatch(p, d, t0, t1);
   stamp(p, 14);
-  __syncthreads();
-  const rsrc_t ri = make_rsrc(p.ids), rw = make_rsrc(p.wts);
-  for (int i = tid(); i < (t1 - t0) * p.k; i += kThreads) {
-    const int r = t0 * p.k + i;
-    st_co4(ri, (uint32_t)(r * 4), (uint32_t)R.ids[r]);
-    st_co4(rw, (uint32_t)(r * 4), __float_as_uint(R.w[r]));
-  }
-  if (p.logits && !p.logits_in) {
-    const rsrc_t rl = make_rsrc(p.logits_f);
-    for (int i = tid(); i < (t1 - t0) * p.E; i += kThreads) {
-      const int t = t0 + i / p.E, e = i % p.E;
-      p.logits[(size_t)t * p.E + e] = logit_of(p, rl, t, e);
-    }
-  }
-  signal_step(d, kCtrRoute);
 }
 
-// The routing state a workgroup needs before its first expert unit.
+// Words of the tagged routes each thread polls at once.
+constexpr int kRouteBatch = 2;
+
+// The routing state a workgroup needs before its first expert unit: the
+// routes (from the caller, or polled from this workgroup's copy of the tagged
+// routes), then the grouping.
 __device__ __forceinline__ void prepare_routing(const BlockParams &p, const Deps &d, const RouteLds &R) {
   const bool out = p.routing_out && blockIdx.x == 0;
   if (p.route_given) {
@@ -742,14 +793,30 @@ __device__ __forceinline__ void prepare_routing(const BlockParams &p, const Deps
     __syncthreads();
     return;
   }
-  wait_step(d, kCtrRoute, p.n_route);
-  stamp(p, 13);
-  const rsrc_t ri = make_rsrc(p.ids), rw = make_rsrc(p.wts);
-  for (int i = tid(); i < p.b * p.k; i += kThreads) {
-    const int e = (int)ld_co4(ri, (uint32_t)(i * 4));
-    R.ids[i] = e;
-    R.w[i] = __uint_as_float(ld_co4(rw, (uint32_t)(i * 4)));
-    mark_route(p, R, i, e);
+  const int Rn = p.b * p.k, R2 = 2 * Rn;
+  const rsrc_t rr = make_rsrc(p.routes_t + (size_t)(blockIdx.x % kRouteReps) * R2 * 2);
+  for (int w0 = 0; w0 < R2; w0 += kThreads * kRouteBatch) {
+    uint32_t off[kRouteBatch];
+    u32x2_t v[kRouteBatch];
+#pragma unroll
+    for (int i = 0; i < kRouteBatch; ++i) {
+      const int w = w0 + (int)tid() + kThreads * i;
+      off[i] = w < R2 ? (uint32_t)w * 8u : kOob;
+      v[i] = ld_co8(rr, off[i]);
+    }
+    await_tagged(d, rr, off, v);
+    stamp(p, 13);
+#pragma unroll
+    for (int i = 0; i < kRouteBatch; ++i) {
+      const int w = w0 + (int)tid() + kThreads * i;
+      if (w < Rn) {
+        const int e = (int)v[i][0];
+        R.ids[w] = e;
+        mark_route(p, R, w, e);
+      } else if (w < R2) {
+        R.w[w - Rn] = __uint_as_float(v[i][0]);
+      }
+    }
   }
   __syncthreads();
   group_routes(p, R, out);
@@ -770,21 +837,23 @@ __device__ __forceinline__ int *proj_flag(unsigned char *lds) {
 // them: kCoherentA); each wave streams its own weights kWideRing chunks of
 // 32 elements ahead.  Rows go in passes of up to 64 (four 16-row MFMA
 // blocks); features and rows past the ends load zeros and are not stored.
-// With ks == 1 the result goes to `out` in bf16, else the fp32 partial to
-// part[q].  `wait` runs after the first weight requests, before the first
+// With ks == 1 the result goes to `out` in bf16 (when not NULL) and to out_t
+// as tagged words (when not NULL: two bf16 per word), else the fp32 partial
+// to part[q].  `wait` runs after the first weight requests, before the first
 // activation request.
 constexpr int kWideRing = 8;
 constexpr int kWideCols = 16 * kWaves;
 template <bool kCoherentA, typename Wait>
 __device__ __forceinline__ void proj_wide(rsrc_t ra, const uint16_t *w, int rows, int n_out, int kdim, int gi, int q,
-                                          int ks, float *part, uint16_t *out, unsigned char *stage, Wait wait) {
+                                          int ks, float *part, uint16_t *out, uint32_t *out_t, uint32_t tag,
+                                          unsigned char *stage, Wait wait) {
   const int lane = (int)(tid() % MB_WAVE), wave = (int)(tid() / MB_WAVE), g = lane >> 4, r16 = lane & 15;
   const int kr = kdim / ks, k0 = q * kr, nch = kr / 32;
   const int f = gi * kWideCols + 16 * wave + r16;  // this lane's weight row
   const rsrc_t rw = make_rsrc(w);
   const uint32_t wrow = f < n_out ? (uint32_t)(((size_t)f * kdim + k0 + 8 * g) * 2) : kOob;
   auto wload = [&](int c) { return ld_nt16(rw, (wrow != kOob && c < nch) ? wrow + (uint32_t)c * 64u : kOob); };
-  const rsrc_t ro = make_rsrc(out), rp = make_rsrc(part);
+  const rsrc_t ro = make_rsrc(out), rp = make_rsrc(part), rt = make_rsrc(out_t);
   for (int t0 = 0; t0 < rows; t0 += 64) {
     const int rp_ = min(64, rows - t0), nb = (rp_ + 15) / 16;
     // Segment length (elements, a multiple of 32 kWideRing): rows x segment fits the stage.
@@ -838,20 +907,22 @@ __device__ __forceinline__ void proj_wide(rsrc_t ra, const uint16_t *w, int rows
     for (int b = 0; b < 4; ++b) {
       const int t = t0 + 16 * b + r16;
       if (b >= nb || t >= rows || n >= n_out) continue;
-      if (ks == 1)
-        st_co8(ro, (uint32_t)(((size_t)t * n_out + n) * 2),
-               u32x2_t{pack_bf16x2(acc[b][0], acc[b][1]), pack_bf16x2(acc[b][2], acc[b][3])});
-      else
+      if (ks == 1) {
+        const uint32_t lo = pack_bf16x2(acc[b][0], acc[b][1]), hi = pack_bf16x2(acc[b][2], acc[b][3]);
+        if (out) st_co8(ro, (uint32_t)(((size_t)t * n_out + n) * 2), u32x2_t{lo, hi});
+        if (out_t) st_co16(rt, (uint32_t)(((size_t)t * n_out + n) * 4), u32x4_t{lo, tag, hi, tag});
+      } else
         st_co16(rp, (uint32_t)((((size_t)q * rows + t) * n_out + n) * 4), __builtin_bit_cast(u32x4_t, acc[b]));
     }
   }
 }
 
 // The last split of a wide tile: out[t, n] = bf16(sum over q of part[q][t][n]),
-// in split order, for the tile's 64 features and every row.
-__device__ __forceinline__ void proj_wide_sum(const float *part, uint16_t *out, int rows, int n_out, int gi,
-                                              int ks) {
-  const rsrc_t rp = make_rsrc(part), ro = make_rsrc(out);
+// in split order, for the tile's 64 features and every row; to `out` (when
+// not NULL) and as tagged words to out_t (when not NULL).
+__device__ __forceinline__ void proj_wide_sum(const float *part, uint16_t *out, uint32_t *out_t, uint32_t tag,
+                                              int rows, int n_out, int gi, int ks) {
+  const rsrc_t rp = make_rsrc(part), ro = make_rsrc(out), rt = make_rsrc(out_t);
   for (int idx = (int)tid(); idx < rows * (kWideCols / 4); idx += kThreads) {
     const int t = idx / (kWideCols / 4), n = gi * kWideCols + 4 * (idx % (kWideCols / 4));
     if (n >= n_out) continue;
@@ -866,7 +937,9 @@ __device__ __forceinline__ void proj_wide_sum(const float *part, uint16_t *out, 
       for (int u = 0; u < 8; ++u)
         if (q0 + u < ks) v = (q0 + u == 0) ? pv[u] : v + pv[u];
     }
-    st_co8(ro, (uint32_t)(((size_t)t * n_out + n) * 2), u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
+    const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+    if (out) st_co8(ro, (uint32_t)(((size_t)t * n_out + n) * 2), u32x2_t{lo, hi});
+    if (out_t) st_co16(rt, (uint32_t)(((size_t)t * n_out + n) * 4), u32x4_t{lo, tag, hi, tag});
   }
 }
 
@@ -973,47 +1046,55 @@ __device__ __forceinline__ bool proj_task(const Deps &d, const uint16_t *a, cons
 }
 
 // Optional pre-expert norm of h row t: thread i takes elements 2i + 512 m,
-// +1, kBoundBatch of them per request.
+// +1 (one tagged word of the pooler's output), kBoundBatch of them per
+// request, polled until this launch's.  The normed row goes out as tagged
+// words (hn_t) and, when asked for, in bf16 to h.
 __device__ __forceinline__ void prenorm_task(const BlockParams &p, const Deps &d, int t,
                                              unsigned char *lds) {
-  wait_step(d, kCtrPool, p.n_pool_tiles);
   float *red = reinterpret_cast<float *>(lds);
-  const rsrc_t rh = make_rsrc(p.h + (size_t)t * p.P), rw = make_rsrc(p.pre_norm_w);
-  const uint32_t P2 = (uint32_t)p.P * 2;
+  const uint32_t W = (uint32_t)p.P / 2;  // words per row
+  const rsrc_t rh = make_rsrc(p.h_t + (size_t)t * W * 2), rn = make_rsrc(p.hn_t + (size_t)t * W * 2),
+               rw = make_rsrc(p.pre_norm_w), ro = make_rsrc(p.h + (size_t)t * p.P);
   float ss = 0.f;
-  for (int i0 = 2 * tid(); i0 < p.P; i0 += 512 * kBoundBatch) {
-    uint32_t v[kBoundBatch];
+  for (uint32_t w0 = tid(); w0 < W; w0 += kThreads * kBoundBatch) {
+    uint32_t off[kBoundBatch];
+    u32x2_t v[kBoundBatch];
 #pragma unroll
     for (int m = 0; m < kBoundBatch; ++m) {
-      const uint32_t off = (uint32_t)(i0 + 512 * m) * 2;
-      v[m] = ld_co4(rh, off < P2 ? off : kOob);
+      const uint32_t w = w0 + kThreads * m;
+      off[m] = w < W ? w * 8u : kOob;
+      v[m] = ld_co8(rh, off[m]);
     }
+    await_tagged(d, rh, off, v);
 #pragma unroll
     for (int m = 0; m < kBoundBatch; ++m) {
-      const float a = bf16_bits_to_f32(v[m] & 0xFFFFu), b = bf16_bits_to_f32(v[m] >> 16);
+      const float a = bf16_bits_to_f32(v[m][0] & 0xFFFFu), b = bf16_bits_to_f32(v[m][0] >> 16);
       ss += a * a + b * b;
     }
   }
   ss = wg_sum(ss, red, 0);
   const float rs = 1.0f / sqrtf(ss / (float)p.P + p.norm_eps);
-  for (int i0 = 2 * tid(); i0 < p.P; i0 += 512 * kBoundBatch) {
-    uint32_t v[kBoundBatch], w[kBoundBatch];
+  const uint32_t tag = d.tag();
+  for (uint32_t w0 = tid(); w0 < W; w0 += kThreads * kBoundBatch) {
+    uint32_t v[kBoundBatch], wv[kBoundBatch];
 #pragma unroll
     for (int m = 0; m < kBoundBatch; ++m) {
-      const uint32_t off = (uint32_t)(i0 + 512 * m) * 2;
-      v[m] = ld_co4(rh, off < P2 ? off : kOob);
-      w[m] = __builtin_amdgcn_raw_buffer_load_b32(rw, off < P2 ? off : kOob, 0, 0);
+      const uint32_t w = w0 + kThreads * m;
+      v[m] = ld_co4(rh, w < W ? w * 8u : kOob);  // (this thread saw these words tagged above)
+      wv[m] = ld_b32(rw, w < W ? w * 4u : kOob);
     }
 #pragma unroll
     for (int m = 0; m < kBoundBatch; ++m) {
-      const int i = i0 + 512 * m;
-      if (i >= p.P) break;
+      const uint32_t w = w0 + kThreads * m;
+      if (w >= W) break;
       const float a = bf16_bits_to_f32(v[m] & 0xFFFFu) * rs, b = bf16_bits_to_f32(v[m] >> 16) * rs;
-      const float wa = bf16_bits_to_f32(w[m] & 0xFFFFu), wb = bf16_bits_to_f32(w[m] >> 16);
-      st_co4(rh, (uint32_t)i * 2, pack_bf16x2(a * wa, b * wb));
+      const float wa = bf16_bits_to_f32(wv[m] & 0xFFFFu), wb = bf16_bits_to_f32(wv[m] >> 16);
+      const uint32_t o = pack_bf16x2(a * wa, b * wb);
+      st_tagged(rn, w * 8u, o, tag);
+      if (p.h_plain) st_co4(ro, w * 4u, o);
     }
   }
-  signal_step(d, kCtrPrenorm);
+  __syncthreads();  // (the workgroup's next task reuses the LDS)
 }
 
 // ---------------------------------------------------------------- experts
@@ -1072,6 +1153,103 @@ __device__ __forceinline__ MxTiles mx_packed(const uint8_t *codes, const uint8_t
 // 16-column MFMA blocks); more rows take several passes.
 __device__ __forceinline__ int pass_rows(int nrows) { return nrows <= 8 ? 8 : nrows <= 16 ? 16 : 32; }
 
+// ---- activation staging
+
+// Where the activation rows of a unit come from: a bf16 matrix, read
+// coherently (the caller wrote it), or the same matrix as tagged words (two
+// bf16 and the writer's tag per 8 bytes: the pooler's h, the up units' act),
+// polled until every word the unit reads carries this launch's tag.
+struct ActSrc {
+  rsrc_t r;
+  bool tagged;
+};
+
+// One batch of staging loads in flight: kStagePieces pieces of 8 elements
+// per thread, piece n being elements e[n] .. + 8 of the matrix (kOob:
+// padding, which loads zeros).  (Small batches: a tagged piece takes 8
+// registers until it arrives, and a down unit holds all its weights then.)
+constexpr int kStagePieces = 2;
+static_assert(kSegLoads % kStagePieces == 0, "whole batches per segment");
+struct StageBatch {
+  uint32_t e[kStagePieces];
+  u32x4_t a[kStagePieces], b[kStagePieces];
+};
+
+// Whether batch n0 (its first piece index per thread) holds a piece of one of
+// the pass's vrows valid rows (ppr pieces per row); the other batches are
+// padding only and skipped (their rows' columns are not stored).
+__device__ __forceinline__ bool batch_needed(int n0, int ppr, int vrows) { return (kThreads * n0) / ppr < vrows; }
+
+// Request batch n0 of the staging of the segment from chunk seg0 (segn
+// chunks, ppr 16-byte pieces per row): piece q = tid + kThreads (n0 + n) is
+// pass row m = q / ppr, elements 128 seg0 + 8 (q % ppr) .. + 8 of it; row_e(m)
+// is the matrix element of row m's element 0, or kOob.  Pieces past the
+// segment's chunks, and rows past pr or without a row, are padding.
+template <typename RowE>
+__device__ __forceinline__ void stage_issue(const ActSrc &A, RowE row_e, int pr, int seg0, int segn, int ppr, int n0,
+                                            StageBatch &S) {
+#pragma unroll
+  for (int n = 0; n < kStagePieces; ++n) {
+    const int q = (int)tid() + kThreads * (n0 + n);
+    const int m = q / ppr, pc = q % ppr;
+    const uint32_t ro = m < pr ? row_e(m) : kOob;
+    S.e[n] = (ro != kOob && pc < segn * 16) ? ro + (uint32_t)(seg0 * 128 + pc * 8) : kOob;
+    if (A.tagged) {
+      S.a[n] = ld_co16(A.r, S.e[n] != kOob ? S.e[n] * 4u : kOob);
+      S.b[n] = ld_co16(A.r, S.e[n] != kOob ? S.e[n] * 4u + 16u : kOob);
+    } else {
+      S.a[n] = ld_co16(A.r, S.e[n] != kOob ? S.e[n] * 2u : kOob);
+    }
+  }
+}
+
+__device__ __forceinline__ bool stage_piece_ready(const StageBatch &S, int n, uint32_t tag) {
+  return S.e[n] == kOob || (S.a[n][1] == tag && S.a[n][3] == tag && S.b[n][1] == tag && S.b[n][3] == tag);
+}
+
+// The batch's pieces (8 bf16 each) once they arrived; tagged, once every word
+// carries this launch's tag (the others requested again).  Bounded like
+// poll_ge.
+__device__ __forceinline__ void stage_complete(const Deps &d, const ActSrc &A, StageBatch &S,
+                                               u32x4_t (&v)[kStagePieces]) {
+  if (A.tagged) {
+    const uint32_t tag = d.tag();
+    unsigned spins = 0;
+    while (true) {
+      bool ok = true;
+#pragma unroll
+      for (int n = 0; n < kStagePieces; ++n) ok = ok && stage_piece_ready(S, n, tag);
+      if (__all((int)ok) || give_up(d, spins)) break;
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int n = 0; n < kStagePieces; ++n)
+        if (!stage_piece_ready(S, n, tag)) {
+          S.a[n] = ld_co16(A.r, S.e[n] * 4u);
+          S.b[n] = ld_co16(A.r, S.e[n] * 4u + 16u);
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < kStagePieces; ++n) v[n] = u32x4_t{S.a[n][0], S.a[n][2], S.b[n][0], S.b[n][2]};
+  } else {
+#pragma unroll
+    for (int n = 0; n < kStagePieces; ++n) v[n] = S.a[n];
+  }
+}
+
+// Batch n0 of the staging into `stage` (rows of srow bytes): complete it,
+// then write its pieces of the pass's pr rows.
+__device__ __forceinline__ void stage_store(const Deps &d, const ActSrc &A, StageBatch &S, int pr, int ppr, int n0,
+                                            int srow, unsigned char *stage) {
+  u32x4_t v[kStagePieces];
+  stage_complete(d, A, S, v);
+#pragma unroll
+  for (int n = 0; n < kStagePieces; ++n) {
+    const int q = (int)tid() + kThreads * (n0 + n);
+    const int m = q / ppr, pc = q % ppr;
+    if (m < pr) *reinterpret_cast<u32x4_t *>(stage + m * srow + pc * 16) = v[n];
+  }
+}
+
 // One wave: D0 = W0 B and D1 = W1 B for two 16-row MXFP4 weight tiles over
 // nch 128-element chunks and a pass of pr activation rows (bf16).  The
 // four waves of a workgroup call this together for units of the same expert
@@ -1080,18 +1258,19 @@ __device__ __forceinline__ int pass_rows(int nrows) { return nrows <= 8 ? 8 : nr
 // Weights: see MxTiles.  Lane l gets output rows 4*(l/16)..+3 of column
 // l % 16; columns past the pass's rows are zero.  Per chunk a lane converts
 // its MX block of each tile row to bf16 in registers for four 16x16x32
-// MFMAs; kRing chunks are in flight, requested before `wait` (which returns
-// once the activations' producers are done).
+// MFMAs; kRing chunks are in flight.
 //
-// Activations (written by other workgroups of the launch, so read
-// coherently): the rows' elements of up to kStageChunkRows / pr chunks at a time are
-// loaded by the whole workgroup in 16-byte pieces into `stage` (row m at
-// m * (its chunks * 256 + 16); chunks past nch as zeros; rows past the pass's
-// vrows valid rows hold whatever the stage held -- their columns are never
-// stored), then
-// each wave reads its MFMA operand from there: lane l reads row l % 8 (pr 8)
-// or l % 16 (of each 16-row block).
-// row_off(m) is the byte offset of pass row m's element 0, or kOob.
+// Activations (stage_issue / stage_complete): the rows' elements of up to
+// kStageChunkRows / pr chunks at a time are loaded by the whole workgroup in
+// 16-byte pieces into `stage` (row m at m * (its chunks * 256 + 16); chunks
+// past nch as zeros; rows past the pass's vrows valid rows hold whatever the
+// stage held -- their columns are never stored), then each wave reads its
+// MFMA operand from there: lane l reads row l % 8 (pr 8) or l % 16 (of each
+// 16-row block).  The first batch is requested before the weights when
+// `early` (the activations are normally complete: the up units), else after
+// them (the down units, whose activations are being written meanwhile).  The
+// order matters because a wait for a load completes in request order: staging
+// loads behind a wave's ring would be held up until the whole ring arrived.
 //
 // Chunks past nch have zero weights and zero activations and add nothing,
 // so the loop has no branches on the data.  Each round of chunks runs at the
@@ -1100,10 +1279,10 @@ __device__ __forceinline__ int pass_rows(int nrows) { return nrows <= 8 ? 8 : nr
 template <bool kLane> struct ScaleWord { using type = u32x4_t; };
 template <> struct ScaleWord<true> { using type = uint32_t; };
 
-template <int kRing, bool kLane, typename Wait, typename RowOff>
-__device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, int pr, int vrows, rsrc_t ra, RowOff row_off,
-                                        unsigned char *stage, f32x4_t (&d0)[2], f32x4_t (&d1)[2], int slot,
-                                        Wait wait) {
+template <int kRing, bool kLane, typename RowE>
+__device__ __forceinline__ void mx_pair(const Deps &d, const MxTiles &T, int nch, int pr, int vrows, const ActSrc &A,
+                                        RowE row_e, unsigned char *stage, f32x4_t (&d0)[2], f32x4_t (&d1)[2],
+                                        int slot, bool early) {
   const int lane = tid() % MB_WAVE, g = lane >> 4;
   const rsrc_t rw = T.rw, rs = T.rs;
   const uint32_t o0 = T.o0, o1 = T.o1, so0 = T.so0, so1 = T.so1, ws = T.wstride, ss = T.sstride;
@@ -1126,6 +1305,18 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, int pr, int v
     if constexpr (kLane) return e8m0_to_f32((v >> (8 * r)) & 0xFFu);
     else return e8m0_to_f32((v[r] >> (8 * g)) & 0xFFu);
   };
+  // pr rows (8, 16 or 32) in segments of seg chunks: pr * seg = 128.
+  const int seg = kStageChunkRows / pr, srow = seg * 256 + 16;  // row stride in the stage
+  const int nb = pr > 16 ? 2 : 1;                             // 16-row column blocks
+  // The first two batches of the first segment: requested before the
+  // weights when early, else right after them.
+  const int segn_first = min(seg, nch), ppr_first = ((segn_first + kRing - 1) / kRing) * kRing * 16;
+  const bool need1 = batch_needed(kStagePieces, ppr_first, vrows);
+  StageBatch first[2];
+  if (early) {
+    stage_issue(A, row_e, pr, 0, segn_first, ppr_first, 0, first[0]);
+    if (need1) stage_issue(A, row_e, pr, 0, segn_first, ppr_first, kStagePieces, first[1]);
+  }
 #pragma unroll
   for (int r = 0; r < kRing; ++r) {
     const bool ok = r < nch;
@@ -1138,10 +1329,10 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, int pr, int v
     S0[q] = scales(so0, 4 * q);
     S1[q] = scales(so1, 4 * q);
   }
-  wait();
-  // pr rows (8, 16 or 32) in segments of seg chunks: pr * seg = 128.
-  const int seg = kStageChunkRows / pr, srow = seg * 256 + 16;  // row stride in the stage
-  const int nb = pr > 16 ? 2 : 1;                             // 16-row column blocks
+  if (!early) {
+    stage_issue(A, row_e, pr, 0, segn_first, ppr_first, 0, first[0]);
+    if (need1) stage_issue(A, row_e, pr, 0, segn_first, ppr_first, kStagePieces, first[1]);
+  }
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     d0[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1152,25 +1343,17 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, int pr, int v
     // This segment's activations, chunks rounded up to whole rounds.
     const int segn = min(seg, nch - seg0);
     const int ppr = ((segn + kRing - 1) / kRing) * kRing * 16;  // 16-byte pieces per row
-    // In two batches of half the pieces (registers); the second only if it
-    // holds one of the pass's vrows rows (the rest are padding: their
-    // columns are not stored).
+    // In batches of kStagePieces pieces per thread, each only if it holds
+    // one of the pass's vrows rows.
 #pragma unroll
-    for (int n0 = 0; n0 < kSegLoads; n0 += kSegLoads / 2) {
-      if (n0 > 0 && (kThreads * n0) / ppr >= vrows) continue;
-      u32x4_t v[kSegLoads / 2];
-#pragma unroll
-      for (int n = 0; n < kSegLoads / 2; ++n) {
-        const int q = (int)tid() + kThreads * (n0 + n);
-        const int m = q / ppr, pc = q % ppr;
-        const uint32_t ro = m < pr ? row_off(m) : kOob;
-        v[n] = ld_co16(ra, (ro != kOob && pc < segn * 16) ? ro + (uint32_t)(seg0 * 256 + pc * 16) : kOob);
-      }
-#pragma unroll
-      for (int n = 0; n < kSegLoads / 2; ++n) {
-        const int q = (int)tid() + kThreads * (n0 + n);
-        const int m = q / ppr, pc = q % ppr;
-        if (m < pr) *reinterpret_cast<u32x4_t *>(stage + m * srow + pc * 16) = v[n];
+    for (int n0 = 0; n0 < kSegLoads; n0 += kStagePieces) {
+      if (n0 > 0 && !batch_needed(n0, ppr, vrows)) continue;
+      if (seg0 == 0 && n0 < 2 * kStagePieces) {
+        stage_store(d, A, first[n0 / kStagePieces], pr, ppr, n0, srow, stage);
+      } else {
+        StageBatch S;
+        stage_issue(A, row_e, pr, seg0, segn, ppr, n0, S);
+        stage_store(d, A, S, pr, ppr, n0, srow, stage);
       }
     }
     __syncthreads();
@@ -1215,13 +1398,14 @@ __device__ __forceinline__ void mx_pair(const MxTiles &T, int nch, int pr, int v
 
 // mx_pair for units of at most kAll chunks and passes of at most 16 rows, in
 // the streaming layout: all of the unit's weights and scales are requested
-// before `wait` (a down unit waits for its expert's up units, so its whole
-// weight stream is in flight meanwhile), then the activations are staged in
-// one segment and every chunk is computed with no further weight requests.
-// Same operands, staging and results as mx_pair (block 0 of d0 / d1 only).
-template <int kAll, typename Wait, typename RowOff>
-__device__ __forceinline__ void mx_pair_all(const MxTiles &T, int nch, int pr, int vrows, rsrc_t ra, RowOff row_off,
-                                            unsigned char *stage, f32x4_t (&d0)[2], f32x4_t (&d1)[2], Wait wait) {
+// first (a down unit's activations are being written by its expert's up units
+// meanwhile), then the activations are staged in one segment and every chunk
+// is computed with no further weight requests.  Same operands, staging and
+// results as mx_pair (block 0 of d0 / d1 only).
+template <int kAll, typename RowE>
+__device__ __forceinline__ void mx_pair_all(const Deps &d, const MxTiles &T, int nch, int pr, int vrows,
+                                            const ActSrc &A, RowE row_e, unsigned char *stage, f32x4_t (&d0)[2],
+                                            f32x4_t (&d1)[2]) {
   static_assert(kAll % 4 == 0 && 16 * kAll <= kStageChunkRows, "whole scale words; 16 rows x kAll chunks staged");
   const int lane = tid() % MB_WAVE, g = lane >> 4;
   const rsrc_t rw = T.rw, rs = T.rs;
@@ -1239,29 +1423,17 @@ __device__ __forceinline__ void mx_pair_all(const MxTiles &T, int nch, int pr, i
     S0[q] = ld_b32(rs, 4 * q < nch ? so0 + ss * (4 * q) : kOob);
     S1[q] = ld_b32(rs, 4 * q < nch ? so1 + ss * (4 * q) : kOob);
   }
-  wait();
   const int srow = kAll * 256 + 16;  // row stride in the stage
   d0[0] = d1[0] = d0[1] = d1[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // Chunks past nch are staged as zeros; the second batch only if it holds
-  // one of the pass's vrows rows.
+  // Chunks past nch are staged as zeros; a batch only if it holds one of the
+  // pass's vrows rows.
   constexpr int ppr = kAll * 16;  // 16-byte pieces per row
 #pragma unroll
-  for (int n0 = 0; n0 < kSegLoads; n0 += kSegLoads / 2) {
-    if (n0 > 0 && (kThreads * n0) / ppr >= vrows) continue;
-    u32x4_t v[kSegLoads / 2];
-#pragma unroll
-    for (int n = 0; n < kSegLoads / 2; ++n) {
-      const int q = (int)tid() + kThreads * (n0 + n);
-      const int m = q / ppr, pc = q % ppr;
-      const uint32_t ro = m < pr ? row_off(m) : kOob;
-      v[n] = ld_co16(ra, (ro != kOob && pc < nch * 16) ? ro + (uint32_t)(pc * 16) : kOob);
-    }
-#pragma unroll
-    for (int n = 0; n < kSegLoads / 2; ++n) {
-      const int q = (int)tid() + kThreads * (n0 + n);
-      const int m = q / ppr, pc = q % ppr;
-      if (m < pr) *reinterpret_cast<u32x4_t *>(stage + m * srow + pc * 16) = v[n];
-    }
+  for (int n0 = 0; n0 < kSegLoads; n0 += kStagePieces) {
+    if (n0 > 0 && !batch_needed(n0, ppr, vrows)) continue;
+    StageBatch S;
+    stage_issue(A, row_e, pr, 0, nch, ppr, n0, S);
+    stage_store(d, A, S, pr, ppr, n0, srow, stage);
   }
   __syncthreads();
   const uint32_t rd_off = (uint32_t)((lane & (pr == 8 ? 7 : 15)) * srow + 64 * g);
@@ -1281,33 +1453,29 @@ __device__ __forceinline__ void mx_pair_all(const MxTiles &T, int nch, int pr, i
 
 // ---- MXFP4 activations (the W4A4 variant), streaming layout only
 
-// Quantized staging of one segment: pass rows 0 .. pr - 1 (row_off(m)), bf16
+// Quantized staging of one segment: pass rows 0 .. pr - 1 (row_e(m)), bf16
 // elements of chunks seg0 .. seg0 + segn (segc >= segn chunks, a multiple of
-// 4), read coherently in 16-byte pieces as the bf16 staging does, quantized
-// per 32-element block (four consecutive lanes hold a block: their amax by
-// two butterfly steps; then the block's E8M0 byte by mx_scale_byte and the
-// elements' E2M1 codes by the hardware's scaled conversion) and written to
-// `stage` rows of srowq
-// bytes: chunk c's block g's 16 code bytes at (4c + g) * 16, its scale byte
-// at segc * 64 + g * segc + c (so a lane's scales of four chunks form one
-// word).  Rows past vrows are left as they are (their columns are not stored).
-template <typename RowOff>
-__device__ __forceinline__ void mxq_stage(rsrc_t ra, RowOff row_off, int pr, int vrows, int seg0, int segn,
-                                          int segc, int srowq, unsigned char *stage) {
+// 4), fetched in 16-byte pieces of 8 elements as the bf16 staging does
+// (stage_issue / stage_complete), quantized per 32-element block (four
+// consecutive lanes hold a block: their amax by two butterfly steps; then the
+// block's E8M0 byte by mx_scale_byte and the elements' E2M1 codes by the
+// hardware's scaled conversion) and written to `stage` rows of srowq bytes:
+// chunk c's block g's 16 code bytes at (4c + g) * 16, its scale byte at
+// segc * 64 + g * segc + c (so a lane's scales of four chunks form one word).
+// Rows past vrows are left as they are (their columns are not stored).
+template <typename RowE>
+__device__ __forceinline__ void mxq_stage(const Deps &d, const ActSrc &A, RowE row_e, int pr, int vrows, int seg0,
+                                          int segn, int segc, int srowq, unsigned char *stage) {
   const int ppr = segc * 16;  // bf16 pieces (8 elements) per row
 #pragma unroll
-  for (int n0 = 0; n0 < kSegLoads; n0 += kSegLoads / 2) {
-    if (n0 > 0 && (kThreads * n0) / ppr >= vrows) continue;
-    u32x4_t v[kSegLoads / 2];
+  for (int n0 = 0; n0 < kSegLoads; n0 += kStagePieces) {
+    if (n0 > 0 && !batch_needed(n0, ppr, vrows)) continue;
+    StageBatch S;
+    u32x4_t v[kStagePieces];
+    stage_issue(A, row_e, pr, seg0, segn, ppr, n0, S);
+    stage_complete(d, A, S, v);
 #pragma unroll
-    for (int n = 0; n < kSegLoads / 2; ++n) {
-      const int q = (int)tid() + kThreads * (n0 + n);
-      const int m = q / ppr, pc = q % ppr;
-      const uint32_t ro = m < pr ? row_off(m) : kOob;
-      v[n] = ld_co16(ra, (ro != kOob && pc < segn * 16) ? ro + (uint32_t)(seg0 * 256 + pc * 16) : kOob);
-    }
-#pragma unroll
-    for (int n = 0; n < kSegLoads / 2; ++n) {
+    for (int n = 0; n < kStagePieces; ++n) {
       const int q = (int)tid() + kThreads * (n0 + n);
       const int m = q / ppr, pc = q % ppr;
       float f[8];
@@ -1359,14 +1527,14 @@ __device__ __forceinline__ f32x4_t mfma_fp4_r(int r, u32x4_t a, u32x4_t b, f32x4
   }
 }
 
-// mx_pair with MXFP4 activations: the same weight ring, scales, waits,
-// passes and results' layout, but the activations staged as MXFP4
-// (mxq_stage) and each chunk of a tile one scaled fp4 x fp4 MFMA with the
-// weights' codes as loaded (no conversion to bf16).
-template <int kRing, typename Wait, typename RowOff>
-__device__ __forceinline__ void mxq_pair(const MxTiles &T, int nch, int pr, int vrows, rsrc_t ra, RowOff row_off,
-                                         unsigned char *stage, f32x4_t (&d0)[2], f32x4_t (&d1)[2], int slot,
-                                         Wait wait) {
+// mx_pair with MXFP4 activations: the same weight ring, scales, passes and
+// results' layout, but the activations staged as MXFP4 (mxq_stage, after
+// the weights are requested) and each chunk of a tile one scaled fp4 x fp4
+// MFMA with the weights' codes as loaded (no conversion to bf16).
+template <int kRing, typename RowE>
+__device__ __forceinline__ void mxq_pair(const Deps &d, const MxTiles &T, int nch, int pr, int vrows,
+                                         const ActSrc &A, RowE row_e, unsigned char *stage, f32x4_t (&d0)[2],
+                                         f32x4_t (&d1)[2], int slot) {
   static_assert(kRing == 4, "one scale word covers the four chunks of a round");
   const int lane = tid() % MB_WAVE, g = lane >> 4;
   const rsrc_t rw = T.rw, rs = T.rs;
@@ -1379,7 +1547,6 @@ __device__ __forceinline__ void mxq_pair(const MxTiles &T, int nch, int pr, int 
     W1[r] = ld_b128(rw, ok ? o1 + ws * r : kOob);
   }
   uint32_t S0 = ld_b32(rs, so0), S1 = ld_b32(rs, so1);
-  wait();
   const int seg = kStageChunkRows / pr, nb = pr > 16 ? 2 : 1;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -1389,7 +1556,7 @@ __device__ __forceinline__ void mxq_pair(const MxTiles &T, int nch, int pr, int 
   const int rrow = lane & (pr == 8 ? 7 : 15);
   for (int seg0 = 0; seg0 < nch; seg0 += seg) {
     const int segn = min(seg, nch - seg0), segc = ((segn + 3) / 4) * 4, srowq = segc * 68 + 16;
-    mxq_stage(ra, row_off, pr, vrows, seg0, segn, segc, srowq, stage);
+    mxq_stage(d, A, row_e, pr, vrows, seg0, segn, segc, srowq, stage);
     __syncthreads();
     for (int c0 = seg0; c0 < seg0 + segn; c0 += kRing) {
       set_slot_priority(slot);
@@ -1424,9 +1591,10 @@ __device__ __forceinline__ void mxq_pair(const MxTiles &T, int nch, int pr, int 
 }
 
 // mx_pair_all with MXFP4 activations (as mxq_pair is to mx_pair).
-template <int kAll, typename Wait, typename RowOff>
-__device__ __forceinline__ void mxq_pair_all(const MxTiles &T, int nch, int pr, int vrows, rsrc_t ra, RowOff row_off,
-                                             unsigned char *stage, f32x4_t (&d0)[2], f32x4_t (&d1)[2], Wait wait) {
+template <int kAll, typename RowE>
+__device__ __forceinline__ void mxq_pair_all(const Deps &d, const MxTiles &T, int nch, int pr, int vrows,
+                                             const ActSrc &A, RowE row_e, unsigned char *stage, f32x4_t (&d0)[2],
+                                             f32x4_t (&d1)[2]) {
   static_assert(kAll % 4 == 0, "whole scale words");
   const int lane = tid() % MB_WAVE, g = lane >> 4;
   const rsrc_t rw = T.rw, rs = T.rs;
@@ -1444,10 +1612,9 @@ __device__ __forceinline__ void mxq_pair_all(const MxTiles &T, int nch, int pr, 
     S0[q] = ld_b32(rs, 4 * q < nch ? so0 + ss * (4 * q) : kOob);
     S1[q] = ld_b32(rs, 4 * q < nch ? so1 + ss * (4 * q) : kOob);
   }
-  wait();
   constexpr int segc = kAll, srowq = segc * 68 + 16;
   d0[0] = d1[0] = d0[1] = d1[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  mxq_stage(ra, row_off, pr, vrows, 0, nch, segc, srowq, stage);
+  mxq_stage(d, A, row_e, pr, vrows, 0, nch, segc, srowq, stage);
   __syncthreads();
   const int rrow = lane & (pr == 8 ? 7 : 15);
   uint32_t sbw[kAll / 4];
@@ -1465,10 +1632,12 @@ __device__ __forceinline__ void mxq_pair_all(const MxTiles &T, int nch, int pr, 
 
 // Up unit: w13 and the gated activation for (active expert, 16 act columns):
 // gate rows i0..i0+15 and up rows I+i0..I+i0+15 of the expert, over P, for
-// the expert's routes in passes of pass_rows.
+// the expert's routes in passes of pass_rows.  h: the pooler's (or the
+// pre-norm's) tagged words of this launch, or the caller's bf16 matrix.  act
+// goes out as tagged words, and in bf16 to act_tap when asked for.
 template <bool kPacked, bool kQ>
 __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, const RouteLds &R, int unit,
-                                        bool &h_ready, unsigned char *stage) {
+                                        unsigned char *stage) {
   const int lane = tid() % MB_WAVE, g = lane >> 4, r16 = lane & 15;
   const int P = p.P, I = p.I;
   const int tiles = I / 16;
@@ -1480,23 +1649,19 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
       kPacked ? mx_packed(p.xp + (size_t)e * p.xp_stride, p.xp + (size_t)e * p.xp_stride + p.xp_up_s, tile, P, lane)
            : mx_plain(p.w13 + (size_t)e * 2 * I * (P / 2), p.w13s + (size_t)e * 2 * I * (P / 32), i0, I + i0, P,
                       lane);
-  const rsrc_t rh = make_rsrc(p.h), ract = make_rsrc(p.act);
+  const ActSrc A{p.h_tagged ? make_rsrc(p.pre_norm_w ? p.hn_t : p.h_t) : make_rsrc(p.h), p.h_tagged != 0};
+  const rsrc_t rat = make_rsrc(p.act_t), rap = make_rsrc(p.act_tap);
+  const uint32_t tag = d.tag();
   const int nch = P / 128;
   const int pr = pass_rows(nrows);
   for (int m0 = 0; m0 < nrows; m0 += pr) {
     f32x4_t gs[2], us[2];
-    auto row_off = [&](int m) { return m0 + m < nrows ? (uint32_t)((R.rl[row0 + m0 + m] / p.k) * P) * 2u : kOob; };
-    auto wait = [&]() {
-      if (!h_ready) {
-        wave_wait_step(d, p.pre_norm_w ? kCtrPrenorm : kCtrPool, p.h_producers);
-        h_ready = true;
-      }
-    };
+    auto row_e = [&](int m) { return m0 + m < nrows ? (uint32_t)((R.rl[row0 + m0 + m] / p.k) * P) : kOob; };
     if constexpr (kQ)
-      mxq_pair<kRingUp>(T, nch, pr, min(pr, nrows - m0), rh, row_off, stage, gs, us, (int)blockIdx.x / p.cus, wait);
+      mxq_pair<kRingUp>(d, T, nch, pr, min(pr, nrows - m0), A, row_e, stage, gs, us, (int)blockIdx.x / p.cus);
     else
-      mx_pair<kRingUp, kPacked>(T, nch, pr, min(pr, nrows - m0), rh, row_off, stage, gs, us, (int)blockIdx.x / p.cus,
-                                wait);
+      mx_pair<kRingUp, kPacked>(d, T, nch, pr, min(pr, nrows - m0), A, row_e, stage, gs, us,
+                                (int)blockIdx.x / p.cus, true);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int m = m0 + 16 * b + r16;
@@ -1507,16 +1672,18 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
           const float z = gs[b][i];
           o[i] = (z / (1.0f + expf(-z))) * us[b][i];
         }
-        st_co8(ract, (uint32_t)((((size_t)(row0 + m)) * I + i0 + 4 * g) * 2),
-               u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
+        const uint32_t lo = pack_bf16x2(o[0], o[1]), hi = pack_bf16x2(o[2], o[3]);
+        const size_t el = (size_t)(row0 + m) * I + i0 + 4 * g;
+        st_co16(rat, (uint32_t)(el * 4), u32x4_t{lo, tag, hi, tag});
+        if (p.act_tap) st_co8(rap, (uint32_t)(el * 2), u32x2_t{lo, hi});
       }
     }
   }
-  signal_units(d.up(e));
 }
 
 // Down unit: w2 for (active expert, 32 output features): y in route order and
-// the route's sum of squares over these 32 features.
+// the route's sum of squares over these 32 features, from the up units'
+// tagged act (the staging polls it).
 template <bool kPacked, bool kQ>
 __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, const RouteLds &R, int unit,
                                           unsigned char *stage) {
@@ -1531,32 +1698,23 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
       kPacked ? mx_packed(p.xp + (size_t)e * p.xp_stride + p.xp_down, p.xp + (size_t)e * p.xp_stride + p.xp_down_s,
                        tile, I, lane)
            : mx_plain(p.w2 + (size_t)e * P * (I / 2), p.w2s + (size_t)e * P * (I / 32), p0, p0 + 16, I, lane);
-  const rsrc_t ract = make_rsrc(p.act), ry = make_rsrc(p.y), rss = make_rsrc(p.ssq);
+  const ActSrc A{make_rsrc(p.act_t), true};
+  const rsrc_t ry = make_rsrc(p.y), rss = make_rsrc(p.ssq);
   const int nch = I / 128;
-  bool ready = false;
   const int pr = pass_rows(nrows);
   for (int m0 = 0; m0 < nrows; m0 += pr) {
     f32x4_t y0[2], y1[2];
-    auto row_off = [&](int m) { return m0 + m < nrows ? (uint32_t)((row0 + m0 + m) * I) * 2u : kOob; };
-    auto wait = [&]() {
-      if (!ready) {
-        // (One wave polls for the workgroup.)
-        if (tid() < MB_WAVE) poll_ge(d, d.up(e), (unsigned)(I / 16));
-        __syncthreads();
-        ready = true;
-      }
-    };
+    auto row_e = [&](int m) { return m0 + m < nrows ? (uint32_t)((row0 + m0 + m) * I) : kOob; };
     if constexpr (kQ) {
       if (nch <= kDownAll && pr <= 16)
-        mxq_pair_all<kDownAll>(T, nch, pr, min(pr, nrows - m0), ract, row_off, stage, y0, y1, wait);
+        mxq_pair_all<kDownAll>(d, T, nch, pr, min(pr, nrows - m0), A, row_e, stage, y0, y1);
       else
-        mxq_pair<kRingDown>(T, nch, pr, min(pr, nrows - m0), ract, row_off, stage, y0, y1, (int)blockIdx.x / p.cus,
-                            wait);
+        mxq_pair<kRingDown>(d, T, nch, pr, min(pr, nrows - m0), A, row_e, stage, y0, y1, (int)blockIdx.x / p.cus);
     } else if (kPacked && nch <= kDownAll && pr <= 16)
-      mx_pair_all<kDownAll>(T, nch, pr, min(pr, nrows - m0), ract, row_off, stage, y0, y1, wait);
+      mx_pair_all<kDownAll>(d, T, nch, pr, min(pr, nrows - m0), A, row_e, stage, y0, y1);
     else
-      mx_pair<kRingDown, kPacked>(T, nch, pr, min(pr, nrows - m0), ract, row_off, stage, y0, y1, (int)blockIdx.x / p.cus,
-                                  wait);
+      mx_pair<kRingDown, kPacked>(d, T, nch, pr, min(pr, nrows - m0), A, row_e, stage, y0, y1,
+                                  (int)blockIdx.x / p.cus, false);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       if (b == 1 && pr <= 16) break;
@@ -1818,61 +1976,85 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     __syncthreads();
   }
 
-  // 1. Workgroup tasks before routing.
+  // 1. Workgroup tasks before routing: router tasks 0 .. nR - 1, then route,
+  // pool and pre-norm tasks, numbered on; the workgroup takes tasks
+  // blockIdx, blockIdx + G, ..  Each kind has a loop of its own, so that no
+  // kind's hoisted constants (the routing's fp64 exp) stay live through
+  // another's.
   {
-    int last = -1;
-    for (int j = blockIdx.x;; j += G) {
-      const BlockParams &p = kparams();
-      const Deps d{p.sync, gen};
-      const RouteLds R = route_lds(p, lds);
-      unsigned char *scratch = lds + p.lds_route_bytes;
-      const int nR = p.n_router, nRT = p.n_route, nP = p.n_pool, nPN = p.n_prenorm;
-      if (j >= nR + nRT + nP + nPN) break;
-      int step, i = j;
-      if (i < nR) {
-        step = 1;
-      } else if ((i -= nR) < nRT) {
-        step = 2;
-      } else if ((i -= nRT) < nP) {
-        step = 3;
-      } else {
-        i -= nP;
-        step = 4;
+    // The first of this workgroup's task numbers at or after lo.
+    auto first_from = [&](int lo) {
+      const int b = (int)blockIdx.x;
+      return lo <= b ? b : b + G * ((lo - b + G - 1) / G);
+    };
+    {
+      bool first = true;
+      for (int j = blockIdx.x; j < kparams().n_router; j += G) {
+        const BlockParams &p = kparams();
+        if (first) stamp(p, 1);
+        first = false;
+        if (p.router_multi) router_task_multi(p, gen, j, lds + p.lds_route_bytes);
+        else router_task(p, gen, j, lds + p.lds_route_bytes);
       }
-      if (step != last) {
-        stamp(p, step);
-        last = step;
+    }
+    {
+      bool first = true;
+      const int lo = kparams().n_router;
+      for (int j = first_from(lo); j < lo + kparams().n_route; j += G) {
+        const BlockParams &p = kparams();
+        if (first) stamp(p, 2);
+        first = false;
+        route_task(p, Deps{p.sync, gen}, j - lo);
       }
-      if (step == 1) {
-        if (p.router_multi) router_task_multi(p, gen, i, scratch);
-        else router_task(p, gen, i, scratch);
-      } else if (step == 2) {
-        route_task(p, d, R, i);
-      } else if (step == 3) {
-        // Pooler: wide tiles, the splits added by the last to finish.
-        const int gi = i / p.pool_ks, q = i % p.pool_ks;
-        proj_wide<false>(make_rsrc(p.x), p.pool_w, p.b, p.P, p.H, gi, q, p.pool_ks, p.pool_part, p.h, scratch,
-                         []() {});
-        bool done = true;
-        if (p.pool_ks > 1) {
-          done = last_arrival(&p.pool_cnt[gi], (unsigned)p.pool_ks, proj_flag(scratch));
-          if (done) {
-            proj_wide_sum(p.pool_part, p.h, p.b, p.P, gi, p.pool_ks);
-            if (tid() == 0) __hip_atomic_store(&p.pool_cnt[gi], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
+    }
+    {
+      bool first = true;
+      const int lo = kparams().n_router + kparams().n_route;
+      for (int j = first_from(lo); j < lo + kparams().n_pool; j += G) {
+        const BlockParams &p = kparams();
+        const Deps d{p.sync, gen};
+        unsigned char *scratch = lds + p.lds_route_bytes;
+        if (first) stamp(p, 3);
+        first = false;
+        // Pooler: wide tiles, the splits added by the last to finish.  h
+        // goes out as tagged words (the up units and the pre-norm poll them),
+        // and in bf16 when asked for (the pre-norm writes that then).
+        const int i = j - lo, gi = i / p.pool_ks, q = i % p.pool_ks;
+        uint16_t *hp = (p.h_plain && !p.pre_norm_w) ? p.h : nullptr;
+        proj_wide<false>(make_rsrc(p.x), p.pool_w, p.b, p.P, p.H, gi, q, p.pool_ks, p.pool_part, hp, p.h_t, d.tag(),
+                         scratch, []() {});
+        if (p.pool_ks > 1 && last_arrival(&p.pool_cnt[gi], (unsigned)p.pool_ks, proj_flag(scratch))) {
+          proj_wide_sum(p.pool_part, hp, p.h_t, d.tag(), p.b, p.P, gi, p.pool_ks);
+          if (tid() == 0) __hip_atomic_store(&p.pool_cnt[gi], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (done) signal_step(d, kCtrPool);
+        __syncthreads();  // (the workgroup's next task reuses the LDS)
         stamp(p, 7);
-      } else {
-        prenorm_task(p, d, i, scratch);
+      }
+    }
+    {
+      bool first = true;
+      const int lo = kparams().n_router + kparams().n_route + kparams().n_pool;
+      for (int j = first_from(lo); j < lo + kparams().n_prenorm; j += G) {
+        const BlockParams &p = kparams();
+        if (first) stamp(p, 4);
+        first = false;
+        prenorm_task(p, Deps{p.sync, gen}, j - lo, lds + p.lds_route_bytes);
       }
     }
   }
 
+  // The launch's generation, kept in LDS from here on: a register holding it
+  // through the later phases would be spilled, and a reload from scratch
+  // memory waits behind every load the wave has in flight.
+  unsigned *const gen_slot = reinterpret_cast<unsigned *>(route_lds(kparams(), lds).nact + 1);
+  if (tid() == 0) *gen_slot = gen;
+  __syncthreads();
+  auto launch_gen = [&]() { return (unsigned)uniform((int)*gen_slot); };
+
   // 2. Routing state (workgroup 0 also writes the routing outputs).
   {
   const BlockParams &p = kparams();
-  const Deps d{p.sync, gen};
+  const Deps d{p.sync, launch_gen()};
   const RouteLds R = route_lds(p, lds);
   if (p.needs_routing && (p.has_up || (p.routing_out && blockIdx.x == 0))) {
     prepare_routing(p, d, R);
@@ -1883,7 +2065,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // 3. Expert units, one wave each.
   if (kparams().has_up) {
     const BlockParams &p = kparams();
-    const Deps d{p.sync, gen};
+    const Deps d{p.sync, launch_gen()};
     const RouteLds R = route_lds(p, lds);
     unsigned char *scratch = lds + p.lds_route_bytes;
     stamp(p, 6);
@@ -1891,7 +2073,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     unsigned char *stage = scratch;
     const int nact = uniform(*R.nact);
     const int nU = nact * (p.I / 16), nD = nact * (p.P / 32);
-    bool h_ready = p.h_producers == 0;
     // Up units and down units are dealt separately, so a wave's down units
     // belong to the experts of its own up units (with as many tiles per
     // expert): they wait on waves that started with them.  (Waves that
@@ -1904,15 +2085,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // (The expert layout and the activation format are template arguments:
     // each has its own registers.)
     if constexpr (kQ) {
-      for (int u = gw; u < nU; u += GW) up_unit<true, true>(p, d, R, u, h_ready, stage);
+      for (int u = gw; u < nU; u += GW) up_unit<true, true>(p, d, R, u, stage);
       stamp(p, 20);
       for (int u = gw; u < nD; u += GW) down_unit<true, true>(p, d, R, u, stage);
     } else if (p.xp) {
-      for (int u = gw; u < nU; u += GW) up_unit<true, false>(p, d, R, u, h_ready, stage);
+      for (int u = gw; u < nU; u += GW) up_unit<true, false>(p, d, R, u, stage);
       stamp(p, 20);
       for (int u = gw; u < nD; u += GW) down_unit<true, false>(p, d, R, u, stage);
     } else {
-      for (int u = gw; u < nU; u += GW) up_unit<false, false>(p, d, R, u, h_ready, stage);
+      for (int u = gw; u < nU; u += GW) up_unit<false, false>(p, d, R, u, stage);
       stamp(p, 20);
       for (int u = gw; u < nD; u += GW) down_unit<false, false>(p, d, R, u, stage);
     }
@@ -1926,7 +2107,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     int last = -1;
     for (int j = blockIdx.x;; j += G) {
       const BlockParams &p = kparams();
-      const Deps d{p.sync, gen};
+      const Deps d{p.sync, launch_gen()};
       const RouteLds R = route_lds(p, lds);
       unsigned char *scratch = lds + p.lds_route_bytes;
       const int nF = p.n_fin, nN = p.n_unpool, nB = p.n_boundary, nQ = kQKV ? p.n_qkv : 0;
@@ -1954,7 +2135,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         if (p.unpool_wide) {
           // Many rows: wide tiles, so each workgroup reads the MoE output once per 64 features.
           proj_wide<true>(make_rsrc(mo), p.unpool_w, p.b, p.H, p.P, i / p.unpool_ks, i % p.unpool_ks, p.unpool_ks,
-                          p.unpool_part, p.u, scratch, [&]() { wait_step(d, kCtrFin, p.n_fin); });
+                          p.unpool_part, p.u, nullptr, 0u, scratch, [&]() { wait_step(d, kCtrFin, p.n_fin); });
         } else {
           proj_task<true>(d, mo, p.unpool_w, p.u, p.b, p.H, p.P, p.unpool_ks, p.unpool_part, p.unpool_cnt, kCtrFin,
                           p.n_fin, false, i, true, scratch);
@@ -1970,16 +2151,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         // added by the last to finish.
         const int gi = i / p.qkv_ks, q = i % p.qkv_ks;
         proj_wide<true>(make_rsrc(p.x_next), p.qkv_w, p.b, p.qkv_rows, p.H, gi, q, p.qkv_ks, p.qkv_part, p.qkvg,
-                        scratch, [&]() { wait_step(d, kCtrBound, p.n_boundary); });
+                        nullptr, 0u, scratch, [&]() { wait_step(d, kCtrBound, p.n_boundary); });
         if (p.qkv_ks > 1 && last_arrival(&p.qkv_cnt[gi], (unsigned)p.qkv_ks, proj_flag(scratch))) {
-          proj_wide_sum(p.qkv_part, p.qkvg, p.b, p.qkv_rows, gi, p.qkv_ks);
+          proj_wide_sum(p.qkv_part, p.qkvg, nullptr, 0u, p.b, p.qkv_rows, gi, p.qkv_ks);
           if (tid() == 0) __hip_atomic_store(&p.qkv_cnt[gi], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         stamp(p, 25);
       }
     }
   }
-  prepare_next_launch(kparams().sync, gen);
+  prepare_next_launch(kparams().sync, launch_gen());
   stamp(kparams(), 15);
 }
 

@@ -78,6 +78,7 @@ constexpr size_t kSetLines = sync_line_logits((kSyncMaxRows + kRouterRowBlock - 
 __host__ __device__ constexpr size_t sync_line_set(int set) { return 1 + kGenLines + (size_t)set * kSetLines; }
 constexpr size_t kSyncWords = sync_line_set(2) * kLine;
 
+constexpr int kRouteReps = 8;  // copies of the tagged routes (each workgroup polls one)
 constexpr int kFinChunk = 1024;  // features per finalize task (4 per thread: the most one task covers)
 constexpr int kMaxPoolSplit = 32;  // contraction splits of the pooler
 constexpr int kMoeReplicas = 8;  // copies of the MoE output for the unpooler tasks
@@ -116,7 +117,7 @@ struct BlockParams {
   // task counts (0 = step absent) and step switches
   int n_logit_producers;           // router tasks to wait for (0: logits given)
   int n_router, n_route, n_pool, n_prenorm, n_fin, n_unpool, n_boundary;
-  int pool_ks, unpool_ks, n_pool_tiles, h_producers;
+  int pool_ks, unpool_ks, n_pool_tiles;
   int has_up, needs_routing, routing_out, route_given, logits_in;
   int unpool_wide;  // unpooler in 64-feature tiles (many rows)
   int router_multi; // router tasks of kRouterExperts experts (many rows)
@@ -154,6 +155,18 @@ struct BlockParams {
   float *qkv_part;
   unsigned *qkv_cnt;
   int qkv_rows, n_qkv, qkv_ks;
+  // Tagged hand-off words (8 bytes: payload, then the writing launch's tag):
+  // the router's fp32 logits [b][E]; the routes, kRouteReps copies of
+  // [2 b k] (ids, then weights).
+  uint32_t *logits_t, *routes_t;
+  // The pooler's h [b][P/2], the pre-norm's normed h (same shape), and act
+  // [R][I/2], as tagged words of two bf16.  h_tagged: the up units read h
+  // from h_t / hn_t (the launch's pooler made it), else from h (the
+  // caller's).  h_plain: also write h in bf16 (an output).  act_tap: also
+  // write act in bf16 there (or NULL).
+  uint32_t *h_t, *hn_t, *act_t;
+  uint16_t *act_tap;
+  int h_tagged, h_plain;
 };
 constexpr int kMaxQkvGroups = 1024;  // 64-feature tiles of the fused projection (qkv_rows <= 65536)
 
@@ -164,7 +177,7 @@ struct RouteLds {
   int *rl;     // [b*k] route list
   int *off;    // [E+1]
   int *act;    // [E]
-  int *nact;   // [1]
+  int *nact;   // [1]; nact[1] holds the launch's generation
   int *red;    // [8] scan scratch
   unsigned long long *bits;  // [E * ceil(b/64)]
 };

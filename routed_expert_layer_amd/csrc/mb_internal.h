@@ -15,14 +15,24 @@ constexpr int kMaxTopK = 16;
 constexpr int kMaxBitmapWords = 4096;  // experts * ceil(rows / 64)
 constexpr int kMaxSplitK = 8;          // split-K factor of the bf16 projections
 
-// Byte offsets of the workspace regions (each 256-byte aligned).
+// Byte offsets of the workspace regions (each 256-byte aligned).  The
+// regions of plain data grow from the start of the workspace; the regions of
+// tagged hand-off words (t_*, offsets from the tagged region's start) sit at
+// its end, in its last `tagged` bytes, so that plain data a call with other
+// sizes leaves behind never lands where a call polls tagged words (given a
+// workspace sized for the largest sizes it serves).
 struct Layout {
   size_t sync, logits, ids, wts, count, offset, route_list, active, n_active;
   size_t h, act, y, ssq, moe_out, moe_rep, u, partial;
-  size_t pool_part, unpool_part, pool_cnt, unpool_cnt, qkv_cnt, qkv_part, total;
+  size_t pool_part, unpool_part, pool_cnt, unpool_cnt, qkv_cnt, qkv_part;
+  size_t t_logits, t_routes, t_h, t_hn, t_act, tagged;
+  size_t total;
 };
 
 Layout layout_of(const mb_dims &d);
+
+// Start of the tagged region in a workspace of ws_bytes (>= L.total) bytes.
+inline size_t tagged_base(const Layout &L, size_t ws_bytes) { return (ws_bytes - L.tagged) & ~(size_t)255; }
 
 template <typename T>
 inline T *at(void *ws, size_t off) {
