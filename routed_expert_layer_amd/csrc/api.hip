@@ -30,7 +30,6 @@ Layout layout_of(const mb_dims &d) {
   static_assert(kMaxRows <= kSyncMaxRows, "the counter sets cover every row count");
   L.sync = take(kSyncWords * 4);
   L.pool_cnt = take((P / 16) * 4);
-  L.unpool_cnt = take((H / 16) * 4);
   L.qkv_cnt = take(kMaxQkvGroups * 4);
   L.logits = take(b * E * 4);
   L.ids = take(R * 4);
@@ -254,7 +253,6 @@ BlockParams base_params(const mb_dims &d, const mb_weights *w, void *ws, size_t 
   p.act = at<uint16_t>(ws, L.act);
   p.moe_rep = at<uint16_t>(ws, L.moe_rep);
   p.pool_cnt = at<unsigned>(ws, L.pool_cnt);
-  p.unpool_cnt = at<unsigned>(ws, L.unpool_cnt);
   p.sync = at<unsigned>(ws, L.sync);
   p.h = at<uint16_t>(ws, L.h);
   p.moe_out = at<uint16_t>(ws, L.moe_out);
@@ -272,17 +270,6 @@ BlockParams base_params(const mb_dims &d, const mb_weights *w, void *ws, size_t 
   p.hn_t = at<uint32_t>(ws, tb + L.t_hn);
   p.act_t = at<uint32_t>(ws, tb + L.t_act);
   return p;
-}
-
-// Split-K factor of a projection with `ntiles` 16-feature tiles over
-// `nchunks` 32-element chunks: as many splits as the `slots` workgroups not
-// taken by the phase's other tasks allow (each workgroup then runs at most
-// one task of the phase), at most kMaxSplitK, and at least 16 chunks each.
-int split_for(int ntiles, int nchunks, int slots) {
-  int ks = ntiles > 0 ? slots / ntiles : 1;
-  if (ks > kMaxSplitK) ks = kMaxSplitK;
-  while (ks > 1 && nchunks / ks < 16) --ks;
-  return ks < 1 ? 1 : ks;
 }
 
 // The next-QKV projection as a step of the persistent launch: 64-feature
@@ -355,19 +342,23 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
     while (ks > 1 && (p.H % ks != 0 || (p.H / ks) % 32 != 0)) --ks;
     p.pool_ks = ks;
   }
-  // The unpooler: 16-feature tiles with every weight requested before the
-  // wait at few rows; at many rows 64-feature tiles, so that the MoE output
-  // is read once per 64 features, split along P to fill the grid (its tasks
-  // follow the finalize tasks, which all end before any unpooler work can
-  // start, so the whole grid is theirs).
-  p.unpool_wide = p.b > 16 ? 1 : 0;
+  // The unpooler: at few rows, tasks of kUnpoolTiles 16-feature tiles over
+  // the fewest contraction splits that let every wave request all its
+  // weights before the wait (at most kUnpoolChunks 32-element chunks each);
+  // at many rows (or contractions too long for that) 64-feature tiles, so
+  // that the MoE output is read once per 64 features, split along P to fill
+  // the grid (its tasks follow the finalize tasks, which all end before any
+  // unpooler work can start, so the whole grid is theirs).
+  int narrow_ks = 1;
+  while (narrow_ks < kMaxSplitK && (p.P / 32 + narrow_ks - 1) / narrow_ks > kBlockWaves * kUnpoolChunks) ++narrow_ks;
+  p.unpool_wide = (p.b > 16 || (p.P / 32 + narrow_ks - 1) / narrow_ks > kBlockWaves * kUnpoolChunks) ? 1 : 0;
   if (p.unpool_wide) {
     const int groups = (p.H + 63) / 64;
     int ks = std::min(kMaxSplitK, std::max(1, grid / groups));
     while (ks > 1 && (p.P % ks != 0 || (p.P / ks) % 32 != 0)) --ks;
     p.unpool_ks = ks;
   } else {
-    p.unpool_ks = split_for(p.H / 16, p.P / 32, grid - n_fin - n_boundary);
+    p.unpool_ks = narrow_ks;
   }
   p.n_pool_tiles = (p.P + 63) / 64;
   p.needs_routing = needs_routing ? 1 : 0;
@@ -381,7 +372,7 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   p.h_tagged = st.pool ? 1 : 0;
   p.has_up = st.experts ? 1 : 0;
   p.n_fin = n_fin;
-  p.n_unpool = st.unpool ? (p.unpool_wide ? (p.H + 63) / 64 : p.H / 16) * p.unpool_ks : 0;
+  p.n_unpool = st.unpool ? (p.unpool_wide ? (p.H + 63) / 64 : p.H / (16 * kUnpoolTiles)) * p.unpool_ks : 0;
   p.n_boundary = n_boundary;
   MB_HIP(launch_block(p, grid, lds, s));
   *used = true;

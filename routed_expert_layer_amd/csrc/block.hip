@@ -54,7 +54,6 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / MB_WAVE;
 static_assert(kWaves == kBlockWaves, "routing LDS is laid out per wave");
 static_assert(kRouterRowBlock == kWaves, "a router task covers as many rows as it has waves");
-constexpr int kPoolMG = 4;      // 16-row groups per projection pass
 // 128-element weight chunks a wave keeps in flight in an up / a down unit.
 constexpr int kRingUp = 4, kRingDown = 4;
 // Down units of at most this many chunks (in the streaming layout, passes of
@@ -63,7 +62,6 @@ constexpr int kDownAll = 8;
 static_assert(kRingUp % 4 == 0 && kRingDown % 4 == 0, "one scale load covers four chunks");
 static_assert((kStageChunkRows / 32) % kRingUp == 0 && (kStageChunkRows / 32) % kRingDown == 0,
               "activation segments hold whole rounds of chunks");
-constexpr int kProjBatch = 8;   // 32-element projection chunks a wave requests at once
 constexpr int kRouterBatch = 4;   // router element blocks a thread requests at once (x 4 rows)
 constexpr int kBoundBatch = 4;   // pre-norm element groups a thread requests at once
 
@@ -824,7 +822,7 @@ __device__ __forceinline__ void prepare_routing(const BlockParams &p, const Deps
 
 // ---------------------------------------------------------------- projections
 
-constexpr size_t kProjRedBytes = kWaves * kPoolMG * MB_WAVE * sizeof(f32x4_t);
+constexpr size_t kProjRedBytes = 4 * kWaves * MB_WAVE * sizeof(f32x4_t);
 __device__ __forceinline__ int *proj_flag(unsigned char *lds) {
   return reinterpret_cast<int *>(lds + kProjRedBytes);
 }
@@ -943,106 +941,74 @@ __device__ __forceinline__ void proj_wide_sum(const float *part, uint16_t *out, 
   }
 }
 
-// One task of out[t, n] = bf16(sum_k a[t, k] w[n, k]): a 16-feature tile and
-// contraction split ks of ks_count, the split's 32-element chunks dealt to the
-// four waves, each requesting up to kProjBatch chunks at once; 16-row groups
-// of activations share each weight fragment (weights in the MFMA A operand,
-// activations in B, read coherently when another workgroup of the launch
-// wrote them: kCoherentA).  The first weight chunks are requested
-// before waiting for `a` (step counter wait_ev), unless wait_first puts the
-// wait before everything; padding chunks and rows load zeros.
-// With ks_count > 1 the fp32 partials go to `part`; then either the consumer
-// adds them (defer_sum) or the last split to finish (tile counter) adds them
-// in split order and writes bf16.  Returns true when the task's part of the
-// output is complete: always with defer_sum, else in the workgroup that
-// completed the tile.
-template <bool kCoherentA>
-__device__ __forceinline__ bool proj_task(const Deps &d, const uint16_t *a, const uint16_t *w, uint16_t *out,
-                                          int rows, int n_out, int kdim, int ks_count, float *part,
-                                          unsigned *tile_ctr, int wait_ev, int wait_arrivals, bool wait_first,
-                                          int task, bool defer_sum, unsigned char *lds) {
+// Unpooler task at few rows (b <= 16): u[t, n] = sum_k moe_out[t, k] Wu[n, k]
+// over features n0 = 32 grp .. + 31 (two 16-feature MFMA tiles, the weights
+// in the A operand) and the contraction split q of ks (32-element chunks
+// [q cps, (q + 1) cps), dealt to the waves in turn), for every row t (the B
+// operand: lane r16 reads row r16 of the MoE output, from the copy `mo`).
+// Every weight chunk of the task is requested before the wait for the
+// finalize tasks (kUnpoolChunks per wave at most: the host sizes the split
+// so), so that only the MoE output is read after it.  The waves' sums are
+// added in wave order through LDS; the fp32 partial goes to part[q]
+// ([ks][b][H]), or u in bf16 when ks == 1.
+constexpr int kUnpoolActBatch = 4;  // activation chunks a wave requests at once
+__device__ __forceinline__ void unpool_task(const BlockParams &p, const Deps &d, const uint16_t *mo, int task,
+                                            unsigned char *lds) {
   const Lane L;
-  const int nchunks = kdim / 32;
-  const int cpw = (nchunks + ks_count - 1) / ks_count;
-  f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);  // [kWaves][kPoolMG][64]
-  int *flag = proj_flag(lds);
-  const int tile = task / ks_count, ks = task % ks_count;
-  const int c_begin = ks * cpw, c_end = min(nchunks, c_begin + cpw);
-  const rsrc_t rw = make_rsrc(w + (size_t)tile * 16 * kdim), ra = make_rsrc(a), ro = make_rsrc(out),
-               rp = make_rsrc(part);
-  const uint32_t wrow = (uint32_t)((L.r16 * kdim + 8 * L.g) * 2);
-  bool waited = false;
-  if (wait_first) {
-    wait_step(d, wait_ev, wait_arrivals);
-    waited = true;
+  const int P = p.P, H = p.H, ks = p.unpool_ks;
+  const int grp = task / ks, q = task % ks;
+  const int nch = P / 32, cps = (nch + ks - 1) / ks;
+  const int c_begin = q * cps, c_end = min(nch, c_begin + cps);
+  const int n0 = grp * 16 * kUnpoolTiles;
+  const rsrc_t rw = make_rsrc(p.unpool_w), ra = make_rsrc(mo);
+  u32x4_t W[kUnpoolTiles][kUnpoolChunks];
+#pragma unroll
+  for (int t = 0; t < kUnpoolTiles; ++t) {
+    const int row = n0 + 16 * t + L.r16;
+    const uint32_t wrow = row < H ? (uint32_t)(((size_t)row * P + 8 * L.g) * 2) : kOob;
+#pragma unroll
+    for (int i = 0; i < kUnpoolChunks; ++i) {
+      const int c = c_begin + L.wave + kWaves * i;
+      W[t][i] = ld_nt16(rw, (wrow != kOob && c < c_end) ? wrow + (uint32_t)c * 64u : kOob);
+    }
   }
-  for (int rb = 0; rb < rows; rb += 16 * kPoolMG) {
-    f32x4_t acc[kPoolMG];
+  wait_step(d, kCtrFin, p.n_fin);
+  f32x4_t acc[kUnpoolTiles];
 #pragma unroll
-    for (int mg = 0; mg < kPoolMG; ++mg) acc[mg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int c = c_begin + L.wave; c < c_end || !waited; c += kWaves * kProjBatch) {
-      u32x4_t wv[kProjBatch];
+  for (int t = 0; t < kUnpoolTiles; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint32_t arow = L.r16 < p.b ? (uint32_t)(((size_t)L.r16 * P + 8 * L.g) * 2) : kOob;
 #pragma unroll
-      for (int u = 0; u < kProjBatch; ++u) {
-        const int cc = c + kWaves * u;
-        wv[u] = ld_nt16(rw, cc < c_end ? wrow + (uint32_t)cc * 64u : kOob);
-      }
-      if (!waited) {
-        wait_step(d, wait_ev, wait_arrivals);
-        waited = true;
-        if (c >= c_end) break;
-      }
+  for (int i0 = 0; i0 < kUnpoolChunks; i0 += kUnpoolActBatch) {
+    u32x4_t A[kUnpoolActBatch];
 #pragma unroll
-      for (int mg = 0; mg < kPoolMG; ++mg) {
-        if (rb + mg * 16 >= rows) break;
-        const int t = rb + mg * 16 + L.r16;
-        const uint32_t arow = t < rows ? (uint32_t)(((size_t)t * kdim + 8 * L.g) * 2) : kOob;
-        u32x4_t av[kProjBatch];
-#pragma unroll
-        for (int u = 0; u < kProjBatch; ++u) {
-          const int cc = c + kWaves * u;
-          const uint32_t off = cc < c_end ? arow + (uint32_t)cc * 64u : kOob;
-          av[u] = kCoherentA ? ld_co16(ra, off) : ld_b128(ra, off);
-        }
-#pragma unroll
-        for (int u = 0; u < kProjBatch; ++u) acc[mg] = mfma_bf16(as_bf16x8(wv[u]), as_bf16x8(av[u]), acc[mg]);
-      }
+    for (int i = 0; i < kUnpoolActBatch; ++i) {
+      const int c = c_begin + L.wave + kWaves * (i0 + i);
+      A[i] = ld_co16(ra, (arow != kOob && c < c_end) ? arow + (uint32_t)c * 64u : kOob);
     }
 #pragma unroll
-    for (int mg = 0; mg < kPoolMG; ++mg) red[(L.wave * kPoolMG + mg) * MB_WAVE + L.lane] = acc[mg];
-    __syncthreads();
-    for (int mg = L.wave; mg < kPoolMG; mg += kWaves) {
-      const int t = rb + mg * 16 + L.r16;
-      if (t >= rows) continue;
-      f32x4_t v = red[(0 * kPoolMG + mg) * MB_WAVE + L.lane];
-      for (int q = 1; q < kWaves; ++q) v += red[(q * kPoolMG + mg) * MB_WAVE + L.lane];
-      const int n0 = tile * 16 + 4 * L.g;
-      if (ks_count == 1)
-        st_co8(ro, (uint32_t)(((size_t)t * n_out + n0) * 2),
+    for (int i = 0; i < kUnpoolActBatch; ++i)
+#pragma unroll
+      for (int t = 0; t < kUnpoolTiles; ++t) acc[t] = mfma_bf16(as_bf16x8(W[t][i0 + i]), as_bf16x8(A[i]), acc[t]);
+  }
+  f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);  // [kWaves][kUnpoolTiles][64]
+#pragma unroll
+  for (int t = 0; t < kUnpoolTiles; ++t) red[(L.wave * kUnpoolTiles + t) * MB_WAVE + L.lane] = acc[t];
+  __syncthreads();
+  // Wave t (< kUnpoolTiles): tile t; lane: row r16, features 4 g .. + 3.
+  if (L.wave < kUnpoolTiles && L.r16 < p.b) {
+    const int t = L.wave;
+    f32x4_t v = red[t * MB_WAVE + L.lane];
+    for (int w = 1; w < kWaves; ++w) v += red[(w * kUnpoolTiles + t) * MB_WAVE + L.lane];
+    const int n = n0 + 16 * t + 4 * L.g;
+    if (n < H) {
+      if (ks == 1)
+        st_co8(make_rsrc(p.u), (uint32_t)(((size_t)L.r16 * H + n) * 2),
                u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
       else
-        st_co16(rp, (uint32_t)((((size_t)ks * rows + t) * n_out + n0) * 4), __builtin_bit_cast(u32x4_t, v));
+        st_co16(make_rsrc(p.unpool_part), (uint32_t)((((size_t)q * p.b + L.r16) * H + n) * 4),
+                __builtin_bit_cast(u32x4_t, v));
     }
-    __syncthreads();
   }
-  if (ks_count == 1 || defer_sum) return true;
-  if (!last_arrival(&tile_ctr[tile], (unsigned)ks_count, flag)) return false;
-  for (int idx = tid(); idx < rows * 4; idx += kThreads) {
-    const int t = idx / 4, n0 = tile * 16 + 4 * (idx % 4);
-    f32x4_t part_v[kMaxSplitK];
-#pragma unroll
-    for (int q = 0; q < kMaxSplitK; ++q)
-      part_v[q] = __builtin_bit_cast(
-          f32x4_t, ld_co16(rp, q < ks_count ? (uint32_t)((((size_t)q * rows + t) * n_out + n0) * 4) : kOob));
-    f32x4_t v = part_v[0];
-#pragma unroll
-    for (int q = 1; q < kMaxSplitK; ++q)
-      if (q < ks_count) v += part_v[q];
-    st_co8(ro, (uint32_t)(((size_t)t * n_out + n0) * 2),
-           u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
-  }
-  if (tid() == 0) __hip_atomic_store(&tile_ctr[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return true;
 }
 
 // Optional pre-expert norm of h row t: thread i takes elements 2i + 512 m,
@@ -2137,8 +2103,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
           proj_wide<true>(make_rsrc(mo), p.unpool_w, p.b, p.H, p.P, i / p.unpool_ks, i % p.unpool_ks, p.unpool_ks,
                           p.unpool_part, p.u, nullptr, 0u, scratch, [&]() { wait_step(d, kCtrFin, p.n_fin); });
         } else {
-          proj_task<true>(d, mo, p.unpool_w, p.u, p.b, p.H, p.P, p.unpool_ks, p.unpool_part, p.unpool_cnt, kCtrFin,
-                          p.n_fin, false, i, true, scratch);
+          unpool_task(p, d, mo, i, scratch);
         }
         signal_step(d, kCtrUnpool);
         stamp(p, 16);

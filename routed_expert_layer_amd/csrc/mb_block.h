@@ -79,6 +79,10 @@ __host__ __device__ constexpr size_t sync_line_set(int set) { return 1 + kGenLin
 constexpr size_t kSyncWords = sync_line_set(2) * kLine;
 
 constexpr int kRouteReps = 8;  // copies of the tagged routes (each workgroup polls one)
+// The few-row unpooler's tasks: kUnpoolTiles 16-feature tiles over a
+// contraction split of at most 4 kUnpoolChunks 32-element chunks.
+constexpr int kUnpoolTiles = 2;
+constexpr int kUnpoolChunks = 12;
 constexpr int kFinChunk = 1024;  // features per finalize task (4 per thread: the most one task covers)
 constexpr int kMaxPoolSplit = 32;  // contraction splits of the pooler
 constexpr int kMoeReplicas = 8;  // copies of the MoE output for the unpooler tasks
@@ -143,7 +147,7 @@ struct BlockParams {
   float *logits_f;  // the router's fp32 logits
   float *pool_part, *unpool_part, *y, *ssq;
   uint16_t *act, *moe_rep;  // moe_rep: kMoeReplicas copies of [b, P]
-  unsigned *pool_cnt, *unpool_cnt, *sync;
+  unsigned *pool_cnt, *sync;
   int64_t *timeline;  // optional [grid][kTimelineSlots]
   // MXFP4 activations into the experts (streaming layout).  Last, so that the
   // other fields keep their kernel-argument offsets.

@@ -24,7 +24,7 @@ constexpr int kMaxSplitK = 8;          // split-K factor of the bf16 projections
 struct Layout {
   size_t sync, logits, ids, wts, count, offset, route_list, active, n_active;
   size_t h, act, y, ssq, moe_out, moe_rep, u, partial;
-  size_t pool_part, unpool_part, pool_cnt, unpool_cnt, qkv_cnt, qkv_part;
+  size_t pool_part, unpool_part, pool_cnt, qkv_cnt, qkv_part;
   size_t t_logits, t_routes, t_h, t_hn, t_act, tagged;
   size_t total;
 };
