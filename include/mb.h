@@ -59,7 +59,9 @@ enum {
   MB_ERR_UNSUPPORTED = 3, /* outside the limits above */
   MB_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
   MB_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than mb_workspace_bytes */
-  MB_ERR_HIP = 6          /* a kernel launch failed */
+  MB_ERR_HIP = 6,         /* a kernel launch failed */
+  MB_ERR_ABORTED = 7      /* (mb_workspace_status) a launch on the workspace
+                             gave up a wait: its results are not to be trusted */
 };
 
 /* Scoring functions ([muse_moe_runner] MuseSpark1xRouter: the score
@@ -311,6 +313,25 @@ int mb_next_qkv(const mb_dims *dims, const uint16_t *x_next, const uint16_t *w_q
  * `stream`.  MB_ERR_DIMS if n <= 0 or gain_center is not finite. */
 int mb_effective_norm_weight(const float *weight, int32_t n, float gain_center, int32_t zero_centered,
                              uint16_t *out, void *stream);
+
+/* Whether a launch on this workspace gave up a wait since the workspace was
+ * zero-filled or last reset.  The block kernel's workgroups hand work to one
+ * another inside the launch, and every wait of one on another is bounded; a
+ * wait that runs out (some workgroups never became resident together with the
+ * others, say, because another kernel held compute units) makes the launch
+ * drain without its results, and records it in the workspace.  Later
+ * launches on the workspace compute as usual; the record stays until
+ * mb_workspace_reset.  Enqueues on `stream` the write of MB_OK or
+ * MB_ERR_ABORTED to *status (int32, device memory), readable once the stream
+ * has reached it; allocates nothing, does not synchronise.  Returns MB_OK
+ * (enqueued), MB_ERR_NULL, MB_ERR_ALIGN, MB_ERR_WORKSPACE (smaller than the
+ * launch state every workspace starts with) or MB_ERR_HIP. */
+int mb_workspace_status(const void *workspace, size_t workspace_bytes, int32_t *status, void *stream);
+
+/* Clears the record mb_workspace_status reads (and nothing else: the
+ * workspace stays ready for the next call).  Enqueued on `stream`; the same
+ * returns as mb_workspace_status (no status argument). */
+int mb_workspace_reset(void *workspace, size_t workspace_bytes, void *stream);
 
 /* A static, human-readable reason for a status code. */
 const char *mb_status_string(int status);

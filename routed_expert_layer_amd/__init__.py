@@ -33,10 +33,13 @@ EXPORTS = (
     "mb_attn_boundary",
     "mb_next_qkv",
     "mb_effective_norm_weight",
+    "mb_workspace_status",
+    "mb_workspace_reset",
     "mb_status_string",
 )
 
-MB_OK, MB_ERR_NULL, MB_ERR_DIMS, MB_ERR_UNSUPPORTED, MB_ERR_ALIGN, MB_ERR_WORKSPACE, MB_ERR_HIP = range(7)
+(MB_OK, MB_ERR_NULL, MB_ERR_DIMS, MB_ERR_UNSUPPORTED, MB_ERR_ALIGN, MB_ERR_WORKSPACE, MB_ERR_HIP,
+ MB_ERR_ABORTED) = range(8)
 MB_SCORING_SIGMOID, MB_SCORING_SOFTMAX = 0, 1
 MB_LOGITS_OUT, MB_LOGITS_IN = 1, 2
 
@@ -98,6 +101,8 @@ def lib() -> ctypes.CDLL:
         L.mb_attn_boundary.argtypes = [P(Dims), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.mb_next_qkv.argtypes = [P(Dims), _vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_size_t, _vp]
         L.mb_effective_norm_weight.argtypes = [_vp, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, _vp, _vp]
+        L.mb_workspace_status.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
+        L.mb_workspace_reset.argtypes = [_vp, ctypes.c_size_t, _vp]
         L.mb_status_string.argtypes = [ctypes.c_int]
         L.mb_status_string.restype = ctypes.c_char_p
         for name in EXPORTS:
@@ -244,6 +249,20 @@ def mb_effective_norm_weight(weight, gain_center: float = 0.0, zero_centered: bo
                                           int(bool(zero_centered)), _p(out), _stream()),
            "mb_effective_norm_weight")
     return out
+
+
+def mb_workspace_status(ws: torch.Tensor) -> torch.Tensor:
+    """A device int32 tensor receiving MB_OK, or MB_ERR_ABORTED if a launch on
+    this workspace gave up a wait since it was zero-filled or reset (read it
+    after the current stream has reached this call)."""
+    out = torch.empty(1, dtype=torch.int32, device=ws.device)
+    _check(lib().mb_workspace_status(_p(ws), ws.numel(), _p(out), _stream()), "mb_workspace_status")
+    return out
+
+
+def mb_workspace_reset(ws: torch.Tensor) -> None:
+    """Clear the record mb_workspace_status reads."""
+    _check(lib().mb_workspace_reset(_p(ws), ws.numel(), _stream()), "mb_workspace_reset")
 
 
 def mb_moe_block(dims: Dims, x, weights: Weights, stream, x_next, ws: torch.Tensor,

@@ -67,6 +67,20 @@ Layout layout_of(const mb_dims &d) {
   return L;
 }
 
+// The abort record (word 1 of the launch state, at the workspace start): read
+// into *status as MB_OK / MB_ERR_ABORTED, or cleared (status NULL).  One
+// thread; a kernel rather than a memset or copy, so that a captured graph
+// replays it as it is.
+__global__ void abort_word_kernel(unsigned *state, int32_t *status) {
+  if (status) *status = __hip_atomic_load(state + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? MB_ERR_ABORTED : MB_OK;
+  else __hip_atomic_store(state + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_abort_word(void *workspace, int32_t *status, hipStream_t s) {
+  hipLaunchKernelGGL(abort_word_kernel, dim3(1), dim3(1), 0, s, static_cast<unsigned *>(workspace), status);
+  return hipGetLastError();
+}
+
 }  // namespace mb
 
 using namespace mb;
@@ -636,6 +650,22 @@ int mb_effective_norm_weight(const float *weight, int32_t n, float gain_center, 
   return MB_OK;
 }
 
+int mb_workspace_status(const void *workspace, size_t workspace_bytes, int32_t *status, void *stream) {
+  if (!workspace || !status) return MB_ERR_NULL;
+  if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(status) & 3u)) return MB_ERR_ALIGN;
+  if (workspace_bytes < kSyncWords * 4) return MB_ERR_WORKSPACE;
+  MB_HIP(launch_abort_word(const_cast<void *>(workspace), status, (hipStream_t)stream));
+  return MB_OK;
+}
+
+int mb_workspace_reset(void *workspace, size_t workspace_bytes, void *stream) {
+  if (!workspace) return MB_ERR_NULL;
+  if (!aligned16(workspace)) return MB_ERR_ALIGN;
+  if (workspace_bytes < kSyncWords * 4) return MB_ERR_WORKSPACE;
+  MB_HIP(launch_abort_word(workspace, nullptr, (hipStream_t)stream));
+  return MB_OK;
+}
+
 const char *mb_status_string(int status) {
   switch (status) {
     case MB_OK: return "ok";
@@ -650,6 +680,9 @@ const char *mb_status_string(int status) {
     case MB_ERR_WORKSPACE: return "workspace (or packed-experts buffer) missing or smaller than "
                                   "mb_workspace_bytes (mb_packed_experts_bytes)";
     case MB_ERR_HIP: return "a kernel launch failed";
+    case MB_ERR_ABORTED: return "a launch on this workspace gave up a wait between its workgroups (not all "
+                                "of them were resident together): its results are not to be trusted; "
+                                "mb_workspace_reset clears the record";
     default: return "unknown status";
   }
 }

@@ -181,22 +181,31 @@ __device__ __forceinline__ bool last_arrival(unsigned *c, unsigned of, int *flag
   return last;
 }
 
+// A polling wave, every 256 polls: whether to stop waiting.  Every wait is
+// bounded: after kSpinLimit polls it gives up and raises the abort word (word
+// 1 of the launch state) to this launch's tag, and every wait of the launch
+// that sees it gives up too, so the grid drains.  The word keeps the tag (it
+// only changes when a later launch times out, or when mb_workspace_reset
+// clears it), so the caller can learn that a launch's results are not to be
+// trusted (mb_workspace_status); later launches compare it with their own
+// tag, so they wait and compute as usual.
+__device__ __forceinline__ bool give_up(const Deps &d, unsigned &spins) {
+  if ((++spins & 255u) != 0) return false;
+  if (__hip_atomic_load(d.abort_word(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == d.tag()) return true;
+  if (spins > kSpinLimit) {
+    if (tid() % MB_WAVE == 0) store_co(d.abort_word(), d.tag());
+    return true;
+  }
+  return false;
+}
+
 // One wave polls, each lane its own word, until every lane's has reached
-// `target`.  Bounded: on timeout the abort word is raised, and a wait that
-// sees it returns at once, so the launch drains.
+// `target`.  Bounded (give_up).
 __device__ __forceinline__ void poll_ge(const Deps &d, const unsigned *mine, unsigned target) {
-  const int lane = tid() % MB_WAVE;
   unsigned spins = 0;
   while (true) {
     const unsigned have = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (__all((int)(have >= target))) return;
-    if ((++spins & 255u) == 0) {
-      if (__hip_atomic_load(d.abort_word(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
-      if (spins > kSpinLimit) {
-        if (lane == 0) store_co(d.abort_word(), 1u);
-        return;
-      }
-    }
+    if (__all((int)(have >= target)) || give_up(d, spins)) return;
     __builtin_amdgcn_s_sleep(2);
   }
 }
@@ -211,14 +220,7 @@ __device__ __forceinline__ void poll_sum_ge(const Deps &d, const unsigned *first
     const unsigned have = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     unsigned sum = 0;
     for (int l = 0; l < n; ++l) sum += __builtin_amdgcn_readlane(have, l);
-    if (sum >= target) return;
-    if ((++spins & 255u) == 0) {
-      if (__hip_atomic_load(d.abort_word(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
-      if (spins > kSpinLimit) {
-        if (lane == 0) store_co(d.abort_word(), 1u);
-        return;
-      }
-    }
+    if (sum >= target || give_up(d, spins)) return;
     __builtin_amdgcn_s_sleep(2);
   }
 }
@@ -249,18 +251,6 @@ __device__ __forceinline__ void wave_wait_step(const Deps &d, int i, int target)
 // of earlier launches carry their own (older) tags.
 __device__ __forceinline__ void st_tagged(rsrc_t r, uint32_t off, uint32_t v, uint32_t tag) {
   st_co8(r, off, u32x2_t{v, tag});
-}
-
-// A polling wave, every 256 polls: whether to stop waiting (the abort word
-// is up, or this wait has run out of polls and raises it).
-__device__ __forceinline__ bool give_up(const Deps &d, unsigned &spins) {
-  if ((++spins & 255u) != 0) return false;
-  if (__hip_atomic_load(d.abort_word(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return true;
-  if (spins > kSpinLimit) {
-    if (tid() % MB_WAVE == 0) store_co(d.abort_word(), 1u);
-    return true;
-  }
-  return false;
 }
 
 // One wave: until every word its lanes hold (v[i] from offset off[i]; kOob:
@@ -808,7 +798,9 @@ __device__ __forceinline__ void prepare_routing(const BlockParams &p, const Deps
     for (int i = 0; i < kRouteBatch; ++i) {
       const int w = w0 + (int)tid() + kThreads * i;
       if (w < Rn) {
-        const int e = (int)v[i][0];
+        // (An id is below E unless a wait gave up and the word is stale or
+        // never written: then expert 0, so that every index stays in range.)
+        const int e = v[i][0] < (uint32_t)p.E ? (int)v[i][0] : 0;
         R.ids[w] = e;
         mark_route(p, R, w, e);
       } else if (w < R2) {
@@ -2132,8 +2124,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 }  // namespace
 
 // An ordinary launch: the host sizes the grid to what the device holds at
-// once.  Should some workgroups only start after others finished work on
-// another kernel, the waits merely take longer (every one is bounded).
+// once.  Should some workgroups not be resident together with the others
+// (another kernel holding compute units), the resident ones may wait on them
+// until a wait runs out of polls: the launch then drains with its results
+// not to be trusted, and the workspace reports it (mb_workspace_status).
 // The W4A4 kernel, the kernel with the fused next-QKV projection and the
 // kernel with both are built from this file in translation units of their own
 // (block_w4a4.hip, block_qkv.hip, block_w4a4_qkv.hip): sharing one code object

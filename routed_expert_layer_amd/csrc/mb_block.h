@@ -15,7 +15,8 @@ constexpr int kRouterExperts = 4;    // experts per router task when there are m
 
 // Cross-workgroup state, at the workspace start, in 128-byte lines of kLine
 // words so that no two counters share a line:
-//   line 0      word 1: the abort word (set when a wait timed out)
+//   line 0      word 1: the abort record (the tag of the last launch a wait
+//               of which ran out of polls; 0 after a zero-fill or reset)
 //   kGenLines lines   the generation words, one per workgroup index
 //   two counter sets of kSetLines lines each, a set being
 //     kNumCtr x kReplicas lines   step counters (kCtr*), each spread over

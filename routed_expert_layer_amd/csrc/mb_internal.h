@@ -80,6 +80,10 @@ hipError_t launch_experts_finalize(const mb_dims &d, const float *y, const float
 hipError_t launch_pack_experts(const mb_dims &d, const uint8_t *w13, const uint8_t *w13s, const uint8_t *w2,
                                const uint8_t *w2s, uint8_t *packed, hipStream_t s);
 
+// The workspace's abort record: read into *status (MB_OK / MB_ERR_ABORTED),
+// or cleared when status is NULL.
+hipError_t launch_abort_word(void *workspace, int32_t *status, hipStream_t s);
+
 // Effective norm multiplier: out = bf16(weight + add).
 hipError_t launch_norm_weight(const float *weight, int n, float add, uint16_t *out, hipStream_t s);
 

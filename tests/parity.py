@@ -58,10 +58,10 @@ class GpuBlock:
         self.weights = rel.make_weights(**self.wt)
 
     def check_no_abort(self):
-        """Word 1 of the workspace is the persistent kernel's abort flag (a
-        grid-barrier wait ran out of time); it must stay zero."""
-        flag = int(self.ws[4:8].cpu().view(torch.int32)[0])
-        assert flag == 0, "block kernel aborted a barrier wait"
+        """No launch on the workspace gave up a wait (mb_workspace_status)."""
+        st = rel.mb_workspace_status(self.ws)
+        torch.cuda.synchronize()
+        assert int(st.item()) == rel.MB_OK, "a block-kernel launch gave up a wait"
 
     def _routing_bufs(self):
         d = self.blk.dims

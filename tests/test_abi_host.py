@@ -8,7 +8,8 @@ import re
 import pytest
 
 import routed_expert_layer_amd as rel
-from routed_expert_layer_amd import MB_ERR_ALIGN, MB_ERR_DIMS, MB_ERR_NULL, MB_ERR_UNSUPPORTED, MB_ERR_WORKSPACE, MB_OK
+from routed_expert_layer_amd import (MB_ERR_ABORTED, MB_ERR_ALIGN, MB_ERR_DIMS, MB_ERR_NULL, MB_ERR_UNSUPPORTED,
+                                     MB_ERR_WORKSPACE, MB_OK)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -27,7 +28,8 @@ def test_header_declares_the_five_calls():
     names = header_functions()
     for n in ("mb_route", "mb_pool", "mb_experts", "mb_unpool_boundary", "mb_moe_block",
               "mb_workspace_bytes", "mb_packed_experts_bytes", "mb_pack_experts", "mb_status_string",
-              "mb_attn_boundary", "mb_next_qkv", "mb_effective_norm_weight"):
+              "mb_attn_boundary", "mb_next_qkv", "mb_effective_norm_weight", "mb_workspace_status",
+              "mb_workspace_reset"):
         assert n in names
     assert set(names) == set(rel.EXPORTS)
 
@@ -80,8 +82,9 @@ def test_bad_dims_rejected(over, code):
 
 def test_status_strings():
     assert rel.status_string(0) == "ok"
-    for st in range(1, 7):
+    for st in range(1, MB_ERR_ABORTED + 1):
         assert len(rel.status_string(st)) > 10
+    assert "reset" in rel.status_string(MB_ERR_ABORTED)
     assert rel.status_string(99) == "unknown status"
 
 
@@ -244,3 +247,18 @@ def test_fused_qkv_options_checked_before_launch():
     w = full_weights(next_qkv_w=FAKE)
     assert L.mb_moe_block(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE, None, FAKE, 1 << 40,
                           None) == MB_ERR_NULL  # qkvg tap missing
+
+
+def test_workspace_status_and_reset_check_arguments():
+    """The abort record's calls check the workspace (and the status pointer)
+    before enqueuing anything."""
+    lib = rel.lib()
+    big = 1 << 30
+    assert lib.mb_workspace_status(None, big, FAKE, None) == MB_ERR_NULL
+    assert lib.mb_workspace_status(FAKE, big, None, None) == MB_ERR_NULL
+    assert lib.mb_workspace_status(FAKE + 4, big, FAKE, None) == MB_ERR_ALIGN
+    assert lib.mb_workspace_status(FAKE, big, FAKE + 2, None) == MB_ERR_ALIGN
+    assert lib.mb_workspace_status(FAKE, 1024, FAKE, None) == MB_ERR_WORKSPACE
+    assert lib.mb_workspace_reset(None, big, None) == MB_ERR_NULL
+    assert lib.mb_workspace_reset(FAKE + 8, big, None) == MB_ERR_ALIGN
+    assert lib.mb_workspace_reset(FAKE, 1024, None) == MB_ERR_WORKSPACE

@@ -84,3 +84,50 @@ def test_captured_block_replays():
         assert np.array_equal(bits(x_next), want["x_next"]), rep
         # Eager work on the device between replays.
         g.run_block()
+
+
+def test_abort_record_reported_and_reset():
+    r"""A launch whose waits give up is reported by mb_workspace_status until
+    mb_workspace_reset, and does not disturb later launches.  The record is
+    pre-set from the host to the next launch's tag (the generation in the
+    workspace's generation words, plus one), so that every bounded wait of
+    that launch gives up after its first 256 polls and the kernel drains as
+    usual: no wait is made to run out for real."""
+    import routed_expert_layer_amd as rel
+    from synth.device import bits
+    blk = synth.make_block("c0", seed=33, dims=_dims(17))
+    g = GpuBlock(blk)
+    say("[gpu] abort record: a normal launch")
+    want = g.run_block()
+    st = rel.mb_workspace_status(g.ws)
+    torch.cuda.synchronize()
+    assert int(st.item()) == rel.MB_OK
+
+    def launch():
+        stream = g.stream0.clone()
+        x_next = torch.zeros((blk.dims.rows, blk.dims.hidden), dtype=torch.bfloat16, device="cuda")
+        rel.mb_moe_block(g.dims, g.x, g.weights, stream, x_next, g.ws)
+        torch.cuda.synchronize()
+        return stream.cpu().numpy(), bits(x_next)
+
+    gen = int(g.ws[128:132].view(torch.int32).item())  # generation word of workgroup 0 (line 1)
+    g.ws[4:8].view(torch.int32).fill_(gen + 1)
+    say("[gpu] abort record: a launch whose waits give up")
+    launch()
+    st = rel.mb_workspace_status(g.ws)
+    torch.cuda.synchronize()
+    assert int(st.item()) == rel.MB_ERR_ABORTED
+    say("[gpu] abort record: the next launch computes as usual, the record stays")
+    s1, x1 = launch()
+    assert np.array_equal(s1, want["stream"]) and np.array_equal(x1, want["x_next"])
+    st = rel.mb_workspace_status(g.ws)
+    torch.cuda.synchronize()
+    assert int(st.item()) == rel.MB_ERR_ABORTED
+    say("[gpu] abort record: reset")
+    rel.mb_workspace_reset(g.ws)
+    st = rel.mb_workspace_status(g.ws)
+    torch.cuda.synchronize()
+    assert int(st.item()) == rel.MB_OK
+    s2, x2 = launch()
+    assert np.array_equal(s2, want["stream"]) and np.array_equal(x2, want["x_next"])
+    g.check_no_abort()
