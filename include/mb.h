@@ -60,9 +60,16 @@ enum {
   MB_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
   MB_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than mb_workspace_bytes */
   MB_ERR_HIP = 6,         /* a kernel launch failed */
-  MB_ERR_ABORTED = 7      /* (mb_workspace_status) a launch on the workspace
+  MB_ERR_ABORTED = 7,     /* (mb_workspace_status) a launch on the workspace
                              gave up a wait: its results are not to be trusted */
+  MB_ERR_SCRATCH = 8      /* (mb_moe_block_noalloc) the sizes need more than its
+                             static scratch */
 };
+
+/* The static scratch of mb_moe_block_noalloc, per GPU: its size, and the
+ * part at its end that holds the block kernel's hand-off words. */
+#define MB_NOALLOC_SCRATCH_BYTES (64u << 20)
+#define MB_NOALLOC_TAGGED_BYTES (8u << 20)
 
 /* Scoring functions ([muse_moe_runner] MuseSpark1xRouter: the score
  * normalisation is "sigmoid" or "softmax"; anything else is a ValueError). */
@@ -249,6 +256,29 @@ int mb_unpool_boundary(const mb_dims *dims, const uint16_t *moe_out,
 int mb_moe_block(const mb_dims *dims, const uint16_t *x, const mb_weights *w,
                  float *stream, uint16_t *x_next, const mb_block_taps *taps,
                  void *workspace, size_t workspace_bytes, void *stream_handle);
+
+/* mb_moe_block for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and results, with the workspace replaced by a static
+ * device array of MB_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds
+ * on every GPU it runs on, until the process ends.  Nothing is allocated
+ * or freed, by the library or any library it calls.
+ *   - Sizes: the workspace layout's buffers must fit in the first 56 MiB and
+ *     its hand-off words in the last MB_NOALLOC_TAGGED_BYTES (8 MiB), else
+ *     MB_ERR_SCRATCH before anything is enqueued.  Up to 94 rows fit at
+ *     H 4096, P 2048, I 1024, E 64, top_k 4 and up to 55 rows at H 7168,
+ *     P 3072, I 1536, E 128, top_k 8; mb_moe_block with a workspace serves
+ *     larger sizes.
+ *   - The first call on a GPU (with that GPU current) looks up the array's
+ *     address there and enqueues its zero-fill on `stream_handle`.
+ *   - Every call on a GPU shares that GPU's array, which keeps the last
+ *     call's state: calls on one GPU must not overlap (one stream, or
+ *     ordered by events); calls that overlap race and their results are
+ *     undefined.  mb_workspace_status / mb_workspace_reset do not reach it.
+ *   - Other arguments, outputs and errors as mb_moe_block. */
+int mb_moe_block_noalloc(const mb_dims *dims, const uint16_t *x, const mb_weights *w,
+                         float *stream, uint16_t *x_next, const mb_block_taps *taps,
+                         void *stream_handle);
 
 /* Bytes of the streaming layout of all E experts (for mb_pack_experts). */
 int mb_packed_experts_bytes(const mb_dims *dims, size_t *bytes);

@@ -28,6 +28,7 @@ EXPORTS = (
     "mb_experts",
     "mb_unpool_boundary",
     "mb_moe_block",
+    "mb_moe_block_noalloc",
     "mb_packed_experts_bytes",
     "mb_pack_experts",
     "mb_attn_boundary",
@@ -39,7 +40,7 @@ EXPORTS = (
 )
 
 (MB_OK, MB_ERR_NULL, MB_ERR_DIMS, MB_ERR_UNSUPPORTED, MB_ERR_ALIGN, MB_ERR_WORKSPACE, MB_ERR_HIP,
- MB_ERR_ABORTED) = range(8)
+ MB_ERR_ABORTED, MB_ERR_SCRATCH) = range(9)
 MB_SCORING_SIGMOID, MB_SCORING_SOFTMAX = 0, 1
 MB_LOGITS_OUT, MB_LOGITS_IN = 1, 2
 
@@ -96,6 +97,7 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_size_t, _vp]
         L.mb_moe_block.argtypes = [P(Dims), _vp, P(Weights), _vp, _vp, P(Taps), _vp,
                                    ctypes.c_size_t, _vp]
+        L.mb_moe_block_noalloc.argtypes = [P(Dims), _vp, P(Weights), _vp, _vp, P(Taps), _vp]
         L.mb_packed_experts_bytes.argtypes = [P(Dims), P(ctypes.c_size_t)]
         L.mb_pack_experts.argtypes = [P(Dims), P(Weights), _vp, ctypes.c_size_t, _vp]
         L.mb_attn_boundary.argtypes = [P(Dims), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -270,3 +272,11 @@ def mb_moe_block(dims: Dims, x, weights: Weights, stream, x_next, ws: torch.Tens
     _check(lib().mb_moe_block(ctypes.byref(dims), _p(x), ctypes.byref(weights), _p(stream),
                               _p(x_next), None if taps is None else ctypes.byref(taps), _p(ws),
                               ws.numel(), _stream()), "mb_moe_block")
+
+
+def mb_moe_block_noalloc(dims: Dims, x, weights: Weights, stream, x_next,
+                         taps: Optional[Taps] = None) -> None:
+    """mb_moe_block on the library's static per-GPU scratch (no workspace)."""
+    _check(lib().mb_moe_block_noalloc(ctypes.byref(dims), _p(x), ctypes.byref(weights), _p(stream),
+                                      _p(x_next), None if taps is None else ctypes.byref(taps),
+                                      _stream()), "mb_moe_block_noalloc")

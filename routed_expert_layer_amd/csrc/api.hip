@@ -4,10 +4,17 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "mb_block.h"
 #include "mb_internal.h"
 #include "mb_sync.h"
+
+// The workspace of mb_moe_block_noalloc: a static device array, of which
+// every GPU the library runs on holds its own copy (at its own address) until
+// the process ends.  Host code uses the per-device address that
+// hipGetSymbolAddress returns for it, never the array's name.
+static __device__ __align__(256) unsigned char scratch[MB_NOALLOC_SCRATCH_BYTES];
 
 namespace mb {
 
@@ -81,6 +88,13 @@ hipError_t launch_abort_word(void *workspace, int32_t *status, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Zero n 16-byte words (a kernel, not a memset: a captured graph replays it
+// as it is).
+__global__ void zero16_kernel(uint4 *p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 }  // namespace mb
 
 using namespace mb;
@@ -116,6 +130,17 @@ int check_ws(const mb_dims *d, const void *ws, size_t bytes) {
   return MB_OK;
 }
 
+// The static scratch serves a call when its buffers fit before the last
+// MB_NOALLOC_TAGGED_BYTES and its hand-off words fit in them: then the
+// buffers of one call never overlap the hand-off words of another (whatever
+// their sizes), so no stale buffer contents can pass for a hand-off word.
+int check_scratch(const mb_dims *d) {
+  const Layout L = layout_of(*d);
+  if (L.tagged > (size_t)MB_NOALLOC_TAGGED_BYTES) return MB_ERR_SCRATCH;
+  if (L.total - L.tagged > (size_t)MB_NOALLOC_SCRATCH_BYTES - MB_NOALLOC_TAGGED_BYTES) return MB_ERR_SCRATCH;
+  return MB_OK;
+}
+
 // Required pointers must be non-NULL; every given pointer must be aligned.
 int need(std::initializer_list<const void *> ptrs) {
   for (const void *p : ptrs)
@@ -141,6 +166,32 @@ int maybe(std::initializer_list<const void *> ptrs) {
   do {                                            \
     if ((expr) != hipSuccess) return MB_ERR_HIP;  \
   } while (0)
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device (with it current), when the array is also zero-filled on the
+// caller's stream: the launch state, the tile counters and the hand-off words
+// must start at zero, as in a zero-filled workspace.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+int noalloc_scratch(hipStream_t s, void **out) {
+  int dev = 0;
+  MB_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return MB_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    MB_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr) return MB_ERR_HIP;
+    hipLaunchKernelGGL(zero16_kernel, dim3(1024), dim3(256), 0, s, static_cast<uint4 *>(ptr),
+                       (size_t)MB_NOALLOC_SCRATCH_BYTES / 16);
+    MB_HIP(hipGetLastError());
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MB_OK;
+}
 
 int check_weights_route(const mb_weights *w, int flags, const uint16_t *x) {
   if (!w) return MB_ERR_NULL;
@@ -393,6 +444,80 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   return MB_OK;
 }
 
+// The arguments of the whole-block call (both forms of it).
+int check_block_args(const mb_dims *dims, const uint16_t *x, const mb_weights *w, float *stream,
+                     uint16_t *x_next, const mb_block_taps *taps) {
+  MB_TRY(check_dims(dims));
+  MB_TRY(check_weights_route(w, 0, x));
+  MB_TRY(check_weights_pool(w));
+  MB_TRY(check_weights_experts(w));
+  MB_TRY(check_weights_boundary(w));
+  MB_TRY(need({stream, x_next}));
+  if (taps)
+    MB_TRY(maybe({taps->logits, taps->topk_ids, taps->topk_w, taps->count, taps->offset, taps->route_list,
+                  taps->active, taps->n_active, taps->h, taps->moe_out, taps->u, taps->timeline, taps->act,
+                  taps->qkvg}));
+  return MB_OK;
+}
+
+// The whole block on a checked workspace `ws` of ws_bytes bytes.
+int run_block_call(const mb_dims &d, const uint16_t *x, const mb_weights *w, float *stream, uint16_t *x_next,
+                   const mb_block_taps *taps, void *ws, size_t ws_bytes, hipStream_t s) {
+  mb_block_taps tp{};
+  if (taps) tp = *taps;
+  const Layout L = layout_of(d);
+  float *logits = tp.logits ? tp.logits : at<float>(ws, L.logits);
+  int32_t *ids = tp.topk_ids ? tp.topk_ids : at<int32_t>(ws, L.ids);
+  float *wts = tp.topk_w ? tp.topk_w : at<float>(ws, L.wts);
+  int32_t *count = tp.count ? tp.count : at<int32_t>(ws, L.count);
+  int32_t *offset = tp.offset ? tp.offset : at<int32_t>(ws, L.offset);
+  int32_t *route_list = tp.route_list ? tp.route_list : at<int32_t>(ws, L.route_list);
+  int32_t *active = tp.active ? tp.active : at<int32_t>(ws, L.active);
+  int32_t *n_active = tp.n_active ? tp.n_active : at<int32_t>(ws, L.n_active);
+  uint16_t *h = tp.h ? tp.h : at<uint16_t>(ws, L.h);
+  uint16_t *moe_out = tp.moe_out ? tp.moe_out : at<uint16_t>(ws, L.moe_out);
+  uint16_t *u = tp.u ? tp.u : at<uint16_t>(ws, L.u);
+  BlockParams p = base_params(d, w, ws, ws_bytes);
+  Steps st;
+  st.router = st.pool = st.experts = st.unpool = true;
+  st.routing_out = tp.topk_ids || tp.topk_w || tp.count || tp.offset || tp.route_list || tp.active ||
+                   tp.n_active || tp.logits;
+  p.x = x;
+  p.logits = tp.logits;
+  p.ids = ids;
+  p.wts = wts;
+  p.count = count;
+  p.offset = offset;
+  p.route_list = route_list;
+  p.active = active;
+  p.n_active = n_active;
+  p.h = h;
+  p.moe_out = moe_out;
+  p.u = u;
+  p.stream = stream;
+  p.x_next = x_next;
+  p.timeline = tp.timeline;
+  p.act_tap = tp.act;
+  p.h_plain = tp.h ? 1 : 0;
+  if (d.qkv_rows > 0) {
+    // The next-QKV projection fused after the boundary.
+    MB_TRY(need({w->next_qkv_w, tp.qkvg}));
+    set_qkv(p, d, w->next_qkv_w, tp.qkvg, ws);
+  }
+  bool used = false;
+  MB_TRY(run_fused(p, st, s, &used));
+  if (used) return MB_OK;
+  if (!has_plain_experts(w)) return MB_ERR_UNSUPPORTED;  // the per-step kernels read the caller's layout
+  MB_TRY(run_route(d, x, w, logits, 0, ids, wts, count, offset, route_list, active, n_active, s));
+  MB_TRY(run_pool(d, x, w, h, ws, s));
+  MB_TRY(run_experts(d, h, wts, offset, route_list, active, n_active, w, moe_out, ws, s, tp.act));
+  MB_TRY(run_unpool_boundary(d, moe_out, w, stream, x_next, u, ws, s));
+  if (d.qkv_rows > 0)
+    MB_HIP(launch_gemm_bf16(x_next, w->next_qkv_w, tp.qkvg, d.rows, d.qkv_rows, d.hidden, at<float>(ws, L.qkv_part),
+                            nullptr, s));
+  return MB_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -512,73 +637,20 @@ int mb_unpool_boundary(const mb_dims *dims, const uint16_t *moe_out, const mb_we
 int mb_moe_block(const mb_dims *dims, const uint16_t *x, const mb_weights *w, float *stream,
                  uint16_t *x_next, const mb_block_taps *taps, void *workspace,
                  size_t workspace_bytes, void *stream_handle) {
-  MB_TRY(check_dims(dims));
-  MB_TRY(check_weights_route(w, 0, x));
-  MB_TRY(check_weights_pool(w));
-  MB_TRY(check_weights_experts(w));
-  MB_TRY(check_weights_boundary(w));
-  MB_TRY(need({stream, x_next}));
-  mb_block_taps tp{};
-  if (taps) {
-    tp = *taps;
-    MB_TRY(maybe({tp.logits, tp.topk_ids, tp.topk_w, tp.count, tp.offset, tp.route_list,
-                  tp.active, tp.n_active, tp.h, tp.moe_out, tp.u, tp.timeline, tp.act, tp.qkvg}));
-  }
+  MB_TRY(check_block_args(dims, x, w, stream, x_next, taps));
   MB_TRY(check_ws(dims, workspace, workspace_bytes));
-  const mb_dims &d = *dims;
-  const Layout L = layout_of(d);
-  void *ws = workspace;
+  return run_block_call(*dims, x, w, stream, x_next, taps, workspace, workspace_bytes,
+                        (hipStream_t)stream_handle);
+}
+
+int mb_moe_block_noalloc(const mb_dims *dims, const uint16_t *x, const mb_weights *w, float *stream,
+                         uint16_t *x_next, const mb_block_taps *taps, void *stream_handle) {
+  MB_TRY(check_block_args(dims, x, w, stream, x_next, taps));
+  MB_TRY(check_scratch(dims));
   const hipStream_t s = (hipStream_t)stream_handle;
-  float *logits = tp.logits ? tp.logits : at<float>(ws, L.logits);
-  int32_t *ids = tp.topk_ids ? tp.topk_ids : at<int32_t>(ws, L.ids);
-  float *wts = tp.topk_w ? tp.topk_w : at<float>(ws, L.wts);
-  int32_t *count = tp.count ? tp.count : at<int32_t>(ws, L.count);
-  int32_t *offset = tp.offset ? tp.offset : at<int32_t>(ws, L.offset);
-  int32_t *route_list = tp.route_list ? tp.route_list : at<int32_t>(ws, L.route_list);
-  int32_t *active = tp.active ? tp.active : at<int32_t>(ws, L.active);
-  int32_t *n_active = tp.n_active ? tp.n_active : at<int32_t>(ws, L.n_active);
-  uint16_t *h = tp.h ? tp.h : at<uint16_t>(ws, L.h);
-  uint16_t *moe_out = tp.moe_out ? tp.moe_out : at<uint16_t>(ws, L.moe_out);
-  uint16_t *u = tp.u ? tp.u : at<uint16_t>(ws, L.u);
-  BlockParams p = base_params(d, w, ws, workspace_bytes);
-  Steps st;
-  st.router = st.pool = st.experts = st.unpool = true;
-  st.routing_out = tp.topk_ids || tp.topk_w || tp.count || tp.offset || tp.route_list || tp.active ||
-                   tp.n_active || tp.logits;
-  p.x = x;
-  p.logits = tp.logits;
-  p.ids = ids;
-  p.wts = wts;
-  p.count = count;
-  p.offset = offset;
-  p.route_list = route_list;
-  p.active = active;
-  p.n_active = n_active;
-  p.h = h;
-  p.moe_out = moe_out;
-  p.u = u;
-  p.stream = stream;
-  p.x_next = x_next;
-  p.timeline = tp.timeline;
-  p.act_tap = tp.act;
-  p.h_plain = tp.h ? 1 : 0;
-  if (d.qkv_rows > 0) {
-    // The next-QKV projection fused after the boundary.
-    MB_TRY(need({w->next_qkv_w, tp.qkvg}));
-    set_qkv(p, d, w->next_qkv_w, tp.qkvg, ws);
-  }
-  bool used = false;
-  MB_TRY(run_fused(p, st, s, &used));
-  if (used) return MB_OK;
-  if (!has_plain_experts(w)) return MB_ERR_UNSUPPORTED;  // the per-step kernels read the caller's layout
-  MB_TRY(run_route(d, x, w, logits, 0, ids, wts, count, offset, route_list, active, n_active, s));
-  MB_TRY(run_pool(d, x, w, h, ws, s));
-  MB_TRY(run_experts(d, h, wts, offset, route_list, active, n_active, w, moe_out, ws, s, tp.act));
-  MB_TRY(run_unpool_boundary(d, moe_out, w, stream, x_next, u, ws, s));
-  if (d.qkv_rows > 0)
-    MB_HIP(launch_gemm_bf16(x_next, w->next_qkv_w, tp.qkvg, d.rows, d.qkv_rows, d.hidden, at<float>(ws, L.qkv_part),
-                            nullptr, s));
-  return MB_OK;
+  void *ws = nullptr;
+  MB_TRY(noalloc_scratch(s, &ws));
+  return run_block_call(*dims, x, w, stream, x_next, taps, ws, (size_t)MB_NOALLOC_SCRATCH_BYTES, s);
 }
 
 int mb_packed_experts_bytes(const mb_dims *dims, size_t *bytes) {
@@ -680,6 +752,9 @@ const char *mb_status_string(int status) {
     case MB_ERR_WORKSPACE: return "workspace (or packed-experts buffer) missing or smaller than "
                                   "mb_workspace_bytes (mb_packed_experts_bytes)";
     case MB_ERR_HIP: return "a kernel launch failed";
+    case MB_ERR_SCRATCH: return "(mb_moe_block_noalloc) the sizes need more than its static scratch: "
+                                "over 56 MiB of buffers or 8 MiB of hand-off words (mb_moe_block "
+                                "with a workspace serves them)";
     case MB_ERR_ABORTED: return "a launch on this workspace gave up a wait between its workgroups (not all "
                                 "of them were resident together): its results are not to be trusted; "
                                 "mb_workspace_reset clears the record";

@@ -8,8 +8,8 @@ import re
 import pytest
 
 import routed_expert_layer_amd as rel
-from routed_expert_layer_amd import (MB_ERR_ABORTED, MB_ERR_ALIGN, MB_ERR_DIMS, MB_ERR_NULL, MB_ERR_UNSUPPORTED,
-                                     MB_ERR_WORKSPACE, MB_OK)
+from routed_expert_layer_amd import (MB_ERR_ABORTED, MB_ERR_ALIGN, MB_ERR_DIMS, MB_ERR_NULL, MB_ERR_SCRATCH,
+                                     MB_ERR_UNSUPPORTED, MB_ERR_WORKSPACE, MB_OK)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -29,7 +29,7 @@ def test_header_declares_the_five_calls():
     for n in ("mb_route", "mb_pool", "mb_experts", "mb_unpool_boundary", "mb_moe_block",
               "mb_workspace_bytes", "mb_packed_experts_bytes", "mb_pack_experts", "mb_status_string",
               "mb_attn_boundary", "mb_next_qkv", "mb_effective_norm_weight", "mb_workspace_status",
-              "mb_workspace_reset"):
+              "mb_workspace_reset", "mb_moe_block_noalloc"):
         assert n in names
     assert set(names) == set(rel.EXPORTS)
 
@@ -82,7 +82,7 @@ def test_bad_dims_rejected(over, code):
 
 def test_status_strings():
     assert rel.status_string(0) == "ok"
-    for st in range(1, MB_ERR_ABORTED + 1):
+    for st in range(1, MB_ERR_SCRATCH + 1):
         assert len(rel.status_string(st)) > 10
     assert "reset" in rel.status_string(MB_ERR_ABORTED)
     assert rel.status_string(99) == "unknown status"
@@ -262,3 +262,27 @@ def test_workspace_status_and_reset_check_arguments():
     assert lib.mb_workspace_reset(None, big, None) == MB_ERR_NULL
     assert lib.mb_workspace_reset(FAKE + 8, big, None) == MB_ERR_ALIGN
     assert lib.mb_workspace_reset(FAKE, 1024, None) == MB_ERR_WORKSPACE
+
+
+def test_noalloc_block_checks_arguments_and_sizes_before_anything():
+    """mb_moe_block_noalloc checks its arguments as mb_moe_block does, then
+    refuses sizes its static scratch cannot hold, before any GPU call (here,
+    without a GPU, anything else would come back as MB_ERR_HIP)."""
+    L = rel.lib()
+    w = full_weights()
+    d = c1_dims()
+    assert L.mb_moe_block_noalloc(ctypes.byref(d), FAKE, ctypes.byref(w), None, FAKE, None, None) == MB_ERR_NULL
+    assert L.mb_moe_block_noalloc(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE + 2, None, None) == MB_ERR_ALIGN
+    bad = c1_dims(top_k=0)
+    assert L.mb_moe_block_noalloc(ctypes.byref(bad), FAKE, ctypes.byref(w), FAKE, FAKE, None, None) == MB_ERR_DIMS
+    big = dict(hidden=7168, pooled=3072, inter=1536, experts=128, top_k=8, scoring="softmax")
+    for rows, fits in ((1, True), (16, True), (32, True), (55, True), (56, False), (64, False), (256, False)):
+        dd = c1_dims(rows=rows, **big)
+        st, n = status_of_ws(dd)
+        assert st == MB_OK
+        got = L.mb_moe_block_noalloc(ctypes.byref(dd), FAKE, ctypes.byref(w), FAKE, FAKE, None, None)
+        if fits:
+            assert got != MB_ERR_SCRATCH, rows
+        else:
+            assert got == MB_ERR_SCRATCH, (rows, n)
+    assert "56 MiB" in rel.status_string(MB_ERR_SCRATCH)
