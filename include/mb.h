@@ -98,8 +98,8 @@ enum {
  * elements scaled and rounded to the nearest E2M1 value, ties to the even
  * code, magnitudes above 6 saturating to 6), and each contraction runs on
  * fp4 x fp4 products.  act_quant 1 runs in the block kernel only: it needs
- * w->experts_packed and sizes the block kernel takes (experts <= 64, hidden
- * <= 8192, route tables within its LDS), else MB_ERR_UNSUPPORTED.
+ * w->experts_packed and sizes the block kernel takes (experts <= 256,
+ * hidden <= 8192, route tables within its LDS), else MB_ERR_UNSUPPORTED.
  * qkv_rows 0: mb_moe_block ends at the boundary.  qkv_rows > 0 (a multiple
  * of 16, at most 65536): mb_moe_block also runs the next layer's QKV
  * projection of x_next (as mb_next_qkv, with w->next_qkv_w bf16

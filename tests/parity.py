@@ -181,6 +181,17 @@ def assert_routing(got: dict, r: oracle.Routing, name: str, check_logits=True) -
     assert np.array_equal(got["active"][: r.n_active], r.active), f"{name}: active"
 
 
+def plain_misses(got: dict, ref: oracle.BlockResult) -> dict:
+    """Elements of u, stream and x_next outside the plain tolerance
+    1e-2 + 2e-2 |ref| against the oracle's end-to-end result."""
+    out = {}
+    for n, r, is_bf16 in (("u", ref.u, True), ("stream", ref.stream, False), ("x_next", ref.x_next, True)):
+        a = f(got[n]) if is_bf16 else np.asarray(got[n], np.float64)
+        b = f(r) if is_bf16 else np.asarray(r, np.float64)
+        out[n] = int((~(np.abs(a - b) <= BF16_ATOL + BF16_RTOL * np.abs(b))).sum())
+    return out
+
+
 def _ulp_bf16(v: np.ndarray) -> np.ndarray:
     """One bf16 unit in the last place of |v| (8 significant bits)."""
     a = np.abs(np.asarray(v, np.float64))
@@ -188,56 +199,73 @@ def _ulp_bf16(v: np.ndarray) -> np.ndarray:
 
 
 def assert_block(got: dict, ref: oracle.BlockResult, name: str, blk=None) -> dict:
-    """Routing bit-exact; h and moe_out within the bf16 tolerance end to end.
+    """Routing bit-exact; h, moe_out and u within the plain bf16 tolerance
+    1e-2 + 2e-2 |ref| end to end; the stream and x_next within it plus what
+    u's tolerance can move them (a bound computed from the oracle's values
+    alone, below).
 
-    u follows a bf16 rounding of moe_out, and the boundary one of u, that either
-    side may take one unit apart (fp32 vs fp64 accumulation before the same
-    rounding).  So u is checked on the GPU's own moe_out, and the boundary
-    twice: on the GPU's own u (oracle boundary of that u:
-    the fp32 stream within 1e-5, x_next within the bf16 tolerance), and end to
-    end within the bf16 tolerance plus what one bf16 unit of u moves it."""
+    Each stage after a bf16 rounding is also checked on the GPU's own input
+    to it (teacher-forced: u on the GPU's moe_out, the boundary on the GPU's
+    u), where only the stage's own arithmetic differs.  End to end, u may
+    differ from the oracle's by up to its tolerance (the MoE output, whose
+    bf16 rounding either side may take differently, feeds a long
+    contraction), and the boundary carries that into the stream: to first
+    order, with r = 1/rms(u), a change du of u moves v = RMSNorm_H(u) w_pff
+    by at most w_pff,n r (|du_n| + |u_n| r^2 sum_k |u_k du_k| / H), and the
+    stream by |g_n| times that; x_next = RMSNorm_H(stream) w_in moves the
+    same way with the stream's bound.  Where |u_n| is several times rms(u)
+    and the stream near zero, one bf16 unit of u already moves the stream
+    by more than the absolute tolerance, so the plain tolerance alone would
+    fail for reasons of rounding, not of a wrong kernel.  How many elements
+    need the extra bound is logged per case."""
     assert_routing(got, ref.routing, name)
     errs = {}
     errs["h"] = assert_close(got["h"], ref.h, f"{name}: h")
     errs["moe_out"] = assert_close(got["moe_out"], ref.moe_out, f"{name}: moe_out")
+    misses = plain_misses(got, ref)
+    mo_ulps = np.abs(f(got["moe_out"]) - f(ref.moe_out)) / _ulp_bf16(f(ref.moe_out))
+    say(f"[parity] {name}: outside 1e-2 + 2e-2|ref| end to end: " +
+        ", ".join(f"{n} {m} of {got[n].size}" for n, m in misses.items()) +
+        f"; moe_out bf16 units apart: max {mo_ulps.max():.1f}, over one {int((mo_ulps > 1).sum())}")
+    errs.update({f"miss_{n}": m for n, m in misses.items()})
+    errs["u"] = assert_close(got["u"], ref.u, f"{name}: u end to end")
     if blk is None:
-        errs["u"] = assert_close(got["u"], ref.u, f"{name}: u")
         errs["stream"] = assert_close(got["stream"], ref.stream, f"{name}: stream", is_bf16=False)
         errs["x_next"] = assert_close(got["x_next"], ref.x_next, f"{name}: x_next")
         return errs
-    # u follows the bf16 rounding of moe_out, which either side may take one
-    # unit apart; over a long contraction such units add up.  So u is checked
-    # on the GPU's own moe_out (the oracle's unpooler of it), and end to end
-    # within the tolerance plus what the measured moe_out difference moves it.
     u_tf = oracle.unpool(got["moe_out"], blk.unpool_w)
     errs["u_tf"] = assert_close(got["u"], u_tf, f"{name}: u on GPU moe_out")
-    drift = np.abs(f(u_tf) - f(ref.u))
-    e_u = np.abs(f(got["u"]) - f(ref.u))
-    bad = e_u > BF16_ATOL + BF16_RTOL * np.abs(f(ref.u)) + drift
-    assert not bad.any(), f"{name}: u end to end outside tolerance at {np.argwhere(bad)[:5].tolist()}"
-    errs["u"] = float(e_u.max())
     eps = blk.dims.norm_eps
     s_tf, x_tf = oracle.boundary(got["u"], blk.stream, blk.gate, blk.ffn_norm_w, blk.next_norm_w, eps)
     errs["stream_tf"] = assert_close(got["stream"], s_tf, f"{name}: stream on GPU u", atol=1e-5,
                                      rtol=1e-5, is_bf16=False)
     errs["x_next_tf"] = assert_close(got["x_next"], x_tf, f"{name}: x_next on GPU u")
-    # End to end, allowing one bf16 unit of u to propagate through the boundary.
+    # End to end: the plain tolerance plus the first-order effect of u's.
+    H = blk.dims.hidden
     uf = f(ref.u)
-    rs_u = 1.0 / np.sqrt(np.mean(uf * uf, axis=1, keepdims=True) + eps)
+    du = BF16_ATOL + BF16_RTOL * np.abs(uf)
     wpff = 1.0 if blk.ffn_norm_w is None else np.abs(f(blk.ffn_norm_w))
     win = 1.0 if blk.next_norm_w is None else np.abs(f(blk.next_norm_w))
-    ds = np.abs(f(blk.gate)) * wpff * rs_u * _ulp_bf16(uf)
+    ds = np.abs(f(blk.gate)) * _rmsnorm_bound(uf, du, eps, H) * wpff
     sref = ref.stream.astype(np.float64)
-    rs_s = 1.0 / np.sqrt(np.mean(sref * sref, axis=1, keepdims=True) + eps)
     e_s = np.abs(got["stream"].astype(np.float64) - sref)
-    bad = e_s > BF16_ATOL + BF16_RTOL * np.abs(sref) + ds
+    s_tol = BF16_ATOL + BF16_RTOL * np.abs(sref)
+    bad = e_s > s_tol + ds
     assert not bad.any(), f"{name}: stream end to end outside tolerance at {np.argwhere(bad)[:5].tolist()}"
     xr = f(ref.x_next)
     e_x = np.abs(f(got["x_next"]) - xr)
-    bad = e_x > BF16_ATOL + BF16_RTOL * np.abs(xr) + rs_s * win * ds
+    dx = win * _rmsnorm_bound(sref, s_tol + ds, eps, H)
+    bad = e_x > BF16_ATOL + BF16_RTOL * np.abs(xr) + dx
     assert not bad.any(), f"{name}: x_next end to end outside tolerance at {np.argwhere(bad)[:5].tolist()}"
     errs["stream"], errs["x_next"] = float(e_s.max()), float(e_x.max())
     return errs
+
+
+def _rmsnorm_bound(a: np.ndarray, da: np.ndarray, eps: float, n: int) -> np.ndarray:
+    """First-order bound on how far a / rms(a) moves, per element, when each
+    a_k moves by at most da_k (rows of a, rms over the last axis of n)."""
+    r = 1.0 / np.sqrt(np.mean(a * a, axis=-1, keepdims=True) + eps)
+    return r * (da + np.abs(a) * r * r * np.sum(np.abs(a) * da, axis=-1, keepdims=True) / n)
 
 
 def slice_result(ref: oracle.BlockResult, b: int, experts: int) -> oracle.BlockResult:

@@ -210,6 +210,20 @@ def test_mxfp4_activations_need_the_streaming_layout():
                         ctypes.byref(w), FAKE, FAKE, 1 << 40, None) == MB_ERR_UNSUPPORTED
 
 
+def test_mxfp4_activations_limited_to_the_block_kernel_sizes():
+    # With the streaming layout, act_quant 1 takes every size the block
+    # kernel takes (up to 256 experts); beyond that it is refused before any
+    # launch (the per-step kernels have no MXFP4-activation path).
+    L = rel.lib()
+    w = full_weights(experts_packed=FAKE)
+    for E, want in ((257, MB_ERR_UNSUPPORTED), (512, MB_ERR_UNSUPPORTED)):
+        d = c1_dims(act_quant=1, experts=E, top_k=8)
+        assert L.mb_moe_block(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE, None, FAKE, 1 << 40,
+                              None) == want, E
+        assert L.mb_experts(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            ctypes.byref(w), FAKE, FAKE, 1 << 40, None) == want, E
+
+
 def test_steps_around_the_block_check_arguments():
     d = c1_dims()
     L = rel.lib()

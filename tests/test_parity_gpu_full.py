@@ -1,23 +1,33 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
 benchmark times (mb_moe_block): the b=16 decode step, the b=64 softmax block
-(both skew readings), the row-bucket sweep at its dims (uniform and both skew
-readings) and the 60-layer stack, checked layer by layer on the GPU's own
-inputs (teacher-forced).  The oracle computes every output of these sizes, so
-the comparison is element by element."""
+(three routings), the row-bucket sweep at its dims (three routings), each in
+both expert layouts (the caller's and the streaming layout the benchmark
+reads), and the 60-layer stack, checked on the GPU's own inputs layer by
+layer (teacher-forced).  The oracle computes every output of these sizes, so
+the comparison is element by element (the 60-layer stack: on a rotating pair
+of rows per layer, rows being independent through the block)."""
+
+import dataclasses
+import functools
+import queue
+import threading
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from parity import GpuBlock, assert_block, assert_close, say, slice_result
+from parity import GpuBlock, assert_block, say, slice_result
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 torch = pytest.importorskip("torch")
 
+LAYOUTS = ["caller", "packed"]
 
-@pytest.mark.parametrize("layout", ["caller", "packed"])
+
+@pytest.mark.parametrize("layout", LAYOUTS)
 def test_c1_decode_step(layout):
     blk = synth.make_block("c1")
     say(f"[gpu] c1 b=16 block, {layout} expert layout")
@@ -26,51 +36,70 @@ def test_c1_decode_step(layout):
         g.use_packed()
     got = g.run_block()
     ref = oracle.block(blk)
-    assert_block(got, ref, "c1", blk)
+    assert_block(got, ref, f"c1 {layout}", blk)
 
 
-@pytest.mark.parametrize("skew,layout", [("calibrated", "caller"), ("literal", "caller"), ("uniform", "caller"),
-                                         ("calibrated", "packed")])
-def test_c2_softmax_block(skew, layout):
+@functools.lru_cache(maxsize=None)
+def _c2(skew):
     blk = synth.make_block("c2", skew=skew)
+    return blk, oracle.block(blk)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("skew", ["calibrated", "literal", "uniform"])
+def test_c2_softmax_block(skew, layout):
+    blk, ref = _c2(skew)
     say(f"[gpu] c2 b=64 skew={skew}, {layout} expert layout")
     g = GpuBlock(blk)
     if layout == "packed":
         g.use_packed()
     got = g.run_block()
-    ref = oracle.block(blk)
-    assert_block(got, ref, f"c2 {skew}", blk)
+    assert_block(got, ref, f"c2 {skew} {layout}", blk)
     hot = synth.hot_experts(2, 128)
     share = np.isin(ref.routing.ids, hot).mean()
     say(f"[gpu] c2 {skew}: hot-expert share of routes {share:.3f}, active experts {ref.routing.n_active}")
 
 
-@pytest.fixture(scope="module")
-def c3_gpu():
-    blk = synth.make_c3_block(None)
-    return GpuBlock(blk), blk
+@functools.lru_cache(maxsize=None)
+def _c3_ref(skew):
+    full = synth.make_c3_block(skew)
+    return full, oracle.block(full)
+
+
+@pytest.fixture(scope="module", params=LAYOUTS)
+def c3_gpu(request):
+    # One upload of the sweep's weights per layout; the routings differ only
+    # in the expert bias.
+    g = GpuBlock(synth.make_c3_block(None))
+    if request.param == "packed":
+        g.use_packed()
+    yield g, request.param
+    del g
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("skew", [None, "calibrated", "literal"])
 def test_c3_bucket_sweep(c3_gpu, skew):
-    g, blk0 = c3_gpu
-    full = synth.make_c3_block(skew) if skew else blk0
-    ref = oracle.block(full)
+    g, layout = c3_gpu
+    full, ref = _c3_ref(skew)
     g.blk = full
     g.set_bias(full.expert_bias)
     base_x, base_s = g.x, g.stream0
-    for b in synth.inputs.C3_BUCKETS:
-        say(f"[gpu] c3 skew={skew} b={b}")
+    try:
+        for b in synth.inputs.C3_BUCKETS:
+            say(f"[gpu] c3 skew={skew} b={b}, {layout} expert layout")
+            g.x, g.stream0, g.blk = base_x, base_s, full
+            g.set_rows(b)
+            got = g.run_block()
+            assert_block(got, slice_result(ref, b, 128), f"c3 {skew} {layout} b={b}", g.blk)
+    finally:
         g.x, g.stream0, g.blk = base_x, base_s, full
-        g.set_rows(b)
-        got = g.run_block()
-        assert_block(got, slice_result(ref, b, 128), f"c3 {skew} b={b}", g.blk)
-    g.x, g.stream0, g.blk = base_x, base_s, full
 
 
 def test_c4_stack_teacher_forced():
-    """Layers 0-2 and 59 of the stack, each checked on the GPU's own input
-    (x, stream) from the layer before; the chain starts at the stack input."""
+    """Layers 0-2 and 59 of the stack, all rows, caller layout, each checked on
+    the GPU's own input (x, stream) from the layer before; the chain starts at
+    the stack input."""
     x, s = synth.make_c4_stream()
     for layer in (0, 1, 2, 59):
         blk = synth.make_c4_layer(layer)
@@ -83,3 +112,126 @@ def test_c4_stack_teacher_forced():
         x, s = got["x_next"], got["stream"]
         del g
         torch.cuda.empty_cache()
+
+
+def _rows_of(blk, x, s, rows):
+    return dataclasses.replace(blk, dims=blk.dims.with_rows(len(rows)), x=np.ascontiguousarray(x[rows]),
+                               stream=np.ascontiguousarray(s[rows]))
+
+
+def _got_rows(got: dict, rows, experts: int) -> dict:
+    """The block taps of some rows; the grouping rebuilt from their ids (the
+    grouping of all rows is compared with the GPU's own ids separately)."""
+    sub = {n: got[n][rows] for n in ("logits", "topk_ids", "topk_w", "h", "moe_out", "u", "stream", "x_next")}
+    gr = oracle.group_routes(sub["topk_ids"], experts)
+    sub.update(count=gr["count"], offset=gr["offset"], route_list=gr["route_list"],
+               active=gr["active"], n_active=np.array([gr["n_active"]], np.int32))
+    return sub
+
+
+def test_c4_stack_all_60_layers_streaming_layout():
+    """All 60 layers of the stack in the streaming expert layout, each layer
+    run on all 32 rows and fed the GPU's own outputs of the layer before.
+
+    Per layer: the grouping of all rows equals the grouping of the GPU's own
+    ids, and two rows (2l, 2l + 1 mod 32, so every row is checked at some
+    layers) match the oracle run on the GPU's inputs of those rows.
+    Alongside, the oracle runs the stack free on row 0 (its own outputs fed
+    forward); the drift of the GPU's row 0 from it is logged per layer, next
+    to the drift of the oracle itself from an input one bf16 unit apart
+    (rounding differences compound over layers and, once they change a
+    selection, grow by the stack's own sensitivity: reported, not asserted).
+    Layer generation and the oracle run in threads beside the GPU chain
+    (numpy releases the GIL)."""
+    n_layers = synth.inputs.C4_LAYERS
+    x, s = synth.make_c4_stream()
+    gen = ThreadPoolExecutor(4)
+    checks = ThreadPoolExecutor(6)
+    ahead = 4
+    futs = {l: gen.submit(synth.make_c4_layer, l) for l in range(min(ahead, n_layers))}
+    # The oracle run free on row 0, one layer after another in a thread of
+    # its own (a bounded queue: the GPU chain waits when it falls behind);
+    # and, as a control of how sensitive the stack itself is, the same from
+    # an input one bf16 unit away in one element.
+    queues = [queue.Queue(maxsize=6), queue.Queue(maxsize=6)]
+    outs, chain_err = [{}, {}], []
+
+    def chain(q, out, xr, sr):
+        try:
+            while True:
+                item = q.get()
+                if item is None:
+                    return
+                l, blk = item
+                ref = oracle.block(_rows_of(blk, xr, sr, [0]))
+                xr, sr = ref.x_next, ref.stream
+                out[l] = (xr[0], sr[0], ref.routing.ids[0])
+        except BaseException as e:  # reported by the main thread
+            chain_err.append(e)
+            while q.get() is not None:
+                pass
+
+    x_pert = x[:1].copy()
+    x_pert[0, 0] += 1  # the next bf16 value (same sign, one unit further from zero)
+    threads = [threading.Thread(target=chain, args=(queues[0], outs[0], x[:1].copy(), s[:1].copy()), daemon=True),
+               threading.Thread(target=chain, args=(queues[1], outs[1], x_pert, s[:1].copy()), daemon=True)]
+    for t in threads:
+        t.start()
+    gpu_row0 = {}
+    pending, results = [], []
+
+    def check(l, blk, xin, sin, got, rows):
+        sub = _rows_of(blk, xin, sin, rows)
+        ref = oracle.block(sub)
+        errs = assert_block(_got_rows(got, rows, blk.dims.experts), ref, f"c4 layer {l} rows {rows}", sub)
+        return l, rows, errs
+
+    try:
+        for l in range(n_layers):
+            blk = futs.pop(l).result()
+            if l + ahead < n_layers:
+                futs[l + ahead] = gen.submit(synth.make_c4_layer, l + ahead)
+            g = GpuBlock(dataclasses.replace(blk, x=x, stream=s))
+            g.use_packed()
+            got = g.run_block()
+            del g
+            torch.cuda.empty_cache()
+            gr = oracle.group_routes(got["topk_ids"], blk.dims.experts)
+            for n in ("count", "offset", "route_list"):
+                assert np.array_equal(got[n], gr[n]), f"c4 layer {l}: {n} of the GPU's own ids"
+            assert int(got["n_active"][0]) == gr["n_active"]
+            assert np.array_equal(got["active"][: gr["n_active"]], gr["active"])
+            rows = [(2 * l) % 32, (2 * l + 1) % 32]
+            pending.append(checks.submit(check, l, blk, x, s, got, rows))
+            while len(pending) > 8:  # bounds the layers held in memory
+                results.append(pending.pop(0).result())
+            gpu_row0[l] = (got["x_next"][0], got["stream"][0], got["topk_ids"][0])
+            for q in queues:
+                q.put((l, blk))
+            x, s = got["x_next"], got["stream"]
+            say(f"[gpu] c4 stack layer {l} run")
+        results += [fu.result() for fu in pending]
+    finally:
+        for q in queues:
+            q.put(None)
+        gen.shutdown(wait=True, cancel_futures=True)
+        checks.shutdown(wait=True, cancel_futures=True)
+    for t in threads:
+        t.join()
+    for l, rows, errs in results:
+        say(f"[gpu] c4 stack layer {l} rows {rows}: max errors " +
+            ", ".join(f"{k} {v:.3g}" for k, v in errs.items()))
+    if chain_err:
+        raise chain_err[0]
+
+    def apart(a, b):
+        (xa, sa, ia), (xb, sb, ib) = a, b
+        rms = float(np.sqrt(np.mean(sb.astype(np.float64) ** 2)))
+        return (f"ids {'same' if np.array_equal(np.sort(ia), np.sort(ib)) else 'differ'}, x_next max |diff| "
+                f"{np.abs(oracle.bf16_to_f64(xa) - oracle.bf16_to_f64(xb)).max():.3g}, stream max |diff| / rms "
+                f"{np.abs(sa.astype(np.float64) - sb.astype(np.float64)).max() / rms:.3g}")
+
+    for l in range(n_layers):
+        say(f"[drift] c4 row 0 after layer {l}: GPU vs oracle: {apart(gpu_row0[l], outs[0][l])}; "
+            f"oracle from x one bf16 unit apart vs oracle: {apart(outs[1][l], outs[0][l])}")
+    assert len(outs[0]) == len(outs[1]) == n_layers

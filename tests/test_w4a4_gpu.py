@@ -107,6 +107,12 @@ def test_w4a4_c1_decode_step():
     check_w4a4(synth.make_block("c1"), "c1")
 
 
+def test_w4a4_c2_softmax_block():
+    """128 experts, top-8, softmax, H 7168 (the larger block's dims, with its
+    hot-expert skew)."""
+    check_w4a4(synth.make_block("c2"), "c2")
+
+
 def test_w4a4_experts_entry_point_matches_block():
     """mb_experts with act_quant on the block's own h and routing gives the
     block's moe_out bit for bit (the same kernel code, deterministic)."""
