@@ -93,91 +93,118 @@ def cpu_baseline(blk, seconds: float, act_quant: bool = False) -> dict:
     return {"value": round(blk.dims.rows * n / el, 3), "unit": "rows/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{n} full b={blk.dims.rows} decode blocks (weight set 0) through the numpy "
-                      f"fp64 oracle, {el:.1f} s; cores = its BLAS thread pool"}
+                      f"fp64 oracle, {el:.1f} s; cores = its BLAS thread pool",
+            "cpu_model": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0))}
 
 
-def sweep(args) -> int:
-    """Every workload once, each on its own seeded weight sets: microseconds per
-    block, rows/s and algorithmic HBM bandwidth for c0, c2 (both skew
-    readings), each c3 row bucket (uniform and calibrated skew) and the
-    60-layer c4 stack.  One JSON line per case on stdout."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def percentiles(us) -> dict:
+    import numpy as np
+
+    a = np.asarray(us, dtype=np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 2), "p50": round(float(np.percentile(a, 50)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2), "n": int(a.size)}
+
+
+def per_launch_us(torch, fn, n: int) -> list:
+    """Durations of n launches one after another on the current stream, from
+    an event recorded between each two (the queue stays full, so each gap is
+    one launch's time on the device)."""
+    cur = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(cur)
+    for i in range(n):
+        fn(i)
+        ev[i + 1].record(cur)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)]
+
+
+def read_probe(mib: int) -> int:
+    """Time the plain HBM read kernel (libmb_readprobe.so): over one buffer
+    of `mib` MiB in each variant and grid, then, in the best variant, at the
+    block's own sizes, each launch reading the next of several buffers that
+    together exceed the 256 MB Infinity Cache four times over.  One JSON line
+    per case."""
+    import ctypes
+
     import numpy as np
     import torch
 
-    import routed_expert_layer_amd as rel
-    import synth
-    from synth.device import dims_kwargs, to_tensor, upload_weights
-
+    lib = ctypes.CDLL(os.path.join(ROOT, "routed_expert_layer_amd", "libmb_readprobe.so"))
+    lib.mbp_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                             ctypes.c_void_p]
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    grids = (256, 512, 1024, 2048, 4096, 8192)
+    sink = torch.zeros(max(grids), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    names = ("4 words in flight, plain loads", "8 words in flight, plain loads",
+             "4 words in flight, nontemporal loads", "8 words in flight, nontemporal loads")
 
-    def prepare(blocks):
-        dims = rel.make_dims(**dims_kwargs(blocks[0].dims), act_quant=int(args.act_quant))
-        tensors = [upload_weights(b, dev) for b in blocks]
-        weights = [rel.make_weights(**t) for t in tensors]
-        if args.layout == "packed":
-            for t, w in zip(tensors, weights):
-                t["experts_packed"] = rel.pack_experts(dims, w, dev)
-            weights = [rel.make_weights(**t) for t in tensors]
-        torch.cuda.synchronize()
-        return dims, tensors, weights
-
-    def n_active(dims, x, w, stream, ws):
-        n = torch.zeros(1, dtype=torch.int32, device=dev)
-        xn = torch.empty((x.shape[0], x.shape[1]), dtype=torch.bfloat16, device=dev)
-        rel.mb_moe_block(dims, x, w, stream.clone(), xn, ws, taps=rel.make_taps(n_active=n))
-        torch.cuda.synchronize()
-        return int(n.item())
-
-    def timed(fn, steps, warmup):
-        for i in range(warmup):
+    def run(bufs, nbytes, grid, variant, case):
+        def fn(i):
+            st = lib.mbp_read(bufs[i % len(bufs)].data_ptr(), nbytes, grid, variant, sink.data_ptr(), stream)
+            if st != 0:
+                raise RuntimeError(f"mbp_read status {st}")
+        for i in range(2 * len(bufs)):
             fn(i)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(steps):
-            fn(i)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / steps
-
-    def report(case, d, us, actives, blocks_per_step=1):
-        b_alg = float(np.mean([algorithmic_bytes(d, a) for a in actives])) * blocks_per_step
-        gbs = b_alg / (us * 1e-6) / 1e9
-        line = {"case": case, "rows": d.rows, "us_per_step": round(us, 2),
-                "blocks_per_step": blocks_per_step,
-                "rows_per_s": round(d.rows * blocks_per_step / (us * 1e-6), 1),
-                "algorithmic_bytes_per_step": int(b_alg), "achieved_GBps": round(gbs, 1),
-                "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4), "active_experts": actives,
-                "expert_layout": args.layout, "act_quant": int(args.act_quant)}
+        us = per_launch_us(torch, fn, max(20, 2 * len(bufs)))
+        med = float(np.median(us))
+        gbs = nbytes / (med * 1e-6) / 1e9
+        line = {"case": case, "variant": names[variant], "workgroups": grid, "bytes": nbytes,
+                "buffers_rotated": len(bufs), "us_per_launch": percentiles(us),
+                "GBps_at_median": round(gbs, 1), "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4)}
         print(json.dumps(line), flush=True)
-        print(f"[sweep] {case}: {us:.1f} us/step, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)",
-              file=sys.stderr, flush=True)
+        return line
 
-    def run_block_case(case, blocks, steps, warmup=10):
-        d = blocks[0].dims
-        dims, tensors, weights = prepare(blocks)
-        x, stream = to_tensor(blocks[0].x, dev), to_tensor(blocks[0].stream, dev)
-        ws = rel.workspace(dims, dev)
-        xn = torch.empty((d.rows, d.hidden), dtype=torch.bfloat16, device=dev)
-        actives = [n_active(dims, x, w, stream, ws) for w in weights]
-        S = len(weights)
-        us = timed(lambda i: rel.mb_moe_block(dims, x, weights[i % S], stream, xn, ws), steps, warmup)
-        report(case, d, us, actives)
+    nbytes = mib << 20
+    big = [torch.ones(nbytes // 4, dtype=torch.float32, device=dev)]
+    best = None
+    for variant in range(4):
+        for grid in grids:
+            line = run(big, nbytes, grid, variant, f"hbm read probe {mib} MiB")
+            if best is None or line["GBps_at_median"] > best["GBps_at_median"]:
+                best = line
+    print(json.dumps({**best, "case": f"hbm read probe {mib} MiB: best"}), flush=True)
+    del big
+    torch.cuda.empty_cache()
+    # The block's sizes: c1's algorithmic bytes (about 169 MB) and neighbours.
+    for size in (64 << 20, 169095936, 512 << 20):
+        n = -(-(1 << 30) // size) + 1
+        bufs = [torch.ones(size // 4, dtype=torch.float32, device=dev) for _ in range(n)]
+        top = None
+        for variant in (2, 3):
+            for grid in grids:
+                line = run(bufs, size, grid, variant, f"hbm read probe {size} B")
+                if top is None or line["GBps_at_median"] > top["GBps_at_median"]:
+                    top = line
+        print(json.dumps({**top, "case": f"hbm read probe {size} B: best"}), flush=True)
+        del bufs
+        torch.cuda.empty_cache()
+    return 0
 
-    def report_bytes(case, rows, us, b_alg):
-        gbs = b_alg / (us * 1e-6) / 1e9
-        line = {"case": case, "rows": rows, "us_per_step": round(us, 2), "blocks_per_step": 1,
-                "rows_per_s": round(rows / (us * 1e-6), 1), "algorithmic_bytes_per_step": int(b_alg),
-                "achieved_GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4),
-                "active_experts": None, "expert_layout": None, "act_quant": None}
-        print(json.dumps(line), flush=True)
-        print(f"[sweep] {case}: {us:.1f} us/step, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)",
-              file=sys.stderr, flush=True)
 
-    # The steps either side of the block at the decode size (b = 16, H = 4096):
-    # the attention boundary, and the next QKV projection with 32 query and 8
-    # KV heads of 128 (10240 rows); four weight sets rotated for the latter.
+def steps_around(args, rel, synth, dims_kwargs, to_tensor, prepare, n_active, timed, report_bytes):
+    """The steps either side of the block at the decode size (b = 16,
+    H = 4096): the attention boundary, and the next QKV projection with 32
+    query and 8 KV heads of 128 (10240 rows), alone, fused into the block's
+    launch and as a second launch."""
+    import numpy as np
+    import torch
+
+    dev = "cuda:0"
     print("[sweep] steps around the block", file=sys.stderr, flush=True)
     b16, H16, NQ = 16, 4096, 10240
     side = synth.make_attn_side(b16, H16, NQ, 80)
@@ -225,44 +252,159 @@ def sweep(args) -> int:
     report_bytes("c1 block, then next qkv 10240 as a second launch", b16, us, bytes_block + NQ * H16 * 2 + b16 * NQ * 2)
     del wq, tp, ws16, blocks, tensors1, weights1, weights_q, wsq
     torch.cuda.empty_cache()
+
+
+def sweep(args) -> int:
+    """Every workload once, each on its own seeded weight sets: microseconds per
+    block, rows/s and algorithmic HBM bandwidth for c0, c2 (both skew
+    readings), each c3 row bucket (uniform and calibrated skew) and the
+    60-layer c4 stack.  One JSON line per case on stdout."""
+    import numpy as np
+    import torch
+
+    import routed_expert_layer_amd as rel
+    import synth
+    from synth.device import dims_kwargs, to_tensor, upload_weights
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    def prepare(blocks):
+        dims = rel.make_dims(**dims_kwargs(blocks[0].dims), act_quant=int(args.act_quant))
+        tensors = [upload_weights(b, dev) for b in blocks]
+        weights = [rel.make_weights(**t) for t in tensors]
+        if args.layout == "packed":
+            for t, w in zip(tensors, weights):
+                t["experts_packed"] = rel.pack_experts(dims, w, dev)
+            weights = [rel.make_weights(**t) for t in tensors]
+        torch.cuda.synchronize()
+        return dims, tensors, weights
+
+    def n_active(dims, x, w, stream, ws):
+        n = torch.zeros(1, dtype=torch.int32, device=dev)
+        xn = torch.empty((x.shape[0], x.shape[1]), dtype=torch.bfloat16, device=dev)
+        rel.mb_moe_block(dims, x, w, stream.clone(), xn, ws, taps=rel.make_taps(n_active=n))
+        torch.cuda.synchronize()
+        return int(n.item())
+
+    def timed(fn, steps, warmup):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    def report(case, d, us, actives, blocks_per_step=1, pct=None):
+        b_alg = float(np.mean([algorithmic_bytes(d, a) for a in actives])) * blocks_per_step
+        gbs = b_alg / (us * 1e-6) / 1e9
+        line = {"case": case, "rows": d.rows, "us_per_step": round(us, 2),
+                "us_per_block_percentiles": pct,
+                "blocks_per_step": blocks_per_step,
+                "rows_per_s": round(d.rows * blocks_per_step / (us * 1e-6), 1),
+                "algorithmic_bytes_per_step": int(b_alg), "achieved_GBps": round(gbs, 1),
+                "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4), "active_experts": actives,
+                "expert_layout": args.layout, "act_quant": int(args.act_quant)}
+        print(json.dumps(line), flush=True)
+        print(f"[sweep] {case}: {us:.1f} us/step, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)",
+              file=sys.stderr, flush=True)
+
+    def run_block_case(case, blocks, steps, warmup=10):
+        d = blocks[0].dims
+        dims, tensors, weights = prepare(blocks)
+        x, stream = to_tensor(blocks[0].x, dev), to_tensor(blocks[0].stream, dev)
+        ws = rel.workspace(dims, dev)
+        xn = torch.empty((d.rows, d.hidden), dtype=torch.bfloat16, device=dev)
+        actives = [n_active(dims, x, w, stream, ws) for w in weights]
+        S = len(weights)
+
+        def fn(i):
+            rel.mb_moe_block(dims, x, weights[i % S], stream, xn, ws)
+
+        us = timed(fn, steps, warmup)
+        report(case, d, us, actives, pct=percentiles(per_launch_us(torch, fn, min(steps, 500))))
+
+    def report_bytes(case, rows, us, b_alg):
+        gbs = b_alg / (us * 1e-6) / 1e9
+        line = {"case": case, "rows": rows, "us_per_step": round(us, 2), "blocks_per_step": 1,
+                "rows_per_s": round(rows / (us * 1e-6), 1), "algorithmic_bytes_per_step": int(b_alg),
+                "achieved_GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4),
+                "active_experts": None, "expert_layout": None, "act_quant": None}
+        print(json.dumps(line), flush=True)
+        print(f"[sweep] {case}: {us:.1f} us/step, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)",
+              file=sys.stderr, flush=True)
+
+    cases = set(args.sweep_cases.split(","))
+    if "around" in cases:
+        steps_around(args, rel, synth, dims_kwargs, to_tensor, prepare, n_active, timed, report_bytes)
     if args.steps_around_only:
         return 0
+    if "c0" in cases:
+        print("[sweep] c0", file=sys.stderr, flush=True)
+        run_block_case("c0 tiny block", [synth.make_block("c0")], 1000)
+    if "c2" in cases:
+        for skew in ("calibrated", "literal"):
+            print(f"[sweep] c2 {skew}: generating 2 weight sets", file=sys.stderr, flush=True)
+            blocks = [synth.make_block("c2", seed=s, skew=skew) for s in (2, 1002)]
+            run_block_case(f"c2 b=64 softmax, skew {skew}", blocks, 200)
+            del blocks
+            torch.cuda.empty_cache()
+    if "c3" in cases:
+        for skew in (None, "calibrated"):
+            print(f"[sweep] c3 skew={skew}: generating 2 weight sets", file=sys.stderr, flush=True)
+            full = [synth.make_c3_block(skew, seed=s) for s in (3, 1003)]
+            for b in synth.inputs.C3_BUCKETS:
+                run_block_case(f"c3 b={b} sigmoid, {skew or 'uniform'}", [f.rows(b) for f in full], 200)
+            del full
+            torch.cuda.empty_cache()
+    if "c4" not in cases:
+        return 0
 
-    print("[sweep] c0", file=sys.stderr, flush=True)
-    run_block_case("c0 tiny block", [synth.make_block("c0")], 1000)
-    for skew in ("calibrated", "literal"):
-        print(f"[sweep] c2 {skew}: generating 2 weight sets", file=sys.stderr, flush=True)
-        blocks = [synth.make_block("c2", seed=s, skew=skew) for s in (2, 1002)]
-        run_block_case(f"c2 b=64 softmax, skew {skew}", blocks, 100)
-        del blocks
-        torch.cuda.empty_cache()
-    for skew in (None, "calibrated"):
-        print(f"[sweep] c3 skew={skew}: generating 2 weight sets", file=sys.stderr, flush=True)
-        full = [synth.make_c3_block(skew, seed=s) for s in (3, 1003)]
-        for b in synth.inputs.C3_BUCKETS:
-            run_block_case(f"c3 b={b} sigmoid, {skew or 'uniform'}", [f.rows(b) for f in full], 100)
-        del full
-        torch.cuda.empty_cache()
-    # c4: 60 chained layers (x_next feeds the next layer); 8 distinct layer
-    # weight sets cycled, about 32 times the Infinity Cache.
-    n_distinct = 8
-    print(f"[sweep] c4: generating {n_distinct} layer weight sets", file=sys.stderr, flush=True)
-    layers = [synth.make_c4_layer(l) for l in range(n_distinct)]
+    # c4: the 60-layer stack, 60 distinct layer weight sets (about 54 GB of
+    # experts in HBM), x_next of each layer feeding the next.  Layers are
+    # drawn in threads and uploaded one by one (their caller-layout experts
+    # dropped once packed).
+    from concurrent.futures import ThreadPoolExecutor
+
+    n_layers = synth.inputs.C4_LAYERS
+    print(f"[sweep] c4: generating and uploading {n_layers} layer weight sets", file=sys.stderr, flush=True)
     x0, s0 = synth.make_c4_stream()
-    d = layers[0].dims
-    dims, tensors, weights = prepare(layers)
     x = to_tensor(x0, dev)
     stream = to_tensor(s0, dev)
-    ws = rel.workspace(dims, dev)
+    weights, actives, dims, ws, d = [], [], None, None, None
+    with ThreadPoolExecutor(4) as pool:
+        futs = [pool.submit(synth.make_c4_layer, l) for l in range(n_layers)]
+        for l, fu in enumerate(futs):
+            blk = fu.result()
+            futs[l] = None
+            d = blk.dims
+            dims_l, tensors, ws_l = prepare([blk])
+            if args.layout == "packed":
+                for n in ("w13", "w13_scale", "w2", "w2_scale"):
+                    tensors[0].pop(n, None)
+                ws_l = [rel.make_weights(**tensors[0])]
+            if dims is None:
+                dims, ws = dims_l, rel.workspace(dims_l, dev)
+            weights.append((tensors[0], ws_l[0]))
+            actives.append(n_active(dims, x, ws_l[0], stream, ws))
+            del blk
     xs = [x.clone(), torch.empty_like(x)]
-    actives = [n_active(dims, x, w, stream, ws) for w in weights]
+
+    def layer(i):
+        rel.mb_moe_block(dims, xs[i % 2], weights[i % n_layers][1], stream, xs[(i + 1) % 2], ws)
 
     def stack(_):
-        for layer in range(60):
-            rel.mb_moe_block(dims, xs[layer % 2], weights[layer % n_distinct], stream, xs[(layer + 1) % 2], ws)
+        for i in range(n_layers):
+            layer(i)
 
-    us = timed(stack, 10, 2)
-    report("c4 60-layer stack b=32 (per stack)", d, us, actives, blocks_per_step=60)
+    us = timed(stack, 4, 1)
+    pct = percentiles(per_launch_us(torch, layer, 4 * n_layers))
+    report(f"c4 {n_layers}-layer stack b=32 (per stack, {n_layers} distinct layers)", d, us, actives,
+           blocks_per_step=n_layers, pct=pct)
     return 0
 
 
@@ -284,6 +426,11 @@ def main() -> int:
                     help="the W4A4 variant: the experts' activations quantized to MXFP4 (needs the "
                          "packed layout); not the headline line")
     ap.add_argument("--print-source-hash", action="store_true")
+    ap.add_argument("--read-probe", type=int, default=0, metavar="MiB",
+                    help="instead of the block, time a plain HBM read kernel over MiB MiB "
+                         "(libmb_readprobe.so) in several variants and grids")
+    ap.add_argument("--sweep-cases", default="around,c0,c2,c3,c4",
+                    help="with --sweep: which cases (comma list of around, c0, c2, c3, c4)")
     ap.add_argument("--steps-around-only", action="store_true",
                     help="with --sweep: only the attention boundary and the next QKV projection")
     ap.add_argument("--sweep", action="store_true",
@@ -302,6 +449,8 @@ def main() -> int:
 
     if args.sweep:
         return sweep(args)
+    if args.read_probe > 0:
+        return read_probe(args.read_probe)
 
     import numpy as np
     import torch
@@ -381,6 +530,13 @@ def main() -> int:
           f"({100 * achieved / HBM_PEAK_GBS:.1f}% of 8 TB/s), wall {wall * 1e3 / args.steps:.2f} "
           f"ms/step, active experts {actives}", file=sys.stderr, flush=True)
 
+    # Per-launch durations (a second pass, events between launches).
+    each = per_launch_us(torch, lambda i: rel.mb_moe_block(dims, x, weights[i % S], stream, x_next, ws),
+                         min(args.steps, 1000))
+    pct = percentiles(each)
+    print(f"[bench] per launch: p10 {pct['p10']} p50 {pct['p50']} p90 {pct['p90']} us", file=sys.stderr,
+          flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -406,6 +562,7 @@ def main() -> int:
             "activations": "mxfp4 (W4A4)" if args.act_quant else "bf16",
             "rows": d.rows, "weight_sets": S, "active_experts": actives,
             "us_per_block": round(us_block, 3),
+            "us_per_launch_percentiles": pct,
             "algorithmic_bytes_per_block": int(b_alg),
         },
         "roofline": {

@@ -172,10 +172,10 @@ typedef struct {
   uint16_t *h;         /* bf16 [b, P] */
   uint16_t *moe_out;   /* bf16 [b, P] */
   uint16_t *u;         /* bf16 [b, H] */
-  int64_t *timeline;   /* tracing: int64 [1024][32]; workgroup w writes the
+  int64_t *timeline;   /* tracing: int64 [1024][32]; workgroup w keeps the
                           100 MHz real-time counter at its phase boundaries
-                          into row w (slots 0..21; the per-step path leaves it
-                          untouched) */
+                          and writes them into row w at its end (0 = slot
+                          not reached; the per-step path leaves it untouched) */
   uint16_t *act;       /* bf16 [b * k, I]: the experts' gated activations
                           act = bf16(silu(gu[0:I]) * gu[I:2I]) (mb_experts),
                           row i for route route_list[i] (grouped by expert) */

@@ -4,7 +4,9 @@
 #include <math.h>
 
 #include <algorithm>
+#include <map>
 #include <mutex>
+#include <tuple>
 
 #include "mb_block.h"
 #include "mb_internal.h"
@@ -265,10 +267,37 @@ int run_unpool_boundary(const mb_dims &d, const uint16_t *moe_out, const mb_weig
 
 // ---- the persistent block kernel (block.hip) --------------------------------
 
+// Launch-shape queries, asked of the runtime once and kept: the current
+// device's CU count, and the block kernel's resident workgroups per CU for
+// each (device, kernel variant, LDS bytes).  0 = the query failed (not kept).
+std::mutex g_shape_mu;
+std::map<int, int> g_cus;
+std::map<std::tuple<int, int, size_t>, int> g_occ;
+
 int device_cus() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(g_shape_mu);
+  const auto it = g_cus.find(dev);
+  if (it != g_cus.end()) return it->second;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 0;
+  g_cus[dev] = n;
+  return n;
+}
+
+int block_occupancy(size_t lds, bool w4a4, bool qkv) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const auto key = std::make_tuple(dev, (w4a4 ? 2 : 0) + (qkv ? 1 : 0), lds);
+  {
+    std::lock_guard<std::mutex> lock(g_shape_mu);
+    const auto it = g_occ.find(key);
+    if (it != g_occ.end()) return it->second;
+  }
+  const int n = block_max_groups_per_cu(lds, w4a4, qkv);
+  if (n < 1) return 0;
+  std::lock_guard<std::mutex> lock(g_shape_mu);
+  g_occ[key] = n;
   return n;
 }
 
@@ -376,7 +405,7 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   const size_t route_bytes = route_lds_bytes(p.b, p.k, p.E);
   const size_t lds = route_bytes + kBlockScratchBytes;
   if (lds > 64 * 1024) return none;
-  const int occ = block_max_groups_per_cu(lds, p.w4a4 != 0, p.n_qkv > 0);
+  const int occ = block_occupancy(lds, p.w4a4 != 0, p.n_qkv > 0);
   const int cus = device_cus();
   if (occ < 1 || cus < 1) return none;
   int grid = cus * (occ < kBlockGroupsPerCu ? occ : kBlockGroupsPerCu);

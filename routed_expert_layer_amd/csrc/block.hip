@@ -282,12 +282,26 @@ __device__ __forceinline__ void await_tagged(const Deps &d, rsrc_t r, const uint
 // boundary done (18), finalize's expert wait over (19), wave 0's up units
 // done (20), finalize done (21), router task done (22), router products
 // summed in wave 0 (23).
+// The workgroup's stamps are kept in LDS and written out at its end: a
+// store to memory at each stamp would count in the wave's outstanding memory
+// operations, and every later wait for a load would wait for it too.
+__shared__ int64_t g_stamps[kTimelineSlots];
+
 __device__ __forceinline__ void stamp(const BlockParams &p, int slot) {
   if (p.timeline && tid() == 0) {
     asm volatile("" ::: "memory");
-    p.timeline[(size_t)blockIdx.x * kTimelineSlots + slot] = (int64_t)wall_clock64();
+    g_stamps[slot] = (int64_t)wall_clock64();
     asm volatile("" ::: "memory");
   }
+}
+
+// (Wave 0, which also takes every stamp: LDS accesses of one wave are in order.)
+__device__ __forceinline__ void stamps_begin(const BlockParams &p) {
+  if (p.timeline && tid() < kTimelineSlots) g_stamps[tid()] = 0;
+}
+__device__ __forceinline__ void stamps_end(const BlockParams &p) {
+  if (p.timeline && tid() < kTimelineSlots)
+    p.timeline[(size_t)blockIdx.x * kTimelineSlots + tid()] = g_stamps[tid()];
 }
 
 // ---------------------------------------------------------------- router
@@ -1919,6 +1933,7 @@ template <bool kQ, bool kQKV = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void block_kernel(BlockParams p_arg) {
   extern __shared__ __align__(16) unsigned char lds[];
   (void)p_arg;  // read through kparams()
+  stamps_begin(kparams());
   stamp(kparams(), 0);
   // Requested now, first needed at a counter.
   // (A workgroup that starts with a router task requests it there.)
@@ -2119,6 +2134,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
   prepare_next_launch(kparams().sync, launch_gen());
   stamp(kparams(), 15);
+  stamps_end(kparams());
 }
 
 }  // namespace

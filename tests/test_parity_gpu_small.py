@@ -82,6 +82,15 @@ def test_shape_edges(case):
     run_and_check(synth.make_block("c0", seed=7, dims=d), f"edge {case}")
 
 
+@pytest.mark.parametrize("rows", [13, 70])
+def test_per_step_kernels_with_norm_weights(rows):
+    """More experts than the block kernel takes (300 > 256): mb_moe_block runs
+    the per-step kernels (router and routing, pooler and its row norm,
+    experts, unpooler and boundary), here with every norm weight."""
+    d = small(rows=rows, experts=300, top_k=6, inter=384, scoring="softmax", multiplier=1.5, eps=1e-6)
+    run_and_check(synth.make_block("c0", seed=60 + rows, dims=d, norm_weights=True), f"per-step E=300 rows={rows}")
+
+
 def test_warm_up_saturated_logits():
     rows = read_golden("warm_up_routing.txt")
     d = small(rows=2, experts=16, top_k=4, eps=None)
