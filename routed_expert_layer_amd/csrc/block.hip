@@ -1292,8 +1292,8 @@ __device__ __forceinline__ void mx_pair(const Deps &d, const MxTiles &T, int nch
 #pragma unroll
   for (int r = 0; r < kRing; ++r) {
     const bool ok = r < nch;
-    W0[r] = ld_b128(rw, ok ? o0 + ws * r : kOob);
-    W1[r] = ld_b128(rw, ok ? o1 + ws * r : kOob);
+    W0[r] = ld_nt16(rw, ok ? o0 + ws * r : kOob);
+    W1[r] = ld_nt16(rw, ok ? o1 + ws * r : kOob);
   }
   SW S0[kRing / 4], S1[kRing / 4];
 #pragma unroll
@@ -1355,8 +1355,8 @@ __device__ __forceinline__ void mx_pair(const Deps &d, const MxTiles &T, int nch
         }
         const int cn = c0 + kRing + r;
         const bool ok = cn < nch;
-        W0[r] = ld_b128(rw, ok ? o0 + ws * cn : kOob);
-        W1[r] = ld_b128(rw, ok ? o1 + ws * cn : kOob);
+        W0[r] = ld_nt16(rw, ok ? o0 + ws * cn : kOob);
+        W1[r] = ld_nt16(rw, ok ? o1 + ws * cn : kOob);
       }
 #pragma unroll
       for (int q = 0; q < kRing / 4; ++q) {
@@ -1387,8 +1387,8 @@ __device__ __forceinline__ void mx_pair_all(const Deps &d, const MxTiles &T, int
 #pragma unroll
   for (int r = 0; r < kAll; ++r) {
     const bool ok = r < nch;
-    W0[r] = ld_b128(rw, ok ? o0 + ws * r : kOob);
-    W1[r] = ld_b128(rw, ok ? o1 + ws * r : kOob);
+    W0[r] = ld_nt16(rw, ok ? o0 + ws * r : kOob);
+    W1[r] = ld_nt16(rw, ok ? o1 + ws * r : kOob);
   }
 #pragma unroll
   for (int q = 0; q < kAll / 4; ++q) {
@@ -1515,8 +1515,8 @@ __device__ __forceinline__ void mxq_pair(const Deps &d, const MxTiles &T, int nc
 #pragma unroll
   for (int r = 0; r < kRing; ++r) {
     const bool ok = r < nch;
-    W0[r] = ld_b128(rw, ok ? o0 + ws * r : kOob);
-    W1[r] = ld_b128(rw, ok ? o1 + ws * r : kOob);
+    W0[r] = ld_nt16(rw, ok ? o0 + ws * r : kOob);
+    W1[r] = ld_nt16(rw, ok ? o1 + ws * r : kOob);
   }
   uint32_t S0 = ld_b32(rs, so0), S1 = ld_b32(rs, so1);
   const int seg = kStageChunkRows / pr, nb = pr > 16 ? 2 : 1;
@@ -1552,8 +1552,8 @@ __device__ __forceinline__ void mxq_pair(const Deps &d, const MxTiles &T, int nc
         }
         const int cn = c0 + kRing + r;
         const bool ok = cn < nch;
-        W0[r] = ld_b128(rw, ok ? o0 + ws * cn : kOob);
-        W1[r] = ld_b128(rw, ok ? o1 + ws * cn : kOob);
+        W0[r] = ld_nt16(rw, ok ? o0 + ws * cn : kOob);
+        W1[r] = ld_nt16(rw, ok ? o1 + ws * cn : kOob);
       }
       S0 = N0;
       S1 = N1;
@@ -1576,8 +1576,8 @@ __device__ __forceinline__ void mxq_pair_all(const Deps &d, const MxTiles &T, in
 #pragma unroll
   for (int r = 0; r < kAll; ++r) {
     const bool ok = r < nch;
-    W0[r] = ld_b128(rw, ok ? o0 + ws * r : kOob);
-    W1[r] = ld_b128(rw, ok ? o1 + ws * r : kOob);
+    W0[r] = ld_nt16(rw, ok ? o0 + ws * r : kOob);
+    W1[r] = ld_nt16(rw, ok ? o1 + ws * r : kOob);
   }
 #pragma unroll
   for (int q = 0; q < kAll / 4; ++q) {
