@@ -346,21 +346,26 @@ def sweep(args) -> int:
     if "c0" in cases:
         print("[sweep] c0", file=sys.stderr, flush=True)
         run_block_case("c0 tiny block", [synth.make_block("c0")], 1000)
-    if "c2" in cases:
-        for skew in ("calibrated", "literal"):
-            print(f"[sweep] c2 {skew}: generating 2 weight sets", file=sys.stderr, flush=True)
-            blocks = [synth.make_block("c2", seed=s, skew=skew) for s in (2, 1002)]
-            run_block_case(f"c2 b=64 softmax, skew {skew}", blocks, 200)
-            del blocks
-            torch.cuda.empty_cache()
-    if "c3" in cases:
-        for skew in (None, "calibrated"):
-            print(f"[sweep] c3 skew={skew}: generating 2 weight sets", file=sys.stderr, flush=True)
-            full = [synth.make_c3_block(skew, seed=s) for s in (3, 1003)]
-            for b in synth.inputs.C3_BUCKETS:
-                run_block_case(f"c3 b={b} sigmoid, {skew or 'uniform'}", [f.rows(b) for f in full], 200)
-            del full
-            torch.cuda.empty_cache()
+    steps = args.sweep_steps
+    for skew in ("calibrated", "literal"):
+        if "c2" not in cases and f"c2-{skew}" not in cases:
+            continue
+        print(f"[sweep] c2 {skew}: generating 2 weight sets", file=sys.stderr, flush=True)
+        blocks = [synth.make_block("c2", seed=s, skew=skew) for s in (2, 1002)]
+        run_block_case(f"c2 b=64 softmax, skew {skew}", blocks, steps or 200)
+        del blocks
+        torch.cuda.empty_cache()
+    for skew in (None, "calibrated"):
+        name = skew or "uniform"
+        buckets = [b for b in synth.inputs.C3_BUCKETS if "c3" in cases or f"c3-{name}-{b}" in cases]
+        if not buckets:
+            continue
+        print(f"[sweep] c3 skew={skew}: generating 2 weight sets", file=sys.stderr, flush=True)
+        full = [synth.make_c3_block(skew, seed=s) for s in (3, 1003)]
+        for b in buckets:
+            run_block_case(f"c3 b={b} sigmoid, {name}", [f.rows(b) for f in full], steps or 200)
+        del full
+        torch.cuda.empty_cache()
     if "c4" not in cases:
         return 0
 
@@ -430,7 +435,10 @@ def main() -> int:
                     help="instead of the block, time a plain HBM read kernel over MiB MiB "
                          "(libmb_readprobe.so) in several variants and grids")
     ap.add_argument("--sweep-cases", default="around,c0,c2,c3,c4",
-                    help="with --sweep: which cases (comma list of around, c0, c2, c3, c4)")
+                    help="with --sweep: which cases (comma list of around, c0, c2, c3, c4, or single "
+                         "cases c2-calibrated, c2-literal, c3-uniform-<b>, c3-calibrated-<b>)")
+    ap.add_argument("--sweep-steps", type=int, default=0,
+                    help="with --sweep: timed launches per c2/c3 case (default 200)")
     ap.add_argument("--steps-around-only", action="store_true",
                     help="with --sweep: only the attention boundary and the next QKV projection")
     ap.add_argument("--sweep", action="store_true",

@@ -306,20 +306,43 @@ __device__ __forceinline__ void stamps_end(const BlockParams &p) {
 
 // ---------------------------------------------------------------- router
 
+// fp64 sum over the wave's 64 lanes, in lane 63 and returned to every lane:
+// DPP row shifts by 1, 2, 4, 8 and the row broadcasts 15 and 31 (each 64-bit
+// value moved as its two halves), a fixed order.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double sum_step64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROWS, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROWS, 0xF, false);
+  return v + __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double wave_sum_dpp64(double v) {
+  v = sum_step64<0x111, 0xF>(v);
+  v = sum_step64<0x112, 0xF>(v);
+  v = sum_step64<0x114, 0xF>(v);
+  v = sum_step64<0x118, 0xF>(v);
+  v = sum_step64<0x142, 0xA>(v);
+  v = sum_step64<0x143, 0xC>(v);
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // Logits of expert e for a block of kRouterRowBlock (4) rows, in fp64 (bf16 x
 // fp32 products are exact in fp64), rounded once to fp32.  The expert's
 // router row is read once per workgroup: wave w takes hidden elements in
 // 256-element blocks w, w + 4, w + 8, ..; its lane q adds, for each of the
 // four rows, the products of elements 4q .. 4q + 3 of those blocks in order,
-// requesting kRouterBatch blocks at once.  The 256 lane sums of a row are
-// then added through LDS in a fixed order (16 groups of 16, then the 16
-// group sums), with no cross-lane shuffles.
+// requesting kRouterBatch blocks at once.  Each wave then sums its lanes
+// (wave_sum_dpp64, the four rows' trees interleaved), and the four wave sums
+// are added in wave order.
 __device__ __forceinline__ void router_task(const BlockParams &p, unsigned &gen, int task, unsigned char *lds) {
   constexpr int RB = kRouterRowBlock;
   const int nrb = (p.b + RB - 1) / RB;
   const int e = task / nrb, t0 = (task % nrb) * RB;
   const int w = tid() / MB_WAVE, q = tid() % MB_WAVE;
-  double *red = reinterpret_cast<double *>(lds);  // [RB][kThreads], then [RB][16]
+  double *red = reinterpret_cast<double *>(lds);  // [kWaves][RB]
   // Padding elements (past H, or rows past b) load zeros and add nothing.
   double acc[RB];
 #pragma unroll
@@ -360,20 +383,18 @@ __device__ __forceinline__ void router_task(const BlockParams &p, unsigned &gen,
   // (A wave with no hidden elements here requests it now.)
   if (need_gen) gen = load_generation(p.sync);
   stamp(p, 23);
+  double ws[RB];
 #pragma unroll
-  for (int r = 0; r < RB; ++r) red[r * kThreads + tid()] = acc[r];
-  __syncthreads();
-  if (tid() < RB * 16) {
-    const double *g = red + (tid() / 16) * kThreads + (tid() % 16) * 16;
-    double v = g[0];
-    for (int i = 1; i < 16; ++i) v += g[i];
-    red[RB * kThreads + tid()] = v;
+  for (int r = 0; r < RB; ++r) ws[r] = wave_sum_dpp64(acc[r]);
+  if (q == 0) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) red[w * RB + r] = ws[r];
   }
   __syncthreads();
   if (tid() < RB && t0 + (int)tid() < p.b) {
-    const double *g = red + RB * kThreads + tid() * 16;
-    double v = g[0];
-    for (int i = 1; i < 16; ++i) v += g[i];
+    double v = red[tid()];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) v += red[ww * RB + tid()];
     const size_t te = (size_t)(t0 + tid()) * p.E + e;
     const Deps d{p.sync, gen};
     st_tagged(make_rsrc(p.logits_t), (uint32_t)(te * 8), __float_as_uint((float)v), d.tag());
@@ -642,18 +663,24 @@ __device__ __forceinline__ void route_rows(const BlockParams &p, const Deps &d, 
     int id;
     float w;
     route_one<PER>(p, l, bias, id, w);
-    if (lane < p.k) {
-      const int r = t * p.k + lane;
-      const uint32_t tag = d.tag();
+    // The kRouteReps copies of the row's ids and weights, one word per lane:
+    // lane l stores slot l % k of copy (l / k) % kRouteReps, an id below
+    // kRouteReps k and a weight above (the slot's values from lane l % k).
+    const uint32_t tag = d.tag();
+    const int nst = 2 * kRouteReps * p.k;
 #pragma unroll 1
-      for (int c = 0; c < kRouteReps; ++c) {
-        st_tagged(rr, (uint32_t)(((size_t)c * R2 + r) * 8), (uint32_t)id, tag);
-        st_tagged(rr, (uint32_t)(((size_t)c * R2 + R2 / 2 + r) * 8), __float_as_uint(w), tag);
-      }
-      if (p.routing_out) {
-        p.ids[r] = id;
-        p.wts[r] = w;
-      }
+    for (int s0 = 0; s0 < nst; s0 += MB_WAVE) {
+      const int si = s0 + lane, j = si % p.k, c = (si / p.k) % kRouteReps, kind = si / (kRouteReps * p.k);
+      const int sid = __shfl(id, j, MB_WAVE);
+      const float sw = __shfl(w, j, MB_WAVE);
+      if (si < nst)
+        st_tagged(rr, (uint32_t)(((size_t)c * R2 + kind * (R2 / 2) + t * p.k + j) * 8),
+                  kind ? __float_as_uint(sw) : (uint32_t)sid, tag);
+    }
+    if (lane < p.k && p.routing_out) {
+      const int r = t * p.k + lane;
+      p.ids[r] = id;
+      p.wts[r] = w;
     }
   }
 }
@@ -847,6 +874,9 @@ __device__ __forceinline__ int *proj_flag(unsigned char *lds) {
 // activation request.
 constexpr int kWideRing = 8;
 constexpr int kWideCols = 16 * kWaves;
+// 16-byte activation pieces per thread and segment: the stage holds 64 rows
+// x 256, 32 x 512 or 16 x 1024 elements, 2048 pieces.
+constexpr int kWidePieces = 2048 / kThreads;
 template <bool kCoherentA, typename Wait>
 __device__ __forceinline__ void proj_wide(rsrc_t ra, const uint16_t *w, int rows, int n_out, int kdim, int gi, int q,
                                           int ks, float *part, uint16_t *out, uint32_t *out_t, uint32_t tag,
@@ -870,27 +900,31 @@ __device__ __forceinline__ void proj_wide(rsrc_t ra, const uint16_t *w, int rows
     f32x4_t acc[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // Rows t0 .. t0 + 16 nb, elements k0 + 32 s0 .. + seg, in 16-byte
+    // pieces (at most kWidePieces per thread): requested into registers one
+    // segment ahead, so that a segment's loads overlap the one before.
+    const int ppr = seg / 8, pieces = 16 * nb * ppr;
+    u32x4_t v[kWidePieces];
+    auto act_req = [&](int s0) {
+#pragma unroll
+      for (int u = 0; u < kWidePieces; ++u) {
+        const int i = (int)tid() + kThreads * u;
+        const int m = i / ppr, pc = i % ppr;
+        const int t = t0 + m, k = 32 * s0 + 8 * pc;
+        const bool in = i < pieces && t < rows && k < kr;
+        const uint32_t off = in ? (uint32_t)(((size_t)t * kdim + k0 + k) * 2) : kOob;
+        v[u] = kCoherentA ? ld_co16(ra, off) : ld_b128(ra, off);
+      }
+    };
+    act_req(0);
     for (int s0 = 0; s0 < nch; s0 += seg / 32) {
-      // Rows t0 .. t0 + 16 nb, elements k0 + 32 s0 .. + seg, in 16-byte pieces.
-      const int ppr = seg / 8, pieces = 16 * nb * ppr;
-      for (int i0 = 0; i0 < pieces; i0 += kThreads * 4) {
-        u32x4_t v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + (int)tid() + kThreads * u;
-          const int m = i / ppr, pc = i % ppr;
-          const int t = t0 + m, k = 32 * s0 + 8 * pc;
-          const bool in = i < pieces && t < rows && k < kr;
-          const uint32_t off = in ? (uint32_t)(((size_t)t * kdim + k0 + k) * 2) : kOob;
-          v[u] = kCoherentA ? ld_co16(ra, off) : ld_b128(ra, off);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + (int)tid() + kThreads * u;
-          if (i < pieces) *reinterpret_cast<u32x4_t *>(stage + (i / ppr) * srow + (i % ppr) * 16) = v[u];
-        }
+      for (int u = 0; u < kWidePieces; ++u) {
+        const int i = (int)tid() + kThreads * u;
+        if (i < pieces) *reinterpret_cast<u32x4_t *>(stage + (i / ppr) * srow + (i % ppr) * 16) = v[u];
       }
       __syncthreads();
+      if (s0 + seg / 32 < nch) act_req(s0 + seg / 32);
       for (int c0 = s0; c0 < s0 + seg / 32 && c0 < nch; c0 += kWideRing) {
 #pragma unroll
         for (int r = 0; r < kWideRing; ++r) {
@@ -983,18 +1017,30 @@ __device__ __forceinline__ void unpool_task(const BlockParams &p, const Deps &d,
 #pragma unroll
   for (int t = 0; t < kUnpoolTiles; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const uint32_t arow = L.r16 < p.b ? (uint32_t)(((size_t)L.r16 * P + 8 * L.g) * 2) : kOob;
-#pragma unroll
-  for (int i0 = 0; i0 < kUnpoolChunks; i0 += kUnpoolActBatch) {
-    u32x4_t A[kUnpoolActBatch];
+  // Activations in batches, the next batch requested before the current
+  // one's products (so the requests overlap); batches past this wave's last
+  // chunk are skipped.
+  constexpr int NB = kUnpoolChunks / kUnpoolActBatch;
+  static_assert(kUnpoolChunks % kUnpoolActBatch == 0, "whole batches");
+  const int nbw = uniform((c_end - c_begin - L.wave + kWaves * kUnpoolActBatch - 1) / (kWaves * kUnpoolActBatch));
+  u32x4_t A[2][kUnpoolActBatch];
+  auto act_batch = [&](int b, u32x4_t(&dst)[kUnpoolActBatch]) {
 #pragma unroll
     for (int i = 0; i < kUnpoolActBatch; ++i) {
-      const int c = c_begin + L.wave + kWaves * (i0 + i);
-      A[i] = ld_co16(ra, (arow != kOob && c < c_end) ? arow + (uint32_t)c * 64u : kOob);
+      const int c = c_begin + L.wave + kWaves * (b * kUnpoolActBatch + i);
+      dst[i] = ld_co16(ra, (arow != kOob && c < c_end) ? arow + (uint32_t)c * 64u : kOob);
     }
+  };
+  act_batch(0, A[0]);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (b >= nbw) break;
+    if (b + 1 < NB && b + 1 < nbw) act_batch(b + 1, A[(b + 1) % 2]);
 #pragma unroll
     for (int i = 0; i < kUnpoolActBatch; ++i)
 #pragma unroll
-      for (int t = 0; t < kUnpoolTiles; ++t) acc[t] = mfma_bf16(as_bf16x8(W[t][i0 + i]), as_bf16x8(A[i]), acc[t]);
+      for (int t = 0; t < kUnpoolTiles; ++t)
+        acc[t] = mfma_bf16(as_bf16x8(W[t][b * kUnpoolActBatch + i]), as_bf16x8(A[b % 2][i]), acc[t]);
   }
   f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);  // [kWaves][kUnpoolTiles][64]
 #pragma unroll
