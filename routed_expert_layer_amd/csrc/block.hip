@@ -1362,17 +1362,20 @@ __device__ __forceinline__ void mx_pair(const Deps &d, const MxTiles &T, int nch
     const int segn = min(seg, nch - seg0);
     const int ppr = ((segn + kRing - 1) / kRing) * kRing * 16;  // 16-byte pieces per row
     // In batches of kStagePieces pieces per thread, each only if it holds
-    // one of the pass's vrows rows.
+    // one of the pass's vrows rows (the batches in row order, so the needed
+    // ones come first); batch k in buf[k % 2], requested one batch ahead of
+    // its completion so that consecutive batches' requests overlap (the
+    // first segment's first two were requested with the weights, into the
+    // same two buffers).
+    StageBatch (&buf)[2] = first;
+    if (seg0 != 0) stage_issue(A, row_e, pr, seg0, segn, ppr, 0, buf[0]);
 #pragma unroll
-    for (int n0 = 0; n0 < kSegLoads; n0 += kStagePieces) {
-      if (n0 > 0 && !batch_needed(n0, ppr, vrows)) continue;
-      if (seg0 == 0 && n0 < 2 * kStagePieces) {
-        stage_store(d, A, first[n0 / kStagePieces], pr, ppr, n0, srow, stage);
-      } else {
-        StageBatch S;
-        stage_issue(A, row_e, pr, seg0, segn, ppr, n0, S);
-        stage_store(d, A, S, pr, ppr, n0, srow, stage);
-      }
+    for (int k = 0; k < kSegLoads / kStagePieces; ++k) {
+      const int n0 = k * kStagePieces, n1 = n0 + kStagePieces;
+      if (k > 0 && !batch_needed(n0, ppr, vrows)) break;
+      if (n1 < kSegLoads && batch_needed(n1, ppr, vrows) && !(seg0 == 0 && k + 1 < 2))
+        stage_issue(A, row_e, pr, seg0, segn, ppr, n1, buf[(k + 1) % 2]);
+      stage_store(d, A, buf[k % 2], pr, ppr, n0, srow, stage);
     }
     __syncthreads();
     for (int c0 = seg0; c0 < seg0 + segn; c0 += kRing) {
