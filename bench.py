@@ -131,6 +131,89 @@ def per_launch_us(torch, fn, n: int) -> list:
     return [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)]
 
 
+# The block kernel's timeline slots (mb_block_taps.timeline): what each
+# workgroup stamps, in microseconds from the launch's first workgroup start.
+TIMELINE_SLOTS = {
+    0: "start", 1: "first router task", 2: "first route task", 3: "first pool task",
+    22: "router task done", 23: "router products summed", 12: "route task: logits seen",
+    14: "route task: rows routed", 7: "pool task done", 13: "routes seen", 5: "routing state ready",
+    6: "units start", 20: "wave 0's up units done", 11: "units done", 8: "first finalize task",
+    19: "finalize: experts' down units seen", 21: "finalize done", 9: "first unpool task",
+    16: "unpool task done", 10: "first boundary task", 17: "boundary: unpooler seen",
+    18: "boundary done", 15: "end"}
+# The steps after the experts, in order, for the per-launch critical chain.
+TIMELINE_CHAIN = (11, 19, 21, 16, 17, 18, 15)
+
+
+def timeline(launches: int, c3_rows: int = 0) -> int:
+    """Per-phase breakdown of the headline block from the kernel's own
+    timeline tap: the four c1 weight sets rotated as in the benchmark (or,
+    with c3_rows, two weight sets of the row-bucket sweep at that many rows,
+    uniform routing), warm-up, then `launches` traced launches (each after an
+    untraced one).  Prints,
+    per slot, how many workgroups stamped it and the p10 / p50 / p90 / max of
+    their stamps over all traced launches, then the mean over launches of the
+    latest and the median stamp of each step after the experts."""
+    import numpy as np
+    import torch
+
+    import routed_expert_layer_amd as rel
+    import synth
+    from synth.device import dims_kwargs, upload, upload_weights
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    if c3_rows:
+        blocks = [synth.make_c3_block(None, seed=s).rows(c3_rows) for s in (3, 1003)]
+    else:
+        blocks = [synth.make_block("c1", seed=s) for s in WEIGHT_SEEDS]
+    d = blocks[0].dims
+    wt0, x, stream = upload(blocks[0], dev)
+    tensors = [wt0] + [upload_weights(b, dev) for b in blocks[1:]]
+    dims = rel.make_dims(**dims_kwargs(d))
+    weights = [rel.make_weights(**t) for t in tensors]
+    for t, w in zip(tensors, weights):
+        t["experts_packed"] = rel.pack_experts(dims, w, dev)
+    weights = [rel.make_weights(**t) for t in tensors]
+    ws = rel.workspace(dims, dev)
+    xn = torch.zeros((d.rows, d.hidden), dtype=torch.bfloat16, device=dev)
+    S = len(weights)
+    for i in range(50):
+        rel.mb_moe_block(dims, x, weights[i % S], stream, xn, ws)
+    torch.cuda.synchronize()
+    acc = {}
+    chains_max, chains_p50 = [], []
+    for rep_ in range(launches):
+        tl = torch.zeros((1024, 32), dtype=torch.int64, device=dev)
+        rel.mb_moe_block(dims, x, weights[rep_ % S], stream, xn, ws)
+        rel.mb_moe_block(dims, x, weights[(rep_ + 1) % S], stream, xn, ws, taps=rel.make_taps(timeline=tl))
+        torch.cuda.synchronize()
+        a = tl.cpu().numpy()
+        a = a[: int((a[:, 0] != 0).sum())]
+        t0 = a[:, 0].min()
+        per = {}
+        for slot in TIMELINE_SLOTS:
+            v = a[:, slot]
+            v = v[v != 0]
+            if v.size:
+                per[slot] = (v - t0) / 100.0
+                acc.setdefault(slot, []).append(per[slot])
+        chains_max.append([per[s].max() if s in per else np.nan for s in TIMELINE_CHAIN])
+        chains_p50.append([np.median(per[s]) if s in per else np.nan for s in TIMELINE_CHAIN])
+    print(f"grid {a.shape[0]} workgroups, {launches} traced launches; us from the first workgroup start")
+    print(f"{'slot':>4}  {'stamp':<36} {'wgs':>5} {'p10':>7} {'p50':>7} {'p90':>7} {'max':>7}")
+    for slot in sorted(acc, key=lambda s: np.median(np.concatenate(acc[s]))):
+        v = np.concatenate(acc[slot])
+        print(f"{slot:>4}  {TIMELINE_SLOTS[slot]:<36} {v.size // launches:>5} {np.percentile(v, 10):7.2f} "
+              f"{np.percentile(v, 50):7.2f} {np.percentile(v, 90):7.2f} {v.max():7.2f}")
+    names = [TIMELINE_SLOTS[s] for s in TIMELINE_CHAIN]
+    for label, ch in (("latest", chains_max), ("median", chains_p50)):
+        m = np.nanmean(np.array(ch), axis=0)
+        print(f"after the experts, {label} workgroup per launch (mean over launches): " +
+              "; ".join(f"{n} {v:.2f}" for n, v in zip(names, m)))
+    return 0
+
+
 def read_probe(mib: int) -> int:
     """Time the plain HBM read kernel (libmb_readprobe.so): over one buffer
     of `mib` MiB in each variant and grid, then, in the best variant, at the
@@ -431,6 +514,11 @@ def main() -> int:
                     help="the W4A4 variant: the experts' activations quantized to MXFP4 (needs the "
                          "packed layout); not the headline line")
     ap.add_argument("--print-source-hash", action="store_true")
+    ap.add_argument("--timeline", type=int, default=0, metavar="LAUNCHES",
+                    help="instead of the metric, a per-phase breakdown of the headline block from the "
+                         "kernel's timeline tap over LAUNCHES traced launches")
+    ap.add_argument("--timeline-c3-rows", type=int, default=0, metavar="B",
+                    help="with --timeline: the row-bucket sweep's dims at B rows instead of the headline block")
     ap.add_argument("--read-probe", type=int, default=0, metavar="MiB",
                     help="instead of the block, time a plain HBM read kernel over MiB MiB "
                          "(libmb_readprobe.so) in several variants and grids")
@@ -459,6 +547,8 @@ def main() -> int:
         return sweep(args)
     if args.read_probe > 0:
         return read_probe(args.read_probe)
+    if args.timeline > 0:
+        return timeline(args.timeline, args.timeline_c3_rows)
 
     import numpy as np
     import torch
