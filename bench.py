@@ -46,7 +46,7 @@ def algorithmic_bytes(d, n_active: int, norm_weights=(False, False, False)) -> i
 
 # Sources whose change invalidates a stored traffic measurement of the block
 # kernel (its code and its launch configuration).
-KERNEL_SOURCES = ("block.hip", "block_w4a4.hip", "block_qkv.hip", "block_w4a4_qkv.hip", "api.hip", "pack.hip", "mb_block.h", "mb_device.h", "mb_sync.h", "mb_internal.h")
+KERNEL_SOURCES = ("block.hip", "block_w4a4.hip", "block_qkv.hip", "block_w4a4_qkv.hip", "block_many.hip", "api.hip", "pack.hip", "mb_block.h", "mb_device.h", "mb_sync.h", "mb_internal.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_kernel_c1_traffic.txt")
 
 

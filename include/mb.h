@@ -265,8 +265,8 @@ int mb_moe_block(const mb_dims *dims, const uint16_t *x, const mb_weights *w,
  * or freed, by the library or any library it calls.
  *   - Sizes: the workspace layout's buffers must fit in the first 56 MiB and
  *     its hand-off words in the last MB_NOALLOC_TAGGED_BYTES (8 MiB), else
- *     MB_ERR_SCRATCH before anything is enqueued.  Up to 94 rows fit at
- *     H 4096, P 2048, I 1024, E 64, top_k 4 and up to 55 rows at H 7168,
+ *     MB_ERR_SCRATCH before anything is enqueued.  Up to 91 rows fit at
+ *     H 4096, P 2048, I 1024, E 64, top_k 4 and up to 53 rows at H 7168,
  *     P 3072, I 1536, E 128, top_k 8; mb_moe_block with a workspace serves
  *     larger sizes.
  *   - The first call on a GPU (with that GPU current) looks up the array's

@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libmb.so")
 # The HBM read probe bench.py --read-probe times (not part of libmb.so).
 PROBE_SRC = "read_probe.hip"
 PROBE_LIB = os.path.join(PKG, "libmb_readprobe.so")
-SOURCES = ["api.hip", "block.hip", "block_w4a4.hip", "block_qkv.hip", "block_w4a4_qkv.hip", "route.hip", "gemm_bf16.hip", "experts.hip", "boundary.hip", "pack.hip"]
+SOURCES = ["api.hip", "block.hip", "block_w4a4.hip", "block_qkv.hip", "block_w4a4_qkv.hip", "block_many.hip", "route.hip", "gemm_bf16.hip", "experts.hip", "boundary.hip", "pack.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

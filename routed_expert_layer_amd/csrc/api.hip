@@ -39,6 +39,7 @@ Layout layout_of(const mb_dims &d) {
   static_assert(kMaxRows <= kSyncMaxRows, "the counter sets cover every row count");
   L.sync = take(kSyncWords * 4);
   L.pool_cnt = take((P / 16) * 4);
+  L.rtr_cnt = take((size_t)kMaxGrid * 4);  // the MFMA router's split counters
   L.qkv_cnt = take(kMaxQkvGroups * 4);
   L.logits = take(b * E * 4);
   L.ids = take(R * 4);
@@ -59,6 +60,9 @@ Layout layout_of(const mb_dims &d) {
   L.pool_part = take((size_t)kMaxPoolSplit * b * P * 4);
   L.unpool_part = take((size_t)kMaxSplitK * b * H * 4);
   L.qkv_part = take((size_t)kMaxSplitK * b * (size_t)d.qkv_rows * 4);
+  // The fp64-MFMA router's split partials (splits x tiles never exceed the
+  // grid; written before they are read).
+  L.rtr_part = take((size_t)kMaxGrid * 256 * 8);
   // Tagged hand-off words of the block kernel (8 bytes each).
   size_t t = 0;
   auto ttake = [&](size_t bytes) {
@@ -285,16 +289,16 @@ int device_cus() {
   return n;
 }
 
-int block_occupancy(size_t lds, bool w4a4, bool qkv) {
+int block_occupancy(size_t lds, bool w4a4, bool qkv, bool many) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  const auto key = std::make_tuple(dev, (w4a4 ? 2 : 0) + (qkv ? 1 : 0), lds);
+  const auto key = std::make_tuple(dev, (w4a4 ? 2 : 0) + (qkv ? 1 : 0) + (many ? 4 : 0), lds);
   {
     std::lock_guard<std::mutex> lock(g_shape_mu);
     const auto it = g_occ.find(key);
     if (it != g_occ.end()) return it->second;
   }
-  const int n = block_max_groups_per_cu(lds, w4a4, qkv);
+  const int n = block_max_groups_per_cu(lds, w4a4, qkv, many);
   if (n < 1) return 0;
   std::lock_guard<std::mutex> lock(g_shape_mu);
   g_occ[key] = n;
@@ -347,6 +351,8 @@ BlockParams base_params(const mb_dims &d, const mb_weights *w, void *ws, size_t 
   p.act = at<uint16_t>(ws, L.act);
   p.moe_rep = at<uint16_t>(ws, L.moe_rep);
   p.pool_cnt = at<unsigned>(ws, L.pool_cnt);
+  p.rtr_part = at<double>(ws, L.rtr_part);
+  p.rtr_cnt = at<unsigned>(ws, L.rtr_cnt);
   p.sync = at<unsigned>(ws, L.sync);
   p.h = at<uint16_t>(ws, L.h);
   p.moe_out = at<uint16_t>(ws, L.moe_out);
@@ -405,7 +411,7 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   const size_t route_bytes = route_lds_bytes(p.b, p.k, p.E);
   const size_t lds = route_bytes + kBlockScratchBytes;
   if (lds > 64 * 1024) return none;
-  const int occ = block_occupancy(lds, p.w4a4 != 0, p.n_qkv > 0);
+  const int occ = block_occupancy(lds, p.w4a4 != 0, p.n_qkv > 0, false);
   const int cus = device_cus();
   if (occ < 1 || cus < 1) return none;
   int grid = cus * (occ < kBlockGroupsPerCu ? occ : kBlockGroupsPerCu);
@@ -416,8 +422,23 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   // when one-expert tasks would not fit the grid at once.
   const int nrb = (p.b + kRouterRowBlock - 1) / kRouterRowBlock;
   p.router_multi = p.E * nrb > grid ? 1 : 0;
+  // From 64 rows: tiles of 16 rows x 16 experts on fp64 MFMA, the
+  // contraction split (in whole 32-element chunks) so that tiles x splits
+  // fill the grid at most once (at 32 rows the four-expert tasks were as fast).
+  const int rtiles = ((p.b + 15) / 16) * ((p.E + 15) / 16);
+  p.router_mma = (st.router && p.router_multi && p.b >= 64) ? 1 : 0;
+  if (p.router_mma && !p.w4a4 && p.n_qkv == 0) {
+    // The plain kernel's many-rows instance, with its own occupancy.
+    const int occ_m = block_occupancy(lds, false, false, true);
+    if (occ_m < 1) return none;
+    if (occ_m < occ) grid = std::min(kMaxGrid, cus * std::min(occ_m, kBlockGroupsPerCu));
+  }
+  p.router_ks = 1;
+  while (p.router_ks * 2 * rtiles <= grid && p.H % (p.router_ks * 2 * 32) == 0) p.router_ks *= 2;
   const int n_router =
-      st.router ? (p.router_multi ? (p.E + kRouterExperts - 1) / kRouterExperts : p.E) * nrb : 0;
+      st.router ? (p.router_mma ? rtiles * p.router_ks
+                                : (p.router_multi ? (p.E + kRouterExperts - 1) / kRouterExperts : p.E) * nrb)
+                : 0;
   const int n_fin = st.experts ? p.b * ((p.P + kFinChunk - 1) / kFinChunk) : 0;
   const int n_boundary = st.unpool ? p.b : 0;
   const int n_prenorm = (st.pool && p.pre_norm_w) ? p.b : 0;

@@ -403,6 +403,100 @@ __device__ __forceinline__ void router_task(const BlockParams &p, unsigned &gen,
   stamp(p, 22);
 }
 
+// Many rows: the logits of a tile of 16 rows x 16 experts over the
+// contraction split q of router_ks (32-element chunks, dealt to the waves in
+// turn), on the fp64 MFMA (bf16 x fp32 products are exact in fp64; each
+// product added in fp64).  For a chunk, lane l (r = l % 16, g = l / 16)
+// loads elements 8g .. 8g + 7 of row r's x and of expert r's router row;
+// step s of eight multiplies element s: A[r][g] = x, B[g][r] = w, so the
+// steps together sum the chunk.  The four waves' tiles are added in wave
+// order; with several splits the last to finish adds the partials in split
+// order; the sum is rounded once to fp32 and goes out as tagged logits.
+constexpr int kRouterMmaAhead = 4;  // chunks requested ahead per wave
+__device__ __forceinline__ void router_mma_task(const BlockParams &p, unsigned &gen, int task, unsigned char *lds) {
+  const int lane = tid() % MB_WAVE, w = tid() / MB_WAVE, r = lane % 16, g = lane / 16;
+  const int ks = p.router_ks, ET = (p.E + 15) / 16;
+  const int tile = task / ks, q = task % ks, rt = tile / ET, et = tile % ET;
+  const int kr = p.H / ks, k0 = q * kr, nchk = kr / 32;
+  const int nw = (nchk - w + kWaves - 1) / kWaves;  // this wave's chunks: w, w + 4, ..
+  const int row = rt * 16 + r, e = et * 16 + r;
+  const uint32_t xrow = row < p.b ? (uint32_t)(((size_t)row * p.H + k0 + 8 * g) * 2) : kOob;
+  const uint32_t wrow = e < p.E ? (uint32_t)(((size_t)e * p.H + k0 + 8 * g) * 4) : kOob;
+  const rsrc_t rx = make_rsrc(p.x), rw = make_rsrc(p.router_w);
+  u32x4_t xv[kRouterMmaAhead], w0[kRouterMmaAhead], w1[kRouterMmaAhead];
+  auto req = [&](int c, int i) {
+    const bool ok = c < nw;
+    const uint32_t cw = (uint32_t)(w + kWaves * c) * 32u;
+    xv[i] = ld_b128(rx, (ok && xrow != kOob) ? xrow + cw * 2u : kOob);
+    w0[i] = ld_b128(rw, (ok && wrow != kOob) ? wrow + cw * 4u : kOob);
+    w1[i] = ld_b128(rw, (ok && wrow != kOob) ? wrow + cw * 4u + 16u : kOob);
+  };
+#pragma unroll
+  for (int i = 0; i < kRouterMmaAhead; ++i) req(i, i);
+  if (gen == kGenPending) gen = load_generation(p.sync);
+  f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+  for (int c0 = 0; c0 < nw; c0 += kRouterMmaAhead) {
+#pragma unroll
+    for (int i = 0; i < kRouterMmaAhead; ++i) {
+      if (c0 + i < nw) {
+        const float wf[8] = {__uint_as_float(w0[i][0]), __uint_as_float(w0[i][1]), __uint_as_float(w0[i][2]),
+                             __uint_as_float(w0[i][3]), __uint_as_float(w1[i][0]), __uint_as_float(w1[i][1]),
+                             __uint_as_float(w1[i][2]), __uint_as_float(w1[i][3])};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const uint32_t xb = (s & 1) ? (xv[i][s / 2] >> 16) : (xv[i][s / 2] & 0xFFFFu);
+          acc = mfma_f64(bf16_bits_to_f32(xb), wf[s], acc);
+        }
+      }
+      req(c0 + kRouterMmaAhead + i, i);
+    }
+  }
+  stamp(p, 23);
+  // Lane l's element v is D[4 v + l / 16][l % 16]; added over the waves in order.
+  double *red = reinterpret_cast<double *>(lds);  // [kWaves][4][64]
+  int *flag = reinterpret_cast<int *>(lds + kWaves * 4 * MB_WAVE * sizeof(double));
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[(w * 4 + v) * MB_WAVE + lane] = acc[v];
+  __syncthreads();
+  const int i = tid() / 16, j = tid() % 16;  // this thread's tile element
+  const int src = (i % 4) * 16 + j, v = i / 4;
+  double sum = red[v * MB_WAVE + src];
+#pragma unroll
+  for (int ww = 1; ww < kWaves; ++ww) sum += red[(ww * 4 + v) * MB_WAVE + src];
+  const int trow = rt * 16 + i, te = et * 16 + j;
+  const Deps d{p.sync, gen};
+  bool out = true;
+  if (ks > 1) {
+    const rsrc_t rp = make_rsrc(p.rtr_part);
+    const uint64_t bits = __builtin_bit_cast(uint64_t, sum);
+    st_co8(rp, (uint32_t)((((size_t)q * ((p.b + 15) / 16) * ET + tile) * 256 + tid()) * 8),
+           u32x2_t{(uint32_t)bits, (uint32_t)(bits >> 32)});
+    out = last_arrival(&p.rtr_cnt[tile], (unsigned)ks, flag);
+    if (out) {
+      u32x2_t pv[8];
+      for (int q0 = 0; q0 < ks; q0 += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          pv[u] = ld_co8(rp, q0 + u < ks
+                                 ? (uint32_t)((((size_t)(q0 + u) * ((p.b + 15) / 16) * ET + tile) * 256 + tid()) * 8)
+                                 : kOob);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const double pu = __builtin_bit_cast(double, ((uint64_t)pv[u][1] << 32) | pv[u][0]);
+          if (q0 + u < ks) sum = (q0 + u == 0) ? pu : sum + pu;
+        }
+      }
+      if (tid() == 0) __hip_atomic_store(&p.rtr_cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (out && trow < p.b && te < p.E) {
+    const size_t idx = (size_t)trow * p.E + te;
+    st_tagged(make_rsrc(p.logits_t), (uint32_t)(idx * 8), __float_as_uint((float)sum), d.tag());
+  }
+  __syncthreads();  // (the workgroup's next task reuses the LDS)
+  stamp(p, 22);
+}
+
 // Many rows (more router tasks than workgroups at one expert each): the
 // logits of kRouterExperts (4) experts for a block of 4 rows.  Same split of
 // the hidden elements over the waves and lanes as router_task, the lane
@@ -1978,7 +2072,9 @@ __device__ __forceinline__ const BlockParams &kparams() {
 // kQ: the W4A4 variant (MXFP4 activations into the experts), a kernel of its
 // own so that each keeps its own code layout and registers.
 // kQKV: the next layer's QKV projection follows the boundary in the launch.
-template <bool kQ, bool kQKV = false>
+// kMR: the fp64-MFMA router tiles (many rows) are compiled in; the plain
+// kernel has a many-rows instance of its own for them, the others take both.
+template <bool kQ, bool kQKV = false, bool kMR = kQ || kQKV>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void block_kernel(BlockParams p_arg) {
   extern __shared__ __align__(16) unsigned char lds[];
   (void)p_arg;  // read through kparams()
@@ -2015,7 +2111,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         const BlockParams &p = kparams();
         if (first) stamp(p, 1);
         first = false;
-        if (p.router_multi) router_task_multi(p, gen, j, lds + p.lds_route_bytes);
+        if (kMR && p.router_mma) router_mma_task(p, gen, j, lds + p.lds_route_bytes);
+        else if (p.router_multi) router_task_multi(p, gen, j, lds + p.lds_route_bytes);
         else router_task(p, gen, j, lds + p.lds_route_bytes);
       }
     }
@@ -2195,19 +2292,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 // not to be trusted, and the workspace reports it (mb_workspace_status).
 // The W4A4 kernel, the kernel with the fused next-QKV projection and the
 // kernel with both are built from this file in translation units of their own
-// (block_w4a4.hip, block_qkv.hip, block_w4a4_qkv.hip): sharing one code object
-// moved the bf16 kernel's code and cost it ~0.6 us per launch.
-#if !defined(MB_BLOCK_W4A4) && !defined(MB_BLOCK_QKV)
+// (block_w4a4.hip, block_qkv.hip, block_w4a4_qkv.hip), and so is the plain
+// kernel's many-rows instance (block_many.hip): sharing one code object moved
+// the bf16 kernel's code and cost it ~0.6 us per launch.
+#if defined(MB_BLOCK_MANY)
+hipError_t launch_block_many(const BlockParams &p, int grid, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL((block_kernel<false, false, true>), dim3(grid), dim3(kThreads), lds, s, p);
+  return hipGetLastError();
+}
+
+int block_max_groups_per_cu_many(size_t lds) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_kernel<false, false, true>, kThreads, lds) !=
+      hipSuccess)
+    return 0;
+  return n;
+}
+#elif !defined(MB_BLOCK_W4A4) && !defined(MB_BLOCK_QKV)
 hipError_t launch_block(const BlockParams &p, int grid, size_t lds, hipStream_t s) {
   if (p.w4a4) return launch_block_w4a4(p, grid, lds, s);
   if (p.n_qkv > 0) return launch_block_qkv(p, grid, lds, s);
+  if (p.router_mma) return launch_block_many(p, grid, lds, s);
   hipLaunchKernelGGL(block_kernel<false>, dim3(grid), dim3(kThreads), lds, s, p);
   return hipGetLastError();
 }
 
-int block_max_groups_per_cu(size_t lds, bool w4a4, bool qkv) {
+int block_max_groups_per_cu(size_t lds, bool w4a4, bool qkv, bool many) {
   if (w4a4) return block_max_groups_per_cu_w4a4(lds, qkv);
   if (qkv) return block_max_groups_per_cu_qkv(lds);
+  if (many) return block_max_groups_per_cu_many(lds);
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_kernel<false>, kThreads, lds) != hipSuccess)
     return 0;

@@ -126,6 +126,10 @@ struct BlockParams {
   int has_up, needs_routing, routing_out, route_given, logits_in;
   int unpool_wide;  // unpooler in 64-feature tiles (many rows)
   int router_multi; // router tasks of kRouterExperts experts (many rows)
+  int router_mma;   // router tiles of 16 rows x 16 experts on fp64 MFMA (many rows)
+  int router_ks;    // their contraction splits (partials added by the last split)
+  double *rtr_part; // [router_ks][tiles][16][16] fp64 partials
+  unsigned *rtr_cnt;  // [tiles] splits done (left at zero)
   int cus;          // compute units (the grid holds grid / cus workgroups per CU)
   int lds_route_bytes;
   // inputs
@@ -228,7 +232,9 @@ constexpr size_t kProjScratchBytes = 4 * 4 * 64 * 16 + 64;
 constexpr size_t kBlockScratchBytes = kProjScratchBytes > kStageBytes ? kProjScratchBytes : kStageBytes;
 
 hipError_t launch_block(const BlockParams &p, int grid, size_t lds, hipStream_t s);
-int block_max_groups_per_cu(size_t lds, bool w4a4, bool qkv);
+int block_max_groups_per_cu(size_t lds, bool w4a4, bool qkv, bool many);
+hipError_t launch_block_many(const BlockParams &p, int grid, size_t lds, hipStream_t s);
+int block_max_groups_per_cu_many(size_t lds);
 hipError_t launch_block_w4a4(const BlockParams &p, int grid, size_t lds, hipStream_t s);
 int block_max_groups_per_cu_w4a4(size_t lds, bool qkv);
 hipError_t launch_block_qkv(const BlockParams &p, int grid, size_t lds, hipStream_t s);

@@ -64,6 +64,13 @@ __device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// D[16x16] += A[16 x 4] * B[4 x 16] in fp64.  Lane l holds A[l % 16][l / 16]
+// and B[l / 16][l % 16]; element v of the result is D[4 v + l / 16][l % 16].
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f64x4_t mfma_f64(double a, double b, f64x4_t c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
 // D += (A with its lanes' E8M0 scales) x (B with theirs), A and B MXFP4: the
 // 16x16x128 scaled MFMA with E2M1 operands.  A lane holds 32 codes (16 bytes,
 // element k at nibble k % 8 of word k / 8, low nibble first) of row / column

@@ -26,6 +26,7 @@ struct Layout {
   size_t h, act, y, ssq, moe_out, moe_rep, u, partial;
   size_t pool_part, unpool_part, pool_cnt, qkv_cnt, qkv_part;
   size_t t_logits, t_routes, t_h, t_hn, t_act, tagged;
+  size_t rtr_part, rtr_cnt;
   size_t total;
 };
 

@@ -290,7 +290,7 @@ def test_noalloc_block_checks_arguments_and_sizes_before_anything():
     bad = c1_dims(top_k=0)
     assert L.mb_moe_block_noalloc(ctypes.byref(bad), FAKE, ctypes.byref(w), FAKE, FAKE, None, None) == MB_ERR_DIMS
     big = dict(hidden=7168, pooled=3072, inter=1536, experts=128, top_k=8, scoring="softmax")
-    for rows, fits in ((1, True), (16, True), (32, True), (55, True), (56, False), (64, False), (256, False)):
+    for rows, fits in ((1, True), (16, True), (32, True), (53, True), (54, False), (64, False), (256, False)):
         dd = c1_dims(rows=rows, **big)
         st, n = status_of_ws(dd)
         assert st == MB_OK

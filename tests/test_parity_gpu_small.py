@@ -76,6 +76,10 @@ def test_ragged_rows(rows):
     dict(rows=1024, inter=128),  # largest row count
     dict(hidden=96, pooled=384, inter=384, rows=21),  # odd multiples of the tile sizes
     dict(hidden=4096, pooled=2048, inter=1024, experts=64, top_k=4, rows=3),
+    # fp64-MFMA router tiles: contraction split 8 ways; and one split (more
+    # tiles than half the grid), rows and experts past whole tiles.
+    dict(rows=64, experts=64, hidden=512, top_k=4),
+    dict(rows=500, experts=136, top_k=2, inter=128),
 ])
 def test_shape_edges(case):
     d = small(**case)
