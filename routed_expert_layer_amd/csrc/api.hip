@@ -38,7 +38,7 @@ Layout layout_of(const mb_dims &d) {
   // and P, so one workspace serves calls of any row count.
   static_assert(kMaxRows <= kSyncMaxRows, "the counter sets cover every row count");
   L.sync = take(kSyncWords * 4);
-  L.pool_cnt = take((P / 16) * 4);
+  L.pool_cnt = take(((P + 63) / 64) * kMaxRowBlocks * 4);  // per pooler tile and 64-row block
   L.rtr_cnt = take((size_t)kMaxGrid * 4);  // the MFMA router's split counters
   L.qkv_cnt = take(kMaxQkvGroups * 4);
   L.logits = take(b * E * 4);
@@ -427,7 +427,9 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   // fill the grid at most once (at 32 rows the four-expert tasks were as fast).
   const int rtiles = ((p.b + 15) / 16) * ((p.E + 15) / 16);
   p.router_mma = (st.router && p.router_multi && p.b >= 64) ? 1 : 0;
-  if (p.router_mma && !p.w4a4 && p.n_qkv == 0) {
+  // Beyond 64 rows the wide projections' tasks take one 64-row block each.
+  p.row_blocks = p.b > 64 ? (p.b + 63) / 64 : 1;
+  if ((p.router_mma || p.row_blocks > 1) && !p.w4a4 && p.n_qkv == 0) {
     // The plain kernel's many-rows instance, with its own occupancy.
     const int occ_m = block_occupancy(lds, false, false, true);
     if (occ_m < 1) return none;
@@ -450,9 +452,14 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   // The pooler: wide tiles of 64 features, split along H so that the router,
   // route and pooler tasks fill the workgroups about once (at least half of
   // them for the pooler), each split a multiple of 32 elements.
+  // Beyond 64 rows the tasks take one 64-row block each (the blocks of a
+  // tile and split on one XCD), split so that they fill the whole grid in
+  // about one and a half rounds: the pooler is then most of the front.
+  auto round8 = [](int v) { return (v + 7) / 8 * 8; };
   {
     const int groups = (p.P + 63) / 64;
-    const int slots = std::max(grid - n_router - n_route - n_prenorm, grid / 2);
+    const int slots = p.row_blocks > 1 ? 3 * grid / 2 / p.row_blocks
+                                       : std::max(grid - n_router - n_route - n_prenorm, grid / 2);
     int ks = std::min(kMaxPoolSplit, std::max(1, slots / groups));
     while (ks > 1 && (p.H % ks != 0 || (p.H / ks) % 32 != 0)) --ks;
     p.pool_ks = ks;
@@ -469,7 +476,7 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   p.unpool_wide = (p.b > 16 || (p.P / 32 + narrow_ks - 1) / narrow_ks > kBlockWaves * kUnpoolChunks) ? 1 : 0;
   if (p.unpool_wide) {
     const int groups = (p.H + 63) / 64;
-    int ks = std::min(kMaxSplitK, std::max(1, grid / groups));
+    int ks = std::min(kMaxSplitK, std::max(1, (p.row_blocks > 1 ? 3 * grid / 2 / p.row_blocks : grid) / groups));
     while (ks > 1 && (p.P % ks != 0 || (p.P / ks) % 32 != 0)) --ks;
     p.unpool_ks = ks;
   } else {
@@ -482,12 +489,21 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   p.n_router = n_router;
   p.n_logit_producers = p.n_router;
   p.n_route = n_route;
-  p.n_pool = st.pool ? p.n_pool_tiles * p.pool_ks : 0;
+  p.n_pool = st.pool ? (p.row_blocks > 1 ? round8(p.n_pool_tiles * p.pool_ks) * p.row_blocks
+                                         : p.n_pool_tiles * p.pool_ks)
+                     : 0;
   p.n_prenorm = n_prenorm;
   p.h_tagged = st.pool ? 1 : 0;
   p.has_up = st.experts ? 1 : 0;
   p.n_fin = n_fin;
-  p.n_unpool = st.unpool ? (p.unpool_wide ? (p.H + 63) / 64 : p.H / (16 * kUnpoolTiles)) * p.unpool_ks : 0;
+  if (!st.unpool) {
+    p.n_unpool = 0;
+  } else if (p.unpool_wide) {
+    const int gq = ((p.H + 63) / 64) * p.unpool_ks;
+    p.n_unpool = p.row_blocks > 1 ? round8(gq) * p.row_blocks : gq;
+  } else {
+    p.n_unpool = p.H / (16 * kUnpoolTiles) * p.unpool_ks;
+  }
   p.n_boundary = n_boundary;
   MB_HIP(launch_block(p, grid, lds, s));
   *used = true;

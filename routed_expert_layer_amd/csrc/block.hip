@@ -966,23 +966,44 @@ __device__ __forceinline__ int *proj_flag(unsigned char *lds) {
 // as tagged words (when not NULL: two bf16 per word), else the fp32 partial
 // to part[q].  `wait` runs after the first weight requests, before the first
 // activation request.
+// Tasks of the wide projections beyond 64 rows: (tile, split) gq and 64-row
+// block rb, numbered so that the row blocks of one (tile, split) are eight
+// task numbers apart -- on workgroups of the same XCD (the grid is a
+// multiple of eight), whose L2 then serves their common weights.  The count
+// is rounded up to whole groups of eight: gq past the last is no task.
+__device__ __forceinline__ void row_block_task(int i, int row_blocks, int &gq, int &rb) {
+  const int hi = i / 8;
+  rb = hi % row_blocks;
+  gq = (hi / row_blocks) * 8 + i % 8;
+}
+
 constexpr int kWideRing = 8;
 constexpr int kWideCols = 16 * kWaves;
 // 16-byte activation pieces per thread and segment: the stage holds 64 rows
 // x 256, 32 x 512 or 16 x 1024 elements, 2048 pieces.
 constexpr int kWidePieces = 2048 / kThreads;
-template <bool kCoherentA, typename Wait>
+//
+// kRB (the kernel's many-rows instances): only rows t_begin .. t_end - 1
+// (one 64-row block of a task of its own), the weights read cached when
+// `cached` (other blocks' tasks read them too).  Without it, every row and
+// nontemporal weights, and none of that bookkeeping in the registers.
+template <bool kCoherentA, bool kRB = false, typename Wait>
 __device__ __forceinline__ void proj_wide(rsrc_t ra, const uint16_t *w, int rows, int n_out, int kdim, int gi, int q,
                                           int ks, float *part, uint16_t *out, uint32_t *out_t, uint32_t tag,
-                                          unsigned char *stage, Wait wait) {
+                                          unsigned char *stage, Wait wait, int t_begin = 0, int t_end = 0,
+                                          bool cached = false) {
   const int lane = (int)(tid() % MB_WAVE), wave = (int)(tid() / MB_WAVE), g = lane >> 4, r16 = lane & 15;
   const int kr = kdim / ks, k0 = q * kr, nch = kr / 32;
   const int f = gi * kWideCols + 16 * wave + r16;  // this lane's weight row
   const rsrc_t rw = make_rsrc(w);
   const uint32_t wrow = f < n_out ? (uint32_t)(((size_t)f * kdim + k0 + 8 * g) * 2) : kOob;
-  auto wload = [&](int c) { return ld_nt16(rw, (wrow != kOob && c < nch) ? wrow + (uint32_t)c * 64u : kOob); };
+  auto wload = [&](int c) {
+    const uint32_t o = (wrow != kOob && c < nch) ? wrow + (uint32_t)c * 64u : kOob;
+    return (kRB && cached) ? ld_b128(rw, o) : ld_nt16(rw, o);
+  };
+  const int tb = kRB ? t_begin : 0, te = kRB ? min(rows, t_end) : rows;
   const rsrc_t ro = make_rsrc(out), rp = make_rsrc(part), rt = make_rsrc(out_t);
-  for (int t0 = 0; t0 < rows; t0 += 64) {
+  for (int t0 = tb; t0 < te; t0 += 64) {
     const int rp_ = min(64, rows - t0), nb = (rp_ + 15) / 16;
     // Segment length (elements, a multiple of 32 kWideRing): rows x segment fits the stage.
     const int seg = min((rp_ <= 16 ? 1024 : rp_ <= 32 ? 512 : 256), ((kr + 255) / 256) * 256);
@@ -990,7 +1011,7 @@ __device__ __forceinline__ void proj_wide(rsrc_t ra, const uint16_t *w, int rows
     u32x4_t W[kWideRing];
 #pragma unroll
     for (int r = 0; r < kWideRing; ++r) W[r] = wload(r);
-    if (t0 == 0) wait();
+    if (t0 == tb) wait();
     f32x4_t acc[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1053,10 +1074,12 @@ __device__ __forceinline__ void proj_wide(rsrc_t ra, const uint16_t *w, int rows
 // in split order, for the tile's 64 features and every row; to `out` (when
 // not NULL) and as tagged words to out_t (when not NULL).
 __device__ __forceinline__ void proj_wide_sum(const float *part, uint16_t *out, uint32_t *out_t, uint32_t tag,
-                                              int rows, int n_out, int gi, int ks) {
+                                              int rows, int n_out, int gi, int ks, int t_begin = 0,
+                                              int t_end = 1 << 30) {
   const rsrc_t rp = make_rsrc(part), ro = make_rsrc(out), rt = make_rsrc(out_t);
-  for (int idx = (int)tid(); idx < rows * (kWideCols / 4); idx += kThreads) {
-    const int t = idx / (kWideCols / 4), n = gi * kWideCols + 4 * (idx % (kWideCols / 4));
+  const int tb = t_begin, te = min(rows, t_end);
+  for (int idx = (int)tid(); idx < (te - tb) * (kWideCols / 4); idx += kThreads) {
+    const int t = tb + idx / (kWideCols / 4), n = gi * kWideCols + 4 * (idx % (kWideCols / 4));
     if (n >= n_out) continue;
     f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int q0 = 0; q0 < ks; q0 += 8) {
@@ -2072,8 +2095,9 @@ __device__ __forceinline__ const BlockParams &kparams() {
 // kQ: the W4A4 variant (MXFP4 activations into the experts), a kernel of its
 // own so that each keeps its own code layout and registers.
 // kQKV: the next layer's QKV projection follows the boundary in the launch.
-// kMR: the fp64-MFMA router tiles (many rows) are compiled in; the plain
-// kernel has a many-rows instance of its own for them, the others take both.
+// kMR: the many-rows paths (the fp64-MFMA router tiles, the wide
+// projections' 64-row block tasks) are compiled in; the plain kernel has a
+// many-rows instance of its own for them, the others take both.
 template <bool kQ, bool kQKV = false, bool kMR = kQ || kQKV>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void block_kernel(BlockParams p_arg) {
   extern __shared__ __align__(16) unsigned char lds[];
@@ -2138,13 +2162,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         // Pooler: wide tiles, the splits added by the last to finish.  h
         // goes out as tagged words (the up units and the pre-norm poll them),
         // and in bf16 when asked for (the pre-norm writes that then).
-        const int i = j - lo, gi = i / p.pool_ks, q = i % p.pool_ks;
         uint16_t *hp = (p.h_plain && !p.pre_norm_w) ? p.h : nullptr;
-        proj_wide<false>(make_rsrc(p.x), p.pool_w, p.b, p.P, p.H, gi, q, p.pool_ks, p.pool_part, hp, p.h_t, d.tag(),
-                         scratch, []() {});
-        if (p.pool_ks > 1 && last_arrival(&p.pool_cnt[gi], (unsigned)p.pool_ks, proj_flag(scratch))) {
-          proj_wide_sum(p.pool_part, hp, p.h_t, d.tag(), p.b, p.P, gi, p.pool_ks);
-          if (tid() == 0) __hip_atomic_store(&p.pool_cnt[gi], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (kMR && p.row_blocks > 1) {
+          // Many rows: one 64-row block per task.
+          int gq, rb;
+          row_block_task(j - lo, p.row_blocks, gq, rb);
+          if (gq < p.n_pool_tiles * p.pool_ks) {
+            const int gi = gq / p.pool_ks, q = gq % p.pool_ks, t0 = rb * 64, t1 = t0 + 64;
+            proj_wide<false, true>(make_rsrc(p.x), p.pool_w, p.b, p.P, p.H, gi, q, p.pool_ks, p.pool_part, hp,
+                                   p.h_t, d.tag(), scratch, []() {}, t0, t1, true);
+            unsigned *cnt = &p.pool_cnt[gi * kMaxRowBlocks + rb];
+            if (p.pool_ks > 1 && last_arrival(cnt, (unsigned)p.pool_ks, proj_flag(scratch))) {
+              proj_wide_sum(p.pool_part, hp, p.h_t, d.tag(), p.b, p.P, gi, p.pool_ks, t0, t1);
+              if (tid() == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+        } else {
+          const int i = j - lo, gi = i / p.pool_ks, q = i % p.pool_ks;
+          proj_wide<false>(make_rsrc(p.x), p.pool_w, p.b, p.P, p.H, gi, q, p.pool_ks, p.pool_part, hp, p.h_t,
+                           d.tag(), scratch, []() {});
+          unsigned *cnt = &p.pool_cnt[gi * kMaxRowBlocks];
+          if (p.pool_ks > 1 && last_arrival(cnt, (unsigned)p.pool_ks, proj_flag(scratch))) {
+            proj_wide_sum(p.pool_part, hp, p.h_t, d.tag(), p.b, p.P, gi, p.pool_ks);
+            if (tid() == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
         __syncthreads();  // (the workgroup's next task reuses the LDS)
         stamp(p, 7);
@@ -2252,9 +2293,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         const uint16_t *mo =
             p.n_fin > 0 ? p.moe_rep + (size_t)(blockIdx.x % kMoeReplicas) * p.b * p.P : p.moe_out;
         if (p.unpool_wide) {
-          // Many rows: wide tiles, so each workgroup reads the MoE output once per 64 features.
-          proj_wide<true>(make_rsrc(mo), p.unpool_w, p.b, p.H, p.P, i / p.unpool_ks, i % p.unpool_ks, p.unpool_ks,
-                          p.unpool_part, p.u, nullptr, 0u, scratch, [&]() { wait_step(d, kCtrFin, p.n_fin); });
+          // Many rows: wide tiles, so each workgroup reads the MoE output once
+          // per 64 features (one 64-row block of it beyond 64 rows).
+          if (kMR && p.row_blocks > 1) {
+            int gq, rb;
+            row_block_task(i, p.row_blocks, gq, rb);
+            if (gq < ((p.H + 63) / 64) * p.unpool_ks)
+              proj_wide<true, true>(make_rsrc(mo), p.unpool_w, p.b, p.H, p.P, gq / p.unpool_ks, gq % p.unpool_ks,
+                                    p.unpool_ks, p.unpool_part, p.u, nullptr, 0u, scratch,
+                                    [&]() { wait_step(d, kCtrFin, p.n_fin); }, rb * 64, rb * 64 + 64, true);
+          } else {
+            proj_wide<true>(make_rsrc(mo), p.unpool_w, p.b, p.H, p.P, i / p.unpool_ks, i % p.unpool_ks, p.unpool_ks,
+                            p.unpool_part, p.u, nullptr, 0u, scratch, [&]() { wait_step(d, kCtrFin, p.n_fin); });
+          }
         } else {
           unpool_task(p, d, mo, i, scratch);
         }
@@ -2312,7 +2363,7 @@ int block_max_groups_per_cu_many(size_t lds) {
 hipError_t launch_block(const BlockParams &p, int grid, size_t lds, hipStream_t s) {
   if (p.w4a4) return launch_block_w4a4(p, grid, lds, s);
   if (p.n_qkv > 0) return launch_block_qkv(p, grid, lds, s);
-  if (p.router_mma) return launch_block_many(p, grid, lds, s);
+  if (p.router_mma || p.row_blocks > 1) return launch_block_many(p, grid, lds, s);
   hipLaunchKernelGGL(block_kernel<false>, dim3(grid), dim3(kThreads), lds, s, p);
   return hipGetLastError();
 }

@@ -86,6 +86,7 @@ constexpr int kUnpoolTiles = 2;
 constexpr int kUnpoolChunks = 12;
 constexpr int kFinChunk = 1024;  // features per finalize task (4 per thread: the most one task covers)
 constexpr int kMaxPoolSplit = 32;  // contraction splits of the pooler
+constexpr int kMaxRowBlocks = 16;  // 64-row blocks of the wide projections' tasks (kMaxRows / 64)
 constexpr int kMoeReplicas = 8;  // copies of the MoE output for the unpooler tasks
 constexpr int kTimelineSlots = 32;
 constexpr int kBlockGroupsPerCu = 3;  // resident workgroups per CU (one wave per SIMD each)
@@ -125,6 +126,7 @@ struct BlockParams {
   int pool_ks, unpool_ks, n_pool_tiles;
   int has_up, needs_routing, routing_out, route_given, logits_in;
   int unpool_wide;  // unpooler in 64-feature tiles (many rows)
+  int row_blocks;   // 64-row blocks of the pooler's and wide unpooler's tasks (1 up to 64 rows)
   int router_multi; // router tasks of kRouterExperts experts (many rows)
   int router_mma;   // router tiles of 16 rows x 16 experts on fp64 MFMA (many rows)
   int router_ks;    // their contraction splits (partials added by the last split)
