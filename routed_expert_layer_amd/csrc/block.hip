@@ -906,7 +906,7 @@ __device__ __forceinline__ void prepare_routing(const BlockParams &p, const Deps
   if (p.route_given) {
     // From the caller (mb_experts).
     for (int i = tid(); i < p.b * p.k; i += kThreads) {
-      R.ids[i] = p.ids[i];
+      R.ids[i] = (unsigned)p.ids[i] < (unsigned)p.E ? p.ids[i] : 0;  // (the caller's ids are below E)
       R.w[i] = p.wts[i];
       R.rl[i] = p.route_list[i];
     }

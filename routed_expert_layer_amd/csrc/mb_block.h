@@ -183,9 +183,9 @@ constexpr int kMaxQkvGroups = 1024;  // 64-feature tiles of the fused projection
 
 // Routing state each workgroup keeps in LDS.
 struct RouteLds {
-  int *ids;    // [b*k]
-  float *w;    // [b*k]
-  int *rl;     // [b*k] route list
+  uint8_t *ids;  // [b*k] (experts < 256)
+  float *w;      // [b*k]
+  uint16_t *rl;  // [b*k] route list (b*k < 65536)
   int *off;    // [E+1]
   int *act;    // [E]
   int *nact;   // [1]; nact[1] holds the launch's generation
@@ -197,19 +197,20 @@ __host__ __device__ inline size_t align16(size_t v) { return (v + 15) & ~(size_t
 
 __host__ __device__ inline size_t route_lds_bytes(int b, int k, int E) {
   const size_t R = (size_t)b * k, W = (size_t)(b + 63) / 64;
-  return align16(R * 4) * 3 + align16((E + 1) * 4) + align16(E * 4) + 16 + 32 + align16(E * W * 8);
+  return align16(R) + align16(R * 4) + align16(R * 2) + align16((E + 1) * 4) + align16(E * 4) + 16 + 32 +
+         align16(E * W * 8);
 }
 
 __device__ inline RouteLds route_lds(const BlockParams &p, unsigned char *base) {
   const size_t R = (size_t)p.b * p.k, W = (size_t)(p.b + 63) / 64;
   RouteLds r;
   size_t o = 0;
-  r.ids = reinterpret_cast<int *>(base + o);
-  o += align16(R * 4);
+  r.ids = base + o;
+  o += align16(R);
   r.w = reinterpret_cast<float *>(base + o);
   o += align16(R * 4);
-  r.rl = reinterpret_cast<int *>(base + o);
-  o += align16(R * 4);
+  r.rl = reinterpret_cast<uint16_t *>(base + o);
+  o += align16(R * 2);
   r.off = reinterpret_cast<int *>(base + o);
   o += align16((p.E + 1) * 4);
   r.act = reinterpret_cast<int *>(base + o);
