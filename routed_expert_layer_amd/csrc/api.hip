@@ -429,12 +429,17 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   p.router_mma = (st.router && p.router_multi && p.b >= 64) ? 1 : 0;
   // Beyond 64 rows the wide projections' tasks take one 64-row block each.
   p.row_blocks = p.b > 64 ? (p.b + 63) / 64 : 1;
-  if ((p.router_mma || p.row_blocks > 1) && !p.w4a4 && p.n_qkv == 0) {
+  const bool many = (p.router_mma || p.row_blocks > 1) && !p.w4a4 && p.n_qkv == 0;
+  if (many) {
     // The plain kernel's many-rows instance, with its own occupancy.
     const int occ_m = block_occupancy(lds, false, false, true);
     if (occ_m < 1) return none;
     if (occ_m < occ) grid = std::min(kMaxGrid, cus * std::min(occ_m, kBlockGroupsPerCu));
   }
+  // In it, the expert units stage plain h and act behind counters: at many
+  // rows every unit stages many rows, and tagged words would double the
+  // bytes it reads and add the tag checks.
+  p.plain_stage = (many && st.experts) ? 1 : 0;
   p.router_ks = 1;
   while (p.router_ks * 2 * rtiles <= grid && p.H % (p.router_ks * 2 * 32) == 0) p.router_ks *= 2;
   const int n_router =
@@ -494,6 +499,12 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
                      : 0;
   p.n_prenorm = n_prenorm;
   p.h_tagged = st.pool ? 1 : 0;
+  // Signals that make h complete under plain staging: every pooler tile (each
+  // 64-row block of it beyond 64 rows), or every pre-norm row, which then
+  // writes h in bf16 itself.
+  p.n_h_ready = !st.pool ? 0 : n_prenorm > 0 ? n_prenorm
+                                             : p.n_pool_tiles * (p.row_blocks > 1 ? p.row_blocks : 1);
+  if (p.plain_stage && n_prenorm > 0) p.h_plain = 1;
   p.has_up = st.experts ? 1 : 0;
   p.n_fin = n_fin;
   if (!st.unpool) {

@@ -1291,12 +1291,16 @@ __device__ __forceinline__ int pass_rows(int nrows) { return nrows <= 8 ? 8 : nr
 // ---- activation staging
 
 // Where the activation rows of a unit come from: a bf16 matrix, read
-// coherently (the caller wrote it), or the same matrix as tagged words (two
-// bf16 and the writer's tag per 8 bytes: the pooler's h, the up units' act),
-// polled until every word the unit reads carries this launch's tag.
+// coherently (the caller wrote it, or another workgroup did before counter
+// `ready` reached `target`: the workgroup waits for that once its weights
+// are requested), or the same matrix as tagged words (two bf16 and the
+// writer's tag per 8 bytes: the pooler's h, the up units' act), polled until
+// every word the unit reads carries this launch's tag.
 struct ActSrc {
   rsrc_t r;
   bool tagged;
+  const unsigned *ready = nullptr;
+  unsigned target = 0;
 };
 
 // One batch of staging loads in flight: kStagePieces pieces of 8 elements
@@ -1465,6 +1469,7 @@ __device__ __forceinline__ void mx_pair(const Deps &d, const MxTiles &T, int nch
     S1[q] = scales(so1, 4 * q);
   }
   if (!early) {
+    if (A.ready) wait_ge(d, A.ready, A.target);
     stage_issue(A, row_e, pr, 0, segn_first, ppr_first, 0, first[0]);
     if (need1) stage_issue(A, row_e, pr, 0, segn_first, ppr_first, kStagePieces, first[1]);
   }
@@ -1563,6 +1568,7 @@ __device__ __forceinline__ void mx_pair_all(const Deps &d, const MxTiles &T, int
   }
   const int srow = kAll * 256 + 16;  // row stride in the stage
   d0[0] = d1[0] = d0[1] = d1[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (A.ready) wait_ge(d, A.ready, A.target);
   // Chunks past nch are staged as zeros; a batch only if it holds one of the
   // pass's vrows rows.
   constexpr int ppr = kAll * 16;  // 16-byte pieces per row
@@ -1772,8 +1778,11 @@ __device__ __forceinline__ void mxq_pair_all(const Deps &d, const MxTiles &T, in
 // gate rows i0..i0+15 and up rows I+i0..I+i0+15 of the expert, over P, for
 // the expert's routes in passes of pass_rows.  h: the pooler's (or the
 // pre-norm's) tagged words of this launch, or the caller's bf16 matrix.  act
-// goes out as tagged words, and in bf16 to act_tap when asked for.
-template <bool kPacked, bool kQ>
+// goes out as tagged words, and in bf16 to act_tap when asked for.  kPS with
+// plain staging (the many-rows instance): h and act in bf16 (the units
+// phase waited for h), each round of units signalled on the expert's up
+// counter.
+template <bool kPacked, bool kQ, bool kPS = false>
 __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, const RouteLds &R, int unit,
                                         unsigned char *stage) {
   const int lane = tid() % MB_WAVE, g = lane >> 4, r16 = lane & 15;
@@ -1787,8 +1796,11 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
       kPacked ? mx_packed(p.xp + (size_t)e * p.xp_stride, p.xp + (size_t)e * p.xp_stride + p.xp_up_s, tile, P, lane)
            : mx_plain(p.w13 + (size_t)e * 2 * I * (P / 2), p.w13s + (size_t)e * 2 * I * (P / 32), i0, I + i0, P,
                       lane);
-  const ActSrc A{p.h_tagged ? make_rsrc(p.pre_norm_w ? p.hn_t : p.h_t) : make_rsrc(p.h), p.h_tagged != 0};
-  const rsrc_t rat = make_rsrc(p.act_t), rap = make_rsrc(p.act_tap);
+  // (Plain staging: h is complete -- the units phase waited for it.)
+  const bool plain = kPS && p.plain_stage;
+  const ActSrc A{(p.h_tagged && !plain) ? make_rsrc(p.pre_norm_w ? p.hn_t : p.h_t) : make_rsrc(p.h),
+                 p.h_tagged != 0 && !plain};
+  const rsrc_t rat = make_rsrc(p.act_t), rap = make_rsrc(p.act_tap), rpl = make_rsrc(p.act);
   const uint32_t tag = d.tag();
   const int nch = P / 128;
   const int pr = pass_rows(nrows);
@@ -1812,17 +1824,20 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
         }
         const uint32_t lo = pack_bf16x2(o[0], o[1]), hi = pack_bf16x2(o[2], o[3]);
         const size_t el = (size_t)(row0 + m) * I + i0 + 4 * g;
-        st_co16(rat, (uint32_t)(el * 4), u32x4_t{lo, tag, hi, tag});
+        if (plain) st_co8(rpl, (uint32_t)(el * 2), u32x2_t{lo, hi});
+        else st_co16(rat, (uint32_t)(el * 4), u32x4_t{lo, tag, hi, tag});
         if (p.act_tap) st_co8(rap, (uint32_t)(el * 2), u32x2_t{lo, hi});
       }
     }
   }
+  if (plain) signal_units(d.up(e));
 }
 
 // Down unit: w2 for (active expert, 32 output features): y in route order and
 // the route's sum of squares over these 32 features, from the up units'
-// tagged act (the staging polls it).
-template <bool kPacked, bool kQ>
+// tagged act (the staging polls it), or under plain staging from their bf16
+// act once the expert's up counter is complete.
+template <bool kPacked, bool kQ, bool kPS = false>
 __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, const RouteLds &R, int unit,
                                           unsigned char *stage) {
   const int lane = tid() % MB_WAVE, g = lane >> 4, r16 = lane & 15;
@@ -1836,7 +1851,10 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
       kPacked ? mx_packed(p.xp + (size_t)e * p.xp_stride + p.xp_down, p.xp + (size_t)e * p.xp_stride + p.xp_down_s,
                        tile, I, lane)
            : mx_plain(p.w2 + (size_t)e * P * (I / 2), p.w2s + (size_t)e * P * (I / 32), p0, p0 + 16, I, lane);
-  const ActSrc A{make_rsrc(p.act_t), true};
+  // Plain staging: act once the expert's up units (I / 16, four per
+  // signal) signalled.
+  const ActSrc A = (kPS && p.plain_stage) ? ActSrc{make_rsrc(p.act), false, d.up(e), (unsigned)(I / 16)}
+                                          : ActSrc{make_rsrc(p.act_t), true};
   const rsrc_t ry = make_rsrc(p.y), rss = make_rsrc(p.ssq);
   const int nch = I / 128;
   const int pr = pass_rows(nrows);
@@ -2100,6 +2118,8 @@ __device__ __forceinline__ const BlockParams &kparams() {
 // many-rows instance of its own for them, the others take both.
 template <bool kQ, bool kQKV = false, bool kMR = kQ || kQKV>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void block_kernel(BlockParams p_arg) {
+  // Plain staging of the expert units' activations: the many-rows instance.
+  constexpr bool kPS = kMR && !kQ && !kQKV;
   extern __shared__ __align__(16) unsigned char lds[];
   (void)p_arg;  // read through kparams()
   stamps_begin(kparams());
@@ -2163,6 +2183,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         // goes out as tagged words (the up units and the pre-norm poll them),
         // and in bf16 when asked for (the pre-norm writes that then).
         uint16_t *hp = (p.h_plain && !p.pre_norm_w) ? p.h : nullptr;
+        uint32_t *ht = p.h_t;
+        // Plain staging without a pre-norm: h only in bf16, each finished
+        // tile (64-row block) signalled.
+        const bool h_signal = kPS && p.plain_stage && !p.pre_norm_w;
+        if (h_signal) {
+          hp = p.h;
+          ht = nullptr;
+        }
         if (kMR && p.row_blocks > 1) {
           // Many rows: one 64-row block per task.
           int gq, rb;
@@ -2170,21 +2198,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
           if (gq < p.n_pool_tiles * p.pool_ks) {
             const int gi = gq / p.pool_ks, q = gq % p.pool_ks, t0 = rb * 64, t1 = t0 + 64;
             proj_wide<false, true>(make_rsrc(p.x), p.pool_w, p.b, p.P, p.H, gi, q, p.pool_ks, p.pool_part, hp,
-                                   p.h_t, d.tag(), scratch, []() {}, t0, t1, true);
+                                   ht, d.tag(), scratch, []() {}, t0, t1, true);
             unsigned *cnt = &p.pool_cnt[gi * kMaxRowBlocks + rb];
-            if (p.pool_ks > 1 && last_arrival(cnt, (unsigned)p.pool_ks, proj_flag(scratch))) {
-              proj_wide_sum(p.pool_part, hp, p.h_t, d.tag(), p.b, p.P, gi, p.pool_ks, t0, t1);
+            if (p.pool_ks == 1) {
+              if (h_signal) signal_step(d, kCtrPool);
+            } else if (last_arrival(cnt, (unsigned)p.pool_ks, proj_flag(scratch))) {
+              proj_wide_sum(p.pool_part, hp, ht, d.tag(), p.b, p.P, gi, p.pool_ks, t0, t1);
               if (tid() == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              if (h_signal) signal_step(d, kCtrPool);
             }
           }
         } else {
           const int i = j - lo, gi = i / p.pool_ks, q = i % p.pool_ks;
-          proj_wide<false>(make_rsrc(p.x), p.pool_w, p.b, p.P, p.H, gi, q, p.pool_ks, p.pool_part, hp, p.h_t,
+          proj_wide<false>(make_rsrc(p.x), p.pool_w, p.b, p.P, p.H, gi, q, p.pool_ks, p.pool_part, hp, ht,
                            d.tag(), scratch, []() {});
           unsigned *cnt = &p.pool_cnt[gi * kMaxRowBlocks];
-          if (p.pool_ks > 1 && last_arrival(cnt, (unsigned)p.pool_ks, proj_flag(scratch))) {
-            proj_wide_sum(p.pool_part, hp, p.h_t, d.tag(), p.b, p.P, gi, p.pool_ks);
+          if (p.pool_ks == 1) {
+            if (h_signal) signal_step(d, kCtrPool);
+          } else if (last_arrival(cnt, (unsigned)p.pool_ks, proj_flag(scratch))) {
+            proj_wide_sum(p.pool_part, hp, ht, d.tag(), p.b, p.P, gi, p.pool_ks);
             if (tid() == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (h_signal) signal_step(d, kCtrPool);
           }
         }
         __syncthreads();  // (the workgroup's next task reuses the LDS)
@@ -2199,6 +2233,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         if (first) stamp(p, 4);
         first = false;
         prenorm_task(p, Deps{p.sync, gen}, j - lo, lds + p.lds_route_bytes);
+        if (kPS && p.plain_stage) signal_step(Deps{p.sync, gen}, kCtrPrenorm);  // (its h row in bf16)
       }
     }
   }
@@ -2244,18 +2279,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const int gw = blockIdx.x * kWaves + uniform(tid() / MB_WAVE);
     // (The expert layout and the activation format are template arguments:
     // each has its own registers.)
+    // Plain staging: h complete before the workgroup's first up unit.
+    if (kPS && p.plain_stage && (int)blockIdx.x * kWaves < nU)
+      wait_step(d, p.pre_norm_w ? kCtrPrenorm : kCtrPool, p.n_h_ready);
     if constexpr (kQ) {
       for (int u = gw; u < nU; u += GW) up_unit<true, true>(p, d, R, u, stage);
       stamp(p, 20);
       for (int u = gw; u < nD; u += GW) down_unit<true, true>(p, d, R, u, stage);
     } else if (p.xp) {
-      for (int u = gw; u < nU; u += GW) up_unit<true, false>(p, d, R, u, stage);
+      for (int u = gw; u < nU; u += GW) up_unit<true, false, kPS>(p, d, R, u, stage);
       stamp(p, 20);
-      for (int u = gw; u < nD; u += GW) down_unit<true, false>(p, d, R, u, stage);
+      for (int u = gw; u < nD; u += GW) down_unit<true, false, kPS>(p, d, R, u, stage);
     } else {
-      for (int u = gw; u < nU; u += GW) up_unit<false, false>(p, d, R, u, stage);
+      for (int u = gw; u < nU; u += GW) up_unit<false, false, kPS>(p, d, R, u, stage);
       stamp(p, 20);
-      for (int u = gw; u < nD; u += GW) down_unit<false, false>(p, d, R, u, stage);
+      for (int u = gw; u < nD; u += GW) down_unit<false, false, kPS>(p, d, R, u, stage);
     }
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();

@@ -178,6 +178,12 @@ struct BlockParams {
   uint32_t *h_t, *hn_t, *act_t;
   uint16_t *act_tap;
   int h_tagged, h_plain;
+  // Plain staging (the many-rows instance only): the expert units stage h
+  // and act as plain bf16 (h, act) behind counters instead of polling tagged
+  // words -- h once every pooler tile (or pre-norm row) signalled its step
+  // counter (n_h_ready signals), act once the expert's up units signalled
+  // its up counter.
+  int plain_stage, n_h_ready;
 };
 constexpr int kMaxQkvGroups = 1024;  // 64-feature tiles of the fused projection (qkv_rows <= 65536)
 

@@ -86,6 +86,16 @@ def test_shape_edges(case):
     run_and_check(synth.make_block("c0", seed=7, dims=d), f"edge {case}")
 
 
+@pytest.mark.parametrize("case", [dict(rows=65), dict(rows=256),
+                                  dict(rows=64, experts=64, hidden=512, top_k=4)])
+def test_many_rows_with_norm_weights(case):
+    """The block kernel's many-rows instance (beyond 64 rows, or the fp64-MFMA
+    router from 64), where the expert units stage plain h and act behind
+    counters; with every norm weight, so the pre-norm rows make h."""
+    d = small(**case)
+    run_and_check(synth.make_block("c0", seed=80 + case["rows"], dims=d, norm_weights=True), f"many rows+norms {case}")
+
+
 @pytest.mark.parametrize("rows", [13, 70])
 def test_per_step_kernels_with_norm_weights(rows):
     """More experts than the block kernel takes (300 > 256): mb_moe_block runs
