@@ -1004,9 +1004,11 @@ __device__ __forceinline__ void proj_wide(rsrc_t ra, const uint16_t *w, int rows
   const int tb = kRB ? t_begin : 0, te = kRB ? min(rows, t_end) : rows;
   const rsrc_t ro = make_rsrc(out), rp = make_rsrc(part), rt = make_rsrc(out_t);
   for (int t0 = tb; t0 < te; t0 += 64) {
-    const int rp_ = min(64, rows - t0), nb = (rp_ + 15) / 16;
+    // (kRB: always four 16-row blocks -- rows past the end are staged as
+    // zeros and not stored -- so the products have no branches.)
+    const int rp_ = min(64, rows - t0), nb = kRB ? 4 : (rp_ + 15) / 16;
     // Segment length (elements, a multiple of 32 kWideRing): rows x segment fits the stage.
-    const int seg = min((rp_ <= 16 ? 1024 : rp_ <= 32 ? 512 : 256), ((kr + 255) / 256) * 256);
+    const int seg = kRB ? 256 : min((rp_ <= 16 ? 1024 : rp_ <= 32 ? 512 : 256), ((kr + 255) / 256) * 256);
     const int srow = seg * 2 + 16;
     u32x4_t W[kWideRing];
 #pragma unroll
@@ -1044,11 +1046,20 @@ __device__ __forceinline__ void proj_wide(rsrc_t ra, const uint16_t *w, int rows
 #pragma unroll
         for (int r = 0; r < kWideRing; ++r) {
           const unsigned char *bp = stage + r16 * srow + ((c0 + r - s0) * 32 + 8 * g) * 2;
+          if constexpr (kRB) {
+            // The four blocks' operands read together, then the products.
+            u32x4_t B[4];
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
-            if (b < nb)
-              acc[b] = mfma_bf16(as_bf16x8(W[r]), as_bf16x8(*reinterpret_cast<const u32x4_t *>(bp + 16 * b * srow)),
-                                 acc[b]);
+            for (int b = 0; b < 4; ++b) B[b] = *reinterpret_cast<const u32x4_t *>(bp + 16 * b * srow);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[b] = mfma_bf16(as_bf16x8(W[r]), as_bf16x8(B[b]), acc[b]);
+          } else {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+              if (b < nb)
+                acc[b] = mfma_bf16(as_bf16x8(W[r]),
+                                   as_bf16x8(*reinterpret_cast<const u32x4_t *>(bp + 16 * b * srow)), acc[b]);
+          }
           W[r] = wload(c0 + kWideRing + r);
         }
       }
