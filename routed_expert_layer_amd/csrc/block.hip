@@ -830,8 +830,14 @@ __device__ __forceinline__ void mark_route(const BlockParams &p, const RouteLds 
   atomicOr(&R.bits[e * W + t / 64], 1ull << (t & 63));
 }
 
-// (Expects every route marked, and a barrier since.)
-__device__ __forceinline__ void group_routes(const BlockParams &p, const RouteLds &R, bool out) {
+// (Expects every route marked, and a barrier since.)  by_count: the
+// workgroup's own list of active experts (R.act) in ascending order of
+// their route counts, ties by id (the routing outputs keep id order), so
+// that each round of expert units -- dealt to the waves in list order --
+// holds experts of about one size on every workgroup.  (The smallest first
+// measured faster than the largest first.)
+__device__ __forceinline__ void group_routes(const BlockParams &p, const RouteLds &R, bool out,
+                                             bool by_count = false) {
   const int W = (p.b + 63) / 64;
   const int Rn = p.b * p.k;
   const int e0 = tid() * 4;
@@ -886,6 +892,22 @@ __device__ __forceinline__ void group_routes(const BlockParams &p, const RouteLd
     if (out) p.route_list[R.off[e] + rank] = r;
   }
   __syncthreads();
+  if (by_count) {
+    static_assert(kBlockMaxExperts <= kThreads, "one active expert per thread");
+    const int na = tot_a, a = tid();
+    int e = -1, rk = 0;
+    if (a < na) {
+      e = R.act[a];
+      const int c = R.off[e + 1] - R.off[e];
+      for (int a2 = 0; a2 < na; ++a2) {
+        const int e2 = R.act[a2], c2 = R.off[e2 + 1] - R.off[e2];
+        rk += (c2 < c || (c2 == c && e2 < e)) ? 1 : 0;
+      }
+    }
+    __syncthreads();
+    if (e >= 0) R.act[rk] = e;
+    __syncthreads();
+  }
 }
 
 // Route task: rows 4 task .. +3, one per wave.
@@ -901,7 +923,8 @@ constexpr int kRouteBatch = 2;
 // The routing state a workgroup needs before its first expert unit: the
 // routes (from the caller, or polled from this workgroup's copy of the tagged
 // routes), then the grouping.
-__device__ __forceinline__ void prepare_routing(const BlockParams &p, const Deps &d, const RouteLds &R) {
+__device__ __forceinline__ void prepare_routing(const BlockParams &p, const Deps &d, const RouteLds &R,
+                                                bool by_count = false) {
   const bool out = p.routing_out && blockIdx.x == 0;
   if (p.route_given) {
     // From the caller (mb_experts).
@@ -944,7 +967,7 @@ __device__ __forceinline__ void prepare_routing(const BlockParams &p, const Deps
     }
   }
   __syncthreads();
-  group_routes(p, R, out);
+  group_routes(p, R, out, by_count);
 }
 
 // ---------------------------------------------------------------- projections
@@ -2263,7 +2286,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const Deps d{p.sync, launch_gen()};
   const RouteLds R = route_lds(p, lds);
   if (p.needs_routing && (p.has_up || (p.routing_out && blockIdx.x == 0))) {
-    prepare_routing(p, d, R);
+    prepare_routing(p, d, R, kPS);
     stamp(p, 5);
   }
   }
