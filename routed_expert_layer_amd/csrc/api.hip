@@ -399,6 +399,27 @@ struct Steps {
   bool route_given = false;  // routing arrays come from the caller
 };
 
+// Contraction split of a wide projection's tasks beyond 64 rows (64-feature
+// tiles x 64-row blocks, the count rounded up to whole groups of eight, dealt
+// to the workgroups in turn): each task streams its split in segments of 256
+// elements, so the phase takes about (rounds of tasks over the grid) x
+// (segments per task); the split with the fewest, then the fewest splits.
+// Each split is a multiple of 32 elements.
+int row_block_split(int groups, int kdim, int row_blocks, int grid, int max_ks) {
+  int best = 1;
+  long best_cost = -1;
+  for (int ks = 1; ks <= max_ks; ++ks) {
+    if (kdim % ks != 0 || (kdim / ks) % 32 != 0) continue;
+    const long tasks = (long)((groups * ks + 7) / 8 * 8) * row_blocks;
+    const long cost = (tasks + grid - 1) / grid * ((kdim / ks + 255) / 256);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = ks;
+    }
+  }
+  return best;
+}
+
 // Launch the persistent kernel for `st`.  *used = false (and nothing
 // launched) when the sizes do not fit it; the caller then runs the per-step
 // kernels instead.
@@ -458,15 +479,19 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   // route and pooler tasks fill the workgroups about once (at least half of
   // them for the pooler), each split a multiple of 32 elements.
   // Beyond 64 rows the tasks take one 64-row block each (the blocks of a
-  // tile and split on one XCD), split so that they fill the whole grid in
-  // about one and a half rounds: the pooler is then most of the front.
+  // tile and split on one XCD), split by row_block_split: the pooler is then
+  // most of the front.
   auto round8 = [](int v) { return (v + 7) / 8 * 8; };
   {
     const int groups = (p.P + 63) / 64;
-    const int slots = p.row_blocks > 1 ? 3 * grid / 2 / p.row_blocks
-                                       : std::max(grid - n_router - n_route - n_prenorm, grid / 2);
-    int ks = std::min(kMaxPoolSplit, std::max(1, slots / groups));
-    while (ks > 1 && (p.H % ks != 0 || (p.H / ks) % 32 != 0)) --ks;
+    int ks;
+    if (p.row_blocks > 1) {
+      ks = row_block_split(groups, p.H, p.row_blocks, grid, kMaxPoolSplit);
+    } else {
+      const int slots = std::max(grid - n_router - n_route - n_prenorm, grid / 2);
+      ks = std::min(kMaxPoolSplit, std::max(1, slots / groups));
+      while (ks > 1 && (p.H % ks != 0 || (p.H / ks) % 32 != 0)) --ks;
+    }
     p.pool_ks = ks;
   }
   // The unpooler: at few rows, tasks of kUnpoolTiles 16-feature tiles over
@@ -481,8 +506,13 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   p.unpool_wide = (p.b > 16 || (p.P / 32 + narrow_ks - 1) / narrow_ks > kBlockWaves * kUnpoolChunks) ? 1 : 0;
   if (p.unpool_wide) {
     const int groups = (p.H + 63) / 64;
-    int ks = std::min(kMaxSplitK, std::max(1, (p.row_blocks > 1 ? 3 * grid / 2 / p.row_blocks : grid) / groups));
-    while (ks > 1 && (p.P % ks != 0 || (p.P / ks) % 32 != 0)) --ks;
+    int ks;
+    if (p.row_blocks > 1) {
+      ks = row_block_split(groups, p.P, p.row_blocks, grid, kMaxSplitK);
+    } else {
+      ks = std::min(kMaxSplitK, std::max(1, grid / groups));
+      while (ks > 1 && (p.P % ks != 0 || (p.P / ks) % 32 != 0)) --ks;
+    }
     p.unpool_ks = ks;
   } else {
     p.unpool_ks = narrow_ks;
