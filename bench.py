@@ -174,6 +174,7 @@ def timeline(launches: int, c3_rows: int = 0) -> int:
     weights = [rel.make_weights(**t) for t in tensors]
     for t, w in zip(tensors, weights):
         t["experts_packed"] = rel.pack_experts(dims, w, dev)
+        t["proj_packed"] = rel.pack_projections(dims, w, dev)
     weights = [rel.make_weights(**t) for t in tensors]
     ws = rel.workspace(dims, dev)
     xn = torch.zeros((d.rows, d.hidden), dtype=torch.bfloat16, device=dev)
@@ -359,6 +360,7 @@ def sweep(args) -> int:
         if args.layout == "packed":
             for t, w in zip(tensors, weights):
                 t["experts_packed"] = rel.pack_experts(dims, w, dev)
+                t["proj_packed"] = rel.pack_projections(dims, w, dev)
             weights = [rel.make_weights(**t) for t in tensors]
         torch.cuda.synchronize()
         return dims, tensors, weights
@@ -454,8 +456,8 @@ def sweep(args) -> int:
 
     # c4: the 60-layer stack, 60 distinct layer weight sets (about 54 GB of
     # experts in HBM), x_next of each layer feeding the next.  Layers are
-    # drawn in threads and uploaded one by one (their caller-layout experts
-    # dropped once packed).
+    # drawn in threads and uploaded one by one (their caller-layout experts,
+    # pooler and unpooler weights dropped once packed).
     from concurrent.futures import ThreadPoolExecutor
 
     n_layers = synth.inputs.C4_LAYERS
@@ -472,7 +474,7 @@ def sweep(args) -> int:
             d = blk.dims
             dims_l, tensors, ws_l = prepare([blk])
             if args.layout == "packed":
-                for n in ("w13", "w13_scale", "w2", "w2_scale"):
+                for n in ("w13", "w13_scale", "w2", "w2_scale", "pool_w", "unpool_w"):
                     tensors[0].pop(n, None)
                 ws_l = [rel.make_weights(**tensors[0])]
             if dims is None:
@@ -508,8 +510,9 @@ def main() -> int:
                     help="first run one plain elementwise copy of MB MiB (reads and writes MB MiB), "
                          "the reference kernel for scaling the HBM byte counters")
     ap.add_argument("--layout", choices=("packed", "caller"), default="packed",
-                    help="expert weights streamed from mb_pack_experts' layout (prepared once per "
-                         "weight set, outside the timed region) or from the caller's layout")
+                    help="expert, pooler and unpooler weights streamed from mb_pack_experts' and "
+                         "mb_pack_projections' layouts (prepared once per weight set, outside the timed "
+                         "region) or from the caller's layout")
     ap.add_argument("--act-quant", action="store_true",
                     help="the W4A4 variant: the experts' activations quantized to MXFP4 (needs the "
                          "packed layout); not the headline line")
@@ -570,9 +573,11 @@ def main() -> int:
     weights = [rel.make_weights(**t) for t in tensors]
     dims = rel.make_dims(**dims_kwargs(d), act_quant=int(args.act_quant))
     if args.layout == "packed":
-        # Load-time preparation: the experts also in the streaming layout.
+        # Load-time preparation: the experts, the pooler's and the unpooler's
+        # weights also in the streaming layouts.
         for t, w in zip(tensors, weights):
             t["experts_packed"] = rel.pack_experts(dims, w, dev)
+            t["proj_packed"] = rel.pack_projections(dims, w, dev)
         weights = [rel.make_weights(**t) for t in tensors]
         torch.cuda.synchronize()
     ws = rel.workspace(dims, dev)

@@ -137,6 +137,10 @@ typedef struct {
  *               streams.  When set, w13, w13_scale, w2 and w2_scale may be
  *               NULL; the per-step kernels (sizes the block kernel does not
  *               take) need them and return MB_ERR_UNSUPPORTED without them.
+ *   proj_packed NULL, or the output of mb_pack_projections for these pool_w /
+ *               unpool_w: both in the layout the block kernel streams.  When
+ *               set, pool_w and unpool_w may be NULL (the per-step kernels
+ *               then return MB_ERR_UNSUPPORTED, as for experts_packed).
  * Norm weights are the effective bf16 multipliers ([mono.decoder]
  * effective_norm_weight), applied after normalising. */
 typedef struct {
@@ -155,6 +159,7 @@ typedef struct {
   const uint16_t *next_norm_w;
   const uint8_t *experts_packed;
   const uint16_t *next_qkv_w;  /* bf16 [dims->qkv_rows, H] or NULL (qkv_rows 0) */
+  const uint8_t *proj_packed;
 } mb_weights;
 
 /* Optional intermediate outputs of mb_moe_block.  A NULL member is kept in
@@ -298,6 +303,27 @@ int mb_packed_experts_bytes(const mb_dims *dims, size_t *bytes);
  * too small. */
 int mb_pack_experts(const mb_dims *dims, const mb_weights *w, uint8_t *packed, size_t packed_bytes,
                     void *stream);
+
+/* Bytes of the streaming layout of the pooler's and unpooler's weights (for
+ * mb_pack_projections). */
+int mb_packed_projections_bytes(const mb_dims *dims, size_t *bytes);
+
+/* Copy the bf16 pooler and unpooler weights (pool_w [P, H] and unpool_w
+ * [H, P] of `w`, both required) into `packed` (device memory, at least
+ * mb_packed_projections_bytes, 16-byte aligned) in the layout the block
+ * kernel streams: per matrix of n_out rows of kdim elements, per 16-row tile t
+ * (rows past n_out zero) and 32-element chunk c, the kilobyte one wave loads,
+ * lane l's 16 bytes at 16 l holding elements 32 c + 8 (l / 16) .. + 7 of row
+ * 16 t + l % 16, at byte (t * kdim / 32 + c) * 1024; pool_w's matrix first,
+ * unpool_w's from byte ceil(ceil(P / 16) * 16 * H * 2 / 256) * 256.  (Sixteen
+ * rows' 64-byte pieces per wave load, as the caller's row-major layout gives,
+ * come at a fraction of the rate of contiguous loads.)  The values are
+ * unchanged, so results are bit-identical to the caller's layout.  Load-time
+ * preparation, as for mb_pack_experts ([muse_moe_runner] MuseSparkAiterExperts
+ * takes its weights prepared at load time); the caller owns `packed`.
+ * Asynchronous on `stream`.  MB_ERR_WORKSPACE if packed_bytes is too small. */
+int mb_pack_projections(const mb_dims *dims, const mb_weights *w, uint8_t *packed, size_t packed_bytes,
+                        void *stream);
 
 /* The attention boundary, the step before the block ([providers]
  * AttentionBoundaryProvider: post_attn_norm, the gated add into the fp32

@@ -31,6 +31,8 @@ EXPORTS = (
     "mb_moe_block_noalloc",
     "mb_packed_experts_bytes",
     "mb_pack_experts",
+    "mb_packed_projections_bytes",
+    "mb_pack_projections",
     "mb_attn_boundary",
     "mb_next_qkv",
     "mb_effective_norm_weight",
@@ -57,7 +59,7 @@ class Dims(ctypes.Structure):
 
 _WEIGHT_FIELDS = ("router_w", "expert_bias", "pool_w", "pre_norm_w", "w13", "w13_scale", "w2",
                   "w2_scale", "post_norm_w", "unpool_w", "ffn_norm_w", "gate", "next_norm_w",
-                  "experts_packed", "next_qkv_w")
+                  "experts_packed", "next_qkv_w", "proj_packed")
 _TAP_FIELDS = ("logits", "topk_ids", "topk_w", "count", "offset", "route_list", "active",
                "n_active", "h", "moe_out", "u", "timeline", "act", "qkvg")
 
@@ -100,6 +102,8 @@ def lib() -> ctypes.CDLL:
         L.mb_moe_block_noalloc.argtypes = [P(Dims), _vp, P(Weights), _vp, _vp, P(Taps), _vp]
         L.mb_packed_experts_bytes.argtypes = [P(Dims), P(ctypes.c_size_t)]
         L.mb_pack_experts.argtypes = [P(Dims), P(Weights), _vp, ctypes.c_size_t, _vp]
+        L.mb_packed_projections_bytes.argtypes = [P(Dims), P(ctypes.c_size_t)]
+        L.mb_pack_projections.argtypes = [P(Dims), P(Weights), _vp, ctypes.c_size_t, _vp]
         L.mb_attn_boundary.argtypes = [P(Dims), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.mb_next_qkv.argtypes = [P(Dims), _vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_size_t, _vp]
         L.mb_effective_norm_weight.argtypes = [_vp, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, _vp, _vp]
@@ -193,6 +197,28 @@ def pack_experts(dims: Dims, weights: Weights, device="cuda") -> torch.Tensor:
     layout (set it as the experts_packed weight; keep it alive with them)."""
     packed = torch.empty(mb_packed_experts_bytes(dims), dtype=torch.uint8, device=device)
     mb_pack_experts(dims, weights, packed)
+    return packed
+
+
+def mb_packed_projections_bytes(dims: Dims) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().mb_packed_projections_bytes(ctypes.byref(dims), ctypes.byref(n)),
+           "mb_packed_projections_bytes")
+    return int(n.value)
+
+
+def mb_pack_projections(dims: Dims, weights: Weights, packed: torch.Tensor) -> None:
+    _check(lib().mb_pack_projections(ctypes.byref(dims), ctypes.byref(weights), _p(packed),
+                                     packed.numel() * packed.element_size(), _stream()),
+           "mb_pack_projections")
+
+
+def pack_projections(dims: Dims, weights: Weights, device="cuda") -> torch.Tensor:
+    """A new device buffer holding the pooler's and unpooler's weights of
+    `weights` in the streaming layout (set it as the proj_packed weight; keep
+    it alive with them)."""
+    packed = torch.empty(mb_packed_projections_bytes(dims), dtype=torch.uint8, device=device)
+    mb_pack_projections(dims, weights, packed)
     return packed
 
 

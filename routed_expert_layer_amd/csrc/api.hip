@@ -217,16 +217,19 @@ int check_weights_experts(const mb_weights *w) {
 
 bool has_plain_experts(const mb_weights *w) { return w->w13 && w->w13_scale && w->w2 && w->w2_scale; }
 
+// (With proj_packed, pool_w and unpool_w may be NULL: the block kernel reads
+// the packed copy, the per-step kernels need the caller's.)
 int check_weights_boundary(const mb_weights *w) {
   if (!w) return MB_ERR_NULL;
-  MB_TRY(need({w->unpool_w, w->gate}));
-  return maybe({w->ffn_norm_w, w->next_norm_w});
+  MB_TRY(need({w->gate}));
+  MB_TRY(maybe({w->unpool_w, w->proj_packed, w->ffn_norm_w, w->next_norm_w}));
+  return w->proj_packed ? MB_OK : need({w->unpool_w});
 }
 
 int check_weights_pool(const mb_weights *w) {
   if (!w) return MB_ERR_NULL;
-  MB_TRY(need({w->pool_w}));
-  return maybe({w->pre_norm_w});
+  MB_TRY(maybe({w->pool_w, w->proj_packed, w->pre_norm_w}));
+  return w->proj_packed ? MB_OK : need({w->pool_w});
 }
 
 int run_route(const mb_dims &d, const uint16_t *x, const mb_weights *w, float *logits, int flags,
@@ -240,6 +243,7 @@ int run_route(const mb_dims &d, const uint16_t *x, const mb_weights *w, float *l
 
 int run_pool(const mb_dims &d, const uint16_t *x, const mb_weights *w, uint16_t *h, void *ws,
              hipStream_t s) {
+  if (!w->pool_w) return MB_ERR_UNSUPPORTED;  // (only proj_packed: the per-step kernels read the caller's layout)
   const Layout L = layout_of(d);
   MB_HIP(launch_gemm_bf16(x, w->pool_w, h, d.rows, d.pooled, d.hidden, at<float>(ws, L.partial),
                           nullptr, s));
@@ -262,6 +266,7 @@ int run_experts(const mb_dims &d, const uint16_t *h, const float *wts, const int
 
 int run_unpool_boundary(const mb_dims &d, const uint16_t *moe_out, const mb_weights *w,
                         float *stream, uint16_t *x_next, uint16_t *u, void *ws, hipStream_t s) {
+  if (!w->unpool_w) return MB_ERR_UNSUPPORTED;  // (only proj_packed, as in run_pool)
   const Layout L = layout_of(d);
   MB_HIP(launch_gemm_bf16(moe_out, w->unpool_w, u, d.rows, d.hidden, d.pooled,
                           at<float>(ws, L.partial), nullptr, s));
@@ -339,6 +344,10 @@ BlockParams base_params(const mb_dims &d, const mb_weights *w, void *ws, size_t 
     p.xp_down_s = X.down_s;
     p.post_norm_w = w->post_norm_w;
     p.unpool_w = w->unpool_w;
+    if (w->proj_packed) {
+      p.pool_wp = reinterpret_cast<const uint16_t *>(w->proj_packed);
+      p.unpool_wp = reinterpret_cast<const uint16_t *>(w->proj_packed + packed_projections(d.pooled, d.hidden).unpool);
+    }
     p.ffn_norm_w = w->ffn_norm_w;
     p.gate = w->gate;
     p.next_norm_w = w->next_norm_w;
@@ -614,7 +623,8 @@ int run_block_call(const mb_dims &d, const uint16_t *x, const mb_weights *w, flo
   bool used = false;
   MB_TRY(run_fused(p, st, s, &used));
   if (used) return MB_OK;
-  if (!has_plain_experts(w)) return MB_ERR_UNSUPPORTED;  // the per-step kernels read the caller's layout
+  // The per-step kernels read the caller's layouts.
+  if (!has_plain_experts(w) || !w->pool_w || !w->unpool_w) return MB_ERR_UNSUPPORTED;
   MB_TRY(run_route(d, x, w, logits, 0, ids, wts, count, offset, route_list, active, n_active, s));
   MB_TRY(run_pool(d, x, w, h, ws, s));
   MB_TRY(run_experts(d, h, wts, offset, route_list, active, n_active, w, moe_out, ws, s, tp.act));
@@ -779,6 +789,25 @@ int mb_pack_experts(const mb_dims *dims, const mb_weights *w, uint8_t *packed, s
   return MB_OK;
 }
 
+int mb_packed_projections_bytes(const mb_dims *dims, size_t *bytes) {
+  MB_TRY(check_dims(dims));
+  if (!bytes) return MB_ERR_NULL;
+  *bytes = packed_projections(dims->pooled, dims->hidden).bytes;
+  return MB_OK;
+}
+
+int mb_pack_projections(const mb_dims *dims, const mb_weights *w, uint8_t *packed, size_t packed_bytes,
+                        void *stream) {
+  MB_TRY(check_dims(dims));
+  if (!w) return MB_ERR_NULL;
+  MB_TRY(need({w->pool_w, w->unpool_w, packed}));
+  size_t bytes = 0;
+  MB_TRY(mb_packed_projections_bytes(dims, &bytes));
+  if (packed_bytes < bytes) return MB_ERR_WORKSPACE;
+  MB_HIP(launch_pack_projections(*dims, w->pool_w, w->unpool_w, packed, (hipStream_t)stream));
+  return MB_OK;
+}
+
 int mb_attn_boundary(const mb_dims *dims, const uint16_t *partial, const uint16_t *post_attn_norm_w,
                      const uint16_t *gate, const uint16_t *pre_ffn_norm_w, float *stream, uint16_t *out,
                      void *stream_handle) {
@@ -856,8 +885,8 @@ const char *mb_status_string(int status) {
                                     "1024, top_k <= 16, experts*ceil(rows/64) <= 4096, hidden % 32, "
                                     "pooled % 128, inter % 128)";
     case MB_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
-    case MB_ERR_WORKSPACE: return "workspace (or packed-experts buffer) missing or smaller than "
-                                  "mb_workspace_bytes (mb_packed_experts_bytes)";
+    case MB_ERR_WORKSPACE: return "workspace (or packed-weights buffer) missing or smaller than "
+                                  "mb_workspace_bytes (mb_packed_experts_bytes, mb_packed_projections_bytes)";
     case MB_ERR_HIP: return "a kernel launch failed";
     case MB_ERR_SCRATCH: return "(mb_moe_block_noalloc) the sizes need more than its static scratch: "
                                 "over 56 MiB of buffers or 8 MiB of hand-off words (mb_moe_block "

@@ -1011,17 +1011,21 @@ constexpr int kWidePieces = 2048 / kThreads;
 // `cached` (other blocks' tasks read them too).  Without it, every row and
 // nontemporal weights, and none of that bookkeeping in the registers.
 template <bool kCoherentA, bool kRB = false, typename Wait>
-__device__ __forceinline__ void proj_wide(rsrc_t ra, const uint16_t *w, int rows, int n_out, int kdim, int gi, int q,
-                                          int ks, float *part, uint16_t *out, uint32_t *out_t, uint32_t tag,
-                                          unsigned char *stage, Wait wait, int t_begin = 0, int t_end = 0,
-                                          bool cached = false) {
+__device__ __forceinline__ void proj_wide(rsrc_t ra, const uint16_t *w, bool wpk, int rows, int n_out, int kdim,
+                                          int gi, int q, int ks, float *part, uint16_t *out, uint32_t *out_t,
+                                          uint32_t tag, unsigned char *stage, Wait wait, int t_begin = 0,
+                                          int t_end = 0, bool cached = false) {
   const int lane = (int)(tid() % MB_WAVE), wave = (int)(tid() / MB_WAVE), g = lane >> 4, r16 = lane & 15;
   const int kr = kdim / ks, k0 = q * kr, nch = kr / 32;
   const int f = gi * kWideCols + 16 * wave + r16;  // this lane's weight row
   const rsrc_t rw = make_rsrc(w);
-  const uint32_t wrow = f < n_out ? (uint32_t)(((size_t)f * kdim + k0 + 8 * g) * 2) : kOob;
+  // (wpk: w in the streaming layout, each chunk's wave load one kilobyte.)
+  const uint32_t wrow = f >= n_out ? kOob
+                        : wpk      ? (uint32_t)packed_offset(gi * kWaves + wave, kdim, k0, lane)
+                                   : (uint32_t)(((size_t)f * kdim + k0 + 8 * g) * 2);
+  const uint32_t wstep = wpk ? 1024u : 64u;
   auto wload = [&](int c) {
-    const uint32_t o = (wrow != kOob && c < nch) ? wrow + (uint32_t)c * 64u : kOob;
+    const uint32_t o = (wrow != kOob && c < nch) ? wrow + (uint32_t)c * wstep : kOob;
     return (kRB && cached) ? ld_b128(rw, o) : ld_nt16(rw, o);
   };
   const int tb = kRB ? t_begin : 0, te = kRB ? min(rows, t_end) : rows;
@@ -1151,16 +1155,20 @@ __device__ __forceinline__ void unpool_task(const BlockParams &p, const Deps &d,
   const int nch = P / 32, cps = (nch + ks - 1) / ks;
   const int c_begin = q * cps, c_end = min(nch, c_begin + cps);
   const int n0 = grp * 16 * kUnpoolTiles;
-  const rsrc_t rw = make_rsrc(p.unpool_w), ra = make_rsrc(mo);
+  const bool wpk = p.unpool_wp != nullptr;  // (the streaming layout)
+  const rsrc_t rw = make_rsrc(wpk ? p.unpool_wp : p.unpool_w), ra = make_rsrc(mo);
+  const uint32_t wstep = wpk ? 1024u : 64u;
   u32x4_t W[kUnpoolTiles][kUnpoolChunks];
 #pragma unroll
   for (int t = 0; t < kUnpoolTiles; ++t) {
     const int row = n0 + 16 * t + L.r16;
-    const uint32_t wrow = row < H ? (uint32_t)(((size_t)row * P + 8 * L.g) * 2) : kOob;
+    const uint32_t wrow = row >= H ? kOob
+                          : wpk    ? (uint32_t)packed_offset(n0 / 16 + t, P, 0, L.lane)
+                                   : (uint32_t)(((size_t)row * P + 8 * L.g) * 2);
 #pragma unroll
     for (int i = 0; i < kUnpoolChunks; ++i) {
       const int c = c_begin + L.wave + kWaves * i;
-      W[t][i] = ld_nt16(rw, (wrow != kOob && c < c_end) ? wrow + (uint32_t)c * 64u : kOob);
+      W[t][i] = ld_nt16(rw, (wrow != kOob && c < c_end) ? wrow + (uint32_t)c * wstep : kOob);
     }
   }
   wait_step(d, kCtrFin, p.n_fin);
@@ -2221,6 +2229,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         // Plain staging without a pre-norm: h only in bf16, each finished
         // tile (64-row block) signalled.
         const bool h_signal = kPS && p.plain_stage && !p.pre_norm_w;
+        const uint16_t *pw = p.pool_wp ? p.pool_wp : p.pool_w;
+        const bool pwk = p.pool_wp != nullptr;
         if (h_signal) {
           hp = p.h;
           ht = nullptr;
@@ -2231,8 +2241,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
           row_block_task(j - lo, p.row_blocks, gq, rb);
           if (gq < p.n_pool_tiles * p.pool_ks) {
             const int gi = gq / p.pool_ks, q = gq % p.pool_ks, t0 = rb * 64, t1 = t0 + 64;
-            proj_wide<false, true>(make_rsrc(p.x), p.pool_w, p.b, p.P, p.H, gi, q, p.pool_ks, p.pool_part, hp,
-                                   ht, d.tag(), scratch, []() {}, t0, t1, true);
+            proj_wide<false, true>(make_rsrc(p.x), pw, pwk, p.b, p.P, p.H, gi, q, p.pool_ks, p.pool_part, hp, ht,
+                                   d.tag(), scratch, []() {}, t0, t1, true);
             unsigned *cnt = &p.pool_cnt[gi * kMaxRowBlocks + rb];
             if (p.pool_ks == 1) {
               if (h_signal) signal_step(d, kCtrPool);
@@ -2244,8 +2254,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
           }
         } else {
           const int i = j - lo, gi = i / p.pool_ks, q = i % p.pool_ks;
-          proj_wide<false>(make_rsrc(p.x), p.pool_w, p.b, p.P, p.H, gi, q, p.pool_ks, p.pool_part, hp, ht,
-                           d.tag(), scratch, []() {});
+          proj_wide<false>(make_rsrc(p.x), pw, pwk, p.b, p.P, p.H, gi, q, p.pool_ks, p.pool_part, hp, ht, d.tag(),
+                           scratch, []() {});
           unsigned *cnt = &p.pool_cnt[gi * kMaxRowBlocks];
           if (p.pool_ks == 1) {
             if (h_signal) signal_step(d, kCtrPool);
@@ -2367,15 +2377,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         if (p.unpool_wide) {
           // Many rows: wide tiles, so each workgroup reads the MoE output once
           // per 64 features (one 64-row block of it beyond 64 rows).
+          const uint16_t *uw = p.unpool_wp ? p.unpool_wp : p.unpool_w;
+          const bool uwk = p.unpool_wp != nullptr;
           if (kMR && p.row_blocks > 1) {
             int gq, rb;
             row_block_task(i, p.row_blocks, gq, rb);
             if (gq < ((p.H + 63) / 64) * p.unpool_ks)
-              proj_wide<true, true>(make_rsrc(mo), p.unpool_w, p.b, p.H, p.P, gq / p.unpool_ks, gq % p.unpool_ks,
+              proj_wide<true, true>(make_rsrc(mo), uw, uwk, p.b, p.H, p.P, gq / p.unpool_ks, gq % p.unpool_ks,
                                     p.unpool_ks, p.unpool_part, p.u, nullptr, 0u, scratch,
                                     [&]() { wait_step(d, kCtrFin, p.n_fin); }, rb * 64, rb * 64 + 64, true);
           } else {
-            proj_wide<true>(make_rsrc(mo), p.unpool_w, p.b, p.H, p.P, i / p.unpool_ks, i % p.unpool_ks, p.unpool_ks,
+            proj_wide<true>(make_rsrc(mo), uw, uwk, p.b, p.H, p.P, i / p.unpool_ks, i % p.unpool_ks, p.unpool_ks,
                             p.unpool_part, p.u, nullptr, 0u, scratch, [&]() { wait_step(d, kCtrFin, p.n_fin); });
           }
         } else {
@@ -2391,8 +2403,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         // The next layer's QKV projection of x_next: wide tiles, the splits
         // added by the last to finish.
         const int gi = i / p.qkv_ks, q = i % p.qkv_ks;
-        proj_wide<true>(make_rsrc(p.x_next), p.qkv_w, p.b, p.qkv_rows, p.H, gi, q, p.qkv_ks, p.qkv_part, p.qkvg,
-                        nullptr, 0u, scratch, [&]() { wait_step(d, kCtrBound, p.n_boundary); });
+        proj_wide<true>(make_rsrc(p.x_next), p.qkv_w, false, p.b, p.qkv_rows, p.H, gi, q, p.qkv_ks, p.qkv_part,
+                        p.qkvg, nullptr, 0u, scratch, [&]() { wait_step(d, kCtrBound, p.n_boundary); });
         if (p.qkv_ks > 1 && last_arrival(&p.qkv_cnt[gi], (unsigned)p.qkv_ks, proj_flag(scratch))) {
           proj_wide_sum(p.qkv_part, p.qkvg, nullptr, 0u, p.b, p.qkv_rows, gi, p.qkv_ks);
           if (tid() == 0) __hip_atomic_store(&p.qkv_cnt[gi], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

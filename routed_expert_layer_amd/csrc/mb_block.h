@@ -117,6 +117,30 @@ __host__ __device__ inline PackedExperts packed_experts(int P, int I) {
   return PackedExperts{up, up + up_s, up + up_s + down, up + up_s + down + down_s};
 }
 
+// The pooler's and unpooler's bf16 weights in the streaming layout
+// (mb_pack_projections): a matrix [n_out][kdim] in tiles of 16 rows (rows
+// past n_out zero) and chunks of 32 elements, each (tile t, chunk c) the
+// kilobyte one wave loads as its MFMA A operand -- lane l's 16 bytes (at
+// 16 l) being elements 32 c + 8 (l / 16) .. + 7 of row 16 t + l % 16 -- at
+// (t * kdim / 32 + c) * 1024.  The pooler's [P][H] first, then the
+// unpooler's [H][P] at `unpool`.
+struct PackedProjections {
+  size_t unpool, bytes;
+};
+__host__ __device__ inline size_t packed_matrix_bytes(int n_out, int kdim) {
+  return (size_t)((n_out + 15) / 16) * 16 * kdim * 2;
+}
+__host__ __device__ inline PackedProjections packed_projections(int P, int H) {
+  const size_t pool = (packed_matrix_bytes(P, H) + 255) / 256 * 256;
+  return PackedProjections{pool, pool + packed_matrix_bytes(H, P)};
+}
+// Offset of lane `lane`'s 16 bytes of chunk 0 of 16-row tile t of a packed
+// matrix with kdim-element rows, from contraction element k0 (a multiple of
+// 32); chunk c + 1 follows chunk c at 1024 bytes.
+__host__ __device__ inline size_t packed_offset(int t, int kdim, int k0, int lane) {
+  return (((size_t)t * (kdim / 32) + k0 / 32) * 64 + lane) * 16;
+}
+
 struct BlockParams {
   int b, H, P, I, E, k, scoring;
   float mult, div_eps, route_scale, norm_eps;
@@ -143,6 +167,9 @@ struct BlockParams {
   const uint8_t *xp;
   size_t xp_stride, xp_up_s, xp_down, xp_down_s;
   const uint16_t *post_norm_w, *unpool_w, *ffn_norm_w, *gate, *next_norm_w;
+  // The pooler's and unpooler's weights in the streaming layout
+  // (PackedProjections), or NULL: pool_w / unpool_w as the caller laid them out.
+  const uint16_t *pool_wp, *unpool_wp;
   // in/out
   float *stream;
   uint16_t *x_next;

@@ -77,6 +77,10 @@ hipError_t launch_experts_finalize(const mb_dims &d, const float *y, const float
                                    const float *wts, const uint16_t *post_norm_w,
                                    uint16_t *moe_out, hipStream_t s);
 
+// The pooler's and unpooler's weights in the streaming layout (PackedProjections).
+hipError_t launch_pack_projections(const mb_dims &d, const uint16_t *pool_w, const uint16_t *unpool_w,
+                                   uint8_t *packed, hipStream_t s);
+
 // The experts' codes and scales in the streaming layout (PackedExperts).
 hipError_t launch_pack_experts(const mb_dims &d, const uint8_t *w13, const uint8_t *w13s, const uint8_t *w2,
                                const uint8_t *w2s, uint8_t *packed, hipStream_t s);

@@ -1,10 +1,13 @@
-// Repacking of the MXFP4 expert weights into the streaming layout the block
-// kernel reads (layout in mb_block.h, PackedExperts).
+// Repacking of the MXFP4 expert weights, and of the pooler's and unpooler's
+// bf16 weights, into the streaming layouts the block kernel reads (layouts in
+// mb_block.h, PackedExperts and PackedProjections).
 //
 // The values are the caller's: the codes and E8M0 scales of w13 and w2 in the
 // layout of [mono.decoder] MonoDims.expert_shapes, moved so that each wave
 // load of an expert unit is one contiguous kilobyte instead of sixteen
-// 64-byte pieces of sixteen rows.  This is done once per set of weights, when
+// 64-byte pieces of sixteen rows; likewise the bf16 pooler and unpooler
+// matrices, whose 64-byte row pieces read from sixteen rows at once reach a
+// quarter of the rate of contiguous loads.  This is done once per set of weights, when
 // they are loaded ([muse_moe_runner] MuseSparkAiterExperts: the ROCm experts
 // likewise take their weights in a layout prepared at load time).
 
@@ -59,6 +62,25 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t *__restr
   }
 }
 
+// One 16-byte piece of a packed bf16 matrix per thread (PackedProjections):
+// piece q is lane q % 64 of chunk (q / 64) % nch of 16-row tile q / (64 nch),
+// i.e. elements 32 c + 8 (lane / 16) .. + 7 of row 16 t + lane % 16 of
+// src [n_out][kdim] (zeros past n_out).
+__global__ __launch_bounds__(256) void pack_dense_kernel(const uint16_t *__restrict__ src, uint8_t *__restrict__ dst,
+                                                         int n_out, int kdim) {
+  const int nch = kdim / 32;
+  const size_t pieces = (size_t)((n_out + 15) / 16) * nch * 64;
+  for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < pieces; q += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(q % 64), c = (int)((q / 64) % nch);
+    const size_t t = q / (64 * (size_t)nch);
+    const size_t row = 16 * t + (size_t)(lane & 15);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (row < (size_t)n_out)
+      v = *reinterpret_cast<const uint4 *>(src + row * (size_t)kdim + 32 * (size_t)c + 8 * (size_t)(lane >> 4));
+    *reinterpret_cast<uint4 *>(dst + 16 * q) = v;
+  }
+}
+
 dim3 grid_for(size_t pieces, int experts) {
   size_t x = (pieces + 255) / 256;
   if (x > 1024) x = 1024;
@@ -82,6 +104,17 @@ hipError_t launch_pack_experts(const mb_dims &d, const uint8_t *w13, const uint8
                      (size_t)P * (I / 2), packed, L.stride, L.down, down_units, down_nch, I, 32, 16);
   hipLaunchKernelGGL(pack_scales_kernel, grid_for((size_t)down_units * down_ngr * 128, E), dim3(256), 0, s, w2s,
                      (size_t)P * (I / 32), packed, L.stride, L.down_s, down_units, down_ngr, I, 32, 16);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_projections(const mb_dims &d, const uint16_t *pool_w, const uint16_t *unpool_w,
+                                   uint8_t *packed, hipStream_t s) {
+  const int P = d.pooled, H = d.hidden;
+  const PackedProjections L = packed_projections(P, H);
+  hipLaunchKernelGGL(pack_dense_kernel, grid_for(packed_matrix_bytes(P, H) / 16, 1), dim3(256), 0, s, pool_w,
+                     packed, P, H);
+  hipLaunchKernelGGL(pack_dense_kernel, grid_for(packed_matrix_bytes(H, P) / 16, 1), dim3(256), 0, s, unpool_w,
+                     packed + L.unpool, H, P);
   return hipGetLastError();
 }
 

@@ -41,13 +41,17 @@ class GpuBlock:
         self.dims = rel.make_dims(**dims_kwargs(self.blk.dims))
 
     def use_packed(self, keep_plain: bool = False) -> torch.Tensor:
-        """Stream the experts from mb_pack_experts' layout (and, unless
-        keep_plain, pass no caller-layout expert pointers at all)."""
+        """Stream the experts from mb_pack_experts' layout and the pooler's
+        and unpooler's weights from mb_pack_projections' (and, unless
+        keep_plain, pass no caller-layout pointers for them at all).  Returns
+        the packed experts; the packed projections stay in proj_packed."""
         packed = rel.pack_experts(self.dims, self.weights)
+        self.proj_packed = rel.pack_projections(self.dims, self.weights)
         torch.cuda.synchronize()
         self.wt["experts_packed"] = packed
+        self.wt["proj_packed"] = self.proj_packed
         if not keep_plain:
-            for n in ("w13", "w13_scale", "w2", "w2_scale"):
+            for n in ("w13", "w13_scale", "w2", "w2_scale", "pool_w", "unpool_w"):
                 self.wt.pop(n, None)
         self.weights = rel.make_weights(**self.wt)
         return packed

@@ -29,7 +29,8 @@ def test_header_declares_the_five_calls():
     for n in ("mb_route", "mb_pool", "mb_experts", "mb_unpool_boundary", "mb_moe_block",
               "mb_workspace_bytes", "mb_packed_experts_bytes", "mb_pack_experts", "mb_status_string",
               "mb_attn_boundary", "mb_next_qkv", "mb_effective_norm_weight", "mb_workspace_status",
-              "mb_workspace_reset", "mb_moe_block_noalloc"):
+              "mb_workspace_reset", "mb_moe_block_noalloc", "mb_packed_projections_bytes",
+              "mb_pack_projections"):
         assert n in names
     assert set(names) == set(rel.EXPORTS)
 
@@ -196,6 +197,55 @@ def test_packed_experts_stand_in_for_the_caller_layout():
     w = full_weights(w13=None)
     assert L.mb_moe_block(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE, None, FAKE, 1 << 40,
                           None) == MB_ERR_NULL
+
+
+def test_packed_projections_bytes():
+    # Both matrices whole (P and H multiples of 16): P*H*2 bytes each, the
+    # second from a 256-byte boundary.
+    n = ctypes.c_size_t(0)
+    assert rel.lib().mb_packed_projections_bytes(ctypes.byref(c1_dims()), ctypes.byref(n)) == MB_OK
+    assert n.value == 2 * (2048 * 4096 * 2)
+    # H = 96 (six 16-row tiles of the unpooler's matrix), P = 128.
+    d = c1_dims(hidden=96, pooled=128, inter=128)
+    assert rel.lib().mb_packed_projections_bytes(ctypes.byref(d), ctypes.byref(n)) == MB_OK
+    assert n.value == (128 * 96 * 2 + 255) // 256 * 256 + 96 * 128 * 2
+    assert rel.lib().mb_packed_projections_bytes(ctypes.byref(c1_dims(pooled=96)), ctypes.byref(n)) == 3
+    assert rel.lib().mb_packed_projections_bytes(ctypes.byref(c1_dims()), None) == MB_ERR_NULL
+
+
+def test_pack_projections_argument_checks_before_launch():
+    d = c1_dims()
+    L = rel.lib()
+    n = ctypes.c_size_t(0)
+    L.mb_packed_projections_bytes(ctypes.byref(d), ctypes.byref(n))
+    w = full_weights()
+    assert L.mb_pack_projections(ctypes.byref(d), ctypes.byref(w), None, n.value, None) == MB_ERR_NULL
+    assert L.mb_pack_projections(ctypes.byref(d), ctypes.byref(w), FAKE, n.value - 1, None) == MB_ERR_WORKSPACE
+    assert L.mb_pack_projections(ctypes.byref(d), ctypes.byref(w), FAKE + 8, n.value, None) == MB_ERR_ALIGN
+    for missing in ("pool_w", "unpool_w"):
+        w = full_weights(**{missing: None})
+        assert L.mb_pack_projections(ctypes.byref(d), ctypes.byref(w), FAKE, n.value, None) == MB_ERR_NULL
+
+
+def test_packed_projections_stand_in_for_the_caller_layout():
+    d = c1_dims()
+    L = rel.lib()
+    # The packed projections alone satisfy the pooler's and unpooler's checks
+    # (the calls then fail on the missing workspace, before any launch) ...
+    w = full_weights(pool_w=None, unpool_w=None, proj_packed=FAKE)
+    assert L.mb_moe_block(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE, None, None, 0,
+                          None) == MB_ERR_WORKSPACE
+    assert L.mb_pool(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, None, 0, None) == MB_ERR_WORKSPACE
+    assert L.mb_unpool_boundary(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE, None, None, 0,
+                                None) == MB_ERR_WORKSPACE
+    # ... a misaligned buffer is refused, and without either layout the weights are missing.
+    w = full_weights(proj_packed=FAKE + 4)
+    assert L.mb_pool(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE, 1 << 40, None) == MB_ERR_ALIGN
+    w = full_weights(pool_w=None)
+    assert L.mb_pool(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE, 1 << 40, None) == MB_ERR_NULL
+    w = full_weights(unpool_w=None)
+    assert L.mb_unpool_boundary(ctypes.byref(d), FAKE, ctypes.byref(w), FAKE, FAKE, None, FAKE, 1 << 40,
+                                None) == MB_ERR_NULL
 
 
 def test_mxfp4_activations_need_the_streaming_layout():

@@ -193,24 +193,49 @@ def packed_reference(blk) -> np.ndarray:
     return np.concatenate(parts, axis=1).reshape(-1)
 
 
+def packed_matrix_reference(m):
+    """mb_pack_projections' layout of one bf16 matrix [n_out, kdim] (bit
+    patterns), as mb.h documents it: per 16-row tile t (rows past n_out zero)
+    and 32-element chunk c, lane l's 8 elements 32 c + 8 (l / 16) .. + 7 of
+    row 16 t + l % 16, lanes in order."""
+    n_out, kdim = m.shape
+    tiles = (n_out + 15) // 16
+    pad = np.zeros((tiles * 16, kdim), np.uint16)
+    pad[:n_out] = m
+    # [t, r, c, g, j] -> [t, c, g, r, j]: lane l = 16 g + r.
+    return pad.reshape(tiles, 16, kdim // 32, 4, 8).transpose(0, 2, 3, 1, 4).reshape(-1).view(np.uint8)
+
+
+def packed_projections_reference(blk):
+    pool = packed_matrix_reference(blk.pool_w)
+    unpool = packed_matrix_reference(blk.unpool_w)
+    gap = np.zeros((-len(pool)) % 256, np.uint8)
+    return np.concatenate([pool, gap, unpool])
+
+
 @pytest.mark.parametrize("dims", [dict(), dict(hidden=96, pooled=640, inter=384, experts=5),
                                   dict(pooled=2048, inter=1024, experts=3)])
 def test_packed_layout_is_the_documented_one(dims):
     blk = synth.make_block("c0", seed=21, dims=small(**dims))
     g = GpuBlock(blk)
-    say(f"[gpu] pack experts {blk.dims}")
+    say(f"[gpu] pack experts and projections {blk.dims}")
     packed = g.use_packed().cpu().numpy()
     want = packed_reference(blk)
     assert packed.shape == want.shape
     assert np.array_equal(packed, want)
+    proj = g.proj_packed.cpu().numpy()
+    want = packed_projections_reference(blk)
+    assert proj.shape == want.shape
+    assert np.array_equal(proj, want)
 
 
 @pytest.mark.parametrize("case", [dict(), dict(rows=17), dict(rows=100, experts=16, top_k=4),
                                   dict(hidden=96, pooled=640, inter=384, rows=21),
                                   dict(hidden=4096, pooled=2048, inter=1024, experts=64, top_k=4, rows=16)])
 def test_packed_experts_match_caller_layout(case):
-    """Same values, same arithmetic order: every output bit-identical to the
-    caller-layout run, and both match the oracle."""
+    """Experts and projections in the streaming layouts: same values, same
+    arithmetic order, so every output is bit-identical to the caller-layout
+    run, and both match the oracle."""
     blk = synth.make_block("c0", seed=31, dims=small(**case))
     g = GpuBlock(blk)
     say(f"[gpu] packed vs caller layout {case}")
