@@ -1140,7 +1140,8 @@ __device__ __forceinline__ void proj_wide_sum(const float *part, uint16_t *out, 
 // over features n0 = 32 grp .. + 31 (two 16-feature MFMA tiles, the weights
 // in the A operand) and the contraction split q of ks (32-element chunks
 // [q cps, (q + 1) cps), dealt to the waves in turn), for every row t (the B
-// operand: lane r16 reads row r16 of the MoE output, from the copy `mo`).
+// operand: lane r16 reads row r16 of the MoE output, from the copy `mo`,
+// which the finalize tasks of the launch write chunk by chunk).
 // Every weight chunk of the task is requested before the wait for the
 // finalize tasks (kUnpoolChunks per wave at most: the host sizes the split
 // so), so that only the MoE output is read after it.  The waves' sums are
@@ -1175,7 +1176,12 @@ __device__ __forceinline__ void unpool_task(const BlockParams &p, const Deps &d,
   f32x4_t acc[kUnpoolTiles];
 #pragma unroll
   for (int t = 0; t < kUnpoolTiles; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const uint32_t arow = L.r16 < p.b ? (uint32_t)(((size_t)L.r16 * P + 8 * L.g) * 2) : kOob;
+  // (mpk: the finalize tasks' copy, chunk by chunk: moe_rep_off.)
+  const bool mpk = p.n_fin > 0;
+  const uint32_t arow = L.r16 >= p.b ? kOob
+                        : mpk         ? (uint32_t)(L.r16 * 64 + L.g * 16)
+                                      : (uint32_t)(((size_t)L.r16 * P + 8 * L.g) * 2);
+  const uint32_t astep = mpk ? (uint32_t)p.b * 64u : 64u;
   // Activations in batches, the next batch requested before the current
   // one's products (so the requests overlap); batches past this wave's last
   // chunk are skipped.
@@ -1187,7 +1193,7 @@ __device__ __forceinline__ void unpool_task(const BlockParams &p, const Deps &d,
 #pragma unroll
     for (int i = 0; i < kUnpoolActBatch; ++i) {
       const int c = c_begin + L.wave + kWaves * (b * kUnpoolActBatch + i);
-      dst[i] = ld_co16(ra, (arow != kOob && c < c_end) ? arow + (uint32_t)c * 64u : kOob);
+      dst[i] = ld_co16(ra, (arow != kOob && c < c_end) ? arow + (uint32_t)c * astep : kOob);
     }
   };
   act_batch(0, A[0]);
@@ -1938,6 +1944,14 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
 
 // ---------------------------------------------------------------- tail
 
+// Byte offset of element p of row t in a copy of the MoE output [b][P] laid
+// out chunk by chunk for the few-row unpooler: per 32-element chunk, the b
+// rows' 64 bytes one after another, so that a chunk's wave load is b * 64
+// contiguous bytes.
+__device__ __forceinline__ uint32_t moe_rep_off(int t, int p, int b) {
+  return (uint32_t)(((p / 32) * b + t) * 64 + (p % 32) * 2);
+}
+
 // moe_out[t, p] = bf16(sum_j (w_j / sqrt(ss_j / P + eps)) y_j[p] * w_post[p]),
 // ss_j = the route's per-tile sums of squares added in tile order, for the
 // task's features of row t (4 per thread); waits for the down units of the
@@ -1993,10 +2007,12 @@ __device__ __forceinline__ void fin_task(const BlockParams &p, const Deps &d, co
     *reinterpret_cast<u32x2_t *>(reinterpret_cast<unsigned char *>(p.moe_out) + off) = v;
     // Copies for the unpooler tasks, each reading the one its workgroup
     // index selects: hundreds of workgroups reading one copy queue on it.
+    // For the few-row unpooler (b <= 16) chunk by chunk (moe_rep_off).
     const rsrc_t rr = make_rsrc(p.moe_rep);
     const uint32_t rep_bytes = (uint32_t)(p.b * P * 2);
+    const uint32_t roff = p.unpool_wide ? off : moe_rep_off(t, p4, p.b);
 #pragma unroll
-    for (int c = 0; c < kMoeReplicas; ++c) st_co8(rr, off + rep_bytes * c, v);
+    for (int c = 0; c < kMoeReplicas; ++c) st_co8(rr, roff + rep_bytes * c, v);
   }
   signal_step(d, kCtrFin);
   stamp(p, 21);
