@@ -831,11 +831,12 @@ __device__ __forceinline__ void mark_route(const BlockParams &p, const RouteLds 
 }
 
 // (Expects every route marked, and a barrier since.)  by_count: the
-// workgroup's own list of active experts (R.act) in ascending order of
-// their route counts, ties by id (the routing outputs keep id order), so
-// that each round of expert units -- dealt to the waves in list order --
-// holds experts of about one size on every workgroup.  (The smallest first
-// measured faster than the largest first.)
+// workgroup's own list of active experts (R.act) in descending order of
+// their route counts, ties by id (the routing outputs keep id order): the
+// many-rows instance claims its rounds of up units, then of down units, in
+// list order, the costliest first.  (Measured against ascending order and
+// against down units in the reverse order: faster at every size but the
+// literal skew's, where ascending is ~3 us faster.)
 __device__ __forceinline__ void group_routes(const BlockParams &p, const RouteLds &R, bool out,
                                              bool by_count = false) {
   const int W = (p.b + 63) / 64;
@@ -901,7 +902,7 @@ __device__ __forceinline__ void group_routes(const BlockParams &p, const RouteLd
       const int c = R.off[e + 1] - R.off[e];
       for (int a2 = 0; a2 < na; ++a2) {
         const int e2 = R.act[a2], c2 = R.off[e2 + 1] - R.off[e2];
-        rk += (c2 < c || (c2 == c && e2 < e)) ? 1 : 0;
+        rk += (c2 > c || (c2 == c && e2 < e)) ? 1 : 0;
       }
     }
     __syncthreads();
@@ -2342,18 +2343,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // Plain staging: h complete before the workgroup's first up unit.
     if (kPS && p.plain_stage && (int)blockIdx.x * kWaves < nU)
       wait_step(d, p.pre_norm_w ? kCtrPrenorm : kCtrPool, p.n_h_ready);
-    if constexpr (kQ) {
+    if constexpr (kPS) {
+      // Many rows: units cost more or less with their expert's rows, so
+      // after a first round dealt by workgroup index each workgroup claims
+      // its next round of four units (one expert's) from a counter -- every
+      // up round before any down round, so a down unit only ever waits for
+      // up units that running workgroups hold.
+      int *slot = R.red;
+      auto next = [&](int ctr) {
+        if (tid() == 0) *slot = (int)atomic_inc(d.ctr(ctr));
+        __syncthreads();
+        const int q = G + uniform(*slot);
+        __syncthreads();
+        return q;
+      };
+      const int w = uniform(tid() / MB_WAVE);
+      if (p.xp) {
+        for (int q = blockIdx.x; kWaves * q < nU; q = next(kCtrUpQueue))
+          up_unit<true, false, kPS>(p, d, R, kWaves * q + w, stage);
+        stamp(p, 20);
+        for (int q = blockIdx.x; kWaves * q < nD; q = next(kCtrDownQueue))
+          down_unit<true, false, kPS>(p, d, R, kWaves * q + w, stage);
+      } else {
+        for (int q = blockIdx.x; kWaves * q < nU; q = next(kCtrUpQueue))
+          up_unit<false, false, kPS>(p, d, R, kWaves * q + w, stage);
+        stamp(p, 20);
+        for (int q = blockIdx.x; kWaves * q < nD; q = next(kCtrDownQueue))
+          down_unit<false, false, kPS>(p, d, R, kWaves * q + w, stage);
+      }
+    } else if constexpr (kQ) {
       for (int u = gw; u < nU; u += GW) up_unit<true, true>(p, d, R, u, stage);
       stamp(p, 20);
       for (int u = gw; u < nD; u += GW) down_unit<true, true>(p, d, R, u, stage);
     } else if (p.xp) {
-      for (int u = gw; u < nU; u += GW) up_unit<true, false, kPS>(p, d, R, u, stage);
+      for (int u = gw; u < nU; u += GW) up_unit<true, false>(p, d, R, u, stage);
       stamp(p, 20);
-      for (int u = gw; u < nD; u += GW) down_unit<true, false, kPS>(p, d, R, u, stage);
+      for (int u = gw; u < nD; u += GW) down_unit<true, false>(p, d, R, u, stage);
     } else {
-      for (int u = gw; u < nU; u += GW) up_unit<false, false, kPS>(p, d, R, u, stage);
+      for (int u = gw; u < nU; u += GW) up_unit<false, false>(p, d, R, u, stage);
       stamp(p, 20);
-      for (int u = gw; u < nD; u += GW) down_unit<false, false, kPS>(p, d, R, u, stage);
+      for (int u = gw; u < nD; u += GW) down_unit<false, false>(p, d, R, u, stage);
     }
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();

@@ -48,7 +48,9 @@ enum : int {
   kCtrFin = 3,       // finalize tasks done
   kCtrUnpool = 4,    // unpooler tasks done
   kCtrBound = 5,     // boundary rows done (awaited by the fused next-QKV tiles)
-  kNumCtr = 6,
+  kCtrUpQueue = 6,   // up-unit rounds claimed past the first (many-rows instance)
+  kCtrDownQueue = 7, // down-unit rounds claimed past the first (many-rows instance)
+  kNumCtr = 8,
 };
 // Copies and stripes of step counter i (replicas x stripes <= kReplicas).
 // The route and pre-norm counters have few producers and are awaited by
