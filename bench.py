@@ -219,8 +219,9 @@ def read_probe(mib: int) -> int:
     """Time the plain HBM read kernel (libmb_readprobe.so): over one buffer
     of `mib` MiB in each variant and grid, then, in the best variant, at the
     block's own sizes, each launch reading the next of several buffers that
-    together exceed the 256 MB Infinity Cache four times over.  One JSON line
-    per case."""
+    together exceed the 256 MB Infinity Cache four times over; then L2-resident
+    reads in the two shapes of a weight tile's wave loads.  One JSON line per
+    case."""
     import ctypes
 
     import numpy as np
@@ -277,6 +278,33 @@ def read_probe(mib: int) -> int:
         print(json.dumps({**top, "case": f"hbm read probe {size} B: best"}), flush=True)
         del bufs
         torch.cuda.empty_cache()
+    # The L2: a weight tile's wave loads as one contiguous kilobyte (the
+    # streaming layouts) against 16 rows x 64 bytes of a row-major matrix
+    # (the caller's layout), the rows as long as the pooler's (H = 7168) and
+    # the unpooler's (P = 3072) bf16 rows, and one odd length.
+    lib.mbp_tile_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint32, ctypes.c_uint32,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    buf = torch.ones(16 << 18, dtype=torch.float32, device=dev)  # 16 MiB
+    grid, steps = 768, 64
+    for tile, nbytes, rows, row_bytes, what in (
+            (0, 1 << 20, 0, 0, "contiguous 1 KB per wave load, 1 MiB buffer"),
+            (0, 2 << 20, 0, 0, "contiguous 1 KB per wave load, 2 MiB buffer"),
+            (1, 16 << 20, 64, 14336, "16 rows x 64 B per wave load, rows of 14336 B (64 rows)"),
+            (1, 16 << 20, 64, 6144, "16 rows x 64 B per wave load, rows of 6144 B (64 rows)"),
+            (1, 16 << 20, 64, 14400, "16 rows x 64 B per wave load, rows of 14400 B (64 rows)")):
+        def fn(_):
+            st = lib.mbp_tile_read(buf.data_ptr(), nbytes, tile, rows, row_bytes, steps, grid, sink.data_ptr(),
+                                   stream)
+            if st != 0:
+                raise RuntimeError(f"mbp_tile_read status {st}")
+        for i in range(3):
+            fn(i)
+        us = per_launch_us(torch, fn, 20)
+        med = float(np.median(us))
+        read = grid * 256 * 128 * steps
+        print(json.dumps({"case": f"l2 read probe: {what}", "workgroups": grid, "bytes_read": read,
+                          "us_per_launch": percentiles(us), "TBps_at_median": round(read / (med * 1e-6) / 1e12, 2)}),
+              flush=True)
     return 0
 
 
