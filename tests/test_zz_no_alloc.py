@@ -1,7 +1,7 @@
 """GPU: mb_moe_block_noalloc (the block on the library's static per-GPU
 scratch) gives mb_moe_block's results bit for bit, call after call: at the
 b = 16 decode step, then at fewer rows, then at other dims (E 128, H 7168),
-then at the first size again (the kernels are deterministic, so any state
+then at 80 rows (the many-rows kernel instance), then at the first size again (the kernels are deterministic, so any state
 the scratch carried over wrongly would show as a difference)."""
 
 import numpy as np
@@ -62,6 +62,12 @@ def test_noalloc_block_matches_the_workspace_block_call_after_call():
     big.use_packed()
     _same(big, "b=24, H 7168, E 128 (skewed routing)")
     del big
+    torch.cuda.empty_cache()
+    many = GpuBlock(synth.make_block("c1", seed=5, dims=synth.inputs.C1.with_rows(80)))
+    many.use_packed()
+    _same(many, "b=80 at the decode dims (the many-rows instance: fp64-MFMA router, 64-row block "
+                "tasks, plain staging, claimed unit rounds)")
+    del many
     torch.cuda.empty_cache()
     c1 = GpuBlock(synth.make_block("c1"))
     _same(c1, "b=16 again, caller expert layout")
