@@ -2337,7 +2337,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // P / 32 tiles per expert) and so is the wave count, so the four waves of
     // a workgroup always have units, of one expert, in the same rounds: the
     // units' workgroup barriers and signals rely on it.
-    const int gw = blockIdx.x * kWaves + uniform(tid() / MB_WAVE);
+    //
+    // The last resident slot's workgroups on the first quarter of the CUs
+    // take the last unit slots (the rest of that slot moving up): when the
+    // units leave workgroups idle (704 of 768 busy at the decode step), the
+    // idle ones sit on those CUs, whose workgroups measured the slowest to
+    // stream their units -- with the experts dealt in either order, so it is
+    // the CUs, not the data (c1 49.3 -> 48.7 us; reversing the whole last
+    // slot instead gained 0.1 us).
+    const int bx = (int)blockIdx.x, last = (G / p.cus - 1) * p.cus, quarter = p.cus / 4;
+    const int wslot = bx >= last ? last + (bx - last + p.cus - quarter) % p.cus : bx;
+    const int gw = wslot * kWaves + uniform(tid() / MB_WAVE);
     // (The expert layout and the activation format are template arguments:
     // each has its own registers.)
     // Plain staging: h complete before the workgroup's first up unit.
