@@ -819,6 +819,25 @@ __device__ __forceinline__ int wg_excl_scan(int v, int *red, int &total) {
   return pre + x - v;
 }
 
+// Many-rows instance: each active expert's rows in passes of up to 32 (the
+// units' two 16-column MFMA blocks), every pass an entry of vact with units
+// of its own, in the order of act: an expert with more rows than one pass
+// takes more workgroups, where a unit covering all its rows would stream the
+// expert's weights once per pass.
+__device__ __forceinline__ void build_passes(const RouteLds &R) {
+  const int na = uniform(*R.nact), a = tid();
+  int e = 0, np = 0;
+  if (a < na) {
+    e = R.act[a];
+    np = (R.off[e + 1] - R.off[e] + 31) / 32;
+  }
+  int tot = 0;
+  const int pos = wg_excl_scan(np, R.red, tot);
+  for (int j = 0; j < np; ++j) R.vact[pos + j] = (uint16_t)(e | (j << 8));
+  if (tid() == 0) R.nact[2] = tot;
+  __syncthreads();
+}
+
 // Route grouping from R.ids: per-expert bitmaps over rows (LDS atomics, so
 // independent of order), popcount counts, exclusive scans for offsets and
 // the active list, and route (t, j) of expert e at offset[e] + the number of
@@ -834,9 +853,10 @@ __device__ __forceinline__ void mark_route(const BlockParams &p, const RouteLds 
 // workgroup's own list of active experts (R.act) in descending order of
 // their route counts, ties by id (the routing outputs keep id order): the
 // many-rows instance claims its rounds of up units, then of down units, in
-// list order, the costliest first.  (Measured against ascending order and
-// against down units in the reverse order: faster at every size but the
-// literal skew's, where ascending is ~3 us faster.)
+// list order, the costliest first, each expert's rows in passes of up to 32
+// (build_passes).  (Measured against ascending order and against down units
+// in the reverse order: faster at every size but the literal skew's, where
+// ascending is ~3 us faster.)
 __device__ __forceinline__ void group_routes(const BlockParams &p, const RouteLds &R, bool out,
                                              bool by_count = false) {
   const int W = (p.b + 63) / 64;
@@ -908,6 +928,7 @@ __device__ __forceinline__ void group_routes(const BlockParams &p, const RouteLd
     __syncthreads();
     if (e >= 0) R.act[rk] = e;
     __syncthreads();
+    build_passes(R);
   }
 }
 
@@ -923,7 +944,8 @@ constexpr int kRouteBatch = 2;
 
 // The routing state a workgroup needs before its first expert unit: the
 // routes (from the caller, or polled from this workgroup's copy of the tagged
-// routes), then the grouping.
+// routes), then the grouping; by_count: the many-rows instance's order and
+// passes (group_routes).
 __device__ __forceinline__ void prepare_routing(const BlockParams &p, const Deps &d, const RouteLds &R,
                                                 bool by_count = false) {
   const bool out = p.routing_out && blockIdx.x == 0;
@@ -938,6 +960,7 @@ __device__ __forceinline__ void prepare_routing(const BlockParams &p, const Deps
     for (int i = tid(); i < p.E; i += kThreads) R.act[i] = p.active[i];
     if (tid() == 0) *R.nact = *p.n_active;
     __syncthreads();
+    if (by_count) build_passes(R);
     return;
   }
   const int Rn = p.b * p.k, R2 = 2 * Rn;
@@ -1838,8 +1861,11 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
   const int P = p.P, I = p.I;
   const int tiles = I / 16;
   const int a = unit / tiles, tile = unit % tiles;
-  const int e = uniform(R.act[a]);
-  const int row0 = uniform(R.off[e]), nrows = uniform(R.off[e + 1]) - row0;
+  // Many rows: the unit covers one pass of its expert's rows (build_passes).
+  const int ev = kPS ? uniform((int)R.vact[a]) : uniform(R.act[a]);
+  const int e = ev & 0xFF, m_begin = 32 * (ev >> 8);
+  const int row0 = uniform(R.off[e]), rows_e = uniform(R.off[e + 1]) - row0;
+  const int nrows = kPS ? min(rows_e, m_begin + 32) : rows_e;
   const int i0 = tile * 16;
   const MxTiles T =
       kPacked ? mx_packed(p.xp + (size_t)e * p.xp_stride, p.xp + (size_t)e * p.xp_stride + p.xp_up_s, tile, P, lane)
@@ -1852,8 +1878,8 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
   const rsrc_t rat = make_rsrc(p.act_t), rap = make_rsrc(p.act_tap), rpl = make_rsrc(p.act);
   const uint32_t tag = d.tag();
   const int nch = P / 128;
-  const int pr = pass_rows(nrows);
-  for (int m0 = 0; m0 < nrows; m0 += pr) {
+  const int pr = pass_rows(nrows - m_begin);
+  for (int m0 = m_begin; m0 < nrows; m0 += pr) {
     f32x4_t gs[2], us[2];
     auto row_e = [&](int m) { return m0 + m < nrows ? (uint32_t)((R.rl[row0 + m0 + m] / p.k) * P) : kOob; };
     if constexpr (kQ)
@@ -1893,21 +1919,24 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
   const int P = p.P, I = p.I;
   const int tiles = P / 32;
   const int a = unit / tiles, tile = unit % tiles;
-  const int e = uniform(R.act[a]);
-  const int row0 = uniform(R.off[e]), nrows = uniform(R.off[e + 1]) - row0;
+  const int ev = kPS ? uniform((int)R.vact[a]) : uniform(R.act[a]);
+  const int e = ev & 0xFF, m_begin = 32 * (ev >> 8);
+  const int row0 = uniform(R.off[e]), rows_e = uniform(R.off[e + 1]) - row0;
+  const int nrows = kPS ? min(rows_e, m_begin + 32) : rows_e;
   const int p0 = tile * 32;
   const MxTiles T =
       kPacked ? mx_packed(p.xp + (size_t)e * p.xp_stride + p.xp_down, p.xp + (size_t)e * p.xp_stride + p.xp_down_s,
                        tile, I, lane)
            : mx_plain(p.w2 + (size_t)e * P * (I / 2), p.w2s + (size_t)e * P * (I / 32), p0, p0 + 16, I, lane);
-  // Plain staging: act once the expert's up units (I / 16, four per
-  // signal) signalled.
-  const ActSrc A = (kPS && p.plain_stage) ? ActSrc{make_rsrc(p.act), false, d.up(e), (unsigned)(I / 16)}
-                                          : ActSrc{make_rsrc(p.act_t), true};
+  // Plain staging: act once the expert's up units (I / 16 per pass, four
+  // per signal) signalled.
+  const ActSrc A = (kPS && p.plain_stage)
+                       ? ActSrc{make_rsrc(p.act), false, d.up(e), (unsigned)(I / 16 * ((rows_e + 31) / 32))}
+                       : ActSrc{make_rsrc(p.act_t), true};
   const rsrc_t ry = make_rsrc(p.y), rss = make_rsrc(p.ssq);
   const int nch = I / 128;
-  const int pr = pass_rows(nrows);
-  for (int m0 = 0; m0 < nrows; m0 += pr) {
+  const int pr = pass_rows(nrows - m_begin);
+  for (int m0 = m_begin; m0 < nrows; m0 += pr) {
     f32x4_t y0[2], y1[2];
     auto row_e = [&](int m) { return m0 + m < nrows ? (uint32_t)((row0 + m0 + m) * I) : kOob; };
     if constexpr (kQ) {
@@ -1958,6 +1987,7 @@ __device__ __forceinline__ uint32_t moe_rep_off(int t, int p, int b) {
 // task's features of row t (4 per thread); waits for the down units of the
 // row's experts.  The post-norm weights are requested before the wait, the
 // route rows of y and the sums of squares together after it.
+template <bool kPasses>
 __device__ __forceinline__ void fin_task(const BlockParams &p, const Deps &d, const RouteLds &R,
                                          int task, unsigned char *lds) {
   const int P = p.P, k = p.k;
@@ -1969,7 +1999,12 @@ __device__ __forceinline__ void fin_task(const BlockParams &p, const Deps &d, co
   const int p4 = p_begin + tid() * 4;
   const bool mine = p4 < p_end;
   const u32x2_t pw = ld_b64(make_rsrc(p.post_norm_w), mine ? (uint32_t)p4 * 2 : kOob);
-  if (tid() < MB_WAVE) poll_ge(d, d.down(R.ids[t * k + (lane < k ? lane : 0)]), (unsigned)tiles);
+  if (tid() < MB_WAVE) {
+    // (kPasses: the expert's down units come per pass of 32 rows.)
+    const int e = R.ids[t * k + (lane < k ? lane : 0)];
+    const unsigned passes = kPasses ? (unsigned)(R.off[e + 1] - R.off[e] + 31) / 32u : 1u;
+    poll_ge(d, d.down(e), (unsigned)tiles * passes);
+  }
   __syncthreads();
   stamp(p, 19);
   float *coef = reinterpret_cast<float *>(lds);  // [k]
@@ -2327,7 +2362,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     stamp(p, 6);
     const int GW = G * kWaves;
     unsigned char *stage = scratch;
-    const int nact = uniform(*R.nact);
+    // (Many rows: units per pass of an expert's rows, build_passes.)
+    const int nact = kPS ? uniform(R.nact[2]) : uniform(*R.nact);
     const int nU = nact * (p.I / 16), nD = nact * (p.P / 32);
     // Up units and down units are dealt separately, so a wave's down units
     // belong to the experts of its own up units (with as many tiles per
@@ -2425,7 +2461,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         last = step;
       }
       if (step == 8) {
-        fin_task(p, d, R, i, scratch);
+        fin_task<kPS>(p, d, R, i, scratch);
       } else if (step == 9) {
         const uint16_t *mo =
             p.n_fin > 0 ? p.moe_rep + (size_t)(blockIdx.x % kMoeReplicas) * p.b * p.P : p.moe_out;
@@ -2475,6 +2511,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
 }  // namespace
 
+// Workgroups of kernel f, with lds bytes of dynamic LDS, that a CU holds at
+// once.  The occupancy query counts LDS in finer steps than gfx950 allocates
+// it: measured with workgroups that only stamp their start and spin, a CU
+// holds 5 of 32000 bytes (dynamic and static) but 4 of 32001, and 3 of 53760
+// but 2 of 53761, where the query answers 5 and 3 -- allocation in 1280-byte
+// steps of the CU's 160 KB.  The persistent kernel needs its whole grid
+// resident at once, so the query's answer is capped by that allocation.
+static int resident_groups(const void *f, size_t lds) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kThreads, lds) != hipSuccess) return 0;
+  hipFuncAttributes a{};
+  if (hipFuncGetAttributes(&a, f) != hipSuccess) return 0;
+  constexpr size_t kLdsPerCu = 160 * 1024, kLdsStep = 1280;
+  const size_t step = (lds + a.sharedSizeBytes + kLdsStep - 1) / kLdsStep * kLdsStep;
+  const int by_lds = (int)(kLdsPerCu / step);
+  return n < by_lds ? n : by_lds;
+}
+
 // An ordinary launch: the host sizes the grid to what the device holds at
 // once.  Should some workgroups not be resident together with the others
 // (another kernel holding compute units), the resident ones may wait on them
@@ -2492,11 +2546,7 @@ hipError_t launch_block_many(const BlockParams &p, int grid, size_t lds, hipStre
 }
 
 int block_max_groups_per_cu_many(size_t lds) {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_kernel<false, false, true>, kThreads, lds) !=
-      hipSuccess)
-    return 0;
-  return n;
+  return resident_groups(reinterpret_cast<const void *>(block_kernel<false, false, true>), lds);
 }
 #elif !defined(MB_BLOCK_W4A4) && !defined(MB_BLOCK_QKV)
 hipError_t launch_block(const BlockParams &p, int grid, size_t lds, hipStream_t s) {
@@ -2511,10 +2561,7 @@ int block_max_groups_per_cu(size_t lds, bool w4a4, bool qkv, bool many) {
   if (w4a4) return block_max_groups_per_cu_w4a4(lds, qkv);
   if (qkv) return block_max_groups_per_cu_qkv(lds);
   if (many) return block_max_groups_per_cu_many(lds);
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_kernel<false>, kThreads, lds) != hipSuccess)
-    return 0;
-  return n;
+  return resident_groups(reinterpret_cast<const void *>(block_kernel<false>), lds);
 }
 #elif defined(MB_BLOCK_W4A4) && !defined(MB_BLOCK_QKV)
 hipError_t launch_block_w4a4(const BlockParams &p, int grid, size_t lds, hipStream_t s) {
@@ -2525,10 +2572,7 @@ hipError_t launch_block_w4a4(const BlockParams &p, int grid, size_t lds, hipStre
 
 int block_max_groups_per_cu_w4a4(size_t lds, bool qkv) {
   if (qkv) return block_max_groups_per_cu_w4a4_qkv(lds);
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_kernel<true>, kThreads, lds) != hipSuccess)
-    return 0;
-  return n;
+  return resident_groups(reinterpret_cast<const void *>(block_kernel<true>), lds);
 }
 #elif defined(MB_BLOCK_QKV) && !defined(MB_BLOCK_W4A4)
 hipError_t launch_block_qkv(const BlockParams &p, int grid, size_t lds, hipStream_t s) {
@@ -2537,10 +2581,7 @@ hipError_t launch_block_qkv(const BlockParams &p, int grid, size_t lds, hipStrea
 }
 
 int block_max_groups_per_cu_qkv(size_t lds) {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_kernel<false, true>, kThreads, lds) != hipSuccess)
-    return 0;
-  return n;
+  return resident_groups(reinterpret_cast<const void *>(block_kernel<false, true>), lds);
 }
 #else
 hipError_t launch_block_w4a4_qkv(const BlockParams &p, int grid, size_t lds, hipStream_t s) {
@@ -2549,10 +2590,7 @@ hipError_t launch_block_w4a4_qkv(const BlockParams &p, int grid, size_t lds, hip
 }
 
 int block_max_groups_per_cu_w4a4_qkv(size_t lds) {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_kernel<true, true>, kThreads, lds) != hipSuccess)
-    return 0;
-  return n;
+  return resident_groups(reinterpret_cast<const void *>(block_kernel<true, true>), lds);
 }
 #endif
 

@@ -223,9 +223,15 @@ struct RouteLds {
   uint16_t *rl;  // [b*k] route list (b*k < 65536)
   int *off;    // [E+1]
   int *act;    // [E]
-  int *nact;   // [1]; nact[1] holds the launch's generation
+  int *nact;   // [1]; nact[1] holds the launch's generation, nact[2] the entries of vact
   int *red;    // [8] scan scratch
   unsigned long long *bits;  // [E * ceil(b/64)]
+  // Many-rows instance: the active experts' passes of up to 32 rows, each
+  // with units of its own (expert | pass << 8), in the order of act.  Written
+  // once the grouping has read the bitmaps, over them: at most E + b k / 32
+  // entries of 2 bytes, within the bitmaps' 8 E ceil(b / 64) bytes for any b
+  // (k <= E).
+  uint16_t *vact;
 };
 
 __host__ __device__ inline size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
@@ -255,6 +261,7 @@ __device__ inline RouteLds route_lds(const BlockParams &p, unsigned char *base) 
   r.red = reinterpret_cast<int *>(base + o);
   o += 32;
   r.bits = reinterpret_cast<unsigned long long *>(base + o);
+  r.vact = reinterpret_cast<uint16_t *>(r.bits);
   (void)W;
   return r;
 }

@@ -96,6 +96,19 @@ def test_many_rows_with_norm_weights(case):
     run_and_check(synth.make_block("c0", seed=80 + case["rows"], dims=d, norm_weights=True), f"many rows+norms {case}")
 
 
+def test_many_rows_experts_in_passes():
+    """mb_experts from the oracle's h and routing at 200 rows over 8 experts:
+    the many-rows instance with the caller's routing, where every expert's
+    rows go to units in passes of 32 (several per expert here)."""
+    d = small(rows=200, experts=8, top_k=2)
+    blk = synth.make_block("c0", seed=90, dims=d)
+    ref = oracle.block(blk)
+    assert ref.routing.count.max() > 64
+    g = GpuBlock(blk)
+    say("[gpu] many-rows experts in passes")
+    assert_close(g.run_experts(ref.h, ref.routing), ref.moe_out, "many-rows experts")
+
+
 @pytest.mark.parametrize("rows", [13, 70])
 def test_per_step_kernels_with_norm_weights(rows):
     """More experts than the block kernel takes (300 > 256): mb_moe_block runs
@@ -138,6 +151,28 @@ def test_exact_ties_go_to_lowest_id():
     ref = oracle.route(blk)
     assert (ref.ids == np.array([2, 9, 12])).all()
     assert_routing(got, ref, "ties")
+
+
+@pytest.mark.parametrize("experts", [16, 128])
+def test_block_exact_ties_go_to_lowest_id(experts):
+    """The fused block's own routing (one wave per row: 32-bit order values,
+    the lowest id among equal ones) on exact ties: copies of one router row,
+    biased to win, go out in id order.  With 128 experts a lane holds experts
+    e and e + 64, and the copies sit in both halves."""
+    d = small(rows=6, experts=experts, top_k=3)
+    blk = synth.make_block("c0", seed=5, dims=d)
+    a, b, c = (2, 9, 12) if experts == 16 else (66, 2, 73)
+    w = blk.router_w
+    w[b] = w[a]
+    w[c] = w[a]
+    blk.expert_bias = np.zeros(experts, np.float32)
+    blk.expert_bias[[a, b, c]] = 2.0
+    ref = oracle.block(blk)
+    assert (ref.routing.ids == np.array(sorted([a, b, c]))).all()
+    g = GpuBlock(blk)
+    say(f"[gpu] block exact ties E={experts}")
+    got = g.run_block()
+    assert_block(got, ref, f"block ties E={experts}", blk)
 
 
 def test_block_is_deterministic():
