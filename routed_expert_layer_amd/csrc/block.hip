@@ -1863,7 +1863,7 @@ __device__ __forceinline__ void up_unit(const BlockParams &p, const Deps &d, con
   const int a = unit / tiles, tile = unit % tiles;
   // Many rows: the unit covers one pass of its expert's rows (build_passes).
   const int ev = kPS ? uniform((int)R.vact[a]) : uniform(R.act[a]);
-  const int e = ev & 0xFF, m_begin = 32 * (ev >> 8);
+  const int e = kPS ? ev & 0xFF : ev, m_begin = kPS ? 32 * (ev >> 8) : 0;
   const int row0 = uniform(R.off[e]), rows_e = uniform(R.off[e + 1]) - row0;
   const int nrows = kPS ? min(rows_e, m_begin + 32) : rows_e;
   const int i0 = tile * 16;
@@ -1920,7 +1920,7 @@ __device__ __forceinline__ void down_unit(const BlockParams &p, const Deps &d, c
   const int tiles = P / 32;
   const int a = unit / tiles, tile = unit % tiles;
   const int ev = kPS ? uniform((int)R.vact[a]) : uniform(R.act[a]);
-  const int e = ev & 0xFF, m_begin = 32 * (ev >> 8);
+  const int e = kPS ? ev & 0xFF : ev, m_begin = kPS ? 32 * (ev >> 8) : 0;
   const int row0 = uniform(R.off[e]), rows_e = uniform(R.off[e + 1]) - row0;
   const int nrows = kPS ? min(rows_e, m_begin + 32) : rows_e;
   const int p0 = tile * 32;
