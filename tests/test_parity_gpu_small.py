@@ -118,6 +118,15 @@ def test_per_step_kernels_with_norm_weights(rows):
     run_and_check(synth.make_block("c0", seed=60 + rows, dims=d, norm_weights=True), f"per-step E=300 rows={rows}")
 
 
+def test_per_step_kernels_wider():
+    """The per-step kernels at a wider shape than the test above: 320 experts
+    (more than the block kernel takes), H 2048, P 512, I 256, top-8 of
+    sigmoid scores, 24 rows, with every norm weight, so that the pooler's
+    row norm, the expert kernels and the boundary run over many tiles."""
+    d = small(rows=24, hidden=2048, pooled=512, inter=256, experts=320, top_k=8, eps=1e-6)
+    run_and_check(synth.make_block("c0", seed=71, dims=d, norm_weights=True), "per-step E=320 H=2048")
+
+
 def test_warm_up_saturated_logits():
     rows = read_golden("warm_up_routing.txt")
     d = small(rows=2, experts=16, top_k=4, eps=None)
