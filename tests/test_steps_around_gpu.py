@@ -125,7 +125,7 @@ def _block_with_qkv(g, n_out, w_qkvg):
     return {"stream": stream.cpu().numpy(), "x_next": bits(x_next), "qkvg": bits(qkvg)}, (dims, wt, ws)
 
 
-@pytest.mark.parametrize("case,n_out", [("c1", QKVG_C1), ("b37", 1040), ("c2", 2048), ("b1", 16)])
+@pytest.mark.parametrize("case,n_out", [("c1", QKVG_C1), ("b37", 1040), ("c2", 2048), ("b1", 16), ("b100", 528)])
 def test_fused_next_qkv(case, n_out):
     """The block with the projection fused: the block's own outputs bit-identical
     to the block without it, qkvg within the bf16 tolerance of the oracle's
@@ -136,6 +136,9 @@ def test_fused_next_qkv(case, n_out):
         blk = synth.make_block("c0", seed=47, dims=synth.Dims(37, 512, 384, 640, 16, 4, "sigmoid", 2.5, None, 1e-20))
     elif case == "b1":
         blk = synth.make_block("c0", seed=48, dims=synth.Dims(1, 256, 128, 256, 8, 2, "sigmoid", 2.5, None, 1e-20))
+    elif case == "b100":
+        # Beyond 64 rows: the block's 64-row block tasks and the projection's rows in two passes.
+        blk = synth.make_block("c0", seed=49, dims=synth.Dims(100, 256, 256, 1280, 8, 4, "softmax", 1.0, 1.5, 1e-6))
     else:
         blk = synth.make_block(case)
     d = blk.dims
