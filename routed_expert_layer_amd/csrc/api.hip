@@ -454,7 +454,8 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   p.router_multi = p.E * nrb > grid ? 1 : 0;
   // From 64 rows: tiles of 16 rows x 16 experts on fp64 MFMA, the
   // contraction split (in whole 32-element chunks) so that tiles x splits
-  // fill the grid at most once (at 32 rows the four-expert tasks were as fast).
+  // fill at most half of the grid (below; at 32 rows the four-expert tasks
+  // were as fast).
   const int rtiles = ((p.b + 15) / 16) * ((p.E + 15) / 16);
   p.router_mma = (st.router && p.router_multi && p.b >= 64) ? 1 : 0;
   // Beyond 64 rows the wide projections' tasks take one 64-row block each.
@@ -470,8 +471,12 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   // rows every unit stages many rows, and tagged words would double the
   // bytes it reads and add the tag checks.
   p.plain_stage = (many && st.experts) ? 1 : 0;
+  // The MFMA router's tasks take at most half of the grid, so that the
+  // pooler's tasks start in the same round beside them (at c2 with the whole
+  // grid: 512 router tasks, and 144 of the 384 pooler tasks ran after a
+  // router task; c2 210 -> 206 us, c3 b = 64 221 -> 217, b = 256 329 -> 327).
   p.router_ks = 1;
-  while (p.router_ks * 2 * rtiles <= grid && p.H % (p.router_ks * 2 * 32) == 0) p.router_ks *= 2;
+  while (p.router_ks * 2 * rtiles <= grid / 2 && p.H % (p.router_ks * 2 * 32) == 0) p.router_ks *= 2;
   const int n_router =
       st.router ? (p.router_mma ? rtiles * p.router_ks
                                 : (p.router_multi ? (p.E + kRouterExperts - 1) / kRouterExperts : p.E) * nrb)
