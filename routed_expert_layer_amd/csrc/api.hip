@@ -449,9 +449,13 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
   p.lds_route_bytes = (int)route_bytes;
   p.cus = cus;
   // Router tasks: one expert x 4 rows, or kRouterExperts experts x 4 rows
-  // when one-expert tasks would not fit the grid at once.
+  // when one-expert tasks would take more than one and a half rounds of the
+  // grid (against four-expert tasks, c3 b = 28 and 32, 896 and 1024
+  // one-expert tasks: 190.2 -> 185.1 and 196.3 -> 194.0 us; b = 48, two
+  // rounds: +0.9 us; b = 16, four-expert tasks to leave the pooler a round
+  // to itself: +8.6 us).
   const int nrb = (p.b + kRouterRowBlock - 1) / kRouterRowBlock;
-  p.router_multi = p.E * nrb > grid ? 1 : 0;
+  p.router_multi = 2 * p.E * nrb > 3 * grid ? 1 : 0;
   // From 64 rows: tiles of 16 rows x 16 experts on fp64 MFMA, the
   // contraction split (in whole 32-element chunks) so that tiles x splits
   // fill at most half of the grid (below; at 32 rows the four-expert tasks
