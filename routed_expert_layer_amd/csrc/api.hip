@@ -526,7 +526,10 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
     const int groups = (p.H + 63) / 64;
     int ks;
     if (p.row_blocks > 1) {
-      ks = row_block_split(groups, p.P, p.row_blocks, grid, kMaxSplitK);
+      // Two splits (pooled % 128 == 0): against the cost model's three, c3
+      // b = 96 and 128 236.0 -> 233.4 and 245.6 -> 243.3 us, b = 192 and 256
+      // the same; one split is between the two.
+      ks = 2;
     } else {
       ks = std::min(kMaxSplitK, std::max(1, grid / groups));
       while (ks > 1 && (p.P % ks != 0 || (p.P / ks) % 32 != 0)) --ks;
