@@ -531,7 +531,10 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
       // the same; one split is between the two.
       ks = 2;
     } else {
-      ks = std::min(kMaxSplitK, std::max(1, grid / groups));
+      // At most three splits: against min(8, grid / tiles) (six at H 7168),
+      // c2 206.2 -> 201.2 us, c3 b = 64 217.3 -> 212.6, b = 32 195.1 ->
+      // 191.8 (two and four splits in between).
+      ks = std::min(3, std::max(1, grid / groups));
       while (ks > 1 && (p.P % ks != 0 || (p.P / ks) % 32 != 0)) --ks;
     }
     p.unpool_ks = ks;
