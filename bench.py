@@ -684,7 +684,9 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        # The expert products' operand types: bf16 activations against the
+        # MXFP4 weights dequantized to bf16, or both MXFP4 (--act-quant).
+        "dtype": "fp4" if args.act_quant else "bf16",
         "data": "synthetic",
         "config": {
             "workload": "decode verify step b=16: H=4096 P=2048 I=1024 E=64 top_k=4 sigmoid, "
