@@ -2040,15 +2040,23 @@ __device__ __forceinline__ void fin_task(const BlockParams &p, const Deps &d, co
     const float o3 = acc[3] * bf16_bits_to_f32(pw[1] >> 16);
     const u32x2_t v = u32x2_t{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
     const uint32_t off = (uint32_t)(((size_t)t * P + p4) * 2);
-    *reinterpret_cast<u32x2_t *>(reinterpret_cast<unsigned char *>(p.moe_out) + off) = v;
-    // Copies for the unpooler tasks, each reading the one its workgroup
-    // index selects: hundreds of workgroups reading one copy queue on it.
-    // For the few-row unpooler (b <= 16) chunk by chunk (moe_rep_off).
-    const rsrc_t rr = make_rsrc(p.moe_rep);
-    const uint32_t rep_bytes = (uint32_t)(p.b * P * 2);
-    const uint32_t roff = p.unpool_wide ? off : moe_rep_off(t, p4, p.b);
+    if (p.unpool_wide) {
+      // The wide unpooler's tasks read moe_out itself (each 64-row block
+      // task a slice of it): kMoeReplicas copies of b x P cost the finalize
+      // more stores than they save the readers beyond 16 rows (c3 b = 256
+      // 322.9 -> 318.1 us, b = 128 244.2 -> 241.8, c2 201.1 -> 200.1).
+      st_co8(make_rsrc(p.moe_out), off, v);
+    } else {
+      *reinterpret_cast<u32x2_t *>(reinterpret_cast<unsigned char *>(p.moe_out) + off) = v;
+      // Copies for the few-row unpooler's tasks, each reading the one its
+      // workgroup index selects (hundreds of workgroups reading one copy
+      // queue on it), chunk by chunk (moe_rep_off).
+      const rsrc_t rr = make_rsrc(p.moe_rep);
+      const uint32_t rep_bytes = (uint32_t)(p.b * P * 2);
+      const uint32_t roff = moe_rep_off(t, p4, p.b);
 #pragma unroll
-    for (int c = 0; c < kMoeReplicas; ++c) st_co8(rr, roff + rep_bytes * c, v);
+      for (int c = 0; c < kMoeReplicas; ++c) st_co8(rr, roff + rep_bytes * c, v);
+    }
   }
   signal_step(d, kCtrFin);
   stamp(p, 21);
@@ -2464,7 +2472,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         fin_task<kPS>(p, d, R, i, scratch);
       } else if (step == 9) {
         const uint16_t *mo =
-            p.n_fin > 0 ? p.moe_rep + (size_t)(blockIdx.x % kMoeReplicas) * p.b * p.P : p.moe_out;
+            (p.n_fin > 0 && !p.unpool_wide) ? p.moe_rep + (size_t)(blockIdx.x % kMoeReplicas) * p.b * p.P : p.moe_out;
         if (p.unpool_wide) {
           // Many rows: wide tiles, so each workgroup reads the MoE output once
           // per 64 features (one 64-row block of it beyond 64 rows).
