@@ -526,10 +526,12 @@ int run_fused(BlockParams &p, const Steps &st, hipStream_t s, bool *used) {
     const int groups = (p.H + 63) / 64;
     int ks;
     if (p.row_blocks > 1) {
-      // Two splits (pooled % 128 == 0): against the cost model's three, c3
-      // b = 96 and 128 236.0 -> 233.4 and 245.6 -> 243.3 us, b = 192 and 256
-      // the same; one split is between the two.
-      ks = 2;
+      // Two splits (pooled % 128 == 0) up to three row blocks, one from
+      // four: against the cost model's three, c3 b = 96 and 128 236.0 ->
+      // 233.4 and 245.6 -> 243.3 us with two (one in between), b = 192 the
+      // same with two (+0.7 with one); at b = 256 one split against two
+      // 319.9 -> 308.9 us.
+      ks = p.row_blocks >= 4 ? 1 : 2;
     } else {
       // At most three splits: against min(8, grid / tiles) (six at H 7168),
       // c2 206.2 -> 201.2 us, c3 b = 64 217.3 -> 212.6, b = 32 195.1 ->
